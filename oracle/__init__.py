@@ -1,0 +1,304 @@
+"""CPU oracle for the ternary selective-SSM mixer forward (test infrastructure).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``oracle.c`` (plain C, fp64)
+through ctypes and shares nothing with the HIP library.  What each function
+computes, and the passage of the pages it follows, is documented in
+``oracle.c``.
+
+Parity pins: every function below is pinned in ``tests/test_oracle_pins.py``
+against closed forms, brute force, invariants or the printed fixtures under
+``tests/golden/``; none is "parity unpinned" except the whole-mixer numerical
+values beyond the composition of pinned stages (no page prints a mixer output).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+_c_f32p = ctypes.POINTER(ctypes.c_float)
+_c_f64p = ctypes.POINTER(ctypes.c_double)
+_c_i8p = ctypes.POINTER(ctypes.c_int8)
+_c_u8p = ctypes.POINTER(ctypes.c_uint8)
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math, no contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+               "-fopenmp", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _MixerWeights(ctypes.Structure):
+    _fields_ = [("c_in", _c_i8p), ("c_x", _c_i8p), ("c_dt", _c_i8p), ("c_out", _c_i8p),
+                ("s_in", _c_f32p), ("s_x", _c_f32p), ("s_dt", _c_f32p), ("s_out", _c_f32p),
+                ("g_in", _c_f32p), ("g_x", _c_f32p), ("g_dt", _c_f32p), ("g_out", _c_f32p),
+                ("dt_bias", _c_f32p), ("A", _c_f32p), ("D", _c_f32p)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        L.orc_round_bf16.argtypes = [ctypes.c_float]
+        L.orc_round_bf16.restype = ctypes.c_float
+        L.orc_round_array.argtypes = [_c_f64p, _c_f32p, _i64, ctypes.c_int]
+        L.orc_absmean.argtypes = [_c_f32p, _i64, _i64, _i64, _c_f32p]
+        L.orc_ternarize.argtypes = [_c_f32p, _i64, _i64, _i64, _c_f32p, _c_i8p]
+        L.orc_ternarize.restype = _i64
+        L.orc_packed_row_bytes.argtypes = [_i64]
+        L.orc_packed_row_bytes.restype = _i64
+        L.orc_pack.argtypes = [_c_i8p, _i64, _i64, _c_u8p]
+        L.orc_unpack.argtypes = [_c_u8p, _i64, _i64, _c_i8p]
+        L.orc_unpack.restype = _i64
+        L.orc_rms_scale.argtypes = [_c_f32p, _i64, ctypes.c_float]
+        L.orc_rms_scale.restype = ctypes.c_float
+        L.orc_norm_row.argtypes = [_c_f32p, _i64, _c_f32p, ctypes.c_float, _c_f32p]
+        L.orc_quant_row.argtypes = [_c_f32p, _i64, _c_i8p]
+        L.orc_quant_row.restype = ctypes.c_float
+        L.orc_bitlinear.argtypes = [_c_f32p, _i64, _i64, _i64, _c_f32p, ctypes.c_float, ctypes.c_int,
+                                    _c_i8p, _c_f32p, _i64, _i64, _c_f32p, _c_f64p, _c_i8p, _c_f32p,
+                                    _c_i32p]
+        L.orc_bitlinear.restype = ctypes.c_int
+        L.orc_softplus.argtypes = [ctypes.c_double]
+        L.orc_softplus.restype = ctypes.c_double
+        scan_args = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, _c_f32p, _c_f32p, _c_f32p, ctypes.c_int,
+                     _c_f32p, _c_f32p, _c_f32p, _c_f32p]
+        L.orc_selective_scan.argtypes = scan_args + [_c_f32p, _c_f64p, _c_f64p]
+        L.orc_selective_scan_blelloch.argtypes = scan_args + [_c_f32p, _c_f64p, _c_f64p]
+        L.orc_selective_scan_quadratic.argtypes = scan_args + [_c_f64p]
+        L.orc_mixer.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_float, ctypes.POINTER(_MixerWeights), _c_f32p,
+                                _i64, _i64, ctypes.c_int, _c_f64p]
+        L.orc_mixer.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- helpers
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _p(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctype)
+
+
+def round_bf16(a) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 (ties to even), returned as fp32."""
+    a = _f32(a)
+    d = a.astype(np.float64)
+    out = np.empty_like(a)
+    lib().orc_round_array(_p(d, _c_f64p), _p(out, _c_f32p), a.size, BF16)
+    return out
+
+
+# ---------------------------------------------------------------- O0
+
+def absmean(w, group: int = 0) -> np.ndarray:
+    w = _f32(w)
+    n, k = w.shape
+    out = np.empty(1 if group == 0 else n * (k // group), dtype=np.float32)
+    lib().orc_absmean(_p(w, _c_f32p), n, k, group, _p(out, _c_f32p))
+    return out if group == 0 else out.reshape(n, k // group)
+
+
+def ternarize(w, group: int, scale) -> tuple[np.ndarray, int]:
+    w = _f32(w)
+    n, k = w.shape
+    scale = _f32(scale)
+    codes = np.empty((n, k), dtype=np.int8)
+    zeros = lib().orc_ternarize(_p(w, _c_f32p), n, k, group, _p(scale, _c_f32p), _p(codes, _c_i8p))
+    return codes, int(zeros)
+
+
+def quantize_weights(w, group: int = 0, scale_in=None):
+    """(codes int8 [n,k], scale fp32, zero count): absmean (or caller) scale, then codes."""
+    scale = absmean(w, group) if scale_in is None else _f32(scale_in)
+    codes, zeros = ternarize(w, group, scale)
+    return codes, scale, zeros
+
+
+def packed_row_bytes(k: int) -> int:
+    return int(lib().orc_packed_row_bytes(k))
+
+
+def pack(codes) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    n, k = codes.shape
+    out = np.empty((n, packed_row_bytes(k)), dtype=np.uint8)
+    lib().orc_pack(_p(codes, _c_i8p), n, k, _p(out, _c_u8p))
+    return out
+
+
+def unpack(packed, k: int) -> tuple[np.ndarray, int]:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    n = packed.shape[0]
+    codes = np.empty((n, k), dtype=np.int8)
+    bad = lib().orc_unpack(_p(packed, _c_u8p), n, k, _p(codes, _c_i8p))
+    return codes, int(bad)
+
+
+# ---------------------------------------------------------------- O1 / O2
+
+def rms_scale(v, eps: float = 1e-5) -> np.float32:
+    v = _f32(v)
+    return np.float32(lib().orc_rms_scale(_p(v, _c_f32p), v.size, eps))
+
+
+def norm_row(v, g=None, eps: float = 1e-5) -> np.ndarray:
+    v = _f32(v)
+    g = None if g is None else _f32(g)
+    out = np.empty_like(v)
+    lib().orc_norm_row(_p(v, _c_f32p), v.size, _p(g, _c_f32p), eps, _p(out, _c_f32p))
+    return out
+
+
+def quant_row(xh) -> tuple[np.ndarray, np.float32]:
+    xh = _f32(xh)
+    q = np.empty(xh.size, dtype=np.int8)
+    m = lib().orc_quant_row(_p(xh, _c_f32p), xh.size, _p(q, _c_i8p))
+    return q, np.float32(m)
+
+
+# ---------------------------------------------------------------- O3 / O4
+
+def bitlinear(x, codes, w_scale, group: int = 0, act_bits: int = 8, norm_w=None, eps: float = 1e-5,
+              bias=None, k: int | None = None):
+    """BitLinear on rows x[m, 0:k] (x may be wider: its row stride is x.shape[1]).
+
+    Returns (y fp64 [m,n], xq int8 [m,k] or None, absmax fp32 [m] or None, acc int32 [m,n] or None).
+    """
+    x = _f32(x)
+    m, ldx = x.shape
+    k = ldx if k is None else k
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    n = codes.shape[0]
+    assert codes.shape[1] == k
+    w_scale = _f32(w_scale)
+    norm_w = None if norm_w is None else _f32(norm_w)
+    bias = None if bias is None else _f32(bias)
+    y = np.empty((m, n), dtype=np.float64)
+    if act_bits == 8:
+        xq = np.empty((m, k), dtype=np.int8)
+        am = np.empty(m, dtype=np.float32)
+        acc = np.empty((m, n), dtype=np.int32)
+    else:
+        xq = am = acc = None
+    rc = lib().orc_bitlinear(_p(x, _c_f32p), m, k, ldx, _p(norm_w, _c_f32p), eps, act_bits,
+                             _p(codes, _c_i8p), _p(w_scale, _c_f32p), n, group, _p(bias, _c_f32p),
+                             _p(y, _c_f64p), _p(xq, _c_i8p), _p(am, _c_f32p), _p(acc, _c_i32p))
+    if rc != 0:
+        raise OverflowError("int32 accumulator overflow")
+    return y, xq, am, acc
+
+
+# ---------------------------------------------------------------- O5 / O6 / O7
+
+def softplus(v: float) -> float:
+    return float(lib().orc_softplus(v))
+
+
+def _scan_common(x, delta, A, Bm, Cm, D, delta_bias, h0):
+    x, delta, A, Bm, Cm = _f32(x), _f32(delta), _f32(A), _f32(Bm), _f32(Cm)
+    batch, L, H = delta.shape
+    HP = x.shape[2]
+    P = HP // H
+    N = Bm.shape[2]
+    a_per_state = 1 if A.ndim == 2 else 0
+    D = None if D is None else _f32(D)
+    delta_bias = None if delta_bias is None else _f32(delta_bias)
+    h0 = None if h0 is None else _f32(h0)
+    return x, delta, A, Bm, Cm, D, delta_bias, h0, batch, L, H, P, N, a_per_state
+
+
+def selective_scan(x, delta, A, Bm, Cm, D=None, delta_bias=None, softplus: bool = True, h0=None,
+                   method: str = "loop"):
+    """Selective scan. x [B,L,H*P], delta [B,L,H], A [H,N] (Mamba-1) or [H] (SSD),
+    Bm/Cm [B,L,N], D [H].  Returns (y fp64 [B,L,H*P], h_last fp64 [B,H,P,N] or None).
+    method: "loop" (sequential recurrence), "blelloch" (parallel associative scan),
+    "quadratic" (state-space-duality masked form; h0 must be None; no h_last)."""
+    (x, delta, A, Bm, Cm, D, delta_bias, h0, batch, L, H, P, N,
+     aps) = _scan_common(x, delta, A, Bm, Cm, D, delta_bias, h0)
+    y = np.empty((batch, L, H * P), dtype=np.float64)
+    common = (batch, L, H, P, N, aps, _p(x, _c_f32p), _p(delta, _c_f32p), _p(delta_bias, _c_f32p),
+              int(softplus), _p(A, _c_f32p), _p(Bm, _c_f32p), _p(Cm, _c_f32p), _p(D, _c_f32p))
+    if method == "quadratic":
+        assert h0 is None
+        lib().orc_selective_scan_quadratic(*common, _p(y, _c_f64p))
+        return y, None
+    hl = np.empty((batch, H, P, N), dtype=np.float64)
+    fn = lib().orc_selective_scan if method == "loop" else lib().orc_selective_scan_blelloch
+    fn(*common, _p(h0, _c_f32p), _p(y, _c_f64p), _p(hl, _c_f64p))
+    return y, hl
+
+
+# ---------------------------------------------------------------- mixer
+
+MAMBA1, SSD = 0, 1
+
+
+def mixer(cfg, weights: dict, u, residual: bool = True) -> np.ndarray:
+    """One mixer layer.  cfg: mapping with kind, d_model, d_inner, d_state, dt_rank,
+    nheads, headdim, group_size, act_bits, act_dtype (F32/BF16), norm_eps.
+    weights: codes c_in/c_x/c_dt/c_out, scales s_*, dt_bias, A, D (gains optional g_*).
+    u: [B, L, d_model] values (bf16-representable when act_dtype is BF16).
+    Returns out fp64 [B, L, d_model], each value already rounded to act_dtype."""
+    u = _f32(u)
+    batch, L, dm = u.shape
+    keep = []
+
+    def arr(name, dtype, ctype):
+        a = weights.get(name)
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a, dtype=dtype)
+        keep.append(a)
+        return a.ctypes.data_as(ctype)
+
+    w = _MixerWeights(
+        arr("c_in", np.int8, _c_i8p), arr("c_x", np.int8, _c_i8p), arr("c_dt", np.int8, _c_i8p),
+        arr("c_out", np.int8, _c_i8p), arr("s_in", np.float32, _c_f32p), arr("s_x", np.float32, _c_f32p),
+        arr("s_dt", np.float32, _c_f32p), arr("s_out", np.float32, _c_f32p),
+        arr("g_in", np.float32, _c_f32p), arr("g_x", np.float32, _c_f32p), arr("g_dt", np.float32, _c_f32p),
+        arr("g_out", np.float32, _c_f32p), arr("dt_bias", np.float32, _c_f32p),
+        arr("A", np.float32, _c_f32p), arr("D", np.float32, _c_f32p))
+    out = np.empty((batch, L, dm), dtype=np.float64)
+    rc = lib().orc_mixer(int(cfg["kind"]), cfg["d_model"], cfg["d_inner"], cfg["d_state"], cfg.get("dt_rank", 0),
+                         cfg.get("nheads", 0), cfg.get("headdim", 0), cfg.get("group_size", 0), cfg["act_bits"],
+                         cfg["act_dtype"], cfg.get("norm_eps", 1e-5), ctypes.byref(w), _p(u, _c_f32p), batch, L,
+                         int(residual), _p(out, _c_f64p))
+    if rc != 0:
+        raise OverflowError("int32 accumulator overflow in the mixer")
+    return out
+
+
+def mixer_stack(cfg, layers: list, u) -> np.ndarray:
+    """out = u + mixer_l(u) applied layer after layer; returns fp64 of the stored values."""
+    h = _f32(u)
+    out = None
+    for wts in layers:
+        out = mixer(cfg, wts, h, residual=True)
+        h = out.astype(np.float32)
+    return out

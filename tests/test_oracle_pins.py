@@ -1,0 +1,554 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Each test names the passage or the mathematical fact it checks.  None of them
+re-types the oracle's own formula: they use hand-worked fixtures, closed forms,
+invariants, brute force, or an independent algorithm (numpy integer/fp64
+contractions, the Blelloch tree, the state-space-duality quadratic form).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rest = line.partition(":")
+            rows = [r.split() for r in rest.split(";")]
+            vals[key.strip()] = rows
+    return vals
+
+
+def _ints(rows, base=10):
+    return np.array([[int(v, base) for v in r] for r in rows])
+
+
+def _floats(rows):
+    return np.array([[float(v) for v in r] for r in rows], dtype=np.float32)
+
+
+# ------------------------------------------------------------------ O0: ternary weights
+
+def test_ternary_hand_examples():
+    """Absmean scale and codes on hand-worked examples (tests/golden/ternary_examples.txt)."""
+    g = _read_golden("ternary_examples.txt")
+    w1 = _floats(g["W1"])
+    codes, scale, zeros = oracle.quantize_weights(w1, 0)
+    assert np.float32(scale[0]) == pytest.approx(0.19375, rel=1e-6)
+    np.testing.assert_array_equal(codes, _ints(g["codes1"]))
+    assert zeros == 2
+    w2 = _floats(g["W2"])
+    codes, scale, _ = oracle.quantize_weights(w2, 4)
+    np.testing.assert_allclose(scale.ravel(), [0.225, 0.925], rtol=1e-6)
+    np.testing.assert_array_equal(codes, _ints(g["codes2"]))
+    codes, scale, _ = oracle.quantize_weights(_floats(g["W3"]), 0)
+    assert scale[0] == 0.5
+    np.testing.assert_array_equal(codes, _ints(g["codes3"]))
+
+
+@pytest.mark.parametrize("shape,group", [((512, 256), 0), ((48, 512), 0), ((64, 512), 128), ((7, 384), 128)])
+def test_ternary_set_membership_and_absmean(shape, group):
+    """Codes lie in {-1,0,+1} (TriSSM README; TernarySSM Key Points) and the stored scale is
+    mean|W| (BitNet b1.58 absmean), checked against an exactly rounded sum (math.fsum)."""
+    w = wl.normal(wl.rng(3), shape, 0.0, 0.02)
+    codes, scale, zeros = oracle.quantize_weights(w, group)
+    assert set(np.unique(codes)).issubset({-1, 0, 1})
+    assert zeros == int((codes == 0).sum())
+    if group == 0:
+        exact = np.float32(math.fsum(np.abs(w.astype(np.float64)).ravel()) / w.size)
+        assert abs(float(scale[0]) - float(exact)) <= float(np.spacing(exact))
+    else:
+        for i in range(shape[0]):
+            for gi in range(shape[1] // group):
+                seg = np.abs(w[i, gi * group:(gi + 1) * group].astype(np.float64))
+                exact = np.float32(math.fsum(seg) / group)
+                assert abs(float(scale[i, gi]) - float(exact)) <= float(np.spacing(exact))
+
+
+def test_ternary_codes_are_nearest_level():
+    """Each code is the nearest of {-1,0,+1} to w/gamma (decided in fp64 away from the
+    0.5 boundary): the definition of round-then-clamp."""
+    w = wl.normal(wl.rng(4), (256, 256), 0.0, 0.02)
+    codes, scale, _ = oracle.quantize_weights(w, 0)
+    r = w.astype(np.float64) / float(scale[0])
+    far = np.abs(np.abs(r) - 0.5) > 1e-5
+    expect = np.where(r > 0.5, 1, np.where(r < -0.5, -1, 0))
+    np.testing.assert_array_equal(codes[far], expect[far])
+
+
+def test_ternary_sign_symmetry():
+    """quantise(-W) = -codes with the same scale (round-half-even is odd-symmetric)."""
+    w = wl.normal(wl.rng(5), (64, 128), 0.0, 0.02)
+    c1, s1, _ = oracle.quantize_weights(w, 0)
+    c2, s2, _ = oracle.quantize_weights(-w, 0)
+    np.testing.assert_array_equal(c2, -c1)
+    assert s1[0] == s2[0]
+
+
+@pytest.mark.parametrize("j", [-3, 1, 4])
+def test_ternary_power_of_two_invariance(j):
+    """quantise(2^j W): same codes, scale * 2^j exactly (binary scaling is exact)."""
+    w = wl.normal(wl.rng(6), (64, 256), 0.0, 0.02)
+    for group in (0, 128):
+        c1, s1, _ = oracle.quantize_weights(w, group)
+        c2, s2, _ = oracle.quantize_weights(np.ldexp(w, j).astype(np.float32), group)
+        np.testing.assert_array_equal(c1, c2)
+        np.testing.assert_array_equal(np.ldexp(s1, j).astype(np.float32), s2)
+
+
+def test_ternary_gaussian_zero_ratio():
+    """Zero ratio (named in the Ternary Mamba abstract) of Gaussian weights: a code is 0
+    iff |w| < gamma/2 with gamma = sigma sqrt(2/pi), so the ratio is erf(sqrt(2/pi)/2/sqrt 2)
+    = 0.3101.  131,072 weights (an in_proj of the TriSSM shape): binomial sigma 0.0013."""
+    expect = math.erf(math.sqrt(2.0 / math.pi) / 2.0 / math.sqrt(2.0))
+    assert expect == pytest.approx(0.3101, abs=1e-4)
+    w = wl.normal(wl.rng(7), (512, 256), 0.0, 0.02)
+    _, _, zeros = oracle.quantize_weights(w, 0)
+    assert abs(zeros / w.size - expect) < 0.006
+
+
+def test_ternary_group_equals_tensor_on_slices():
+    """A per-group scale is the per-tensor rule applied to each (row, group) slice."""
+    g = wl.rng(8)
+    w = wl.normal(g, (5, 512), 0.0, 0.02) * np.repeat(
+        np.array([0.1, 1.0, 10.0, 3.0], np.float32), 128)[None, :]
+    w = w.astype(np.float32)
+    codes, scale, _ = oracle.quantize_weights(w, 128)
+    for i in range(5):
+        for gi in range(4):
+            sl = np.ascontiguousarray(w[i:i + 1, gi * 128:(gi + 1) * 128])
+            c, s, _ = oracle.quantize_weights(sl, 0)
+            assert s[0] == scale[i, gi]
+            np.testing.assert_array_equal(c[0], codes[i, gi * 128:(gi + 1) * 128])
+
+
+def test_ternary_zero_tensor_and_caller_scale():
+    """All-zero weights: scale 0 and all codes 0 (the 1e-5 floor guards the division).
+    A caller-supplied scale (learned scales, Ternary Mamba abstract) is used as given."""
+    codes, scale, zeros = oracle.quantize_weights(np.zeros((4, 16), np.float32), 0)
+    assert scale[0] == 0.0 and zeros == 64 and not codes.any()
+    w = np.array([[0.5, -0.5, 0.26, -0.24]], np.float32)
+    codes, scale, _ = oracle.quantize_weights(w, 0, scale_in=np.array([0.5], np.float32))
+    np.testing.assert_array_equal(codes, [[1, -1, 1, 0]])  # 0.52 -> 1, -0.48 -> 0
+
+
+def test_pack_golden_word():
+    """Packed bytes of a fixed 16-weight word and of a k = 8 row (tests/golden/pack_word.txt)."""
+    g = _read_golden("pack_word.txt")
+    codes = _ints(g["codes"]).astype(np.int8)
+    np.testing.assert_array_equal(oracle.pack(codes)[0], _ints(g["bytes"], 16)[0])
+    codes8 = _ints(g["codes8"]).astype(np.int8)
+    assert oracle.packed_row_bytes(8) == 4
+    np.testing.assert_array_equal(oracle.pack(codes8)[0], _ints(g["bytes8"], 16)[0])
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (3, 8), (5, 16), (7, 40), (64, 512), (4416, 32)])
+def test_pack_roundtrip_and_size(n, k):
+    """unpack(pack(q)) = q; n * 4 * ceil(k/16) bytes; the unused code 0b10 never appears."""
+    q = wl.rng(9).integers(-1, 2, size=(n, k)).astype(np.int8)
+    p = oracle.pack(q)
+    assert p.shape == (n, 4 * ((k + 15) // 16))
+    back, bad = oracle.unpack(p, k)
+    assert bad == 0
+    np.testing.assert_array_equal(back, q)
+    # 2 bits per weight: the packed tensor is 1/16 the size of the fp32 latent weights
+    if k % 16 == 0:
+        assert p.nbytes * 16 == q.size * 4
+
+
+# ------------------------------------------------------------------ O1/O2: RMSNorm + absmax int8
+
+def test_act_quant_hand_examples():
+    """RMSNorm + absmax int8 codes on hand-worked rows (tests/golden/act_quant_examples.txt)."""
+    g = _read_golden("act_quant_examples.txt")
+    for vk, qk in (("v1", "q1"), ("v2", "q2")):
+        v = _floats(g[vk])[0]
+        q, m = oracle.quant_row(oracle.norm_row(v))
+        np.testing.assert_array_equal(q, _ints(g[qk])[0])
+
+
+@pytest.mark.parametrize("k", [1, 8, 16, 63, 64, 65, 256, 1000, 4096])
+def test_rms_scale_error_bound(k):
+    """1/sqrt(mean v^2 + eps) to within fp32 rounding of the exact (fsum) value."""
+    v = wl.normal(wl.rng(10 + k), (k,))
+    exact = 1.0 / math.sqrt(math.fsum(float(a) * float(a) for a in v) / k + 1e-5)
+    r = float(oracle.rms_scale(v, 1e-5))
+    # k fp32 additions, a division, sqrt, a division: a few ulp plus k*2^-24 of the sum
+    assert abs(r - exact) / exact < (4 + k) * 2.0 ** -24
+
+
+def test_rms_scale_exact_on_integers():
+    """Small-integer rows sum exactly in any order, so the fp32 result is exactly
+    1 / sqrt(S/k + eps) evaluated in fp32 (order cannot matter)."""
+    v = np.array([(i % 7) - 3 for i in range(200)], np.float32)
+    S = np.float32(sum(int(a) * int(a) for a in v))
+    expect = np.float32(1.0) / np.sqrt(S / np.float32(200) + np.float32(1e-5))
+    assert oracle.rms_scale(v, 1e-5) == expect
+
+
+def test_act_quant_properties():
+    """For 2,300 random fp32 tokens (K = 64..512): max|q| = 127 exactly, |xh - q/sigma| <= 0.5/sigma,
+    quant(-x) = -quant(x), and eps = 0 gives exact power-of-two invariance of the codes."""
+    g = wl.rng(11)
+    for k in (64, 100, 512):
+        rows = wl.normal(g, (300 if k == 512 else 1000, k)) * np.exp(g.uniform(-4, 4, (1, 1))).astype(np.float32)
+        for v in rows:
+            xh = oracle.norm_row(v)
+            q, m = oracle.quant_row(xh)
+            assert np.abs(q).max() == 127
+            sigma = np.float32(127.0) / max(m, np.float32(1e-5))
+            # |xh*sigma - q| <= 1/2 plus the fp32 rounding of the product (<= 128 * 2^-24)
+            assert np.all(np.abs(xh.astype(np.float64) - q / float(sigma)) <= (0.5 + 2.0 ** -17) / float(sigma))
+            qn, _ = oracle.quant_row(oracle.norm_row(-v))
+            np.testing.assert_array_equal(qn, -q)
+        for v in rows[:50]:
+            q1, _ = oracle.quant_row(oracle.norm_row(v, eps=0.0))
+            q2, _ = oracle.quant_row(oracle.norm_row(np.ldexp(v, 3).astype(np.float32), eps=0.0))
+            np.testing.assert_array_equal(q1, q2)
+
+
+def test_act_quant_degenerate_rows():
+    """All-zero token: absmax 0, codes 0.  One-hot token: the hot element gets 127, others 0."""
+    q, m = oracle.quant_row(oracle.norm_row(np.zeros(64, np.float32)))
+    assert m == 0.0 and not q.any()
+    v = np.zeros(256, np.float32)
+    v[17] = -3.5
+    q, m = oracle.quant_row(oracle.norm_row(v))
+    assert q[17] == -127 and np.count_nonzero(q) == 1
+    assert m == pytest.approx(3.5 / math.sqrt(3.5 ** 2 / 256 + 1e-5), rel=1e-6)
+
+
+def test_norm_gain():
+    """Gains multiply the normalised row elementwise: gains of 2 double xh exactly."""
+    v = wl.normal(wl.rng(12), (96,))
+    a = oracle.norm_row(v)
+    b = oracle.norm_row(v, g=np.full(96, 2.0, np.float32))
+    np.testing.assert_array_equal(b, 2 * a)
+
+
+# ------------------------------------------------------------------ O3/O4: BitLinear
+
+def test_multiply_free_identity_exhaustive():
+    """TernarySSM abstract: ternary weights make the contraction add / subtract / skip.
+    All 3^4 ternary rows against 64 int8 vectors at K = 4: acc = sum_{w=+1} q - sum_{w=-1} q."""
+    rows = np.array(np.meshgrid(*[[-1, 0, 1]] * 4, indexing="ij")).reshape(4, -1).T.astype(np.int8)
+    g = wl.rng(13)
+    xs = g.integers(-128, 128, size=(64, 4))
+    xs[0] = 127
+    xs[1] = -128
+    for x in xs:
+        # rows of v whose codes are all int8 and whose normalised absmax hits 127 on
+        # the largest element: feed integer vectors scaled so quantisation is the identity
+        # is not possible in general, so check the identity on the accumulators directly
+        add = np.where(rows == 1, x[None, :], 0).sum(1)
+        sub = np.where(rows == -1, x[None, :], 0).sum(1)
+        np.testing.assert_array_equal(add - sub, rows.astype(np.int64) @ x)
+    # and through the oracle's BitLinear: accumulators equal the add/sub/skip sums of its codes
+    v = wl.normal(g, (64, 4))
+    _, xq, _, acc = oracle.bitlinear(v, rows, np.array([0.02], np.float32))
+    add = np.where(rows[None, :, :] == 1, xq[:, None, :].astype(np.int64), 0).sum(2)
+    sub = np.where(rows[None, :, :] == -1, xq[:, None, :].astype(np.int64), 0).sum(2)
+    np.testing.assert_array_equal(acc, add - sub)
+
+
+@pytest.mark.parametrize("m,k,n,group", [(37, 256, 48, 0), (16, 8, 128, 0), (9, 512, 64, 128), (5, 1024, 40, 0)])
+def test_bitlinear_a8_vs_numpy(m, k, n, group):
+    """A8 BitLinear: int8 codes of each row equal the row-wise quantiser; int32
+    accumulators equal an int64 numpy matmul of (codes x weight codes); |acc| <= 127 k;
+    dequantised output within the quantisation bound of the fp64 unquantised product."""
+    g = wl.rng(14)
+    x = wl.normal(g, (m, k))
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    codes, scale, _ = oracle.quantize_weights(w, group)
+    bias = wl.normal(g, (n,))
+    y, xq, am, acc = oracle.bitlinear(x, codes, scale, group, 8, bias=bias)
+    for i in range(m):
+        q, mm = oracle.quant_row(oracle.norm_row(x[i]))
+        np.testing.assert_array_equal(xq[i], q)
+        assert am[i] == mm
+    ref_acc = xq.astype(np.int64) @ codes.astype(np.int64).T
+    np.testing.assert_array_equal(acc, ref_acc)
+    assert np.abs(acc).max() <= 127 * k
+    # dequant: y - bias = s * acc * max(m)/127 per group
+    deq = np.maximum(am.astype(np.float64), 1e-5) / 127.0
+    if group == 0:
+        ref = acc * float(scale[0]) * deq[:, None]
+        sw = np.full((n, 1), float(scale[0]))
+        wf = codes.astype(np.float64) * float(scale[0])
+    else:
+        ng = k // group
+        ref = np.zeros((m, n))
+        for gi in range(ng):
+            a = xq[:, gi * group:(gi + 1) * group].astype(np.int64) @ codes[:, gi * group:(gi + 1) * group].astype(np.int64).T
+            ref += a * scale[:, gi].astype(np.float64)[None, :]
+        ref *= deq[:, None]
+        wf = codes.astype(np.float64) * np.repeat(scale.astype(np.float64), group, axis=1)
+    np.testing.assert_allclose(y - bias.astype(np.float64), ref, rtol=1e-12, atol=1e-12)
+    # quantisation error bound against the unquantised product s * W . xh
+    xh = np.stack([oracle.norm_row(x[i]) for i in range(m)]).astype(np.float64)
+    exact = xh @ wf.T
+    sigma = 127.0 / np.maximum(am.astype(np.float64), 1e-5)
+    bound = (np.abs(wf).sum(1)[None, :] * (0.5 / sigma)[:, None]) * (1 + 1e-5) + 1e-12
+    assert np.all(np.abs((y - bias) - exact) <= bound)
+
+
+@pytest.mark.parametrize("group", [0, 128])
+def test_bitlinear_a16_vs_numpy(group):
+    """A16 (W1.58A16, Ternary Mamba abstract): unquantised normalised activations times
+    per-group-scaled ternary weights, against an fp64 numpy matmul."""
+    g = wl.rng(15)
+    m, k, n = 23, 512, 72
+    x = wl.normal(g, (m, k))
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    codes, scale, _ = oracle.quantize_weights(w, group)
+    y, *_ = oracle.bitlinear(x, codes, scale, group, 16)
+    xh = np.stack([oracle.norm_row(x[i]) for i in range(m)]).astype(np.float64)
+    if group == 0:
+        wf = codes * float(scale[0])
+    else:
+        wf = codes * np.repeat(scale.astype(np.float64), group, axis=1)
+    np.testing.assert_allclose(y, xh @ wf.T, rtol=1e-12, atol=1e-12)
+
+
+def test_bitlinear_strided_input():
+    """A row stride wider than k reads the first k columns only (the dt projection reads
+    the first dt_rank columns of the x_proj output)."""
+    g = wl.rng(16)
+    wide = wl.normal(g, (11, 48))
+    codes, scale, _ = oracle.quantize_weights(wl.normal(g, (64, 16), 0, 0.02), 0)
+    y1, *_ = oracle.bitlinear(wide, codes, scale, k=16)
+    y2, *_ = oracle.bitlinear(np.ascontiguousarray(wide[:, :16]), codes, scale)
+    np.testing.assert_array_equal(y1, y2)
+
+
+# ------------------------------------------------------------------ O5-O7: selective scan
+
+def _scan(p, **kw):
+    return oracle.selective_scan(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p.get("D"),
+                                 p.get("dt_bias"), **kw)
+
+
+@pytest.mark.parametrize("H,P,N,aps,L", [(6, 1, 16, True, 37), (3, 4, 8, False, 64), (2, 1, 4, True, 1)])
+def test_scan_parallel_equals_sequential(H, P, N, aps, L):
+    """TriSSM README / TernarySSM abstract: the recurrence is evaluated with a parallel
+    associative scan; the Blelloch tree over (a, b) pairs equals the sequential loop."""
+    p = wl.scan_problem(2, L, H, P, N, aps, seed=17)
+    h0 = wl.normal(wl.rng(18), (2, H, P, N))
+    y1, h1 = _scan(p, h0=h0)
+    y2, h2 = _scan(p, h0=h0, method="blelloch")
+    np.testing.assert_allclose(y2, y1, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(h2, h1, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("aps", [True, False])
+def test_scan_quadratic_form(aps):
+    """State space duality ("Transformers are SSMs", cited by SSDi8): the masked quadratic
+    form sum_{s<=t} (C_t . B_s) exp(A sum_{s<r<=t} dt_r) dt_s x_s + D x_t equals the recurrence."""
+    H, P = (5, 1) if aps else (3, 4)
+    p = wl.scan_problem(2, 40, H, P, 8, aps, seed=19)
+    y1, _ = _scan(p)
+    y2, _ = _scan(p, method="quadratic")
+    np.testing.assert_allclose(y1, y2, rtol=1e-10, atol=1e-10)
+
+
+def test_scan_zero_B():
+    """B = 0: no input reaches the state, y = D x exactly."""
+    p = wl.scan_problem(2, 30, 4, 1, 16, True, seed=20)
+    p["Bm"] = np.zeros_like(p["Bm"])
+    y, h = _scan(p)
+    np.testing.assert_array_equal(y, p["x"].astype(np.float64) * p["D"].astype(np.float64)[None, None, :])
+    assert not h.any()
+
+
+def test_scan_zero_A_is_prefix_sum():
+    """A = 0: exp(dt A) = 1, so h_t = h0 + sum_{s<=t} dt_s x_s B_s (a cumulative sum)."""
+    p = wl.scan_problem(1, 25, 3, 1, 4, True, seed=21)
+    p["A"] = np.zeros_like(p["A"])
+    h0 = wl.normal(wl.rng(22), (1, 3, 1, 4))
+    y, h = _scan(p, h0=h0)
+    dt = np.log1p(np.exp(p["delta"].astype(np.float64) + p["dt_bias"][None, None, :]))[0]  # [L, H]
+    x = p["x"][0].astype(np.float64)
+    B = p["Bm"][0].astype(np.float64)
+    C = p["Cm"][0].astype(np.float64)
+    hs = h0[0, :, 0, :][None] + np.cumsum((dt * x)[:, :, None] * B[:, None, :], axis=0)  # [L, H, N]
+    yref = (hs * C[:, None, :]).sum(-1) + p["D"][None, :] * x
+    np.testing.assert_allclose(y[0], yref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(h[0, :, 0, :], hs[-1], rtol=1e-10)
+
+
+def test_scan_fast_decay_limit():
+    """Large dt with A = -1: exp(-dt) ~ 1e-22 forgets the past, so y_t = dt x_t (C_t.B_t) + D x_t."""
+    p = wl.scan_problem(1, 20, 3, 1, 8, True, seed=23)
+    p["A"] = -np.ones_like(p["A"])
+    p["delta"] = np.full_like(p["delta"], 50.0)
+    p["dt_bias"] = np.zeros_like(p["dt_bias"])
+    y, _ = _scan(p)
+    x = p["x"][0].astype(np.float64)
+    cb = (p["Cm"][0].astype(np.float64) * p["Bm"][0]).sum(-1)
+    yref = 50.0 * x * cb[:, None] + p["D"][None, :] * x
+    np.testing.assert_allclose(y[0], yref, rtol=1e-12, atol=1e-12)
+
+
+def test_scan_lti_convolution():
+    """Constant dt, B, C over time (S4, cited by SSDi8): the map is a causal convolution with
+    kernel K_j = sum_n C_n exp(dt A_n)^j dt B_n, checked against a direct O(L^2) convolution."""
+    L, H, N = 48, 2, 6
+    p = wl.scan_problem(1, L, H, 1, N, True, seed=24)
+    g = wl.rng(25)
+    for key in ("delta", "Bm", "Cm"):
+        p[key] = np.repeat(p[key][:, :1, :], L, axis=1)
+    y, _ = _scan(p)
+    dt = np.log1p(np.exp(p["delta"][0, 0].astype(np.float64) + p["dt_bias"]))  # [H]
+    B = p["Bm"][0, 0].astype(np.float64)
+    C = p["Cm"][0, 0].astype(np.float64)
+    x = p["x"][0].astype(np.float64)
+    for hd in range(H):
+        a = np.exp(dt[hd] * p["A"][hd].astype(np.float64))  # [N]
+        kern = np.array([(C * a ** j * dt[hd] * B).sum() for j in range(L)])
+        conv = np.array([sum(kern[t - s] * x[s, hd] for s in range(t + 1)) for t in range(L)])
+        np.testing.assert_allclose(y[0, :, hd], conv + p["D"][hd] * x[:, hd], rtol=1e-10, atol=1e-12)
+    del g
+
+
+def test_scan_first_order_iir_by_hand():
+    """One channel, one state, L = 3, no softplus: the first-order IIR unrolled by hand."""
+    x = np.array([1.0, 2.0, -1.0], np.float32).reshape(1, 3, 1)
+    dt = np.array([0.5, 1.0, 0.25], np.float32).reshape(1, 3, 1)
+    B = np.array([1.0, 1.0, 2.0], np.float32).reshape(1, 3, 1)
+    C = np.array([1.0, 0.5, 1.0], np.float32).reshape(1, 3, 1)
+    A = np.array([[-2.0]], np.float32)
+    D = np.array([0.1], np.float32)
+    y, h = oracle.selective_scan(x, dt, A, B, C, D, None, softplus=False)
+    h1 = 0.5 * 1 * 1
+    h2 = math.exp(-2.0) * h1 + 1.0 * 2 * 1
+    h3 = math.exp(-0.5) * h2 + 0.25 * -1 * 2
+    d = float(D[0])  # 0.1 as stored in fp32
+    np.testing.assert_allclose(y.ravel(), [h1 + d, 0.5 * h2 + 2 * d, h3 - d], rtol=1e-14)
+    assert h.ravel()[0] == pytest.approx(h3, rel=1e-14)
+
+
+def test_softplus():
+    """softplus(0) = ln 2; identity above 20; log(1 + e^v) below (Mamba's dt activation)."""
+    assert oracle.softplus(0.0) == pytest.approx(math.log(2.0), rel=1e-15)
+    assert oracle.softplus(25.0) == 25.0
+    assert oracle.softplus(-3.0) == pytest.approx(math.log1p(math.exp(-3.0)), rel=1e-15)
+    assert oracle.softplus(19.9) == pytest.approx(19.9 + math.log1p(math.exp(-19.9)), rel=1e-15)
+
+
+def test_scan_causality_and_streaming():
+    """Perturbing token t leaves y before t bitwise unchanged; a scan of L equals a scan of
+    L1 followed by a scan of L - L1 started from the carried state (to fp32 state rounding)."""
+    p = wl.scan_problem(2, 50, 4, 2, 8, False, seed=26)
+    y, h = _scan(p)
+    q = {k: v.copy() for k, v in p.items()}
+    q["x"][:, 30] += 1.0
+    q["delta"][:, 30] -= 0.7
+    q["Bm"][:, 30] *= 2
+    y2, _ = _scan(q)
+    np.testing.assert_array_equal(y2[:, :30], y[:, :30])
+    assert not np.array_equal(y2[:, 30], y[:, 30])
+    a = {k: (v[:, :20] if v.ndim == 3 else v) for k, v in p.items()}
+    b = {k: (v[:, 20:] if v.ndim == 3 else v) for k, v in p.items()}
+    ya, ha = _scan(a)
+    yb, hb = _scan(b, h0=ha.astype(np.float32))
+    np.testing.assert_allclose(np.concatenate([ya, yb], 1), y, rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(hb, h, rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------------------------ mixer composition
+
+def _layer_codes(cfg, lat):
+    out = {"dt_bias": lat["dt_bias"], "A": lat["A"], "D": lat["D"]}
+    for name in cfg.proj_shapes:
+        c, s, _ = oracle.quantize_weights(lat["W_" + name], cfg.group_size)
+        out["c_" + name] = c
+        out["s_" + name] = s
+    return out
+
+
+def _cfg_dict(cfg):
+    return dict(kind=cfg.kind, d_model=cfg.d_model, d_inner=cfg.d_inner, d_state=cfg.d_state, dt_rank=cfg.dt_rank,
+                nheads=cfg.nheads, headdim=cfg.headdim, group_size=cfg.group_size, act_bits=cfg.act_bits,
+                act_dtype=oracle.BF16 if cfg.act_dtype == "bf16" else oracle.F32, norm_eps=cfg.norm_eps)
+
+
+def test_mixer_mamba1_composition():
+    """TriSSM README: RMSNorm -> ternary BitLinear for the Delta, B, C projections, then the
+    scan.  The oracle mixer equals the composition of the separately pinned stages."""
+    cfg = wl.CONFIGS["bitssm_tiny"]
+    lat, u = wl.mixer_problem(cfg, seed=42)
+    w = _layer_codes(cfg, lat[0])
+    out = oracle.mixer(_cfg_dict(cfg), w, u)
+    M = cfg.tokens
+    uu = u.reshape(M, -1)
+    x, *_ = oracle.bitlinear(uu, w["c_in"], w["s_in"])
+    x = x.astype(np.float32)
+    p, *_ = oracle.bitlinear(x, w["c_x"], w["s_x"])
+    p = p.astype(np.float32)
+    R, N = cfg.dt_rank, cfg.d_state
+    z, *_ = oracle.bitlinear(p, w["c_dt"], w["s_dt"], k=R)
+    B = p[:, R:R + N].reshape(cfg.batch, cfg.seqlen, N)
+    C = p[:, R + N:].reshape(cfg.batch, cfg.seqlen, N)
+    y, _ = oracle.selective_scan(x.reshape(cfg.batch, cfg.seqlen, -1), z.astype(np.float32).reshape(cfg.batch, cfg.seqlen, -1),
+                                 w["A"], B, C, w["D"], w["dt_bias"])
+    o, *_ = oracle.bitlinear(y.astype(np.float32).reshape(M, -1), w["c_out"], w["s_out"])
+    ref = (o + uu).astype(np.float32).astype(np.float64).reshape(out.shape)
+    np.testing.assert_array_equal(out, ref)
+
+
+def test_mixer_ssd_composition():
+    """Ternary Mamba abstract (W1.58A16, grouped scales) on an SSD-shaped mixer: in_proj
+    columns [x | B | C | dt], scalar A per head; equals the composition of pinned stages."""
+    cfg = wl.CONFIGS["mamba2_ssd"].with_(d_model=256, d_inner=256, d_state=16, nheads=4, headdim=64, batch=2,
+                                          seqlen=24, act_dtype="f32")
+    lat, u = wl.mixer_problem(cfg, seed=42)
+    w = _layer_codes(cfg, lat[0])
+    out = oracle.mixer(_cfg_dict(cfg), w, u, residual=False)
+    M, H, P, N = cfg.tokens, cfg.nheads, cfg.headdim, cfg.d_state
+    v, *_ = oracle.bitlinear(u.reshape(M, -1), w["c_in"], w["s_in"], 128, 16)
+    v = v.astype(np.float32)
+    sh = (cfg.batch, cfg.seqlen)
+    y, _ = oracle.selective_scan(v[:, :H * P].reshape(*sh, -1), v[:, H * P + 2 * N:].reshape(*sh, -1), w["A"],
+                                 v[:, H * P:H * P + N].reshape(*sh, -1), v[:, H * P + N:H * P + 2 * N].reshape(*sh, -1),
+                                 w["D"], w["dt_bias"])
+    o, *_ = oracle.bitlinear(y.astype(np.float32).reshape(M, -1), w["c_out"], w["s_out"], 128, 16)
+    np.testing.assert_array_equal(out, o.astype(np.float32).astype(np.float64).reshape(out.shape))
+
+
+def test_mixer_causality():
+    """TriSSM README tests list causality: perturbing token t of u leaves every output before
+    t bitwise unchanged (oracle, Mamba-1 and SSD kinds)."""
+    for cfg in (wl.CONFIGS["bitssm_tiny"],
+                wl.CONFIGS["mamba2_ssd"].with_(d_model=128, d_inner=128, d_state=16, nheads=2, headdim=64,
+                                               batch=1, seqlen=32)):
+        lat, u = wl.mixer_problem(cfg, seed=43)
+        w = _layer_codes(cfg, lat[0])
+        if cfg.act_dtype == "bf16":
+            u = oracle.round_bf16(u)
+        out = oracle.mixer(_cfg_dict(cfg), w, u)
+        u2 = u.copy()
+        u2[:, 20] = -u2[:, 20] + 0.5
+        out2 = oracle.mixer(_cfg_dict(cfg), w, u2)
+        np.testing.assert_array_equal(out2[:, :20], out[:, :20])
+        assert not np.array_equal(out2[:, 20], out[:, 20])
+
+
+def test_round_bf16():
+    """bf16 rounding: nearest, ties to even, against values with a known bf16 neighbourhood."""
+    one = 1.0
+    ulp = 2.0 ** -7
+    vals = np.array([one, one + ulp / 2, one + ulp * 1.5, one + ulp / 4, -(one + ulp * 0.75), 3.0e-39], np.float32)
+    got = oracle.round_bf16(vals)
+    np.testing.assert_array_equal(got[:5], np.array([one, one, one + 2 * ulp, one, -(one + ulp)], np.float32))
+    assert got[5] == pytest.approx(3.0e-39, rel=2 ** -7)
