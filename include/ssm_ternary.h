@@ -1,0 +1,248 @@
+/*
+ * ssm_ternary.h -- C ABI of the MI355X (gfx950) ternary selective-SSM mixer forward.
+ *
+ * What is computed (cited by page title and section):
+ *  - "Associative Recall Under Ternary Quantization ... at 5M Parameters" (TriSSM
+ *    repository README), intro and BitSSM mixer paragraphs: the Delta, B, C
+ *    projections of a selective SSM are BitNet b1.58 BitLinear layers (ternary
+ *    weights, int8 activations); an RMSNorm precedes each ternary projection; the
+ *    recurrence is evaluated with a parallel associative scan.
+ *  - "Ternary Mamba: Grouped Quantization-Aware Training of W1.58A16 State Space
+ *    Models", abstract: per-group ternary scales with unquantised (16-bit)
+ *    activations (W1.58A16) on a Mamba-2 (SSD) model; the zero ratio of the codes.
+ *  - "Ternary State-Space Models ...", Key Points / Abstract: weights in {-1,0,+1},
+ *    multiply-free (add/subtract/skip) inference, SSM parallel scan.
+ *  - Works cited by title in "Baseline Shape Decides the Verdict ..." (Builds on):
+ *    BitNet b1.58 (absmean weight scale, absmax int8 activations) and Mamba
+ *    (softplus Delta, exp(Delta A) discretisation, selective recurrence); in
+ *    "SSDi8 ..." (Builds on): "Transformers are SSMs" (scalar A per head, SSD).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must be device memory of the current HIP
+ *    device; the caller owns all memory (inputs, outputs, weights, workspace).  The
+ *    library never allocates or frees device memory and keeps no device state.
+ *  - Work is enqueued on `stream` and runs asynchronously: no entry point
+ *    synchronises or copies to the host.
+ *  - Activations are token-major, row-major: element (token m, column c) is at
+ *    m * ld + c, token m = b * L + t for batch b and position t.
+ *  - Shapes, strides, dtypes and alignments are validated on the host before
+ *    anything is launched; a failing call launches nothing and returns a status
+ *    other than SSM_OK, with a message in ssm_last_error().  A failure reported by
+ *    the HIP runtime at launch returns SSM_ERR_DEVICE.  Nothing throws or aborts.
+ *  - Outputs must not overlap inputs unless an entry point says otherwise.
+ *  - Calls are thread-safe; the only global state is a thread-local error string.
+ *  - Results do not depend on the launch configuration or on earlier calls: every
+ *    integer stage is exact and every float reduction has a fixed order.
+ */
+#ifndef SSM_TERNARY_H
+#define SSM_TERNARY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSM_ERR_SHAPE = 2,       /* a size or stride is out of range or inconsistent */
+  SSM_ERR_DTYPE = 3,       /* dtype not supported for this argument */
+  SSM_ERR_ALIGN = 4,       /* a pointer or stride is not aligned as required */
+  SSM_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the *_workspace_bytes value */
+  SSM_ERR_UNSUPPORTED = 6, /* valid request this library does not implement */
+  SSM_ERR_DEVICE = 7       /* the HIP runtime reported an error */
+} ssm_status;
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1, SSM_I8 = 2 } ssm_dtype;
+
+/* Version of this ABI and of the packed weight format (bumps when either changes). */
+int ssm_abi_version(void);
+/* Static description of a status code. */
+const char* ssm_status_string(int status);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* ssm_last_error(void);
+
+/*
+ * Packed ternary weights (2 bits per weight).  The pages fix no storage format; this
+ * is the library's: a row of k weights occupies ssm_packed_row_bytes(k) =
+ * 4 * ceil(k / 16) bytes of little-endian 32-bit words, each word holding 16
+ * consecutive weights of the row.  Weight i of a word (i = 4 j + p, 0 <= j, p < 4)
+ * sits in byte p at bits 2j..2j+1: code 0b00 = 0, 0b01 = +1, 0b11 = -1 (0b10 is never
+ * written).  Weights past k in a row's last word are 0.  A tensor [n_out, k] is
+ * n_out such rows back to back, row-major.
+ */
+int64_t ssm_packed_row_bytes(int64_t k);
+
+/*
+ * ssm_ternary_quantize_weights -- absmean ternarisation and 2-bit packing (BitNet b1.58
+ * absmean scale; per-group scales from the Ternary Mamba abstract; the zero ratio it
+ * monitors).
+ *   w_latent   device fp32 [n_out, k] row-major latent weights.
+ *   group_size 0: one scale gamma = mean|W| for the tensor; > 0: one scale per run of
+ *              group_size consecutive weights of a row (k % group_size == 0).  The sum
+ *              of |w| is taken in fp64, each row (or row-group) in ascending k, the
+ *              row sums of a per-tensor scale in ascending row order; gamma is the fp32
+ *              rounding of sum / count.
+ *   scale_in   NULL: absmean scales as above.  Else device fp32, shaped like w_scale:
+ *              caller-supplied (e.g. learned) scales, used and copied as given.
+ *   w_packed   device out, n_out * ssm_packed_row_bytes(k) bytes.  Codes are
+ *              clamp(round_half_even(w / max(gamma, 1e-5)), -1, 1), fp32 IEEE division.
+ *   w_scale    device fp32 out, [1] or [n_out, k / group_size].
+ *   zero_count NULL or device int64 out: number of zero codes (overwritten).
+ *   workspace  device memory of ssm_ternary_quantize_workspace_bytes() bytes (fp64 row
+ *              sums); may be NULL when that size is 0.
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE (n_out < 1, k < 1, k % group_size != 0),
+ * SSM_ERR_WORKSPACE, SSM_ERR_DEVICE.
+ */
+size_t ssm_ternary_quantize_workspace_bytes(int64_t n_out, int64_t k, int64_t group_size,
+                                            const float* scale_in);
+ssm_status ssm_ternary_quantize_weights(const float* w_latent, int64_t n_out, int64_t k,
+                                        int64_t group_size, const float* scale_in,
+                                        uint8_t* w_packed, float* w_scale, int64_t* zero_count,
+                                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ssm_bitlinear_fwd -- RMSNorm -> activation quantisation -> ternary contraction ->
+ * rescale (TriSSM README: BitLinear with ternary weights and int8 activations, an
+ * RMSNorm before each ternary projection; W1.58A16 from the Ternary Mamba abstract).
+ * For each row m of x (the first k columns; row stride ldx):
+ *   r = 1 / sqrt(mean_k x^2 + norm_eps), fp32, summed as 64 partials (partial j takes
+ *       columns j, j+64, ... in ascending order with fused multiply-adds from 0) that
+ *       are then combined pairwise at distances 32, 16, 8, 4, 2, 1;
+ *   xh = (x * r) * norm_weight (fp32; no multiply when norm_weight is NULL).
+ *   act_bits 8 (A8): a = max|xh|; q = clamp(round_half_even(xh * (127 / max(a, 1e-5))),
+ *       -128, 127) int8; acc = sum_k q * w (int32, exact: the multiply-free
+ *       add/subtract/skip sum); y = acc * s_w * max(a, 1e-5) / 127 (per group: each
+ *       group's partial accumulator times its scale).
+ *   act_bits 16 (A16): y = sum_groups s[n, g] * sum_{k in g} bf16(xh) * w, fp32
+ *       accumulation (no activation quantisation).
+ *   then y += bias (if given) and y += residual (if given); stored as y_dtype.
+ * x_dtype SSM_I8 (A8 only): x already holds int8 codes and x_absmax their per-row
+ * absmax a; the norm and quantisation are skipped.
+ * Optional stage outputs (A8 only; each NULL or a device buffer): dbg_xq int8 [m, k],
+ * dbg_absmax fp32 [m], dbg_acc int32 [m, n_out] (sum over all groups).
+ * Requirements: 1 <= k <= 65536; n_out >= 1; m >= 0 (m == 0 launches nothing);
+ * ldx >= k, ldy >= n_out, ld_res >= n_out; group_size 0 or a multiple of 64 dividing k;
+ * act_bits 16 requires x_dtype F32 or BF16; residual has y_dtype.
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_WORKSPACE,
+ * SSM_ERR_UNSUPPORTED, SSM_ERR_DEVICE.
+ */
+typedef struct {
+  const void* x;
+  int32_t x_dtype; /* ssm_dtype */
+  int32_t act_bits;
+  int64_t m, k, ldx;
+  const float* x_absmax;    /* [m], required iff x_dtype == SSM_I8 */
+  const float* norm_weight; /* [k] RMSNorm gains or NULL (ones) */
+  float norm_eps;
+  int32_t pad0;
+  const uint8_t* w_packed;  /* [n_out, ssm_packed_row_bytes(k)] */
+  const float* w_scale;     /* [1] or [n_out, k / group_size] */
+  int64_t n_out, group_size;
+  const float* bias;        /* [n_out] or NULL */
+  const void* residual;     /* [m, ld_res] of y_dtype, or NULL */
+  int64_t ld_res;
+  void* y;
+  int32_t y_dtype;          /* SSM_F32 or SSM_BF16 */
+  int32_t pad1;
+  int64_t ldy;
+  int8_t* dbg_xq;
+  float* dbg_absmax;
+  int32_t* dbg_acc;
+} ssm_bitlinear_args;
+
+size_t ssm_bitlinear_workspace_bytes(const ssm_bitlinear_args* a);
+ssm_status ssm_bitlinear_fwd(const ssm_bitlinear_args* a, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * ssm_selective_scan_fwd -- the selective recurrence (Mamba; Transformers are SSMs),
+ * evaluated as a chunked parallel scan with an fp32 state carried across chunks
+ * (TriSSM README: parallel associative scan).  For batch b, head h, channel p of the
+ * head, state n and position t:
+ *   dt  = softplus(delta[b,t,h] + delta_bias[h]) if delta_softplus, else delta + bias;
+ *         softplus(v) = v for v > 20, else log(1 + e^v)
+ *   h_t = exp(dt * A) * h_{t-1} + (dt * x[b,t,h,p]) * B[b,t,n],  h_{-1} = h0 (or 0)
+ *   y[b,t,h,p] = sum_n C[b,t,n] * h_t[n] + D[h] * x[b,t,h,p]
+ * with A = A[h, n] (a_per_state = 1: Mamba-1, headdim 1, one channel per head) or
+ * A = A[h] (a_per_state = 0: SSD, a scalar per head).  B and C are shared by all heads.
+ * The state stays fp32 whatever act_dtype is.
+ *   x     [B, L, nheads * headdim], row stride ld_x;  delta [B, L, nheads], ld_delta;
+ *   Bm/Cm [B, L, d_state], ld_B / ld_C;  y [B, L, nheads * headdim], ld_y;
+ *   x, delta, Bm, Cm, y have act_dtype (SSM_F32 or SSM_BF16); A, D, delta_bias, h0,
+ *   h_last are fp32; h0 / h_last are [B, nheads, headdim, d_state] or NULL.
+ * Supported: a_per_state = 1 with headdim = 1 and d_state in {4, 8, 16, 32, 64};
+ * a_per_state = 0 with headdim in {16, 32, 64, 128} and d_state in {16, 32, 64, 128}.
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_WORKSPACE,
+ * SSM_ERR_UNSUPPORTED, SSM_ERR_DEVICE.
+ */
+typedef struct {
+  int64_t batch, seqlen, nheads, headdim, d_state;
+  int32_t a_per_state;
+  int32_t act_dtype; /* ssm_dtype */
+  const void* x;      int64_t ld_x;
+  const void* delta;  int64_t ld_delta;
+  const float* delta_bias;
+  int32_t delta_softplus;
+  int32_t pad0;
+  const float* A;
+  const void* Bm;     int64_t ld_B;
+  const void* Cm;     int64_t ld_C;
+  const float* D;
+  const float* h0;
+  float* h_last;
+  void* y;            int64_t ld_y;
+} ssm_scan_args;
+
+size_t ssm_selective_scan_workspace_bytes(const ssm_scan_args* a);
+ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
+ * ssm_mixer_fwd -- one ternary selective-SSM mixer layer (TriSSM README BitSSM mixer;
+ * Ternary Mamba abstract for the SSD / W1.58A16 kind), on u [B, L, d_model]:
+ *  SSM_MIXER_MAMBA1:  x = BL(u; W_in) [M, d_inner];  p = BL(x; W_x) = [dr | B | C]
+ *      [M, dt_rank + 2 d_state];  z = BL(dr; W_dt) [M, d_inner] (internal, fp32);
+ *      y = scan(x, z, dt_bias, A [d_inner, d_state], B, C, D);  out = BL(y; W_out).
+ *  SSM_MIXER_SSD:     v = BL(u; W_in) = [x (nheads*headdim) | B | C | dt (nheads)];
+ *      y = scan(x, dt, dt_bias, A [nheads], B, C, D);  out = BL(y; W_out).
+ *  BL is ssm_bitlinear_fwd with the configuration's act_bits, group_size and norm_eps;
+ *  x, p, v, y and out are stored in act_dtype; out += u when add_residual != 0.
+ * u and out have row stride d_model; out may equal u (in place) only when
+ * add_residual != 0.  workspace: ssm_mixer_workspace_bytes() bytes of device memory.
+ * Requirements: those of the BitLinear and scan calls above; Mamba-1 kind needs
+ * act_bits 8 and dt_rank <= 64.
+ * Errors: as ssm_bitlinear_fwd and ssm_selective_scan_fwd.
+ */
+typedef enum { SSM_MIXER_MAMBA1 = 0, SSM_MIXER_SSD = 1 } ssm_mixer_kind;
+
+typedef struct {
+  int32_t kind; /* ssm_mixer_kind */
+  int32_t act_bits;
+  int64_t d_model, d_inner, d_state, dt_rank, nheads, headdim, group_size;
+  int32_t act_dtype; /* ssm_dtype */
+  float norm_eps;
+} ssm_mixer_config;
+
+typedef struct {
+  const uint8_t *w_in, *w_x, *w_dt, *w_out; /* packed; w_x, w_dt unused by SSD */
+  const float *s_in, *s_x, *s_dt, *s_out;   /* scales as ssm_ternary_quantize_weights writes */
+  const float *g_in, *g_x, *g_dt, *g_out;   /* RMSNorm gains or NULL */
+  const float *dt_bias, *A, *D;
+} ssm_mixer_weights;
+
+size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64_t seqlen);
+ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u,
+                         void* out, int64_t batch, int64_t seqlen, int32_t add_residual,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_TERNARY_H */

@@ -1,0 +1,276 @@
+"""Python binding of libssm_ternary (MI355X / gfx950 ternary selective-SSM mixer forward).
+
+Argument marshalling only: every step runs in the HIP library behind the C ABI declared
+in include/ssm_ternary.h.  PyTorch supplies device memory and the current stream.  If the
+library has not been built, every entry point raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssm_ternary.so")
+
+SSM_F32, SSM_BF16, SSM_I8 = 0, 1, 2
+SSM_MIXER_MAMBA1, SSM_MIXER_SSD = 0, 1
+_DTYPES = {torch.float32: SSM_F32, torch.bfloat16: SSM_BF16, torch.int8: SSM_I8}
+_TORCH = {SSM_F32: torch.float32, SSM_BF16: torch.bfloat16, SSM_I8: torch.int8}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+class BitlinearArgs(ctypes.Structure):
+    _fields_ = [("x", _vp), ("x_dtype", _i32), ("act_bits", _i32), ("m", _i64), ("k", _i64), ("ldx", _i64),
+                ("x_absmax", _vp), ("norm_weight", _vp), ("norm_eps", ctypes.c_float), ("pad0", _i32),
+                ("w_packed", _vp), ("w_scale", _vp), ("n_out", _i64), ("group_size", _i64), ("bias", _vp),
+                ("residual", _vp), ("ld_res", _i64), ("y", _vp), ("y_dtype", _i32), ("pad1", _i32), ("ldy", _i64),
+                ("dbg_xq", _vp), ("dbg_absmax", _vp), ("dbg_acc", _vp)]
+
+
+class ScanArgs(ctypes.Structure):
+    _fields_ = [("batch", _i64), ("seqlen", _i64), ("nheads", _i64), ("headdim", _i64), ("d_state", _i64),
+                ("a_per_state", _i32), ("act_dtype", _i32), ("x", _vp), ("ld_x", _i64), ("delta", _vp),
+                ("ld_delta", _i64), ("delta_bias", _vp), ("delta_softplus", _i32), ("pad0", _i32), ("A", _vp),
+                ("Bm", _vp), ("ld_B", _i64), ("Cm", _vp), ("ld_C", _i64), ("D", _vp), ("h0", _vp),
+                ("h_last", _vp), ("y", _vp), ("ld_y", _i64)]
+
+
+class MixerConfig(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("act_bits", _i32), ("d_model", _i64), ("d_inner", _i64), ("d_state", _i64),
+                ("dt_rank", _i64), ("nheads", _i64), ("headdim", _i64), ("group_size", _i64), ("act_dtype", _i32),
+                ("norm_eps", ctypes.c_float)]
+
+
+class MixerWeights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w_in", "w_x", "w_dt", "w_out", "s_in", "s_x", "s_dt", "s_out", "g_in", "g_x",
+                                   "g_dt", "g_out", "dt_bias", "A", "D")]
+
+
+class SsmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed_row_bytes",
+           "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
+           "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
+           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd"]
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                               "g.build()'` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ssm_abi_version.restype = ctypes.c_int
+        L.ssm_status_string.argtypes = [ctypes.c_int]
+        L.ssm_status_string.restype = ctypes.c_char_p
+        L.ssm_last_error.restype = ctypes.c_char_p
+        L.ssm_packed_row_bytes.argtypes = [_i64]
+        L.ssm_packed_row_bytes.restype = _i64
+        L.ssm_ternary_quantize_workspace_bytes.argtypes = [_i64, _i64, _i64, _vp]
+        L.ssm_ternary_quantize_workspace_bytes.restype = _sz
+        L.ssm_ternary_quantize_weights.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.ssm_ternary_quantize_weights.restype = ctypes.c_int
+        L.ssm_bitlinear_workspace_bytes.argtypes = [ctypes.POINTER(BitlinearArgs)]
+        L.ssm_bitlinear_workspace_bytes.restype = _sz
+        L.ssm_bitlinear_fwd.argtypes = [ctypes.POINTER(BitlinearArgs), _vp, _sz, _vp]
+        L.ssm_bitlinear_fwd.restype = ctypes.c_int
+        L.ssm_selective_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanArgs)]
+        L.ssm_selective_scan_workspace_bytes.restype = _sz
+        L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp, _sz, _vp]
+        L.ssm_selective_scan_fwd.restype = ctypes.c_int
+        L.ssm_mixer_workspace_bytes.argtypes = [ctypes.POINTER(MixerConfig), _i64, _i64]
+        L.ssm_mixer_workspace_bytes.restype = _sz
+        L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
+                                    _i32, _vp, _sz, _vp]
+        L.ssm_mixer_fwd.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise SsmError(status, f"{L.ssm_status_string(status).decode()}: {L.ssm_last_error().decode()}")
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _rows(t: torch.Tensor, name: str):
+    """(row count, row stride) of a token-major tensor whose last dim is contiguous."""
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+    if t.dim() == 2:
+        return t.shape[0], t.stride(0)
+    if t.dim() == 3:
+        if t.shape[0] > 1 and t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError(f"{name}: rows of all batches must be evenly strided")
+        return t.shape[0] * t.shape[1], t.stride(1)
+    raise ValueError(f"{name}: expected 2 or 3 dims")
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    if nbytes == 0:
+        return None
+    if workspace is not None and workspace.numel() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+
+def ssm_abi_version() -> int:
+    return lib().ssm_abi_version()
+
+
+def ssm_packed_row_bytes(k: int) -> int:
+    return int(lib().ssm_packed_row_bytes(k))
+
+
+def ssm_ternary_quantize_weights(w: torch.Tensor, group_size: int = 0, scale_in: torch.Tensor | None = None,
+                                 stream=None):
+    """Absmean ternarisation + 2-bit packing.  Returns (packed uint8 [n, row_bytes], scale fp32
+    [1] or [n, k/group], zero_count int64 [1])."""
+    if w.dtype != torch.float32 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D float32 tensor")
+    n, k = w.shape
+    L = lib()
+    packed = torch.empty((n, ssm_packed_row_bytes(k)), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((1,) if group_size == 0 else (n, max(1, k // max(group_size, 1))), dtype=torch.float32,
+                        device=w.device)
+    zc = torch.empty(1, dtype=torch.int64, device=w.device)
+    nb = L.ssm_ternary_quantize_workspace_bytes(n, k, group_size, _p(scale_in))
+    ws = _workspace(nb, w.device)
+    _check(L.ssm_ternary_quantize_weights(_p(w), n, k, group_size, _p(scale_in), _p(packed), _p(scale), _p(zc),
+                                          _p(ws), nb, _stream(stream)))
+    return packed, scale, zc
+
+
+def ssm_bitlinear_fwd(x: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, n_out: int, *,
+                      act_bits: int = 8, group_size: int = 0, k: int | None = None,
+                      x_absmax: torch.Tensor | None = None, norm_weight: torch.Tensor | None = None,
+                      norm_eps: float = 1e-5, bias: torch.Tensor | None = None,
+                      residual: torch.Tensor | None = None, y_dtype: torch.dtype | None = None,
+                      out: torch.Tensor | None = None, debug: bool = False, workspace: torch.Tensor | None = None,
+                      stream=None):
+    """RMSNorm -> (int8 absmax | bf16) -> ternary contraction -> rescale (+ bias) (+ residual).
+    x: [m, >= k] (or [B, L, >= k]) rows with a contiguous last dimension.  Returns y [m, n_out]
+    (or (y, xq, absmax, acc) with debug=True)."""
+    m, ldx = _rows(x, "x")
+    k = x.shape[-1] if k is None else k
+    y_dtype = (x.dtype if x.dtype != torch.int8 else torch.float32) if y_dtype is None else y_dtype
+    if out is None:
+        out = torch.empty((m, n_out), dtype=y_dtype, device=x.device)
+    ym, ldy = _rows(out, "out")
+    a = BitlinearArgs()
+    a.x, a.x_dtype, a.act_bits = _p(x), _DTYPES[x.dtype], act_bits
+    a.m, a.k, a.ldx = m, k, ldx
+    a.x_absmax, a.norm_weight, a.norm_eps = _p(x_absmax), _p(norm_weight), norm_eps
+    a.w_packed, a.w_scale, a.n_out, a.group_size = _p(w_packed), _p(w_scale), n_out, group_size
+    a.bias = _p(bias)
+    if residual is not None:
+        _, a.ld_res = _rows(residual, "residual")
+        a.residual = _p(residual)
+    a.y, a.y_dtype, a.ldy = _p(out), _DTYPES[out.dtype], ldy
+    dbg = None
+    if debug:
+        dbg = (torch.empty((m, k), dtype=torch.int8, device=x.device),
+               torch.empty(m, dtype=torch.float32, device=x.device),
+               torch.empty((m, n_out), dtype=torch.int32, device=x.device))
+        a.dbg_xq, a.dbg_absmax, a.dbg_acc = (_p(t) for t in dbg)
+    L = lib()
+    nb = L.ssm_bitlinear_workspace_bytes(ctypes.byref(a))
+    ws = _workspace(nb, x.device, workspace)
+    _check(L.ssm_bitlinear_fwd(ctypes.byref(a), _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
+    return (out, *dbg) if debug else out
+
+
+def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+                           Cm: torch.Tensor, D: torch.Tensor | None = None, delta_bias: torch.Tensor | None = None,
+                           softplus: bool = True, h0: torch.Tensor | None = None, return_last_state: bool = False,
+                           out: torch.Tensor | None = None, stream=None):
+    """Selective scan.  x [B, L, H*P], delta [B, L, H], Bm/Cm [B, L, N]; A [H, N] (Mamba-1 kind,
+    P = 1) or [H] (SSD kind).  Views with a contiguous last dim and even row strides are fine."""
+    batch, seqlen, _ = delta.shape
+    H = delta.shape[2]
+    HP = x.shape[2]
+    N = Bm.shape[2]
+    aps = 1 if A.dim() == 2 else 0
+    if out is None:
+        out = torch.empty((batch, seqlen, HP), dtype=x.dtype, device=x.device)
+    hl = torch.empty((batch, H, HP // H, N), dtype=torch.float32, device=x.device) if return_last_state else None
+    a = ScanArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.d_state = batch, seqlen, H, HP // H, N
+    a.a_per_state, a.act_dtype = aps, _DTYPES[x.dtype]
+    a.x, a.ld_x = _p(x), _rows(x, "x")[1]
+    a.delta, a.ld_delta = _p(delta), _rows(delta, "delta")[1]
+    a.delta_bias, a.delta_softplus = _p(delta_bias), int(softplus)
+    a.A = _p(A)
+    a.Bm, a.ld_B = _p(Bm), _rows(Bm, "Bm")[1]
+    a.Cm, a.ld_C = _p(Cm), _rows(Cm, "Cm")[1]
+    a.D, a.h0, a.h_last = _p(D), _p(h0), _p(hl)
+    a.y, a.ld_y = _p(out), _rows(out, "out")[1]
+    L = lib()
+    nb = L.ssm_selective_scan_workspace_bytes(ctypes.byref(a))
+    ws = _workspace(nb, x.device)
+    _check(L.ssm_selective_scan_fwd(ctypes.byref(a), _p(ws), nb, _stream(stream)))
+    return (out, hl) if return_last_state else out
+
+
+def mixer_config(kind: int, d_model: int, d_inner: int, d_state: int, *, dt_rank: int = 0, nheads: int = 0,
+                 headdim: int = 0, act_bits: int = 8, group_size: int = 0, act_dtype: torch.dtype = torch.float32,
+                 norm_eps: float = 1e-5) -> MixerConfig:
+    c = MixerConfig()
+    c.kind, c.act_bits = kind, act_bits
+    c.d_model, c.d_inner, c.d_state, c.dt_rank = d_model, d_inner, d_state, dt_rank
+    c.nheads, c.headdim, c.group_size = nheads, headdim, group_size
+    c.act_dtype, c.norm_eps = _DTYPES[act_dtype], norm_eps
+    return c
+
+
+def ssm_mixer_workspace_bytes(cfg: MixerConfig, batch: int, seqlen: int) -> int:
+    return int(lib().ssm_mixer_workspace_bytes(ctypes.byref(cfg), batch, seqlen))
+
+
+def mixer_weights(w: dict) -> MixerWeights:
+    """w: packed weights w_in/w_x/w_dt/w_out, scales s_*, optional gains g_*, dt_bias, A, D (device tensors)."""
+    mw = MixerWeights()
+    for name, _ in MixerWeights._fields_:
+        setattr(mw, name, _p(w.get(name)))
+    return mw
+
+
+def ssm_mixer_fwd(cfg: MixerConfig, weights, u: torch.Tensor, add_residual: bool = True,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """One mixer layer on u [B, L, d_model] (contiguous).  weights: MixerWeights or dict."""
+    if not u.is_contiguous():
+        raise ValueError("u must be contiguous")
+    batch, seqlen, _ = u.shape
+    mw = weights if isinstance(weights, MixerWeights) else mixer_weights(weights)
+    if out is None:
+        out = torch.empty_like(u)
+    L = lib()
+    nb = L.ssm_mixer_workspace_bytes(ctypes.byref(cfg), batch, seqlen)
+    ws = _workspace(nb, u.device, workspace)
+    _check(L.ssm_mixer_fwd(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, seqlen, int(add_residual),
+                           _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
+    return out

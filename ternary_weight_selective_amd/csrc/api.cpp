@@ -1,0 +1,414 @@
+// C ABI entry points: host-side validation, workspace carving and launch sequencing.
+// Nothing here touches device memory except through kernel launches on the caller's stream.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+#include "ssm_ternary.h"
+
+using namespace ssm;
+
+namespace {
+
+thread_local std::string g_err;
+
+ssm_status fail(ssm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ssm_status dev(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SSM_OK;
+  return fail(SSM_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool act_dtype_ok(int32_t t) { return t == SSM_F32 || t == SSM_BF16; }
+size_t act_size(int32_t t) { return t == SSM_BF16 ? 2 : 4; }
+constexpr int64_t kMaxK = 4096;
+
+// ------------------------------------------------------------------ BitLinear
+
+struct BLPlan {
+  int64_t Kp = 0;
+  bool norm = false;
+  size_t off_am = 0, total = 0;
+};
+
+ssm_status bl_plan(const ssm_bitlinear_args* a, BLPlan* p) {
+  if (!a) return fail(SSM_ERR_NULL, "bitlinear: args is NULL");
+  if (a->act_bits != 8 && a->act_bits != 16) return fail(SSM_ERR_UNSUPPORTED, "bitlinear: act_bits must be 8 or 16");
+  if (a->x_dtype != SSM_F32 && a->x_dtype != SSM_BF16 && a->x_dtype != SSM_I8)
+    return fail(SSM_ERR_DTYPE, "bitlinear: x_dtype %d", a->x_dtype);
+  if (a->x_dtype == SSM_I8 && a->act_bits != 8) return fail(SSM_ERR_DTYPE, "bitlinear: int8 input needs act_bits 8");
+  if (!act_dtype_ok(a->y_dtype)) return fail(SSM_ERR_DTYPE, "bitlinear: y_dtype %d", a->y_dtype);
+  if (a->m < 0) return fail(SSM_ERR_SHAPE, "bitlinear: m = %lld", (long long)a->m);
+  if (a->k < 1 || a->k > kMaxK) return fail(SSM_ERR_SHAPE, "bitlinear: k = %lld not in [1, %lld]", (long long)a->k, (long long)kMaxK);
+  if (a->n_out < 1 || a->n_out > (1LL << 24)) return fail(SSM_ERR_SHAPE, "bitlinear: n_out = %lld", (long long)a->n_out);
+  if (a->ldx < a->k) return fail(SSM_ERR_SHAPE, "bitlinear: ldx %lld < k %lld", (long long)a->ldx, (long long)a->k);
+  if (a->ldy < a->n_out) return fail(SSM_ERR_SHAPE, "bitlinear: ldy %lld < n_out %lld", (long long)a->ldy, (long long)a->n_out);
+  if (a->residual && a->ld_res < a->n_out) return fail(SSM_ERR_SHAPE, "bitlinear: ld_res < n_out");
+  if (a->group_size < 0 || (a->group_size > 0 && (a->group_size % 64 != 0 || a->k % a->group_size != 0)))
+    return fail(SSM_ERR_SHAPE, "bitlinear: group_size %lld must be 0 or a multiple of 64 dividing k", (long long)a->group_size);
+  if (!a->w_packed || !a->w_scale) return fail(SSM_ERR_NULL, "bitlinear: w_packed / w_scale is NULL");
+  if (!aligned(a->w_packed, 4)) return fail(SSM_ERR_ALIGN, "bitlinear: w_packed must be 4-byte aligned");
+  if (a->m > 0 && (!a->x || !a->y)) return fail(SSM_ERR_NULL, "bitlinear: x / y is NULL");
+  if (a->act_bits == 16 && (a->dbg_xq || a->dbg_absmax || a->dbg_acc))
+    return fail(SSM_ERR_UNSUPPORTED, "bitlinear: stage outputs exist for act_bits 8 only");
+  p->Kp = round_up(a->k, 64);
+  p->norm = a->x_dtype != SSM_I8;
+  if (!p->norm) {
+    if (!a->x_absmax && a->m > 0) return fail(SSM_ERR_NULL, "bitlinear: x_absmax is required for int8 input");
+    if (a->k % 64 != 0 || a->ldx % 16 != 0 || !aligned(a->x, 16))
+      return fail(SSM_ERR_UNSUPPORTED, "bitlinear: int8 input needs k %% 64 == 0, ldx %% 16 == 0, 16-byte alignment");
+    p->total = 0;
+    return SSM_OK;
+  }
+  // A8: int8 codes; A16: bf16 rows, two terms (hi, lo) when the output is fp32
+  const size_t elt = a->act_bits == 8 ? 1 : (a->y_dtype == SSM_F32 ? 4 : 2);
+  p->off_am = align_up((size_t)a->m * p->Kp * elt);
+  p->total = a->act_bits == 8 ? align_up(p->off_am + (size_t)a->m * 4) : p->off_am;
+  return SSM_OK;
+}
+
+// Runs a planned BitLinear with its workspace.
+ssm_status bl_run(const ssm_bitlinear_args* a, const BLPlan& p, void* ws, hipStream_t s) {
+  if (a->m == 0) return SSM_OK;
+  GemmArgs g{};
+  g.W = (const uint32_t*)a->w_packed;
+  g.w_row_words = cdiv(a->k, 16);
+  g.w_scale = a->w_scale;
+  g.group = a->group_size;
+  g.M = a->m;
+  g.N = a->n_out;
+  g.K = a->k;
+  g.Kp = p.Kp;
+  g.bias = a->bias;
+  g.residual = a->residual;
+  g.ld_res = a->ld_res;
+  g.y = a->y;
+  g.ldy = a->ldy;
+  g.y_bf16 = a->y_dtype == SSM_BF16;
+  g.dbg_acc = a->dbg_acc;
+  if (!p.norm) {
+    g.A = a->x;
+    g.lda = a->ldx;
+    g.absmax = a->x_absmax;
+    return dev(launch_gemm_i8(g, s), "bitlinear gemm");
+  }
+  const int xb = a->x_dtype == SSM_BF16;
+  if (a->act_bits == 8) {
+    int8_t* q = (int8_t*)ws;
+    float* am = a->dbg_absmax ? a->dbg_absmax : (float*)((char*)ws + p.off_am);
+    ssm_status st = dev(launch_norm(a->x, xb, a->m, (int)a->k, a->ldx, a->norm_weight, a->norm_eps, 8, (int)p.Kp, q,
+                                    am, a->dbg_xq, nullptr, nullptr, s),
+                        "bitlinear norm");
+    if (st != SSM_OK) return st;
+    g.A = q;
+    g.lda = p.Kp;
+    g.absmax = am;
+    return dev(launch_gemm_i8(g, s), "bitlinear gemm");
+  }
+  bf16_t* xh = (bf16_t*)ws;
+  bf16_t* xh_lo = a->y_dtype == SSM_F32 ? xh + (size_t)a->m * p.Kp : nullptr;
+  ssm_status st = dev(launch_norm(a->x, xb, a->m, (int)a->k, a->ldx, a->norm_weight, a->norm_eps, 16, (int)p.Kp,
+                                  nullptr, nullptr, nullptr, xh, xh_lo, s),
+                      "bitlinear norm");
+  if (st != SSM_OK) return st;
+  g.A = xh;
+  g.A2 = xh_lo;
+  g.lda = p.Kp;
+  return dev(launch_gemm_bf16(g, s), "bitlinear gemm");
+}
+
+// ------------------------------------------------------------------ scan
+
+ssm_status scan_check(const ssm_scan_args* a) {
+  if (!a) return fail(SSM_ERR_NULL, "scan: args is NULL");
+  if (a->batch < 0 || a->seqlen < 0) return fail(SSM_ERR_SHAPE, "scan: negative batch / seqlen");
+  if (a->nheads < 1 || a->headdim < 1 || a->d_state < 1) return fail(SSM_ERR_SHAPE, "scan: nheads, headdim, d_state must be >= 1");
+  if (!act_dtype_ok(a->act_dtype)) return fail(SSM_ERR_DTYPE, "scan: act_dtype %d", a->act_dtype);
+  if (a->a_per_state == 1) {
+    if (a->headdim != 1) return fail(SSM_ERR_UNSUPPORTED, "scan: a_per_state = 1 needs headdim = 1");
+    const int64_t n = a->d_state;
+    if (n != 4 && n != 8 && n != 16 && n != 32 && n != 64) return fail(SSM_ERR_UNSUPPORTED, "scan: d_state %lld (Mamba-1 kind: 4, 8, 16, 32, 64)", (long long)n);
+  } else if (a->a_per_state == 0) {
+    const int64_t n = a->d_state;
+    if (n != 16 && n != 32 && n != 64 && n != 128) return fail(SSM_ERR_UNSUPPORTED, "scan: d_state %lld (SSD kind: 16, 32, 64, 128)", (long long)n);
+    if (a->headdim > 256) return fail(SSM_ERR_UNSUPPORTED, "scan: headdim %lld > 256", (long long)a->headdim);
+  } else {
+    return fail(SSM_ERR_SHAPE, "scan: a_per_state must be 0 or 1");
+  }
+  const int64_t HP = a->nheads * a->headdim;
+  if (a->ld_x < HP || a->ld_y < HP || a->ld_delta < a->nheads || a->ld_B < a->d_state || a->ld_C < a->d_state)
+    return fail(SSM_ERR_SHAPE, "scan: a row stride is smaller than its row");
+  if (a->batch * a->seqlen > 0 && (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->y))
+    return fail(SSM_ERR_NULL, "scan: x, delta, A, Bm, Cm and y are required");
+  return SSM_OK;
+}
+
+ScanArgs to_scan(const ssm_scan_args* a) {
+  ScanArgs s{};
+  s.batch = a->batch;
+  s.L = a->seqlen;
+  s.H = a->nheads;
+  s.P = a->headdim;
+  s.N = a->d_state;
+  s.act_bf16 = a->act_dtype == SSM_BF16;
+  s.x = a->x; s.ld_x = a->ld_x;
+  s.delta = a->delta; s.ld_delta = a->ld_delta;
+  s.delta_bias = a->delta_bias; s.softplus = a->delta_softplus;
+  s.A = a->A;
+  s.Bm = a->Bm; s.ld_B = a->ld_B;
+  s.Cm = a->Cm; s.ld_C = a->ld_C;
+  s.D = a->D; s.h0 = a->h0; s.h_last = a->h_last;
+  s.y = a->y; s.ld_y = a->ld_y;
+  return s;
+}
+
+// ------------------------------------------------------------------ mixer
+
+struct MixPlan {
+  int64_t M = 0, Kp = 0, PW = 0, VW = 0;
+  size_t off_am = 0, off_x = 0, off_p = 0, off_y = 0, off_scan = 0, total = 0;
+};
+
+ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, MixPlan* p) {
+  if (!c) return fail(SSM_ERR_NULL, "mixer: config is NULL");
+  if (batch < 0 || seqlen < 0) return fail(SSM_ERR_SHAPE, "mixer: negative batch / seqlen");
+  if (!act_dtype_ok(c->act_dtype)) return fail(SSM_ERR_DTYPE, "mixer: act_dtype %d", c->act_dtype);
+  if (c->d_model < 1 || c->d_model > kMaxK || c->d_inner < 1 || c->d_inner > kMaxK)
+    return fail(SSM_ERR_SHAPE, "mixer: d_model and d_inner must be in [1, %lld]", (long long)kMaxK);
+  if (c->act_bits != 8 && c->act_bits != 16) return fail(SSM_ERR_UNSUPPORTED, "mixer: act_bits must be 8 or 16");
+  if (c->group_size < 0 || (c->group_size > 0 && (c->group_size % 64 || c->d_model % c->group_size || c->d_inner % c->group_size)))
+    return fail(SSM_ERR_SHAPE, "mixer: group_size must be 0 or a multiple of 64 dividing d_model and d_inner");
+  p->M = batch * seqlen;
+  p->Kp = round_up(c->d_model > c->d_inner ? c->d_model : c->d_inner, 64);
+  const size_t as = act_size(c->act_dtype);
+  size_t off = 0;
+  const size_t qbytes = (size_t)p->M * p->Kp * (c->act_bits == 8 ? 1 : (c->act_dtype == SSM_F32 ? 4 : 2));
+  off = align_up(qbytes);
+  p->off_am = off;
+  off = align_up(off + (size_t)p->M * 4);
+  if (c->kind == SSM_MIXER_MAMBA1) {
+    if (c->act_bits != 8 || c->group_size != 0) return fail(SSM_ERR_UNSUPPORTED, "mixer: Mamba-1 kind needs act_bits 8 and group_size 0");
+    if (c->dt_rank < 1 || c->dt_rank > 64) return fail(SSM_ERR_UNSUPPORTED, "mixer: dt_rank must be in [1, 64]");
+    const int64_t n = c->d_state;
+    if (n != 4 && n != 8 && n != 16 && n != 32 && n != 64) return fail(SSM_ERR_UNSUPPORTED, "mixer: d_state %lld", (long long)n);
+    p->PW = c->dt_rank + 2 * c->d_state;
+    p->off_x = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
+    p->off_p = off; off = align_up(off + (size_t)p->M * p->PW * as);
+    p->off_y = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
+  } else if (c->kind == SSM_MIXER_SSD) {
+    if (c->nheads < 1 || c->headdim < 1 || c->nheads * c->headdim != c->d_inner)
+      return fail(SSM_ERR_SHAPE, "mixer: nheads * headdim must equal d_inner");
+    const int64_t n = c->d_state;
+    if (n != 16 && n != 32 && n != 64 && n != 128) return fail(SSM_ERR_UNSUPPORTED, "mixer: d_state %lld", (long long)n);
+    p->VW = c->d_inner + 2 * c->d_state + c->nheads;
+    p->off_p = off; off = align_up(off + (size_t)p->M * p->VW * as);
+    p->off_y = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
+    p->off_scan = off;
+  } else {
+    return fail(SSM_ERR_UNSUPPORTED, "mixer: kind %d", c->kind);
+  }
+  p->total = off;
+  return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(int s) {
+  switch (s) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "invalid size or stride";
+    case SSM_ERR_DTYPE: return "unsupported dtype";
+    case SSM_ERR_ALIGN: return "misaligned pointer or stride";
+    case SSM_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SSM_ERR_DEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ssm_last_error(void) { return g_err.c_str(); }
+
+int64_t ssm_packed_row_bytes(int64_t k) { return k <= 0 ? 0 : 4 * ((k + 15) / 16); }
+
+size_t ssm_ternary_quantize_workspace_bytes(int64_t n_out, int64_t k, int64_t group_size, const float* scale_in) {
+  if (scale_in || n_out < 1 || k < 1 || group_size < 0 || (group_size > 0 && k % group_size)) return 0;
+  return (size_t)n_out * (group_size ? k / group_size : 1) * sizeof(double);
+}
+
+ssm_status ssm_ternary_quantize_weights(const float* w, int64_t n, int64_t k, int64_t group, const float* scale_in,
+                                        uint8_t* packed, float* scale, int64_t* zero_count, void* ws, size_t wsb,
+                                        hipStream_t stream) {
+  g_err.clear();
+  if (!w || !packed || !scale) return fail(SSM_ERR_NULL, "quantize: w_latent, w_packed and w_scale are required");
+  if (n < 1 || k < 1) return fail(SSM_ERR_SHAPE, "quantize: n_out = %lld, k = %lld", (long long)n, (long long)k);
+  if (group < 0 || (group > 0 && k % group)) return fail(SSM_ERR_SHAPE, "quantize: group_size %lld does not divide k", (long long)group);
+  if (!aligned(packed, 4)) return fail(SSM_ERR_ALIGN, "quantize: w_packed must be 4-byte aligned");
+  const size_t need = ssm_ternary_quantize_workspace_bytes(n, k, group, scale_in);
+  if (need && (!ws || wsb < need)) return fail(SSM_ERR_WORKSPACE, "quantize: workspace needs %zu bytes", need);
+  if (need && !aligned(ws, 8)) return fail(SSM_ERR_ALIGN, "quantize: workspace must be 8-byte aligned");
+  ssm_status st;
+  if (!scale_in) {
+    st = dev(launch_abs_partials(w, n, k, group, (double*)ws, stream), "quantize partials");
+    if (st != SSM_OK) return st;
+  }
+  st = dev(launch_scales((const double*)ws, n, k, group, scale_in, scale, stream), "quantize scales");
+  if (st != SSM_OK) return st;
+  return dev(launch_pack(w, n, k, group, scale, (uint32_t*)packed, zero_count, stream), "quantize pack");
+}
+
+size_t ssm_bitlinear_workspace_bytes(const ssm_bitlinear_args* a) {
+  BLPlan p;
+  std::string keep = g_err;
+  const ssm_status st = bl_plan(a, &p);
+  g_err = keep;
+  return st == SSM_OK ? p.total : 0;
+}
+
+ssm_status ssm_bitlinear_fwd(const ssm_bitlinear_args* a, void* ws, size_t wsb, hipStream_t stream) {
+  g_err.clear();
+  BLPlan p;
+  ssm_status st = bl_plan(a, &p);
+  if (st != SSM_OK) return st;
+  if (p.total && (!ws || wsb < p.total)) return fail(SSM_ERR_WORKSPACE, "bitlinear: workspace needs %zu bytes", p.total);
+  if (p.total && !aligned(ws, 16)) return fail(SSM_ERR_ALIGN, "bitlinear: workspace must be 16-byte aligned");
+  return bl_run(a, p, ws, stream);
+}
+
+size_t ssm_selective_scan_workspace_bytes(const ssm_scan_args* a) {
+  std::string keep = g_err;
+  const ssm_status st = scan_check(a);
+  g_err = keep;
+  if (st != SSM_OK) return 0;
+  return a->a_per_state ? 0 : scan_ssd_workspace(to_scan(a));
+}
+
+ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* ws, size_t wsb, hipStream_t stream) {
+  g_err.clear();
+  ssm_status st = scan_check(a);
+  if (st != SSM_OK) return st;
+  const ScanArgs s = to_scan(a);
+  if (a->a_per_state) return dev(launch_scan_m1(s, stream), "scan");
+  const size_t need = scan_ssd_workspace(s);
+  if (need && (!ws || wsb < need)) return fail(SSM_ERR_WORKSPACE, "scan: workspace needs %zu bytes", need);
+  return dev(launch_scan_ssd(s, ws, wsb, stream), "scan");
+}
+
+size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64_t seqlen) {
+  std::string keep = g_err;
+  MixPlan p;
+  const ssm_status st = mix_plan(c, batch, seqlen, &p);
+  g_err = keep;
+  if (st != SSM_OK) return 0;
+  if (c->kind == SSM_MIXER_SSD) {
+    ScanArgs s{};
+    s.batch = batch; s.L = seqlen; s.H = c->nheads; s.P = c->headdim; s.N = c->d_state;
+    return p.total + align_up(scan_ssd_workspace(s));
+  }
+  return p.total;
+}
+
+ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
+                         int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb,
+                         hipStream_t stream) {
+  g_err.clear();
+  MixPlan p;
+  ssm_status st = mix_plan(c, batch, seqlen, &p);
+  if (st != SSM_OK) return st;
+  if (!w || !w->w_in || !w->w_out || !w->s_in || !w->s_out || !w->A)
+    return fail(SSM_ERR_NULL, "mixer: w_in, w_out, s_in, s_out and A are required");
+  if (c->kind == SSM_MIXER_MAMBA1 && (!w->w_x || !w->w_dt || !w->s_x || !w->s_dt))
+    return fail(SSM_ERR_NULL, "mixer: w_x, w_dt, s_x and s_dt are required for the Mamba-1 kind");
+  if (p.M > 0 && (!u || !out)) return fail(SSM_ERR_NULL, "mixer: u / out is NULL");
+  if (out == u && !add_residual) return fail(SSM_ERR_SHAPE, "mixer: out may alias u only with add_residual");
+  const size_t need = ssm_mixer_workspace_bytes(c, batch, seqlen);
+  if (!ws || wsb < need) return fail(SSM_ERR_WORKSPACE, "mixer: workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(SSM_ERR_ALIGN, "mixer: workspace must be 256-byte aligned");
+  if (p.M == 0) return SSM_OK;
+  char* base = (char*)ws;
+  float* am = (float*)(base + p.off_am);
+
+  auto bitlinear = [&](const void* x, int64_t k, int64_t ldx, const uint8_t* wp, const float* sc, const float* g,
+                       int64_t n, void* y, int64_t ldy, const void* res) -> ssm_status {
+    ssm_bitlinear_args a{};
+    a.x = x; a.x_dtype = c->act_dtype; a.act_bits = c->act_bits;
+    a.m = p.M; a.k = k; a.ldx = ldx;
+    a.norm_weight = g; a.norm_eps = c->norm_eps;
+    a.w_packed = wp; a.w_scale = sc; a.n_out = n; a.group_size = c->group_size;
+    a.residual = res; a.ld_res = c->d_model;
+    a.y = y; a.y_dtype = c->act_dtype; a.ldy = ldy;
+    BLPlan bp;
+    ssm_status s2 = bl_plan(&a, &bp);
+    if (s2 != SSM_OK) return s2;
+    if (c->act_bits == 8) {  // codes in the shared buffer, absmax in its own region
+      a.dbg_absmax = am;
+    }
+    return bl_run(&a, bp, base, stream);
+  };
+
+  const void* res = add_residual ? u : nullptr;
+  if (c->kind == SSM_MIXER_MAMBA1) {
+    void* x = base + p.off_x;
+    void* pp = base + p.off_p;
+    void* y = base + p.off_y;
+    st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, c->d_inner, x, c->d_inner, nullptr);
+    if (st != SSM_OK) return st;
+    st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
+    if (st != SSM_OK) return st;
+    ScanArgs s{};
+    const size_t as = act_size(c->act_dtype);
+    s.batch = batch; s.L = seqlen; s.H = c->d_inner; s.P = 1; s.N = c->d_state;
+    s.act_bf16 = c->act_dtype == SSM_BF16;
+    s.x = x; s.ld_x = c->d_inner;
+    s.delta = nullptr; s.ld_delta = 0;
+    s.delta_bias = w->dt_bias; s.softplus = 1;
+    s.A = w->A;
+    s.Bm = (const char*)pp + c->dt_rank * as; s.ld_B = p.PW;
+    s.Cm = (const char*)pp + (c->dt_rank + c->d_state) * as; s.ld_C = p.PW;
+    s.D = w->D;
+    s.y = y; s.ld_y = c->d_inner;
+    s.dr = pp; s.ld_dr = p.PW; s.R = (int)c->dt_rank;
+    s.w_dt = (const uint32_t*)w->w_dt; s.w_dt_row_words = cdiv(c->dt_rank, 16);
+    s.s_dt = w->s_dt; s.g_dt = w->g_dt; s.eps = c->norm_eps;
+    st = dev(launch_scan_m1(s, stream), "mixer scan");
+    if (st != SSM_OK) return st;
+    return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
+  }
+  // SSD kind
+  void* v = base + p.off_p;
+  void* y = base + p.off_y;
+  st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, p.VW, v, p.VW, nullptr);
+  if (st != SSM_OK) return st;
+  const size_t as = act_size(c->act_dtype);
+  ScanArgs s{};
+  s.batch = batch; s.L = seqlen; s.H = c->nheads; s.P = c->headdim; s.N = c->d_state;
+  s.act_bf16 = c->act_dtype == SSM_BF16;
+  s.x = v; s.ld_x = p.VW;
+  s.Bm = (const char*)v + c->d_inner * as; s.ld_B = p.VW;
+  s.Cm = (const char*)v + (c->d_inner + c->d_state) * as; s.ld_C = p.VW;
+  s.delta = (const char*)v + (c->d_inner + 2 * c->d_state) * as; s.ld_delta = p.VW;
+  s.delta_bias = w->dt_bias; s.softplus = 1;
+  s.A = w->A; s.D = w->D;
+  s.y = y; s.ld_y = c->d_inner;
+  st = dev(launch_scan_ssd(s, base + p.off_scan, wsb - p.off_scan, stream), "mixer scan");
+  if (st != SSM_OK) return st;
+  return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace ssm {
+
+// ---- ternarisation + packing (quant.hip)
+hipError_t launch_abs_partials(const float* w, int64_t n, int64_t k, int64_t group, double* part,
+                               hipStream_t s);
+hipError_t launch_scales(const double* part, int64_t n, int64_t k, int64_t group, const float* scale_in,
+                         float* scale, hipStream_t s);
+hipError_t launch_pack(const float* w, int64_t n, int64_t k, int64_t group, const float* scale,
+                       uint32_t* packed, int64_t* zero_count, hipStream_t s);
+
+// ---- RMSNorm + activation quantisation (norm.hip)
+// mode 8: int8 codes q [m, ldo] (zero past k) + absmax [m] (+ optional q2 [m, k]);
+// mode 16: bf16 normalised rows xh [m, ldo] (zero past k), and when xh_lo is given the
+// remainder xh_lo = bf16(x - xh) so that xh + xh_lo carries about 16 significant bits.
+hipError_t launch_norm(const void* x, int x_bf16, int64_t m, int k, int64_t ldx, const float* gain,
+                       float eps, int mode, int ldo, int8_t* q, float* absmax, int8_t* q2, bf16_t* xh,
+                       bf16_t* xh_lo, hipStream_t s);
+
+// ---- ternary contraction (bitlinear.hip)
+struct GemmArgs {
+  const void* A;          // int8 (A8) or bf16 (A16) rows [M, lda], zero-padded to Kp columns
+  const void* A2;         // A16 only, or null: second bf16 term of each activation (same layout)
+  int64_t lda;
+  const float* absmax;    // A8: [M]
+  const uint32_t* W;      // packed words [N, w_row_words]
+  int64_t w_row_words;
+  const float* w_scale;   // [1] or [N, K / group]
+  int64_t group;          // 0 or a multiple of 64
+  int64_t M, N, K, Kp;
+  const float* bias;      // [N] or null
+  const void* residual;   // [M, ld_res] of the output dtype or null
+  int64_t ld_res;
+  void* y;
+  int64_t ldy;
+  int y_bf16;
+  int32_t* dbg_acc;       // [M, N] or null (A8)
+};
+hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+
+// ---- selective scan (scan.hip: Mamba-1 kind; ssd.hip: SSD kind)
+struct ScanArgs {
+  int64_t batch, L, H, P, N;
+  int act_bf16;
+  const void* x; int64_t ld_x;
+  const void* delta; int64_t ld_delta;   // pre-activation dt [B, L, H] (unused when fused)
+  const float* delta_bias; int softplus;
+  const float* A;
+  const void* Bm; int64_t ld_B;
+  const void* Cm; int64_t ld_C;
+  const float* D;
+  const float* h0;
+  float* h_last;
+  void* y; int64_t ld_y;
+  // Mamba-1 only: dt computed in the scan from a low-rank input (a BitLinear of k = R)
+  const void* dr; int64_t ld_dr; int R;
+  const uint32_t* w_dt; int64_t w_dt_row_words;
+  const float* s_dt; const float* g_dt; float eps;
+};
+hipError_t launch_scan_m1(const ScanArgs& a, hipStream_t s);
+hipError_t launch_scan_ssd(const ScanArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+size_t scan_ssd_workspace(const ScanArgs& a);
+
+}  // namespace ssm

@@ -1,0 +1,176 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every function that
+include/ssm_ternary.h declares, and rejects invalid calls on the host with the documented
+status before anything is launched (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_selective_amd as tws
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm_ternary.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED, DEVICE = range(8)
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = tws.lib()
+    declared = _declared()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(tws.EXPORTS) == declared
+
+
+def test_version_and_status_strings():
+    L = tws.lib()
+    assert tws.ssm_abi_version() == 1
+    for s in range(8):
+        assert L.ssm_status_string(s)
+    assert tws.ssm_packed_row_bytes(8) == 4
+    assert tws.ssm_packed_row_bytes(16) == 4
+    assert tws.ssm_packed_row_bytes(17) == 8
+    assert tws.ssm_packed_row_bytes(4096) == 1024
+    assert tws.ssm_packed_row_bytes(0) == 0
+
+
+def _bl(**kw):
+    a = tws.BitlinearArgs()
+    a.x, a.x_dtype, a.act_bits = FAKE, tws.SSM_F32, 8
+    a.m, a.k, a.ldx = 16, 64, 64
+    a.norm_eps = 1e-5
+    a.w_packed, a.w_scale, a.n_out, a.group_size = FAKE, FAKE, 32, 0
+    a.y, a.y_dtype, a.ldy = FAKE, tws.SSM_F32, 32
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(act_bits=4), UNSUPPORTED),
+    (dict(x_dtype=7), DTYPE),
+    (dict(x_dtype=tws.SSM_I8, act_bits=16), DTYPE),
+    (dict(y_dtype=tws.SSM_I8), DTYPE),
+    (dict(k=0), SHAPE),
+    (dict(k=5000, ldx=5000), SHAPE),
+    (dict(m=-1), SHAPE),
+    (dict(n_out=0), SHAPE),
+    (dict(ldx=32), SHAPE),
+    (dict(ldy=8), SHAPE),
+    (dict(group_size=32), SHAPE),
+    (dict(group_size=128), SHAPE),
+    (dict(w_packed=None), NULL),
+    (dict(w_scale=None), NULL),
+    (dict(x=None), NULL),
+    (dict(y=None), NULL),
+    (dict(w_packed=FAKE + 2), ALIGN),
+    (dict(act_bits=16, dbg_acc=FAKE), UNSUPPORTED),
+    (dict(x_dtype=tws.SSM_I8), NULL),
+    (dict(x_dtype=tws.SSM_I8, x_absmax=FAKE, k=40, ldx=64), UNSUPPORTED),
+])
+def test_bitlinear_rejects(kw, status):
+    L = tws.lib()
+    a = _bl(**kw)
+    assert L.ssm_bitlinear_fwd(ctypes.byref(a), None, 0, None) == status
+    assert L.ssm_last_error().decode()
+
+
+def test_bitlinear_workspace_checks():
+    L = tws.lib()
+    a = _bl()
+    need = L.ssm_bitlinear_workspace_bytes(ctypes.byref(a))
+    assert need >= 16 * 64 + 16 * 4
+    assert L.ssm_bitlinear_fwd(ctypes.byref(a), None, 0, None) == WORKSPACE
+    assert L.ssm_bitlinear_fwd(ctypes.byref(a), FAKE, need - 1, None) == WORKSPACE
+    assert L.ssm_bitlinear_workspace_bytes(ctypes.byref(_bl(k=0))) == 0
+
+
+def _scan(**kw):
+    a = tws.ScanArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.d_state = 2, 64, 128, 1, 16
+    a.a_per_state, a.act_dtype = 1, tws.SSM_F32
+    a.x, a.ld_x, a.delta, a.ld_delta = FAKE, 128, FAKE, 128
+    a.A, a.Bm, a.ld_B, a.Cm, a.ld_C = FAKE, FAKE, 16, FAKE, 16
+    a.y, a.ld_y = FAKE, 128
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_state=12), UNSUPPORTED),
+    (dict(headdim=2, ld_x=256, ld_y=256), UNSUPPORTED),
+    (dict(a_per_state=0, d_state=8), UNSUPPORTED),
+    (dict(a_per_state=2), SHAPE),
+    (dict(act_dtype=tws.SSM_I8), DTYPE),
+    (dict(ld_x=100), SHAPE),
+    (dict(ld_B=8), SHAPE),
+    (dict(nheads=0), SHAPE),
+    (dict(batch=-1), SHAPE),
+    (dict(x=None), NULL),
+    (dict(A=None), NULL),
+    (dict(Cm=None), NULL),
+])
+def test_scan_rejects(kw, status):
+    L = tws.lib()
+    a = _scan(**kw)
+    assert L.ssm_selective_scan_fwd(ctypes.byref(a), None, 0, None) == status
+
+
+def test_scan_empty_is_noop():
+    """batch 0 or L 0: validated, nothing launched (no device needed)."""
+    L = tws.lib()
+    for kw in (dict(batch=0), dict(seqlen=0)):
+        a = _scan(x=None, delta=None, A=None, Bm=None, Cm=None, y=None, **kw)
+        assert L.ssm_selective_scan_fwd(ctypes.byref(a), None, 0, None) == OK
+
+
+def test_quantize_rejects():
+    L = tws.lib()
+    q = L.ssm_ternary_quantize_weights
+    assert q(None, 4, 16, 0, None, FAKE, FAKE, None, None, 0, None) == NULL
+    assert q(FAKE, 0, 16, 0, None, FAKE, FAKE, None, None, 0, None) == SHAPE
+    assert q(FAKE, 4, 100, 64, None, FAKE, FAKE, None, None, 0, None) == SHAPE
+    assert q(FAKE, 4, 16, 0, None, FAKE + 1, FAKE, None, None, 0, None) == ALIGN
+    assert q(FAKE, 4, 16, 0, None, FAKE, FAKE, None, None, 0, None) == WORKSPACE
+    assert L.ssm_ternary_quantize_workspace_bytes(4, 256, 128, None) == 4 * 2 * 8
+    assert L.ssm_ternary_quantize_workspace_bytes(4, 256, 0, None) == 4 * 8
+    assert L.ssm_ternary_quantize_workspace_bytes(4, 256, 0, FAKE) == 0
+
+
+def test_mixer_rejects():
+    L = tws.lib()
+    w = tws.MixerWeights()
+    for name, _ in tws.MixerWeights._fields_:
+        setattr(w, name, FAKE)
+    good = tws.mixer_config(0, 64, 128, 16, dt_rank=8)
+    assert L.ssm_mixer_workspace_bytes(ctypes.byref(good), 2, 64) > 0
+    cases = [
+        (tws.mixer_config(0, 64, 128, 16, dt_rank=8, act_bits=16), UNSUPPORTED),
+        (tws.mixer_config(0, 64, 128, 16, dt_rank=0), UNSUPPORTED),
+        (tws.mixer_config(0, 64, 128, 16, dt_rank=80), UNSUPPORTED),
+        (tws.mixer_config(0, 64, 128, 12, dt_rank=8), UNSUPPORTED),
+        (tws.mixer_config(1, 64, 128, 16, nheads=3, headdim=64), SHAPE),
+        (tws.mixer_config(1, 64, 128, 16, nheads=2, headdim=64, group_size=100), SHAPE),
+        (tws.mixer_config(0, 8192, 128, 16, dt_rank=8), SHAPE),
+        (tws.mixer_config(5, 64, 128, 16), UNSUPPORTED),
+    ]
+    for cfg, status in cases:
+        assert L.ssm_mixer_fwd(ctypes.byref(cfg), ctypes.byref(w), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 1 << 30,
+                               None) == status
+    # missing weights, in-place without residual, too-small workspace
+    w2 = tws.MixerWeights()
+    assert L.ssm_mixer_fwd(ctypes.byref(good), ctypes.byref(w2), FAKE, FAKE, 2, 64, 1, FAKE, 1 << 30, None) == NULL
+    assert L.ssm_mixer_fwd(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE, 2, 64, 0, FAKE, 1 << 30, None) == SHAPE
+    assert L.ssm_mixer_fwd(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 16, None) == WORKSPACE
+    assert L.ssm_mixer_fwd(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, 64, 1, FAKE + 8, 1 << 30,
+                           None) == ALIGN

@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element, through the C ABI.
+
+Integer stages (packed weights, scales, int8 activations, absmax, int32 accumulators) are
+bit-exact and checked stage-wise: the GPU stage is fed the oracle's exact stage input.
+Float outputs: norm-wise relative error <= 1e-4 (fp32) or <= 2e-2 (bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ternary_weight_selective_amd as tws
+import workloads as wl
+from gpu_helpers import (DEV, TOL, bf16_values, gpu_config, host, oracle_config, quantize_layer, rel_err,
+                         run_gpu_stack, to_dev, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ S0: ternarise + pack
+
+PROJ_SHAPES = sorted({(n, k, c.group_size) for c in wl.CONFIGS.values() for (n, k) in c.proj_shapes.values()})
+
+
+@pytest.mark.parametrize("n,k,group", PROJ_SHAPES)
+def test_pack_bit_exact_config_shapes(n, k, group):
+    """Every projection shape of the five workloads: packed bytes, scales, zero count bit-exact."""
+    w = wl.normal(wl.rng(n * 7 + k), (n, k), 0.0, 0.02)
+    packed, scale, zc = tws.ssm_ternary_quantize_weights(to_dev(w), group)
+    codes, oscale, zeros = oracle.quantize_weights(w, group)
+    np.testing.assert_array_equal(host(packed), oracle.pack(codes))
+    np.testing.assert_array_equal(host(scale).ravel(), np.asarray(oscale).ravel())
+    assert int(host(zc)[0]) == zeros
+
+
+@pytest.mark.parametrize("n,k,group", [(1, 1, 0), (3, 7, 0), (5, 40, 0), (33, 200, 0), (17, 384, 128), (2, 4096, 64)])
+def test_pack_ragged_and_edges(n, k, group):
+    """Ragged rows (k not a multiple of 16), single weights, grouped scales, exact ties."""
+    g = wl.rng(k)
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    w[0, : min(k, 4)] = np.array([1.0, -0.5, 0.25, 0.25], np.float32)[: min(k, 4)]
+    packed, scale, zc = tws.ssm_ternary_quantize_weights(to_dev(w), group)
+    codes, oscale, zeros = oracle.quantize_weights(w, group)
+    np.testing.assert_array_equal(host(packed), oracle.pack(codes))
+    np.testing.assert_array_equal(host(scale).ravel(), np.asarray(oscale).ravel())
+    assert int(host(zc)[0]) == zeros
+
+
+def test_pack_zero_tensor_and_caller_scale():
+    w = np.zeros((8, 64), np.float32)
+    packed, scale, zc = tws.ssm_ternary_quantize_weights(to_dev(w))
+    assert not host(packed).any() and host(scale)[0] == 0.0 and int(host(zc)[0]) == 8 * 64
+    w = wl.normal(wl.rng(5), (16, 128), 0.0, 0.02)
+    s_in = np.array([0.013], np.float32)
+    packed, scale, _ = tws.ssm_ternary_quantize_weights(to_dev(w), 0, scale_in=to_dev(s_in))
+    codes, _, _ = oracle.quantize_weights(w, 0, scale_in=s_in)
+    np.testing.assert_array_equal(host(packed), oracle.pack(codes))
+    assert host(scale)[0] == s_in[0]
+
+
+# ------------------------------------------------------------------ S1-S4: BitLinear
+
+BL_CASES = [  # (m, k, n, group, act_bits, x dtype, y dtype)
+    (128, 64, 128, 0, 8, "f32", "f32"),      # bitssm_tiny in_proj
+    (130, 128, 40, 0, 8, "f32", "f32"),      # x_proj, ragged m
+    (67, 8, 128, 0, 8, "f32", "f32"),        # dt_proj, k = 8
+    (1000, 256, 512, 0, 8, "f32", "f32"),    # trissm in_proj rows
+    (515, 512, 48, 0, 8, "f32", "f32"),      # trissm x_proj
+    (333, 16, 512, 0, 8, "f32", "f32"),      # trissm dt_proj
+    (260, 1024, 512, 0, 8, "bf16", "bf16"),  # ternaryssm50m out_proj
+    (129, 32, 1024, 0, 8, "bf16", "bf16"),   # ternaryssm50m dt_proj
+    (200, 512, 256, 128, 8, "f32", "f32"),   # grouped A8
+    (97, 2048, 300, 128, 16, "bf16", "bf16"),  # mamba2_ssd in_proj rows, N ragged
+    (64, 4096, 256, 128, 16, "bf16", "bf16"),  # mamba2_ssd out_proj rows
+    (50, 256, 64, 0, 16, "f32", "f32"),      # A16 per tensor
+    (1, 100, 70, 0, 8, "f32", "f32"),        # one row, ragged k
+]
+
+
+@pytest.mark.parametrize("m,k,n,group,bits,xd,yd", BL_CASES)
+def test_bitlinear_parity(m, k, n, group, bits, xd, yd):
+    g = wl.rng(m + 3 * k + 7 * n)
+    x = wl.normal(g, (m, k))
+    if xd == "bf16":
+        x = bf16_values(x)
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    bias = wl.normal(g, (n,), 0.0, 0.1)
+    packed, scale, _ = tws.ssm_ternary_quantize_weights(to_dev(w), group)
+    codes, oscale, _ = oracle.quantize_weights(w, group)
+    xdt = torch.bfloat16 if xd == "bf16" else torch.float32
+    ydt = torch.bfloat16 if yd == "bf16" else torch.float32
+    xt = to_dev(x, xdt)
+    ref, oxq, oam, oacc = oracle.bitlinear(x, codes, oscale, group, bits, bias=bias)
+    if bits == 8:
+        y, xq, am, acc = tws.ssm_bitlinear_fwd(xt, packed, scale, n, act_bits=bits, group_size=group,
+                                               bias=to_dev(bias), y_dtype=ydt, debug=True)
+        np.testing.assert_array_equal(host(xq), oxq)          # S2 int8 codes
+        np.testing.assert_array_equal(host(am), oam)          # S2 absmax
+        np.testing.assert_array_equal(host(acc), oacc)        # S3 int32 accumulators
+        # S4: the fp64 dequantisation rounded once gives the oracle's stored value exactly
+        stored = ref.astype(np.float32)
+        np.testing.assert_array_equal(host(y), bf16_values(stored) if yd == "bf16" else stored)
+    else:
+        y = tws.ssm_bitlinear_fwd(xt, packed, scale, n, act_bits=bits, group_size=group, bias=to_dev(bias),
+                                  y_dtype=ydt)
+    assert rel_err(host(y), ref) <= TOL[yd]
+
+
+@pytest.mark.parametrize("m,k,n", [(256, 256, 512), (77, 1024, 64), (64, 2048, 4416)])
+def test_bitlinear_int32_from_oracle_codes(m, k, n):
+    """Stage-wise S3: the GPU contraction fed the oracle's exact int8 codes and absmax."""
+    g = wl.rng(k + n)
+    x = wl.normal(g, (m, k))
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    codes, oscale, _ = oracle.quantize_weights(w, 0)
+    ref, oxq, oam, oacc = oracle.bitlinear(x, codes, oscale)
+    packed = to_dev(oracle.pack(codes), torch.uint8)
+    y, _, _, acc = tws.ssm_bitlinear_fwd(to_dev(oxq, torch.int8), packed, to_dev(oscale), n,
+                                         x_absmax=to_dev(oam), debug=True)
+    np.testing.assert_array_equal(host(acc), oacc)
+    assert rel_err(host(y), ref) <= 1e-5
+
+
+def test_bitlinear_edge_rows():
+    """All-zero token rows give bias only; a one-hot row quantises to a single 127; m = 0 is a no-op."""
+    k, n = 256, 64
+    x = wl.normal(wl.rng(1), (5, k))
+    x[1] = 0.0
+    x[3] = 0.0
+    x[3, 17] = -3.5
+    w = wl.normal(wl.rng(2), (n, k), 0.0, 0.02)
+    bias = wl.normal(wl.rng(3), (n,))
+    packed, scale, _ = tws.ssm_ternary_quantize_weights(to_dev(w))
+    codes, oscale, _ = oracle.quantize_weights(w, 0)
+    y, xq, am, acc = tws.ssm_bitlinear_fwd(to_dev(x), packed, scale, n, bias=to_dev(bias), debug=True)
+    ref, oxq, oam, oacc = oracle.bitlinear(x, codes, oscale, bias=bias)
+    np.testing.assert_array_equal(host(xq), oxq)
+    np.testing.assert_array_equal(host(acc), oacc)
+    yh = host(y)
+    np.testing.assert_array_equal(yh[1], bias)
+    assert host(xq)[3, 17] == -127
+    assert rel_err(yh, ref) <= 1e-4
+    empty = tws.ssm_bitlinear_fwd(torch.empty((0, k), device=DEV), packed, scale, n)
+    assert empty.shape == (0, n)
+
+
+def test_bitlinear_residual_and_strided_input():
+    """A row stride wider than k (the dt input inside the x_proj output) and a residual add."""
+    g = wl.rng(9)
+    wide = wl.normal(g, (300, 48))
+    w = wl.normal(g, (512, 16), 0.0, 0.02)
+    res = wl.normal(g, (300, 512))
+    packed, scale, _ = tws.ssm_ternary_quantize_weights(to_dev(w))
+    codes, oscale, _ = oracle.quantize_weights(w, 0)
+    xt = to_dev(wide)
+    y = tws.ssm_bitlinear_fwd(xt[:, :16], packed, scale, 512, k=16, residual=to_dev(res))
+    ref, *_ = oracle.bitlinear(wide, codes, oscale, k=16)
+    assert rel_err(host(y), ref + res) <= 1e-6
+
+
+# ------------------------------------------------------------------ S5-S8: selective scan
+
+def _scan_gpu(p, dtype=torch.float32, h0=None, last=False):
+    return tws.ssm_selective_scan_fwd(to_dev(p["x"], dtype), to_dev(p["delta"], dtype), to_dev(p["A"]),
+                                      to_dev(p["Bm"], dtype), to_dev(p["Cm"], dtype), to_dev(p["D"]),
+                                      to_dev(p["dt_bias"]), True, None if h0 is None else to_dev(h0),
+                                      return_last_state=last)
+
+
+def _bf16_problem(p):
+    return {k: (bf16_values(v) if k in ("x", "delta", "Bm", "Cm") else v) for k, v in p.items()}
+
+
+SCAN_CASES = [  # (batch, L, H, P, N, a_per_state, dtype)
+    (2, 64, 128, 1, 16, True, "f32"),
+    (3, 1, 512, 1, 16, True, "f32"),
+    (2, 33, 100, 1, 16, True, "f32"),      # ragged channels and time tile
+    (1, 300, 64, 1, 4, True, "f32"),
+    (1, 97, 64, 1, 8, True, "f32"),
+    (1, 70, 32, 1, 32, True, "f32"),
+    (1, 70, 16, 1, 64, True, "f32"),
+    (2, 100, 256, 1, 16, True, "bf16"),
+    (2, 50, 4, 64, 128, False, "f32"),     # SSD kind
+    (1, 77, 3, 16, 16, False, "f32"),
+    (1, 40, 2, 32, 64, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("batch,L,H,P,N,aps,dt", SCAN_CASES)
+def test_scan_parity(batch, L, H, P, N, aps, dt):
+    p = wl.scan_problem(batch, L, H, P, N, aps, seed=L + H)
+    if dt == "bf16":
+        p = _bf16_problem(p)
+    h0 = wl.normal(wl.rng(4), (batch, H, P, N), 0.0, 0.5)
+    ref, href = oracle.selective_scan(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["D"], p["dt_bias"], h0=h0)
+    y, hl = _scan_gpu(p, torch.bfloat16 if dt == "bf16" else torch.float32, h0=h0, last=True)
+    assert rel_err(host(y), ref) <= TOL[dt]
+    assert rel_err(host(hl), href) <= 1e-5
+
+
+def test_scan_long_sequence_sampled():
+    """long_scan workload (batch 8, L 8192, 512 channels, d_state 16), full size on the GPU;
+    the oracle checks 24 channels of every sequence (channels are independent)."""
+    cfg = wl.CONFIGS["long_scan"]
+    p = wl.scan_problem(cfg.batch, cfg.seqlen, cfg.d_inner, 1, cfg.d_state, True, seed=42)
+    y, hl = _scan_gpu(p, last=True)
+    yh, hh = host(y), host(hl)
+    ch = np.array([0, 1, 63, 64, 100, 127, 128, 200, 255, 256, 300, 311, 383, 384, 400, 447, 448, 480, 500, 505,
+                   509, 510, 511, 17])
+    sub = dict(p, x=p["x"][:, :, ch], delta=p["delta"][:, :, ch], A=p["A"][ch], D=p["D"][ch],
+               dt_bias=p["dt_bias"][ch])
+    ref, href = oracle.selective_scan(sub["x"], sub["delta"], sub["A"], sub["Bm"], sub["Cm"], sub["D"],
+                                      sub["dt_bias"])
+    assert rel_err(yh[:, :, ch], ref) <= 1e-4
+    assert rel_err(hh[:, ch], href) <= 1e-4
+
+
+def test_scan_causality_determinism_streaming():
+    """Perturbing token t leaves y before t bitwise unchanged; two runs are bitwise equal;
+    a scan of L equals a scan of L1 then L - L1 from the carried state."""
+    p = wl.scan_problem(2, 200, 256, 1, 16, True, seed=7)
+    y1 = host(_scan_gpu(p))
+    y2 = host(_scan_gpu(p))
+    np.testing.assert_array_equal(y1, y2)
+    q = {k: v.copy() for k, v in p.items()}
+    q["x"][:, 120] += 1.0
+    q["delta"][:, 120] -= 0.5
+    y3 = host(_scan_gpu(q))
+    np.testing.assert_array_equal(y3[:, :120], y1[:, :120])
+    assert not np.array_equal(y3[:, 120], y1[:, 120])
+    a = {k: (v[:, :77] if v.ndim == 3 else v) for k, v in p.items()}
+    b = {k: (v[:, 77:] if v.ndim == 3 else v) for k, v in p.items()}
+    ya, ha = _scan_gpu(a, last=True)
+    yb = _scan_gpu(b, h0=host(ha))
+    np.testing.assert_allclose(np.concatenate([host(ya), host(yb)], 1), y1, rtol=1e-5, atol=1e-5)
+
+
+def test_scan_special_cases():
+    """B = 0 gives y = D x exactly; empty batch / sequence is a no-op."""
+    p = wl.scan_problem(1, 50, 64, 1, 16, True, seed=8)
+    p["Bm"] = np.zeros_like(p["Bm"])
+    y = host(_scan_gpu(p))
+    np.testing.assert_allclose(y, p["x"] * p["D"][None, None, :], rtol=1e-6, atol=0)
+    e = dict(p, x=p["x"][:, :0], delta=p["delta"][:, :0], Bm=p["Bm"][:, :0], Cm=p["Cm"][:, :0])
+    assert _scan_gpu(e).shape == (1, 0, 64)
+
+
+# ------------------------------------------------------------------ S9: mixer
+
+@pytest.mark.parametrize("seed", [42, 43, 44])
+def test_mixer_bitssm_tiny(seed):
+    """bitssm_tiny workload in full (one layer, fp32): GPU mixer vs oracle mixer."""
+    cfg = wl.CONFIGS["bitssm_tiny"]
+    lat, u = wl.mixer_problem(cfg, seed=seed)
+    gw, ow = quantize_layer(cfg, lat[0])
+    out = run_gpu_stack(cfg, [gw], u)
+    ref = oracle.mixer(oracle_config(cfg), ow, u)
+    assert rel_err(host(out), ref) <= TOL["f32"]
+
+
+def test_mixer_causality_and_determinism():
+    cfg = wl.CONFIGS["bitssm_tiny"]
+    lat, u = wl.mixer_problem(cfg, seed=42)
+    gw, _ = quantize_layer(cfg, lat[0])
+    o1 = host(run_gpu_stack(cfg, [gw], u))
+    o2 = host(run_gpu_stack(cfg, [gw], u))
+    np.testing.assert_array_equal(o1, o2)
+    u2 = u.copy()
+    u2[:, 40] = -u2[:, 40] + 0.3
+    o3 = host(run_gpu_stack(cfg, [gw], u2))
+    np.testing.assert_array_equal(o3[:, :40], o1[:, :40])
+    assert not np.array_equal(o3[:, 40], o1[:, 40])
+
+
+def _stack_sampled(name, seqs, seed=42):
+    """Full-size stack on the GPU (the launch configuration the benchmark times).  Each layer is
+    checked against the oracle given the same layer input (the GPU's stored input of the
+    sampled sequences; sequences are independent): that is the parity bar per mixer output.
+    The free-running drift (oracle stack from u, no re-synchronisation) is returned too: a
+    one-ulp difference anywhere can flip an int8 code at a .5 boundary, and flips compound
+    through a quantised stack, so the drift is reported, not held to the per-mixer bar."""
+    cfg = wl.CONFIGS[name]
+    lat, u = wl.mixer_problem(cfg, seed=seed)
+    if cfg.act_dtype == "bf16":
+        u = bf16_values(u)
+    pairs = [quantize_layer(cfg, l) for l in lat]
+    c = gpu_config(cfg)
+    h = to_dev(u, torch_dtype(cfg))
+    ws = torch.empty(tws.ssm_mixer_workspace_bytes(c, cfg.batch, cfg.seqlen), dtype=torch.uint8, device=DEV)
+    per_layer = []
+    for gw, ow in pairs:
+        h_in = host(h)[seqs]
+        h = tws.ssm_mixer_fwd(c, tws.mixer_weights(gw), h, add_residual=True, out=h, workspace=ws)
+        ref = oracle.mixer(oracle_config(cfg), ow, h_in)
+        per_layer.append(rel_err(host(h)[seqs], ref))
+    free = oracle.mixer_stack(oracle_config(cfg), [o for _, o in pairs], u[seqs])
+    drift = rel_err(host(h)[seqs], free)
+    print(f"{name}: per-layer rel err {['%.2e' % e for e in per_layer]}, free-running drift {drift:.2e}")
+    return per_layer, drift
+
+
+def test_mixer_trissm_stack_sampled():
+    per_layer, drift = _stack_sampled("trissm", [0, 37, 63])
+    assert max(per_layer) <= TOL["f32"], per_layer
+    assert drift <= 0.05, drift
+
+
+def test_mixer_long_scan_sampled():
+    per_layer, drift = _stack_sampled("long_scan", [5])
+    assert max(per_layer) <= TOL["f32"], per_layer
+
+
+def test_mixer_ternaryssm50m_stack_sampled():
+    per_layer, drift = _stack_sampled("ternaryssm50m", [0, 15])
+    assert max(per_layer) <= TOL["bf16"], per_layer
+    assert drift <= 0.1, drift
+
+
+def test_mixer_mamba2_ssd_sampled():
+    per_layer, drift = _stack_sampled("mamba2_ssd", [2])
+    assert max(per_layer) <= TOL["bf16"], per_layer
+
+
+def test_mixer_ssd_small_fp32():
+    """SSD kind at a small fp32 shape (several heads, ragged time tile)."""
+    cfg = wl.CONFIGS["mamba2_ssd"].with_(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2,
+                                          seqlen=45, act_dtype="f32")
+    lat, u = wl.mixer_problem(cfg, seed=11)
+    gw, ow = quantize_layer(cfg, lat[0])
+    out = run_gpu_stack(cfg, [gw], u)
+    ref = oracle.mixer(oracle_config(cfg), ow, u)
+    assert rel_err(host(out), ref) <= TOL["f32"]
