@@ -1,0 +1,440 @@
+#!/usr/bin/env python3
+"""Throughput of the ternary selective-SSM mixer forward on one MI355X.
+
+A step is one forward pass of the whole hot path over one batch: for the default
+workload, the TriSSM-shaped stack of 12 BitSSM mixer layers (d_model 256, d_inner 512,
+d_state 16, dt_rank 16, batch 64 x L 256, fp32 activations, int8 activations into the
+ternary projections), out = u + mixer(u) per layer.  Inputs are seeded synthetic data,
+resident in HBM before the timed region.  Prints one JSON line.
+
+Also measured, in a second timed loop that runs the same kernels through the stage entry
+points with HIP events around each stage: the average duration of every kernel stage, and
+the roofline of the dominant one.  The CPU oracle is timed on a bounded sample of the same
+workload on the host cores (a reported baseline, not the target).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import ternary_weight_selective_amd as tws  # noqa: E402
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (FMA = 2 FLOP per lane)
+INT8_MFMA_PEAK_TOPS = 5000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+# One VALU lane-instruction slot counts as 2 FLOP-equivalents (an FMA); a transcendental
+# (v_exp_f32) occupies 4 slots (quarter rate).  The Mamba-1 recurrence needs, per
+# (token, channel, state): dt*A, exp2, (dt*x)*B, fma for h, fma for y = 4 slots + 4 slots.
+SCAN_M1_SLOTS_PER_STATE_STEP = 8
+
+KERNEL_SOURCES = {  # source files whose text defines each timed kernel (for stale-counter checks)
+    "scan_m1": ["scan.hip", "common.hpp", "launch.hpp"],
+    "ssd": ["ssd.hip", "common.hpp", "launch.hpp"],
+    "bitlinear": ["norm.hip", "bitlinear.hip", "common.hpp", "launch.hpp"],
+}
+
+
+def kernel_src_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "ternary_weight_selective_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="trissm", choices=list(wl.CONFIGS))
+    ap.add_argument("--seed", type=int, default=42)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--stages-only", action="store_true", help="skip the headline loop (profiling runs)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ set-up
+
+class Problem:
+    """Device-resident weights, input and buffers of one workload."""
+
+    def __init__(self, cfg: wl.MixerConfig, seed: int, dev):
+        self.cfg = cfg
+        self.dev = dev
+        lat, u = wl.mixer_problem(cfg, seed=seed)
+        self.u_host = u
+        self.act = torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32
+        self.layers = []  # dicts of device tensors
+        for lw in lat:
+            d = {}
+            for name in cfg.proj_shapes:
+                packed, scale, _ = tws.ssm_ternary_quantize_weights(
+                    torch.from_numpy(lw["W_" + name]).to(dev), cfg.group_size)
+                d["w_" + name], d["s_" + name] = packed, scale
+            for key in ("A", "D", "dt_bias"):
+                d[key] = torch.from_numpy(lw[key]).to(dev)
+            self.layers.append(d)
+        self.c = tws.mixer_config(cfg.kind, cfg.d_model, cfg.d_inner, cfg.d_state, dt_rank=cfg.dt_rank,
+                                  nheads=cfg.nheads, headdim=cfg.headdim, act_bits=cfg.act_bits,
+                                  group_size=cfg.group_size, act_dtype=self.act, norm_eps=cfg.norm_eps)
+        self.mws = [tws.mixer_weights(d) for d in self.layers]
+        self.u = torch.from_numpy(u).to(dev).to(self.act)
+        self.bufs = [torch.empty_like(self.u), torch.empty_like(self.u)]
+        self.ws_bytes = tws.ssm_mixer_workspace_bytes(self.c, cfg.batch, cfg.seqlen)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, stream_handle):
+        """One pass of the stack: out = u + mixer_l(u) layer after layer (ping-pong buffers)."""
+        L = tws.lib()
+        h = self.u
+        cb = ctypes.byref(self.c)
+        for i, mw in enumerate(self.mws):
+            out = self.bufs[i % 2]
+            st = L.ssm_mixer_fwd(cb, ctypes.byref(mw), h.data_ptr(), out.data_ptr(), self.cfg.batch,
+                                 self.cfg.seqlen, 1, self.ws.data_ptr(), self.ws_bytes, stream_handle)
+            if st != 0:
+                raise tws.SsmError(st, L.ssm_last_error().decode())
+            h = out
+        return h
+
+
+class StagePlan:
+    """The same layer as ssm_mixer_fwd, issued stage by stage through the public entry points
+    (identical kernels and arguments), so that HIP events can bracket each stage."""
+
+    def __init__(self, prob: Problem):
+        cfg = prob.cfg
+        dev = prob.dev
+        M = cfg.tokens
+        es = 2 if prob.act == torch.bfloat16 else 4
+        dt = tws._DTYPES[prob.act]
+        self.prob = prob
+        self.stages = []  # per layer: list of (name, fn, args ctypes object)
+        if cfg.kind == wl.MAMBA1:
+            PW = cfg.dt_rank + 2 * cfg.d_state
+            self.x = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev)
+            self.p = torch.empty((M, PW), dtype=prob.act, device=dev)
+            self.y = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev)
+        else:
+            VW = cfg.d_inner + 2 * cfg.d_state + cfg.nheads
+            self.v = torch.empty((M, VW), dtype=prob.act, device=dev)
+            self.y = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev)
+        self.bl_ws = torch.empty(prob.ws_bytes, dtype=torch.uint8, device=dev)
+        L = tws.lib()
+
+        def bl(x_ptr, k, ldx, w, s, n, y_ptr, ldy, res_ptr):
+            a = tws.BitlinearArgs()
+            a.x, a.x_dtype, a.act_bits, a.m, a.k, a.ldx = x_ptr, dt, cfg.act_bits, M, k, ldx
+            a.norm_eps = cfg.norm_eps
+            a.w_packed, a.w_scale, a.n_out, a.group_size = w.data_ptr(), s.data_ptr(), n, cfg.group_size
+            a.residual, a.ld_res = res_ptr, cfg.d_model
+            a.y, a.y_dtype, a.ldy = y_ptr, dt, ldy
+            assert L.ssm_bitlinear_workspace_bytes(ctypes.byref(a)) <= prob.ws_bytes
+            return a
+
+        for li, d in enumerate(prob.layers):
+            src = prob.u if li == 0 else prob.bufs[(li - 1) % 2]
+            dst = prob.bufs[li % 2]
+            st = []
+            if cfg.kind == wl.MAMBA1:
+                R, N = cfg.dt_rank, cfg.d_state
+                st.append(("bitlinear_in", bl(src.data_ptr(), cfg.d_model, cfg.d_model, d["w_in"], d["s_in"],
+                                              cfg.d_inner, self.x.data_ptr(), cfg.d_inner, None)))
+                st.append(("bitlinear_x", bl(self.x.data_ptr(), cfg.d_inner, cfg.d_inner, d["w_x"], d["s_x"], PW,
+                                             self.p.data_ptr(), PW, None)))
+                a = tws.ScanArgs()
+                a.batch, a.seqlen, a.nheads, a.headdim, a.d_state = cfg.batch, cfg.seqlen, cfg.d_inner, 1, N
+                a.a_per_state, a.act_dtype = 1, dt
+                a.x, a.ld_x = self.x.data_ptr(), cfg.d_inner
+                a.delta_bias, a.delta_softplus = d["dt_bias"].data_ptr(), 1
+                a.A = d["A"].data_ptr()
+                a.Bm, a.ld_B = self.p.data_ptr() + R * es, PW
+                a.Cm, a.ld_C = self.p.data_ptr() + (R + N) * es, PW
+                a.D = d["D"].data_ptr()
+                a.y, a.ld_y = self.y.data_ptr(), cfg.d_inner
+                a.dt_in, a.ld_dt_in, a.dt_rank = self.p.data_ptr(), PW, R
+                a.w_dt, a.s_dt, a.dt_eps = d["w_dt"].data_ptr(), d["s_dt"].data_ptr(), cfg.norm_eps
+                st.append(("scan", a))
+                st.append(("bitlinear_out", bl(self.y.data_ptr(), cfg.d_inner, cfg.d_inner, d["w_out"], d["s_out"],
+                                               cfg.d_model, dst.data_ptr(), cfg.d_model, src.data_ptr())))
+            else:
+                H, P, N = cfg.nheads, cfg.headdim, cfg.d_state
+                VW = cfg.d_inner + 2 * N + H
+                st.append(("bitlinear_in", bl(src.data_ptr(), cfg.d_model, cfg.d_model, d["w_in"], d["s_in"], VW,
+                                              self.v.data_ptr(), VW, None)))
+                a = tws.ScanArgs()
+                a.batch, a.seqlen, a.nheads, a.headdim, a.d_state = cfg.batch, cfg.seqlen, H, P, N
+                a.a_per_state, a.act_dtype = 0, dt
+                base = self.v.data_ptr()
+                a.x, a.ld_x = base, VW
+                a.Bm, a.ld_B = base + cfg.d_inner * es, VW
+                a.Cm, a.ld_C = base + (cfg.d_inner + N) * es, VW
+                a.delta, a.ld_delta = base + (cfg.d_inner + 2 * N) * es, VW
+                a.delta_bias, a.delta_softplus = d["dt_bias"].data_ptr(), 1
+                a.A, a.D = d["A"].data_ptr(), d["D"].data_ptr()
+                a.y, a.ld_y = self.y.data_ptr(), cfg.d_inner
+                st.append(("scan", a))
+                st.append(("bitlinear_out", bl(self.y.data_ptr(), cfg.d_inner, cfg.d_inner, d["w_out"], d["s_out"],
+                                               cfg.d_model, dst.data_ptr(), cfg.d_model, src.data_ptr())))
+            self.stages.append(st)
+        self.scan_ws_bytes = max(1, L.ssm_selective_scan_workspace_bytes(ctypes.byref(self.stages[0][-2][1])))
+        self.scan_ws = torch.empty(self.scan_ws_bytes, dtype=torch.uint8, device=dev)
+
+    def run(self, stream_handle, events=None):
+        L = tws.lib()
+        for st in self.stages:
+            for name, a in st:
+                if events is not None:
+                    events[name][0].append(torch.cuda.Event(enable_timing=True))
+                    events[name][0][-1].record()
+                if name == "scan":
+                    rc = L.ssm_selective_scan_fwd(ctypes.byref(a), self.scan_ws.data_ptr(), self.scan_ws_bytes,
+                                                  stream_handle)
+                else:
+                    rc = L.ssm_bitlinear_fwd(ctypes.byref(a), self.bl_ws.data_ptr(), self.prob.ws_bytes,
+                                             stream_handle)
+                if rc != 0:
+                    raise tws.SsmError(rc, L.ssm_last_error().decode())
+                if events is not None:
+                    events[name][1].append(torch.cuda.Event(enable_timing=True))
+                    events[name][1][-1].record()
+
+
+# ------------------------------------------------------------------ algorithmic cost per launch
+
+def stage_cost(cfg: wl.MixerConfig, name: str) -> dict:
+    """Algorithmic HBM bytes and work of one launch of a stage over the whole batch."""
+    M = cfg.tokens
+    es = 2 if cfg.act_dtype == "bf16" else 4
+    shapes = cfg.proj_shapes
+    if name.startswith("bitlinear"):
+        n, k = shapes[name.split("_")[1]]
+        wbytes = n * 4 * ((k + 15) // 16)
+        byts = M * (k + n) * es + wbytes + (M * n * es if name == "bitlinear_out" else 0)
+        return {"bytes": byts, "ops": 2 * M * n * k, "ops_unit": "int8-OP" if cfg.act_bits == 8 else "bf16-FLOP"}
+    if cfg.kind == wl.MAMBA1:
+        PW = cfg.dt_rank + 2 * cfg.d_state
+        byts = M * (cfg.d_inner + PW + cfg.d_inner) * es
+        slots = M * cfg.d_inner * cfg.d_state * SCAN_M1_SLOTS_PER_STATE_STEP
+        return {"bytes": byts, "ops": 2 * slots, "ops_unit": "fp32-FLOP-eq"}
+    VW = cfg.d_inner + 2 * cfg.d_state + cfg.nheads
+    byts = M * (VW + cfg.d_inner) * es
+    return {"bytes": byts, "ops": None, "ops_unit": None}
+
+
+def read_traffic(kind: str, name: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None when absent or
+    taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_src_sha") != kernel_src_hash(kind):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(cfg: wl.MixerConfig, seed: int, target_s: float) -> dict:
+    import oracle
+    from oracle import mixer_stack
+    lat, u = wl.mixer_problem(cfg, seed=seed)
+    if cfg.act_dtype == "bf16":
+        u = torch.from_numpy(u).to(torch.bfloat16).float().numpy()
+    layers = []
+    for lw in lat:
+        w = {"A": lw["A"], "D": lw["D"], "dt_bias": lw["dt_bias"]}
+        for name in cfg.proj_shapes:
+            c, s, _ = oracle.quantize_weights(lw["W_" + name], cfg.group_size)
+            w["c_" + name], w["s_" + name] = c, s
+        layers.append(w)
+    oc = dict(kind=cfg.kind, d_model=cfg.d_model, d_inner=cfg.d_inner, d_state=cfg.d_state, dt_rank=cfg.dt_rank,
+              nheads=cfg.nheads, headdim=cfg.headdim, group_size=cfg.group_size, act_bits=cfg.act_bits,
+              act_dtype=oracle.BF16 if cfg.act_dtype == "bf16" else oracle.F32, norm_eps=cfg.norm_eps)
+    # calibrate on one sequence, then run enough whole sequences to fill the target time
+    t0 = time.perf_counter()
+    mixer_stack(oc, layers, u[:1])
+    t1 = time.perf_counter() - t0
+    nseq = int(max(1, min(cfg.batch, round(target_s / max(t1, 1e-3)))))
+    t0 = time.perf_counter()
+    mixer_stack(oc, layers, u[:nseq])
+    el = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": nseq * cfg.seqlen / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nseq} of {cfg.batch} sequences x {cfg.seqlen} tokens through all {cfg.layers} layers "
+                      f"({el:.1f} s, fp64 oracle with OpenMP)"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (sequences are independent, "
+              "so a data-parallel run would shard the batch with no exchange). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    cfg = wl.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    prob = Problem(cfg, args.seed, dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    result = {}
+    if not args.stages_only:
+        for _ in range(args.warmup):
+            prob.step(sh)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            prob.step(sh)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        eager_ms = e0.elapsed_time(e1) / args.steps
+        result["eager_ms_per_step"] = eager_ms
+        result["eager_wall_ms_per_step"] = wall * 1e3 / args.steps
+        step_ms = eager_ms
+        if not args.no_graph:
+            g = torch.cuda.CUDAGraph()
+            s2 = torch.cuda.Stream()
+            s2.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s2):
+                prob.step(s2.cuda_stream)  # warm the capture stream
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=s2):
+                    prob.step(s2.cuda_stream)
+            torch.cuda.synchronize()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1) / args.steps
+            result["graph_ms_per_step"] = graph_ms
+            step_ms = min(step_ms, graph_ms)
+        result["ms_per_step"] = step_ms
+
+    # per-stage durations (same kernels, issued stage by stage with events in between)
+    plan = StagePlan(prob)
+    for _ in range(max(1, args.warmup)):
+        plan.run(sh)
+    torch.cuda.synchronize()
+    names = [n for n, _ in plan.stages[0]]
+    events = {n: ([], []) for n in names}
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(args.steps):
+        plan.run(sh, events)
+    s1.record()
+    torch.cuda.synchronize()
+    stage_total_ms = s0.elapsed_time(s1) / args.steps
+    stages = {}
+    for n in names:
+        durs = [a.elapsed_time(b) for a, b in zip(*events[n])]
+        cost = stage_cost(cfg, n)
+        avg_s = float(np.mean(durs)) * 1e-3
+        stages[n] = {"avg_us": avg_s * 1e6, "launches": len(durs), "GBps": cost["bytes"] / avg_s / 1e9,
+                     "bytes": cost["bytes"]}
+        if cost["ops"]:
+            stages[n]["T" + cost["ops_unit"] + "/s"] = cost["ops"] / avg_s / 1e12
+    dominant = max(names, key=lambda n: stages[n]["avg_us"] * stages[n]["launches"])
+
+    cost = stage_cost(cfg, dominant)
+    avg_s = stages[dominant]["avg_us"] * 1e-6
+    if dominant == "scan" and cfg.kind == wl.MAMBA1:
+        kind = "scan_m1"
+        alu_t = cost["ops"] / (FP32_VECTOR_PEAK_TFLOPS * 1e12)
+        hbm_t = cost["bytes"] / (HBM_PEAK_GBPS * 1e9)
+        bound = "alu" if alu_t >= hbm_t else "hbm"
+    elif dominant == "scan":
+        kind, bound = "ssd", "hbm"
+    else:
+        kind = "bitlinear"
+        ai = cost["ops"] / cost["bytes"]
+        ridge = (INT8_MFMA_PEAK_TOPS if cfg.act_bits == 8 else BF16_MFMA_PEAK_TFLOPS) * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        bound = "mfma" if ai >= ridge else "hbm"
+    if bound == "alu":
+        roof = {"bound": "alu", "achieved": cost["ops"] / avg_s / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif bound == "mfma":
+        pk = INT8_MFMA_PEAK_TOPS if cfg.act_bits == 8 else BF16_MFMA_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": cost["ops"] / avg_s / 1e12, "peak": pk, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": cost["bytes"] / avg_s / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = read_traffic(kind, dominant, args.workload)
+    roof["kernel"] = dominant
+    roof["avg_launch_us"] = stages[dominant]["avg_us"]
+    roof["hbm_frac"] = cost["bytes"] / avg_s / 1e9 / HBM_PEAK_GBPS
+
+    if args.stages_only:
+        print(json.dumps({"stages": stages, "stage_ms_per_step": stage_total_ms, "roofline": roof}))
+        return
+
+    tokens = cfg.tokens
+    line = {
+        "metric": "mixer tokens/s at TriSSM shape" if args.workload == "trissm" else f"mixer tokens/s ({cfg.name})",
+        "value": tokens / (result["ms_per_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": result["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.act_dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.layers}-layer ternary selective-SSM mixer stack" if cfg.layers > 1
+                   else f"{cfg.name}: one ternary selective-SSM mixer layer",
+                   "kind": "mamba1" if cfg.kind == wl.MAMBA1 else "ssd", "layers": cfg.layers,
+                   "d_model": cfg.d_model, "d_inner": cfg.d_inner, "d_state": cfg.d_state, "dt_rank": cfg.dt_rank,
+                   "nheads": cfg.nheads, "headdim": cfg.headdim, "batch": cfg.batch, "seq_len": cfg.seqlen,
+                   "tokens_per_step": tokens, "act_bits": cfg.act_bits, "group_size": cfg.group_size,
+                   "contraction": "int8 x ternary -> int32 (MFMA)" if cfg.act_bits == 8 else
+                   "bf16 x ternary -> fp32 (MFMA)", "scan_state": "fp32"},
+        "timing": {k: v for k, v in result.items() if k != "ms_per_step"},
+        "stages": stages,
+        "stage_ms_per_step": stage_total_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -117,18 +117,22 @@ ssm_status ssm_ternary_quantize_weights(const float* w_latent, int64_t n_out, in
  *   xh = (x * r) * norm_weight (fp32; no multiply when norm_weight is NULL).
  *   act_bits 8 (A8): a = max|xh|; q = clamp(round_half_even(xh * (127 / max(a, 1e-5))),
  *       -128, 127) int8; acc = sum_k q * w (int32, exact: the multiply-free
- *       add/subtract/skip sum); y = acc * s_w * max(a, 1e-5) / 127 (per group: each
- *       group's partial accumulator times its scale).
- *   act_bits 16 (A16): y = sum_groups s[n, g] * sum_{k in g} bf16(xh) * w, fp32
- *       accumulation (no activation quantisation).
- *   then y += bias (if given) and y += residual (if given); stored as y_dtype.
+ *       add/subtract/skip sum); y = (s_w * acc) * (max(a, 1e-5) / 127) evaluated in fp64
+ *       (per group: the fp64 sum over groups, in order, of s[n, g] * acc_g), plus bias,
+ *       plus residual, rounded once to fp32 (then to bf16 for a bf16 output).
+ *   act_bits 16 (A16): y = sum_groups s[n, g] * sum_{k in g} xh * w with xh carried as
+ *       bf16 (bf16 output) or as the sum of two bf16 terms (fp32 output), fp32
+ *       accumulation; no activation quantisation.  Then + bias + residual.
  * x_dtype SSM_I8 (A8 only): x already holds int8 codes and x_absmax their per-row
  * absmax a; the norm and quantisation are skipped.
  * Optional stage outputs (A8 only; each NULL or a device buffer): dbg_xq int8 [m, k],
- * dbg_absmax fp32 [m], dbg_acc int32 [m, n_out] (sum over all groups).
- * Requirements: 1 <= k <= 65536; n_out >= 1; m >= 0 (m == 0 launches nothing);
+ * dbg_absmax fp32 [m], dbg_acc int32 [m, n_out] (sum over all groups).  dbg_xq and
+ * dbg_absmax are written only when the norm runs (x_dtype F32 or BF16).
+ * Requirements: 1 <= k <= 4096; 1 <= n_out; m >= 0 (m == 0 launches nothing);
  * ldx >= k, ldy >= n_out, ld_res >= n_out; group_size 0 or a multiple of 64 dividing k;
- * act_bits 16 requires x_dtype F32 or BF16; residual has y_dtype.
+ * act_bits 16 requires x_dtype F32 or BF16; residual has y_dtype; w_packed 4-byte
+ * aligned; int8 input needs k % 64 == 0, ldx % 16 == 0 and 16-byte alignment.
+ * workspace: ssm_bitlinear_workspace_bytes() bytes, 16-byte aligned (0 for int8 input).
  * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_WORKSPACE,
  * SSM_ERR_UNSUPPORTED, SSM_ERR_DEVICE.
  */
@@ -176,9 +180,16 @@ ssm_status ssm_bitlinear_fwd(const ssm_bitlinear_args* a, void* workspace, size_
  *   Bm/Cm [B, L, d_state], ld_B / ld_C;  y [B, L, nheads * headdim], ld_y;
  *   x, delta, Bm, Cm, y have act_dtype (SSM_F32 or SSM_BF16); A, D, delta_bias, h0,
  *   h_last are fp32; h0 / h_last are [B, nheads, headdim, d_state] or NULL.
+ * Optional dt projection (Mamba-1 kind; the TriSSM README's ternary Delta projection):
+ * when dt_in is not NULL, delta is ignored and the pre-activation dt of channel h at token
+ * m is the A8 BitLinear (as ssm_bitlinear_fwd, fp32 out, no bias) of dt_in's first dt_rank
+ * columns (row stride ld_dt_in, act_dtype) with packed weights w_dt [nheads, dt_rank],
+ * scale s_dt [1], RMSNorm gains g_dt [dt_rank] or NULL and epsilon dt_eps; it is computed
+ * inside the scan and never stored.  dt_rank must be in [1, 64].
  * Supported: a_per_state = 1 with headdim = 1 and d_state in {4, 8, 16, 32, 64};
- * a_per_state = 0 with headdim in {16, 32, 64, 128} and d_state in {16, 32, 64, 128}.
- * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_WORKSPACE,
+ * a_per_state = 0 with headdim <= 256 and d_state in {16, 32, 64, 128}.
+ * batch == 0 or seqlen == 0 launches nothing (h_last is then not written).
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_ALIGN, SSM_ERR_WORKSPACE,
  * SSM_ERR_UNSUPPORTED, SSM_ERR_DEVICE.
  */
 typedef struct {
@@ -197,6 +208,14 @@ typedef struct {
   const float* h0;
   float* h_last;
   void* y;            int64_t ld_y;
+  /* optional dt projection (see above) */
+  const void* dt_in;  int64_t ld_dt_in;
+  int64_t dt_rank;
+  const uint8_t* w_dt;
+  const float* s_dt;
+  const float* g_dt;
+  float dt_eps;
+  int32_t pad1;
 } ssm_scan_args;
 
 size_t ssm_selective_scan_workspace_bytes(const ssm_scan_args* a);

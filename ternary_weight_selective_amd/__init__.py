@@ -38,7 +38,8 @@ class ScanArgs(ctypes.Structure):
                 ("a_per_state", _i32), ("act_dtype", _i32), ("x", _vp), ("ld_x", _i64), ("delta", _vp),
                 ("ld_delta", _i64), ("delta_bias", _vp), ("delta_softplus", _i32), ("pad0", _i32), ("A", _vp),
                 ("Bm", _vp), ("ld_B", _i64), ("Cm", _vp), ("ld_C", _i64), ("D", _vp), ("h0", _vp),
-                ("h_last", _vp), ("y", _vp), ("ld_y", _i64)]
+                ("h_last", _vp), ("y", _vp), ("ld_y", _i64), ("dt_in", _vp), ("ld_dt_in", _i64), ("dt_rank", _i64),
+                ("w_dt", _vp), ("s_dt", _vp), ("g_dt", _vp), ("dt_eps", ctypes.c_float), ("pad1", _i32)]
 
 
 class MixerConfig(ctypes.Structure):
@@ -204,15 +205,17 @@ def ssm_bitlinear_fwd(x: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Te
     return (out, *dbg) if debug else out
 
 
-def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor,
+def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch.Tensor, Bm: torch.Tensor,
                            Cm: torch.Tensor, D: torch.Tensor | None = None, delta_bias: torch.Tensor | None = None,
                            softplus: bool = True, h0: torch.Tensor | None = None, return_last_state: bool = False,
-                           out: torch.Tensor | None = None, stream=None):
+                           out: torch.Tensor | None = None, dt_proj: dict | None = None, stream=None):
     """Selective scan.  x [B, L, H*P], delta [B, L, H], Bm/Cm [B, L, N]; A [H, N] (Mamba-1 kind,
-    P = 1) or [H] (SSD kind).  Views with a contiguous last dim and even row strides are fine."""
-    batch, seqlen, _ = delta.shape
-    H = delta.shape[2]
-    HP = x.shape[2]
+    P = 1) or [H] (SSD kind).  Views with a contiguous last dim and even row strides are fine.
+    dt_proj (Mamba-1 kind): dict(dt_in [B, L, >= R] view, w_dt packed [H, row bytes], s_dt [1],
+    dt_rank R, optional g_dt, eps): dt is the A8 BitLinear of dt_in computed inside the scan
+    (delta is then ignored and may be None)."""
+    batch, seqlen, HP = x.shape
+    H = A.shape[0] if A.dim() == 2 else (delta.shape[2] if delta is not None else A.shape[0])
     N = Bm.shape[2]
     aps = 1 if A.dim() == 2 else 0
     if out is None:
@@ -222,7 +225,12 @@ def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor
     a.batch, a.seqlen, a.nheads, a.headdim, a.d_state = batch, seqlen, H, HP // H, N
     a.a_per_state, a.act_dtype = aps, _DTYPES[x.dtype]
     a.x, a.ld_x = _p(x), _rows(x, "x")[1]
-    a.delta, a.ld_delta = _p(delta), _rows(delta, "delta")[1]
+    if delta is not None:
+        a.delta, a.ld_delta = _p(delta), _rows(delta, "delta")[1]
+    if dt_proj is not None:
+        a.dt_in, a.ld_dt_in = _p(dt_proj["dt_in"]), _rows(dt_proj["dt_in"], "dt_in")[1]
+        a.dt_rank, a.w_dt, a.s_dt = dt_proj["dt_rank"], _p(dt_proj["w_dt"]), _p(dt_proj["s_dt"])
+        a.g_dt, a.dt_eps = _p(dt_proj.get("g_dt")), dt_proj.get("eps", 1e-5)
     a.delta_bias, a.delta_softplus = _p(delta_bias), int(softplus)
     a.A = _p(A)
     a.Bm, a.ld_B = _p(Bm), _rows(Bm, "Bm")[1]

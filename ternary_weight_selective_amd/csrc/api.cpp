@@ -148,10 +148,18 @@ ssm_status scan_check(const ssm_scan_args* a) {
     return fail(SSM_ERR_SHAPE, "scan: a_per_state must be 0 or 1");
   }
   const int64_t HP = a->nheads * a->headdim;
-  if (a->ld_x < HP || a->ld_y < HP || a->ld_delta < a->nheads || a->ld_B < a->d_state || a->ld_C < a->d_state)
+  const bool proj = a->dt_in != nullptr;
+  if (a->ld_x < HP || a->ld_y < HP || a->ld_B < a->d_state || a->ld_C < a->d_state || (!proj && a->ld_delta < a->nheads))
     return fail(SSM_ERR_SHAPE, "scan: a row stride is smaller than its row");
-  if (a->batch * a->seqlen > 0 && (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->y))
-    return fail(SSM_ERR_NULL, "scan: x, delta, A, Bm, Cm and y are required");
+  if (proj) {
+    if (a->a_per_state != 1) return fail(SSM_ERR_UNSUPPORTED, "scan: the dt projection exists for the Mamba-1 kind only");
+    if (a->dt_rank < 1 || a->dt_rank > 64) return fail(SSM_ERR_UNSUPPORTED, "scan: dt_rank must be in [1, 64]");
+    if (a->ld_dt_in < a->dt_rank) return fail(SSM_ERR_SHAPE, "scan: ld_dt_in < dt_rank");
+    if (!a->w_dt || !a->s_dt) return fail(SSM_ERR_NULL, "scan: w_dt and s_dt are required with dt_in");
+    if (!aligned(a->w_dt, 4)) return fail(SSM_ERR_ALIGN, "scan: w_dt must be 4-byte aligned");
+  }
+  if (a->batch * a->seqlen > 0 && (!a->x || (!proj && !a->delta) || !a->A || !a->Bm || !a->Cm || !a->y))
+    return fail(SSM_ERR_NULL, "scan: x, delta (or dt_in), A, Bm, Cm and y are required");
   return SSM_OK;
 }
 
@@ -171,6 +179,11 @@ ScanArgs to_scan(const ssm_scan_args* a) {
   s.Cm = a->Cm; s.ld_C = a->ld_C;
   s.D = a->D; s.h0 = a->h0; s.h_last = a->h_last;
   s.y = a->y; s.ld_y = a->ld_y;
+  if (a->dt_in) {
+    s.dr = a->dt_in; s.ld_dr = a->ld_dt_in; s.R = (int)a->dt_rank;
+    s.w_dt = (const uint32_t*)a->w_dt; s.w_dt_row_words = cdiv(a->dt_rank, 16);
+    s.s_dt = a->s_dt; s.g_dt = a->g_dt; s.eps = a->dt_eps;
+  }
   return s;
 }
 
@@ -371,22 +384,22 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
     if (st != SSM_OK) return st;
     st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
     if (st != SSM_OK) return st;
-    ScanArgs s{};
     const size_t as = act_size(c->act_dtype);
-    s.batch = batch; s.L = seqlen; s.H = c->d_inner; s.P = 1; s.N = c->d_state;
-    s.act_bf16 = c->act_dtype == SSM_BF16;
-    s.x = x; s.ld_x = c->d_inner;
-    s.delta = nullptr; s.ld_delta = 0;
-    s.delta_bias = w->dt_bias; s.softplus = 1;
-    s.A = w->A;
-    s.Bm = (const char*)pp + c->dt_rank * as; s.ld_B = p.PW;
-    s.Cm = (const char*)pp + (c->dt_rank + c->d_state) * as; s.ld_C = p.PW;
-    s.D = w->D;
-    s.y = y; s.ld_y = c->d_inner;
-    s.dr = pp; s.ld_dr = p.PW; s.R = (int)c->dt_rank;
-    s.w_dt = (const uint32_t*)w->w_dt; s.w_dt_row_words = cdiv(c->dt_rank, 16);
-    s.s_dt = w->s_dt; s.g_dt = w->g_dt; s.eps = c->norm_eps;
-    st = dev(launch_scan_m1(s, stream), "mixer scan");
+    ssm_scan_args sa{};
+    sa.batch = batch; sa.seqlen = seqlen; sa.nheads = c->d_inner; sa.headdim = 1; sa.d_state = c->d_state;
+    sa.a_per_state = 1; sa.act_dtype = c->act_dtype;
+    sa.x = x; sa.ld_x = c->d_inner;
+    sa.delta_bias = w->dt_bias; sa.delta_softplus = 1;
+    sa.A = w->A;
+    sa.Bm = (const char*)pp + c->dt_rank * as; sa.ld_B = p.PW;
+    sa.Cm = (const char*)pp + (c->dt_rank + c->d_state) * as; sa.ld_C = p.PW;
+    sa.D = w->D;
+    sa.y = y; sa.ld_y = c->d_inner;
+    sa.dt_in = pp; sa.ld_dt_in = p.PW; sa.dt_rank = c->dt_rank;
+    sa.w_dt = w->w_dt; sa.s_dt = w->s_dt; sa.g_dt = w->g_dt; sa.dt_eps = c->norm_eps;
+    st = scan_check(&sa);
+    if (st != SSM_OK) return st;
+    st = dev(launch_scan_m1(to_scan(&sa), stream), "mixer scan");
     if (st != SSM_OK) return st;
     return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
   }
