@@ -220,6 +220,7 @@ ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, Mi
     p->off_x = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
     p->off_p = off; off = align_up(off + (size_t)p->M * p->PW * as);
     p->off_y = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
+    p->off_scan = off;
   } else if (c->kind == SSM_MIXER_SSD) {
     if (c->nheads < 1 || c->headdim < 1 || c->nheads * c->headdim != c->d_inner)
       return fail(SSM_ERR_SHAPE, "mixer: nheads * headdim must equal d_inner");
@@ -309,7 +310,7 @@ size_t ssm_selective_scan_workspace_bytes(const ssm_scan_args* a) {
   const ssm_status st = scan_check(a);
   g_err = keep;
   if (st != SSM_OK) return 0;
-  return a->a_per_state ? 0 : scan_ssd_workspace(to_scan(a));
+  return a->a_per_state ? scan_m1_workspace(to_scan(a)) : scan_ssd_workspace(to_scan(a));
 }
 
 ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* ws, size_t wsb, hipStream_t stream) {
@@ -317,9 +318,10 @@ ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* ws, size_t wsb, 
   ssm_status st = scan_check(a);
   if (st != SSM_OK) return st;
   const ScanArgs s = to_scan(a);
-  if (a->a_per_state) return dev(launch_scan_m1(s, stream), "scan");
-  const size_t need = scan_ssd_workspace(s);
+  const size_t need = a->a_per_state ? scan_m1_workspace(s) : scan_ssd_workspace(s);
   if (need && (!ws || wsb < need)) return fail(SSM_ERR_WORKSPACE, "scan: workspace needs %zu bytes", need);
+  if (need && !aligned(ws, 16)) return fail(SSM_ERR_ALIGN, "scan: workspace must be 16-byte aligned");
+  if (a->a_per_state) return dev(launch_scan_m1(s, ws, stream), "scan");
   return dev(launch_scan_ssd(s, ws, wsb, stream), "scan");
 }
 
@@ -329,12 +331,14 @@ size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64
   const ssm_status st = mix_plan(c, batch, seqlen, &p);
   g_err = keep;
   if (st != SSM_OK) return 0;
+  ScanArgs s{};
+  s.batch = batch; s.L = seqlen; s.N = c->d_state;
   if (c->kind == SSM_MIXER_SSD) {
-    ScanArgs s{};
-    s.batch = batch; s.L = seqlen; s.H = c->nheads; s.P = c->headdim; s.N = c->d_state;
+    s.H = c->nheads; s.P = c->headdim;
     return p.total + align_up(scan_ssd_workspace(s));
   }
-  return p.total;
+  s.H = c->d_inner; s.P = 1;
+  return p.total + align_up(scan_m1_workspace(s));
 }
 
 ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
@@ -399,7 +403,7 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
     sa.w_dt = w->w_dt; sa.s_dt = w->s_dt; sa.g_dt = w->g_dt; sa.dt_eps = c->norm_eps;
     st = scan_check(&sa);
     if (st != SSM_OK) return st;
-    st = dev(launch_scan_m1(to_scan(&sa), stream), "mixer scan");
+    st = dev(launch_scan_m1(to_scan(&sa), base + p.off_scan, stream), "mixer scan");
     if (st != SSM_OK) return st;
     return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
   }

@@ -64,7 +64,8 @@ struct ScanArgs {
   const uint32_t* w_dt; int64_t w_dt_row_words;
   const float* s_dt; const float* g_dt; float eps;
 };
-hipError_t launch_scan_m1(const ScanArgs& a, hipStream_t s);
+hipError_t launch_scan_m1(const ScanArgs& a, void* ws, hipStream_t s);
+size_t scan_m1_workspace(const ScanArgs& a);
 hipError_t launch_scan_ssd(const ScanArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 size_t scan_ssd_workspace(const ScanArgs& a);
 

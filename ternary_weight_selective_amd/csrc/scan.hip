@@ -1,187 +1,430 @@
 // Selective scan, Mamba-1 kind (Mamba, cited by title in "Baseline Shape Decides the
-// Verdict ...", Builds on; TriSSM README: input-dependent Delta, B, C, parallel
-// associative scan).  A is per (channel, state); one channel per head.
+// Verdict ...", Builds on; TriSSM README: input-dependent Delta, B, C, and the recurrence
+// evaluated with a parallel associative scan).  A is per (channel, state); one channel per
+// head.
 //
-// Each lane owns SPL states of one channel and runs the recurrence over time in
-// registers; the NS / SPL lanes of a channel are adjacent and add their readout partials
-// with xor shuffles.  Time is staged through LDS in tiles of TT steps with coalesced
-// loads of x, dt, B, C and a coalesced store of y.  Per state and step the lane does one
-// exp2 (A is pre-scaled by log2 e), two multiplies and two fused multiply-adds.
+// Work split.  A block owns 64 channels (the lanes) of one sequence and one time chunk; its
+// 4 waves split the NS states into 4 groups, so that B and C of a step are the same for a
+// whole wave: they are read from LDS at wave-uniform addresses (a broadcast), for a group of
+// steps at a time with one wait.  Each lane runs the recurrence of NS / 4 states over time in
+// registers: per state and step one exp2 (A is pre-scaled by log2 e), two multiplies and two
+// fused multiply-adds; the kernel is bound by VALU issue.  The waves' readout partials meet
+// in LDS and are added in wave order.
 //
-// Optionally (the mixer path) the dt projection is computed here: the low-rank input dr
-// (k = R <= 64 columns) of each token is RMS-normalised and absmax-quantised by one wave
-// in the same fixed order as the standalone BitLinear, and each channel's int32 dot
-// product with its ternary weight row is four-way int8 dot products (v_dot4), dequantised
-// in fp64 exactly as the BitLinear epilogue does.
+// Time is staged through LDS in tiles of 32 steps: the next tile's x, B, C (and dt input
+// codes) are loaded into registers, coalesced, while the current tile runs.
+//
+// Chunks (the carried inter-chunk state).  When batch x channel tiles give too few blocks
+// to fill the chip, the sequence is cut into T chunks: pass 1 runs every chunk but the last
+// from a zero state and keeps its end state h_loc and sum(dt); pass 2 composes the chunks
+// in order with the associative operator (P, h_loc) o h = P * h + h_loc, P = exp(A sum dt);
+// pass 3 reruns every chunk from its true incoming state and writes y.
+//
+// Optionally (the mixer path) dt is the A8 BitLinear of a low-rank input dr (k = R <= 64
+// columns), computed here: a pre-kernel RMS-normalises and absmax-quantises each token's
+// row once, with a group of 16..64 lanes in the same fixed order as the standalone
+// BitLinear (for k <= 64 the 64-lane butterfly reduces to the group's butterfly plus exact
+// zero additions); in the scan each channel's int32 dot product with its ternary weight
+// row is v_dot4 instructions, and the dequantisation is the BitLinear epilogue's fp64
+// expression.
 #include "launch.hpp"
 
 namespace ssm {
 
 namespace {
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int RMAX = 64;
 
-__device__ __forceinline__ float softplus_f(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+// softplus(v) = log(1 + e^v), the identity above 20.  With z = e^v and u = 1 + z,
+// log1p(z) = log(u) * z / (u - 1) compensates the rounding of u; below z = 1e-4 the
+// series z - z^2 / 2 is used.  Branch-free, on the hardware exp2 / log2 / reciprocal.
+__device__ __forceinline__ float softplus_f(float v) {
+  const float z = __builtin_amdgcn_exp2f(v * LOG2E);
+  const float u = 1.0f + z;
+  const float um1 = u - 1.0f;
+  const float big = (0.69314718055994531f * __builtin_amdgcn_logf(u)) * (z * __builtin_amdgcn_rcpf(um1));
+  const float small = z * __builtin_fmaf(-0.5f, z, 1.0f);
+  const float r = z < 1e-4f ? small : big;
+  return v > 20.0f ? v : r;
+}
+
+struct ChunkArgs {
+  int64_t chunk_len;  // time steps per chunk (a multiple of the tile length)
+  int nchunks;
+  float* st;          // [B, nchunks, Di, NS]: pass 1 end states, then (pass 2) incoming states
+  float* sdt;         // [B, nchunks, Di]: sum of dt over each chunk
+};
+
 }  // namespace
 
-template <int NS, typename T, bool FUSED>
-__global__ __launch_bounds__(256) void k_scan_m1(ScanArgs a) {
-  constexpr int SPL = NS < 4 ? NS : 4;
-  constexpr int LPC = NS / SPL;   // lanes per channel
-  constexpr int CPB = 256 / LPC;  // channels per block
-  constexpr int TSTEP = 256 / CPB;
-  constexpr int TT = CPB >= 256 ? 8 : (CPB >= 128 ? 16 : 32);  // time steps per LDS tile
-  __shared__ float2 s_dd[TT][CPB];  // (dt, dt * x)
-  __shared__ float s_dx[TT][CPB];   // D * x
-  __shared__ float s_y[TT][CPB];
-  __shared__ float s_B[TT][NS];
-  __shared__ float s_C[TT][NS];
-  __shared__ __align__(16) int8_t s_q[TT][64];
-  __shared__ double s_rf[TT];
+// dt-input quantisation, once per token: int8 codes [M, 16 * RW] (zero past R) and the fp64
+// dequantisation factor max(m, 1e-5) / 127 [M].  A group of G = 16, 32 or 64 lanes per token.
+__global__ __launch_bounds__(256) void k_dt_codes(const void* __restrict__ dr, int bf16, int64_t M, int64_t ld,
+                                                  int R, const float* __restrict__ g, float eps,
+                                                  int8_t* __restrict__ codes, int cw, double* __restrict__ deq) {
+  const int lane = threadIdx.x & 63;
+  const int G = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
+  const int gl = lane & (G - 1);
+  const int64_t tok = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
+  const bool ok = tok < M;
+  float v = 0.0f;
+  if (ok && gl < R)
+    v = bf16 ? bf16_to_f32(((const bf16_t*)dr)[tok * ld + gl]) : ((const float*)dr)[tok * ld + gl];
+  float s = __builtin_fmaf(v, v, 0.0f);
+  for (int dd = G / 2; dd >= 1; dd >>= 1) s = s + __shfl_xor(s, dd, 64);
+  const float ms = __fdiv_rn(s, (float)R);
+  const float r = __fdiv_rn(1.0f, sqrt_rn(ms + eps));
+  float xh = v * r;
+  if (g) xh = gl < R ? xh * g[gl] : 0.0f;
+  float m = fabsf(xh);
+  for (int dd = G / 2; dd >= 1; dd >>= 1) m = fmaxf(m, __shfl_xor(m, dd, 64));
+  const float sigma = __fdiv_rn(127.0f, fmaxf(m, 1e-5f));
+  float q = rintf(xh * sigma);
+  q = fminf(fmaxf(q, -128.0f), 127.0f);
+  if (ok && gl < cw) codes[tok * cw + gl] = (int8_t)(int)q;
+  if (ok && gl == 0) deq[tok] = (double)fmaxf(m, 1e-5f) / 127.0;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+namespace {
+struct DtCodes {
+  const int8_t* codes;  // [M, 16 * RW]
+  const double* deq;    // [M]
+};
+}  // namespace
+
+// Lanes are 64 channels; the 4 waves of a block are 4 groups of NS / 4 states, so B and C of
+// a step are the same for a whole wave and are read with scalar loads into SGPRs.  Each wave
+// writes its readout partial per (step, channel) to LDS; the partials are added in wave
+// order, plus D x, when the tile is stored.
+// LOCAL: pass 1 (zero start, no readout; writes the chunk's end state and sum(dt)).
+template <int NS, typename T, bool FUSED, bool LOCAL>
+__global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, DtCodes dc) {
+  constexpr int SPL = NS / 4;     // states per lane
+  constexpr int CPB = 64;         // channels per block
+  constexpr int TT = 32;          // time steps per tile
+  constexpr int XPT = TT * CPB / 256;
+  constexpr int GT = SPL <= 4 ? 8 : (SPL == 8 ? 4 : 2);  // steps per group of LDS reads
+  constexpr int BPT = (TT * NS + 255) / 256;             // B (and C) elements per thread per tile
+  __shared__ float s_x[TT][CPB];
+  __shared__ float s_d[FUSED ? 1 : TT][CPB];
+  __shared__ __align__(16) int8_t s_q[FUSED ? TT : 1][64];
+  __shared__ double s_rf[FUSED ? TT : 1];
+  __shared__ float2 s_dd[TT][CPB];  // (dt, dt * x)
+  __shared__ __align__(16) float s_B[TT][NS];
+  __shared__ __align__(16) float s_C[LOCAL ? 1 : TT][NS];
+  __shared__ float s_yp[LOCAL ? 1 : 4][LOCAL ? 1 : TT][CPB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t Di = a.H, L = a.L;
   const int64_t b = blockIdx.y;
-  // recurrence role
-  const int c = tid / LPC, qq = tid % LPC;
-  const int64_t d = (int64_t)blockIdx.x * CPB + c;
+  const int chunk = blockIdx.z;
+  const int64_t tb = (int64_t)chunk * ch.chunk_len;
+  const int64_t te = (tb + ch.chunk_len < L) ? tb + ch.chunk_len : L;
+  const int64_t d0 = (int64_t)blockIdx.x * CPB;
+  const int64_t d = d0 + lane;
   const bool dv = d < Di;
-  // staging role: a fixed channel per thread
-  const int cs = tid % CPB, ts0 = tid / CPB;
-  const int64_t ds = (int64_t)blockIdx.x * CPB + cs;
-  const bool dsv = ds < Di;
-  const float bias_s = (dsv && a.delta_bias) ? a.delta_bias[ds] : 0.0f;
-  const float D_s = (dsv && a.D) ? a.D[ds] : 0.0f;
+  // staging role: thread -> (channel lane, rows w, w + 4, ...)
+  const float bias_s = (dv && a.delta_bias) ? a.delta_bias[d] : 0.0f;
+  const float D_s = (dv && a.D) ? a.D[d] : 0.0f;
+  const int cw = FUSED ? 16 * (int)((a.R + 15) / 16) : 0;  // code bytes per token
+
+  const T* X = (const T*)a.x;
+  const T* DL = (const T*)a.delta;
 
   v4i wdt[4];
-  int RW = 0;
+  double s_dt = 0.0;
   if (FUSED) {
-    RW = (int)cdiv(a.R, 16);
+    s_dt = (double)a.s_dt[0];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int q = 0; q < 4; ++q) {
       uint32_t wv = 0;
-      if (dsv && w < RW) wv = a.w_dt[ds * a.w_dt_row_words + w];
-      wdt[w] = unpack16_i8(wv);
+      if (dv && q * 16 < cw) wv = a.w_dt[d * a.w_dt_row_words + q];
+      wdt[q] = unpack16_i8(wv);
     }
   }
 
   float Al[SPL], h[SPL];
 #pragma unroll
   for (int i = 0; i < SPL; ++i) {
-    const int n = qq * SPL + i;
+    const int n = w * SPL + i;
     Al[i] = dv ? a.A[d * NS + n] * LOG2E : 0.0f;
-    h[i] = (dv && a.h0) ? a.h0[(b * Di + d) * NS + n] : 0.0f;
+    float h_init = 0.0f;
+    if (!LOCAL && dv) {
+      if (chunk == 0) h_init = a.h0 ? a.h0[(b * Di + d) * NS + n] : 0.0f;
+      else h_init = ch.st[((b * ch.nchunks + chunk - 1) * Di + d) * NS + n];
+    }
+    h[i] = h_init;
   }
+  float sum_dt = 0.0f;
 
-  const T* X = (const T*)a.x;
-  const T* Bm = (const T*)a.Bm;
-  const T* Cm = (const T*)a.Cm;
-  T* Y = (T*)a.y;
-
-  for (int64_t t0 = 0; t0 < L; t0 += TT) {
-    for (int e = tid; e < TT * NS; e += 256) {
-      const int t = e / NS, n = e % NS;
-      const bool valid = t0 + t < L;
+  // prefetch registers: x (and delta) of the next tile; its dt codes and factors
+  float rx[XPT], rd[FUSED ? 1 : XPT], rb[BPT], rc[BPT];
+  int rq[2] = {0, 0};
+  double rf = 0.0;
+  auto load_tile = [&](int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int t = w + 4 * i;
+      const bool ok = (t0 + t < te) && dv;
       const int64_t tok = b * L + t0 + t;
-      s_B[t][n] = valid ? ld_act(Bm + tok * a.ld_B + n) : 0.0f;
-      s_C[t][n] = valid ? ld_act(Cm + tok * a.ld_C + n) : 0.0f;
+      rx[i] = ok ? ld_act(X + tok * a.ld_x + d) : 0.0f;
+      if (!FUSED) rd[FUSED ? 0 : i] = ok ? ld_act(DL + tok * a.ld_delta + d) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int e = tid + 256 * i, t = e / NS, n = e % NS;
+      const bool ok = (e < TT * NS) && (t0 + t < te);
+      const int64_t tok = b * L + t0 + t;
+      rb[i] = ok ? ld_act((const T*)a.Bm + tok * a.ld_B + n) : 0.0f;
+      rc[i] = (ok && !LOCAL) ? ld_act((const T*)a.Cm + tok * a.ld_C + n) : 0.0f;
     }
     if (FUSED) {
-      const T* DR = (const T*)a.dr;
-      for (int t = wave; t < TT; t += 4) {
-        const bool valid = t0 + t < L;
-        const int64_t tok = b * L + t0 + t;
-        const float v = (valid && lane < a.R) ? ld_act(DR + tok * a.ld_dr + lane) : 0.0f;
-        float s = __builtin_fmaf(v, v, 0.0f);
-        s = wave_sum_butterfly(s);
-        const float ms = __fdiv_rn(s, (float)a.R);
-        const float r = __fdiv_rn(1.0f, sqrt_rn(ms + a.eps));
-        float xh = v * r;
-        if (a.g_dt) xh = lane < a.R ? xh * a.g_dt[lane] : 0.0f;
-        const float m = wave_max(fabsf(xh));
-        const float sigma = __fdiv_rn(127.0f, fmaxf(m, 1e-5f));
-        float rr = rintf(xh * sigma);
-        rr = fminf(fmaxf(rr, -128.0f), 127.0f);
-        s_q[t][lane] = (int8_t)(int)rr;
-        if (lane == 0) s_rf[t] = (double)fmaxf(m, 1e-5f) / 127.0;
+      const int nq = TT * cw / 4;  // 4-byte words of codes in the tile (<= 512)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = tid + 256 * k, t = e * 4 / cw;
+        rq[k] = (e < nq && t0 + t < te) ? ((const int*)dc.codes)[((b * L + t0) * cw) / 4 + e] : 0;
       }
-      __syncthreads();
+      rf = (tid < TT && t0 + tid < te) ? dc.deq[b * L + t0 + tid] : 0.0;
     }
-    for (int t = ts0; t < TT; t += TSTEP) {
-      const bool valid = (t0 + t < L) && dsv;
-      const int64_t tok = b * L + t0 + t;
-      const float xv = valid ? ld_act(X + tok * a.ld_x + ds) : 0.0f;
-      float dt;
+  };
+
+  load_tile(tb);
+  for (int64_t t0 = tb; t0 < te; t0 += TT) {
+    // 1. registers -> LDS
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      s_x[w + 4 * i][lane] = rx[i];
+      if (!FUSED) s_d[FUSED ? 0 : w + 4 * i][lane] = rd[FUSED ? 0 : i];
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int e = tid + 256 * i;
+      if (e < TT * NS) {
+        s_B[e / NS][e % NS] = rb[i];
+        if (!LOCAL) s_C[LOCAL ? 0 : e / NS][e % NS] = rc[i];
+      }
+    }
+    if (FUSED) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = tid + 256 * k;
+        if (e < TT * cw / 4) ((int*)&s_q[0][0])[(e * 4 / cw) * 16 + e % (cw / 4)] = rq[k];
+      }
+      if (tid < TT) s_rf[FUSED ? tid : 0] = rf;
+    }
+    __syncthreads();
+    // 2. next tile in flight while this one is processed
+    if (t0 + TT < te) load_tile(t0 + TT);
+    // 3. per (step, channel): dt, softplus, dt * x
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int t = w + 4 * i;
+      const float xv = s_x[t][lane];
+      float dtv;
       if (FUSED) {
         int acc = 0;
-        const int* qrow = (const int*)&s_q[t][0];
+        const int* qrow = (const int*)&s_q[FUSED ? t : 0][0];
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          if (w < RW) {
+        for (int q = 0; q < 4; ++q)
+          if (q * 16 < cw) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(qrow[w * 4 + j], wdt[w][j], acc, false);
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(qrow[q * 4 + j], wdt[q][j], acc, false);
           }
-        // the same fp64 dequantisation as the BitLinear epilogue: (s_dt * acc) * deq
-        dt = (float)(((double)a.s_dt[0] * (double)acc) * s_rf[t]);
+        dtv = (float)((s_dt * (double)acc) * s_rf[FUSED ? t : 0]);
       } else {
-        dt = valid ? ld_act((const T*)a.delta + tok * a.ld_delta + ds) : 0.0f;
+        dtv = s_d[FUSED ? 0 : t][lane];
       }
-      dt += bias_s;
-      if (a.softplus) dt = softplus_f(dt);
-      s_dd[t][cs] = make_float2(dt, dt * xv);
-      s_dx[t][cs] = D_s * xv;
+      dtv += bias_s;
+      if (a.softplus) dtv = softplus_f(dtv);
+      s_dd[t][lane] = make_float2(dtv, dtv * xv);
     }
     __syncthreads();
-    const int tmax = (int)((L - t0) < TT ? (L - t0) : TT);
-    for (int t = 0; t < tmax; ++t) {
-      const float2 dd = s_dd[t][c];
-      float yp = 0.0f;
+    // 4. recurrence.  B and C of a step are the same for the whole wave (broadcast LDS reads at
+    //    immediate offsets); a group of GT steps issues all its LDS reads, then one wait.
+    const int tmax = (int)((te - t0) < TT ? (te - t0) : TT);
+    for (int tt = 0; tt < tmax; tt += GT) {
+      float bq[GT][SPL], cq[GT][SPL];
+      float2 dd[GT];
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) {
-        const int n = qq * SPL + i;
-        const float ab = __builtin_amdgcn_exp2f(dd.x * Al[i]);
-        h[i] = __builtin_fmaf(ab, h[i], dd.y * s_B[t][n]);
-        yp = __builtin_fmaf(s_C[t][n], h[i], yp);
+      for (int u = 0; u < GT; ++u) {
+        const int t = (tt + u < tmax) ? tt + u : tmax - 1;
+        if (SPL % 4 == 0) {
+#pragma unroll
+          for (int i = 0; i < SPL; i += 4) {
+            const float4 b4 = *(const float4*)&s_B[t][w * SPL + i];
+            bq[u][i] = b4.x; bq[u][(i + 1) % SPL] = b4.y; bq[u][(i + 2) % SPL] = b4.z; bq[u][(i + 3) % SPL] = b4.w;
+            if (!LOCAL) {
+              const float4 c4 = *(const float4*)&s_C[LOCAL ? 0 : t][w * SPL + i];
+              cq[u][i] = c4.x; cq[u][(i + 1) % SPL] = c4.y; cq[u][(i + 2) % SPL] = c4.z; cq[u][(i + 3) % SPL] = c4.w;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < SPL; ++i) {
+            bq[u][i] = s_B[t][w * SPL + i];
+            if (!LOCAL) cq[u][i] = s_C[LOCAL ? 0 : t][w * SPL + i];
+          }
+        }
+        dd[u] = s_dd[t][lane];
       }
 #pragma unroll
-      for (int off = LPC / 2; off >= 1; off >>= 1) yp = yp + __shfl_xor(yp, off, 64);
-      if (qq == 0) s_y[t][c] = yp + s_dx[t][c];
-    }
-    __syncthreads();
-    for (int t = ts0; t < TT; t += TSTEP) {
-      if ((t0 + t < L) && dsv) st_act(Y + (b * L + t0 + t) * a.ld_y + ds, s_y[t][cs]);
-    }
-  }
-  if (a.h_last && dv) {
+      for (int u = 0; u < GT; ++u) {
+        if (tt + u < tmax) {
+          float yp = 0.0f;
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) a.h_last[(b * Di + d) * NS + qq * SPL + i] = h[i];
+          for (int i = 0; i < SPL; ++i) {
+            const float ab = __builtin_amdgcn_exp2f(dd[u].x * Al[i]);
+            h[i] = __builtin_fmaf(ab, h[i], dd[u].y * bq[u][i]);
+            if (!LOCAL) yp = __builtin_fmaf(cq[u][i], h[i], yp);
+          }
+          if (LOCAL) sum_dt += dd[u].x;
+          else s_yp[LOCAL ? 0 : w][LOCAL ? 0 : tt + u][lane] = yp;
+        }
+      }
+    }
+    if (!LOCAL) {
+      __syncthreads();
+      T* Y = (T*)a.y;
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) {
+        const int t = w + 4 * i;
+        if ((t0 + t < te) && dv) {
+          const float y = ((s_yp[0][t][lane] + s_yp[LOCAL ? 0 : 1][t][lane]) + s_yp[LOCAL ? 0 : 2][t][lane]) +
+                          s_yp[LOCAL ? 0 : 3][t][lane];
+          st_act(Y + (b * L + t0 + t) * a.ld_y + d, y + D_s * s_x[t][lane]);
+        }
+      }
+    }
   }
+  if (LOCAL) {
+    if (dv) {
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) ch.st[((b * ch.nchunks + chunk) * Di + d) * NS + w * SPL + i] = h[i];
+      if (w == 0) ch.sdt[(b * ch.nchunks + chunk) * Di + d] = sum_dt;
+    }
+  } else if (a.h_last && dv && chunk == ch.nchunks - 1) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) a.h_last[(b * Di + d) * NS + w * SPL + i] = h[i];
+  }
+}
+
+// Pass 2: for every (sequence, channel, state), compose the chunks in order.  Afterwards
+// st[b, c] holds the state entering chunk c + 1.
+__global__ __launch_bounds__(256) void k_scan_m1_combine(const float* __restrict__ A, const float* __restrict__ h0,
+                                                         float* __restrict__ st, const float* __restrict__ sdt,
+                                                         int64_t B, int64_t Di, int NS, int T) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * Di * NS) return;
+  const int64_t b = i / (Di * NS), dn = i % (Di * NS), d = dn / NS;
+  float h = h0 ? h0[i] : 0.0f;
+  const float a2 = A[dn] * LOG2E;
+  for (int c = 0; c + 1 < T; ++c) {
+    const int64_t si = ((b * T + c) * Di) * NS + dn;
+    const float P = __builtin_amdgcn_exp2f(a2 * sdt[(b * T + c) * Di + d]);
+    h = __builtin_fmaf(P, h, st[si]);
+    st[si] = h;
+  }
+}
+
+namespace {
+constexpr int kCPB = 64;  // channels per block of k_scan_m1
+constexpr int kTT = 32;   // time steps per tile of k_scan_m1
+
+struct ScanPlan {
+  int T = 1;
+  int64_t chunk_len = 0;
+  int cw = 0;             // dt code bytes per token (fused dt projection)
+  size_t off_deq = 0, off_st = 0, ws = 0;
+};
+
+// Chunk count: a pure function of the shape (so results do not depend on the device).
+// Blocks of batch x channel tiles below 512 (two per MI355X compute unit) are multiplied
+// by time chunks of at least 128 steps.
+ScanPlan plan_scan(const ScanArgs& a) {
+  ScanPlan p;
+  const int64_t blocks = cdiv(a.H, kCPB) * a.batch;
+  int64_t T = 1;
+  if (blocks < 512) {
+    T = cdiv(512, blocks);
+    const int64_t tmax = a.L / 128;
+    if (T > tmax) T = tmax;
+    if (T < 1) T = 1;
+  }
+  p.chunk_len = round_up(cdiv(a.L, T), kTT);
+  p.T = (int)cdiv(a.L, p.chunk_len);
+  const int64_t M = a.batch * a.L;
+  size_t off = 0;
+  if (a.dr) {
+    p.cw = 16 * (int)cdiv(a.R, 16);
+    off = round_up((int64_t)M * p.cw, 256);
+    p.off_deq = off;
+    off = round_up(off + (size_t)M * sizeof(double), 256);
+  }
+  p.off_st = off;
+  if (p.T > 1) off += (size_t)a.batch * p.T * a.H * (a.N + 1) * sizeof(float);
+  p.ws = off;
+  return p;
 }
 
 template <int NS, typename T>
-static void launch_m1_t(const ScanArgs& a, hipStream_t s) {
-  constexpr int LPC = NS / (NS < 4 ? NS : 4);
-  constexpr int CPB = 256 / LPC;
-  const dim3 grid((unsigned)cdiv(a.H, CPB), (unsigned)a.batch), block(256);
-  if (a.dr) hipLaunchKernelGGL((k_scan_m1<NS, T, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((k_scan_m1<NS, T, false>), grid, block, 0, s, a);
-}
-
-template <typename T>
-static hipError_t launch_m1_n(const ScanArgs& a, hipStream_t s) {
-  switch (a.N) {
-    case 4: launch_m1_t<4, T>(a, s); break;
-    case 8: launch_m1_t<8, T>(a, s); break;
-    case 16: launch_m1_t<16, T>(a, s); break;
-    case 32: launch_m1_t<32, T>(a, s); break;
-    case 64: launch_m1_t<64, T>(a, s); break;
-    default: return hipErrorInvalidValue;
+hipError_t launch_m1_t(const ScanArgs& a, void* ws, hipStream_t s) {
+  const ScanPlan p = plan_scan(a);
+  ChunkArgs ch{};
+  ch.chunk_len = p.chunk_len;
+  ch.nchunks = p.T;
+  if (p.T > 1) {
+    ch.st = (float*)((char*)ws + p.off_st);
+    ch.sdt = ch.st + (size_t)a.batch * p.T * a.H * NS;
   }
+  DtCodes dc{};
+  const bool fused = a.dr != nullptr;
+  if (fused) {
+    const int64_t M = a.batch * a.L;
+    int8_t* codes = (int8_t*)ws;
+    double* deq = (double*)((char*)ws + p.off_deq);
+    const int G = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
+    const int64_t tok_per_block = 4 * (64 / G);
+    hipLaunchKernelGGL(k_dt_codes, dim3((unsigned)cdiv(M, tok_per_block)), dim3(256), 0, s, a.dr, a.act_bf16, M,
+                       a.ld_dr, a.R, a.g_dt, a.eps, codes, p.cw, deq);
+    dc.codes = codes;
+    dc.deq = deq;
+  }
+  const unsigned gx = (unsigned)cdiv(a.H, kCPB), gy = (unsigned)a.batch;
+  if (p.T > 1) {
+    if (fused) hipLaunchKernelGGL((k_scan_m1<NS, T, true, true>), dim3(gx, gy, p.T - 1), dim3(256), 0, s, a, ch, dc);
+    else hipLaunchKernelGGL((k_scan_m1<NS, T, false, true>), dim3(gx, gy, p.T - 1), dim3(256), 0, s, a, ch, dc);
+    const int64_t n = a.batch * a.H * NS;
+    hipLaunchKernelGGL(k_scan_m1_combine, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, a.A, a.h0, ch.st, ch.sdt,
+                       a.batch, a.H, NS, p.T);
+  }
+  if (fused) hipLaunchKernelGGL((k_scan_m1<NS, T, true, false>), dim3(gx, gy, p.T), dim3(256), 0, s, a, ch, dc);
+  else hipLaunchKernelGGL((k_scan_m1<NS, T, false, false>), dim3(gx, gy, p.T), dim3(256), 0, s, a, ch, dc);
   return hipGetLastError();
 }
 
-hipError_t launch_scan_m1(const ScanArgs& a, hipStream_t s) {
+template <typename T>
+hipError_t launch_m1_n(const ScanArgs& a, void* ws, hipStream_t s) {
+  switch (a.N) {
+    case 4: return launch_m1_t<4, T>(a, ws, s);
+    case 8: return launch_m1_t<8, T>(a, ws, s);
+    case 16: return launch_m1_t<16, T>(a, ws, s);
+    case 32: return launch_m1_t<32, T>(a, ws, s);
+    case 64: return launch_m1_t<64, T>(a, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+size_t scan_m1_workspace(const ScanArgs& a) {
+  if (a.batch == 0 || a.L == 0) return 0;
+  return plan_scan(a).ws;
+}
+
+hipError_t launch_scan_m1(const ScanArgs& a, void* ws, hipStream_t s) {
   if (a.batch == 0 || a.L == 0) return hipSuccess;
-  return a.act_bf16 ? launch_m1_n<bf16_t>(a, s) : launch_m1_n<float>(a, s);
+  return a.act_bf16 ? launch_m1_n<bf16_t>(a, ws, s) : launch_m1_n<float>(a, ws, s);
 }
 
 }  // namespace ssm
