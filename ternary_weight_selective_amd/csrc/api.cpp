@@ -40,6 +40,7 @@ constexpr int64_t kMaxK = 4096;
 struct BLPlan {
   int64_t Kp = 0;
   bool norm = false;
+  bool rows = false;  // row-block kernel (A8, one scale per tensor, k <= 1024)
   size_t off_am = 0, total = 0;
 };
 
@@ -69,6 +70,11 @@ ssm_status bl_plan(const ssm_bitlinear_args* a, BLPlan* p) {
     if (!a->x_absmax && a->m > 0) return fail(SSM_ERR_NULL, "bitlinear: x_absmax is required for int8 input");
     if (a->k % 64 != 0 || a->ldx % 16 != 0 || !aligned(a->x, 16))
       return fail(SSM_ERR_UNSUPPORTED, "bitlinear: int8 input needs k %% 64 == 0, ldx %% 16 == 0, 16-byte alignment");
+    p->total = 0;
+    return SSM_OK;
+  }
+  if (a->act_bits == 8 && a->group_size == 0 && a->k <= kRowsMaxK) {
+    p->rows = true;
     p->total = 0;
     return SSM_OK;
   }
@@ -105,6 +111,13 @@ ssm_status bl_run(const ssm_bitlinear_args* a, const BLPlan& p, void* ws, hipStr
     return dev(launch_gemm_i8(g, s), "bitlinear gemm");
   }
   const int xb = a->x_dtype == SSM_BF16;
+  if (p.rows) {  // row-block kernel: norm, codes, contraction and epilogue in one launch
+    RowArgs r{};
+    r.x = a->x; r.ldx = a->ldx; r.x_bf16 = xb;
+    r.gain = a->norm_weight; r.eps = a->norm_eps;
+    r.dbg_xq = a->dbg_xq; r.dbg_absmax = a->dbg_absmax;
+    return dev(launch_bitlinear_rows(g, r, s), "bitlinear rows");
+  }
   if (a->act_bits == 8) {
     int8_t* q = (int8_t*)ws;
     float* am = a->dbg_absmax ? a->dbg_absmax : (float*)((char*)ws + p.off_am);
@@ -373,7 +386,7 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
     BLPlan bp;
     ssm_status s2 = bl_plan(&a, &bp);
     if (s2 != SSM_OK) return s2;
-    if (c->act_bits == 8) {  // codes in the shared buffer, absmax in its own region
+    if (c->act_bits == 8 && !bp.rows) {  // tiled path: codes in the shared buffer, absmax in its own region
       a.dbg_absmax = am;
     }
     return bl_run(&a, bp, base, stream);

@@ -227,6 +227,129 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     }
 }
 
+
+// ------------------------------------------------------------------------------------------
+// Row-block A8 BitLinear for k <= 1024 (the HBM-bound projections): a block normalises and
+// quantises BR = 16 token rows into LDS (one wave per row at a time, the fixed-order norm),
+// then its 4 waves contract them against every 16-column tile of W with int8 MFMA 16x16x64
+// (packed weights read from L2 and unpacked in registers) and write y from the
+// accumulators with the fp64 epilogue.  x is read once and y written once.
+namespace {
+constexpr int BR = 16;            // token rows per block (one MFMA row tile)
+constexpr int RPW = BR / 4;       // rows per wave in the norm phase
+}
+
+template <typename Tin, typename Tout, int KPL, bool DBG>
+__global__ __launch_bounds__(256) void k_bl_rows(GemmArgs g, RowArgs r) {
+  constexpr int KMAX = 64 * KPL;
+  constexpr int QS = KMAX + 16;               // LDS row stride (bytes): conflict-free b128 reads
+  constexpr int RB = KPL <= 8 ? RPW : (RPW < 4 ? RPW : 4);  // rows per load batch in the norm phase
+  __shared__ __align__(16) int8_t s_q[BR * QS];
+  __shared__ double s_deq[BR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * BR;
+  const int K = (int)g.K;
+  const Tin* X = (const Tin*)r.x;
+  const int nct = (int)cdiv(g.N, 16);
+  const double sw = (double)g.w_scale[0];
+  auto load_w = [&](int ct, uint32_t* dst) {
+    const int64_t n = (int64_t)ct * 16 + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < KPL; ++ks) {
+      const int64_t kw = (int64_t)ks * 4 + (lane >> 4);
+      dst[ks] = (n < g.N && kw < g.w_row_words) ? g.W[n * g.w_row_words + kw] : 0u;
+    }
+  };
+  uint32_t wv[KPL];
+  if (wave < nct) load_w(wave, wv);
+
+  // 1. norm + int8 codes: wave w owns rows RPW w .. RPW w + RPW - 1
+  for (int rb = 0; rb < RPW; rb += RB) {
+    float v[RB][KPL];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int64_t row = m0 + wave * RPW + rb + rr;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int k = lane + 64 * i;
+        v[rr][i] = (row < g.M && k < K) ? ld_act(X + row * r.ldx + k) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int lr = wave * RPW + rb + rr;
+      const int64_t row = m0 + lr;
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) s = __builtin_fmaf(v[rr][i], v[rr][i], s);
+      s = wave_sum_butterfly(s);
+      const float ms = __fdiv_rn(s, (float)K);
+      const float rs = __fdiv_rn(1.0f, sqrt_rn(ms + r.eps));
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int k = lane + 64 * i;
+        float t = v[rr][i] * rs;
+        if (r.gain) t = (k < K) ? t * r.gain[k] : 0.0f;
+        v[rr][i] = t;
+        m = fmaxf(m, fabsf(t));
+      }
+      m = wave_max(m);
+      const float sigma = __fdiv_rn(127.0f, fmaxf(m, 1e-5f));
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int k = lane + 64 * i;
+        float q = rintf(v[rr][i] * sigma);
+        q = fminf(fmaxf(q, -128.0f), 127.0f);
+        s_q[lr * QS + k] = (int8_t)(int)q;
+        if (DBG && r.dbg_xq && row < g.M && k < K) r.dbg_xq[row * K + k] = (int8_t)(int)q;
+      }
+      if (lane == 0) {
+        s_deq[lr] = (double)fmaxf(m, 1e-5f) / 127.0;
+        if (DBG && r.dbg_absmax && row < g.M) r.dbg_absmax[row] = m;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. contraction: wave w owns column tiles w, w + 4, ...; the next tile's packed weights
+  //    are in flight while the current tile runs (the first tile's before the norm phase).
+  for (int ct = wave; ct < nct; ct += 4) {
+    const int64_t n = (int64_t)ct * 16 + (lane & 15);
+    const bool nv = n < g.N;
+    uint32_t wn[KPL];
+    if (ct + 4 < nct) load_w(ct + 4, wn);
+    constexpr int RT = BR / 16;  // MFMA row tiles
+    v4i acc[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) acc[i] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KPL; ++ks) {
+      const v4i bfr = unpack16_i8(wv[ks]);
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const v4i af = *(const v4i*)(s_q + (i * 16 + (lane & 15)) * QS + ks * 64 + (lane >> 4) * 16);
+        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bfr, acc[i], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lr = i * 16 + (lane >> 4) * 4 + q;
+        const int64_t m = m0 + lr;
+        if (m < g.M && nv) {
+          double y = sw * (double)acc[i][q];
+          y = y * s_deq[lr];
+          store_out<Tout>(g, m, n, y);
+          if (DBG && g.dbg_acc) g.dbg_acc[m * g.N + n] = acc[i][q];
+        }
+      }
+#pragma unroll
+    for (int ks = 0; ks < KPL; ++ks) wv[ks] = wn[ks];
+  }
+}
+
 hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   const dim3 grid((unsigned)cdiv(a.N, BN), (unsigned)cdiv(a.M, BM)), block(256);
@@ -256,4 +379,33 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+}  // namespace ssm
+
+namespace ssm {
+template <typename Tin, typename Tout, int KPL>
+static void launch_rows_t(const GemmArgs& g, const RowArgs& r, hipStream_t s) {
+  const dim3 grid((unsigned)cdiv(g.M, BR)), block(256);
+  if (g.dbg_acc || r.dbg_xq || r.dbg_absmax)
+    hipLaunchKernelGGL((k_bl_rows<Tin, Tout, KPL, true>), grid, block, 0, s, g, r);
+  else
+    hipLaunchKernelGGL((k_bl_rows<Tin, Tout, KPL, false>), grid, block, 0, s, g, r);
+}
+
+template <typename Tin, typename Tout>
+static hipError_t launch_rows_k(const GemmArgs& g, const RowArgs& r, hipStream_t s) {
+  if (g.K <= 64) launch_rows_t<Tin, Tout, 1>(g, r, s);
+  else if (g.K <= 128) launch_rows_t<Tin, Tout, 2>(g, r, s);
+  else if (g.K <= 256) launch_rows_t<Tin, Tout, 4>(g, r, s);
+  else if (g.K <= 512) launch_rows_t<Tin, Tout, 8>(g, r, s);
+  else if (g.K <= 1024) launch_rows_t<Tin, Tout, 16>(g, r, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bitlinear_rows(const GemmArgs& g, const RowArgs& r, hipStream_t s) {
+  if (g.M == 0) return hipSuccess;
+  if (g.group != 0) return hipErrorInvalidValue;
+  if (r.x_bf16) return g.y_bf16 ? launch_rows_k<bf16_t, bf16_t>(g, r, s) : launch_rows_k<bf16_t, float>(g, r, s);
+  return g.y_bf16 ? launch_rows_k<float, bf16_t>(g, r, s) : launch_rows_k<float, float>(g, r, s);
+}
 }  // namespace ssm

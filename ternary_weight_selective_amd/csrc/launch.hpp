@@ -43,6 +43,20 @@ struct GemmArgs {
   int32_t* dbg_acc;       // [M, N] or null (A8)
 };
 hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s);
+
+// Row-block A8 BitLinear (norm + int8 codes in LDS + MFMA + epilogue in one kernel), k <= 1024,
+// one scale per tensor.
+struct RowArgs {
+  const void* x;          // rows [M, ldx] (fp32 or bf16)
+  int64_t ldx;
+  int x_bf16;
+  const float* gain;      // RMSNorm gains [K] or null
+  float eps;
+  int8_t* dbg_xq;         // [M, K] or null
+  float* dbg_absmax;      // [M] or null
+};
+hipError_t launch_bitlinear_rows(const GemmArgs& g, const RowArgs& r, hipStream_t s);
+constexpr int64_t kRowsMaxK = 1024;
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 
 // ---- selective scan (scan.hip: Mamba-1 kind; ssd.hip: SSD kind)

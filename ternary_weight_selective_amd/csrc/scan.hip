@@ -27,6 +27,8 @@
 // zero additions); in the scan each channel's int32 dot product with its ternary weight
 // row is v_dot4 instructions, and the dequantisation is the BitLinear epilogue's fp64
 // expression.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace ssm {
@@ -97,8 +99,9 @@ struct DtCodes {
 // writes its readout partial per (step, channel) to LDS; the partials are added in wave
 // order, plus D x, when the tile is stored.
 // LOCAL: pass 1 (zero start, no readout; writes the chunk's end state and sum(dt)).
-template <int NS, typename T, bool FUSED, bool LOCAL>
+template <int NS, typename T, int RW, bool LOCAL>
 __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, DtCodes dc) {
+  constexpr bool FUSED = RW > 0;  // dt from the low-rank input: RW 16-byte code words per token
   constexpr int SPL = NS / 4;     // states per lane
   constexpr int CPB = 64;         // channels per block
   constexpr int TT = 32;          // time steps per tile
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   // staging role: thread -> (channel lane, rows w, w + 4, ...)
   const float bias_s = (dv && a.delta_bias) ? a.delta_bias[d] : 0.0f;
   const float D_s = (dv && a.D) ? a.D[d] : 0.0f;
-  const int cw = FUSED ? 16 * (int)((a.R + 15) / 16) : 0;  // code bytes per token
+  constexpr int cw = 16 * RW;  // code bytes per token
 
   const T* X = (const T*)a.x;
   const T* DL = (const T*)a.delta;
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t wv = 0;
-      if (dv && q * 16 < cw) wv = a.w_dt[d * a.w_dt_row_words + q];
+      if (dv && q < RW) wv = a.w_dt[d * a.w_dt_row_words + q];
       wdt[q] = unpack16_i8(wv);
     }
   }
@@ -180,10 +183,10 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
       rc[i] = (ok && !LOCAL) ? ld_act((const T*)a.Cm + tok * a.ld_C + n) : 0.0f;
     }
     if (FUSED) {
-      const int nq = TT * cw / 4;  // 4-byte words of codes in the tile (<= 512)
+      constexpr int nq = TT * cw / 4;  // 4-byte words of codes in the tile (<= 512)
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int e = tid + 256 * k, t = e * 4 / cw;
+        const int e = tid + 256 * k, t = e * 4 / (cw > 0 ? cw : 1);
         rq[k] = (e < nq && t0 + t < te) ? ((const int*)dc.codes)[((b * L + t0) * cw) / 4 + e] : 0;
       }
       rf = (tid < TT && t0 + tid < te) ? dc.deq[b * L + t0 + tid] : 0.0;
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int e = tid + 256 * k;
-        if (e < TT * cw / 4) ((int*)&s_q[0][0])[(e * 4 / cw) * 16 + e % (cw / 4)] = rq[k];
+        if (e < TT * cw / 4) ((int*)&s_q[0][0])[(e * 4 / (cw > 0 ? cw : 1)) * 16 + e % (cw > 0 ? cw / 4 : 1)] = rq[k];
       }
       if (tid < TT) s_rf[FUSED ? tid : 0] = rf;
     }
@@ -227,11 +230,9 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
         int acc = 0;
         const int* qrow = (const int*)&s_q[FUSED ? t : 0][0];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (q * 16 < cw) {
+        for (int q = 0; q < RW; ++q)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(qrow[q * 4 + j], wdt[q][j], acc, false);
-          }
+          for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(qrow[q * 4 + j], wdt[q][j], acc, false);
         dtv = (float)((s_dt * (double)acc) * s_rf[FUSED ? t : 0]);
       } else {
         dtv = s_d[FUSED ? 0 : t][lane];
@@ -242,14 +243,15 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
     }
     __syncthreads();
     // 4. recurrence.  B and C of a step are the same for the whole wave (broadcast LDS reads at
-    //    immediate offsets); a group of GT steps issues all its LDS reads, then one wait.
+    //    immediate offsets); a group of G steps issues all its LDS reads, then one wait.
     const int tmax = (int)((te - t0) < TT ? (te - t0) : TT);
-    for (int tt = 0; tt < tmax; tt += GT) {
-      float bq[GT][SPL], cq[GT][SPL];
-      float2 dd[GT];
+    auto group = [&](int tt, auto gsz) {
+      constexpr int G = decltype(gsz)::value;
+      float bq[G][SPL], cq[G][SPL];
+      float2 dd[G];
 #pragma unroll
-      for (int u = 0; u < GT; ++u) {
-        const int t = (tt + u < tmax) ? tt + u : tmax - 1;
+      for (int u = 0; u < G; ++u) {
+        const int t = tt + u;
         if (SPL % 4 == 0) {
 #pragma unroll
           for (int i = 0; i < SPL; i += 4) {
@@ -270,19 +272,22 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
         dd[u] = s_dd[t][lane];
       }
 #pragma unroll
-      for (int u = 0; u < GT; ++u) {
-        if (tt + u < tmax) {
-          float yp = 0.0f;
+      for (int u = 0; u < G; ++u) {
+        float yp = 0.0f;
 #pragma unroll
-          for (int i = 0; i < SPL; ++i) {
-            const float ab = __builtin_amdgcn_exp2f(dd[u].x * Al[i]);
-            h[i] = __builtin_fmaf(ab, h[i], dd[u].y * bq[u][i]);
-            if (!LOCAL) yp = __builtin_fmaf(cq[u][i], h[i], yp);
-          }
-          if (LOCAL) sum_dt += dd[u].x;
-          else s_yp[LOCAL ? 0 : w][LOCAL ? 0 : tt + u][lane] = yp;
+        for (int i = 0; i < SPL; ++i) {
+          const float ab = __builtin_amdgcn_exp2f(dd[u].x * Al[i]);
+          h[i] = __builtin_fmaf(ab, h[i], dd[u].y * bq[u][i]);
+          if (!LOCAL) yp = i == 0 ? cq[u][0] * h[0] : __builtin_fmaf(cq[u][i], h[i], yp);
         }
+        if (LOCAL) sum_dt += dd[u].x;
+        else s_yp[LOCAL ? 0 : w][LOCAL ? 0 : tt + u][lane] = yp;
       }
+    };
+    if (tmax == TT) {
+      for (int tt = 0; tt < TT; tt += GT) group(tt, std::integral_constant<int, GT>{});
+    } else {
+      for (int t = 0; t < tmax; ++t) group(t, std::integral_constant<int, 1>{});
     }
     if (!LOCAL) {
       __syncthreads();
@@ -392,15 +397,28 @@ hipError_t launch_m1_t(const ScanArgs& a, void* ws, hipStream_t s) {
     dc.deq = deq;
   }
   const unsigned gx = (unsigned)cdiv(a.H, kCPB), gy = (unsigned)a.batch;
+  const int rw = fused ? p.cw / 16 : 0;
+  auto run = [&](auto rwc, bool local, unsigned gz) {
+    constexpr int RWc = decltype(rwc)::value;
+    if (local) hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, true>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+    else hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, false>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+  };
+  auto run_rw = [&](bool local, unsigned gz) {
+    switch (rw) {
+      case 0: run(std::integral_constant<int, 0>{}, local, gz); break;
+      case 1: run(std::integral_constant<int, 1>{}, local, gz); break;
+      case 2: run(std::integral_constant<int, 2>{}, local, gz); break;
+      case 3: run(std::integral_constant<int, 3>{}, local, gz); break;
+      default: run(std::integral_constant<int, 4>{}, local, gz); break;
+    }
+  };
   if (p.T > 1) {
-    if (fused) hipLaunchKernelGGL((k_scan_m1<NS, T, true, true>), dim3(gx, gy, p.T - 1), dim3(256), 0, s, a, ch, dc);
-    else hipLaunchKernelGGL((k_scan_m1<NS, T, false, true>), dim3(gx, gy, p.T - 1), dim3(256), 0, s, a, ch, dc);
+    run_rw(true, (unsigned)(p.T - 1));
     const int64_t n = a.batch * a.H * NS;
     hipLaunchKernelGGL(k_scan_m1_combine, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, a.A, a.h0, ch.st, ch.sdt,
                        a.batch, a.H, NS, p.T);
   }
-  if (fused) hipLaunchKernelGGL((k_scan_m1<NS, T, true, false>), dim3(gx, gy, p.T), dim3(256), 0, s, a, ch, dc);
-  else hipLaunchKernelGGL((k_scan_m1<NS, T, false, false>), dim3(gx, gy, p.T), dim3(256), 0, s, a, ch, dc);
+  run_rw(false, (unsigned)p.T);
   return hipGetLastError();
 }
 

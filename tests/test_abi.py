@@ -86,9 +86,12 @@ def test_bitlinear_rejects(kw, status):
 
 def test_bitlinear_workspace_checks():
     L = tws.lib()
-    a = _bl()
+    # k <= 1024, A8, one scale: the row-block kernel needs no workspace
+    assert L.ssm_bitlinear_workspace_bytes(ctypes.byref(_bl())) == 0
+    # k > 1024: normalised int8 rows and absmax go through the workspace
+    a = _bl(k=2048, ldx=2048)
     need = L.ssm_bitlinear_workspace_bytes(ctypes.byref(a))
-    assert need >= 16 * 64 + 16 * 4
+    assert need >= 16 * 2048 + 16 * 4
     assert L.ssm_bitlinear_fwd(ctypes.byref(a), None, 0, None) == WORKSPACE
     assert L.ssm_bitlinear_fwd(ctypes.byref(a), FAKE, need - 1, None) == WORKSPACE
     assert L.ssm_bitlinear_workspace_bytes(ctypes.byref(_bl(k=0))) == 0
