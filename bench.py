@@ -67,6 +67,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--stages-only", action="store_true", help="skip the headline loop (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run 3 plain device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -199,12 +201,12 @@ class StagePlan:
         self.scan_ws = torch.empty(self.scan_ws_bytes, dtype=torch.uint8, device=dev)
 
     def run(self, stream_handle, events=None):
+        """events: name -> (iterator of pre-created start events, iterator of end events)."""
         L = tws.lib()
         for st in self.stages:
             for name, a in st:
                 if events is not None:
-                    events[name][0].append(torch.cuda.Event(enable_timing=True))
-                    events[name][0][-1].record()
+                    next(events[name][0]).record()
                 if name == "scan":
                     rc = L.ssm_selective_scan_fwd(ctypes.byref(a), self.scan_ws.data_ptr(), self.scan_ws_bytes,
                                                   stream_handle)
@@ -214,8 +216,7 @@ class StagePlan:
                 if rc != 0:
                     raise tws.SsmError(rc, L.ssm_last_error().decode())
                 if events is not None:
-                    events[name][1].append(torch.cuda.Event(enable_timing=True))
-                    events[name][1][-1].record()
+                    next(events[name][1]).record()
 
 
 # ------------------------------------------------------------------ algorithmic cost per launch
@@ -353,8 +354,12 @@ def main():
         plan.run(sh)
     torch.cuda.synchronize()
     names = [n for n, _ in plan.stages[0]]
-    events = {n: ([], []) for n in names}
+    nper = args.steps * len(plan.stages)
+    ev = {n: ([torch.cuda.Event(enable_timing=True) for _ in range(nper)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(nper)]) for n in names}
+    events = {n: (iter(ev[n][0]), iter(ev[n][1])) for n in names}
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)  # let the host queue the instrumented launches ahead of the GPU
     s0.record()
     for _ in range(args.steps):
         plan.run(sh, events)
@@ -363,7 +368,7 @@ def main():
     stage_total_ms = s0.elapsed_time(s1) / args.steps
     stages = {}
     for n in names:
-        durs = [a.elapsed_time(b) for a, b in zip(*events[n])]
+        durs = [a.elapsed_time(b) for a, b in zip(*ev[n])]
         cost = stage_cost(cfg, n)
         avg_s = float(np.mean(durs)) * 1e-3
         stages[n] = {"avg_us": avg_s * 1e6, "launches": len(durs), "GBps": cost["bytes"] / avg_s / 1e9,
@@ -399,6 +404,14 @@ def main():
     roof["kernel"] = dominant
     roof["avg_launch_us"] = stages[dominant]["avg_us"]
     roof["hbm_frac"] = cost["bytes"] / avg_s / 1e9 / HBM_PEAK_GBPS
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if args.stages_only:
         print(json.dumps({"stages": stages, "stage_ms_per_step": stage_total_ms, "roofline": roof}))
