@@ -73,7 +73,7 @@ ssm_status bl_plan(const ssm_bitlinear_args* a, BLPlan* p) {
     p->total = 0;
     return SSM_OK;
   }
-  if (a->act_bits == 8 && a->group_size == 0 && a->k <= kRowsMaxK) {
+  if (a->act_bits == 8 && a->group_size == 0 && a->k <= kRowsMaxK && (!a->residual || a->n_out <= kRowsResN)) {
     p->rows = true;
     p->total = 0;
     return SSM_OK;

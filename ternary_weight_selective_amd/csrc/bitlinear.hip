@@ -229,124 +229,295 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
 
 
 // ------------------------------------------------------------------------------------------
-// Row-block A8 BitLinear for k <= 1024 (the HBM-bound projections): a block normalises and
-// quantises BR = 16 token rows into LDS (one wave per row at a time, the fixed-order norm),
-// then its 4 waves contract them against every 16-column tile of W with int8 MFMA 16x16x64
-// (packed weights read from L2 and unpacked in registers) and write y from the
-// accumulators with the fp64 epilogue.  x is read once and y written once.
+// Row-block A8 BitLinear for k <= 1024 (the HBM-bound projections), one scale per tensor.
+//
+// A persistent block of 8 waves walks over blocks of BR = 16 token rows (row block
+// blockIdx.x, then + gridDim.x, ...), in two roles:
+//   producers (waves 0-3) load x two row blocks ahead, normalise and quantise 4 rows each
+//     (a wave per row: the fixed-order norm) into one of two LDS code buffers, and stage the
+//     residual rows there too;
+//   consumers (waves 4-7) contract the codes against W with int8 MFMA 16x16x64 and write y
+//     with the fp64 epilogue.
+// One barrier per row block hands a buffer over; it orders LDS only, so the producers' loads
+// in flight and the consumers' stores in flight never wait for each other, and HBM sees
+// loads and stores of different row blocks at the same time.  x is read once, y written once.
+//
+// Producer scalar tail: the lane-partial sums and the absmax of a row are reduced across the
+// wave; the per-row scalar work (the correctly rounded divisions, the square root, the fp64
+// dequantisation factor) is done once for the wave's 4 rows, lane j taking row j mod 4, and
+// read back with readlane.
+//
+// Consumer c owns a contiguous run of 16-column tiles of W.  Their packed words sit in
+// registers, loaded once when the run fits in one round of up to TPR tiles (every projection
+// of the TriSSM and TernarySSM shapes but the widest), else round by round.  W is the MFMA's
+// A operand (rows = output columns), the int8 codes its B operand, so each lane ends with 4
+// consecutive outputs of one token row and stores them as one vector.  The 16-wide k chunks
+// are assigned to (k-step, lane quarter) so that a lane's KPL packed words are consecutive in
+// memory (one vector load per tile); A and B use the same assignment, so the int32 sums are
+// unchanged.
 namespace {
-constexpr int BR = 16;            // token rows per block (one MFMA row tile)
-constexpr int RPW = BR / 4;       // rows per wave in the norm phase
+template <typename Tout> struct Vec4;
+template <> struct Vec4<float> { typedef float4 type; };
+template <> struct Vec4<bf16_t> { typedef uint2 type; };
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-template <typename Tin, typename Tout, int KPL, bool DBG>
-__global__ __launch_bounds__(256) void k_bl_rows(GemmArgs g, RowArgs r) {
+// Block barrier that orders LDS accesses only (outstanding global loads and stores of the
+// waves are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+}  // namespace
+
+constexpr int kRowsBR = 16;       // token rows per row block of k_bl_rows
+
+// RES: a residual of at most kRowsResN columns, staged through registers and LDS.
+template <typename Tin, typename Tout, int KPL, bool RES, bool DBG>
+__global__ __launch_bounds__(512) void k_bl_rows(GemmArgs g, RowArgs r) {
+  constexpr int BR = kRowsBR;
+  constexpr int RPW = BR / 4;                 // rows per producer wave
   constexpr int KMAX = 64 * KPL;
-  constexpr int QS = KMAX + 16;               // LDS row stride (bytes): conflict-free b128 reads
-  constexpr int RB = KPL <= 8 ? RPW : (RPW < 4 ? RPW : 4);  // rows per load batch in the norm phase
-  __shared__ __align__(16) int8_t s_q[BR * QS];
-  __shared__ double s_deq[BR];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * BR;
+  constexpr int QS = KMAX + 16;               // LDS row stride of the codes (bytes)
+  constexpr int TPR = (32 / KPL) < 8 ? (32 / KPL) : 8;  // column tiles per weight round
+  constexpr bool PF2 = KPL <= 8;              // producers keep two row blocks of x in flight
+  constexpr int RN = RES ? kRowsResN / 64 : 1;  // residual elements per lane per row
+  __shared__ __align__(16) int8_t s_q[2][BR * QS];
+  __shared__ double s_deq[2][BR];
+  __shared__ __align__(16) float s_res[RES ? 2 * BR * kRowsResN : 1];  // staged residual rows
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nrb = cdiv(g.M, BR);
+  const int64_t G = gridDim.x, b = blockIdx.x;
+  const int niter = b < nrb ? (int)((nrb - 1 - b) / G + 1) : 0;
   const int K = (int)g.K;
-  const Tin* X = (const Tin*)r.x;
-  const int nct = (int)cdiv(g.N, 16);
-  const double sw = (double)g.w_scale[0];
-  auto load_w = [&](int ct, uint32_t* dst) {
-    const int64_t n = (int64_t)ct * 16 + (lane & 15);
-#pragma unroll
-    for (int ks = 0; ks < KPL; ++ks) {
-      const int64_t kw = (int64_t)ks * 4 + (lane >> 4);
-      dst[ks] = (n < g.N && kw < g.w_row_words) ? g.W[n * g.w_row_words + kw] : 0u;
-    }
-  };
-  uint32_t wv[KPL];
-  if (wave < nct) load_w(wave, wv);
+  const int N = (int)g.N;
 
-  // 1. norm + int8 codes: wave w owns rows RPW w .. RPW w + RPW - 1
-  for (int rb = 0; rb < RPW; rb += RB) {
-    float v[RB][KPL];
+  if (wave < 4) {
+    // ---------------- producer ----------------
+    const Tin* X = (const Tin*)r.x;
+    const Tout* RS = (const Tout*)g.residual;
+    const bool kfull = K == KMAX;
+    float gn[KPL];  // gain, 1 when absent (an exact multiplication)
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int64_t row = m0 + wave * RPW + rb + rr;
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        const int k = lane + 64 * i;
-        v[rr][i] = (row < g.M && k < K) ? ld_act(X + row * r.ldx + k) : 0.0f;
-      }
+    for (int i = 0; i < KPL; ++i) {
+      const int k = lane + 64 * i;
+      gn[i] = (r.gain && k < K) ? r.gain[k] : 1.0f;
     }
+    const int64_t last = b + (int64_t)(niter - 1) * G;  // a row block loaded again past the end
+    // x (and the residual) of the wave's rows of row block it; rows past M and columns past
+    // K read a valid element and are zeroed when used
+    auto load_x = [&](int it, float (&v)[RPW][KPL], float (&res)[RPW][RN]) {
+      int64_t rb = b + (int64_t)it * G;
+      rb = rb < last ? rb : last;
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int lr = wave * RPW + rb + rr;
-      const int64_t row = m0 + lr;
-      float s = 0.0f;
+      for (int rr = 0; rr < RPW; ++rr) {
+        int64_t row = rb * BR + wave * RPW + rr;
+        row = row < g.M ? row : g.M - 1;
+        const Tin* xr = X + row * r.ldx;
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) s = __builtin_fmaf(v[rr][i], v[rr][i], s);
-      s = wave_sum_butterfly(s);
-      const float ms = __fdiv_rn(s, (float)K);
-      const float rs = __fdiv_rn(1.0f, sqrt_rn(ms + r.eps));
-      float m = 0.0f;
+        for (int i = 0; i < KPL; ++i) {
+          int k = lane + 64 * i;
+          if (!kfull) k = k < K ? k : K - 1;
+          v[rr][i] = ld_act(xr + k);
+        }
+        if (RES) {
+          const Tout* rp = RS + row * g.ld_res;
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        const int k = lane + 64 * i;
-        float t = v[rr][i] * rs;
-        if (r.gain) t = (k < K) ? t * r.gain[k] : 0.0f;
-        v[rr][i] = t;
-        m = fmaxf(m, fabsf(t));
-      }
-      m = wave_max(m);
-      const float sigma = __fdiv_rn(127.0f, fmaxf(m, 1e-5f));
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) {
-        const int k = lane + 64 * i;
-        float q = rintf(v[rr][i] * sigma);
-        q = fminf(fmaxf(q, -128.0f), 127.0f);
-        s_q[lr * QS + k] = (int8_t)(int)q;
-        if (DBG && r.dbg_xq && row < g.M && k < K) r.dbg_xq[row * K + k] = (int8_t)(int)q;
-      }
-      if (lane == 0) {
-        s_deq[lr] = (double)fmaxf(m, 1e-5f) / 127.0;
-        if (DBG && r.dbg_absmax && row < g.M) r.dbg_absmax[row] = m;
-      }
-    }
-  }
-  __syncthreads();
-
-  // 2. contraction: wave w owns column tiles w, w + 4, ...; the next tile's packed weights
-  //    are in flight while the current tile runs (the first tile's before the norm phase).
-  for (int ct = wave; ct < nct; ct += 4) {
-    const int64_t n = (int64_t)ct * 16 + (lane & 15);
-    const bool nv = n < g.N;
-    uint32_t wn[KPL];
-    if (ct + 4 < nct) load_w(ct + 4, wn);
-    constexpr int RT = BR / 16;  // MFMA row tiles
-    v4i acc[RT];
-#pragma unroll
-    for (int i = 0; i < RT; ++i) acc[i] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int ks = 0; ks < KPL; ++ks) {
-      const v4i bfr = unpack16_i8(wv[ks]);
-#pragma unroll
-      for (int i = 0; i < RT; ++i) {
-        const v4i af = *(const v4i*)(s_q + (i * 16 + (lane & 15)) * QS + ks * 64 + (lane >> 4) * 16);
-        acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bfr, acc[i], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int lr = i * 16 + (lane >> 4) * 4 + q;
-        const int64_t m = m0 + lr;
-        if (m < g.M && nv) {
-          double y = sw * (double)acc[i][q];
-          y = y * s_deq[lr];
-          store_out<Tout>(g, m, n, y);
-          if (DBG && g.dbg_acc) g.dbg_acc[m * g.N + n] = acc[i][q];
+          for (int j = 0; j < RN; ++j) {
+            int n = lane + 64 * j;
+            n = n < N ? n : N - 1;
+            res[rr][j] = ld_act(rp + n);
+          }
         }
       }
+    };
+    auto produce = [&](int it, float (&v)[RPW][KPL], const float (&res)[RPW][RN]) {
+      const int buf = it & 1;
+      const int64_t m0 = (b + (int64_t)it * G) * BR;
+      int8_t* sq = s_q[buf];
+      if (RES) {  // residual rows of this row block into LDS (fp32 holds every Tout exactly)
+        float* sr = s_res + buf * BR * kRowsResN;
 #pragma unroll
-    for (int ks = 0; ks < KPL; ++ks) wv[ks] = wn[ks];
+        for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+          for (int j = 0; j < RN; ++j) sr[(wave * RPW + rr) * kRowsResN + lane + 64 * j] = res[rr][j];
+      }
+      float ss[RPW];
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const bool rv = m0 + wave * RPW + rr < g.M;
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          v[rr][i] = (rv && (kfull || lane + 64 * i < K)) ? v[rr][i] : 0.0f;
+          s = __builtin_fmaf(v[rr][i], v[rr][i], s);
+        }
+        ss[rr] = wave_sum_butterfly(s);
+      }
+      float sel = ss[0];
+#pragma unroll
+      for (int rr = 1; rr < RPW; ++rr) sel = (lane % RPW) == rr ? ss[rr] : sel;
+      const float rs_l = __fdiv_rn(1.0f, sqrt_rn(__fdiv_rn(sel, (float)K) + r.eps));
+      float mx[RPW];
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const float rs = readlane_f(rs_l, rr);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          const float t = (v[rr][i] * rs) * gn[i];
+          v[rr][i] = t;
+          m = fmaxf(m, fabsf(t));
+        }
+        mx[rr] = wave_max(m);
+      }
+      float msel = mx[0];
+#pragma unroll
+      for (int rr = 1; rr < RPW; ++rr) msel = (lane % RPW) == rr ? mx[rr] : msel;
+      const float mf = fmaxf(msel, 1e-5f);
+      const float sigma_l = __fdiv_rn(127.0f, mf);
+      if (lane < RPW) {
+        const int lr = wave * RPW + lane;
+        s_deq[buf][lr] = (double)mf / 127.0;
+        if (DBG && r.dbg_absmax && m0 + lr < g.M) r.dbg_absmax[m0 + lr] = msel;
+      }
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const int lr = wave * RPW + rr;
+        const float sigma = readlane_f(sigma_l, rr);
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          const int k = lane + 64 * i;
+          float q = rintf(v[rr][i] * sigma);
+          q = fminf(fmaxf(q, -128.0f), 127.0f);
+          sq[lr * QS + k] = (int8_t)(int)q;
+          if (DBG && r.dbg_xq && m0 + lr < g.M && k < K) r.dbg_xq[(m0 + lr) * K + k] = (int8_t)(int)q;
+        }
+      }
+    };
+    float va[RPW][KPL], vb[RPW][KPL], ra[RPW][RN], rb_[RPW][RN];
+    if (niter > 0) load_x(0, va, ra);
+    if (PF2) {
+      if (niter > 1) load_x(1, vb, rb_);
+      for (int it = 0; it < niter; it += 2) {
+        produce(it, va, ra);
+        lds_barrier();
+        load_x(it + 2, va, ra);
+        if (it + 1 >= niter) break;
+        produce(it + 1, vb, rb_);
+        lds_barrier();
+        load_x(it + 3, vb, rb_);
+      }
+    } else {
+      for (int it = 0; it < niter; ++it) {
+        produce(it, va, ra);
+        lds_barrier();
+        load_x(it + 1, va, ra);
+      }
+    }
+  } else {
+    // ---------------- consumer ----------------
+    const int cw = wave - 4;
+    const int nct = (int)cdiv(g.N, 16);
+    const int tpw = (nct + 3) / 4;
+    const int ct0 = cw * tpw;
+    const int ct1 = (ct0 + tpw < nct) ? ct0 + tpw : nct;
+    const bool one_round = ct1 - ct0 <= TPR;
+    const double sw = (double)g.w_scale[0];
+    const int vb_ = (int)sizeof(typename Vec4<Tout>::type);
+    const bool vec_ok = (g.ldy % 4 == 0) && (((uintptr_t)g.y) % vb_ == 0) &&
+                        (!g.bias || ((uintptr_t)g.bias) % 16 == 0);
+    const int kq = lane >> 4, lm = lane & 15;
+    const bool wvec = (KPL % 4 == 0) && (g.w_row_words == 4 * KPL) && (((uintptr_t)g.W) % 16 == 0);
+    uint32_t wv[TPR][KPL];
+    // packed words of tiles c .. c + TPR - 1: lane (n, kq) holds words kq KPL .. kq KPL + KPL - 1
+    // of row n (k chunk kq KPL + ks at k-step ks)
+    auto load_round = [&](int c) {
+#pragma unroll
+      for (int j = 0; j < TPR; ++j) {
+        const int64_t n = (int64_t)(c + j) * 16 + lm;
+        const bool ok = (c + j < ct1) && n < g.N;
+        const uint32_t* wr = g.W + n * g.w_row_words + kq * KPL;
+        if (KPL % 4 == 0 && wvec) {
+#pragma unroll
+          for (int v4 = 0; v4 < KPL / 4; ++v4) {
+            const uint4 u = ok ? ((const uint4*)wr)[v4] : make_uint4(0u, 0u, 0u, 0u);
+            wv[j][4 * v4] = u.x; wv[j][4 * v4 + 1] = u.y; wv[j][4 * v4 + 2] = u.z; wv[j][4 * v4 + 3] = u.w;
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KPL; ++ks) {
+            const int64_t kw = (int64_t)kq * KPL + ks;
+            wv[j][ks] = (ok && kw < g.w_row_words) ? wr[ks] : 0u;
+          }
+        }
+      }
+    };
+    if (ct0 < ct1) load_round(ct0);
+    for (int it = 0; it < niter; ++it) {
+      lds_barrier();
+      const int buf = it & 1;
+      const int64_t m0 = (b + (int64_t)it * G) * BR;
+      const int64_t m = m0 + lm;
+      const double deq = s_deq[buf][lm];
+      const float* sr = s_res + (RES ? buf * BR * kRowsResN + lm * kRowsResN : 0);
+      v4i bq[KPL];  // codes of row lm, k chunk kq KPL + ks
+#pragma unroll
+      for (int ks = 0; ks < KPL; ++ks) bq[ks] = *(const v4i*)(s_q[buf] + lm * QS + (kq * KPL + ks) * 16);
+      for (int c = ct0; c < ct1; c += TPR) {
+        if (!one_round && !(c == ct0 && it == 0)) load_round(c);
+        v4i acc[TPR];
+#pragma unroll
+        for (int j = 0; j < TPR; ++j) {
+          acc[j] = v4i{0, 0, 0, 0};
+          if (c + j < ct1) {
+#pragma unroll
+            for (int ks = 0; ks < KPL; ++ks)
+              acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16_i8(wv[j][ks]), bq[ks], acc[j], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < TPR; ++j) {
+          const int64_t n = (int64_t)(c + j) * 16 + kq * 4;
+          if (c + j < ct1 && m < g.M && n < g.N) {
+            double y[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) y[q] = (sw * (double)acc[j][q]) * deq;
+            if (vec_ok && n + 3 < g.N) {
+              if (g.bias) {
+                const float4 bb = *(const float4*)(g.bias + n);
+                y[0] += bb.x; y[1] += bb.y; y[2] += bb.z; y[3] += bb.w;
+              }
+              if (RES) {
+                const float4 rr4 = *(const float4*)(sr + n);
+                y[0] += rr4.x; y[1] += rr4.y; y[2] += rr4.z; y[3] += rr4.w;
+              }
+              Tout o[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) st_act(&o[q], (float)y[q]);
+              *(typename Vec4<Tout>::type*)((Tout*)g.y + m * g.ldy + n) = *(const typename Vec4<Tout>::type*)o;
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                if (n + q >= g.N) continue;
+                double v = y[q];
+                if (g.bias) v += (double)g.bias[n + q];
+                if (RES) v += (double)sr[n + q];
+                st_act((Tout*)g.y + m * g.ldy + n + q, (float)v);
+              }
+            }
+            if (DBG && g.dbg_acc)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (n + q < g.N) g.dbg_acc[m * g.N + n + q] = acc[j][q];
+          }
+        }
+      }
+    }
   }
 }
 
@@ -382,13 +553,19 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
 }  // namespace ssm
 
 namespace ssm {
+// Persistent grid: one block of 8 waves per compute unit is enough to keep both roles busy.
+// Results do not depend on it (every row is computed the same way by whichever block owns it).
+constexpr int64_t kRowsGrid = 256;
+
 template <typename Tin, typename Tout, int KPL>
 static void launch_rows_t(const GemmArgs& g, const RowArgs& r, hipStream_t s) {
-  const dim3 grid((unsigned)cdiv(g.M, BR)), block(256);
-  if (g.dbg_acc || r.dbg_xq || r.dbg_absmax)
-    hipLaunchKernelGGL((k_bl_rows<Tin, Tout, KPL, true>), grid, block, 0, s, g, r);
-  else
-    hipLaunchKernelGGL((k_bl_rows<Tin, Tout, KPL, false>), grid, block, 0, s, g, r);
+  const int64_t nrb = cdiv(g.M, kRowsBR);
+  const dim3 grid((unsigned)(nrb < kRowsGrid ? nrb : kRowsGrid)), block(512);
+  const bool dbg = g.dbg_acc || r.dbg_xq || r.dbg_absmax;
+#define SSM_ROWS(RES, DBG) hipLaunchKernelGGL((k_bl_rows<Tin, Tout, KPL, RES, DBG>), grid, block, 0, s, g, r)
+  if (g.residual) { if (dbg) SSM_ROWS(true, true); else SSM_ROWS(true, false); }
+  else { if (dbg) SSM_ROWS(false, true); else SSM_ROWS(false, false); }
+#undef SSM_ROWS
 }
 
 template <typename Tin, typename Tout>

@@ -57,6 +57,7 @@ struct RowArgs {
 };
 hipError_t launch_bitlinear_rows(const GemmArgs& g, const RowArgs& r, hipStream_t s);
 constexpr int64_t kRowsMaxK = 1024;
+constexpr int kRowsResN = 512;  // widest residual the row-block kernel stages (more: tiled path)
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 
 // ---- selective scan (scan.hip: Mamba-1 kind; ssd.hip: SSD kind)
