@@ -373,7 +373,7 @@ __global__ __launch_bounds__(512) void k_bl_rows(GemmArgs g, RowArgs r) {
           v[rr][i] = t;
           m = fmaxf(m, fabsf(t));
         }
-        mx[rr] = wave_max(m);
+        mx[rr] = wave_absmax(m);
       }
       float msel = mx[0];
 #pragma unroll

@@ -31,19 +31,49 @@ template <typename T> __device__ __forceinline__ void st_act(T* p, float v);
 template <> __device__ __forceinline__ void st_act<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st_act<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// Cross-lane moves.  ds_swizzle in bit-mask mode: lane j of each 32-lane half reads lane
+// j ^ 16.  DPP (data-parallel primitives): a rotation of each row of 16 lanes, and quad
+// permutations.
+__device__ __forceinline__ float swz_xor16(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowRor8 = 0x128, kDppRowRor4 = 0x124;
+constexpr int kDppXor2 = 0x4E, kDppXor1 = 0xB1;  // quad_perm [2,3,0,1], [1,0,3,2]
+
 // Sum over the 64 lanes of a wave as six rounds in which lane j adds lane j ^ d,
-// d = 32, 16, 8, 4, 2, 1.  fp32 addition is commutative, so every lane ends with the
-// same value and the order of the additions is fixed.
+// d = 32, 16, 8, 4, 2, 1.  fp32 addition is commutative, so every lane ends with the same
+// value and the order of the additions is fixed.  After the rounds at d = 32 and 16 the lanes
+// j, j ^ 16, j ^ 32, j ^ 48 hold equal values, and after d = 8 also j ^ 8: rotating each row
+// of 16 lanes by 8 (then by 4) therefore reads a lane holding exactly the value of lane j ^ 8
+// (then j ^ 4), so the rotations add the same operands as the xor rounds.
 __device__ __forceinline__ float wave_sum_butterfly(float s) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) s = s + __shfl_xor(s, d, 64);
+  s = s + __shfl_xor(s, 32, 64);
+  s = s + swz_xor16(s);
+  s = s + dpp_f<kDppRowRor8>(s);
+  s = s + dpp_f<kDppRowRor4>(s);
+  s = s + dpp_f<kDppXor2>(s);
+  s = s + dpp_f<kDppXor1>(s);
   return s;
 }
 
-__device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-  return m;
+// Maximum over the 64 lanes of non-negative values (absolute values); every lane ends with
+// it.  For non-negative floats the order of the bit patterns as unsigned integers is the
+// numeric order, so the maximum is taken on the bit patterns (exact in any order).
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float wave_absmax(float m) {
+  uint32_t u = __float_as_uint(m);
+  u = max(u, (uint32_t)__shfl_xor((int)u, 32, 64));
+  u = max(u, (uint32_t)__builtin_amdgcn_ds_swizzle((int)u, 0x401F));
+  u = max(u, dpp_u<kDppRowRor8>(u));
+  u = max(u, dpp_u<kDppRowRor4>(u));
+  u = max(u, dpp_u<kDppXor2>(u));
+  u = max(u, dpp_u<kDppXor1>(u));
+  return __uint_as_float(u);
 }
 
 // 16 ternary codes of one packed word -> 16 int8 in weight order.  Dword j of the

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void k_norm(const Tin* __restrict__ x, int64_t
     m = fmaxf(m, fabsf(t));
   }
   if (MODE == 8) {
-    m = wave_max(m);
+    m = wave_absmax(m);
     const float sigma = __fdiv_rn(127.0f, fmaxf(m, 1e-5f));
     int8_t* qr = q + row * ldo;
 #pragma unroll
