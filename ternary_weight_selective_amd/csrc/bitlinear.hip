@@ -18,6 +18,10 @@ constexpr int BM = 64, BN = 64, BK = 64;
 constexpr int LDS_I8 = BK + 16;   // int8 row stride of the LDS tiles (bytes)
 constexpr int LDS_BF = BK + 8;    // bf16 row stride (elements)
 
+template <typename Tout> struct Vec4;
+template <> struct Vec4<float> { typedef float4 type; };
+template <> struct Vec4<bf16_t> { typedef uint2 type; };
+
 template <typename Tout, typename V>
 __device__ __forceinline__ void store_out(const GemmArgs& a, int64_t m, int64_t n, V v) {
   if (a.bias) v += (V)a.bias[n];
@@ -109,6 +113,140 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
         if (DBG) a.dbg_acc[m * a.N + n] = GROUPED ? tot[i][j][r] : acc[i][j][r];
       }
     }
+}
+
+// ------------------------------------------------------------------------------------------
+// Large-tile A8 contraction, one scale per tensor: the MFMA-bound shapes (k > 1024, e.g. the
+// Mamba-2 projections (8192, 4416, 2048) and (8192, 2048, 4096)).
+//
+// Block tile 256 tokens x BN outputs and 4 waves, one per SIMD, each owning 128 tokens x BN / 2
+// outputs as 8 x BN / 32 MFMA 16x16x64 tiles with the int32 accumulators in the AGPRs, so that
+// every operand fragment read from LDS feeds 8 (weights) or BN / 32 (activations) MFMAs.
+// Per 64-deep k step the next step's activation chunks and packed weight words are loaded into
+// registers while the current step is contracted; then the activations are stored to the other
+// LDS buffer and the weights unpacked into it as int8 (each packed word once per block: the
+// 2-bit -> int8 unpacking costs about 11 vector instructions per 16 weights, too much to repeat
+// in every wave that uses a fragment).  W is the A operand (rows = outputs) and the
+// activations the B operand, so a lane ends with 4 consecutive outputs of one token and stores
+// them as one vector.
+//
+// Tile order: blocks are dealt to the 8 XCDs round-robin, so block b works on tile
+// (b mod 8) * ceil(T / 8) + b / 8: each XCD takes a contiguous run of tiles (outputs
+// fastest) and its L2 serves the activation rows of few token tiles.
+template <typename Tout, int BN, bool DBG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_i8_big(GemmArgs a) {
+  constexpr int BMT = 256, BKT = 64, AS = BKT + 16;
+  constexpr int WN = BN / 2, NT = WN / 16, MT = 8;
+  constexpr int CPT = BMT * 4 / 256;   // activation chunks (16 bytes) per thread and k step
+  constexpr int WPT = BN * 4 / 256;    // packed weight words per thread and k step
+  __shared__ __align__(16) int8_t s_a[2][BMT * AS];
+  __shared__ __align__(16) int8_t s_w[2][BN * AS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int kq = lane >> 4, l16 = lane & 15;
+  const int64_t nb = cdiv(a.N, BN), T = cdiv(a.M, BMT) * nb;
+  const int64_t chunk = cdiv(T, 8);
+  const int64_t li = blockIdx.x / 8, t = (blockIdx.x % 8) * chunk + li;
+  if (li >= chunk || t >= T) return;
+  const int64_t m0 = (t / nb) * BMT, n0 = (t % nb) * BN;
+  const int8_t* A = (const int8_t*)a.A;
+  v4i pa[CPT];
+  uint32_t pw[WPT];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int e = tid + 256 * c, r = e >> 2, q = e & 3;
+      const int64_t gm = m0 + r;
+      pa[c] = gm < a.M ? *(const v4i*)(A + gm * a.lda + k0 + q * 16) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < WPT; ++c) {
+      const int e = tid + 256 * c, r = e >> 2, q = e & 3;
+      const int64_t gn = n0 + r, kw = k0 / 16 + q;
+      pw[c] = (gn < a.N && kw < a.w_row_words) ? a.W[gn * a.w_row_words + kw] : 0u;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int e = tid + 256 * c, r = e >> 2, q = e & 3;
+      *(v4i*)(&s_a[buf][r * AS + q * 16]) = pa[c];
+    }
+#pragma unroll
+    for (int c = 0; c < WPT; ++c) {
+      const int e = tid + 256 * c, r = e >> 2, q = e & 3;
+      *(v4i*)(&s_w[buf][r * AS + q * 16]) = unpack16_i8(pw[c]);
+    }
+  };
+  v4i acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  const int nk = (int)(a.Kp / BKT);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) load((int64_t)(ks + 1) * BKT);
+    v4i wf[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) wf[j] = *(const v4i*)(&s_w[buf][(wn * WN + j * 16 + l16) * AS + kq * 16]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const v4i bfr = *(const v4i*)(&s_a[buf][(wm * 128 + i * 16 + l16) * AS + kq * 16]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[j], bfr, acc[i][j], 0, 0, 0);
+    }
+    if (ks + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds token l16 of each token tile and outputs 4 kq .. 4 kq + 3 of each
+  // output tile
+  const double sw = (double)a.w_scale[0];
+  const int vb = (int)sizeof(typename Vec4<Tout>::type);
+  const bool vec_ok = (a.ldy % 4 == 0) && (((uintptr_t)a.y) % vb == 0) &&
+                      (!a.bias || ((uintptr_t)a.bias) % 16 == 0);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int64_t m = m0 + wm * 128 + i * 16 + l16;
+    if (m >= a.M) continue;
+    const double deq = (double)fmaxf(a.absmax[m], 1e-5f) / 127.0;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t n = n0 + wn * WN + j * 16 + kq * 4;
+      if (n >= a.N) continue;
+      double y[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = (sw * (double)acc[i][j][q]) * deq;
+      if (vec_ok && n + 3 < a.N) {
+        if (a.bias) {
+          const float4 bb = *(const float4*)(a.bias + n);
+          y[0] += bb.x; y[1] += bb.y; y[2] += bb.z; y[3] += bb.w;
+        }
+        if (a.residual) {
+          const Tout* rp = (const Tout*)a.residual + m * a.ld_res + n;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] += (double)ld_act(rp + q);
+        }
+        Tout o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st_act(&o[q], (float)y[q]);
+        *(typename Vec4<Tout>::type*)((Tout*)a.y + m * a.ldy + n) = *(const typename Vec4<Tout>::type*)o;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (n + q < a.N) store_out<Tout>(a, m, n + q, y[q]);
+      }
+      if (DBG)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (n + q < a.N) a.dbg_acc[m * a.N + n + q] = acc[i][j][q];
+    }
+  }
 }
 
 // A16: same tiling; bf16 MFMA 16x16x32, two per 64-deep K-step.  With SPLIT each activation
@@ -256,9 +394,6 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
 // memory (one vector load per tile); A and B use the same assignment, so the int32 sums are
 // unchanged.
 namespace {
-template <typename Tout> struct Vec4;
-template <> struct Vec4<float> { typedef float4 type; };
-template <> struct Vec4<bf16_t> { typedef uint2 type; };
 
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
@@ -521,8 +656,26 @@ __global__ __launch_bounds__(512) void k_bl_rows(GemmArgs g, RowArgs r) {
   }
 }
 
+// Output-tile width of k_gemm_i8_big: 256 or 192, whichever leaves fewer padded columns.
+static int big_bn(int64_t N) { return (cdiv(N, 192) * 192 - N) < (cdiv(N, 256) * 256 - N) ? 192 : 256; }
+
+template <typename Tout, bool DBG>
+static void launch_big(const GemmArgs& a, hipStream_t s) {
+  const int bn = big_bn(a.N);
+  const int64_t T = cdiv(a.M, 256) * cdiv(a.N, bn);
+  const dim3 grid((unsigned)(8 * cdiv(T, 8))), block(256);
+  if (bn == 192) hipLaunchKernelGGL((k_gemm_i8_big<Tout, 192, DBG>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((k_gemm_i8_big<Tout, 256, DBG>), grid, block, 0, s, a);
+}
+
 hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (a.group == 0) {
+    const bool d = a.dbg_acc != nullptr;
+    if (a.y_bf16) { if (d) launch_big<bf16_t, true>(a, s); else launch_big<bf16_t, false>(a, s); }
+    else { if (d) launch_big<float, true>(a, s); else launch_big<float, false>(a, s); }
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)cdiv(a.N, BN), (unsigned)cdiv(a.M, BM)), block(256);
   const bool g = a.group > 0, d = a.dbg_acc != nullptr;
 #define SSM_GEMM_I8(T, G, D) hipLaunchKernelGGL((k_gemm_i8<T, G, D>), grid, block, 0, s, a)

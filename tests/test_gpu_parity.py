@@ -74,6 +74,8 @@ BL_CASES = [  # (m, k, n, group, act_bits, x dtype, y dtype)
     (64, 4096, 256, 128, 16, "bf16", "bf16"),  # mamba2_ssd out_proj rows
     (50, 256, 64, 0, 16, "f32", "f32"),      # A16 per tensor
     (1, 100, 70, 0, 8, "f32", "f32"),        # one row, ragged k
+    (100, 2048, 4416, 0, 8, "bf16", "bf16"),  # mamba2_a8 in_proj (tiled int8 path)
+    (77, 4096, 2048, 0, 8, "bf16", "bf16"),   # mamba2_a8 out_proj
 ]
 
 

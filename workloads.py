@@ -13,6 +13,9 @@ The five workloads follow the model shapes of the pages:
                   activations with an fp32 scan state, 8 layers
   * mamba2_ssd    a Mamba-2 1.3B-shaped W1.58A16 SSD mixer (the Ternary Mamba
                   abstract): per-group (128) ternary scales, bf16 activations
+  * mamba2_a8     the same SSD mixer shape with int8 absmax activations and one scale
+                  per tensor: the A8 contraction at its largest shapes, (8192, 4416, 2048)
+                  and (8192, 2048, 4096), where it is bound by the int8 matrix cores
 Distributions: activations u ~ N(0,1); latent weights ~ N(0, 0.02); A = -exp(U[ln 1,
 ln 16]) per (channel, state) (per head for SSD); D ~ N(1, 0.1); dt_bias ~ N(-2, 1);
 RMSNorm gains are ones.  No dataset is read: these stand in for the activations of
@@ -75,8 +78,10 @@ CONFIGS = {
                                  dt_rank=32, act_dtype="bf16"),
     "mamba2_ssd": MixerConfig("mamba2_ssd", SSD, 2048, 4096, 128, batch=4, seqlen=2048, nheads=64, headdim=64,
                               act_dtype="bf16", act_bits=16, group_size=128),
+    "mamba2_a8": MixerConfig("mamba2_a8", SSD, 2048, 4096, 128, batch=4, seqlen=2048, nheads=64, headdim=64,
+                             act_dtype="bf16", act_bits=8, group_size=0),
 }
-CONFIG_ORDER = ["bitssm_tiny", "trissm", "long_scan", "ternaryssm50m", "mamba2_ssd"]
+CONFIG_ORDER = ["bitssm_tiny", "trissm", "long_scan", "ternaryssm50m", "mamba2_ssd", "mamba2_a8"]
 
 
 def rng(seed: int) -> np.random.Generator:
