@@ -2,9 +2,10 @@
 // on; the Mamba-2 shape of the Ternary Mamba abstract): scalar A per head, a state of
 // headdim x d_state per head, B and C shared by all heads.
 //
-// Recurrent evaluation: each lane owns 8 states of one (head, channel) pair; the
-// d_state / 8 lanes of a channel add their readout partials with xor shuffles.  The decay
-// exp(dt A) is one value per (token, head) and is computed once per LDS tile.
+// Two evaluations: the chunked one on the matrix cores (below, bf16 activations, headdim 64,
+// d_state 64 or 128), and a recurrent one for every other shape: each lane owns 8 states of
+// one (head, channel) pair; the d_state / 8 lanes of a channel add their readout partials with
+// xor shuffles.  The decay exp(dt A) is one value per (token, head), computed once per tile.
 #include "launch.hpp"
 
 namespace ssm {
@@ -100,6 +101,282 @@ __global__ __launch_bounds__(256) void k_scan_ssd_rec(ScanArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Chunked evaluation on the matrix cores (the state-space duality of "Transformers are
+// SSMs"): bf16 activations, headdim 64, d_state 64 or 128, chunks of Q = 64 steps.
+// A block owns one (sequence, head) and walks its chunks in order, the P x N state in MFMA
+// accumulators.  With cs_t the inclusive cumulative sum of dt_s A inside a chunk and h_in the
+// state entering it, for t in the chunk
+//   y_t = sum_{s <= t} (C_t . B_s) exp(cs_t - cs_s) dt_s x_s  +  exp(cs_t) C_t h_in^T  +  D x_t
+//   h_out = exp(cs_end) h_in + sum_s exp(cs_end - cs_s) dt_s x_s B_s^T
+// which is the recurrence h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t, y_t = C_t h_t + D x_t
+// regrouped.  Per chunk (4 waves, wave w owning chunk rows 16 w .. 16 w + 15):
+//   G = C B^T (bf16 x bf16, exact products, fp32 sums), then the masked, decayed M (fp32);
+//   Y = M X and Z = C h_in^T; y = Y + exp(cs_t) Z + D x;
+//   h = exp(cs_end) h + (w X)^T B, w_s = exp(cs_end - cs_s) dt_s.
+// The fp32 operands (M, h_in, w X) enter the bf16 MFMAs as two bf16 terms (value = hi + lo,
+// about 16 significant bits), the bf16 activations as they are.
+// LDS holds the chunk's x, x^T, B, B^T, C (bf16), the waves' M rows and h_in (hi, lo).
+namespace {
+__device__ __forceinline__ uint16_t bf_bits(float f) { return f32_to_bf16(f); }
+__device__ __forceinline__ float bf_val(uint16_t b) { return bf16_to_f32(b); }
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// softplus(v) = log(1 + e^v) (the identity above 20) on the hardware exp2 / log2; below
+// e^v = 1e-4 the series e^v (1 - e^v / 2).
+__device__ __forceinline__ float softplus_hw(float v) {
+  const float z = exp_hw(v);
+  const float big = 0.69314718055994531f * __builtin_amdgcn_logf(1.0f + z);
+  const float small = z * __builtin_fmaf(-0.5f, z, 1.0f);
+  const float r = z < 1e-4f ? small : big;
+  return v > 20.0f ? v : r;
+}
+}  // namespace
+
+constexpr int kSsdQ = 64, kSsdP = 64;
+
+template <int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_ssd_chunk(ScanArgs a) {
+  constexpr int Q = kSsdQ, P = kSsdP;
+  constexpr int XS = Q + 8;          // row stride (elements) of the [.][Q] arrays
+  constexpr int NSP = NS + 8;        // row stride of the [.][NS] arrays
+  constexpr int NTN = NS / 16;       // 16-wide n tiles
+  constexpr int KN = NS / 32;        // k steps over n
+  __shared__ __align__(16) uint16_t sX[Q * XS];        // x  [t][p]
+  __shared__ __align__(16) uint16_t sXT[P * XS];       // x^T [p][s]
+  __shared__ __align__(16) uint16_t sB[Q * NSP];       // B  [s][n]
+  __shared__ __align__(16) uint16_t sBT[NS * XS];      // B^T [n][s]
+  __shared__ __align__(16) uint16_t sC[Q * NSP];       // C  [t][n]
+  __shared__ __align__(16) uint16_t sM[4][2][16 * XS]; // per wave: M rows (hi, lo) [t][s]
+  __shared__ __align__(16) uint16_t sH[2][P * NSP];    // h_in (hi, lo) [p][n]
+  __shared__ float s_dt[Q], s_cs[Q];
+  __shared__ float s_w[Q], s_et[Q];  // exp(cs_end - cs_s) dt_s and exp(cs_t)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = lane >> 4, l16 = lane & 15;
+  const int64_t L = a.L, H = a.H;
+  const int64_t hd = blockIdx.x % H, b = blockIdx.x / H;
+  const float A_h = a.A[hd];
+  const float bias_h = a.delta_bias ? a.delta_bias[hd] : 0.0f;
+  const float D_h = a.D ? a.D[hd] : 0.0f;
+  const bf16_t* X = (const bf16_t*)a.x;
+  const bf16_t* Bm = (const bf16_t*)a.Bm;
+  const bf16_t* Cm = (const bf16_t*)a.Cm;
+  const bf16_t* DT = (const bf16_t*)a.delta;
+  bf16_t* Y = (bf16_t*)a.y;
+
+  // state: lane holds h[p = 16 w + 4 kq + r][n = 16 jn + l16]
+  v4f h[NTN];
+#pragma unroll
+  for (int jn = 0; jn < NTN; ++jn)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int pp = 16 * w + 4 * kq + r, n = 16 * jn + l16;
+      h[jn][r] = a.h0 ? a.h0[((b * H + hd) * P + pp) * NS + n] : 0.0f;
+    }
+  auto write_h = [&]() {
+#pragma unroll
+    for (int jn = 0; jn < NTN; ++jn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * w + 4 * kq + r, n = 16 * jn + l16;
+        const uint16_t hi = bf_bits(h[jn][r]);
+        sH[0][pp * NSP + n] = hi;
+        sH[1][pp * NSP + n] = bf_bits(h[jn][r] - bf_val(hi));
+      }
+  };
+  write_h();
+
+  // chunk loads, 16-byte chunks with the step index fastest across the lanes (lane = step t,
+  // chunk column q = wave + 4 i), so that the transposed LDS copies are written along rows
+  constexpr int XC = Q * P / 8 / 256, BC = Q * NS / 8 / 256;
+  v4i px[XC], pb[BC], pc[BC];
+  float pdt = 0.0f;
+  auto load = [&](int64_t c0) {
+    const bool ok = c0 + lane < L;
+    const int64_t tok = b * L + c0 + lane;
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int q = w + 4 * i;
+      px[i] = ok ? *(const v4i*)(X + tok * a.ld_x + hd * P + q * 8) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < BC; ++i) {
+      const int q = w + 4 * i;
+      pb[i] = ok ? *(const v4i*)(Bm + tok * a.ld_B + q * 8) : v4i{0, 0, 0, 0};
+      pc[i] = ok ? *(const v4i*)(Cm + tok * a.ld_C + q * 8) : v4i{0, 0, 0, 0};
+    }
+    if (w == 0) pdt = ok ? bf16_to_f32(DT[tok * a.ld_delta + hd]) : 0.0f;
+  };
+  auto stage = [&](int64_t c0) {
+    const int t = lane;
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int q = w + 4 * i;
+      *(v4i*)(&sX[t * XS + q * 8]) = px[i];
+      const uint16_t* v = (const uint16_t*)&px[i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sXT[(q * 8 + u) * XS + t] = v[u];
+    }
+#pragma unroll
+    for (int i = 0; i < BC; ++i) {
+      const int q = w + 4 * i;
+      *(v4i*)(&sB[t * NSP + q * 8]) = pb[i];
+      *(v4i*)(&sC[t * NSP + q * 8]) = pc[i];
+      const uint16_t* v = (const uint16_t*)&pb[i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sBT[(q * 8 + u) * XS + t] = v[u];
+    }
+    if (w == 0) {  // dt = softplus(delta + bias) (0 past the end), cs = inclusive cumsum of dt A
+      float dt = 0.0f;
+      if (c0 + lane < L) {
+        dt = pdt + bias_h;
+        if (a.softplus) dt = softplus_hw(dt);
+      }
+      float cs = dt * A_h;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(cs, d, 64);
+        if (lane >= d) cs += o;
+      }
+      const float cend = __shfl(cs, 63, 64);
+      s_dt[lane] = dt;
+      s_cs[lane] = cs;
+      s_w[lane] = exp_hw(cend - cs) * dt;
+      s_et[lane] = exp_hw(cs);
+    }
+  };
+
+  const int64_t nch = cdiv(L, Q);
+  load(0);
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    const int64_t c0 = ch * Q;
+    stage(c0);
+    __syncthreads();
+    if (ch + 1 < nch) load(c0 + Q);
+    const float cs_end = s_cs[Q - 1];
+
+    // G = C B^T for rows 16 w .., s tiles j <= w (the rest is masked); then M into LDS
+    {
+      v4f g[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) g[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk) {
+        const v8bf af = __builtin_bit_cast(v8bf, *(const v4i*)(&sC[(16 * w + l16) * NSP + kk * 32 + kq * 8]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j > w) continue;
+          const v8bf bfr = __builtin_bit_cast(v8bf, *(const v4i*)(&sB[(16 * j + l16) * NSP + kk * 32 + kq * 8]));
+          g[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, g[j], 0, 0, 0);
+        }
+      }
+      // M[t][s] = G exp(cs_t - cs_s) dt_s for s <= t; lane holds t = 16 w + 4 kq + r, s = 16 j + l16
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tl = 4 * kq + r, t = 16 * w + tl, sidx = 16 * j + l16;
+          float m = 0.0f;
+          if (j <= w && sidx <= t) m = g[j][r] * (exp_hw(s_cs[t] - s_cs[sidx]) * s_dt[sidx]);
+          const uint16_t hi = bf_bits(m);
+          sM[w][0][tl * XS + sidx] = hi;
+          sM[w][1][tl * XS + sidx] = bf_bits(m - bf_val(hi));
+        }
+    }
+    __syncthreads();
+
+    // Y = M X (s < 16 w + 16) and Z = C h_in^T; lane holds t = 16 w + 4 kq + r, p = 16 jp + l16
+    v4f yacc[4], zacc[4];
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) { yacc[jp] = v4f{0.f, 0.f, 0.f, 0.f}; zacc[jp] = v4f{0.f, 0.f, 0.f, 0.f}; }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (kk * 32 > 16 * w + 15) continue;
+      const v8bf mh = __builtin_bit_cast(v8bf, *(const v4i*)(&sM[w][0][l16 * XS + kk * 32 + kq * 8]));
+      const v8bf ml = __builtin_bit_cast(v8bf, *(const v4i*)(&sM[w][1][l16 * XS + kk * 32 + kq * 8]));
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) {
+        const v8bf xf = __builtin_bit_cast(v8bf, *(const v4i*)(&sXT[(16 * jp + l16) * XS + kk * 32 + kq * 8]));
+        yacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh, xf, yacc[jp], 0, 0, 0);
+        yacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml, xf, yacc[jp], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk) {
+      const v8bf cf = __builtin_bit_cast(v8bf, *(const v4i*)(&sC[(16 * w + l16) * NSP + kk * 32 + kq * 8]));
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) {
+        const int off = (16 * jp + l16) * NSP + kk * 32 + kq * 8;
+        const v8bf hh = __builtin_bit_cast(v8bf, *(const v4i*)(&sH[0][off]));
+        const v8bf hl = __builtin_bit_cast(v8bf, *(const v4i*)(&sH[1][off]));
+        zacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, hh, zacc[jp], 0, 0, 0);
+        zacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, hl, zacc[jp], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * w + 4 * kq + r;
+      if (c0 + t >= L) continue;
+      const float et = s_et[t];
+      bf16_t* yr = Y + (b * L + c0 + t) * a.ld_y + hd * P;
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) {
+        const int pp = 16 * jp + l16;
+        const float yv = yacc[jp][r] + et * zacc[jp][r] + D_h * bf_val(sX[t * XS + pp]);
+        yr[pp] = f32_to_bf16(yv);
+      }
+    }
+
+    // state: h = exp(cs_end) h + (w X)^T B; A fragment: p = 16 w + l16, s = 32 kk + 8 kq + u
+    const float ed = exp_hw(cs_end);
+#pragma unroll
+    for (int jn = 0; jn < NTN; ++jn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) h[jn][r] *= ed;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint16_t* xr = &sXT[(16 * w + l16) * XS + kk * 32 + kq * 8];
+      uint16_t ahi[8], alo[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sidx = kk * 32 + kq * 8 + u;
+        const float v = bf_val(xr[u]) * s_w[sidx];
+        ahi[u] = bf_bits(v);
+        alo[u] = bf_bits(v - bf_val(ahi[u]));
+      }
+      const v8bf ah = __builtin_bit_cast(v8bf, *(const v4i*)ahi);
+      const v8bf al = __builtin_bit_cast(v8bf, *(const v4i*)alo);
+#pragma unroll
+      for (int jn = 0; jn < NTN; ++jn) {
+        const v8bf bfr = __builtin_bit_cast(v8bf, *(const v4i*)(&sBT[(16 * jn + l16) * XS + kk * 32 + kq * 8]));
+        h[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bfr, h[jn], 0, 0, 0);
+        h[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfr, h[jn], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    write_h();
+  }
+  if (a.h_last) {
+#pragma unroll
+    for (int jn = 0; jn < NTN; ++jn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pp = 16 * w + 4 * kq + r, n = 16 * jn + l16;
+        a.h_last[((b * H + hd) * P + pp) * NS + n] = h[jn][r];
+      }
+  }
+}
+
+// The chunked kernel takes bf16 activations with headdim 64, d_state 64 or 128, and row
+// strides and bases that allow 16-byte loads of x, B and C.
+static bool ssd_chunk_ok(const ScanArgs& a) {
+  auto al = [](const void* p) { return ((uintptr_t)p % 16) == 0; };
+  return a.act_bf16 && a.P == kSsdP && (a.N == 64 || a.N == 128) && a.ld_x % 8 == 0 && a.ld_B % 8 == 0 &&
+         a.ld_C % 8 == 0 && al(a.x) && al(a.Bm) && al(a.Cm);
+}
+
 template <int NS, typename T>
 static void launch_ssd_t(const ScanArgs& a, hipStream_t s) {
   constexpr int PPB = 256 / (NS / 8);
@@ -123,6 +400,12 @@ size_t scan_ssd_workspace(const ScanArgs&) { return 0; }
 
 hipError_t launch_scan_ssd(const ScanArgs& a, void*, size_t, hipStream_t s) {
   if (a.batch == 0 || a.L == 0) return hipSuccess;
+  if (ssd_chunk_ok(a)) {
+    const dim3 grid((unsigned)(a.batch * a.H)), block(256);
+    if (a.N == 128) hipLaunchKernelGGL((k_ssd_chunk<128>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ssd_chunk<64>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   return a.act_bf16 ? launch_ssd_n<bf16_t>(a, s) : launch_ssd_n<float>(a, s);
 }
 

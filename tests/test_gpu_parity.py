@@ -185,6 +185,8 @@ SCAN_CASES = [  # (batch, L, H, P, N, a_per_state, dtype)
     (2, 50, 4, 64, 128, False, "f32"),     # SSD kind
     (1, 77, 3, 16, 16, False, "f32"),
     (1, 40, 2, 32, 64, False, "bf16"),
+    (2, 200, 4, 64, 128, False, "bf16"),   # SSD chunked (matrix-core) path, ragged last chunk
+    (1, 130, 3, 64, 64, False, "bf16"),
 ]
 
 
@@ -197,7 +199,9 @@ def test_scan_parity(batch, L, H, P, N, aps, dt):
     ref, href = oracle.selective_scan(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["D"], p["dt_bias"], h0=h0)
     y, hl = _scan_gpu(p, torch.bfloat16 if dt == "bf16" else torch.float32, h0=h0, last=True)
     assert rel_err(host(y), ref) <= TOL[dt]
-    assert rel_err(host(hl), href) <= 1e-5
+    # the SSD chunked path (bf16 activations) carries fp32 operands of its matrix products as
+    # two bf16 terms (about 16 significant bits), hence the wider bound on its final state
+    assert rel_err(host(hl), href) <= (1e-4 if dt == "bf16" else 1e-5)
 
 
 def test_scan_long_sequence_sampled():
