@@ -191,15 +191,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int ks = 0; ks < nk; ++ks) {
     const int buf = ks & 1;
     if (ks + 1 < nk) load((int64_t)(ks + 1) * BKT);
-    v4i wf[NT];
+    // all operand fragments of the step first (one LDS wait), then its MFMAs
+    v4i wf[NT], bfr[MT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) wf[j] = *(const v4i*)(&s_w[buf][(wn * WN + j * 16 + l16) * AS + kq * 16]);
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const v4i bfr = *(const v4i*)(&s_a[buf][(wm * 128 + i * 16 + l16) * AS + kq * 16]);
+    for (int i = 0; i < MT; ++i) bfr[i] = *(const v4i*)(&s_a[buf][(wm * 128 + i * 16 + l16) * AS + kq * 16]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs (the scheduler sinks them)
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[j], bfr, acc[i][j], 0, 0, 0);
-    }
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[j], bfr[i], acc[i][j], 0, 0, 0);
     if (ks + 1 < nk) store(buf ^ 1);
     __syncthreads();
   }
