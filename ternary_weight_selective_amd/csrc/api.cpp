@@ -397,10 +397,13 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
     void* x = base + p.off_x;
     void* pp = base + p.off_p;
     void* y = base + p.off_y;
-    st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, c->d_inner, x, c->d_inner, nullptr);
-    if (st != SSM_OK) return st;
-    st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
-    if (st != SSM_OK) return st;
+    const bool front = front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank);
+    if (!front) {
+      st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, c->d_inner, x, c->d_inner, nullptr);
+      if (st != SSM_OK) return st;
+      st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
+      if (st != SSM_OK) return st;
+    }
     const size_t as = act_size(c->act_dtype);
     ssm_scan_args sa{};
     sa.batch = batch; sa.seqlen = seqlen; sa.nheads = c->d_inner; sa.headdim = 1; sa.d_state = c->d_state;
@@ -416,7 +419,23 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
     sa.w_dt = w->w_dt; sa.s_dt = w->s_dt; sa.g_dt = w->g_dt; sa.dt_eps = c->norm_eps;
     st = scan_check(&sa);
     if (st != SSM_OK) return st;
-    st = dev(launch_scan_m1(to_scan(&sa), base + p.off_scan, stream), "mixer scan");
+    ScanArgs sc = to_scan(&sa);
+    if (front) {  // in_proj, x_proj and the dt input's codes in one kernel, codes into the scan's workspace
+      FrontArgs fa{};
+      fa.M = p.M; fa.u = u; fa.act_bf16 = c->act_dtype == SSM_BF16;
+      fa.Dm = (int)c->d_model; fa.Di = (int)c->d_inner; fa.PW = (int)p.PW; fa.R = (int)c->dt_rank;
+      fa.w_in = (const uint32_t*)w->w_in; fa.s_in = w->s_in; fa.g_in = w->g_in;
+      fa.w_x = (const uint32_t*)w->w_x; fa.s_x = w->s_x; fa.g_x = w->g_x;
+      fa.eps = c->norm_eps; fa.x = x; fa.p = pp; fa.g_dt = w->g_dt;
+      size_t off_deq = 0;
+      scan_m1_code_layout(sc, &fa.cw, &off_deq);
+      fa.codes = (int8_t*)(base + p.off_scan);
+      fa.deq = (double*)(base + p.off_scan + off_deq);
+      st = dev(launch_m1_front(fa, stream), "mixer front");
+      if (st != SSM_OK) return st;
+      sc.dt_codes_ready = 1;
+    }
+    st = dev(launch_scan_m1(sc, base + p.off_scan, stream), "mixer scan");
     if (st != SSM_OK) return st;
     return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
   }

@@ -78,9 +78,29 @@ struct ScanArgs {
   const void* dr; int64_t ld_dr; int R;
   const uint32_t* w_dt; int64_t w_dt_row_words;
   const float* s_dt; const float* g_dt; float eps;
+  int dt_codes_ready;  // the dt input's int8 codes and factors are already in the workspace
 };
 hipError_t launch_scan_m1(const ScanArgs& a, void* ws, hipStream_t s);
 size_t scan_m1_workspace(const ScanArgs& a);
+// Where the scan keeps the dt input's codes ([M, *cw] int8 at offset 0) and their fp64
+// dequantisation factors ([M] at *off_deq) in its workspace.
+void scan_m1_code_layout(const ScanArgs& a, int* cw, size_t* off_deq);
+
+// ---- Mamba-1 mixer front (front.hip): x = BitLinear(u; W_in), p = BitLinear(x; W_x) and the
+// dt input's int8 codes in one kernel (A8, one scale per tensor)
+struct FrontArgs {
+  int64_t M;
+  const void* u; int act_bf16;
+  int Dm, Di, PW, R;
+  const uint32_t* w_in; const float* s_in; const float* g_in;
+  const uint32_t* w_x; const float* s_x; const float* g_x;
+  float eps;
+  void* x; void* p;
+  const float* g_dt;
+  int8_t* codes; int cw; double* deq;
+};
+bool front_supported(int Dm, int Di, int PW, int R);
+hipError_t launch_m1_front(const FrontArgs& f, hipStream_t s);
 hipError_t launch_scan_ssd(const ScanArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
 size_t scan_ssd_workspace(const ScanArgs& a);
 

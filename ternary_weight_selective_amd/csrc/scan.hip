@@ -389,10 +389,12 @@ hipError_t launch_m1_t(const ScanArgs& a, void* ws, hipStream_t s) {
     const int64_t M = a.batch * a.L;
     int8_t* codes = (int8_t*)ws;
     double* deq = (double*)((char*)ws + p.off_deq);
-    const int G = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
-    const int64_t tok_per_block = 4 * (64 / G);
-    hipLaunchKernelGGL(k_dt_codes, dim3((unsigned)cdiv(M, tok_per_block)), dim3(256), 0, s, a.dr, a.act_bf16, M,
-                       a.ld_dr, a.R, a.g_dt, a.eps, codes, p.cw, deq);
+    if (!a.dt_codes_ready) {
+      const int G = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
+      const int64_t tok_per_block = 4 * (64 / G);
+      hipLaunchKernelGGL(k_dt_codes, dim3((unsigned)cdiv(M, tok_per_block)), dim3(256), 0, s, a.dr, a.act_bf16, M,
+                         a.ld_dr, a.R, a.g_dt, a.eps, codes, p.cw, deq);
+    }
     dc.codes = codes;
     dc.deq = deq;
   }
@@ -434,6 +436,12 @@ hipError_t launch_m1_n(const ScanArgs& a, void* ws, hipStream_t s) {
   }
 }
 }  // namespace
+
+void scan_m1_code_layout(const ScanArgs& a, int* cw, size_t* off_deq) {
+  const ScanPlan p = plan_scan(a);
+  *cw = p.cw;
+  *off_deq = p.off_deq;
+}
 
 size_t scan_m1_workspace(const ScanArgs& a) {
   if (a.batch == 0 || a.L == 0) return 0;
