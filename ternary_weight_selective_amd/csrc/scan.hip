@@ -120,11 +120,11 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t Di = a.H, L = a.L;
-  const int64_t b = blockIdx.y;
+  const int64_t b = blockIdx.x;   // sequence fastest: the channel tiles of a sequence share an XCD
   const int chunk = blockIdx.z;
   const int64_t tb = (int64_t)chunk * ch.chunk_len;
   const int64_t te = (tb + ch.chunk_len < L) ? tb + ch.chunk_len : L;
-  const int64_t d0 = (int64_t)blockIdx.x * CPB;
+  const int64_t d0 = (int64_t)blockIdx.y * CPB;
   const int64_t d = d0 + lane;
   const bool dv = d < Di;
   // staging role: thread -> (channel lane, rows w, w + 4, ...)
@@ -285,7 +285,41 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
       }
     };
     if (tmax == TT) {
-      for (int tt = 0; tt < TT; tt += GT) group(tt, std::integral_constant<int, GT>{});
+      // full tile: groups of GQ steps, software-pipelined: the LDS reads of group g + 1 are
+      // issued before the arithmetic of group g
+      constexpr int GQ = GT < 4 ? GT : 4, NG = TT / GQ;
+      float bq[2][GQ][SPL], cq[2][GQ][SPL];
+      float2 dd[2][GQ];
+      auto ld = [&](int tt, int sl) {
+#pragma unroll
+        for (int u = 0; u < GQ; ++u) {
+          const int t = tt + u;
+#pragma unroll
+          for (int i = 0; i < SPL; ++i) {
+            bq[sl][u][i] = s_B[t][w * SPL + i];
+            if (!LOCAL) cq[sl][u][i] = s_C[LOCAL ? 0 : t][w * SPL + i];
+          }
+          dd[sl][u] = s_dd[t][lane];
+        }
+      };
+      ld(0, 0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int sl = g & 1;
+        if (g + 1 < NG) ld((g + 1) * GQ, sl ^ 1);
+#pragma unroll
+        for (int u = 0; u < GQ; ++u) {
+          float yp = 0.0f;
+#pragma unroll
+          for (int i = 0; i < SPL; ++i) {
+            const float ab = __builtin_amdgcn_exp2f(dd[sl][u].x * Al[i]);
+            h[i] = __builtin_fmaf(ab, h[i], dd[sl][u].y * bq[sl][u][i]);
+            if (!LOCAL) yp = i == 0 ? cq[sl][u][0] * h[0] : __builtin_fmaf(cq[sl][u][i], h[i], yp);
+          }
+          if (LOCAL) sum_dt += dd[sl][u].x;
+          else s_yp[LOCAL ? 0 : w][LOCAL ? 0 : g * GQ + u][lane] = yp;
+        }
+      }
     } else {
       for (int t = 0; t < tmax; ++t) group(t, std::integral_constant<int, 1>{});
     }
@@ -398,7 +432,10 @@ hipError_t launch_m1_t(const ScanArgs& a, void* ws, hipStream_t s) {
     dc.codes = codes;
     dc.deq = deq;
   }
-  const unsigned gx = (unsigned)cdiv(a.H, kCPB), gy = (unsigned)a.batch;
+  // grid (sequence, channel tile, chunk): blocks are dealt to the 8 XCDs round-robin by linear
+  // index, so with the sequence fastest the channel tiles of sequence b all run on XCD b mod 8
+  // and share its L2 for B, C and the dt codes
+  const unsigned gx = (unsigned)a.batch, gy = (unsigned)cdiv(a.H, kCPB);
   const int rw = fused ? p.cw / 16 : 0;
   auto run = [&](auto rwc, bool local, unsigned gz) {
     constexpr int RWc = decltype(rwc)::value;
