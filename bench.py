@@ -377,6 +377,36 @@ def main():
             stages[n]["T" + cost["ops_unit"] + "/s"] = cost["ops"] / avg_s / 1e12
     dominant = max(names, key=lambda n: stages[n]["avg_us"] * stages[n]["launches"])
 
+    # whole mixer layers (ssm_mixer_fwd, as in the headline step), bracketed per layer: for the
+    # Mamba-1 kind the mixer runs in_proj, x_proj and the dt-input quantisation as one fused
+    # kernel, whose time is the layer time minus the scan and out_proj stages
+    L = tws.lib()
+    nl = len(prob.mws)
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps * nl)]
+    torch.cuda._sleep(20_000_000)
+    k = 0
+    for _ in range(args.steps):
+        h = prob.u
+        for i, mw in enumerate(prob.mws):
+            out = prob.bufs[i % 2]
+            lev[k][0].record()
+            st = L.ssm_mixer_fwd(ctypes.byref(prob.c), ctypes.byref(mw), h.data_ptr(), out.data_ptr(), cfg.batch,
+                                 cfg.seqlen, 1, prob.ws.data_ptr(), prob.ws_bytes, sh)
+            lev[k][1].record()
+            if st != 0:
+                raise tws.SsmError(st, L.ssm_last_error().decode())
+            h = out
+            k += 1
+    torch.cuda.synchronize()
+    layer_us = float(np.mean([a.elapsed_time(b) for a, b in lev])) * 1e3
+    layer = {"avg_us": layer_us, "launches": len(lev)}
+    if cfg.kind == wl.MAMBA1 and L.ssm_mixer_fuses_front(ctypes.byref(prob.c)):
+        front_us = layer_us - stages["scan"]["avg_us"] - stages["bitlinear_out"]["avg_us"]
+        byts = cfg.tokens * (cfg.d_model + cfg.d_inner + cfg.dt_rank + 2 * cfg.d_state) * (2 if cfg.act_dtype == "bf16" else 4)
+        layer["front_fused_us_derived"] = front_us
+        layer["front_fused_GBps_derived"] = byts / (front_us * 1e-6) / 1e9
+
     cost = stage_cost(cfg, dominant)
     avg_s = stages[dominant]["avg_us"] * 1e-6
     if dominant == "scan" and cfg.kind == wl.MAMBA1:
@@ -414,7 +444,7 @@ def main():
         del src, dst
 
     if args.stages_only:
-        print(json.dumps({"stages": stages, "stage_ms_per_step": stage_total_ms, "roofline": roof}))
+        print(json.dumps({"stages": stages, "stage_ms_per_step": stage_total_ms, "layer": layer, "roofline": roof}))
         return
 
     tokens = cfg.tokens
@@ -442,6 +472,7 @@ def main():
         "timing": {k: v for k, v in result.items() if k != "ms_per_step"},
         "stages": stages,
         "stage_ms_per_step": stage_total_ms,
+        "layer": layer,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -260,6 +260,16 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
                          void* out, int64_t batch, int64_t seqlen, int32_t add_residual,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * ssm_mixer_fuses_front -- 1 when ssm_mixer_fwd evaluates this configuration's x = BL(u; W_in),
+ * p = BL(x; W_x) and the quantisation of dr (the dt projection's input) as one fused kernel
+ * (Mamba-1 kind, d_model 64..512, d_inner 128..1024 but not 512 with 1024, dt_rank + 2 d_state
+ * <= 64), 0 when it issues them as separate BitLinear calls.  The results are the same either
+ * way; this only tells a profiler which kernels to expect.  Host-only, no device access;
+ * returns 0 for a NULL or invalid configuration.
+ */
+int32_t ssm_mixer_fuses_front(const ssm_mixer_config* c);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,7 +63,7 @@ _lib = None
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed_row_bytes",
            "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
-           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd"]
+           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front"]
 
 
 def lib():
@@ -94,6 +94,8 @@ def lib():
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
         L.ssm_mixer_workspace_bytes.argtypes = [ctypes.POINTER(MixerConfig), _i64, _i64]
         L.ssm_mixer_workspace_bytes.restype = _sz
+        L.ssm_mixer_fuses_front.argtypes = [ctypes.POINTER(MixerConfig)]
+        L.ssm_mixer_fuses_front.restype = ctypes.c_int32
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
         L.ssm_mixer_fwd.restype = ctypes.c_int
@@ -253,6 +255,10 @@ def mixer_config(kind: int, d_model: int, d_inner: int, d_state: int, *, dt_rank
     c.nheads, c.headdim, c.group_size = nheads, headdim, group_size
     c.act_dtype, c.norm_eps = _DTYPES[act_dtype], norm_eps
     return c
+
+
+def ssm_mixer_fuses_front(cfg: MixerConfig) -> bool:
+    return bool(lib().ssm_mixer_fuses_front(ctypes.byref(cfg)))
 
 
 def ssm_mixer_workspace_bytes(cfg: MixerConfig, batch: int, seqlen: int) -> int:

@@ -354,6 +354,15 @@ size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64
   return p.total + align_up(scan_m1_workspace(s));
 }
 
+int32_t ssm_mixer_fuses_front(const ssm_mixer_config* c) {
+  std::string keep = g_err;
+  MixPlan p;
+  const ssm_status st = mix_plan(c, 1, 1, &p);
+  g_err = keep;
+  if (st != SSM_OK || c->kind != SSM_MIXER_MAMBA1) return 0;
+  return front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank) ? 1 : 0;
+}
+
 ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
                          int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb,
                          hipStream_t stream) {

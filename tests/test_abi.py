@@ -177,3 +177,14 @@ def test_mixer_rejects():
     assert L.ssm_mixer_fwd(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 16, None) == WORKSPACE
     assert L.ssm_mixer_fwd(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, 64, 1, FAKE + 8, 1 << 30,
                            None) == ALIGN
+
+
+def test_mixer_fuses_front_query():
+    """Host-only query: which Mamba-1 shapes run in_proj, x_proj and the dt quantisation fused."""
+    L = tws.lib()
+    trissm = tws.mixer_config(0, 256, 512, 16, dt_rank=16)
+    assert L.ssm_mixer_fuses_front(ctypes.byref(trissm)) == 1
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 512, 1024, 16, dt_rank=32))) == 0
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(1, 256, 256, 64, nheads=4, headdim=64))) == 0
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 100, 512, 16, dt_rank=16))) == 0
+    assert L.ssm_mixer_fuses_front(None) == 0
