@@ -261,6 +261,23 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * ssm_mixer_step -- one decoding step of the mixer layer: ONE new token per sequence, the
+ * recurrence carried between calls (the recurrent, linear-time inference the TernarySSM and
+ * TriSSM pages describe for these models).  The result is that of ssm_mixer_fwd with
+ * seqlen = 1 whose scan starts from, and ends in, state.
+ *  u, out:  [batch, d_model] in act_dtype (out may equal u when add_residual != 0);
+ *  state:   device fp32, [batch, d_inner, d_state] (Mamba-1 kind) or
+ *           [batch, nheads, headdim, d_state] (SSD kind); read as the state before the token
+ *           and overwritten with the state after it (zeros before the first token).
+ *  workspace: ssm_mixer_workspace_bytes(c, batch, 1) bytes of device memory.
+ * Decoding a sequence token by token reproduces the outputs of ssm_mixer_fwd over the whole
+ * sequence.  Errors: as ssm_mixer_fwd; SSM_ERR_NULL when state is NULL and batch > 0.
+ */
+ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
+                          int64_t batch, float* state, int32_t add_residual, void* workspace,
+                          size_t ws_bytes, hipStream_t stream);
+
+/*
  * ssm_mixer_fuses_front -- 1 when ssm_mixer_fwd evaluates this configuration's x = BL(u; W_in),
  * p = BL(x; W_x) and the quantisation of dr (the dt projection's input) as one fused kernel
  * (Mamba-1 kind, d_model 64..512, d_inner 128..1024 but not 512 with 1024, dt_rank + 2 d_state

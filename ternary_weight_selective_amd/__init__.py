@@ -63,7 +63,7 @@ _lib = None
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed_row_bytes",
            "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
-           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front"]
+           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front", "ssm_mixer_step"]
 
 
 def lib():
@@ -96,6 +96,9 @@ def lib():
         L.ssm_mixer_workspace_bytes.restype = _sz
         L.ssm_mixer_fuses_front.argtypes = [ctypes.POINTER(MixerConfig)]
         L.ssm_mixer_fuses_front.restype = ctypes.c_int32
+        L.ssm_mixer_step.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64,
+                                     _vp, ctypes.c_int32, _vp, _sz, _vp]
+        L.ssm_mixer_step.restype = ctypes.c_int
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
         L.ssm_mixer_fwd.restype = ctypes.c_int
@@ -287,4 +290,24 @@ def ssm_mixer_fwd(cfg: MixerConfig, weights, u: torch.Tensor, add_residual: bool
     ws = _workspace(nb, u.device, workspace)
     _check(L.ssm_mixer_fwd(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, seqlen, int(add_residual),
                            _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def ssm_mixer_step(cfg: MixerConfig, weights, u: torch.Tensor, state: torch.Tensor, add_residual: bool = True,
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """One decoding step on u [B, d_model] (one token per sequence); state (fp32, contiguous) is
+    read and overwritten in place."""
+    if not u.is_contiguous() or not state.is_contiguous():
+        raise ValueError("u and state must be contiguous")
+    if state.dtype != torch.float32:
+        raise ValueError("state must be float32")
+    batch = u.shape[0]
+    mw = weights if isinstance(weights, MixerWeights) else mixer_weights(weights)
+    if out is None:
+        out = torch.empty_like(u)
+    L = lib()
+    nb = L.ssm_mixer_workspace_bytes(ctypes.byref(cfg), batch, 1)
+    ws = _workspace(nb, u.device, workspace)
+    _check(L.ssm_mixer_step(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, _p(state),
+                            int(add_residual), _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
     return out

@@ -351,6 +351,7 @@ size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64
     return p.total + align_up(scan_ssd_workspace(s));
   }
   s.H = c->d_inner; s.P = 1;
+  s.R = (int)c->dt_rank;  // dt_proj runs inside the scan: room for the dt input's codes
   return p.total + align_up(scan_m1_workspace(s));
 }
 
@@ -363,10 +364,35 @@ int32_t ssm_mixer_fuses_front(const ssm_mixer_config* c) {
   return front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank) ? 1 : 0;
 }
 
+namespace {
+// One mixer layer; state (nullable): the scan's initial state, overwritten with its final state
+// (used for one token per sequence only, where no time chunks are formed).
+ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
+                     int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb, hipStream_t stream,
+                     float* state);
+}  // namespace
+
 ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
                          int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb,
                          hipStream_t stream) {
   g_err.clear();
+  return mixer_run(c, w, u, out, batch, seqlen, add_residual, ws, wsb, stream, nullptr);
+}
+
+ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
+                          int64_t batch, float* state, int32_t add_residual, void* ws, size_t wsb,
+                          hipStream_t stream) {
+  g_err.clear();
+  if (batch > 0 && !state) return fail(SSM_ERR_NULL, "mixer step: state is NULL");
+  return mixer_run(c, w, u, out, batch, 1, add_residual, ws, wsb, stream, state);
+}
+
+}  // extern "C"
+
+namespace {
+ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
+                     int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb, hipStream_t stream,
+                     float* state) {
   MixPlan p;
   ssm_status st = mix_plan(c, batch, seqlen, &p);
   if (st != SSM_OK) return st;
@@ -407,12 +433,6 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
     void* pp = base + p.off_p;
     void* y = base + p.off_y;
     const bool front = front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank);
-    if (!front) {
-      st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, c->d_inner, x, c->d_inner, nullptr);
-      if (st != SSM_OK) return st;
-      st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
-      if (st != SSM_OK) return st;
-    }
     const size_t as = act_size(c->act_dtype);
     ssm_scan_args sa{};
     sa.batch = batch; sa.seqlen = seqlen; sa.nheads = c->d_inner; sa.headdim = 1; sa.d_state = c->d_state;
@@ -423,12 +443,21 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
     sa.Bm = (const char*)pp + c->dt_rank * as; sa.ld_B = p.PW;
     sa.Cm = (const char*)pp + (c->dt_rank + c->d_state) * as; sa.ld_C = p.PW;
     sa.D = w->D;
+    sa.h0 = state; sa.h_last = state;
     sa.y = y; sa.ld_y = c->d_inner;
     sa.dt_in = pp; sa.ld_dt_in = p.PW; sa.dt_rank = c->dt_rank;
     sa.w_dt = w->w_dt; sa.s_dt = w->s_dt; sa.g_dt = w->g_dt; sa.dt_eps = c->norm_eps;
     st = scan_check(&sa);
     if (st != SSM_OK) return st;
     ScanArgs sc = to_scan(&sa);
+    if (p.off_scan + scan_m1_workspace(sc) > wsb)  // the scan's codes region lies inside the workspace
+      return fail(SSM_ERR_WORKSPACE, "mixer: scan workspace exceeds %zu bytes", wsb);
+    if (!front) {
+      st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, c->d_inner, x, c->d_inner, nullptr);
+      if (st != SSM_OK) return st;
+      st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
+      if (st != SSM_OK) return st;
+    }
     if (front) {  // in_proj, x_proj and the dt input's codes in one kernel, codes into the scan's workspace
       FrontArgs fa{};
       fa.M = p.M; fa.u = u; fa.act_bf16 = c->act_dtype == SSM_BF16;
@@ -463,10 +492,12 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
   s.delta = (const char*)v + (c->d_inner + 2 * c->d_state) * as; s.ld_delta = p.VW;
   s.delta_bias = w->dt_bias; s.softplus = 1;
   s.A = w->A; s.D = w->D;
+  s.h0 = state; s.h_last = state;
   s.y = y; s.ld_y = c->d_inner;
   st = dev(launch_scan_ssd(s, base + p.off_scan, wsb - p.off_scan, stream), "mixer scan");
   if (st != SSM_OK) return st;
   return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
 }
 
-}  // extern "C"
+}  // namespace
+

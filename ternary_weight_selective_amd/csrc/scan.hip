@@ -95,27 +95,34 @@ struct DtCodes {
 }  // namespace
 
 // Lanes are 64 channels; the 4 waves of a block are 4 groups of NS / 4 states, so B and C of
-// a step are the same for a whole wave and are read with scalar loads into SGPRs.  Each wave
-// writes its readout partial per (step, channel) to LDS; the partials are added in wave
-// order, plus D x, when the tile is stored.
+// a step are the same for a whole wave and are read from LDS at wave-uniform addresses.  Each
+// wave writes its readout partial per (step, channel) to LDS; the partials are added in wave
+// order, plus D x, one tile later.
+//
+// One barrier per tile of TT = 16 steps, with double-buffered LDS: per tile i a thread
+//   1. stages tile i: B, C into LDS, and for its (step, channel) items the step's dt (dot
+//      product of the step's dt codes, held in registers since the previous tile, with the
+//      channel's ternary row; fp64 dequantisation; bias; softplus) and dt x;
+//   2. requests tile i + 1 (x, B, C, codes) into registers;
+//   3. barrier;
+//   4. adds the four waves' readout partials of tile i - 1, plus D x, and stores y;
+//   5. runs the recurrence over tile i, writing its partials.
+// A buffer of tile i is rewritten at tile i + 2, after the barrier of tile i + 1 that every
+// wave reaches only once it has finished with tile i.
 // LOCAL: pass 1 (zero start, no readout; writes the chunk's end state and sum(dt)).
 template <int NS, typename T, int RW, bool LOCAL>
 __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, DtCodes dc) {
   constexpr bool FUSED = RW > 0;  // dt from the low-rank input: RW 16-byte code words per token
   constexpr int SPL = NS / 4;     // states per lane
   constexpr int CPB = 64;         // channels per block
-  constexpr int TT = 32;          // time steps per tile
-  constexpr int XPT = TT * CPB / 256;
-  constexpr int GT = SPL <= 4 ? 8 : (SPL == 8 ? 4 : 2);  // steps per group of LDS reads
+  constexpr int TT = 16;          // time steps per tile
+  constexpr int XPT = TT * CPB / 256;                    // (step, channel) items per thread
   constexpr int BPT = (TT * NS + 255) / 256;             // B (and C) elements per thread per tile
-  __shared__ float s_x[TT][CPB];
-  __shared__ float s_d[FUSED ? 1 : TT][CPB];
-  __shared__ __align__(16) int8_t s_q[FUSED ? TT : 1][64];
-  __shared__ double s_rf[FUSED ? TT : 1];
-  __shared__ float2 s_dd[TT][CPB];  // (dt, dt * x)
-  __shared__ __align__(16) float s_B[TT][NS];
-  __shared__ __align__(16) float s_C[LOCAL ? 1 : TT][NS];
-  __shared__ float s_yp[LOCAL ? 1 : 4][LOCAL ? 1 : TT][CPB];
+  constexpr int RWQ = FUSED ? RW : 1;
+  __shared__ float2 s_dd[2][TT][CPB];  // (dt, dt * x)
+  __shared__ __align__(16) float s_B[2][TT][NS];
+  __shared__ __align__(16) float s_C[LOCAL ? 1 : 2][LOCAL ? 1 : TT][NS];
+  __shared__ float s_yp[LOCAL ? 1 : 2][LOCAL ? 1 : 4][LOCAL ? 1 : TT][CPB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   const int64_t d0 = (int64_t)blockIdx.y * CPB;
   const int64_t d = d0 + lane;
   const bool dv = d < Di;
-  // staging role: thread -> (channel lane, rows w, w + 4, ...)
+  // staging role: thread -> (channel lane, steps w, w + 4, ...)
   const float bias_s = (dv && a.delta_bias) ? a.delta_bias[d] : 0.0f;
   const float D_s = (dv && a.D) ? a.D[d] : 0.0f;
   constexpr int cw = 16 * RW;  // code bytes per token
@@ -161,18 +168,26 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   }
   float sum_dt = 0.0f;
 
-  // prefetch registers: x (and delta) of the next tile; its dt codes and factors
+  // prefetch registers for the next tile: x (and delta) of the thread's items, B, C, the
+  // items' dt codes (a whole wave reads the same token row) and dequantisation factors
   float rx[XPT], rd[FUSED ? 1 : XPT], rb[BPT], rc[BPT];
-  int rq[2] = {0, 0};
-  double rf = 0.0;
+  v4i rq[FUSED ? XPT : 1][RWQ];
+  double rf[FUSED ? XPT : 1];
   auto load_tile = [&](int64_t t0) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int t = w + 4 * i;
-      const bool ok = (t0 + t < te) && dv;
+      const bool okt = t0 + t < te;
+      const bool ok = okt && dv;
       const int64_t tok = b * L + t0 + t;
       rx[i] = ok ? ld_act(X + tok * a.ld_x + d) : 0.0f;
       if (!FUSED) rd[FUSED ? 0 : i] = ok ? ld_act(DL + tok * a.ld_delta + d) : 0.0f;
+      if (FUSED) {
+#pragma unroll
+        for (int q = 0; q < RWQ; ++q)
+          rq[FUSED ? i : 0][q] = okt ? ((const v4i*)(dc.codes + tok * cw))[q] : v4i{0, 0, 0, 0};
+        rf[FUSED ? i : 0] = okt ? dc.deq[tok] : 0.0;
+      }
     }
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
@@ -182,112 +197,71 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
       rb[i] = ok ? ld_act((const T*)a.Bm + tok * a.ld_B + n) : 0.0f;
       rc[i] = (ok && !LOCAL) ? ld_act((const T*)a.Cm + tok * a.ld_C + n) : 0.0f;
     }
-    if (FUSED) {
-      constexpr int nq = TT * cw / 4;  // 4-byte words of codes in the tile (<= 512)
+  };
+
+  float xprev[XPT];  // x of the previous tile's items, for D x
+  int64_t tprev = -1;  // first step of the tile whose readout is pending
+  auto store_y = [&](int buf, int64_t t0p) {
+    T* Y = (T*)a.y;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int e = tid + 256 * k, t = e * 4 / (cw > 0 ? cw : 1);
-        rq[k] = (e < nq && t0 + t < te) ? ((const int*)dc.codes)[((b * L + t0) * cw) / 4 + e] : 0;
+    for (int i = 0; i < XPT; ++i) {
+      const int t = w + 4 * i;
+      if ((t0p + t < te) && dv) {
+        const float y = ((s_yp[LOCAL ? 0 : buf][0][t][lane] + s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 1][t][lane]) +
+                         s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 2][t][lane]) + s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 3][t][lane];
+        st_act(Y + (b * L + t0p + t) * a.ld_y + d, y + D_s * xprev[i]);
       }
-      rf = (tid < TT && t0 + tid < te) ? dc.deq[b * L + t0 + tid] : 0.0;
     }
   };
 
   load_tile(tb);
-  for (int64_t t0 = tb; t0 < te; t0 += TT) {
-    // 1. registers -> LDS
+  int buf = 0;
+  for (int64_t t0 = tb; t0 < te; t0 += TT, buf ^= 1) {
+    // 1. stage this tile: B, C; per item dt, softplus, dt * x
+    float xcur[XPT];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      s_x[w + 4 * i][lane] = rx[i];
-      if (!FUSED) s_d[FUSED ? 0 : w + 4 * i][lane] = rd[FUSED ? 0 : i];
+      const int t = w + 4 * i;
+      const float xv = rx[i];
+      xcur[i] = xv;
+      float dtv;
+      if (FUSED) {
+        int acc = 0;
+#pragma unroll
+        for (int q = 0; q < RW; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(rq[FUSED ? i : 0][q][j], wdt[q][j], acc, false);
+        dtv = (float)((s_dt * (double)acc) * rf[FUSED ? i : 0]);
+      } else {
+        dtv = rd[FUSED ? 0 : i];
+      }
+      dtv += bias_s;
+      if (a.softplus) dtv = softplus_f(dtv);
+      s_dd[buf][t][lane] = make_float2(dtv, dtv * xv);
     }
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
       const int e = tid + 256 * i;
       if (e < TT * NS) {
-        s_B[e / NS][e % NS] = rb[i];
-        if (!LOCAL) s_C[LOCAL ? 0 : e / NS][e % NS] = rc[i];
+        s_B[buf][e / NS][e % NS] = rb[i];
+        if (!LOCAL) s_C[LOCAL ? 0 : buf][LOCAL ? 0 : e / NS][e % NS] = rc[i];
       }
     }
-    if (FUSED) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int e = tid + 256 * k;
-        if (e < TT * cw / 4) ((int*)&s_q[0][0])[(e * 4 / (cw > 0 ? cw : 1)) * 16 + e % (cw > 0 ? cw / 4 : 1)] = rq[k];
-      }
-      if (tid < TT) s_rf[FUSED ? tid : 0] = rf;
-    }
-    __syncthreads();
-    // 2. next tile in flight while this one is processed
+    // 2. next tile in flight
     if (t0 + TT < te) load_tile(t0 + TT);
-    // 3. per (step, channel): dt, softplus, dt * x
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int t = w + 4 * i;
-      const float xv = s_x[t][lane];
-      float dtv;
-      if (FUSED) {
-        int acc = 0;
-        const int* qrow = (const int*)&s_q[FUSED ? t : 0][0];
-#pragma unroll
-        for (int q = 0; q < RW; ++q)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(qrow[q * 4 + j], wdt[q][j], acc, false);
-        dtv = (float)((s_dt * (double)acc) * s_rf[FUSED ? t : 0]);
-      } else {
-        dtv = s_d[FUSED ? 0 : t][lane];
-      }
-      dtv += bias_s;
-      if (a.softplus) dtv = softplus_f(dtv);
-      s_dd[t][lane] = make_float2(dtv, dtv * xv);
-    }
+    // 3.
     __syncthreads();
-    // 4. recurrence.  B and C of a step are the same for the whole wave (broadcast LDS reads at
-    //    immediate offsets); a group of G steps issues all its LDS reads, then one wait.
+    // 4. readout of the previous tile
+    if (!LOCAL && tprev >= 0) store_y(buf ^ 1, tprev);
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) xprev[i] = xcur[i];
+    tprev = t0;
+    // 5. recurrence.  B and C of a step are the same for the whole wave (broadcast LDS reads);
+    //    groups of GQ steps, software-pipelined: the LDS reads of group g + 1 are issued before
+    //    the arithmetic of group g
     const int tmax = (int)((te - t0) < TT ? (te - t0) : TT);
-    auto group = [&](int tt, auto gsz) {
-      constexpr int G = decltype(gsz)::value;
-      float bq[G][SPL], cq[G][SPL];
-      float2 dd[G];
-#pragma unroll
-      for (int u = 0; u < G; ++u) {
-        const int t = tt + u;
-        if (SPL % 4 == 0) {
-#pragma unroll
-          for (int i = 0; i < SPL; i += 4) {
-            const float4 b4 = *(const float4*)&s_B[t][w * SPL + i];
-            bq[u][i] = b4.x; bq[u][(i + 1) % SPL] = b4.y; bq[u][(i + 2) % SPL] = b4.z; bq[u][(i + 3) % SPL] = b4.w;
-            if (!LOCAL) {
-              const float4 c4 = *(const float4*)&s_C[LOCAL ? 0 : t][w * SPL + i];
-              cq[u][i] = c4.x; cq[u][(i + 1) % SPL] = c4.y; cq[u][(i + 2) % SPL] = c4.z; cq[u][(i + 3) % SPL] = c4.w;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < SPL; ++i) {
-            bq[u][i] = s_B[t][w * SPL + i];
-            if (!LOCAL) cq[u][i] = s_C[LOCAL ? 0 : t][w * SPL + i];
-          }
-        }
-        dd[u] = s_dd[t][lane];
-      }
-#pragma unroll
-      for (int u = 0; u < G; ++u) {
-        float yp = 0.0f;
-#pragma unroll
-        for (int i = 0; i < SPL; ++i) {
-          const float ab = __builtin_amdgcn_exp2f(dd[u].x * Al[i]);
-          h[i] = __builtin_fmaf(ab, h[i], dd[u].y * bq[u][i]);
-          if (!LOCAL) yp = i == 0 ? cq[u][0] * h[0] : __builtin_fmaf(cq[u][i], h[i], yp);
-        }
-        if (LOCAL) sum_dt += dd[u].x;
-        else s_yp[LOCAL ? 0 : w][LOCAL ? 0 : tt + u][lane] = yp;
-      }
-    };
     if (tmax == TT) {
-      // full tile: groups of GQ steps, software-pipelined: the LDS reads of group g + 1 are
-      // issued before the arithmetic of group g
-      constexpr int GQ = GT < 4 ? GT : 4, NG = TT / GQ;
+      constexpr int GQ = 4, NG = TT / GQ;
       float bq[2][GQ][SPL], cq[2][GQ][SPL];
       float2 dd[2][GQ];
       auto ld = [&](int tt, int sl) {
@@ -296,10 +270,10 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
           const int t = tt + u;
 #pragma unroll
           for (int i = 0; i < SPL; ++i) {
-            bq[sl][u][i] = s_B[t][w * SPL + i];
-            if (!LOCAL) cq[sl][u][i] = s_C[LOCAL ? 0 : t][w * SPL + i];
+            bq[sl][u][i] = s_B[buf][t][w * SPL + i];
+            if (!LOCAL) cq[sl][u][i] = s_C[LOCAL ? 0 : buf][LOCAL ? 0 : t][w * SPL + i];
           }
-          dd[sl][u] = s_dd[t][lane];
+          dd[sl][u] = s_dd[buf][t][lane];
         }
       };
       ld(0, 0);
@@ -317,25 +291,28 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
             if (!LOCAL) yp = i == 0 ? cq[sl][u][0] * h[0] : __builtin_fmaf(cq[sl][u][i], h[i], yp);
           }
           if (LOCAL) sum_dt += dd[sl][u].x;
-          else s_yp[LOCAL ? 0 : w][LOCAL ? 0 : g * GQ + u][lane] = yp;
+          else s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : w][LOCAL ? 0 : g * GQ + u][lane] = yp;
         }
       }
     } else {
-      for (int t = 0; t < tmax; ++t) group(t, std::integral_constant<int, 1>{});
-    }
-    if (!LOCAL) {
-      __syncthreads();
-      T* Y = (T*)a.y;
+      for (int t = 0; t < tmax; ++t) {
+        const float2 ddt = s_dd[buf][t][lane];
+        float yp = 0.0f;
 #pragma unroll
-      for (int i = 0; i < XPT; ++i) {
-        const int t = w + 4 * i;
-        if ((t0 + t < te) && dv) {
-          const float y = ((s_yp[0][t][lane] + s_yp[LOCAL ? 0 : 1][t][lane]) + s_yp[LOCAL ? 0 : 2][t][lane]) +
-                          s_yp[LOCAL ? 0 : 3][t][lane];
-          st_act(Y + (b * L + t0 + t) * a.ld_y + d, y + D_s * s_x[t][lane]);
+        for (int i = 0; i < SPL; ++i) {
+          const float ab = __builtin_amdgcn_exp2f(ddt.x * Al[i]);
+          h[i] = __builtin_fmaf(ab, h[i], ddt.y * s_B[buf][t][w * SPL + i]);
+          if (!LOCAL) yp = i == 0 ? s_C[LOCAL ? 0 : buf][LOCAL ? 0 : t][w * SPL] * h[0]
+                                  : __builtin_fmaf(s_C[LOCAL ? 0 : buf][LOCAL ? 0 : t][w * SPL + i], h[i], yp);
         }
+        if (LOCAL) sum_dt += ddt.x;
+        else s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : w][LOCAL ? 0 : t][lane] = yp;
       }
     }
+  }
+  if (!LOCAL && tprev >= 0) {
+    __syncthreads();
+    store_y(buf ^ 1, tprev);
   }
   if (LOCAL) {
     if (dv) {
@@ -369,7 +346,7 @@ __global__ __launch_bounds__(256) void k_scan_m1_combine(const float* __restrict
 
 namespace {
 constexpr int kCPB = 64;  // channels per block of k_scan_m1
-constexpr int kTT = 32;   // time steps per tile of k_scan_m1
+constexpr int kTT = 16;   // time steps per tile of k_scan_m1
 
 struct ScanPlan {
   int T = 1;
@@ -395,7 +372,7 @@ ScanPlan plan_scan(const ScanArgs& a) {
   p.T = (int)cdiv(a.L, p.chunk_len);
   const int64_t M = a.batch * a.L;
   size_t off = 0;
-  if (a.dr) {
+  if (a.R > 0) {  // the dt input's codes and dequantisation factors (dt_proj fused into the scan)
     p.cw = 16 * (int)cdiv(a.R, 16);
     off = round_up((int64_t)M * p.cw, 256);
     p.off_deq = off;

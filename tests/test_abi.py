@@ -179,6 +179,21 @@ def test_mixer_rejects():
                            None) == ALIGN
 
 
+def test_mixer_step_rejects():
+    L = tws.lib()
+    w = tws.MixerWeights()
+    for name, _ in tws.MixerWeights._fields_:
+        setattr(w, name, FAKE)
+    good = tws.mixer_config(0, 64, 128, 16, dt_rank=8)
+    step = L.ssm_mixer_step
+    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, None, 1, FAKE, 1 << 30, None) == NULL
+    assert step(ctypes.byref(tws.mixer_config(0, 64, 128, 16, dt_rank=0)), ctypes.byref(w), FAKE, FAKE + 4096, 2,
+                FAKE + 8192, 1, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, FAKE + 8192, 1, FAKE, 16,
+                None) == WORKSPACE
+    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE, 2, FAKE + 8192, 0, FAKE, 1 << 30, None) == SHAPE
+
+
 def test_mixer_fuses_front_query():
     """Host-only query: which Mamba-1 shapes run in_proj, x_proj and the dt quantisation fused."""
     L = tws.lib()

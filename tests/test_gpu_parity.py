@@ -336,3 +336,71 @@ def test_mixer_ssd_small_fp32():
     out = run_gpu_stack(cfg, [gw], u)
     ref = oracle.mixer(oracle_config(cfg), ow, u)
     assert rel_err(host(out), ref) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("name,over", [
+    ("trissm", dict(batch=2, seqlen=3, layers=1)),          # fused front
+    ("bitssm_tiny", dict(batch=3, seqlen=17)),
+    ("ternaryssm50m", dict(batch=1, seqlen=5, layers=1)),   # separate in_proj / x_proj
+    ("mamba2_ssd", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=7,
+                        layers=1)),
+])
+def test_mixer_stays_inside_workspace(name, over):
+    """Everything the mixer writes to its workspace lies within ssm_mixer_workspace_bytes: a
+    guard region after it keeps its fill pattern."""
+    cfg = wl.CONFIGS[name].with_(**over)
+    lat, u = wl.mixer_problem(cfg, seed=3, layers=1)
+    gw, _ = quantize_layer(cfg, lat[0])
+    c = gpu_config(cfg)
+    nb = tws.ssm_mixer_workspace_bytes(c, cfg.batch, cfg.seqlen)
+    buf = torch.full((nb + 4096,), 0xA5, dtype=torch.uint8, device=DEV)
+    h = to_dev(u, torch_dtype(cfg))
+    tws.ssm_mixer_fwd(c, tws.mixer_weights(gw), h, add_residual=True, out=h, workspace=buf[:nb])
+    assert bool((buf[nb:] == 0xA5).all())
+
+
+# ------------------------------------------------------------------ decode step
+
+def _decode(cfg, gw, u_host):
+    """Feed u [B, L, d] to ssm_mixer_step one token at a time from a zero state."""
+    c = gpu_config(cfg)
+    u = to_dev(u_host, torch_dtype(cfg))
+    B, L, _ = u.shape
+    shape = (B, cfg.d_inner, cfg.d_state) if cfg.kind == wl.MAMBA1 else (B, cfg.nheads, cfg.headdim, cfg.d_state)
+    state = torch.zeros(shape, dtype=torch.float32, device=DEV)
+    ws = torch.empty(tws.ssm_mixer_workspace_bytes(c, B, 1), dtype=torch.uint8, device=DEV)
+    mw = tws.mixer_weights(gw)
+    out = torch.empty_like(u)
+    for t in range(L):
+        tok = u[:, t].contiguous()
+        out[:, t] = tws.ssm_mixer_step(c, mw, tok, state, add_residual=True, workspace=ws)
+    return out, state
+
+
+DECODE_CASES = [
+    ("bitssm_tiny", {}, 42),
+    ("trissm", dict(batch=4, seqlen=24, layers=1), 7),
+    ("ternaryssm50m", dict(batch=3, seqlen=16, layers=1), 8),
+    ("mamba2_ssd", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=20,
+                        act_dtype="f32", layers=1), 9),
+    ("mamba2_ssd", dict(d_model=256, d_inner=256, d_state=128, nheads=4, headdim=64, batch=2, seqlen=12,
+                        layers=1), 10),
+]
+
+
+@pytest.mark.parametrize("name,over,seed", DECODE_CASES)
+def test_mixer_decode_step(name, over, seed):
+    """Token-by-token decoding reproduces the oracle's mixer over the whole sequence, and the
+    GPU's own whole-sequence forward."""
+    cfg = wl.CONFIGS[name].with_(**over)
+    lat, u = wl.mixer_problem(cfg, seed=seed, layers=1)
+    if cfg.act_dtype == "bf16":
+        u = bf16_values(u)
+    gw, ow = quantize_layer(cfg, lat[0])
+    out, state = _decode(cfg, gw, u)
+    ref = oracle.mixer(oracle_config(cfg), ow, u)
+    tol = TOL["bf16"] if cfg.act_dtype == "bf16" else TOL["f32"]
+    assert rel_err(host(out), ref) <= tol
+    full = host(run_gpu_stack(cfg, [gw], u))
+    assert rel_err(host(out), full) <= tol
+    assert bool(torch.isfinite(state).all()) and float(state.abs().max()) > 0
