@@ -11,6 +11,9 @@ Also measured, in a second timed loop that runs the same kernels through the sta
 points with HIP events around each stage: the average duration of every kernel stage, and
 the roofline of the dominant one.  The CPU oracle is timed on a bounded sample of the same
 workload on the host cores (a reported baseline, not the target).
+
+Also measured: token-by-token decoding of the same stack (one ssm_mixer_step per layer, the
+recurrent state carried in HBM), at the workload's batch and at batch 1.
 """
 from __future__ import annotations
 
@@ -67,6 +70,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--stages-only", action="store_true", help="skip the headline loop (profiling runs)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the token-by-token decode measurement")
+    ap.add_argument("--decode-only", action="store_true", help="only the decode measurement (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 3 plain device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -263,6 +268,63 @@ def read_traffic(kind: str, name: str, workload: str):
 
 # ------------------------------------------------------------------ CPU baseline
 
+def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
+    """Token-by-token decoding through the whole stack (ssm_mixer_step per layer, one token per
+    sequence, the recurrent state of every layer carried in HBM), one token step captured as a
+    HIP graph and replayed.  Algorithmic bytes per token step: the packed ternary weights and
+    scales of every layer, the fp32 state read and written, and the token's input and output."""
+    cfg = prob.cfg
+    L = tws.lib()
+    cb = ctypes.byref(prob.c)
+    es = 2 if prob.act == torch.bfloat16 else 4
+    wbytes = sum(t.numel() * t.element_size() for d in prob.layers for k, t in d.items())
+    out = {}
+    for B in batches:
+        nb = tws.ssm_mixer_workspace_bytes(prob.c, B, 1)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=prob.dev)
+        shape = (B, cfg.d_inner, cfg.d_state) if cfg.kind == wl.MAMBA1 else (B, cfg.nheads, cfg.headdim, cfg.d_state)
+        states = [torch.zeros(shape, dtype=torch.float32, device=prob.dev) for _ in prob.mws]
+        u = prob.u[:B, 0].contiguous()
+        bufs = [torch.empty_like(u), torch.empty_like(u)]
+
+        def token_step(sh):
+            h = u
+            for i, mw in enumerate(prob.mws):
+                o = bufs[i % 2]
+                st = L.ssm_mixer_step(cb, ctypes.byref(mw), h.data_ptr(), o.data_ptr(), B, states[i].data_ptr(), 1,
+                                      ws.data_ptr(), nb, sh)
+                if st != 0:
+                    raise tws.SsmError(st, L.ssm_last_error().decode())
+                h = o
+
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            token_step(s2.cuda_stream)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s2):
+                token_step(s2.cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        sbytes = 2 * sum(t.numel() * 4 for t in states)
+        byts = wbytes + sbytes + 2 * B * cfg.d_model * es
+        out[f"batch_{B}"] = {"us_per_token_step": us, "tokens_per_s": B / (us * 1e-6), "layers": len(prob.mws),
+                             "bytes_per_step": byts, "GBps": byts / (us * 1e-6) / 1e9,
+                             "finite": bool(all(torch.isfinite(t).all() for t in states))}
+        del g
+    return out
+
+
 def cpu_baseline(cfg: wl.MixerConfig, seed: int, target_s: float) -> dict:
     import oracle
     from oracle import mixer_stack
@@ -311,6 +373,10 @@ def main():
     prob = Problem(cfg, args.seed, dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+
+    if args.decode_only:
+        print(json.dumps({"decode": decode_bench(prob, args.steps, args.warmup, (cfg.batch, 1))}))
+        return
 
     result = {}
     if not args.stages_only:
@@ -479,6 +545,8 @@ def main():
         "layer": layer,
         "roofline": roof,
     }
+    if not args.no_decode:
+        line["decode"] = decode_bench(prob, max(args.steps, 50), args.warmup, (cfg.batch, 1))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds)
     print(json.dumps(line))
