@@ -49,7 +49,7 @@ class _MixerWeights(ctypes.Structure):
     _fields_ = [("c_in", _c_i8p), ("c_x", _c_i8p), ("c_dt", _c_i8p), ("c_out", _c_i8p),
                 ("s_in", _c_f32p), ("s_x", _c_f32p), ("s_dt", _c_f32p), ("s_out", _c_f32p),
                 ("g_in", _c_f32p), ("g_x", _c_f32p), ("g_dt", _c_f32p), ("g_out", _c_f32p),
-                ("dt_bias", _c_f32p), ("A", _c_f32p), ("D", _c_f32p)]
+                ("dt_bias", _c_f32p), ("A", _c_f32p), ("D", _c_f32p), ("conv_w", _c_f32p), ("conv_b", _c_f32p)]
 
 
 def lib():
@@ -87,8 +87,12 @@ def lib():
         L.orc_selective_scan_quadratic.argtypes = scan_args + [_c_f64p]
         L.orc_mixer.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_float, ctypes.POINTER(_MixerWeights), _c_f32p,
-                                _i64, _i64, ctypes.c_int, _c_f64p]
+                                _i64, _i64, ctypes.c_int, ctypes.c_int, _i64, _c_f64p]
         L.orc_mixer.restype = ctypes.c_int
+        L.orc_silu.argtypes = [ctypes.c_double]
+        L.orc_silu.restype = ctypes.c_double
+        L.orc_conv_silu.argtypes = [_i64, _i64, _i64, _i64, _c_f32p, _i64, _c_f32p, _c_f32p, _c_f32p, ctypes.c_int,
+                                    _c_f32p, _c_f32p]
         _lib = L
     return _lib
 
@@ -254,6 +258,32 @@ def selective_scan(x, delta, A, Bm, Cm, D=None, delta_bias=None, softplus: bool 
     return y, hl
 
 
+# ---------------------------------------------------------------- gated block
+
+def silu(v: float) -> float:
+    return float(lib().orc_silu(v))
+
+
+def conv_silu(x, w, bias=None, state=None, act_dtype: int = 0, channels: int | None = None):
+    """Causal depthwise convolution of width K = w.shape[1] along time, then SiLU (fp64,
+    rounded to act_dtype).  x [B, L, ldx] (first `channels` columns used), w [C, K],
+    bias [C] or None, state [B, K-1, C] or None (inputs before t = 0; zeros if None).
+    Returns (out [B, L, C] fp32, state after the sequence [B, K-1, C] fp32)."""
+    x = _f32(x)
+    batch, L, ldx = x.shape
+    w = _f32(w)
+    C, K = w.shape
+    if channels is not None and channels != C:
+        raise ValueError("w rows must equal channels")
+    b = None if bias is None else _f32(bias)
+    st = None if state is None else _f32(state)
+    out = np.empty((batch, L, C), dtype=np.float32)
+    st_out = np.empty((batch, max(K - 1, 0), C), dtype=np.float32)
+    lib().orc_conv_silu(batch, L, C, K, _p(x, _c_f32p), ldx, _p(w, _c_f32p), _p(b, _c_f32p), _p(st, _c_f32p),
+                        act_dtype, _p(out, _c_f32p), _p(st_out, _c_f32p) if K > 1 else None)
+    return out, st_out
+
+
 # ---------------------------------------------------------------- mixer
 
 MAMBA1, SSD = 0, 1
@@ -262,7 +292,8 @@ MAMBA1, SSD = 0, 1
 def mixer(cfg, weights: dict, u, residual: bool = True) -> np.ndarray:
     """One mixer layer.  cfg: mapping with kind, d_model, d_inner, d_state, dt_rank,
     nheads, headdim, group_size, act_bits, act_dtype (F32/BF16), norm_eps.
-    weights: codes c_in/c_x/c_dt/c_out, scales s_*, dt_bias, A, D (gains optional g_*).
+    weights: codes c_in/c_x/c_dt/c_out, scales s_*, dt_bias, A, D (gains optional g_*); for the
+    gated block (cfg gated = 1, d_conv) also conv_w [Cc, d_conv] and conv_b [Cc] (optional).
     u: [B, L, d_model] values (bf16-representable when act_dtype is BF16).
     Returns out fp64 [B, L, d_model], each value already rounded to act_dtype."""
     u = _f32(u)
@@ -283,12 +314,13 @@ def mixer(cfg, weights: dict, u, residual: bool = True) -> np.ndarray:
         arr("s_dt", np.float32, _c_f32p), arr("s_out", np.float32, _c_f32p),
         arr("g_in", np.float32, _c_f32p), arr("g_x", np.float32, _c_f32p), arr("g_dt", np.float32, _c_f32p),
         arr("g_out", np.float32, _c_f32p), arr("dt_bias", np.float32, _c_f32p),
-        arr("A", np.float32, _c_f32p), arr("D", np.float32, _c_f32p))
+        arr("A", np.float32, _c_f32p), arr("D", np.float32, _c_f32p), arr("conv_w", np.float32, _c_f32p),
+        arr("conv_b", np.float32, _c_f32p))
     out = np.empty((batch, L, dm), dtype=np.float64)
     rc = lib().orc_mixer(int(cfg["kind"]), cfg["d_model"], cfg["d_inner"], cfg["d_state"], cfg.get("dt_rank", 0),
                          cfg.get("nheads", 0), cfg.get("headdim", 0), cfg.get("group_size", 0), cfg["act_bits"],
                          cfg["act_dtype"], cfg.get("norm_eps", 1e-5), ctypes.byref(w), _p(u, _c_f32p), batch, L,
-                         int(residual), _p(out, _c_f64p))
+                         int(residual), int(cfg.get("gated", 0)), int(cfg.get("d_conv", 0)), _p(out, _c_f64p))
     if rc != 0:
         raise OverflowError("int32 accumulator overflow in the mixer")
     return out

@@ -26,6 +26,9 @@
  *             exp(Delta A) discretisation, selective recurrence); and in
  *             "SSDi8 ...", section "Builds on": "Transformers are SSMs" (state
  *             space duality, scalar A per head) and S4 (convolution mode).
+ *  [Shape]    "Baseline Shape Decides the Verdict: A Controlled Re-Examination of
+ *             Ternary Language Models at 60K Parameters", abstract, finding (ii):
+ *             a plain gated diagonal-SSM block is the strongest block measured.
  *
  * Precision: every floating-point result is computed in fp64, except the steps
  * whose float value decides an integer (the absmean scale feeding the ternary
@@ -452,6 +455,51 @@ void orc_selective_scan_quadratic(int64_t batch, int64_t L, int64_t H, int64_t P
 }
 
 /* ------------------------------------------------------------------------- */
+/* O8: the gated block around the mixer ([Builds-on] Mamba: the block's short   */
+/* causal depthwise convolution with SiLU on the SSM input, and the SiLU gate   */
+/* from the second in_proj branch; [Shape]: the gated diagonal-SSM block)      */
+/* ------------------------------------------------------------------------- */
+
+/* SiLU (x times the logistic sigmoid of x), fp64. */
+double orc_silu(double a) { return a / (1.0 + exp(-a)); }
+
+/*
+ * Causal depthwise convolution of width K along time, then SiLU, per channel:
+ *   a[b, t, c] = bias[c] + sum_{j=0..K-1} w[c, j] * x[b, t - (K - 1) + j, c]
+ *   out[b, t, c] = silu(a), fp64, rounded to act_dtype.
+ * x[b, t, c] at t < 0 is state[b, t + K - 1, c] when state is given, else 0.
+ * Layout: x [B, L, ldx] (channels 0..C-1 used), w [C, K], bias [C] or NULL,
+ * state [B, K - 1, C] or NULL, out [B, L, C].  state_out (nullable) [B, K - 1, C]
+ * receives the last K - 1 inputs (from state and x), i.e. the state after the sequence.
+ */
+void orc_conv_silu(int64_t batch, int64_t L, int64_t C, int64_t K, const float* x, int64_t ldx,
+                   const float* w, const float* bias, const float* state, int act_dtype, float* out,
+                   float* state_out) {
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t c = 0; c < C; ++c) {
+      for (int64_t t = 0; t < L; ++t) {
+        double a = bias ? (double)bias[c] : 0.0;
+        for (int64_t j = 0; j < K; ++j) {
+          int64_t ts = t - (K - 1) + j;
+          double xv = 0.0;
+          if (ts >= 0) xv = (double)x[(b * L + ts) * ldx + c];
+          else if (state) xv = (double)state[(b * (K - 1) + (ts + K - 1)) * C + c];
+          a += (double)w[c * K + j] * xv;
+        }
+        out[(b * L + t) * C + c] = (float)store_as(orc_silu(a), act_dtype);
+      }
+      if (state_out)
+        for (int64_t i = 0; i < K - 1; ++i) {
+          int64_t ts = L - (K - 1) + i;  /* input time held in slot i */
+          float v = 0.0f;
+          if (ts >= 0) v = x[(b * L + ts) * ldx + c];
+          else if (state) v = state[(b * (K - 1) + (ts + K - 1)) * C + c];
+          state_out[(b * (K - 1) + i) * C + c] = v;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* O5 / O6: the mixer ([TriSSM] BitSSM mixer; [TMamba] W1.58A16 SSD shape)     */
 /* ------------------------------------------------------------------------- */
 
@@ -465,6 +513,7 @@ typedef struct {
   const float *s_in, *s_x, *s_dt, *s_out;
   const float *g_in, *g_x, *g_dt, *g_out; /* RMSNorm gains or NULL */
   const float *dt_bias, *A, *D;
+  const float *conv_w, *conv_b; /* gated block only: [Cc, d_conv], [Cc] or NULL */
 } orc_mixer_weights;
 
 /*
@@ -477,18 +526,25 @@ typedef struct {
  *   y = scan(x, softplus(dt + dt_bias), A[H], B, C, D);  out = BL(y; W_out) (+ u).
  * Every stored activation (x, p, v, y, out) is rounded to act_dtype, as a
  * kernel that stores it must.
+ * Gated block (gated != 0, O8): in_proj gains Di output rows for the gate branch
+ * zg, placed after the others ([x | zg] for Mamba-1, [x | B | C | dt | zg] for
+ * SSD); the SSM input channels (x for Mamba-1, x, B and C for SSD; Cc of them)
+ * go through orc_conv_silu of width d_conv before anything reads them, and the
+ * scan output becomes y * silu(zg) (fp64, rounded to act_dtype) before out_proj.
  */
 int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
               int64_t nheads, int64_t headdim, int64_t group, int act_bits, int act_dtype,
               float eps, const orc_mixer_weights* w, const float* u, int64_t batch, int64_t L,
-              int residual, double* out) {
+              int residual, int gated, int64_t d_conv, double* out) {
   int64_t M = batch * L, Dm = d_model, Di = d_inner, N = d_state, R = dt_rank;
   int rc = 0;
   float* y32 = (float*)malloc(sizeof(float) * (size_t)(M * Di));
   double* yd = (double*)malloc(sizeof(double) * (size_t)(M * Di));
+  float* zg = gated ? (float*)malloc(sizeof(float) * (size_t)(M * Di)) : NULL;
   if (kind == 0) {
-    int64_t PW = R + 2 * N;
-    double* xd = (double*)malloc(sizeof(double) * (size_t)(M * Di));
+    int64_t PW = R + 2 * N, XW = gated ? 2 * Di : Di;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)(M * XW));
+    float* xz = (float*)malloc(sizeof(float) * (size_t)(M * XW));
     float* x32 = (float*)malloc(sizeof(float) * (size_t)(M * Di));
     double* pd = (double*)malloc(sizeof(double) * (size_t)(M * PW));
     float* p32 = (float*)malloc(sizeof(float) * (size_t)(M * PW));
@@ -496,9 +552,16 @@ int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64
     float* z32 = (float*)malloc(sizeof(float) * (size_t)(M * Di));
     float* B32 = (float*)malloc(sizeof(float) * (size_t)(M * N));
     float* C32 = (float*)malloc(sizeof(float) * (size_t)(M * N));
-    rc |= orc_bitlinear(u, M, Dm, Dm, w->g_in, eps, act_bits, w->c_in, w->s_in, Di, group, NULL,
+    rc |= orc_bitlinear(u, M, Dm, Dm, w->g_in, eps, act_bits, w->c_in, w->s_in, XW, group, NULL,
                         xd, NULL, NULL, NULL);
-    orc_round_array(xd, x32, M * Di, act_dtype);
+    orc_round_array(xd, xz, M * XW, act_dtype);
+    if (gated) {
+      orc_conv_silu(batch, L, Di, d_conv, xz, XW, w->conv_w, w->conv_b, NULL, act_dtype, x32, NULL);
+      for (int64_t i = 0; i < M; ++i)
+        for (int64_t c = 0; c < Di; ++c) zg[i * Di + c] = xz[i * XW + Di + c];
+    } else {
+      memcpy(x32, xz, sizeof(float) * (size_t)(M * Di));
+    }
     rc |= orc_bitlinear(x32, M, Di, Di, w->g_x, eps, act_bits, w->c_x, w->s_x, PW, group, NULL, pd,
                         NULL, NULL, NULL);
     orc_round_array(pd, p32, M * PW, act_dtype);
@@ -514,11 +577,13 @@ int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64
       }
     orc_selective_scan(batch, L, Di, 1, N, 1, x32, z32, w->dt_bias, 1, w->A, B32, C32, w->D, NULL,
                        yd, NULL);
-    free(xd); free(x32); free(pd); free(p32); free(zd); free(z32); free(B32); free(C32);
+    free(xd); free(xz); free(x32); free(pd); free(p32); free(zd); free(z32); free(B32); free(C32);
   } else {
-    int64_t H = nheads, P = headdim, VW = H * P + 2 * N + H;
+    int64_t H = nheads, P = headdim, VW0 = H * P + 2 * N + H, VW = gated ? VW0 + Di : VW0;
+    int64_t Cc = H * P + 2 * N;
     double* vd = (double*)malloc(sizeof(double) * (size_t)(M * VW));
     float* v32 = (float*)malloc(sizeof(float) * (size_t)(M * VW));
+    float* xbc = (float*)malloc(sizeof(float) * (size_t)(M * Cc));
     float* xs = (float*)malloc(sizeof(float) * (size_t)(M * H * P));
     float* B32 = (float*)malloc(sizeof(float) * (size_t)(M * N));
     float* C32 = (float*)malloc(sizeof(float) * (size_t)(M * N));
@@ -526,18 +591,29 @@ int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64
     rc |= orc_bitlinear(u, M, Dm, Dm, w->g_in, eps, act_bits, w->c_in, w->s_in, VW, group, NULL, vd,
                         NULL, NULL, NULL);
     orc_round_array(vd, v32, M * VW, act_dtype);
+    if (gated) {
+      orc_conv_silu(batch, L, Cc, d_conv, v32, VW, w->conv_w, w->conv_b, NULL, act_dtype, xbc, NULL);
+    } else {
+      for (int64_t i = 0; i < M; ++i)
+        for (int64_t c = 0; c < Cc; ++c) xbc[i * Cc + c] = v32[i * VW + c];
+    }
     for (int64_t i = 0; i < M; ++i) {
-      for (int64_t c = 0; c < H * P; ++c) xs[i * H * P + c] = v32[i * VW + c];
+      for (int64_t c = 0; c < H * P; ++c) xs[i * H * P + c] = xbc[i * Cc + c];
       for (int64_t s = 0; s < N; ++s) {
-        B32[i * N + s] = v32[i * VW + H * P + s];
-        C32[i * N + s] = v32[i * VW + H * P + N + s];
+        B32[i * N + s] = xbc[i * Cc + H * P + s];
+        C32[i * N + s] = xbc[i * Cc + H * P + N + s];
       }
       for (int64_t hd = 0; hd < H; ++hd) dt32[i * H + hd] = v32[i * VW + H * P + 2 * N + hd];
+      if (gated)
+        for (int64_t c = 0; c < Di; ++c) zg[i * Di + c] = v32[i * VW + VW0 + c];
     }
     orc_selective_scan(batch, L, H, P, N, 0, xs, dt32, w->dt_bias, 1, w->A, B32, C32, w->D, NULL,
                        yd, NULL);
-    free(vd); free(v32); free(xs); free(B32); free(C32); free(dt32);
+    free(vd); free(v32); free(xbc); free(xs); free(B32); free(C32); free(dt32);
   }
+  if (gated)
+    for (int64_t i = 0; i < M * Di; ++i) yd[i] = yd[i] * orc_silu((double)zg[i]);
+  free(zg);
   orc_round_array(yd, y32, M * Di, act_dtype);
   rc |= orc_bitlinear(y32, M, Di, Di, w->g_out, eps, act_bits, w->c_out, w->s_out, Dm, group, NULL,
                       out, NULL, NULL, NULL);

@@ -10,6 +10,7 @@ import os
 
 import numpy as np
 import pytest
+from scipy.special import expit
 
 import oracle
 import workloads as wl
@@ -552,3 +553,176 @@ def test_round_bf16():
     got = oracle.round_bf16(vals)
     np.testing.assert_array_equal(got[:5], np.array([one, one, one + 2 * ulp, one, -(one + ulp)], np.float32))
     assert got[5] == pytest.approx(3.0e-39, rel=2 ** -7)
+
+
+# ------------------------------------------------------------------ gated block (conv + SiLU gate)
+
+def _silu_tanh(a):
+    """SiLU through library routines, not the oracle's form: a * expit(a) (scipy's logistic
+    sigmoid); on |a| <= 8 also checked against the identity a (1 + tanh(a / 2)) / 2."""
+    a = np.asarray(a, dtype=np.float64)
+    return a * expit(a)
+
+
+def test_silu_values():
+    """SiLU: silu(0) = 0, silu(a) - silu(-a) = a, sigmoid(1) = e / (1 + e), and the tanh form."""
+    assert oracle.silu(0.0) == 0.0
+    for a in (0.3, 1.0, 2.5, 7.0, 19.0):
+        assert abs((oracle.silu(a) - oracle.silu(-a)) - a) <= 4e-16 * max(1.0, a)
+    assert oracle.silu(1.0) == pytest.approx(math.e / (1.0 + math.e), rel=1e-15)
+    for a in np.linspace(-30.0, 30.0, 121):
+        assert oracle.silu(float(a)) == pytest.approx(float(_silu_tanh(a)), rel=1e-13, abs=1e-300)
+        if abs(a) <= 8.0:
+            assert oracle.silu(float(a)) == pytest.approx(float(a * (1.0 + math.tanh(a / 2.0)) / 2.0), rel=1e-12)
+    assert oracle.silu(-800.0) == 0.0  # exp overflow: the product underflows to zero
+
+
+def _conv_ref(x, w, bias, state=None):
+    """Brute force through numpy's full convolution, per (sequence, channel), fp64."""
+    batch, L, _ = x.shape
+    C, K = w.shape
+    out = np.zeros((batch, L, C))
+    for b in range(batch):
+        for c in range(C):
+            seq = x[b, :, c].astype(np.float64)
+            pre = np.zeros(K - 1) if state is None else state[b, :, c].astype(np.float64)
+            full = np.convolve(np.concatenate([pre, seq]), w[c, ::-1].astype(np.float64))
+            out[b, :, c] = full[K - 1:K - 1 + L] + (0.0 if bias is None else float(bias[c]))
+    return _silu_tanh(out)
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_conv_silu_vs_numpy_convolve(K):
+    g = wl.rng(5 + K)
+    x = wl.normal(g, (2, 37, 24))
+    w = wl.normal(g, (20, K), 0.0, 0.5)
+    bias = wl.normal(g, (20,), 0.0, 0.2)
+    out, _ = oracle.conv_silu(x, w, bias)
+    ref = _conv_ref(x[:, :, :20], w, bias)
+    np.testing.assert_allclose(out, ref, rtol=2 ** -23, atol=1e-30)
+    assert out.dtype == np.float32
+
+
+def test_conv_silu_taps_direction():
+    """A one-hot kernel at the last tap is SiLU of the current input; at the first tap it is
+    SiLU of the input K - 1 steps back, with zeros (SiLU(0) = 0) before the sequence starts."""
+    g = wl.rng(11)
+    x = wl.normal(g, (1, 9, 3))
+    K = 4
+    w_now = np.zeros((3, K), np.float32)
+    w_now[:, K - 1] = 1.0
+    out, _ = oracle.conv_silu(x, w_now)
+    np.testing.assert_allclose(out, _silu_tanh(x), rtol=2 ** -23)
+    w_old = np.zeros((3, K), np.float32)
+    w_old[:, 0] = 1.0
+    out, _ = oracle.conv_silu(x, w_old)
+    assert np.all(out[:, :K - 1] == 0.0)
+    np.testing.assert_allclose(out[:, K - 1:], _silu_tanh(x[:, :-(K - 1)]), rtol=2 ** -23)
+
+
+def test_conv_silu_streaming_state():
+    """Splitting a sequence and carrying the state gives the same values bit for bit; the
+    state after a sequence is its last K - 1 inputs."""
+    g = wl.rng(12)
+    x = wl.normal(g, (2, 30, 8))
+    w = wl.normal(g, (8, 4), 0.0, 0.5)
+    bias = wl.normal(g, (8,), 0.0, 0.2)
+    full, st_full = oracle.conv_silu(x, w, bias)
+    a, st_a = oracle.conv_silu(x[:, :11], w, bias)
+    b, st_b = oracle.conv_silu(x[:, 11:], w, bias, state=st_a)
+    np.testing.assert_array_equal(np.concatenate([a, b], axis=1), full)
+    np.testing.assert_array_equal(st_b, st_full)
+    np.testing.assert_array_equal(st_full, x[:, -3:])
+    # a short piece (fewer inputs than K - 1) shifts the old state
+    c, st_c = oracle.conv_silu(x[:, 11:13], w, bias, state=st_a)
+    np.testing.assert_array_equal(st_c, np.concatenate([st_a[:, 2:], x[:, 11:13]], axis=1))
+    np.testing.assert_array_equal(c, full[:, 11:13])
+
+
+def _gated_layer(cfg, seed):
+    lat, u = wl.mixer_problem(cfg, seed=seed)
+    w = _layer_codes(cfg, lat[0])
+    w["conv_w"], w["conv_b"] = lat[0]["conv_w"], lat[0]["conv_b"]
+    return w, u
+
+
+def _gated_cfg_dict(cfg):
+    d = _cfg_dict(cfg)
+    d.update(gated=cfg.gated, d_conv=cfg.d_conv)
+    return d
+
+
+GATED_SMALL = {
+    "mamba1": wl.CONFIGS["bitssm_tiny"].with_(gated=1, d_conv=4, seqlen=24),
+    "ssd": wl.CONFIGS["mamba2_ssd_gated"].with_(d_model=128, d_inner=128, d_state=16, nheads=2, headdim=64,
+                                                  batch=2, seqlen=20, act_dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("kind", ["mamba1", "ssd"])
+def test_mixer_gated_zero_gate_is_identity(kind):
+    """Gate rows of W_in all zero: SiLU(0) = 0 zeroes the scan output, out_proj of a zero row is
+    zero, so the layer returns u exactly -- the gate acts between the scan and out_proj."""
+    cfg = GATED_SMALL[kind]
+    w, u = _gated_layer(cfg, 21)
+    zg0 = w["c_in"].shape[0] - cfg.d_inner
+    w["c_in"] = w["c_in"].copy()
+    w["c_in"][zg0:] = 0
+    out = oracle.mixer(_gated_cfg_dict(cfg), w, u)
+    np.testing.assert_array_equal(out, u.astype(np.float64))
+    # with the gate rows back, the layer is not the identity
+    w2, _ = _gated_layer(cfg, 21)
+    assert not np.array_equal(oracle.mixer(_gated_cfg_dict(cfg), w2, u), u.astype(np.float64))
+
+
+@pytest.mark.parametrize("kind", ["mamba1", "ssd"])
+def test_mixer_gated_zero_conv_is_identity(kind):
+    """Convolution weights and bias zero: every SSM input (x; and B, C for SSD) is SiLU(0) = 0,
+    so x_proj, the scan state, C h and D x all vanish and the layer returns u exactly -- the
+    convolved values feed x_proj and the scan, including the D x term."""
+    cfg = GATED_SMALL[kind]
+    w, u = _gated_layer(cfg, 22)
+    w["conv_w"] = np.zeros_like(w["conv_w"])
+    w["conv_b"] = np.zeros_like(w["conv_b"])
+    out = oracle.mixer(_gated_cfg_dict(cfg), w, u)
+    np.testing.assert_array_equal(out, u.astype(np.float64))
+
+
+@pytest.mark.parametrize("kind", ["mamba1", "ssd"])
+def test_mixer_gated_delay_tap(kind):
+    """Kernel one-hot at the oldest tap, no bias: the SSM sees inputs delayed by K - 1 steps and
+    zeros before, so the first K - 1 outputs are u exactly and the K-th is not (causal order of
+    the taps)."""
+    cfg = GATED_SMALL[kind]
+    w, u = _gated_layer(cfg, 23)
+    K = cfg.d_conv
+    cw = np.zeros_like(w["conv_w"])
+    cw[:, 0] = 1.0
+    w["conv_w"], w["conv_b"] = cw, np.zeros_like(w["conv_b"])
+    out = oracle.mixer(_gated_cfg_dict(cfg), w, u)
+    np.testing.assert_array_equal(out[:, :K - 1], u[:, :K - 1].astype(np.float64))
+    assert not np.array_equal(out[:, K - 1], u[:, K - 1].astype(np.float64))
+
+
+def test_mixer_gated_mamba1_composition():
+    """The gated Mamba-1 layer equals in_proj -> [x | zg], conv + SiLU on x (pinned above), the
+    ungated stages on the convolved x, the gate y * SiLU(zg) (tanh form here) and out_proj."""
+    cfg = GATED_SMALL["mamba1"]
+    w, u = _gated_layer(cfg, 24)
+    out = oracle.mixer(_gated_cfg_dict(cfg), w, u)
+    M, Di, R, N = cfg.tokens, cfg.d_inner, cfg.dt_rank, cfg.d_state
+    sh = (cfg.batch, cfg.seqlen)
+    uu = u.reshape(M, -1)
+    xz, *_ = oracle.bitlinear(uu, w["c_in"], w["s_in"])
+    xz = xz.astype(np.float32)
+    xc, _ = oracle.conv_silu(xz[:, :Di].reshape(*sh, -1), w["conv_w"], w["conv_b"])
+    xc = xc.reshape(M, Di)
+    p, *_ = oracle.bitlinear(xc, w["c_x"], w["s_x"])
+    p = p.astype(np.float32)
+    z, *_ = oracle.bitlinear(p, w["c_dt"], w["s_dt"], k=R)
+    y, _ = oracle.selective_scan(xc.reshape(*sh, -1), z.astype(np.float32).reshape(*sh, -1), w["A"],
+                                 p[:, R:R + N].reshape(*sh, -1), p[:, R + N:].reshape(*sh, -1), w["D"], w["dt_bias"])
+    yg = (y.reshape(M, Di) * _silu_tanh(xz[:, Di:])).astype(np.float32)
+    o, *_ = oracle.bitlinear(yg, w["c_out"], w["s_out"])
+    ref = (o + uu).astype(np.float32).astype(np.float64).reshape(out.shape)
+    np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-6)

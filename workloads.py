@@ -4,7 +4,7 @@ This module only draws random numbers and describes shapes; it holds none of
 the mixer's arithmetic.  Both the HIP path and the CPU oracle receive exactly
 the arrays drawn here.
 
-The five workloads follow the model shapes of the pages:
+The workloads follow the model shapes of the pages:
   * bitssm_tiny   one BitSSM mixer layer, fp32 (a small case the oracle finishes quickly)
   * trissm        the TriSSM stack of the TriSSM README ("selective SSM, 12 layers,
                   d=256", trained on 64 x 256-token batches), fp32 activations
@@ -16,9 +16,12 @@ The five workloads follow the model shapes of the pages:
   * mamba2_a8     the same SSD mixer shape with int8 absmax activations and one scale
                   per tensor: the A8 contraction at its largest shapes, (8192, 4416, 2048)
                   and (8192, 2048, 4096), where it is bound by the int8 matrix cores
+  * trissm_gated, mamba2_ssd_gated: the same shapes as the gated block (a short causal
+                  convolution of width 4 with SiLU on the SSM input, a SiLU gate from a
+                  second in_proj branch)
 Distributions: activations u ~ N(0,1); latent weights ~ N(0, 0.02); A = -exp(U[ln 1,
 ln 16]) per (channel, state) (per head for SSD); D ~ N(1, 0.1); dt_bias ~ N(-2, 1);
-RMSNorm gains are ones.  No dataset is read: these stand in for the activations of
+convolution weights and biases ~ U(-1/sqrt(width), 1/sqrt(width)); RMSNorm gains are ones.  No dataset is read: these stand in for the activations of
 TinyStories / WikiText-103 / zero-shot-suite runs, which are not available here.
 """
 from __future__ import annotations
@@ -48,6 +51,8 @@ class MixerConfig:
     act_bits: int = 8           # 8: int8 absmax activations (A8); 16: unquantised (A16)
     group_size: int = 0         # 0: one absmean scale per tensor; >0: per (row, group)
     norm_eps: float = 1e-5
+    gated: int = 0              # 1: the gated block (short causal convolution + SiLU gate)
+    d_conv: int = 0             # width of that convolution
 
     @property
     def tokens(self) -> int:
@@ -56,13 +61,19 @@ class MixerConfig:
     @property
     def proj_shapes(self) -> dict:
         """(n_out, k) of each ternary projection."""
+        zg = self.d_inner if self.gated else 0  # gate branch rows of in_proj
         if self.kind == MAMBA1:
-            return {"in": (self.d_inner, self.d_model),
+            return {"in": (self.d_inner + zg, self.d_model),
                     "x": (self.dt_rank + 2 * self.d_state, self.d_inner),
                     "dt": (self.d_inner, self.dt_rank),
                     "out": (self.d_model, self.d_inner)}
         vw = self.nheads * self.headdim + 2 * self.d_state + self.nheads
-        return {"in": (vw, self.d_model), "out": (self.d_model, self.d_inner)}
+        return {"in": (vw + zg, self.d_model), "out": (self.d_model, self.d_inner)}
+
+    @property
+    def conv_channels(self) -> int:
+        """Channels through the short convolution: x (Mamba-1), or x, B and C (SSD)."""
+        return self.d_inner if self.kind == MAMBA1 else self.d_inner + 2 * self.d_state
 
     def with_(self, **kw) -> "MixerConfig":
         d = dict(self.__dict__)
@@ -81,7 +92,12 @@ CONFIGS = {
     "mamba2_a8": MixerConfig("mamba2_a8", SSD, 2048, 4096, 128, batch=4, seqlen=2048, nheads=64, headdim=64,
                              act_dtype="bf16", act_bits=8, group_size=0),
 }
-CONFIG_ORDER = ["bitssm_tiny", "trissm", "long_scan", "ternaryssm50m", "mamba2_ssd", "mamba2_a8"]
+# the gated block around the mixer (short causal convolution of width 4 with SiLU on the SSM
+# input, SiLU gate from a second in_proj branch), at the TriSSM and Mamba-2 shapes
+CONFIGS["trissm_gated"] = CONFIGS["trissm"].with_(name="trissm_gated", gated=1, d_conv=4)
+CONFIGS["mamba2_ssd_gated"] = CONFIGS["mamba2_ssd"].with_(name="mamba2_ssd_gated", gated=1, d_conv=4)
+CONFIG_ORDER = ["bitssm_tiny", "trissm", "long_scan", "ternaryssm50m", "mamba2_ssd", "mamba2_a8", "trissm_gated",
+                "mamba2_ssd_gated"]
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -106,6 +122,10 @@ def layer_latent(cfg: MixerConfig, g: np.random.Generator) -> dict:
     out["A"] = a_log_uniform(g, (h, cfg.d_state) if cfg.kind == MAMBA1 else (h,))
     out["D"] = normal(g, (h,), 1.0, 0.1)
     out["dt_bias"] = normal(g, (h,), -2.0, 1.0)
+    if cfg.gated:  # depthwise convolution, uniform on +-1/sqrt(width) (fan-in of one channel)
+        bnd = 1.0 / math.sqrt(cfg.d_conv)
+        out["conv_w"] = g.uniform(-bnd, bnd, (cfg.conv_channels, cfg.d_conv)).astype(np.float32)
+        out["conv_b"] = g.uniform(-bnd, bnd, (cfg.conv_channels,)).astype(np.float32)
     return out
 
 
