@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum {
   SSM_OK = 0,
@@ -186,6 +186,9 @@ ssm_status ssm_bitlinear_fwd(const ssm_bitlinear_args* a, void* workspace, size_
  * columns (row stride ld_dt_in, act_dtype) with packed weights w_dt [nheads, dt_rank],
  * scale s_dt [1], RMSNorm gains g_dt [dt_rank] or NULL and epsilon dt_eps; it is computed
  * inside the scan and never stored.  dt_rank must be in [1, 64].
+ * Optional gate (the gated block: Mamba's SiLU gate from a second in_proj branch): when
+ * gate is not NULL ([B, L, nheads * headdim] of act_dtype, row stride ld_gate), the stored
+ * y is the y above times SiLU(gate) = gate / (1 + exp(-gate)), computed in fp32.
  * Supported: a_per_state = 1 with headdim = 1 and d_state in {4, 8, 16, 32, 64};
  * a_per_state = 0 with headdim <= 256 and d_state in {16, 32, 64, 128}.
  * batch == 0 or seqlen == 0 launches nothing (h_last is then not written).
@@ -216,6 +219,8 @@ typedef struct {
   const float* g_dt;
   float dt_eps;
   int32_t pad1;
+  /* optional gate (see above) */
+  const void* gate;   int64_t ld_gate;
 } ssm_scan_args;
 
 size_t ssm_selective_scan_workspace_bytes(const ssm_scan_args* a);
@@ -232,6 +237,12 @@ ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* workspace, size_
  *      y = scan(x, dt, dt_bias, A [nheads], B, C, D);  out = BL(y; W_out).
  *  BL is ssm_bitlinear_fwd with the configuration's act_bits, group_size and norm_eps;
  *  x, p, v, y and out are stored in act_dtype; out += u when add_residual != 0.
+ *  Gated block (gated = 1; Mamba's block around the selective SSM, the gated diagonal-SSM
+ *  block of "Baseline Shape Decides the Verdict ...", abstract (ii)): W_in gains d_inner
+ *  rows for a gate branch zg placed last ([x | zg], or [x | B | C | dt | zg] for SSD); the
+ *  SSM input channels (x; for SSD x, B and C) first go through ssm_conv1d_silu_fwd of
+ *  width d_conv with weights conv_w [channels, d_conv] and bias conv_b (nullable), and
+ *  the scan output is multiplied by SiLU(zg) before out_proj (the scan's gate).
  * u and out have row stride d_model; out may equal u (in place) only when
  * add_residual != 0.  workspace: ssm_mixer_workspace_bytes() bytes of device memory.
  * Requirements: those of the BitLinear and scan calls above; Mamba-1 kind needs
@@ -246,6 +257,8 @@ typedef struct {
   int64_t d_model, d_inner, d_state, dt_rank, nheads, headdim, group_size;
   int32_t act_dtype; /* ssm_dtype */
   float norm_eps;
+  int32_t gated;     /* 0: the mixer alone; 1: the gated block (convolution + SiLU gate) */
+  int32_t d_conv;    /* width of the block's convolution, 1 .. 8 when gated, else 0 */
 } ssm_mixer_config;
 
 typedef struct {
@@ -253,6 +266,7 @@ typedef struct {
   const float *s_in, *s_x, *s_dt, *s_out;   /* scales as ssm_ternary_quantize_weights writes */
   const float *g_in, *g_x, *g_dt, *g_out;   /* RMSNorm gains or NULL */
   const float *dt_bias, *A, *D;
+  const float *conv_w, *conv_b;             /* gated block: [channels, d_conv], [channels] or NULL */
 } ssm_mixer_weights;
 
 size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64_t seqlen);
@@ -269,13 +283,39 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
  *  state:   device fp32, [batch, d_inner, d_state] (Mamba-1 kind) or
  *           [batch, nheads, headdim, d_state] (SSD kind); read as the state before the token
  *           and overwritten with the state after it (zeros before the first token).
+ *  conv_state: gated block with d_conv > 1 only (else ignored, may be NULL): device fp32
+ *           [batch, d_conv - 1, channels], the previous d_conv - 1 inputs of the convolution,
+ *           oldest first; read and overwritten like state (zeros before the first token).
  *  workspace: ssm_mixer_workspace_bytes(c, batch, 1) bytes of device memory.
  * Decoding a sequence token by token reproduces the outputs of ssm_mixer_fwd over the whole
- * sequence.  Errors: as ssm_mixer_fwd; SSM_ERR_NULL when state is NULL and batch > 0.
+ * sequence.  Errors: as ssm_mixer_fwd; SSM_ERR_NULL when state (or a needed conv_state) is
+ * NULL and batch > 0.
  */
 ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
-                          int64_t batch, float* state, int32_t add_residual, void* workspace,
-                          size_t ws_bytes, hipStream_t stream);
+                          int64_t batch, float* state, float* conv_state, int32_t add_residual,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ssm_conv1d_silu_fwd -- the gated block's short causal depthwise convolution with SiLU
+ * (Mamba, cited under "Builds on" of "Baseline Shape Decides the Verdict ..."):
+ *   a[b, t, c] = bias[c] + sum_{j < width} w[c, j] * x[b, t - width + 1 + j, c]
+ *   out[b, t, c] = a / (1 + exp(-a))
+ * computed in fp64 and rounded once to dtype (the value feeds an int8 quantisation).
+ *  x:   [batch, seqlen, ldx] of dtype (SSM_F32 / SSM_BF16), channels 0 .. channels-1 used;
+ *  w:   fp32 [channels, width], width in [1, 8];  bias: fp32 [channels] or NULL;
+ *  state_in:  fp32 [batch, width - 1, channels] or NULL: the inputs before t = 0 (oldest
+ *             first; zeros when NULL);
+ *  state_out: fp32 [batch, width - 1, channels] or NULL: receives the last width - 1
+ *             inputs (the state after the sequence); may equal state_in;
+ *  out: [batch, seqlen, ldo] of dtype; must not alias x.
+ * All device pointers; caller-owned; asynchronous on stream.
+ * Errors: SSM_ERR_DTYPE, SSM_ERR_SHAPE (sizes, strides, width, out == x), SSM_ERR_NULL,
+ * SSM_ERR_DEVICE.
+ */
+ssm_status ssm_conv1d_silu_fwd(const void* x, int32_t dtype, int64_t batch, int64_t seqlen, int64_t channels,
+                               int64_t ldx, const float* w, int32_t width, const float* bias,
+                               const float* state_in, float* state_out, void* out, int64_t ldo,
+                               hipStream_t stream);
 
 /*
  * ssm_mixer_fuses_front -- 1 when ssm_mixer_fwd evaluates this configuration's x = BL(u; W_in),

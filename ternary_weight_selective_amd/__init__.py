@@ -39,18 +39,19 @@ class ScanArgs(ctypes.Structure):
                 ("ld_delta", _i64), ("delta_bias", _vp), ("delta_softplus", _i32), ("pad0", _i32), ("A", _vp),
                 ("Bm", _vp), ("ld_B", _i64), ("Cm", _vp), ("ld_C", _i64), ("D", _vp), ("h0", _vp),
                 ("h_last", _vp), ("y", _vp), ("ld_y", _i64), ("dt_in", _vp), ("ld_dt_in", _i64), ("dt_rank", _i64),
-                ("w_dt", _vp), ("s_dt", _vp), ("g_dt", _vp), ("dt_eps", ctypes.c_float), ("pad1", _i32)]
+                ("w_dt", _vp), ("s_dt", _vp), ("g_dt", _vp), ("dt_eps", ctypes.c_float), ("pad1", _i32),
+                ("gate", _vp), ("ld_gate", _i64)]
 
 
 class MixerConfig(ctypes.Structure):
     _fields_ = [("kind", _i32), ("act_bits", _i32), ("d_model", _i64), ("d_inner", _i64), ("d_state", _i64),
                 ("dt_rank", _i64), ("nheads", _i64), ("headdim", _i64), ("group_size", _i64), ("act_dtype", _i32),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("gated", _i32), ("d_conv", _i32)]
 
 
 class MixerWeights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("w_in", "w_x", "w_dt", "w_out", "s_in", "s_x", "s_dt", "s_out", "g_in", "g_x",
-                                   "g_dt", "g_out", "dt_bias", "A", "D")]
+                                   "g_dt", "g_out", "dt_bias", "A", "D", "conv_w", "conv_b")]
 
 
 class SsmError(RuntimeError):
@@ -63,7 +64,8 @@ _lib = None
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed_row_bytes",
            "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
-           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front", "ssm_mixer_step"]
+           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front", "ssm_mixer_step",
+           "ssm_conv1d_silu_fwd"]
 
 
 def lib():
@@ -97,7 +99,9 @@ def lib():
         L.ssm_mixer_fuses_front.argtypes = [ctypes.POINTER(MixerConfig)]
         L.ssm_mixer_fuses_front.restype = ctypes.c_int32
         L.ssm_mixer_step.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64,
-                                     _vp, ctypes.c_int32, _vp, _sz, _vp]
+                                     _vp, _vp, ctypes.c_int32, _vp, _sz, _vp]
+        L.ssm_conv1d_silu_fwd.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp]
+        L.ssm_conv1d_silu_fwd.restype = ctypes.c_int
         L.ssm_mixer_step.restype = ctypes.c_int
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
@@ -213,12 +217,14 @@ def ssm_bitlinear_fwd(x: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Te
 def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch.Tensor, Bm: torch.Tensor,
                            Cm: torch.Tensor, D: torch.Tensor | None = None, delta_bias: torch.Tensor | None = None,
                            softplus: bool = True, h0: torch.Tensor | None = None, return_last_state: bool = False,
-                           out: torch.Tensor | None = None, dt_proj: dict | None = None, stream=None):
+                           out: torch.Tensor | None = None, dt_proj: dict | None = None,
+                           gate: torch.Tensor | None = None, stream=None):
     """Selective scan.  x [B, L, H*P], delta [B, L, H], Bm/Cm [B, L, N]; A [H, N] (Mamba-1 kind,
     P = 1) or [H] (SSD kind).  Views with a contiguous last dim and even row strides are fine.
     dt_proj (Mamba-1 kind): dict(dt_in [B, L, >= R] view, w_dt packed [H, row bytes], s_dt [1],
     dt_rank R, optional g_dt, eps): dt is the A8 BitLinear of dt_in computed inside the scan
-    (delta is then ignored and may be None)."""
+    (delta is then ignored and may be None).  gate [B, L, H*P] (optional): y is multiplied by
+    SiLU(gate) before it is stored."""
     batch, seqlen, HP = x.shape
     H = A.shape[0] if A.dim() == 2 else (delta.shape[2] if delta is not None else A.shape[0])
     N = Bm.shape[2]
@@ -242,6 +248,8 @@ def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch
     a.Cm, a.ld_C = _p(Cm), _rows(Cm, "Cm")[1]
     a.D, a.h0, a.h_last = _p(D), _p(h0), _p(hl)
     a.y, a.ld_y = _p(out), _rows(out, "out")[1]
+    if gate is not None:
+        a.gate, a.ld_gate = _p(gate), _rows(gate, "gate")[1]
     L = lib()
     nb = L.ssm_selective_scan_workspace_bytes(ctypes.byref(a))
     ws = _workspace(nb, x.device)
@@ -251,8 +259,9 @@ def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch
 
 def mixer_config(kind: int, d_model: int, d_inner: int, d_state: int, *, dt_rank: int = 0, nheads: int = 0,
                  headdim: int = 0, act_bits: int = 8, group_size: int = 0, act_dtype: torch.dtype = torch.float32,
-                 norm_eps: float = 1e-5) -> MixerConfig:
+                 norm_eps: float = 1e-5, gated: int = 0, d_conv: int = 0) -> MixerConfig:
     c = MixerConfig()
+    c.gated, c.d_conv = gated, d_conv
     c.kind, c.act_bits = kind, act_bits
     c.d_model, c.d_inner, c.d_state, c.dt_rank = d_model, d_inner, d_state, dt_rank
     c.nheads, c.headdim, c.group_size = nheads, headdim, group_size
@@ -294,13 +303,17 @@ def ssm_mixer_fwd(cfg: MixerConfig, weights, u: torch.Tensor, add_residual: bool
 
 
 def ssm_mixer_step(cfg: MixerConfig, weights, u: torch.Tensor, state: torch.Tensor, add_residual: bool = True,
-                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
-    """One decoding step on u [B, d_model] (one token per sequence); state (fp32, contiguous) is
-    read and overwritten in place."""
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   conv_state: torch.Tensor | None = None, stream=None):
+    """One decoding step on u [B, d_model] (one token per sequence); state (and, for the gated
+    block, conv_state [B, d_conv - 1, channels]) (fp32, contiguous) are read and overwritten
+    in place."""
     if not u.is_contiguous() or not state.is_contiguous():
         raise ValueError("u and state must be contiguous")
-    if state.dtype != torch.float32:
-        raise ValueError("state must be float32")
+    if state.dtype != torch.float32 or (conv_state is not None and conv_state.dtype != torch.float32):
+        raise ValueError("state and conv_state must be float32")
+    if conv_state is not None and not conv_state.is_contiguous():
+        raise ValueError("conv_state must be contiguous")
     batch = u.shape[0]
     mw = weights if isinstance(weights, MixerWeights) else mixer_weights(weights)
     if out is None:
@@ -308,6 +321,22 @@ def ssm_mixer_step(cfg: MixerConfig, weights, u: torch.Tensor, state: torch.Tens
     L = lib()
     nb = L.ssm_mixer_workspace_bytes(ctypes.byref(cfg), batch, 1)
     ws = _workspace(nb, u.device, workspace)
-    _check(L.ssm_mixer_step(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, _p(state),
+    _check(L.ssm_mixer_step(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, _p(state), _p(conv_state),
                             int(add_residual), _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def ssm_conv1d_silu_fwd(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
+                        state_in: torch.Tensor | None = None, state_out: torch.Tensor | None = None,
+                        channels: int | None = None, out: torch.Tensor | None = None, stream=None):
+    """Causal depthwise convolution of width w.shape[1] + SiLU on the first `channels` columns
+    of x [B, L, ldx] (a view with a contiguous last dim).  state_in / state_out: fp32
+    [B, width - 1, channels] (optional; may be the same tensor)."""
+    batch, seqlen, _ = x.shape
+    C = w.shape[0] if channels is None else channels
+    if out is None:
+        out = torch.empty((batch, seqlen, C), dtype=x.dtype, device=x.device)
+    _check(lib().ssm_conv1d_silu_fwd(_p(x), _DTYPES[x.dtype], batch, seqlen, C, _rows(x, "x")[1], _p(w),
+                                     int(w.shape[1]), _p(bias), _p(state_in), _p(state_out), _p(out),
+                                     _rows(out, "out")[1], _stream(stream)))
     return out

@@ -173,6 +173,7 @@ ssm_status scan_check(const ssm_scan_args* a) {
   }
   if (a->batch * a->seqlen > 0 && (!a->x || (!proj && !a->delta) || !a->A || !a->Bm || !a->Cm || !a->y))
     return fail(SSM_ERR_NULL, "scan: x, delta (or dt_in), A, Bm, Cm and y are required");
+  if (a->gate && a->ld_gate < HP) return fail(SSM_ERR_SHAPE, "scan: ld_gate < nheads * headdim");
   return SSM_OK;
 }
 
@@ -192,6 +193,7 @@ ScanArgs to_scan(const ssm_scan_args* a) {
   s.Cm = a->Cm; s.ld_C = a->ld_C;
   s.D = a->D; s.h0 = a->h0; s.h_last = a->h_last;
   s.y = a->y; s.ld_y = a->ld_y;
+  s.gate = a->gate; s.ld_gate = a->ld_gate;
   if (a->dt_in) {
     s.dr = a->dt_in; s.ld_dr = a->ld_dt_in; s.R = (int)a->dt_rank;
     s.w_dt = (const uint32_t*)a->w_dt; s.w_dt_row_words = cdiv(a->dt_rank, 16);
@@ -204,7 +206,10 @@ ScanArgs to_scan(const ssm_scan_args* a) {
 
 struct MixPlan {
   int64_t M = 0, Kp = 0, PW = 0, VW = 0;
-  size_t off_am = 0, off_x = 0, off_p = 0, off_y = 0, off_scan = 0, total = 0;
+  int64_t XW = 0;   // Mamba-1: in_proj width (d_inner, or 2 d_inner with the gate branch)
+  int64_t VW0 = 0;  // SSD: [x | B | C | dt] width; VW adds the gate branch
+  int64_t Cc = 0;   // channels through the convolution of the gated block
+  size_t off_am = 0, off_x = 0, off_xc = 0, off_p = 0, off_y = 0, off_scan = 0, total = 0;
 };
 
 ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, MixPlan* p) {
@@ -216,6 +221,9 @@ ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, Mi
   if (c->act_bits != 8 && c->act_bits != 16) return fail(SSM_ERR_UNSUPPORTED, "mixer: act_bits must be 8 or 16");
   if (c->group_size < 0 || (c->group_size > 0 && (c->group_size % 64 || c->d_model % c->group_size || c->d_inner % c->group_size)))
     return fail(SSM_ERR_SHAPE, "mixer: group_size must be 0 or a multiple of 64 dividing d_model and d_inner");
+  if (c->gated != 0 && c->gated != 1) return fail(SSM_ERR_SHAPE, "mixer: gated must be 0 or 1");
+  if (c->gated ? (c->d_conv < 1 || c->d_conv > kConvMaxK) : c->d_conv != 0)
+    return fail(SSM_ERR_SHAPE, "mixer: d_conv %d (1 .. %d with gated = 1, else 0)", (int)c->d_conv, kConvMaxK);
   p->M = batch * seqlen;
   p->Kp = round_up(c->d_model > c->d_inner ? c->d_model : c->d_inner, 64);
   const size_t as = act_size(c->act_dtype);
@@ -230,7 +238,10 @@ ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, Mi
     const int64_t n = c->d_state;
     if (n != 4 && n != 8 && n != 16 && n != 32 && n != 64) return fail(SSM_ERR_UNSUPPORTED, "mixer: d_state %lld", (long long)n);
     p->PW = c->dt_rank + 2 * c->d_state;
-    p->off_x = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
+    p->XW = c->gated ? 2 * c->d_inner : c->d_inner;
+    p->Cc = c->d_inner;
+    p->off_x = off; off = align_up(off + (size_t)p->M * p->XW * as);
+    if (c->gated) { p->off_xc = off; off = align_up(off + (size_t)p->M * c->d_inner * as); }
     p->off_p = off; off = align_up(off + (size_t)p->M * p->PW * as);
     p->off_y = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
     p->off_scan = off;
@@ -239,8 +250,11 @@ ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, Mi
       return fail(SSM_ERR_SHAPE, "mixer: nheads * headdim must equal d_inner");
     const int64_t n = c->d_state;
     if (n != 16 && n != 32 && n != 64 && n != 128) return fail(SSM_ERR_UNSUPPORTED, "mixer: d_state %lld", (long long)n);
-    p->VW = c->d_inner + 2 * c->d_state + c->nheads;
+    p->VW0 = c->d_inner + 2 * c->d_state + c->nheads;
+    p->VW = c->gated ? p->VW0 + c->d_inner : p->VW0;
+    p->Cc = c->d_inner + 2 * c->d_state;
     p->off_p = off; off = align_up(off + (size_t)p->M * p->VW * as);
+    if (c->gated) { p->off_xc = off; off = align_up(off + (size_t)p->M * p->Cc * as); }
     p->off_y = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
     p->off_scan = off;
   } else {
@@ -360,7 +374,7 @@ int32_t ssm_mixer_fuses_front(const ssm_mixer_config* c) {
   MixPlan p;
   const ssm_status st = mix_plan(c, 1, 1, &p);
   g_err = keep;
-  if (st != SSM_OK || c->kind != SSM_MIXER_MAMBA1) return 0;
+  if (st != SSM_OK || c->kind != SSM_MIXER_MAMBA1 || c->gated) return 0;
   return front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank) ? 1 : 0;
 }
 
@@ -369,22 +383,43 @@ namespace {
 // (used for one token per sequence only, where no time chunks are formed).
 ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
                      int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb, hipStream_t stream,
-                     float* state);
+                     float* state, float* conv_state);
 }  // namespace
 
 ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
                          int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb,
                          hipStream_t stream) {
   g_err.clear();
-  return mixer_run(c, w, u, out, batch, seqlen, add_residual, ws, wsb, stream, nullptr);
+  return mixer_run(c, w, u, out, batch, seqlen, add_residual, ws, wsb, stream, nullptr, nullptr);
 }
 
 ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
-                          int64_t batch, float* state, int32_t add_residual, void* ws, size_t wsb,
+                          int64_t batch, float* state, float* conv_state, int32_t add_residual, void* ws, size_t wsb,
                           hipStream_t stream) {
   g_err.clear();
   if (batch > 0 && !state) return fail(SSM_ERR_NULL, "mixer step: state is NULL");
-  return mixer_run(c, w, u, out, batch, 1, add_residual, ws, wsb, stream, state);
+  if (batch > 0 && c && c->gated && c->d_conv > 1 && !conv_state)
+    return fail(SSM_ERR_NULL, "mixer step: conv_state is NULL (gated block)");
+  return mixer_run(c, w, u, out, batch, 1, add_residual, ws, wsb, stream, state, conv_state);
+}
+
+ssm_status ssm_conv1d_silu_fwd(const void* x, int32_t dtype, int64_t batch, int64_t seqlen, int64_t channels,
+                               int64_t ldx, const float* w, int32_t width, const float* bias, const float* state_in,
+                               float* state_out, void* out, int64_t ldo, hipStream_t stream) {
+  g_err.clear();
+  if (!act_dtype_ok(dtype)) return fail(SSM_ERR_DTYPE, "conv: dtype %d", dtype);
+  if (batch < 0 || seqlen < 0 || channels < 1) return fail(SSM_ERR_SHAPE, "conv: batch, seqlen >= 0 and channels >= 1");
+  if (width < 1 || width > kConvMaxK) return fail(SSM_ERR_SHAPE, "conv: width %d not in [1, %d]", (int)width, kConvMaxK);
+  if (ldx < channels || ldo < channels) return fail(SSM_ERR_SHAPE, "conv: ldx / ldo < channels");
+  if (batch * seqlen > 0 && (!x || !w || !out)) return fail(SSM_ERR_NULL, "conv: x, w and out are required");
+  if (batch * seqlen > 0 && out == x) return fail(SSM_ERR_SHAPE, "conv: out may not alias x");
+  ConvArgs a{};
+  a.batch = batch; a.L = seqlen; a.C = channels; a.K = width; a.act_bf16 = dtype == SSM_BF16;
+  a.x = x; a.ldx = ldx; a.w = w; a.bias = bias;
+  a.state_in = width > 1 ? state_in : nullptr;
+  a.state_out = width > 1 ? state_out : nullptr;
+  a.out = out; a.ldo = ldo;
+  return dev(launch_conv_silu(a, stream), "conv");
 }
 
 }  // extern "C"
@@ -392,7 +427,7 @@ ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w,
 namespace {
 ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
                      int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb, hipStream_t stream,
-                     float* state) {
+                     float* state, float* conv_state) {
   MixPlan p;
   ssm_status st = mix_plan(c, batch, seqlen, &p);
   if (st != SSM_OK) return st;
@@ -400,6 +435,7 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     return fail(SSM_ERR_NULL, "mixer: w_in, w_out, s_in, s_out and A are required");
   if (c->kind == SSM_MIXER_MAMBA1 && (!w->w_x || !w->w_dt || !w->s_x || !w->s_dt))
     return fail(SSM_ERR_NULL, "mixer: w_x, w_dt, s_x and s_dt are required for the Mamba-1 kind");
+  if (c->gated && !w->conv_w) return fail(SSM_ERR_NULL, "mixer: conv_w is required for the gated block");
   if (p.M > 0 && (!u || !out)) return fail(SSM_ERR_NULL, "mixer: u / out is NULL");
   if (out == u && !add_residual) return fail(SSM_ERR_SHAPE, "mixer: out may alias u only with add_residual");
   const size_t need = ssm_mixer_workspace_bytes(c, batch, seqlen);
@@ -408,6 +444,7 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
   if (p.M == 0) return SSM_OK;
   char* base = (char*)ws;
   float* am = (float*)(base + p.off_am);
+  const size_t as = act_size(c->act_dtype);
 
   auto bitlinear = [&](const void* x, int64_t k, int64_t ldx, const uint8_t* wp, const float* sc, const float* g,
                        int64_t n, void* y, int64_t ldy, const void* res) -> ssm_status {
@@ -426,14 +463,24 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     }
     return bl_run(&a, bp, base, stream);
   };
+  // gated block: causal convolution + SiLU of the SSM input channels (Cc of them, row stride ld)
+  auto conv = [&](const void* x, int64_t ld, void* xc) -> ssm_status {
+    ConvArgs ca{};
+    ca.batch = batch; ca.L = seqlen; ca.C = p.Cc; ca.K = (int)c->d_conv; ca.act_bf16 = c->act_dtype == SSM_BF16;
+    ca.x = x; ca.ldx = ld; ca.w = w->conv_w; ca.bias = w->conv_b;
+    ca.state_in = c->d_conv > 1 ? conv_state : nullptr;
+    ca.state_out = c->d_conv > 1 ? conv_state : nullptr;
+    ca.out = xc; ca.ldo = p.Cc;
+    return dev(launch_conv_silu(ca, stream), "mixer conv");
+  };
 
   const void* res = add_residual ? u : nullptr;
   if (c->kind == SSM_MIXER_MAMBA1) {
-    void* x = base + p.off_x;
+    void* xz = base + p.off_x;                         // in_proj output [x | zg]
+    void* x = c->gated ? base + p.off_xc : xz;         // the SSM input
     void* pp = base + p.off_p;
     void* y = base + p.off_y;
-    const bool front = front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank);
-    const size_t as = act_size(c->act_dtype);
+    const bool front = !c->gated && front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank);
     ssm_scan_args sa{};
     sa.batch = batch; sa.seqlen = seqlen; sa.nheads = c->d_inner; sa.headdim = 1; sa.d_state = c->d_state;
     sa.a_per_state = 1; sa.act_dtype = c->act_dtype;
@@ -447,17 +494,12 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     sa.y = y; sa.ld_y = c->d_inner;
     sa.dt_in = pp; sa.ld_dt_in = p.PW; sa.dt_rank = c->dt_rank;
     sa.w_dt = w->w_dt; sa.s_dt = w->s_dt; sa.g_dt = w->g_dt; sa.dt_eps = c->norm_eps;
+    if (c->gated) { sa.gate = (const char*)xz + c->d_inner * as; sa.ld_gate = p.XW; }
     st = scan_check(&sa);
     if (st != SSM_OK) return st;
     ScanArgs sc = to_scan(&sa);
     if (p.off_scan + scan_m1_workspace(sc) > wsb)  // the scan's codes region lies inside the workspace
       return fail(SSM_ERR_WORKSPACE, "mixer: scan workspace exceeds %zu bytes", wsb);
-    if (!front) {
-      st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, c->d_inner, x, c->d_inner, nullptr);
-      if (st != SSM_OK) return st;
-      st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
-      if (st != SSM_OK) return st;
-    }
     if (front) {  // in_proj, x_proj and the dt input's codes in one kernel, codes into the scan's workspace
       FrontArgs fa{};
       fa.M = p.M; fa.u = u; fa.act_bf16 = c->act_dtype == SSM_BF16;
@@ -472,28 +514,45 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
       st = dev(launch_m1_front(fa, stream), "mixer front");
       if (st != SSM_OK) return st;
       sc.dt_codes_ready = 1;
+    } else {
+      st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, p.XW, xz, p.XW, nullptr);
+      if (st != SSM_OK) return st;
+      if (c->gated) {
+        st = conv(xz, p.XW, x);
+        if (st != SSM_OK) return st;
+      }
+      st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
+      if (st != SSM_OK) return st;
     }
     st = dev(launch_scan_m1(sc, base + p.off_scan, stream), "mixer scan");
     if (st != SSM_OK) return st;
     return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
   }
-  // SSD kind
+  // SSD kind: v = [x | B | C | dt (| zg)]; the gated block reads x, B and C from their convolution
   void* v = base + p.off_p;
   void* y = base + p.off_y;
   st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, p.VW, v, p.VW, nullptr);
   if (st != SSM_OK) return st;
-  const size_t as = act_size(c->act_dtype);
+  const void* xbc = v;
+  int64_t ld_xbc = p.VW;
+  if (c->gated) {
+    st = conv(v, p.VW, base + p.off_xc);
+    if (st != SSM_OK) return st;
+    xbc = base + p.off_xc;
+    ld_xbc = p.Cc;
+  }
   ScanArgs s{};
   s.batch = batch; s.L = seqlen; s.H = c->nheads; s.P = c->headdim; s.N = c->d_state;
   s.act_bf16 = c->act_dtype == SSM_BF16;
-  s.x = v; s.ld_x = p.VW;
-  s.Bm = (const char*)v + c->d_inner * as; s.ld_B = p.VW;
-  s.Cm = (const char*)v + (c->d_inner + c->d_state) * as; s.ld_C = p.VW;
+  s.x = xbc; s.ld_x = ld_xbc;
+  s.Bm = (const char*)xbc + c->d_inner * as; s.ld_B = ld_xbc;
+  s.Cm = (const char*)xbc + (c->d_inner + c->d_state) * as; s.ld_C = ld_xbc;
   s.delta = (const char*)v + (c->d_inner + 2 * c->d_state) * as; s.ld_delta = p.VW;
   s.delta_bias = w->dt_bias; s.softplus = 1;
   s.A = w->A; s.D = w->D;
   s.h0 = state; s.h_last = state;
   s.y = y; s.ld_y = c->d_inner;
+  if (c->gated) { s.gate = (const char*)v + p.VW0 * as; s.ld_gate = p.VW; }
   st = dev(launch_scan_ssd(s, base + p.off_scan, wsb - p.off_scan, stream), "mixer scan");
   if (st != SSM_OK) return st;
   return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);

@@ -31,6 +31,12 @@ template <typename T> __device__ __forceinline__ void st_act(T* p, float v);
 template <> __device__ __forceinline__ void st_act<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st_act<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// SiLU of the gate branch, fp32: z / (1 + 2^(-z log2 e)) with the hardware exp2 (an infinite
+// exponential for very negative z gives -0).
+__device__ __forceinline__ float silu_gate(float z) {
+  return z / (1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
 // Cross-lane moves.  ds_swizzle in bit-mask mode: lane j of each 32-lane half reads lane
 // j ^ 16.  DPP (data-parallel primitives): a rotation of each row of 16 lanes, and quad
 // permutations.

@@ -79,12 +79,28 @@ struct ScanArgs {
   const uint32_t* w_dt; int64_t w_dt_row_words;
   const float* s_dt; const float* g_dt; float eps;
   int dt_codes_ready;  // the dt input's int8 codes and factors are already in the workspace
+  const void* gate; int64_t ld_gate;  // nullable: y is multiplied by SiLU(gate) before it is stored
 };
 hipError_t launch_scan_m1(const ScanArgs& a, void* ws, hipStream_t s);
 size_t scan_m1_workspace(const ScanArgs& a);
 // Where the scan keeps the dt input's codes ([M, *cw] int8 at offset 0) and their fp64
 // dequantisation factors ([M] at *off_deq) in its workspace.
 void scan_m1_code_layout(const ScanArgs& a, int* cw, size_t* off_deq);
+
+// ---- causal depthwise convolution + SiLU (conv.hip)
+struct ConvArgs {
+  int64_t batch, L, C;
+  int K;                        // width, 1 .. kConvMaxK
+  int act_bf16;
+  const void* x; int64_t ldx;   // [B, L, ldx], channels 0 .. C-1
+  const float* w;               // [C, K]
+  const float* bias;            // [C] or null
+  const float* state_in;        // [B, K-1, C] fp32 or null (zeros before t = 0)
+  float* state_out;             // [B, K-1, C] fp32 or null; may equal state_in
+  void* out; int64_t ldo;       // [B, L, ldo]
+};
+constexpr int kConvMaxK = 8;
+hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t s);
 
 // ---- Mamba-1 mixer front (front.hip): x = BitLinear(u; W_in), p = BitLinear(x; W_x) and the
 // dt input's int8 codes in one kernel (A8, one scale per tensor)

@@ -109,9 +109,12 @@ struct DtCodes {
 //   5. runs the recurrence over tile i, writing its partials.
 // A buffer of tile i is rewritten at tile i + 2, after the barrier of tile i + 1 that every
 // wave reaches only once it has finished with tile i.
-// LOCAL: pass 1 (zero start, no readout; writes the chunk's end state and sum(dt)).
-template <int NS, typename T, int RW, bool LOCAL>
+// MODE 1 (LOCAL): pass 1 (zero start, no readout; writes the chunk's end state and sum(dt)).
+// MODE 2 (GATE): the readout is multiplied by SiLU of the gate input before it is stored.
+template <int NS, typename T, int RW, int MODE>
 __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, DtCodes dc) {
+  constexpr bool LOCAL = MODE == 1;
+  constexpr bool GATE = MODE == 2;
   constexpr bool FUSED = RW > 0;  // dt from the low-rank input: RW 16-byte code words per token
   constexpr int SPL = NS / 4;     // states per lane
   constexpr int CPB = 64;         // channels per block
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
 
   // prefetch registers for the next tile: x (and delta) of the thread's items, B, C, the
   // items' dt codes (a whole wave reads the same token row) and dequantisation factors
-  float rx[XPT], rd[FUSED ? 1 : XPT], rb[BPT], rc[BPT];
+  float rx[XPT], rd[FUSED ? 1 : XPT], rb[BPT], rc[BPT], rz[GATE ? XPT : 1];
   v4i rq[FUSED ? XPT : 1][RWQ];
   double rf[FUSED ? XPT : 1];
   auto load_tile = [&](int64_t t0) {
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
       const bool ok = okt && dv;
       const int64_t tok = b * L + t0 + t;
       rx[i] = ok ? ld_act(X + tok * a.ld_x + d) : 0.0f;
+      if (GATE) rz[GATE ? i : 0] = ok ? ld_act((const T*)a.gate + tok * a.ld_gate + d) : 0.0f;
       if (!FUSED) rd[FUSED ? 0 : i] = ok ? ld_act(DL + tok * a.ld_delta + d) : 0.0f;
       if (FUSED) {
 #pragma unroll
@@ -200,6 +204,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   };
 
   float xprev[XPT];  // x of the previous tile's items, for D x
+  float zprev[GATE ? XPT : 1];  // and their gate inputs
   int64_t tprev = -1;  // first step of the tile whose readout is pending
   auto store_y = [&](int buf, int64_t t0p) {
     T* Y = (T*)a.y;
@@ -209,7 +214,9 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
       if ((t0p + t < te) && dv) {
         const float y = ((s_yp[LOCAL ? 0 : buf][0][t][lane] + s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 1][t][lane]) +
                          s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 2][t][lane]) + s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 3][t][lane];
-        st_act(Y + (b * L + t0p + t) * a.ld_y + d, y + D_s * xprev[i]);
+        float yo = y + D_s * xprev[i];
+        if (GATE) yo = yo * silu_gate(zprev[GATE ? i : 0]);
+        st_act(Y + (b * L + t0p + t) * a.ld_y + d, yo);
       }
     }
   };
@@ -218,12 +225,13 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   int buf = 0;
   for (int64_t t0 = tb; t0 < te; t0 += TT, buf ^= 1) {
     // 1. stage this tile: B, C; per item dt, softplus, dt * x
-    float xcur[XPT];
+    float xcur[XPT], zcur[GATE ? XPT : 1];
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int t = w + 4 * i;
       const float xv = rx[i];
       xcur[i] = xv;
+      if (GATE) zcur[GATE ? i : 0] = rz[GATE ? i : 0];
       float dtv;
       if (FUSED) {
         int acc = 0;
@@ -254,7 +262,10 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
     // 4. readout of the previous tile
     if (!LOCAL && tprev >= 0) store_y(buf ^ 1, tprev);
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) xprev[i] = xcur[i];
+    for (int i = 0; i < XPT; ++i) {
+      xprev[i] = xcur[i];
+      if (GATE) zprev[GATE ? i : 0] = zcur[GATE ? i : 0];
+    }
     tprev = t0;
     // 5. recurrence.  B and C of a step are the same for the whole wave (broadcast LDS reads);
     //    groups of GQ steps, software-pipelined: the LDS reads of group g + 1 are issued before
@@ -416,8 +427,9 @@ hipError_t launch_m1_t(const ScanArgs& a, void* ws, hipStream_t s) {
   const int rw = fused ? p.cw / 16 : 0;
   auto run = [&](auto rwc, bool local, unsigned gz) {
     constexpr int RWc = decltype(rwc)::value;
-    if (local) hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, true>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
-    else hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, false>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+    if (local) hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, 1>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+    else if (a.gate) hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, 2>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+    else hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, 0>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
   };
   auto run_rw = [&](bool local, unsigned gz) {
     switch (rw) {

@@ -92,7 +92,11 @@ __global__ __launch_bounds__(256) void k_scan_ssd_rec(ScanArgs a) {
     for (int e = tid; e < TT * PPB; e += 256) {
       const int t = e / PPB, pp = e % PPB;
       const int64_t pg = (int64_t)blockIdx.x * PPB + pp;
-      if ((t0 + t < L) && pg < P) st_act(Y + (b * L + t0 + t) * a.ld_y + hd * P + pg, s_y[t][pp]);
+      if ((t0 + t < L) && pg < P) {
+        float yv = s_y[t][pp];
+        if (a.gate) yv = yv * silu_gate(ld_act((const T*)a.gate + (b * L + t0 + t) * a.ld_gate + hd * P + pg));
+        st_act(Y + (b * L + t0 + t) * a.ld_y + hd * P + pg, yv);
+      }
     }
   }
   if (a.h_last && pv) {
@@ -321,10 +325,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (c0 + t >= L) continue;
       const float et = s_et[t];
       bf16_t* yr = Y + (b * L + c0 + t) * a.ld_y + hd * P;
+      const bf16_t* gr = a.gate ? (const bf16_t*)a.gate + (b * L + c0 + t) * a.ld_gate + hd * P : nullptr;
 #pragma unroll
       for (int jp = 0; jp < 4; ++jp) {
         const int pp = 16 * jp + l16;
-        const float yv = yacc[jp][r] + et * zacc[jp][r] + D_h * bf_val(sX[t * XS + pp]);
+        float yv = yacc[jp][r] + et * zacc[jp][r] + D_h * bf_val(sX[t * XS + pp]);
+        if (gr) yv = yv * silu_gate(bf_val(gr[pp]));
         yr[pp] = f32_to_bf16(yv);
       }
     }
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 static bool ssd_chunk_ok(const ScanArgs& a) {
   auto al = [](const void* p) { return ((uintptr_t)p % 16) == 0; };
   return a.act_bf16 && a.P == kSsdP && (a.N == 64 || a.N == 128) && a.ld_x % 8 == 0 && a.ld_B % 8 == 0 &&
-         a.ld_C % 8 == 0 && al(a.x) && al(a.Bm) && al(a.Cm);
+         a.ld_C % 8 == 0 && al(a.x) && al(a.Bm) && al(a.Cm);  // (the gate is read element-wise)
 }
 
 template <int NS, typename T>

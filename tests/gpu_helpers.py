@@ -52,22 +52,25 @@ def quantize_layer(cfg, lat, check: bool = True):
             assert int(host(zc)[0]) == ozeros, name
         gw["w_" + name], gw["s_" + name] = packed, scale
         ow["c_" + name], ow["s_" + name] = codes, oscale
-    for key in ("A", "D", "dt_bias"):
-        gw[key] = to_dev(lat[key])
-        ow[key] = lat[key]
+    for key in ("A", "D", "dt_bias", "conv_w", "conv_b"):
+        if key in lat:
+            gw[key] = to_dev(lat[key])
+            ow[key] = lat[key]
     return gw, ow
 
 
 def gpu_config(cfg):
     return tws.mixer_config(cfg.kind, cfg.d_model, cfg.d_inner, cfg.d_state, dt_rank=cfg.dt_rank,
                             nheads=cfg.nheads, headdim=cfg.headdim, act_bits=cfg.act_bits,
-                            group_size=cfg.group_size, act_dtype=torch_dtype(cfg), norm_eps=cfg.norm_eps)
+                            group_size=cfg.group_size, act_dtype=torch_dtype(cfg), norm_eps=cfg.norm_eps,
+                            gated=cfg.gated, d_conv=cfg.d_conv)
 
 
 def oracle_config(cfg):
     return dict(kind=cfg.kind, d_model=cfg.d_model, d_inner=cfg.d_inner, d_state=cfg.d_state, dt_rank=cfg.dt_rank,
                 nheads=cfg.nheads, headdim=cfg.headdim, group_size=cfg.group_size, act_bits=cfg.act_bits,
-                act_dtype=oracle.BF16 if cfg.act_dtype == "bf16" else oracle.F32, norm_eps=cfg.norm_eps)
+                act_dtype=oracle.BF16 if cfg.act_dtype == "bf16" else oracle.F32, norm_eps=cfg.norm_eps,
+                gated=cfg.gated, d_conv=cfg.d_conv)
 
 
 def run_gpu_stack(cfg, gws, u_host, workspace=None):

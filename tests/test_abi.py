@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = tws.lib()
-    assert tws.ssm_abi_version() == 1
+    assert tws.ssm_abi_version() == 2
     for s in range(8):
         assert L.ssm_status_string(s)
     assert tws.ssm_packed_row_bytes(8) == 4
@@ -166,6 +166,10 @@ def test_mixer_rejects():
         (tws.mixer_config(1, 64, 128, 16, nheads=2, headdim=64, group_size=100), SHAPE),
         (tws.mixer_config(0, 8192, 128, 16, dt_rank=8), SHAPE),
         (tws.mixer_config(5, 64, 128, 16), UNSUPPORTED),
+        (tws.mixer_config(0, 64, 128, 16, dt_rank=8, gated=1, d_conv=0), SHAPE),
+        (tws.mixer_config(0, 64, 128, 16, dt_rank=8, gated=1, d_conv=9), SHAPE),
+        (tws.mixer_config(0, 64, 128, 16, dt_rank=8, gated=0, d_conv=4), SHAPE),
+        (tws.mixer_config(0, 64, 128, 16, dt_rank=8, gated=2, d_conv=4), SHAPE),
     ]
     for cfg, status in cases:
         assert L.ssm_mixer_fwd(ctypes.byref(cfg), ctypes.byref(w), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 1 << 30,
@@ -186,12 +190,45 @@ def test_mixer_step_rejects():
         setattr(w, name, FAKE)
     good = tws.mixer_config(0, 64, 128, 16, dt_rank=8)
     step = L.ssm_mixer_step
-    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, None, 1, FAKE, 1 << 30, None) == NULL
+    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, None, None, 1, FAKE, 1 << 30,
+                None) == NULL
     assert step(ctypes.byref(tws.mixer_config(0, 64, 128, 16, dt_rank=0)), ctypes.byref(w), FAKE, FAKE + 4096, 2,
-                FAKE + 8192, 1, FAKE, 1 << 30, None) == UNSUPPORTED
-    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, FAKE + 8192, 1, FAKE, 16,
+                FAKE + 8192, None, 1, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE + 4096, 2, FAKE + 8192, None, 1, FAKE, 16,
                 None) == WORKSPACE
-    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE, 2, FAKE + 8192, 0, FAKE, 1 << 30, None) == SHAPE
+    assert step(ctypes.byref(good), ctypes.byref(w), FAKE, FAKE, 2, FAKE + 8192, None, 0, FAKE, 1 << 30,
+                None) == SHAPE
+    gated = tws.mixer_config(0, 64, 128, 16, dt_rank=8, gated=1, d_conv=4)
+    assert step(ctypes.byref(gated), ctypes.byref(w), FAKE, FAKE + 4096, 2, FAKE + 8192, None, 1, FAKE, 1 << 30,
+                None) == NULL  # the convolution's state is required
+
+
+def test_mixer_gated_needs_conv_weights_and_room():
+    L = tws.lib()
+    w = tws.MixerWeights()
+    for name, _ in tws.MixerWeights._fields_:
+        setattr(w, name, FAKE)
+    w.conv_w = None
+    gated = tws.mixer_config(0, 64, 128, 16, dt_rank=8, gated=1, d_conv=4)
+    plain = tws.mixer_config(0, 64, 128, 16, dt_rank=8)
+    assert L.ssm_mixer_fwd(ctypes.byref(gated), ctypes.byref(w), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 1 << 30,
+                           None) == NULL
+    # the gate branch and the convolved copy need room beyond the plain mixer's workspace
+    assert L.ssm_mixer_workspace_bytes(ctypes.byref(gated), 2, 64) > L.ssm_mixer_workspace_bytes(ctypes.byref(plain), 2, 64)
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 256, 512, 16, dt_rank=16, gated=1, d_conv=4))) == 0
+
+
+def test_conv_rejects():
+    L = tws.lib()
+    c = L.ssm_conv1d_silu_fwd
+    assert c(FAKE, 5, 2, 8, 16, 16, FAKE, 4, None, None, None, FAKE + 4096, 16, None) == DTYPE
+    assert c(FAKE, 0, 2, 8, 16, 16, FAKE, 0, None, None, None, FAKE + 4096, 16, None) == SHAPE
+    assert c(FAKE, 0, 2, 8, 16, 16, FAKE, 9, None, None, None, FAKE + 4096, 16, None) == SHAPE
+    assert c(FAKE, 0, 2, 8, 16, 8, FAKE, 4, None, None, None, FAKE + 4096, 16, None) == SHAPE
+    assert c(FAKE, 0, 2, 8, 16, 16, FAKE, 4, None, None, None, FAKE + 4096, 8, None) == SHAPE
+    assert c(FAKE, 0, 2, 8, 16, 16, None, 4, None, None, None, FAKE + 4096, 16, None) == NULL
+    assert c(FAKE, 0, 2, 8, 16, 16, FAKE, 4, None, None, None, FAKE, 16, None) == SHAPE
+    assert c(FAKE, 0, -1, 8, 16, 16, FAKE, 4, None, None, None, FAKE + 4096, 16, None) == SHAPE
 
 
 def test_mixer_fuses_front_query():

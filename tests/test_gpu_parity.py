@@ -344,6 +344,9 @@ def test_mixer_ssd_small_fp32():
     ("ternaryssm50m", dict(batch=1, seqlen=5, layers=1)),   # separate in_proj / x_proj
     ("mamba2_ssd", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=7,
                         layers=1)),
+    ("trissm_gated", dict(batch=2, seqlen=19, layers=1)),
+    ("mamba2_ssd_gated", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=7,
+                              layers=1)),
 ])
 def test_mixer_stays_inside_workspace(name, over):
     """Everything the mixer writes to its workspace lies within ssm_mixer_workspace_bytes: a
@@ -368,17 +371,22 @@ def _decode(cfg, gw, u_host):
     B, L, _ = u.shape
     shape = (B, cfg.d_inner, cfg.d_state) if cfg.kind == wl.MAMBA1 else (B, cfg.nheads, cfg.headdim, cfg.d_state)
     state = torch.zeros(shape, dtype=torch.float32, device=DEV)
+    cst = (torch.zeros((B, cfg.d_conv - 1, cfg.conv_channels), dtype=torch.float32, device=DEV)
+           if cfg.gated and cfg.d_conv > 1 else None)
     ws = torch.empty(tws.ssm_mixer_workspace_bytes(c, B, 1), dtype=torch.uint8, device=DEV)
     mw = tws.mixer_weights(gw)
     out = torch.empty_like(u)
     for t in range(L):
         tok = u[:, t].contiguous()
-        out[:, t] = tws.ssm_mixer_step(c, mw, tok, state, add_residual=True, workspace=ws)
+        out[:, t] = tws.ssm_mixer_step(c, mw, tok, state, add_residual=True, workspace=ws, conv_state=cst)
     return out, state
 
 
 DECODE_CASES = [
     ("bitssm_tiny", {}, 42),
+    ("trissm_gated", dict(batch=3, seqlen=20, layers=1), 12),
+    ("mamba2_ssd_gated", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=14,
+                              layers=1), 13),
     ("trissm", dict(batch=4, seqlen=24, layers=1), 7),
     ("ternaryssm50m", dict(batch=3, seqlen=16, layers=1), 8),
     ("mamba2_ssd", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=20,
@@ -404,3 +412,120 @@ def test_mixer_decode_step(name, over, seed):
     full = host(run_gpu_stack(cfg, [gw], u))
     assert rel_err(host(out), full) <= tol
     assert bool(torch.isfinite(state).all()) and float(state.abs().max()) > 0
+
+
+# ------------------------------------------------------------------ gated block
+
+def _ulp_diff(got, ref, bf16: bool):
+    """Distance in units of the last place of the stored type (fp32 or bf16 bit patterns)."""
+    g = np.asarray(got, np.float32).view(np.int32).astype(np.int64)
+    r = np.asarray(ref, np.float32).view(np.int32).astype(np.int64)
+    if bf16:
+        g, r = g >> 16, r >> 16
+    return np.abs(g - r)
+
+
+CONV_CASES = [  # (batch, seqlen, channels, ldx, width, dtype, state)
+    (2, 37, 100, 130, 4, "f32", None),
+    (3, 70, 256, 512, 4, "bf16", None),
+    (1, 5, 64, 64, 3, "f32", "separate"),
+    (2, 1, 200, 400, 4, "f32", "inplace"),
+    (2, 2, 72, 72, 4, "bf16", "inplace"),
+    (2, 33, 48, 48, 1, "f32", None),
+    (1, 64, 4352, 8512, 4, "bf16", None),  # the Mamba-2 gated block's x, B, C channels
+]
+
+
+@pytest.mark.parametrize("batch,L,C,ldx,K,dt,state", CONV_CASES)
+def test_conv_silu_parity(batch, L, C, ldx, K, dt, state):
+    """Causal convolution + SiLU: fp64 on both sides, rounded once to the stored type, so the
+    values agree to the last bit except where the two fp64 exponentials straddle a rounding
+    boundary (at most one unit of the last place, rarely)."""
+    g = wl.rng(batch * 1000 + L * 10 + K)
+    x = wl.normal(g, (batch, L, ldx))
+    if dt == "bf16":
+        x = bf16_values(x)
+    w = g.uniform(-0.5, 0.5, (C, K)).astype(np.float32)
+    b = g.uniform(-0.5, 0.5, (C,)).astype(np.float32)
+    st = wl.normal(g, (batch, K - 1, C)) if state else None
+    if st is not None and dt == "bf16":
+        st = bf16_values(st)
+    ref, ref_st = oracle.conv_silu(x[:, :, :C], w, b, state=st, act_dtype=oracle.BF16 if dt == "bf16" else oracle.F32)
+    xd = to_dev(x, torch.bfloat16 if dt == "bf16" else torch.float32)
+    sin = to_dev(st) if st is not None else None
+    sout = (sin if state == "inplace" else torch.empty_like(sin)) if st is not None else None
+    got = tws.ssm_conv1d_silu_fwd(xd, to_dev(w), to_dev(b), state_in=sin, state_out=sout, channels=C)
+    d = _ulp_diff(host(got), ref, dt == "bf16")
+    assert d.max() <= 1 and np.mean(d > 0) <= 1e-3, (d.max(), np.mean(d > 0))
+    if st is not None:
+        np.testing.assert_array_equal(host(sout), ref_st)
+
+
+def test_conv_silu_streaming_equals_whole():
+    """Chunks of a sequence with the state carried give the whole sequence's values bit for bit."""
+    g = wl.rng(77)
+    x = wl.normal(g, (2, 50, 96))
+    w = g.uniform(-0.5, 0.5, (96, 4)).astype(np.float32)
+    xd = to_dev(x)
+    wd = to_dev(w)
+    whole = host(tws.ssm_conv1d_silu_fwd(xd, wd))
+    st = torch.zeros((2, 3, 96), device=DEV)
+    parts = []
+    for a, b in ((0, 17), (17, 18), (18, 50)):
+        parts.append(host(tws.ssm_conv1d_silu_fwd(xd[:, a:b].contiguous(), wd, state_in=st, state_out=st)))
+    np.testing.assert_array_equal(np.concatenate(parts, axis=1), whole)
+
+
+@pytest.mark.parametrize("kind,dt", [("m1", "f32"), ("m1", "bf16"), ("ssd", "f32"), ("ssd", "bf16")])
+def test_scan_gate_parity(kind, dt):
+    """The scan's gate: y * SiLU(gate), against the oracle scan's y times SiLU in fp64."""
+    if kind == "m1":
+        p = wl.scan_problem(2, 45, 70, 1, 16, True, seed=5)
+        H, P = 70, 1
+    else:
+        p = wl.scan_problem(2, 130, 4, 64, 64, False, seed=6)
+        H, P = 4, 64
+    gate = wl.normal(wl.rng(9), (2, p["x"].shape[1], H * P), 0.0, 2.0)
+    if dt == "bf16":
+        p = _bf16_problem(p)
+        gate = bf16_values(gate)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    y = tws.ssm_selective_scan_fwd(to_dev(p["x"], tdt), to_dev(p["delta"], tdt), to_dev(p["A"]),
+                                   to_dev(p["Bm"], tdt), to_dev(p["Cm"], tdt), to_dev(p["D"]),
+                                   to_dev(p["dt_bias"]), True, gate=to_dev(gate, tdt))
+    ref, _ = oracle.selective_scan(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["D"], p["dt_bias"])
+    sil = np.vectorize(oracle.silu)(gate.astype(np.float64))
+    assert rel_err(host(y), ref * sil) <= (TOL["bf16"] if dt == "bf16" else 1e-5)
+
+
+GATED_MIXER_CASES = [
+    ("trissm_gated", dict(batch=2, seqlen=40, layers=1), 31),
+    ("trissm_gated", dict(batch=1, seqlen=19, layers=1, act_dtype="bf16"), 32),
+    ("mamba2_ssd_gated", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=45,
+                              act_dtype="f32", layers=1), 33),
+    ("mamba2_ssd_gated", dict(d_model=256, d_inner=256, d_state=128, nheads=4, headdim=64, batch=2, seqlen=130,
+                              layers=1), 34),
+]
+
+
+@pytest.mark.parametrize("name,over,seed", GATED_MIXER_CASES)
+def test_mixer_gated_parity(name, over, seed):
+    """The gated block (convolution + SiLU on the SSM input, SiLU gate) against the oracle."""
+    cfg = wl.CONFIGS[name].with_(**over)
+    lat, u = wl.mixer_problem(cfg, seed=seed, layers=1)
+    if cfg.act_dtype == "bf16":
+        u = bf16_values(u)
+    gw, ow = quantize_layer(cfg, lat[0])
+    out = run_gpu_stack(cfg, [gw], u)
+    ref = oracle.mixer(oracle_config(cfg), ow, u)
+    assert rel_err(host(out), ref) <= (TOL["bf16"] if cfg.act_dtype == "bf16" else TOL["f32"])
+
+
+def test_mixer_trissm_gated_stack_sampled():
+    per_layer, drift = _stack_sampled("trissm_gated", [0, 41])
+    assert max(per_layer) <= TOL["f32"], per_layer
+
+
+def test_mixer_mamba2_ssd_gated_sampled():
+    per_layer, drift = _stack_sampled("mamba2_ssd_gated", [1])
+    assert max(per_layer) <= TOL["bf16"], per_layer
