@@ -95,12 +95,14 @@ class Problem:
                 packed, scale, _ = tws.ssm_ternary_quantize_weights(
                     torch.from_numpy(lw["W_" + name]).to(dev), cfg.group_size)
                 d["w_" + name], d["s_" + name] = packed, scale
-            for key in ("A", "D", "dt_bias"):
-                d[key] = torch.from_numpy(lw[key]).to(dev)
+            for key in ("A", "D", "dt_bias", "conv_w", "conv_b"):
+                if key in lw:
+                    d[key] = torch.from_numpy(lw[key]).to(dev)
             self.layers.append(d)
         self.c = tws.mixer_config(cfg.kind, cfg.d_model, cfg.d_inner, cfg.d_state, dt_rank=cfg.dt_rank,
                                   nheads=cfg.nheads, headdim=cfg.headdim, act_bits=cfg.act_bits,
-                                  group_size=cfg.group_size, act_dtype=self.act, norm_eps=cfg.norm_eps)
+                                  group_size=cfg.group_size, act_dtype=self.act, norm_eps=cfg.norm_eps,
+                                  gated=cfg.gated, d_conv=cfg.d_conv)
         self.mws = [tws.mixer_weights(d) for d in self.layers]
         self.u = torch.from_numpy(u).to(dev).to(self.act)
         self.bufs = [torch.empty_like(self.u), torch.empty_like(self.u)]
@@ -135,14 +137,20 @@ class StagePlan:
         dt = tws._DTYPES[prob.act]
         self.prob = prob
         self.stages = []  # per layer: list of (name, fn, args ctypes object)
+        ZG = cfg.d_inner if cfg.gated else 0  # gate branch columns of the in_proj output
+        Cc = cfg.conv_channels
         if cfg.kind == wl.MAMBA1:
             PW = cfg.dt_rank + 2 * cfg.d_state
-            self.x = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev)
+            XW = cfg.d_inner + ZG
+            self.xz = torch.empty((M, XW), dtype=prob.act, device=dev)
+            self.x = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev) if cfg.gated else self.xz
             self.p = torch.empty((M, PW), dtype=prob.act, device=dev)
             self.y = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev)
         else:
-            VW = cfg.d_inner + 2 * cfg.d_state + cfg.nheads
+            VW0 = cfg.d_inner + 2 * cfg.d_state + cfg.nheads
+            VW = VW0 + ZG
             self.v = torch.empty((M, VW), dtype=prob.act, device=dev)
+            self.xbc = torch.empty((M, Cc), dtype=prob.act, device=dev) if cfg.gated else None
             self.y = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev)
         self.bl_ws = torch.empty(prob.ws_bytes, dtype=torch.uint8, device=dev)
         L = tws.lib()
@@ -157,6 +165,10 @@ class StagePlan:
             assert L.ssm_bitlinear_workspace_bytes(ctypes.byref(a)) <= prob.ws_bytes
             return a
 
+        def conv(x_ptr, ldx, d, out_ptr):  # arguments of ssm_conv1d_silu_fwd (stream appended at run)
+            return (x_ptr, dt, cfg.batch, cfg.seqlen, Cc, ldx, d["conv_w"].data_ptr(), cfg.d_conv,
+                    d["conv_b"].data_ptr(), None, None, out_ptr, Cc)
+
         for li, d in enumerate(prob.layers):
             src = prob.u if li == 0 else prob.bufs[(li - 1) % 2]
             dst = prob.bufs[li % 2]
@@ -164,7 +176,9 @@ class StagePlan:
             if cfg.kind == wl.MAMBA1:
                 R, N = cfg.dt_rank, cfg.d_state
                 st.append(("bitlinear_in", bl(src.data_ptr(), cfg.d_model, cfg.d_model, d["w_in"], d["s_in"],
-                                              cfg.d_inner, self.x.data_ptr(), cfg.d_inner, None)))
+                                              XW, self.xz.data_ptr(), XW, None)))
+                if cfg.gated:
+                    st.append(("conv", conv(self.xz.data_ptr(), XW, d, self.x.data_ptr())))
                 st.append(("bitlinear_x", bl(self.x.data_ptr(), cfg.d_inner, cfg.d_inner, d["w_x"], d["s_x"], PW,
                                              self.p.data_ptr(), PW, None)))
                 a = tws.ScanArgs()
@@ -179,22 +193,29 @@ class StagePlan:
                 a.y, a.ld_y = self.y.data_ptr(), cfg.d_inner
                 a.dt_in, a.ld_dt_in, a.dt_rank = self.p.data_ptr(), PW, R
                 a.w_dt, a.s_dt, a.dt_eps = d["w_dt"].data_ptr(), d["s_dt"].data_ptr(), cfg.norm_eps
+                if cfg.gated:
+                    a.gate, a.ld_gate = self.xz.data_ptr() + cfg.d_inner * es, XW
                 st.append(("scan", a))
                 st.append(("bitlinear_out", bl(self.y.data_ptr(), cfg.d_inner, cfg.d_inner, d["w_out"], d["s_out"],
                                                cfg.d_model, dst.data_ptr(), cfg.d_model, src.data_ptr())))
             else:
                 H, P, N = cfg.nheads, cfg.headdim, cfg.d_state
-                VW = cfg.d_inner + 2 * N + H
                 st.append(("bitlinear_in", bl(src.data_ptr(), cfg.d_model, cfg.d_model, d["w_in"], d["s_in"], VW,
                                               self.v.data_ptr(), VW, None)))
+                base = self.v.data_ptr()
+                xb, ldb = base, VW
+                if cfg.gated:
+                    st.append(("conv", conv(base, VW, d, self.xbc.data_ptr())))
+                    xb, ldb = self.xbc.data_ptr(), Cc
                 a = tws.ScanArgs()
                 a.batch, a.seqlen, a.nheads, a.headdim, a.d_state = cfg.batch, cfg.seqlen, H, P, N
                 a.a_per_state, a.act_dtype = 0, dt
-                base = self.v.data_ptr()
-                a.x, a.ld_x = base, VW
-                a.Bm, a.ld_B = base + cfg.d_inner * es, VW
-                a.Cm, a.ld_C = base + (cfg.d_inner + N) * es, VW
+                a.x, a.ld_x = xb, ldb
+                a.Bm, a.ld_B = xb + cfg.d_inner * es, ldb
+                a.Cm, a.ld_C = xb + (cfg.d_inner + N) * es, ldb
                 a.delta, a.ld_delta = base + (cfg.d_inner + 2 * N) * es, VW
+                if cfg.gated:
+                    a.gate, a.ld_gate = base + VW0 * es, VW
                 a.delta_bias, a.delta_softplus = d["dt_bias"].data_ptr(), 1
                 a.A, a.D = d["A"].data_ptr(), d["D"].data_ptr()
                 a.y, a.ld_y = self.y.data_ptr(), cfg.d_inner
@@ -215,6 +236,8 @@ class StagePlan:
                 if name == "scan":
                     rc = L.ssm_selective_scan_fwd(ctypes.byref(a), self.scan_ws.data_ptr(), self.scan_ws_bytes,
                                                   stream_handle)
+                elif name == "conv":
+                    rc = L.ssm_conv1d_silu_fwd(*a, stream_handle)
                 else:
                     rc = L.ssm_bitlinear_fwd(ctypes.byref(a), self.bl_ws.data_ptr(), self.prob.ws_bytes,
                                              stream_handle)
@@ -236,13 +259,16 @@ def stage_cost(cfg: wl.MixerConfig, name: str) -> dict:
         wbytes = n * 4 * ((k + 15) // 16)
         byts = M * (k + n) * es + wbytes + (M * n * es if name == "bitlinear_out" else 0)
         return {"bytes": byts, "ops": 2 * M * n * k, "ops_unit": "int8-OP" if cfg.act_bits == 8 else "bf16-FLOP"}
+    if name == "conv":  # read and write each convolved channel once
+        return {"bytes": 2 * M * cfg.conv_channels * es, "ops": None, "ops_unit": None}
+    gate = M * cfg.d_inner * es if cfg.gated else 0
     if cfg.kind == wl.MAMBA1:
         PW = cfg.dt_rank + 2 * cfg.d_state
-        byts = M * (cfg.d_inner + PW + cfg.d_inner) * es
+        byts = M * (cfg.d_inner + PW + cfg.d_inner) * es + gate
         slots = M * cfg.d_inner * cfg.d_state * SCAN_M1_SLOTS_PER_STATE_STEP
         return {"bytes": byts, "ops": 2 * slots, "ops_unit": "fp32-FLOP-eq"}
     VW = cfg.d_inner + 2 * cfg.d_state + cfg.nheads
-    byts = M * (VW + cfg.d_inner) * es
+    byts = M * (VW + cfg.d_inner) * es + gate
     return {"bytes": byts, "ops": None, "ops_unit": None}
 
 
@@ -284,6 +310,9 @@ def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
         ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=prob.dev)
         shape = (B, cfg.d_inner, cfg.d_state) if cfg.kind == wl.MAMBA1 else (B, cfg.nheads, cfg.headdim, cfg.d_state)
         states = [torch.zeros(shape, dtype=torch.float32, device=prob.dev) for _ in prob.mws]
+        cshape = (B, cfg.d_conv - 1, cfg.conv_channels)
+        cstates = [torch.zeros(cshape, dtype=torch.float32, device=prob.dev) if cfg.gated and cfg.d_conv > 1 else None
+                   for _ in prob.mws]
         u = prob.u[:B, 0].contiguous()
         bufs = [torch.empty_like(u), torch.empty_like(u)]
 
@@ -291,7 +320,8 @@ def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
             h = u
             for i, mw in enumerate(prob.mws):
                 o = bufs[i % 2]
-                st = L.ssm_mixer_step(cb, ctypes.byref(mw), h.data_ptr(), o.data_ptr(), B, states[i].data_ptr(), 1,
+                cs = None if cstates[i] is None else cstates[i].data_ptr()
+                st = L.ssm_mixer_step(cb, ctypes.byref(mw), h.data_ptr(), o.data_ptr(), B, states[i].data_ptr(), cs, 1,
                                       ws.data_ptr(), nb, sh)
                 if st != 0:
                     raise tws.SsmError(st, L.ssm_last_error().decode())
@@ -316,7 +346,7 @@ def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / steps
-        sbytes = 2 * sum(t.numel() * 4 for t in states)
+        sbytes = 2 * sum(t.numel() * 4 for t in states + [c for c in cstates if c is not None])
         byts = wbytes + sbytes + 2 * B * cfg.d_model * es
         out[f"batch_{B}"] = {"us_per_token_step": us, "tokens_per_s": B / (us * 1e-6), "layers": len(prob.mws),
                              "bytes_per_step": byts, "GBps": byts / (us * 1e-6) / 1e9,
@@ -333,14 +363,15 @@ def cpu_baseline(cfg: wl.MixerConfig, seed: int, target_s: float) -> dict:
         u = torch.from_numpy(u).to(torch.bfloat16).float().numpy()
     layers = []
     for lw in lat:
-        w = {"A": lw["A"], "D": lw["D"], "dt_bias": lw["dt_bias"]}
+        w = {k: lw[k] for k in ("A", "D", "dt_bias", "conv_w", "conv_b") if k in lw}
         for name in cfg.proj_shapes:
             c, s, _ = oracle.quantize_weights(lw["W_" + name], cfg.group_size)
             w["c_" + name], w["s_" + name] = c, s
         layers.append(w)
     oc = dict(kind=cfg.kind, d_model=cfg.d_model, d_inner=cfg.d_inner, d_state=cfg.d_state, dt_rank=cfg.dt_rank,
               nheads=cfg.nheads, headdim=cfg.headdim, group_size=cfg.group_size, act_bits=cfg.act_bits,
-              act_dtype=oracle.BF16 if cfg.act_dtype == "bf16" else oracle.F32, norm_eps=cfg.norm_eps)
+              act_dtype=oracle.BF16 if cfg.act_dtype == "bf16" else oracle.F32, norm_eps=cfg.norm_eps,
+              gated=cfg.gated, d_conv=cfg.d_conv)
     # calibrate on one sequence, then run enough whole sequences (the whole batch repeated, when
     # one pass over it is shorter than the target) to fill the target time
     t0 = time.perf_counter()
@@ -518,6 +549,7 @@ def main():
         return
 
     tokens = cfg.tokens
+    blk = "gated block (conv + SiLU gate around the mixer)" if cfg.gated else "mixer"
     line = {
         "metric": "mixer tokens/s at TriSSM shape" if args.workload == "trissm" else f"mixer tokens/s ({cfg.name})",
         "value": tokens / (result["ms_per_step"] * 1e-3),
@@ -531,14 +563,14 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if cfg.act_dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.layers}-layer ternary selective-SSM mixer stack" if cfg.layers > 1
-                   else f"{cfg.name}: one ternary selective-SSM mixer layer",
+        "config": {"workload": f"{cfg.name}: {cfg.layers}-layer ternary selective-SSM {blk} stack" if cfg.layers > 1
+                   else f"{cfg.name}: one ternary selective-SSM {blk} layer",
                    "kind": "mamba1" if cfg.kind == wl.MAMBA1 else "ssd", "layers": cfg.layers,
                    "d_model": cfg.d_model, "d_inner": cfg.d_inner, "d_state": cfg.d_state, "dt_rank": cfg.dt_rank,
                    "nheads": cfg.nheads, "headdim": cfg.headdim, "batch": cfg.batch, "seq_len": cfg.seqlen,
                    "tokens_per_step": tokens, "act_bits": cfg.act_bits, "group_size": cfg.group_size,
                    "contraction": "int8 x ternary -> int32 (MFMA)" if cfg.act_bits == 8 else
-                   "bf16 x ternary -> fp32 (MFMA)", "scan_state": "fp32"},
+                   "bf16 x ternary -> fp32 (MFMA)", "scan_state": "fp32", "gated": cfg.gated, "d_conv": cfg.d_conv},
         "timing": {k: v for k, v in result.items() if k != "ms_per_step"},
         "stages": stages,
         "stage_ms_per_step": stage_total_ms,

@@ -41,8 +41,7 @@ __global__ __launch_bounds__(256) void k_conv_silu(ConvArgs a, int64_t chunk_len
     else if (a.state_in) v = a.state_in[(b * (K - 1) + (ts + K - 1)) * a.C + c];
     win[j] = v;
   }
-  for (int64_t t = t0; t < t1; ++t) {
-    const float xv = ld_act(X + (b * a.L + t) * a.ldx + c);
+  auto step = [&](float xv, int64_t t) {
     double acc = bias;
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) acc = acc + wk[j] * (double)win[j];
@@ -52,7 +51,8 @@ __global__ __launch_bounds__(256) void k_conv_silu(ConvArgs a, int64_t chunk_len
 #pragma unroll
     for (int j = 0; j + 1 < K - 1; ++j) win[j] = win[j + 1];
     if (K > 1) win[K > 1 ? K - 2 : 0] = xv;
-  }
+  };
+  for (int64_t t = t0; t < t1; ++t) step(ld_act(X + (b * a.L + t) * a.ldx + c), t);
   // the state after the sequence: its last K - 1 inputs (the window after the last step)
   if (a.state_out && t1 == a.L) {
 #pragma unroll

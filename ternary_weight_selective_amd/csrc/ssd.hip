@@ -147,6 +147,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NTN = NS / 16;       // 16-wide n tiles
   constexpr int KN = NS / 32;        // k steps over n
   __shared__ __align__(16) uint16_t sX[Q * XS];        // x  [t][p]
+  __shared__ __align__(16) uint16_t sG[Q * XS];        // gate [t][p] (gated block)
   __shared__ __align__(16) uint16_t sXT[P * XS];       // x^T [p][s]
   __shared__ __align__(16) uint16_t sB[Q * NSP];       // B  [s][n]
   __shared__ __align__(16) uint16_t sBT[NS * XS];      // B^T [n][s]
@@ -195,8 +196,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // chunk loads, 16-byte chunks with the step index fastest across the lanes (lane = step t,
   // chunk column q = wave + 4 i), so that the transposed LDS copies are written along rows
   constexpr int XC = Q * P / 8 / 256, BC = Q * NS / 8 / 256;
-  v4i px[XC], pb[BC], pc[BC];
+  v4i px[XC], pg[XC], pb[BC], pc[BC];
   float pdt = 0.0f;
+  const bf16_t* G = (const bf16_t*)a.gate;
   auto load = [&](int64_t c0) {
     const bool ok = c0 + lane < L;
     const int64_t tok = b * L + c0 + lane;
@@ -204,6 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < XC; ++i) {
       const int q = w + 4 * i;
       px[i] = ok ? *(const v4i*)(X + tok * a.ld_x + hd * P + q * 8) : v4i{0, 0, 0, 0};
+      if (G) pg[i] = ok ? *(const v4i*)(G + tok * a.ld_gate + hd * P + q * 8) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
@@ -219,6 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < XC; ++i) {
       const int q = w + 4 * i;
       *(v4i*)(&sX[t * XS + q * 8]) = px[i];
+      if (G) *(v4i*)(&sG[t * XS + q * 8]) = pg[i];
       const uint16_t* v = (const uint16_t*)&px[i];
 #pragma unroll
       for (int u = 0; u < 8; ++u) sXT[(q * 8 + u) * XS + t] = v[u];
@@ -325,12 +329,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (c0 + t >= L) continue;
       const float et = s_et[t];
       bf16_t* yr = Y + (b * L + c0 + t) * a.ld_y + hd * P;
-      const bf16_t* gr = a.gate ? (const bf16_t*)a.gate + (b * L + c0 + t) * a.ld_gate + hd * P : nullptr;
 #pragma unroll
       for (int jp = 0; jp < 4; ++jp) {
         const int pp = 16 * jp + l16;
         float yv = yacc[jp][r] + et * zacc[jp][r] + D_h * bf_val(sX[t * XS + pp]);
-        if (gr) yv = yv * silu_gate(bf_val(gr[pp]));
+        if (G) yv = yv * silu_gate(bf_val(sG[t * XS + pp]));
         yr[pp] = f32_to_bf16(yv);
       }
     }
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 static bool ssd_chunk_ok(const ScanArgs& a) {
   auto al = [](const void* p) { return ((uintptr_t)p % 16) == 0; };
   return a.act_bf16 && a.P == kSsdP && (a.N == 64 || a.N == 128) && a.ld_x % 8 == 0 && a.ld_B % 8 == 0 &&
-         a.ld_C % 8 == 0 && al(a.x) && al(a.Bm) && al(a.Cm);  // (the gate is read element-wise)
+         a.ld_C % 8 == 0 && al(a.x) && al(a.Bm) && al(a.Cm) && (!a.gate || (a.ld_gate % 8 == 0 && al(a.gate)));
 }
 
 template <int NS, typename T>

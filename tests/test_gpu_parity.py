@@ -503,7 +503,8 @@ GATED_MIXER_CASES = [
     ("trissm_gated", dict(batch=1, seqlen=19, layers=1, act_dtype="bf16"), 32),
     ("mamba2_ssd_gated", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=45,
                               act_dtype="f32", layers=1), 33),
-    ("mamba2_ssd_gated", dict(d_model=256, d_inner=256, d_state=128, nheads=4, headdim=64, batch=2, seqlen=130,
+    # eight heads: every in_proj column block starts 16-byte aligned, so the chunked SSD kernel runs
+    ("mamba2_ssd_gated", dict(d_model=256, d_inner=512, d_state=128, nheads=8, headdim=64, batch=2, seqlen=130,
                               layers=1), 34),
 ]
 
