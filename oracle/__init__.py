@@ -49,7 +49,8 @@ class _MixerWeights(ctypes.Structure):
     _fields_ = [("c_in", _c_i8p), ("c_x", _c_i8p), ("c_dt", _c_i8p), ("c_out", _c_i8p),
                 ("s_in", _c_f32p), ("s_x", _c_f32p), ("s_dt", _c_f32p), ("s_out", _c_f32p),
                 ("g_in", _c_f32p), ("g_x", _c_f32p), ("g_dt", _c_f32p), ("g_out", _c_f32p),
-                ("dt_bias", _c_f32p), ("A", _c_f32p), ("D", _c_f32p), ("conv_w", _c_f32p), ("conv_b", _c_f32p)]
+                ("dt_bias", _c_f32p), ("A", _c_f32p), ("D", _c_f32p), ("conv_w", _c_f32p), ("conv_b", _c_f32p),
+                ("f_in", _c_f32p), ("f_x", _c_f32p), ("f_dt", _c_f32p), ("f_out", _c_f32p)]
 
 
 def lib():
@@ -87,7 +88,8 @@ def lib():
         L.orc_selective_scan_quadratic.argtypes = scan_args + [_c_f64p]
         L.orc_mixer.argtypes = [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_float, ctypes.POINTER(_MixerWeights), _c_f32p,
-                                _i64, _i64, ctypes.c_int, ctypes.c_int, _i64, _c_f64p]
+                                _i64, _i64, ctypes.c_int, ctypes.c_int, _i64, ctypes.c_int, _c_f64p]
+        L.orc_dense.argtypes = [_c_f32p, _i64, _i64, _i64, _c_f32p, _i64, _c_f64p]
         L.orc_mixer.restype = ctypes.c_int
         L.orc_silu.argtypes = [ctypes.c_double]
         L.orc_silu.restype = ctypes.c_double
@@ -284,6 +286,22 @@ def conv_silu(x, w, bias=None, state=None, act_dtype: int = 0, channels: int | N
     return out, st_out
 
 
+# ---------------------------------------------------------------- full-precision projection
+
+def dense(x, W, k: int | None = None) -> np.ndarray:
+    """y = x[:, :k] W^T in fp64 (a full-precision linear layer: no norm, no quantisation)."""
+    x = _f32(x)
+    m, ldx = x.shape
+    W = _f32(W)
+    n, kk = W.shape
+    k = kk if k is None else k
+    if k != kk:
+        raise ValueError("W must have k columns")
+    y = np.empty((m, n), dtype=np.float64)
+    lib().orc_dense(_p(x, _c_f32p), m, k, ldx, _p(W, _c_f32p), n, _p(y, _c_f64p))
+    return y
+
+
 # ---------------------------------------------------------------- mixer
 
 MAMBA1, SSD = 0, 1
@@ -293,7 +311,9 @@ def mixer(cfg, weights: dict, u, residual: bool = True) -> np.ndarray:
     """One mixer layer.  cfg: mapping with kind, d_model, d_inner, d_state, dt_rank,
     nheads, headdim, group_size, act_bits, act_dtype (F32/BF16), norm_eps.
     weights: codes c_in/c_x/c_dt/c_out, scales s_*, dt_bias, A, D (gains optional g_*); for the
-    gated block (cfg gated = 1, d_conv) also conv_w [Cc, d_conv] and conv_b [Cc] (optional).
+    gated block (cfg gated = 1, d_conv) also conv_w [Cc, d_conv] and conv_b [Cc] (optional);
+    for full-precision projections (cfg fp_proj = 1: in/out, 2: all) f_in / f_x / f_dt / f_out
+    [n_out, k] weight values.
     u: [B, L, d_model] values (bf16-representable when act_dtype is BF16).
     Returns out fp64 [B, L, d_model], each value already rounded to act_dtype."""
     u = _f32(u)
@@ -315,12 +335,14 @@ def mixer(cfg, weights: dict, u, residual: bool = True) -> np.ndarray:
         arr("g_in", np.float32, _c_f32p), arr("g_x", np.float32, _c_f32p), arr("g_dt", np.float32, _c_f32p),
         arr("g_out", np.float32, _c_f32p), arr("dt_bias", np.float32, _c_f32p),
         arr("A", np.float32, _c_f32p), arr("D", np.float32, _c_f32p), arr("conv_w", np.float32, _c_f32p),
-        arr("conv_b", np.float32, _c_f32p))
+        arr("conv_b", np.float32, _c_f32p), arr("f_in", np.float32, _c_f32p), arr("f_x", np.float32, _c_f32p),
+        arr("f_dt", np.float32, _c_f32p), arr("f_out", np.float32, _c_f32p))
     out = np.empty((batch, L, dm), dtype=np.float64)
     rc = lib().orc_mixer(int(cfg["kind"]), cfg["d_model"], cfg["d_inner"], cfg["d_state"], cfg.get("dt_rank", 0),
                          cfg.get("nheads", 0), cfg.get("headdim", 0), cfg.get("group_size", 0), cfg["act_bits"],
                          cfg["act_dtype"], cfg.get("norm_eps", 1e-5), ctypes.byref(w), _p(u, _c_f32p), batch, L,
-                         int(residual), int(cfg.get("gated", 0)), int(cfg.get("d_conv", 0)), _p(out, _c_f64p))
+                         int(residual), int(cfg.get("gated", 0)), int(cfg.get("d_conv", 0)), int(cfg.get("fp_proj", 0)),
+                         _p(out, _c_f64p))
     if rc != 0:
         raise OverflowError("int32 accumulator overflow in the mixer")
     return out

@@ -455,6 +455,26 @@ void orc_selective_scan_quadratic(int64_t batch, int64_t L, int64_t H, int64_t P
 }
 
 /* ------------------------------------------------------------------------- */
+/* O9: full-precision projections ([TriSSM]: the model keeps its in and out    */
+/* projections in full precision, only Delta, B, C are ternary; its fp_ssm      */
+/* baseline has no ternary projection)                                          */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * y[m, n] = sum_k x[m, k] * W[n, k], fp64, for a full-precision linear layer: no
+ * RMSNorm, no quantisation, no bias.  x [m, ldx] (first k columns), W [n, k].
+ */
+void orc_dense(const float* x, int64_t m, int64_t k, int64_t ldx, const float* W, int64_t n, double* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t j = 0; j < n; ++j) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < k; ++c) acc += (double)x[i * ldx + c] * (double)W[j * k + c];
+      y[i * n + j] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* O8: the gated block around the mixer ([Builds-on] Mamba: the block's short   */
 /* causal depthwise convolution with SiLU on the SSM input, and the SiLU gate   */
 /* from the second in_proj branch; [Shape]: the gated diagonal-SSM block)      */
@@ -514,6 +534,7 @@ typedef struct {
   const float *g_in, *g_x, *g_dt, *g_out; /* RMSNorm gains or NULL */
   const float *dt_bias, *A, *D;
   const float *conv_w, *conv_b; /* gated block only: [Cc, d_conv], [Cc] or NULL */
+  const float *f_in, *f_x, *f_dt, *f_out; /* full-precision weights [n_out, k] (O9) or NULL */
 } orc_mixer_weights;
 
 /*
@@ -531,11 +552,15 @@ typedef struct {
  * SSD); the SSM input channels (x for Mamba-1, x, B and C for SSD; Cc of them)
  * go through orc_conv_silu of width d_conv before anything reads them, and the
  * scan output becomes y * silu(zg) (fp64, rounded to act_dtype) before out_proj.
+ * fp_proj (O9): 0 every projection ternary; 1 in_proj and out_proj full precision
+ * (orc_dense with f_in / f_out; the TriSSM model); 2 every projection full precision
+ * (the fp_ssm baseline; the Mamba-1 dt projection output is then stored in act_dtype
+ * before the scan reads it, like every other stored activation).
  */
 int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64_t dt_rank,
               int64_t nheads, int64_t headdim, int64_t group, int act_bits, int act_dtype,
               float eps, const orc_mixer_weights* w, const float* u, int64_t batch, int64_t L,
-              int residual, int gated, int64_t d_conv, double* out) {
+              int residual, int gated, int64_t d_conv, int fp_proj, double* out) {
   int64_t M = batch * L, Dm = d_model, Di = d_inner, N = d_state, R = dt_rank;
   int rc = 0;
   float* y32 = (float*)malloc(sizeof(float) * (size_t)(M * Di));
@@ -552,8 +577,9 @@ int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64
     float* z32 = (float*)malloc(sizeof(float) * (size_t)(M * Di));
     float* B32 = (float*)malloc(sizeof(float) * (size_t)(M * N));
     float* C32 = (float*)malloc(sizeof(float) * (size_t)(M * N));
-    rc |= orc_bitlinear(u, M, Dm, Dm, w->g_in, eps, act_bits, w->c_in, w->s_in, XW, group, NULL,
-                        xd, NULL, NULL, NULL);
+    if (fp_proj >= 1) orc_dense(u, M, Dm, Dm, w->f_in, XW, xd);
+    else rc |= orc_bitlinear(u, M, Dm, Dm, w->g_in, eps, act_bits, w->c_in, w->s_in, XW, group, NULL,
+                             xd, NULL, NULL, NULL);
     orc_round_array(xd, xz, M * XW, act_dtype);
     if (gated) {
       orc_conv_silu(batch, L, Di, d_conv, xz, XW, w->conv_w, w->conv_b, NULL, act_dtype, x32, NULL);
@@ -562,14 +588,20 @@ int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64
     } else {
       memcpy(x32, xz, sizeof(float) * (size_t)(M * Di));
     }
-    rc |= orc_bitlinear(x32, M, Di, Di, w->g_x, eps, act_bits, w->c_x, w->s_x, PW, group, NULL, pd,
-                        NULL, NULL, NULL);
+    if (fp_proj >= 2) orc_dense(x32, M, Di, Di, w->f_x, PW, pd);
+    else rc |= orc_bitlinear(x32, M, Di, Di, w->g_x, eps, act_bits, w->c_x, w->s_x, PW, group, NULL, pd,
+                             NULL, NULL, NULL);
     orc_round_array(pd, p32, M * PW, act_dtype);
     /* dt projection reads the first R columns of p (row stride PW) */
-    rc |= orc_bitlinear(p32, M, R, PW, w->g_dt, eps, act_bits, w->c_dt, w->s_dt, Di, group, NULL,
-                        zd, NULL, NULL, NULL);
-    /* z is not stored: pass it to the scan at fp32 width (the scan's input type) */
-    for (int64_t i = 0; i < M * Di; ++i) z32[i] = (float)zd[i];
+    if (fp_proj >= 2) {
+      orc_dense(p32, M, R, PW, w->f_dt, Di, zd);
+      orc_round_array(zd, z32, M * Di, act_dtype); /* stored, then read by the scan */
+    } else {
+      rc |= orc_bitlinear(p32, M, R, PW, w->g_dt, eps, act_bits, w->c_dt, w->s_dt, Di, group, NULL,
+                          zd, NULL, NULL, NULL);
+      /* z is not stored: pass it to the scan at fp32 width (the scan's input type) */
+      for (int64_t i = 0; i < M * Di; ++i) z32[i] = (float)zd[i];
+    }
     for (int64_t i = 0; i < M; ++i)
       for (int64_t s = 0; s < N; ++s) {
         B32[i * N + s] = p32[i * PW + R + s];
@@ -588,8 +620,9 @@ int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64
     float* B32 = (float*)malloc(sizeof(float) * (size_t)(M * N));
     float* C32 = (float*)malloc(sizeof(float) * (size_t)(M * N));
     float* dt32 = (float*)malloc(sizeof(float) * (size_t)(M * H));
-    rc |= orc_bitlinear(u, M, Dm, Dm, w->g_in, eps, act_bits, w->c_in, w->s_in, VW, group, NULL, vd,
-                        NULL, NULL, NULL);
+    if (fp_proj >= 1) orc_dense(u, M, Dm, Dm, w->f_in, VW, vd);
+    else rc |= orc_bitlinear(u, M, Dm, Dm, w->g_in, eps, act_bits, w->c_in, w->s_in, VW, group, NULL, vd,
+                             NULL, NULL, NULL);
     orc_round_array(vd, v32, M * VW, act_dtype);
     if (gated) {
       orc_conv_silu(batch, L, Cc, d_conv, v32, VW, w->conv_w, w->conv_b, NULL, act_dtype, xbc, NULL);
@@ -615,8 +648,9 @@ int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64
     for (int64_t i = 0; i < M * Di; ++i) yd[i] = yd[i] * orc_silu((double)zg[i]);
   free(zg);
   orc_round_array(yd, y32, M * Di, act_dtype);
-  rc |= orc_bitlinear(y32, M, Di, Di, w->g_out, eps, act_bits, w->c_out, w->s_out, Dm, group, NULL,
-                      out, NULL, NULL, NULL);
+  if (fp_proj >= 1) orc_dense(y32, M, Di, Di, w->f_out, Dm, out);
+  else rc |= orc_bitlinear(y32, M, Di, Di, w->g_out, eps, act_bits, w->c_out, w->s_out, Dm, group, NULL,
+                           out, NULL, NULL, NULL);
   if (residual)
     for (int64_t i = 0; i < M * Dm; ++i) out[i] += (double)u[i];
   for (int64_t i = 0; i < M * Dm; ++i) out[i] = store_as(out[i], act_dtype);

@@ -726,3 +726,104 @@ def test_mixer_gated_mamba1_composition():
     o, *_ = oracle.bitlinear(yg, w["c_out"], w["s_out"])
     ref = (o + uu).astype(np.float32).astype(np.float64).reshape(out.shape)
     np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------------------------ full-precision projections
+
+def test_dense_vs_numpy():
+    """A full-precision linear layer is x W^T: numpy's fp64 matmul, and a strided input."""
+    g = wl.rng(31)
+    x = wl.normal(g, (13, 40))
+    W = wl.normal(g, (9, 24))
+    y = oracle.dense(x, W, k=24)
+    np.testing.assert_allclose(y, x[:, :24].astype(np.float64) @ W.T.astype(np.float64), rtol=1e-13, atol=1e-13)
+    eye = np.eye(24, dtype=np.float32)
+    np.testing.assert_array_equal(oracle.dense(x, eye, k=24), x[:, :24].astype(np.float64))
+
+
+def _fp_layer(cfg, seed):
+    lat, u = wl.mixer_problem(cfg, seed=seed)
+    w = {"dt_bias": lat[0]["dt_bias"], "A": lat[0]["A"], "D": lat[0]["D"]}
+    for name in cfg.proj_shapes:
+        if cfg.is_fp(name):
+            w["f_" + name] = lat[0]["W_" + name]
+        else:
+            c, s, _ = oracle.quantize_weights(lat[0]["W_" + name], cfg.group_size)
+            w["c_" + name], w["s_" + name] = c, s
+    return w, u
+
+
+def _fp_cfg_dict(cfg):
+    d = _cfg_dict(cfg)
+    d["fp_proj"] = cfg.fp_proj
+    return d
+
+
+FP_SMALL = {
+    "inout": wl.CONFIGS["trissm_fp_inout"].with_(d_model=64, d_inner=128, dt_rank=8, batch=2, seqlen=24, layers=1),
+    "all": wl.CONFIGS["trissm_fp"].with_(d_model=64, d_inner=128, dt_rank=8, batch=2, seqlen=24, layers=1),
+    "ssd": wl.CONFIGS["mamba2_ssd_fp"].with_(d_model=128, d_inner=128, d_state=16, nheads=2, headdim=64, batch=1,
+                                             seqlen=20, act_dtype="f32", layers=1),
+}
+
+
+@pytest.mark.parametrize("mode", ["inout", "all", "ssd"])
+def test_mixer_fp_zero_out_proj_is_identity(mode):
+    """Full-precision out_proj weights zero: the layer returns u exactly (residual only)."""
+    cfg = FP_SMALL[mode]
+    w, u = _fp_layer(cfg, 41)
+    w["f_out"] = np.zeros_like(w["f_out"])
+    np.testing.assert_array_equal(oracle.mixer(_fp_cfg_dict(cfg), w, u), u.astype(np.float64))
+
+
+@pytest.mark.parametrize("mode", ["inout", "all", "ssd"])
+def test_mixer_fp_zero_in_proj_is_identity(mode):
+    """Full-precision in_proj weights zero: x (and B, C for SSD) vanish, so C h and D x vanish and
+    the layer returns u exactly -- in_proj feeds both x_proj and the scan."""
+    cfg = FP_SMALL[mode]
+    w, u = _fp_layer(cfg, 42)
+    w["f_in"] = np.zeros_like(w["f_in"])
+    np.testing.assert_array_equal(oracle.mixer(_fp_cfg_dict(cfg), w, u), u.astype(np.float64))
+
+
+def test_mixer_fp_inout_composition():
+    """TriSSM's split: x = u W_in^T (numpy), the ternary x_proj / dt / scan stages (pinned above),
+    out = y W_out^T (numpy), + u."""
+    cfg = FP_SMALL["inout"]
+    w, u = _fp_layer(cfg, 43)
+    out = oracle.mixer(_fp_cfg_dict(cfg), w, u)
+    M, R, N = cfg.tokens, cfg.dt_rank, cfg.d_state
+    sh = (cfg.batch, cfg.seqlen)
+    uu = u.reshape(M, -1)
+    x = (uu.astype(np.float64) @ w["f_in"].T.astype(np.float64)).astype(np.float32)
+    p, *_ = oracle.bitlinear(x, w["c_x"], w["s_x"])
+    p = p.astype(np.float32)
+    z, *_ = oracle.bitlinear(p, w["c_dt"], w["s_dt"], k=R)
+    y, _ = oracle.selective_scan(x.reshape(*sh, -1), z.astype(np.float32).reshape(*sh, -1), w["A"],
+                                 p[:, R:R + N].reshape(*sh, -1), p[:, R + N:].reshape(*sh, -1), w["D"], w["dt_bias"])
+    o = y.astype(np.float32).reshape(M, -1).astype(np.float64) @ w["f_out"].T.astype(np.float64)
+    ref = (o + uu).astype(np.float32).astype(np.float64).reshape(out.shape)
+    np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-7)
+
+
+def test_mixer_fp_all_dt_stored():
+    """fp_ssm baseline: the dt projection output is stored in the activation type before the
+    scan reads it (a bf16 layer equals the composition with that rounding)."""
+    cfg = FP_SMALL["all"].with_(act_dtype="bf16")
+    w, u = _fp_layer(cfg, 44)
+    u = oracle.round_bf16(u)
+    out = oracle.mixer(_fp_cfg_dict(cfg), w, u)
+    M, R, N = cfg.tokens, cfg.dt_rank, cfg.d_state
+    sh = (cfg.batch, cfg.seqlen)
+    rb = oracle.round_bf16
+    uu = u.reshape(M, -1)
+    x = rb((uu.astype(np.float64) @ w["f_in"].T.astype(np.float64)).astype(np.float32))
+    p = rb((x.astype(np.float64) @ w["f_x"].T.astype(np.float64)).astype(np.float32))
+    dt = rb((p[:, :R].astype(np.float64) @ w["f_dt"].T.astype(np.float64)).astype(np.float32))
+    y, _ = oracle.selective_scan(x.reshape(*sh, -1), dt.reshape(*sh, -1), w["A"], p[:, R:R + N].reshape(*sh, -1),
+                                 p[:, R + N:].reshape(*sh, -1), w["D"], w["dt_bias"])
+    y = rb(y.astype(np.float32)).reshape(M, -1)
+    o = y.astype(np.float64) @ w["f_out"].T.astype(np.float64)
+    ref = rb((o + uu).astype(np.float32)).astype(np.float64).reshape(out.shape)
+    bad = np.abs(out - ref) > 2 ** -7 * np.abs(ref) + 1e-6
+    assert bad.mean() < 1e-3, bad.mean()

@@ -16,6 +16,9 @@ The workloads follow the model shapes of the pages:
   * mamba2_a8     the same SSD mixer shape with int8 absmax activations and one scale
                   per tensor: the A8 contraction at its largest shapes, (8192, 4416, 2048)
                   and (8192, 2048, 4096), where it is bound by the int8 matrix cores
+  * trissm_fp_inout, trissm_fp, mamba2_ssd_fp: full-precision projections (the TriSSM
+                  model's in/out projections; all of them for the fp_ssm baseline), weights
+                  ~ N(0, 1/k) for those
   * trissm_gated, mamba2_ssd_gated: the same shapes as the gated block (a short causal
                   convolution of width 4 with SiLU on the SSM input, a SiLU gate from a
                   second in_proj branch)
@@ -53,6 +56,7 @@ class MixerConfig:
     norm_eps: float = 1e-5
     gated: int = 0              # 1: the gated block (short causal convolution + SiLU gate)
     d_conv: int = 0             # width of that convolution
+    fp_proj: int = 0            # 0 all projections ternary; 1 in/out full precision; 2 all full precision
 
     @property
     def tokens(self) -> int:
@@ -69,6 +73,12 @@ class MixerConfig:
                     "out": (self.d_model, self.d_inner)}
         vw = self.nheads * self.headdim + 2 * self.d_state + self.nheads
         return {"in": (vw + zg, self.d_model), "out": (self.d_model, self.d_inner)}
+
+    def is_fp(self, name: str) -> bool:
+        """Whether projection `name` is full precision (dense weights) rather than ternary."""
+        if self.fp_proj >= 2:
+            return True
+        return self.fp_proj == 1 and name in ("in", "out")
 
     @property
     def conv_channels(self) -> int:
@@ -96,8 +106,13 @@ CONFIGS = {
 # input, SiLU gate from a second in_proj branch), at the TriSSM and Mamba-2 shapes
 CONFIGS["trissm_gated"] = CONFIGS["trissm"].with_(name="trissm_gated", gated=1, d_conv=4)
 CONFIGS["mamba2_ssd_gated"] = CONFIGS["mamba2_ssd"].with_(name="mamba2_ssd_gated", gated=1, d_conv=4)
+# full-precision projections: the TriSSM model's own split (in/out full precision, Delta, B, C
+# ternary) and its fp_ssm baseline (no ternary projection); the Mamba-2 layer in bf16
+CONFIGS["trissm_fp_inout"] = CONFIGS["trissm"].with_(name="trissm_fp_inout", fp_proj=1)
+CONFIGS["trissm_fp"] = CONFIGS["trissm"].with_(name="trissm_fp", fp_proj=2)
+CONFIGS["mamba2_ssd_fp"] = CONFIGS["mamba2_ssd"].with_(name="mamba2_ssd_fp", fp_proj=2)
 CONFIG_ORDER = ["bitssm_tiny", "trissm", "long_scan", "ternaryssm50m", "mamba2_ssd", "mamba2_a8", "trissm_gated",
-                "mamba2_ssd_gated"]
+                "mamba2_ssd_gated", "trissm_fp_inout", "trissm_fp", "mamba2_ssd_fp"]
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -117,7 +132,8 @@ def layer_latent(cfg: MixerConfig, g: np.random.Generator) -> dict:
     """Latent fp32 weights of one layer, drawn in a fixed order: projections, A, D, dt_bias."""
     out = {}
     for name, (n, k) in cfg.proj_shapes.items():
-        out["W_" + name] = normal(g, (n, k), 0.0, 0.02)
+        # full-precision projections have no RMSNorm in front: unit-variance outputs (std 1/sqrt(k))
+        out["W_" + name] = normal(g, (n, k), 0.0, 1.0 / math.sqrt(k) if cfg.is_fp(name) else 0.02)
     h = cfg.d_inner if cfg.kind == MAMBA1 else cfg.nheads
     out["A"] = a_log_uniform(g, (h, cfg.d_state) if cfg.kind == MAMBA1 else (h,))
     out["D"] = normal(g, (h,), 1.0, 0.1)
