@@ -39,6 +39,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (FMA = 2 FLOP per lane)
 INT8_MFMA_PEAK_TOPS = 5000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_MATRIX_PEAK_TFLOPS = 157.3  # MI355X fp32 on the matrix cores (the full-precision baselines)
 # One VALU lane-instruction slot counts as 2 FLOP-equivalents (an FMA); a transcendental
 # (v_exp_f32) occupies 4 slots (quarter rate).  The Mamba-1 recurrence needs, per
 # (token, channel, state): dt*A, exp2, (dt*x)*B, fma for h, fma for y = 4 slots + 4 slots.
@@ -48,6 +49,8 @@ KERNEL_SOURCES = {  # source files whose text defines each timed kernel (for sta
     "scan_m1": ["scan.hip", "common.hpp", "launch.hpp"],
     "ssd": ["ssd.hip", "common.hpp", "launch.hpp"],
     "bitlinear": ["norm.hip", "bitlinear.hip", "common.hpp", "launch.hpp"],
+    "conv": ["conv.hip", "common.hpp", "launch.hpp"],
+    "dense": ["dense.cpp", "launch.hpp"],
 }
 
 
@@ -92,6 +95,9 @@ class Problem:
         for lw in lat:
             d = {}
             for name in cfg.proj_shapes:
+                if cfg.is_fp(name):  # full-precision projection: dense weights in the act dtype
+                    d["fw_" + name] = torch.from_numpy(lw["W_" + name]).to(dev).to(self.act)
+                    continue
                 packed, scale, _ = tws.ssm_ternary_quantize_weights(
                     torch.from_numpy(lw["W_" + name]).to(dev), cfg.group_size)
                 d["w_" + name], d["s_" + name] = packed, scale
@@ -102,7 +108,7 @@ class Problem:
         self.c = tws.mixer_config(cfg.kind, cfg.d_model, cfg.d_inner, cfg.d_state, dt_rank=cfg.dt_rank,
                                   nheads=cfg.nheads, headdim=cfg.headdim, act_bits=cfg.act_bits,
                                   group_size=cfg.group_size, act_dtype=self.act, norm_eps=cfg.norm_eps,
-                                  gated=cfg.gated, d_conv=cfg.d_conv)
+                                  gated=cfg.gated, d_conv=cfg.d_conv, fp_proj=cfg.fp_proj)
         self.mws = [tws.mixer_weights(d) for d in self.layers]
         self.u = torch.from_numpy(u).to(dev).to(self.act)
         self.bufs = [torch.empty_like(self.u), torch.empty_like(self.u)]
@@ -145,6 +151,7 @@ class StagePlan:
             self.xz = torch.empty((M, XW), dtype=prob.act, device=dev)
             self.x = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev) if cfg.gated else self.xz
             self.p = torch.empty((M, PW), dtype=prob.act, device=dev)
+            self.dl = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev) if cfg.fp_proj == 2 else None
             self.y = torch.empty((M, cfg.d_inner), dtype=prob.act, device=dev)
         else:
             VW0 = cfg.d_inner + 2 * cfg.d_state + cfg.nheads
@@ -165,6 +172,15 @@ class StagePlan:
             assert L.ssm_bitlinear_workspace_bytes(ctypes.byref(a)) <= prob.ws_bytes
             return a
 
+        def dense(x_ptr, k, ldx, w, n, y_ptr, ldy, res_ptr):  # arguments of ssm_dense_fwd
+            return (x_ptr, dt, M, k, ldx, w.data_ptr(), n, res_ptr, cfg.d_model if res_ptr else 0, y_ptr, ldy)
+
+        def proj(name, x_ptr, k, ldx, d, n, y_ptr, ldy, res_ptr):
+            """(stage name, args) of one projection, ternary or full precision."""
+            if cfg.is_fp(name):
+                return ("dense_" + name, dense(x_ptr, k, ldx, d["fw_" + name], n, y_ptr, ldy, res_ptr))
+            return ("bitlinear_" + name, bl(x_ptr, k, ldx, d["w_" + name], d["s_" + name], n, y_ptr, ldy, res_ptr))
+
         def conv(x_ptr, ldx, d, out_ptr):  # arguments of ssm_conv1d_silu_fwd (stream appended at run)
             return (x_ptr, dt, cfg.batch, cfg.seqlen, Cc, ldx, d["conv_w"].data_ptr(), cfg.d_conv,
                     d["conv_b"].data_ptr(), None, None, out_ptr, Cc)
@@ -175,12 +191,13 @@ class StagePlan:
             st = []
             if cfg.kind == wl.MAMBA1:
                 R, N = cfg.dt_rank, cfg.d_state
-                st.append(("bitlinear_in", bl(src.data_ptr(), cfg.d_model, cfg.d_model, d["w_in"], d["s_in"],
-                                              XW, self.xz.data_ptr(), XW, None)))
+                st.append(proj("in", src.data_ptr(), cfg.d_model, cfg.d_model, d, XW, self.xz.data_ptr(), XW, None))
                 if cfg.gated:
                     st.append(("conv", conv(self.xz.data_ptr(), XW, d, self.x.data_ptr())))
-                st.append(("bitlinear_x", bl(self.x.data_ptr(), cfg.d_inner, cfg.d_inner, d["w_x"], d["s_x"], PW,
-                                             self.p.data_ptr(), PW, None)))
+                st.append(proj("x", self.x.data_ptr(), cfg.d_inner, cfg.d_inner, d, PW, self.p.data_ptr(), PW, None))
+                if cfg.fp_proj == 2:
+                    st.append(proj("dt", self.p.data_ptr(), R, PW, d, cfg.d_inner, self.dl.data_ptr(), cfg.d_inner,
+                                   None))
                 a = tws.ScanArgs()
                 a.batch, a.seqlen, a.nheads, a.headdim, a.d_state = cfg.batch, cfg.seqlen, cfg.d_inner, 1, N
                 a.a_per_state, a.act_dtype = 1, dt
@@ -191,17 +208,19 @@ class StagePlan:
                 a.Cm, a.ld_C = self.p.data_ptr() + (R + N) * es, PW
                 a.D = d["D"].data_ptr()
                 a.y, a.ld_y = self.y.data_ptr(), cfg.d_inner
-                a.dt_in, a.ld_dt_in, a.dt_rank = self.p.data_ptr(), PW, R
-                a.w_dt, a.s_dt, a.dt_eps = d["w_dt"].data_ptr(), d["s_dt"].data_ptr(), cfg.norm_eps
+                if cfg.fp_proj == 2:
+                    a.delta, a.ld_delta = self.dl.data_ptr(), cfg.d_inner
+                else:
+                    a.dt_in, a.ld_dt_in, a.dt_rank = self.p.data_ptr(), PW, R
+                    a.w_dt, a.s_dt, a.dt_eps = d["w_dt"].data_ptr(), d["s_dt"].data_ptr(), cfg.norm_eps
                 if cfg.gated:
                     a.gate, a.ld_gate = self.xz.data_ptr() + cfg.d_inner * es, XW
                 st.append(("scan", a))
-                st.append(("bitlinear_out", bl(self.y.data_ptr(), cfg.d_inner, cfg.d_inner, d["w_out"], d["s_out"],
-                                               cfg.d_model, dst.data_ptr(), cfg.d_model, src.data_ptr())))
+                st.append(proj("out", self.y.data_ptr(), cfg.d_inner, cfg.d_inner, d, cfg.d_model, dst.data_ptr(),
+                               cfg.d_model, src.data_ptr()))
             else:
                 H, P, N = cfg.nheads, cfg.headdim, cfg.d_state
-                st.append(("bitlinear_in", bl(src.data_ptr(), cfg.d_model, cfg.d_model, d["w_in"], d["s_in"], VW,
-                                              self.v.data_ptr(), VW, None)))
+                st.append(proj("in", src.data_ptr(), cfg.d_model, cfg.d_model, d, VW, self.v.data_ptr(), VW, None))
                 base = self.v.data_ptr()
                 xb, ldb = base, VW
                 if cfg.gated:
@@ -220,8 +239,8 @@ class StagePlan:
                 a.A, a.D = d["A"].data_ptr(), d["D"].data_ptr()
                 a.y, a.ld_y = self.y.data_ptr(), cfg.d_inner
                 st.append(("scan", a))
-                st.append(("bitlinear_out", bl(self.y.data_ptr(), cfg.d_inner, cfg.d_inner, d["w_out"], d["s_out"],
-                                               cfg.d_model, dst.data_ptr(), cfg.d_model, src.data_ptr())))
+                st.append(proj("out", self.y.data_ptr(), cfg.d_inner, cfg.d_inner, d, cfg.d_model, dst.data_ptr(),
+                               cfg.d_model, src.data_ptr()))
             self.stages.append(st)
         self.scan_ws_bytes = max(1, L.ssm_selective_scan_workspace_bytes(ctypes.byref(self.stages[0][-2][1])))
         self.scan_ws = torch.empty(self.scan_ws_bytes, dtype=torch.uint8, device=dev)
@@ -238,6 +257,8 @@ class StagePlan:
                                                   stream_handle)
                 elif name == "conv":
                     rc = L.ssm_conv1d_silu_fwd(*a, stream_handle)
+                elif name.startswith("dense"):
+                    rc = L.ssm_dense_fwd(*a, stream_handle)
                 else:
                     rc = L.ssm_bitlinear_fwd(ctypes.byref(a), self.bl_ws.data_ptr(), self.prob.ws_bytes,
                                              stream_handle)
@@ -254,6 +275,10 @@ def stage_cost(cfg: wl.MixerConfig, name: str) -> dict:
     M = cfg.tokens
     es = 2 if cfg.act_dtype == "bf16" else 4
     shapes = cfg.proj_shapes
+    if name.startswith("dense"):  # full-precision projection: dense weights in the act dtype
+        n, k = shapes[name.split("_")[1]]
+        byts = M * (k + n) * es + n * k * es + (M * n * es if name == "dense_out" else 0)
+        return {"bytes": byts, "ops": 2 * M * n * k, "ops_unit": "bf16-FLOP" if es == 2 else "fp32-FLOP"}
     if name.startswith("bitlinear"):
         n, k = shapes[name.split("_")[1]]
         wbytes = n * 4 * ((k + 15) // 16)
@@ -365,13 +390,17 @@ def cpu_baseline(cfg: wl.MixerConfig, seed: int, target_s: float) -> dict:
     for lw in lat:
         w = {k: lw[k] for k in ("A", "D", "dt_bias", "conv_w", "conv_b") if k in lw}
         for name in cfg.proj_shapes:
+            if cfg.is_fp(name):
+                wv = lw["W_" + name]
+                w["f_" + name] = torch.from_numpy(wv).to(torch.bfloat16).float().numpy() if cfg.act_dtype == "bf16" else wv
+                continue
             c, s, _ = oracle.quantize_weights(lw["W_" + name], cfg.group_size)
             w["c_" + name], w["s_" + name] = c, s
         layers.append(w)
     oc = dict(kind=cfg.kind, d_model=cfg.d_model, d_inner=cfg.d_inner, d_state=cfg.d_state, dt_rank=cfg.dt_rank,
               nheads=cfg.nheads, headdim=cfg.headdim, group_size=cfg.group_size, act_bits=cfg.act_bits,
               act_dtype=oracle.BF16 if cfg.act_dtype == "bf16" else oracle.F32, norm_eps=cfg.norm_eps,
-              gated=cfg.gated, d_conv=cfg.d_conv)
+              gated=cfg.gated, d_conv=cfg.d_conv, fp_proj=cfg.fp_proj)
     # calibrate on one sequence, then run enough whole sequences (the whole batch repeated, when
     # one pass over it is shorter than the target) to fill the target time
     t0 = time.perf_counter()
@@ -517,6 +546,12 @@ def main():
         bound = "alu" if alu_t >= hbm_t else "hbm"
     elif dominant == "scan":
         kind, bound = "ssd", "hbm"
+    elif dominant == "conv":
+        kind, bound = "conv", "hbm"
+    elif dominant.startswith("dense"):  # full-precision projection on rocBLAS (fp32 or bf16 matrix cores)
+        kind = "dense"
+        pk = FP32_MATRIX_PEAK_TFLOPS if cfg.act_dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
+        bound = "mfma" if cost["ops"] / cost["bytes"] >= pk * 1e12 / (HBM_PEAK_GBPS * 1e9) else "hbm"
     else:
         kind = "bitlinear"
         ai = cost["ops"] / cost["bytes"]
@@ -526,7 +561,10 @@ def main():
         roof = {"bound": "alu", "achieved": cost["ops"] / avg_s / 1e12, "peak": FP32_VECTOR_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     elif bound == "mfma":
-        pk = INT8_MFMA_PEAK_TOPS if cfg.act_bits == 8 else BF16_MFMA_PEAK_TFLOPS
+        if kind == "dense":
+            pk = FP32_MATRIX_PEAK_TFLOPS if cfg.act_dtype == "f32" else BF16_MFMA_PEAK_TFLOPS
+        else:
+            pk = INT8_MFMA_PEAK_TOPS if cfg.act_bits == 8 else BF16_MFMA_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": cost["ops"] / avg_s / 1e12, "peak": pk, "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": cost["bytes"] / avg_s / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
@@ -572,6 +610,7 @@ def main():
                    "contraction": "int8 x ternary -> int32 (MFMA)" if cfg.act_bits == 8 else
                    "bf16 x ternary -> fp32 (MFMA)", "scan_state": "fp32", "gated": cfg.gated, "d_conv": cfg.d_conv},
         "timing": {k: v for k, v in result.items() if k != "ms_per_step"},
+        "weight_bytes": sum(t.numel() * t.element_size() for d in prob.layers for t in d.values()),
         "stages": stages,
         "stage_ms_per_step": stage_total_ms,
         "layer": layer,

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef enum {
   SSM_OK = 0,
@@ -243,6 +243,12 @@ ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* workspace, size_
  *  SSM input channels (x; for SSD x, B and C) first go through ssm_conv1d_silu_fwd of
  *  width d_conv with weights conv_w [channels, d_conv] and bias conv_b (nullable), and
  *  the scan output is multiplied by SiLU(zg) before out_proj (the scan's gate).
+ *  Full-precision projections (fp_proj; the TriSSM model keeps in_proj and out_proj in full
+ *  precision and makes only Delta, B, C ternary, and compares with an fp_ssm baseline):
+ *  fp_proj = 1: in_proj and out_proj are ssm_dense_fwd with fw_in / fw_out; fp_proj = 2:
+ *  every projection is (for the Mamba-1 kind the dt projection output is then stored in
+ *  act_dtype and read by the scan).  The SSD kind has only in_proj and out_proj, so 1 and 2
+ *  mean the same there.
  * u and out have row stride d_model; out may equal u (in place) only when
  * add_residual != 0.  workspace: ssm_mixer_workspace_bytes() bytes of device memory.
  * Requirements: those of the BitLinear and scan calls above; Mamba-1 kind needs
@@ -259,6 +265,8 @@ typedef struct {
   float norm_eps;
   int32_t gated;     /* 0: the mixer alone; 1: the gated block (convolution + SiLU gate) */
   int32_t d_conv;    /* width of the block's convolution, 1 .. 8 when gated, else 0 */
+  int32_t fp_proj;   /* 0 all projections ternary; 1 in/out full precision; 2 all full precision */
+  int32_t pad0;
 } ssm_mixer_config;
 
 typedef struct {
@@ -267,6 +275,8 @@ typedef struct {
   const float *g_in, *g_x, *g_dt, *g_out;   /* RMSNorm gains or NULL */
   const float *dt_bias, *A, *D;
   const float *conv_w, *conv_b;             /* gated block: [channels, d_conv], [channels] or NULL */
+  const void *fw_in, *fw_x, *fw_dt, *fw_out; /* full-precision weights [n_out, k] in act_dtype
+                                                (used where fp_proj asks for them) */
 } ssm_mixer_weights;
 
 size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64_t seqlen);
@@ -312,6 +322,21 @@ ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w,
  * Errors: SSM_ERR_DTYPE, SSM_ERR_SHAPE (sizes, strides, width, out == x), SSM_ERR_NULL,
  * SSM_ERR_DEVICE.
  */
+/*
+ * ssm_dense_fwd -- a full-precision linear layer, y = x W^T (+ residual): the in and out
+ * projections of the TriSSM model, and every projection of its fp_ssm baseline (TriSSM
+ * README).  No RMSNorm, no quantisation, no bias.  A plain dense GEMM, delegated to rocBLAS
+ * (fp32; or bf16 operands with fp32 accumulation and a bf16 result).
+ *  x: [m, ldx] of dtype (first k columns);  w: [n, k] of dtype, row-major;
+ *  residual: [m, ld_res] of dtype or NULL (may equal y);  y: [m, ldy] of dtype, not x.
+ * The first call on a device creates that device's rocBLAS handle (rocBLAS then sets up its
+ * own workspace); nothing else is allocated.  Asynchronous on stream.
+ * Errors: SSM_ERR_DTYPE, SSM_ERR_SHAPE (sizes, strides, sizes of 2^31 or more, y == x),
+ * SSM_ERR_NULL, SSM_ERR_DEVICE.
+ */
+ssm_status ssm_dense_fwd(const void* x, int32_t dtype, int64_t m, int64_t k, int64_t ldx, const void* w, int64_t n,
+                         const void* residual, int64_t ld_res, void* y, int64_t ldy, hipStream_t stream);
+
 ssm_status ssm_conv1d_silu_fwd(const void* x, int32_t dtype, int64_t batch, int64_t seqlen, int64_t channels,
                                int64_t ldx, const float* w, int32_t width, const float* bias,
                                const float* state_in, float* state_out, void* out, int64_t ldo,

@@ -46,12 +46,13 @@ class ScanArgs(ctypes.Structure):
 class MixerConfig(ctypes.Structure):
     _fields_ = [("kind", _i32), ("act_bits", _i32), ("d_model", _i64), ("d_inner", _i64), ("d_state", _i64),
                 ("dt_rank", _i64), ("nheads", _i64), ("headdim", _i64), ("group_size", _i64), ("act_dtype", _i32),
-                ("norm_eps", ctypes.c_float), ("gated", _i32), ("d_conv", _i32)]
+                ("norm_eps", ctypes.c_float), ("gated", _i32), ("d_conv", _i32), ("fp_proj", _i32), ("pad0", _i32)]
 
 
 class MixerWeights(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("w_in", "w_x", "w_dt", "w_out", "s_in", "s_x", "s_dt", "s_out", "g_in", "g_x",
-                                   "g_dt", "g_out", "dt_bias", "A", "D", "conv_w", "conv_b")]
+                                   "g_dt", "g_out", "dt_bias", "A", "D", "conv_w", "conv_b", "fw_in", "fw_x",
+                                   "fw_dt", "fw_out")]
 
 
 class SsmError(RuntimeError):
@@ -65,7 +66,7 @@ EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed
            "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
            "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front", "ssm_mixer_step",
-           "ssm_conv1d_silu_fwd"]
+           "ssm_conv1d_silu_fwd", "ssm_dense_fwd"]
 
 
 def lib():
@@ -102,6 +103,8 @@ def lib():
                                      _vp, _vp, ctypes.c_int32, _vp, _sz, _vp]
         L.ssm_conv1d_silu_fwd.argtypes = [_vp, _i32, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp]
         L.ssm_conv1d_silu_fwd.restype = ctypes.c_int
+        L.ssm_dense_fwd.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+        L.ssm_dense_fwd.restype = ctypes.c_int
         L.ssm_mixer_step.restype = ctypes.c_int
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
@@ -259,9 +262,9 @@ def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch
 
 def mixer_config(kind: int, d_model: int, d_inner: int, d_state: int, *, dt_rank: int = 0, nheads: int = 0,
                  headdim: int = 0, act_bits: int = 8, group_size: int = 0, act_dtype: torch.dtype = torch.float32,
-                 norm_eps: float = 1e-5, gated: int = 0, d_conv: int = 0) -> MixerConfig:
+                 norm_eps: float = 1e-5, gated: int = 0, d_conv: int = 0, fp_proj: int = 0) -> MixerConfig:
     c = MixerConfig()
-    c.gated, c.d_conv = gated, d_conv
+    c.gated, c.d_conv, c.fp_proj = gated, d_conv, fp_proj
     c.kind, c.act_bits = kind, act_bits
     c.d_model, c.d_inner, c.d_state, c.dt_rank = d_model, d_inner, d_state, dt_rank
     c.nheads, c.headdim, c.group_size = nheads, headdim, group_size
@@ -323,6 +326,20 @@ def ssm_mixer_step(cfg: MixerConfig, weights, u: torch.Tensor, state: torch.Tens
     ws = _workspace(nb, u.device, workspace)
     _check(L.ssm_mixer_step(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, _p(state), _p(conv_state),
                             int(add_residual), _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def ssm_dense_fwd(x: torch.Tensor, w: torch.Tensor, residual: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None, stream=None):
+    """Full-precision linear layer y = x W^T (+ residual); x [m, k] or [B, L, k] (contiguous last
+    dim, even row strides), w [n, k] of x's dtype (fp32 or bf16)."""
+    m, ldx = _rows(x, "x")
+    n, k = w.shape
+    if out is None:
+        out = torch.empty((*x.shape[:-1], n), dtype=x.dtype, device=x.device)
+    ld_res = _rows(residual, "residual")[1] if residual is not None else 0
+    _check(lib().ssm_dense_fwd(_p(x), _DTYPES[x.dtype], m, k, ldx, _p(w.contiguous()), n, _p(residual), ld_res,
+                               _p(out), _rows(out, "out")[1], _stream(stream)))
     return out
 
 

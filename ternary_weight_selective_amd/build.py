@@ -12,7 +12,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libssm_ternary.so")
 
-SOURCES = ["quant.hip", "norm.hip", "bitlinear.hip", "front.hip", "conv.hip", "scan.hip", "ssd.hip", "api.cpp"]
+SOURCES = ["quant.hip", "norm.hip", "bitlinear.hip", "front.hip", "conv.hip", "scan.hip", "ssd.hip", "dense.cpp",
+           "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -40,7 +41,8 @@ def build_library() -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp, "-L/opt/rocm/lib", "-lrocblas",
+           "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

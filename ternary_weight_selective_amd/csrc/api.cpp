@@ -209,7 +209,7 @@ struct MixPlan {
   int64_t XW = 0;   // Mamba-1: in_proj width (d_inner, or 2 d_inner with the gate branch)
   int64_t VW0 = 0;  // SSD: [x | B | C | dt] width; VW adds the gate branch
   int64_t Cc = 0;   // channels through the convolution of the gated block
-  size_t off_am = 0, off_x = 0, off_xc = 0, off_p = 0, off_y = 0, off_scan = 0, total = 0;
+  size_t off_am = 0, off_x = 0, off_xc = 0, off_p = 0, off_dl = 0, off_y = 0, off_scan = 0, total = 0;
 };
 
 ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, MixPlan* p) {
@@ -224,6 +224,7 @@ ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, Mi
   if (c->gated != 0 && c->gated != 1) return fail(SSM_ERR_SHAPE, "mixer: gated must be 0 or 1");
   if (c->gated ? (c->d_conv < 1 || c->d_conv > kConvMaxK) : c->d_conv != 0)
     return fail(SSM_ERR_SHAPE, "mixer: d_conv %d (1 .. %d with gated = 1, else 0)", (int)c->d_conv, kConvMaxK);
+  if (c->fp_proj < 0 || c->fp_proj > 2) return fail(SSM_ERR_SHAPE, "mixer: fp_proj must be 0, 1 or 2");
   p->M = batch * seqlen;
   p->Kp = round_up(c->d_model > c->d_inner ? c->d_model : c->d_inner, 64);
   const size_t as = act_size(c->act_dtype);
@@ -243,6 +244,7 @@ ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, Mi
     p->off_x = off; off = align_up(off + (size_t)p->M * p->XW * as);
     if (c->gated) { p->off_xc = off; off = align_up(off + (size_t)p->M * c->d_inner * as); }
     p->off_p = off; off = align_up(off + (size_t)p->M * p->PW * as);
+    if (c->fp_proj == 2) { p->off_dl = off; off = align_up(off + (size_t)p->M * c->d_inner * as); }  // stored dt
     p->off_y = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
     p->off_scan = off;
   } else if (c->kind == SSM_MIXER_SSD) {
@@ -365,7 +367,7 @@ size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64
     return p.total + align_up(scan_ssd_workspace(s));
   }
   s.H = c->d_inner; s.P = 1;
-  s.R = (int)c->dt_rank;  // dt_proj runs inside the scan: room for the dt input's codes
+  s.R = c->fp_proj == 2 ? 0 : (int)c->dt_rank;  // a ternary dt_proj runs inside the scan: its input's codes
   return p.total + align_up(scan_m1_workspace(s));
 }
 
@@ -374,7 +376,7 @@ int32_t ssm_mixer_fuses_front(const ssm_mixer_config* c) {
   MixPlan p;
   const ssm_status st = mix_plan(c, 1, 1, &p);
   g_err = keep;
-  if (st != SSM_OK || c->kind != SSM_MIXER_MAMBA1 || c->gated) return 0;
+  if (st != SSM_OK || c->kind != SSM_MIXER_MAMBA1 || c->gated || c->fp_proj) return 0;
   return front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank) ? 1 : 0;
 }
 
@@ -422,6 +424,23 @@ ssm_status ssm_conv1d_silu_fwd(const void* x, int32_t dtype, int64_t batch, int6
   return dev(launch_conv_silu(a, stream), "conv");
 }
 
+ssm_status ssm_dense_fwd(const void* x, int32_t dtype, int64_t m, int64_t k, int64_t ldx, const void* w, int64_t n,
+                         const void* residual, int64_t ld_res, void* y, int64_t ldy, hipStream_t stream) {
+  g_err.clear();
+  if (!act_dtype_ok(dtype)) return fail(SSM_ERR_DTYPE, "dense: dtype %d", dtype);
+  const int64_t kMaxDim = 0x7fffffff;
+  if (m < 0 || k < 1 || n < 1 || m > kMaxDim || k > kMaxDim || n > kMaxDim)
+    return fail(SSM_ERR_SHAPE, "dense: m >= 0, k >= 1, n >= 1 (each below 2^31)");
+  if (ldx < k || ldy < n || (residual && ld_res < n) || ldx > kMaxDim || ldy > kMaxDim)
+    return fail(SSM_ERR_SHAPE, "dense: a row stride is smaller than its row");
+  if (m > 0 && (!x || !w || !y)) return fail(SSM_ERR_NULL, "dense: x, w and y are required");
+  if (m > 0 && x == y) return fail(SSM_ERR_SHAPE, "dense: y may not alias x");
+  DenseArgs d{};
+  d.M = m; d.N = n; d.K = k; d.bf16 = dtype == SSM_BF16;
+  d.x = x; d.ldx = ldx; d.W = w; d.residual = residual; d.ld_res = ld_res; d.y = y; d.ldy = ldy;
+  return dev(launch_dense(d, stream), "dense");
+}
+
 }  // extern "C"
 
 namespace {
@@ -431,10 +450,16 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
   MixPlan p;
   ssm_status st = mix_plan(c, batch, seqlen, &p);
   if (st != SSM_OK) return st;
-  if (!w || !w->w_in || !w->w_out || !w->s_in || !w->s_out || !w->A)
-    return fail(SSM_ERR_NULL, "mixer: w_in, w_out, s_in, s_out and A are required");
-  if (c->kind == SSM_MIXER_MAMBA1 && (!w->w_x || !w->w_dt || !w->s_x || !w->s_dt))
-    return fail(SSM_ERR_NULL, "mixer: w_x, w_dt, s_x and s_dt are required for the Mamba-1 kind");
+  // full-precision projections: in and out (fp_proj >= 1), x and dt too (fp_proj == 2)
+  const bool f_io = c->fp_proj >= 1, f_xdt = c->fp_proj == 2;
+  if (!w || !w->A) return fail(SSM_ERR_NULL, "mixer: weights and A are required");
+  if (f_io ? (!w->fw_in || !w->fw_out) : (!w->w_in || !w->w_out || !w->s_in || !w->s_out))
+    return fail(SSM_ERR_NULL, f_io ? "mixer: fw_in and fw_out are required (fp_proj >= 1)"
+                                   : "mixer: w_in, w_out, s_in and s_out are required");
+  if (c->kind == SSM_MIXER_MAMBA1 &&
+      (f_xdt ? (!w->fw_x || !w->fw_dt) : (!w->w_x || !w->w_dt || !w->s_x || !w->s_dt)))
+    return fail(SSM_ERR_NULL, f_xdt ? "mixer: fw_x and fw_dt are required (fp_proj == 2)"
+                                    : "mixer: w_x, w_dt, s_x and s_dt are required for the Mamba-1 kind");
   if (c->gated && !w->conv_w) return fail(SSM_ERR_NULL, "mixer: conv_w is required for the gated block");
   if (p.M > 0 && (!u || !out)) return fail(SSM_ERR_NULL, "mixer: u / out is NULL");
   if (out == u && !add_residual) return fail(SSM_ERR_SHAPE, "mixer: out may alias u only with add_residual");
@@ -463,6 +488,13 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     }
     return bl_run(&a, bp, base, stream);
   };
+  auto dense = [&](const void* x, int64_t k, int64_t ldx, const void* W, int64_t n, void* y, int64_t ldy,
+                   const void* r) -> ssm_status {
+    DenseArgs d{};
+    d.M = p.M; d.N = n; d.K = k; d.bf16 = c->act_dtype == SSM_BF16;
+    d.x = x; d.ldx = ldx; d.W = W; d.residual = r; d.ld_res = c->d_model; d.y = y; d.ldy = ldy;
+    return dev(launch_dense(d, stream), "mixer dense projection");
+  };
   // gated block: causal convolution + SiLU of the SSM input channels (Cc of them, row stride ld)
   auto conv = [&](const void* x, int64_t ld, void* xc) -> ssm_status {
     ConvArgs ca{};
@@ -480,7 +512,8 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     void* x = c->gated ? base + p.off_xc : xz;         // the SSM input
     void* pp = base + p.off_p;
     void* y = base + p.off_y;
-    const bool front = !c->gated && front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank);
+    const bool front = !c->gated && !c->fp_proj &&
+                       front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank);
     ssm_scan_args sa{};
     sa.batch = batch; sa.seqlen = seqlen; sa.nheads = c->d_inner; sa.headdim = 1; sa.d_state = c->d_state;
     sa.a_per_state = 1; sa.act_dtype = c->act_dtype;
@@ -492,8 +525,12 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     sa.D = w->D;
     sa.h0 = state; sa.h_last = state;
     sa.y = y; sa.ld_y = c->d_inner;
-    sa.dt_in = pp; sa.ld_dt_in = p.PW; sa.dt_rank = c->dt_rank;
-    sa.w_dt = w->w_dt; sa.s_dt = w->s_dt; sa.g_dt = w->g_dt; sa.dt_eps = c->norm_eps;
+    if (f_xdt) {  // full-precision dt projection, stored, then read by the scan
+      sa.delta = base + p.off_dl; sa.ld_delta = c->d_inner;
+    } else {      // ternary dt projection inside the scan
+      sa.dt_in = pp; sa.ld_dt_in = p.PW; sa.dt_rank = c->dt_rank;
+      sa.w_dt = w->w_dt; sa.s_dt = w->s_dt; sa.g_dt = w->g_dt; sa.dt_eps = c->norm_eps;
+    }
     if (c->gated) { sa.gate = (const char*)xz + c->d_inner * as; sa.ld_gate = p.XW; }
     st = scan_check(&sa);
     if (st != SSM_OK) return st;
@@ -515,23 +552,31 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
       if (st != SSM_OK) return st;
       sc.dt_codes_ready = 1;
     } else {
-      st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, p.XW, xz, p.XW, nullptr);
+      st = f_io ? dense(u, c->d_model, c->d_model, w->fw_in, p.XW, xz, p.XW, nullptr)
+                : bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, p.XW, xz, p.XW, nullptr);
       if (st != SSM_OK) return st;
       if (c->gated) {
         st = conv(xz, p.XW, x);
         if (st != SSM_OK) return st;
       }
-      st = bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
+      st = f_xdt ? dense(x, c->d_inner, c->d_inner, w->fw_x, p.PW, pp, p.PW, nullptr)
+                 : bitlinear(x, c->d_inner, c->d_inner, w->w_x, w->s_x, w->g_x, p.PW, pp, p.PW, nullptr);
       if (st != SSM_OK) return st;
+      if (f_xdt) {
+        st = dense(pp, c->dt_rank, p.PW, w->fw_dt, c->d_inner, base + p.off_dl, c->d_inner, nullptr);
+        if (st != SSM_OK) return st;
+      }
     }
     st = dev(launch_scan_m1(sc, base + p.off_scan, stream), "mixer scan");
     if (st != SSM_OK) return st;
-    return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
+    return f_io ? dense(y, c->d_inner, c->d_inner, w->fw_out, c->d_model, out, c->d_model, res)
+                : bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
   }
   // SSD kind: v = [x | B | C | dt (| zg)]; the gated block reads x, B and C from their convolution
   void* v = base + p.off_p;
   void* y = base + p.off_y;
-  st = bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, p.VW, v, p.VW, nullptr);
+  st = f_io ? dense(u, c->d_model, c->d_model, w->fw_in, p.VW, v, p.VW, nullptr)
+            : bitlinear(u, c->d_model, c->d_model, w->w_in, w->s_in, w->g_in, p.VW, v, p.VW, nullptr);
   if (st != SSM_OK) return st;
   const void* xbc = v;
   int64_t ld_xbc = p.VW;
@@ -555,7 +600,8 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
   if (c->gated) { s.gate = (const char*)v + p.VW0 * as; s.ld_gate = p.VW; }
   st = dev(launch_scan_ssd(s, base + p.off_scan, wsb - p.off_scan, stream), "mixer scan");
   if (st != SSM_OK) return st;
-  return bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
+  return f_io ? dense(y, c->d_inner, c->d_inner, w->fw_out, c->d_model, out, c->d_model, res)
+              : bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
 }
 
 }  // namespace

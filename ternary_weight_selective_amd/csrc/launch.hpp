@@ -102,6 +102,17 @@ struct ConvArgs {
 constexpr int kConvMaxK = 8;
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t s);
 
+// ---- full-precision linear layer (dense.cpp, rocBLAS): y[M, N] = x[M, K] W[N, K]^T (+ residual)
+struct DenseArgs {
+  int64_t M, N, K;
+  int bf16;                      // activations and weights bf16 (else fp32)
+  const void* x; int64_t ldx;
+  const void* W;                 // [N, K] row-major
+  const void* residual; int64_t ld_res;  // nullable; may equal y
+  void* y; int64_t ldy;
+};
+hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
+
 // ---- Mamba-1 mixer front (front.hip): x = BitLinear(u; W_in), p = BitLinear(x; W_x) and the
 // dt input's int8 codes in one kernel (A8, one scale per tensor)
 struct FrontArgs {

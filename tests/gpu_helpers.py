@@ -44,6 +44,11 @@ def quantize_layer(cfg, lat, check: bool = True):
     gw, ow = {}, {}
     for name in cfg.proj_shapes:
         w = lat["W_" + name]
+        if cfg.is_fp(name):  # full-precision projection: the weights as stored in the act dtype
+            wv = bf16_values(w) if cfg.act_dtype == "bf16" else w
+            gw["fw_" + name] = to_dev(wv, torch_dtype(cfg))
+            ow["f_" + name] = wv
+            continue
         packed, scale, zc = tws.ssm_ternary_quantize_weights(to_dev(w), cfg.group_size)
         codes, oscale, ozeros = oracle.quantize_weights(w, cfg.group_size)
         if check:
@@ -63,14 +68,14 @@ def gpu_config(cfg):
     return tws.mixer_config(cfg.kind, cfg.d_model, cfg.d_inner, cfg.d_state, dt_rank=cfg.dt_rank,
                             nheads=cfg.nheads, headdim=cfg.headdim, act_bits=cfg.act_bits,
                             group_size=cfg.group_size, act_dtype=torch_dtype(cfg), norm_eps=cfg.norm_eps,
-                            gated=cfg.gated, d_conv=cfg.d_conv)
+                            gated=cfg.gated, d_conv=cfg.d_conv, fp_proj=cfg.fp_proj)
 
 
 def oracle_config(cfg):
     return dict(kind=cfg.kind, d_model=cfg.d_model, d_inner=cfg.d_inner, d_state=cfg.d_state, dt_rank=cfg.dt_rank,
                 nheads=cfg.nheads, headdim=cfg.headdim, group_size=cfg.group_size, act_bits=cfg.act_bits,
                 act_dtype=oracle.BF16 if cfg.act_dtype == "bf16" else oracle.F32, norm_eps=cfg.norm_eps,
-                gated=cfg.gated, d_conv=cfg.d_conv)
+                gated=cfg.gated, d_conv=cfg.d_conv, fp_proj=cfg.fp_proj)
 
 
 def run_gpu_stack(cfg, gws, u_host, workspace=None):

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = tws.lib()
-    assert tws.ssm_abi_version() == 2
+    assert tws.ssm_abi_version() == 3
     for s in range(8):
         assert L.ssm_status_string(s)
     assert tws.ssm_packed_row_bytes(8) == 4
@@ -216,6 +216,45 @@ def test_mixer_gated_needs_conv_weights_and_room():
     # the gate branch and the convolved copy need room beyond the plain mixer's workspace
     assert L.ssm_mixer_workspace_bytes(ctypes.byref(gated), 2, 64) > L.ssm_mixer_workspace_bytes(ctypes.byref(plain), 2, 64)
     assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 256, 512, 16, dt_rank=16, gated=1, d_conv=4))) == 0
+
+
+def test_dense_rejects():
+    L = tws.lib()
+    d = L.ssm_dense_fwd
+    assert d(FAKE, 7, 4, 16, 16, FAKE, 8, None, 0, FAKE + 4096, 8, None) == DTYPE
+    assert d(FAKE, 0, 4, 0, 16, FAKE, 8, None, 0, FAKE + 4096, 8, None) == SHAPE
+    assert d(FAKE, 0, 4, 16, 8, FAKE, 8, None, 0, FAKE + 4096, 8, None) == SHAPE
+    assert d(FAKE, 0, 4, 16, 16, FAKE, 8, None, 0, FAKE + 4096, 4, None) == SHAPE
+    assert d(FAKE, 0, 4, 16, 16, FAKE, 8, FAKE + 8192, 4, FAKE + 4096, 8, None) == SHAPE
+    assert d(FAKE, 0, 1 << 31, 16, 16, FAKE, 8, None, 0, FAKE + 4096, 8, None) == SHAPE
+    assert d(FAKE, 0, 4, 16, 16, None, 8, None, 0, FAKE + 4096, 8, None) == NULL
+    assert d(FAKE, 0, 4, 16, 16, FAKE, 8, None, 0, FAKE, 16, None) == SHAPE
+
+
+def test_mixer_fp_proj_rejects():
+    L = tws.lib()
+    w = tws.MixerWeights()
+    for name, _ in tws.MixerWeights._fields_:
+        setattr(w, name, FAKE)
+    bad = tws.mixer_config(0, 64, 128, 16, dt_rank=8, fp_proj=3)
+    assert L.ssm_mixer_fwd(ctypes.byref(bad), ctypes.byref(w), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 1 << 30,
+                           None) == SHAPE
+    for mode, missing in ((1, "fw_in"), (1, "fw_out"), (2, "fw_x"), (2, "fw_dt")):
+        w2 = tws.MixerWeights()
+        for name, _ in tws.MixerWeights._fields_:
+            setattr(w2, name, FAKE)
+        setattr(w2, missing, None)
+        c = tws.mixer_config(0, 64, 128, 16, dt_rank=8, fp_proj=mode)
+        assert L.ssm_mixer_fwd(ctypes.byref(c), ctypes.byref(w2), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 1 << 30,
+                               None) == NULL, (mode, missing)
+    # ternary weights are not needed where the projections are full precision
+    w3 = tws.MixerWeights()
+    for name in ("fw_in", "fw_out", "fw_x", "fw_dt", "A"):
+        setattr(w3, name, FAKE)
+    c = tws.mixer_config(0, 64, 128, 16, dt_rank=8, fp_proj=2)
+    assert L.ssm_mixer_fwd(ctypes.byref(c), ctypes.byref(w3), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 16,
+                           None) == WORKSPACE
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 256, 512, 16, dt_rank=16, fp_proj=1))) == 0
 
 
 def test_conv_rejects():

@@ -345,6 +345,7 @@ def test_mixer_ssd_small_fp32():
     ("mamba2_ssd", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=7,
                         layers=1)),
     ("trissm_gated", dict(batch=2, seqlen=19, layers=1)),
+    ("trissm_fp", dict(batch=2, seqlen=19, layers=1)),                 # stored dt
     ("mamba2_ssd_gated", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=7,
                               layers=1)),
 ])
@@ -384,6 +385,7 @@ def _decode(cfg, gw, u_host):
 
 DECODE_CASES = [
     ("bitssm_tiny", {}, 42),
+    ("trissm_fp_inout", dict(batch=2, seqlen=12, layers=1), 14),
     ("trissm_gated", dict(batch=3, seqlen=20, layers=1), 12),
     ("mamba2_ssd_gated", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=14,
                               layers=1), 13),
@@ -530,3 +532,60 @@ def test_mixer_trissm_gated_stack_sampled():
 def test_mixer_mamba2_ssd_gated_sampled():
     per_layer, drift = _stack_sampled("mamba2_ssd_gated", [1])
     assert max(per_layer) <= TOL["bf16"], per_layer
+
+
+# ------------------------------------------------------------------ full-precision projections
+
+DENSE_CASES = [  # (m, k, n, dtype, residual, ldx)
+    (100, 256, 512, "f32", False, 256),
+    (77, 512, 256, "f32", True, 600),
+    (64, 2048, 4416, "bf16", False, 2048),
+    (33, 4096, 2048, "bf16", True, 4096),
+    (1, 16, 512, "f32", False, 48),
+]
+
+
+@pytest.mark.parametrize("m,k,n,dt,res,ldx", DENSE_CASES)
+def test_dense_parity(m, k, n, dt, res, ldx):
+    """Full-precision linear layer (rocBLAS) against the oracle's fp64 x W^T."""
+    g = wl.rng(m + k + n)
+    x = wl.normal(g, (m, ldx))
+    W = wl.normal(g, (n, k), 0.0, 1.0 / np.sqrt(k))
+    r = wl.normal(g, (m, n)) if res else None
+    if dt == "bf16":
+        x, W = bf16_values(x), bf16_values(W)
+        r = bf16_values(r) if res else None
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    xd = to_dev(x, tdt)
+    y = tws.ssm_dense_fwd(xd[:, :k], to_dev(W, tdt), residual=to_dev(r, tdt) if res else None)
+    ref = oracle.dense(x, W, k=k) + (r if res else 0.0)
+    assert rel_err(host(y), ref) <= (4e-3 if dt == "bf16" else 1e-6)
+
+
+FP_MIXER_CASES = [
+    ("trissm_fp_inout", dict(batch=2, seqlen=40, layers=1), 51),
+    ("trissm_fp", dict(batch=2, seqlen=40, layers=1), 52),
+    ("trissm_fp", dict(batch=1, seqlen=33, layers=1, act_dtype="bf16"), 53),
+    ("mamba2_ssd_fp", dict(d_model=256, d_inner=512, d_state=128, nheads=8, headdim=64, batch=2, seqlen=130,
+                           layers=1), 54),
+]
+
+
+@pytest.mark.parametrize("name,over,seed", FP_MIXER_CASES)
+def test_mixer_fp_proj_parity(name, over, seed):
+    """Full-precision projections (TriSSM's in/out split; the fp_ssm baseline): the mixer output
+    alone (no residual, which would dominate) against the oracle, then with the residual in place."""
+    cfg = wl.CONFIGS[name].with_(**over)
+    lat, u = wl.mixer_problem(cfg, seed=seed, layers=1)
+    if cfg.act_dtype == "bf16":
+        u = bf16_values(u)
+    gw, ow = quantize_layer(cfg, lat[0])
+    c = gpu_config(cfg)
+    tol = TOL["bf16"] if cfg.act_dtype == "bf16" else TOL["f32"]
+    h = to_dev(u, torch_dtype(cfg))
+    out = tws.ssm_mixer_fwd(c, tws.mixer_weights(gw), h, add_residual=False)
+    ref = oracle.mixer(oracle_config(cfg), ow, u, residual=False)
+    assert rel_err(host(out), ref) <= tol
+    out2 = tws.ssm_mixer_fwd(c, tws.mixer_weights(gw), h, add_residual=True, out=h)
+    ref2 = oracle.mixer(oracle_config(cfg), ow, u, residual=True)
+    assert rel_err(host(out2), ref2) <= tol
