@@ -17,6 +17,7 @@ namespace {
 constexpr int BM = 64, BN = 64, BK = 64;
 constexpr int LDS_I8 = BK + 16;   // int8 row stride of the LDS tiles (bytes)
 constexpr int LDS_BF = BK + 8;    // bf16 row stride (elements)
+constexpr int kA16MaxGroups = 64;  // scale groups per row the large A16 tile stages in LDS
 
 template <typename Tout> struct Vec4;
 template <> struct Vec4<float> { typedef float4 type; };
@@ -658,6 +659,182 @@ __global__ __launch_bounds__(512) void k_bl_rows(GemmArgs g, RowArgs r) {
   }
 }
 
+// A16 large tile (one bf16 activation term): x̂ x ternary weights on bf16 MFMA 16x16x32.
+// Block tile 256 tokens x 128 outputs, 8 waves (two per SIMD) with 64 x 64 tiles of 4 x 4 MFMA
+// blocks; k steps of 64 double-buffered through LDS; each packed weight word is unpacked to
+// bf16 +-1 / 0 once per block.  The MFMA accumulators hold one scale group's partial sums; at
+// the group's end each is folded into an fp32 total with that group's scale (one FMA per
+// output, VALU work that overlaps the matrix cores), the block's scales staged in LDS.  With
+// one scale per tensor the accumulators run over all of k and are scaled once.
+template <typename Tout>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_a16_big(GemmArgs a) {
+  constexpr int NTH = 512;
+  constexpr int BMT = 256, BNT = 128, BKT = 64, AS = BKT + 8;  // AS: LDS row stride in bf16 elements
+  constexpr int WM = 64, WN = 64, NT = WN / 16, MT = WM / 16;
+  constexpr int CPT = BMT * BKT * 2 / 16 / NTH;  // 16-byte activation chunks per thread and k step
+  constexpr int WPT = BNT * (BKT / 16) / NTH;    // packed weight words per thread and k step
+  constexpr int NGP = kA16MaxGroups + 1;         // LDS row stride of the scales
+  __shared__ __align__(16) bf16_t s_a[2][BMT * AS];
+  __shared__ __align__(16) bf16_t s_w[2][BNT * AS];
+  __shared__ float s_sc[BNT * NGP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves
+  const int kq = lane >> 4, l16 = lane & 15;
+  const int64_t nb = cdiv(a.N, BNT), T = cdiv(a.M, BMT) * nb;
+  const int64_t chunk = cdiv(T, 8);
+  const int64_t li = blockIdx.x / 8, t = (blockIdx.x % 8) * chunk + li;  // an XCD walks consecutive tiles
+  if (li >= chunk || t >= T) return;
+  const int64_t m0 = (t / nb) * BMT, n0 = (t % nb) * BNT;
+  const bf16_t* A = (const bf16_t*)a.A;
+  const int ng = a.group ? (int)(a.K / a.group) : 1;
+  const int gsteps = a.group ? (int)(a.group / BKT) : (int)(a.Kp / BKT);  // k steps per scale group
+  for (int e = tid; e < BNT * ng; e += NTH) {
+    const int nl = e / ng, g = e % ng;
+    const int64_t n = n0 + nl;
+    s_sc[nl * NGP + g] = n < a.N ? (a.group ? a.w_scale[n * ng + g] : a.w_scale[0]) : 0.0f;
+  }
+  v4i pa[2][CPT];  // two k steps in flight in registers
+  uint32_t pw[2][WPT];
+  auto load = [&](int64_t k0, v4i (&pa)[CPT], uint32_t (&pw)[WPT]) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int e = tid + NTH * c, r = e >> 3, q = e & 7;
+      const int64_t gm = m0 + r;
+      pa[c] = gm < a.M ? *(const v4i*)(A + gm * a.lda + k0 + q * 8) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int c = 0; c < WPT; ++c) {
+      const int e = tid + NTH * c, r = e >> 2, q = e & 3;
+      const int64_t gn = n0 + r, kw = k0 / 16 + q;
+      pw[c] = (gn < a.N && kw < a.w_row_words) ? a.W[gn * a.w_row_words + kw] : 0u;
+    }
+  };
+  auto store = [&](int buf, const v4i (&pa)[CPT], const uint32_t (&pw)[WPT]) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int e = tid + NTH * c, r = e >> 3, q = e & 7;
+      *(v4i*)(&s_a[buf][r * AS + q * 8]) = pa[c];
+    }
+#pragma unroll
+    for (int c = 0; c < WPT; ++c) {
+      const int e = tid + NTH * c, r = e >> 2, q = e & 3;
+      v4i o0, o1;
+      unpack16_bf16(pw[c], o0, o1);
+      v4i* dst = (v4i*)(&s_w[buf][r * AS + q * 16]);
+      dst[0] = o0;
+      dst[1] = o1;
+    }
+  };
+  v4f acc[MT][NT];
+  float tot[MT][NT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[i][j][q] = 0.0f;
+    }
+  const int nk = (int)(a.Kp / BKT);
+  // step ks: tile ks is in LDS buffer ks & 1 and tile ks + 1 in registers pa[(ks + 1) & 1];
+  // the step requests tile ks + 2 into pa[ks & 1], contracts tile ks, then moves tile ks + 1
+  // into the other buffer (read at step ks - 1, which ended with a barrier): each load has
+  // two steps of work to arrive
+  load(0, pa[0], pw[0]);
+  if (nk > 1) load(BKT, pa[1], pw[1]);
+  store(0, pa[0], pw[0]);
+  __syncthreads();
+  auto step = [&](int ks, v4i (&pn)[CPT], uint32_t (&wn_)[WPT], const v4i (&pc)[CPT], const uint32_t (&wc)[WPT]) {
+    const int buf = ks & 1;
+    if (ks + 2 < nk) load((int64_t)(ks + 2) * BKT, pn, wn_);
+    // fragments of both 32-deep halves of the k step: the second half's are read while the
+    // first half's MFMAs run
+    v8bf wf[2][NT], bfr[2][MT];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        wf[h][j] = __builtin_bit_cast(v8bf, *(const v4i*)(&s_w[buf][(wn * WN + j * 16 + l16) * AS + h * 32 + kq * 8]));
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        bfr[h][i] = __builtin_bit_cast(v8bf, *(const v4i*)(&s_a[buf][(wm * WM + i * 16 + l16) * AS + h * 32 + kq * 8]));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[h][j], bfr[h][i], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NT + MT, 0);  // first half's LDS reads
+#pragma unroll
+    for (int r = 0; r < NT + MT; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // two MFMAs of the first half
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one read of the second half
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MT * NT, 0);  // second half's MFMAs
+    if ((ks + 1) % gsteps == 0) {  // end of a scale group: fold its partials with the group's scale
+      const int g = a.group ? ks / gsteps : 0;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sc = s_sc[(wn * WN + j * 16 + kq * 4 + q) * NGP + g];
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            tot[i][j][q] = __builtin_fmaf(acc[i][j][q], sc, tot[i][j][q]);
+            acc[i][j][q] = 0.0f;
+          }
+        }
+    }
+    if (ks + 1 < nk) store(buf ^ 1, pc, wc);
+    __syncthreads();
+  };
+  for (int ks = 0; ks < nk; ks += 2) {
+    step(ks, pa[0], pw[0], pa[1], pw[1]);
+    if (ks + 1 < nk) step(ks + 1, pa[1], pw[1], pa[0], pw[0]);
+  }
+
+  // epilogue: lane holds token l16 of each token tile and outputs 4 kq .. 4 kq + 3 of each
+  // output tile
+  const int vb = (int)sizeof(typename Vec4<Tout>::type);
+  const bool vec_ok = (a.ldy % 4 == 0) && (((uintptr_t)a.y) % vb == 0) &&
+                      (!a.bias || ((uintptr_t)a.bias) % 16 == 0);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int64_t m = m0 + wm * WM + i * 16 + l16;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t n = n0 + wn * WN + j * 16 + kq * 4;
+      if (n >= a.N) continue;
+      float y[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) y[q] = tot[i][j][q];
+      if (vec_ok && n + 3 < a.N) {
+        if (a.bias) {
+          const float4 bb = *(const float4*)(a.bias + n);
+          y[0] += bb.x; y[1] += bb.y; y[2] += bb.z; y[3] += bb.w;
+        }
+        if (a.residual) {
+          const Tout* rp = (const Tout*)a.residual + m * a.ld_res + n;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] += ld_act(rp + q);
+        }
+        Tout o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) st_act(&o[q], y[q]);
+        *(typename Vec4<Tout>::type*)((Tout*)a.y + m * a.ldy + n) = *(const typename Vec4<Tout>::type*)o;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (n + q < a.N) store_out<Tout>(a, m, n + q, y[q]);
+      }
+    }
+  }
+}
+
 // Output-tile width of k_gemm_i8_big: 256 or 192, whichever leaves fewer padded columns.
 static int big_bn(int64_t N) { return (cdiv(N, 192) * 192 - N) < (cdiv(N, 256) * 256 - N) ? 192 : 256; }
 
@@ -694,6 +871,13 @@ hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (!a.A2 && (a.group == 0 || (a.group % 64 == 0 && a.K / a.group <= kA16MaxGroups))) {
+    const int64_t T = cdiv(a.M, 256) * cdiv(a.N, 128);
+    const dim3 grid((unsigned)(8 * cdiv(T, 8))), block(512);
+    if (a.y_bf16) hipLaunchKernelGGL((k_gemm_a16_big<bf16_t>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_gemm_a16_big<float>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)cdiv(a.N, BN), (unsigned)cdiv(a.M, BM)), block(256);
   if (a.y_bf16) {
     if (a.A2) hipLaunchKernelGGL((k_gemm_bf16<bf16_t, true>), grid, block, 0, s, a);

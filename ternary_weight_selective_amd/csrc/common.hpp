@@ -95,6 +95,25 @@ __device__ __forceinline__ v4i unpack16_i8(uint32_t w) {
   return r;
 }
 
+// 16 ternary codes of one packed word -> 16 bf16 (+1 = 0x3F80, -1 = 0xBF80, 0 = 0) in weight
+// order, two per dword: o0 holds weights 0..7, o1 weights 8..15.  For j = 0..3 the codes of
+// weights 4j..4j+3 are isolated one per byte (x); a byte permute spreads them into selectors
+// [c, c | 4, c', c' | 4], and a second one looks the selectors up in an 8-byte table whose
+// low half holds the bf16 low bytes (0x00, 0x80, -, 0x80) and high half the high bytes
+// (0x00, 0x3F, -, 0xBF), indexed by the code.
+__device__ __forceinline__ void unpack16_bf16(uint32_t w, v4i& o0, v4i& o1) {
+  uint32_t d[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t x = (w >> (2 * j)) & 0x03030303u;
+    const uint32_t x4 = x | 0x04040404u;
+    d[2 * j] = __builtin_amdgcn_perm(0xBF003F00u, 0x80008000u, __builtin_amdgcn_perm(x4, x, 0x05010400u));
+    d[2 * j + 1] = __builtin_amdgcn_perm(0xBF003F00u, 0x80008000u, __builtin_amdgcn_perm(x4, x, 0x07030602u));
+  }
+  o0 = v4i{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+  o1 = v4i{(int)d[4], (int)d[5], (int)d[6], (int)d[7]};
+}
+
 // Two int8 ternary values (low two bytes of b) -> two bf16 (+1 = 0x3F80, -1 = 0xBF80, 0 = 0).
 __device__ __forceinline__ uint32_t tern2_to_bf16x2(uint32_t b) {
   uint32_t lo = b & 0xFFu, hi = (b >> 8) & 0xFFu;
