@@ -356,3 +356,62 @@ def mixer_stack(cfg, layers: list, u) -> np.ndarray:
         out = mixer(cfg, wts, h, residual=True)
         h = out.astype(np.float32)
     return out
+
+
+# ---------------------------------------------------------------- O10: STE backward, one QAT step
+
+def bitlinear_bwd(x, codes, w_scale, dy, group: int = 0, norm_w=None, eps: float = 1e-5, w_latent=None) -> dict:
+    """Backward of the A8 BitLinear with straight-through estimators (TriSSM README: BitLinear
+    trained with straight-through estimators; the estimator of "Estimating or Propagating
+    Gradients Through Stochastic Neurons ...", cited under "Builds on"), fp64.
+
+    Forward being differentiated: x̂ = RMSNorm(x) g;  x̃ = q_x max(m, 1e-5) / 127 (the int8
+    codes of the forward, dequantised);  W̃ = s q_w (the ternary codes times their scale);
+    y = x̃ W̃^T.  The estimator passes gradients through both roundings unchanged (the absmax
+    and the scale are held fixed there), so
+      dx̂ = dy W̃,   dW = dy^T x̃  (the latent weights receive W̃'s gradient),
+      dx  = r g dx̂ - x (r^3 / k) sum_j g_j dx̂_j x_j   (RMSNorm, r = 1 / sqrt(mean x^2 + eps)).
+    Learnable scales (Ternary Mamba abstract: grouped QAT with learnable quantisation scales),
+    given the latent weights: with v = W / s, dW̃/ds is q - v where |v| <= 1 and q where the
+    clip is active (the step-size rule of learned-step-size quantisation), summed over each
+    scale's group:  ds = sum dW (q - v or q).
+    Returns dict(dx [m,k], dw [n,k], ds (scalar array or [n, k/group]) or None, x_tilde, r)."""
+    x = _f32(x)
+    m, k = x.shape
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    n = codes.shape[0]
+    dy = np.asarray(dy, dtype=np.float64)
+    _, xq, am, _ = bitlinear(x, codes, w_scale, group, 8, norm_w, eps)
+    r = np.array([rms_scale(x[i], eps) for i in range(m)], dtype=np.float32).astype(np.float64)
+    xt = xq.astype(np.float64) * (np.maximum(am, np.float32(1e-5)).astype(np.float64) / 127.0)[:, None]
+    sc = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
+    s_full = np.full((n, k), sc.ravel()[0]) if group == 0 else np.repeat(sc.reshape(n, k // group), group, axis=1)
+    wt = s_full * codes.astype(np.float64)
+    g = np.ones(k) if norm_w is None else np.asarray(norm_w, dtype=np.float32).astype(np.float64)
+    xd = x.astype(np.float64)
+    dxh = dy @ wt
+    dot = np.sum(g[None, :] * dxh * xd, axis=1)
+    dx = r[:, None] * (g[None, :] * dxh) - xd * (r ** 3 / k)[:, None] * dot[:, None]
+    dw = dy.T @ xt
+    ds = None
+    if w_latent is not None:
+        v = np.asarray(w_latent, dtype=np.float32).astype(np.float64) / s_full
+        fac = np.where(np.abs(v) <= 1.0, codes - v, codes.astype(np.float64))
+        gs = dw * fac
+        ds = np.array([gs.sum()]) if group == 0 else gs.reshape(n, k // group, group).sum(axis=2)
+    return dict(dx=dx, dw=dw, ds=ds, x_tilde=xt, r=r)
+
+
+def qat_step(w_latent, w_scale, dw, ds, lr: float, lr_scale: float, group: int = 0):
+    """One SGD step of quantisation-aware training on the latent weights and their learnable
+    scales (Ternary Mamba abstract), then the codes under the updated scales:
+      W <- W - lr dW,  s <- s - lr_scale ds  (each rounded once to fp32),
+      q = clamp(round(W / s), -1, 1).
+    Returns (W fp32, s fp32, codes int8, zero count) -- the zero count is the zero ratio the
+    abstract watches (it collapses when learnable scales grow)."""
+    W = (np.asarray(w_latent, np.float32).astype(np.float64) - np.float64(np.float32(lr)) * np.asarray(dw, np.float64))
+    W = W.astype(np.float32)
+    s = np.asarray(w_scale, np.float32).astype(np.float64) - np.float64(np.float32(lr_scale)) * np.asarray(ds, np.float64).reshape(np.shape(w_scale))
+    s = s.astype(np.float32)
+    codes, zeros = ternarize(W, group, s)
+    return W, s, codes, zeros

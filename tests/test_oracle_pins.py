@@ -827,3 +827,119 @@ def test_mixer_fp_all_dt_stored():
     ref = rb((o + uu).astype(np.float32)).astype(np.float64).reshape(out.shape)
     bad = np.abs(out - ref) > 2 ** -7 * np.abs(ref) + 1e-6
     assert bad.mean() < 1e-3, bad.mean()
+
+
+# ------------------------------------------------------------------ STE backward, QAT step
+
+def _fd_grad(f, x, h=1e-6):
+    """Central finite differences of a scalar function of an fp64 array."""
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        xp, xm = x.copy(), x.copy()
+        xp[i] += h
+        xm[i] -= h
+        g[i] = (f(xp) - f(xm)) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("gain", [False, True])
+def test_bwd_dx_is_rmsnorm_gradient(gain):
+    """The estimator passes dx̂ = dy W̃ through the activation quantiser unchanged, so dx is the
+    exact gradient of <dy, RMSNorm(x) g W̃^T> with W̃ held fixed: checked by finite differences."""
+    g = wl.rng(61)
+    m, k, n = 3, 16, 5
+    x = wl.normal(g, (m, k))
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    gn = (1.0 + 0.3 * wl.normal(g, (k,))).astype(np.float32) if gain else None
+    codes, s, _ = oracle.quantize_weights(w, 0)
+    dy = wl.normal(g, (m, n)).astype(np.float64)
+    out = oracle.bitlinear_bwd(x, codes, s, dy, norm_w=gn)
+    wt = float(s[0]) * codes.astype(np.float64)
+    gv = np.ones(k) if gn is None else gn.astype(np.float64)
+    eps = 1e-5
+
+    def f(xx):
+        r = 1.0 / np.sqrt(np.mean(xx * xx, axis=1, keepdims=True) + eps)
+        return float(np.sum(dy * ((xx * r * gv) @ wt.T)))
+
+    fd = _fd_grad(f, x.astype(np.float64))
+    # the oracle uses the forward's fp32 scale r, so agreement is to fp32 precision
+    np.testing.assert_allclose(out["dx"], fd, rtol=2e-5, atol=2e-6)
+
+
+def test_bwd_dw_and_dequantised_activations():
+    """dW is the gradient of the bilinear form <dy, x̃ W̃^T> in W̃ (finite differences), and
+    x̃ is the forward's int8 codes times max(m, 1e-5) / 127, within half a step of x̂."""
+    g = wl.rng(62)
+    m, k, n = 4, 8, 3
+    x = wl.normal(g, (m, k))
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    codes, s, _ = oracle.quantize_weights(w, 0)
+    dy = wl.normal(g, (m, n)).astype(np.float64)
+    out = oracle.bitlinear_bwd(x, codes, s, dy)
+    xt = out["x_tilde"]
+    fd = _fd_grad(lambda W: float(np.sum(dy * (xt @ W.T))), float(s[0]) * codes.astype(np.float64))
+    np.testing.assert_allclose(out["dw"], fd, rtol=1e-7, atol=1e-8)
+    _, xq, am, _ = oracle.bitlinear(x, codes, s)
+    step = np.maximum(am.astype(np.float64), 1e-5) / 127.0
+    np.testing.assert_allclose(xt, xq * step[:, None], rtol=0, atol=0)
+    xh = np.stack([oracle.norm_row(x[i]) for i in range(m)]).astype(np.float64)
+    assert np.all(np.abs(xt - xh) <= 0.5 * step[:, None] * (1 + 1e-6))
+
+
+def test_bwd_scale_gradient_by_hand():
+    """Step-size rule for one scale s = 0.5, latent W = (0.2, 0.7, -1.0, 0.05): v = W / s =
+    (0.4, 1.4, -2, 0.1), codes (0, 1, -1, 0); the clip is active at 1.4 and -2, so the factors
+    are (0 - 0.4, 1, -1, 0 - 0.1); with dW = (1, 2, 3, 4), ds = -0.4 + 2 - 3 - 0.4 = -1.8."""
+    w = np.array([[0.2, 0.7, -1.0, 0.05]], np.float32)
+    s = np.array([0.5], np.float32)
+    codes, _ = oracle.ternarize(w, 0, s)
+    np.testing.assert_array_equal(codes, [[0, 1, -1, 0]])
+    x = np.ones((1, 4), np.float32)
+    dw_target = np.array([[1.0, 2.0, 3.0, 4.0]])
+    # choose dy so that dW = dy^T x̃ equals dw_target: x̃ is all ones here (one token of ones)
+    out = oracle.bitlinear_bwd(x, codes, s, np.array([[1.0]]), w_latent=w)
+    xt = out["x_tilde"][0]
+    np.testing.assert_allclose(xt, np.ones(4), rtol=1e-4)  # RMSNorm of ones is 1 / sqrt(1 + eps)
+    v = w.astype(np.float64)[0] / 0.5
+    fac = np.where(np.abs(v) <= 1.0, codes[0] - v, codes[0])
+    assert np.allclose(fac, [-0.4, 1.0, -1.0, -0.1])
+    assert abs(float(np.sum(dw_target[0] * fac)) - (-1.8)) < 1e-6  # the weights are fp32 values
+    np.testing.assert_allclose(out["ds"], [np.sum(out["dw"][0] * fac)], rtol=1e-12)
+
+
+def test_bwd_grouped_scale_gradient_is_per_group():
+    """With groups, each scale sums only its own group's terms: the per-tensor result equals
+    the sum of the per-group results when every group has the same scale."""
+    g = wl.rng(63)
+    m, k, n, G = 5, 256, 4, 128
+    x = wl.normal(g, (m, k))
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    s0 = oracle.absmean(w, 0)
+    sg = np.full((n, k // G), s0[0], np.float32)
+    c0, _ = oracle.ternarize(w, 0, s0)
+    cg, _ = oracle.ternarize(w, G, sg)
+    np.testing.assert_array_equal(c0, cg)
+    dy = wl.normal(g, (m, n)).astype(np.float64)
+    a = oracle.bitlinear_bwd(x, c0, s0, dy, w_latent=w)
+    b = oracle.bitlinear_bwd(x, cg, sg, dy, group=G, w_latent=w)
+    np.testing.assert_allclose(b["dx"], a["dx"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(b["ds"].sum(), a["ds"][0], rtol=1e-10)
+
+
+def test_qat_step_zero_lr_and_zero_ratio():
+    """lr = 0 leaves weights, scales and codes as they were; raising a scale can only turn
+    codes into zeros (the zero ratio grows with the scale -- the collapse the Ternary Mamba
+    abstract reports for learnable scales)."""
+    g = wl.rng(64)
+    w = wl.normal(g, (16, 128), 0.0, 0.02)
+    codes, s, zeros = oracle.quantize_weights(w, 0)
+    W, s2, c2, z2 = oracle.qat_step(w, s, np.ones_like(w), np.ones(1), 0.0, 0.0)
+    np.testing.assert_array_equal(W, w)
+    np.testing.assert_array_equal(c2, codes)
+    assert z2 == zeros
+    _, _, c3, z3 = oracle.qat_step(w, s, np.zeros_like(w), np.array([-0.5 * float(s[0])]), 0.0, 1.0)
+    assert z3 > zeros
+    assert np.all((c3 == 0) | (c3 == codes))
