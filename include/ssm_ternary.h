@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 typedef enum {
   SSM_OK = 0,
@@ -322,6 +322,58 @@ ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w,
  * Errors: SSM_ERR_DTYPE, SSM_ERR_SHAPE (sizes, strides, width, out == x), SSM_ERR_NULL,
  * SSM_ERR_DEVICE.
  */
+/*
+ * ssm_bitlinear_bwd -- the backward pass of the A8 BitLinear with straight-through
+ * estimators (TriSSM README: BitLinear layers trained with straight-through estimators; the
+ * estimator of "Estimating or Propagating Gradients Through Stochastic Neurons ...", cited
+ * under "Builds on" of "Baseline Shape Decides the Verdict ...").  With x̂ = RMSNorm(x) g,
+ * x̃ = the forward's int8 codes times max(absmax, 1e-5) / 127, W̃ = scale * codes, the forward
+ * is y = x̃ W̃^T; the estimator passes gradients through both roundings (absmax and scale held
+ * fixed there):
+ *   dx̂ = dy W̃;  dx = r g dx̂ - x (r^3 / k) sum_j g_j dx̂_j x_j  (r = 1 / sqrt(mean x^2 + eps));
+ *   dW = dy^T x̃ (the gradient of the latent weights);
+ *   d_scale = sum over each scale's weights of dW (q - W/s) where |W/s| <= 1, dW q elsewhere
+ *   (learnable scales, Ternary Mamba abstract; the learned-step-size rule).
+ * All fp32 except x (act dtype).  The forward's codes are rebuilt from x exactly as the
+ * forward computes them.  The two contractions are dense fp32 GEMMs on rocBLAS.
+ *  x [m, ldx] (first k columns), norm_weight [k] or NULL, w_packed / w_scale / group_size as
+ *  ssm_ternary_quantize_weights wrote them, w_latent [n_out, k] (for d_scale), dy [m, ld_dy],
+ *  dx [m, ld_dx] (written), dw [n_out, k] or NULL, d_scale [1] or [n_out, k/group] or NULL.
+ *  workspace: ssm_bitlinear_bwd_workspace_bytes(), 256-byte aligned.
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_ALIGN, SSM_ERR_WORKSPACE,
+ * SSM_ERR_DEVICE.
+ */
+typedef struct {
+  const void* x; int32_t x_dtype; int32_t pad0;
+  int64_t m, k, ldx;
+  const float* norm_weight; float norm_eps; int32_t pad1;
+  const uint8_t* w_packed; const float* w_scale;
+  int64_t n_out, group_size;
+  const float* w_latent;
+  const float* dy; int64_t ld_dy;
+  float* dx; int64_t ld_dx;
+  float* dw;
+  float* d_scale;
+} ssm_bitlinear_bwd_args;
+
+size_t ssm_bitlinear_bwd_workspace_bytes(const ssm_bitlinear_bwd_args* a);
+ssm_status ssm_bitlinear_bwd(const ssm_bitlinear_bwd_args* a, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * ssm_qat_sgd_step -- one step of quantisation-aware training (Ternary Mamba abstract:
+ * grouped QAT with learnable quantisation scales): w_latent -= lr * dw and, when d_scale is
+ * given, w_scale -= lr_scale * d_scale (fp32 fused multiply-adds, in place); then the weights
+ * are ternarised under the updated scales (not their absmean) into w_packed, and zero_count
+ * (nullable, device int64) receives the number of zero codes -- the zero ratio that collapses
+ * when learnable scales grow.  Shapes as ssm_ternary_quantize_weights.  Asynchronous.
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_ALIGN, SSM_ERR_DEVICE.
+ */
+ssm_status ssm_qat_sgd_step(float* w_latent, float* w_scale, const float* dw, const float* d_scale,
+                            int64_t n_out, int64_t k, int64_t group_size, float lr, float lr_scale,
+                            uint8_t* w_packed, int64_t* zero_count, void* workspace, size_t ws_bytes,
+                            hipStream_t stream);
+
 /*
  * ssm_dense_fwd -- a full-precision linear layer, y = x W^T (+ residual): the in and out
  * projections of the TriSSM model, and every projection of its fp_ssm baseline (TriSSM

@@ -43,6 +43,13 @@ class ScanArgs(ctypes.Structure):
                 ("gate", _vp), ("ld_gate", _i64)]
 
 
+class BitlinearBwdArgs(ctypes.Structure):
+    _fields_ = [("x", _vp), ("x_dtype", _i32), ("pad0", _i32), ("m", _i64), ("k", _i64), ("ldx", _i64),
+                ("norm_weight", _vp), ("norm_eps", ctypes.c_float), ("pad1", _i32), ("w_packed", _vp),
+                ("w_scale", _vp), ("n_out", _i64), ("group_size", _i64), ("w_latent", _vp), ("dy", _vp),
+                ("ld_dy", _i64), ("dx", _vp), ("ld_dx", _i64), ("dw", _vp), ("d_scale", _vp)]
+
+
 class MixerConfig(ctypes.Structure):
     _fields_ = [("kind", _i32), ("act_bits", _i32), ("d_model", _i64), ("d_inner", _i64), ("d_state", _i64),
                 ("dt_rank", _i64), ("nheads", _i64), ("headdim", _i64), ("group_size", _i64), ("act_dtype", _i32),
@@ -66,7 +73,8 @@ EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed
            "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
            "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front", "ssm_mixer_step",
-           "ssm_conv1d_silu_fwd", "ssm_dense_fwd"]
+           "ssm_conv1d_silu_fwd", "ssm_dense_fwd", "ssm_bitlinear_bwd_workspace_bytes", "ssm_bitlinear_bwd",
+           "ssm_qat_sgd_step"]
 
 
 def lib():
@@ -105,6 +113,13 @@ def lib():
         L.ssm_conv1d_silu_fwd.restype = ctypes.c_int
         L.ssm_dense_fwd.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
         L.ssm_dense_fwd.restype = ctypes.c_int
+        L.ssm_bitlinear_bwd_workspace_bytes.argtypes = [ctypes.POINTER(BitlinearBwdArgs)]
+        L.ssm_bitlinear_bwd_workspace_bytes.restype = _sz
+        L.ssm_bitlinear_bwd.argtypes = [ctypes.POINTER(BitlinearBwdArgs), _vp, _sz, _vp]
+        L.ssm_bitlinear_bwd.restype = ctypes.c_int
+        L.ssm_qat_sgd_step.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float, _vp, _vp,
+                                       _vp, _sz, _vp]
+        L.ssm_qat_sgd_step.restype = ctypes.c_int
         L.ssm_mixer_step.restype = ctypes.c_int
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
@@ -327,6 +342,49 @@ def ssm_mixer_step(cfg: MixerConfig, weights, u: torch.Tensor, state: torch.Tens
     _check(L.ssm_mixer_step(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, _p(state), _p(conv_state),
                             int(add_residual), _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
     return out
+
+
+def ssm_bitlinear_bwd(x: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, n_out: int,
+                      dy: torch.Tensor, group_size: int = 0, norm_weight: torch.Tensor | None = None,
+                      norm_eps: float = 1e-5, w_latent: torch.Tensor | None = None, want_dw: bool = True,
+                      stream=None):
+    """Straight-through-estimator backward of the A8 BitLinear.  x [m, k] (fp32 / bf16, rows with
+    a contiguous last dim), dy [m, n_out] fp32.  Returns (dx fp32 [m, k], dw fp32 [n_out, k] or
+    None, d_scale fp32 or None -- d_scale when w_latent is given)."""
+    m, ldx = _rows(x, "x")
+    k = x.shape[-1]
+    if dy.dtype != torch.float32:
+        raise ValueError("dy must be float32")
+    dx = torch.empty((m, k), dtype=torch.float32, device=x.device)
+    dw = torch.empty((n_out, k), dtype=torch.float32, device=x.device) if (want_dw or w_latent is not None) else None
+    ns = 1 if group_size == 0 else n_out * (k // group_size)
+    ds = torch.empty(ns, dtype=torch.float32, device=x.device) if w_latent is not None else None
+    a = BitlinearBwdArgs()
+    a.x, a.x_dtype, a.m, a.k, a.ldx = _p(x), _DTYPES[x.dtype], m, k, ldx
+    a.norm_weight, a.norm_eps = _p(norm_weight), norm_eps
+    a.w_packed, a.w_scale, a.n_out, a.group_size = _p(w_packed), _p(w_scale), n_out, group_size
+    a.w_latent = _p(w_latent)
+    a.dy, a.ld_dy = _p(dy), _rows(dy, "dy")[1]
+    a.dx, a.ld_dx = _p(dx), k
+    a.dw, a.d_scale = _p(dw), _p(ds)
+    L = lib()
+    nb = L.ssm_bitlinear_bwd_workspace_bytes(ctypes.byref(a))
+    ws = _workspace(nb, x.device)
+    _check(L.ssm_bitlinear_bwd(ctypes.byref(a), _p(ws), nb, _stream(stream)))
+    return dx, dw, ds
+
+
+def ssm_qat_sgd_step(w_latent: torch.Tensor, w_scale: torch.Tensor, dw: torch.Tensor, d_scale: torch.Tensor | None,
+                     lr: float, lr_scale: float, group_size: int = 0, w_packed: torch.Tensor | None = None,
+                     stream=None):
+    """One QAT step in place on w_latent [n, k] and w_scale; returns (w_packed, zero count tensor)."""
+    n, k = w_latent.shape
+    if w_packed is None:
+        w_packed = torch.empty((n, ssm_packed_row_bytes(k)), dtype=torch.uint8, device=w_latent.device)
+    zc = torch.zeros(1, dtype=torch.int64, device=w_latent.device)
+    _check(lib().ssm_qat_sgd_step(_p(w_latent), _p(w_scale), _p(dw), _p(d_scale), n, k, group_size, lr, lr_scale,
+                                  _p(w_packed), _p(zc), None, 0, _stream(stream)))
+    return w_packed, zc
 
 
 def ssm_dense_fwd(x: torch.Tensor, w: torch.Tensor, residual: torch.Tensor | None = None,

@@ -266,6 +266,34 @@ ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, Mi
   return SSM_OK;
 }
 
+ssm_status ste_check(const ssm_bitlinear_bwd_args* a, SteArgs* o) {
+  if (!a) return fail(SSM_ERR_NULL, "bitlinear bwd: args is NULL");
+  if (a->x_dtype != SSM_F32 && a->x_dtype != SSM_BF16) return fail(SSM_ERR_DTYPE, "bitlinear bwd: x_dtype %d", a->x_dtype);
+  if (a->m < 0 || a->k < 1 || a->k > kMaxK || a->n_out < 1 || a->n_out > 0x7fffffff || a->m > 0x7fffffff)
+    return fail(SSM_ERR_SHAPE, "bitlinear bwd: m >= 0, 1 <= k <= %lld, n_out >= 1", (long long)kMaxK);
+  if (a->ldx < a->k || a->ld_dy < a->n_out || a->ld_dx < a->k)
+    return fail(SSM_ERR_SHAPE, "bitlinear bwd: a row stride is smaller than its row");
+  if (a->group_size < 0 || (a->group_size > 0 && (a->group_size % 64 != 0 || a->k % a->group_size != 0)))
+    return fail(SSM_ERR_SHAPE, "bitlinear bwd: group_size must be 0 or a multiple of 64 dividing k");
+  if (!a->w_packed || !a->w_scale) return fail(SSM_ERR_NULL, "bitlinear bwd: w_packed / w_scale is NULL");
+  if (!aligned(a->w_packed, 4)) return fail(SSM_ERR_ALIGN, "bitlinear bwd: w_packed must be 4-byte aligned");
+  if (a->m > 0 && (!a->x || !a->dy || !a->dx)) return fail(SSM_ERR_NULL, "bitlinear bwd: x, dy and dx are required");
+  if (a->d_scale && (!a->dw || !a->w_latent))
+    return fail(SSM_ERR_NULL, "bitlinear bwd: d_scale needs dw and w_latent");
+  SteArgs& s = *o;
+  s = SteArgs{};
+  s.M = a->m; s.K = a->k; s.N = a->n_out;
+  s.x = a->x; s.ldx = a->ldx; s.x_bf16 = a->x_dtype == SSM_BF16;
+  s.gain = a->norm_weight; s.eps = a->norm_eps;
+  s.W = (const uint32_t*)a->w_packed; s.w_row_words = cdiv(a->k, 16);
+  s.scale = a->w_scale; s.group = a->group_size;
+  s.w_latent = a->w_latent;
+  s.dy = a->dy; s.ld_dy = a->ld_dy;
+  s.dx = a->dx; s.ld_dx = a->ld_dx;
+  s.dw = a->dw; s.dscale = a->d_scale;
+  return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -422,6 +450,45 @@ ssm_status ssm_conv1d_silu_fwd(const void* x, int32_t dtype, int64_t batch, int6
   a.state_out = width > 1 ? state_out : nullptr;
   a.out = out; a.ldo = ldo;
   return dev(launch_conv_silu(a, stream), "conv");
+}
+
+size_t ssm_bitlinear_bwd_workspace_bytes(const ssm_bitlinear_bwd_args* a) {
+  std::string keep = g_err;
+  SteArgs s;
+  const ssm_status st = ste_check(a, &s);
+  g_err = keep;
+  return st == SSM_OK ? ste_workspace(s) : 0;
+}
+
+ssm_status ssm_bitlinear_bwd(const ssm_bitlinear_bwd_args* a, void* ws, size_t wsb, hipStream_t stream) {
+  g_err.clear();
+  SteArgs s;
+  ssm_status st = ste_check(a, &s);
+  if (st != SSM_OK) return st;
+  if (s.M == 0) return SSM_OK;
+  const size_t need = ste_workspace(s);
+  if (!ws || wsb < need) return fail(SSM_ERR_WORKSPACE, "bitlinear bwd: workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(SSM_ERR_ALIGN, "bitlinear bwd: workspace must be 256-byte aligned");
+  return dev(launch_ste_bwd(s, ws, stream), "bitlinear bwd");
+}
+
+ssm_status ssm_qat_sgd_step(float* w_latent, float* w_scale, const float* dw, const float* d_scale, int64_t n_out,
+                            int64_t k, int64_t group_size, float lr, float lr_scale, uint8_t* w_packed,
+                            int64_t* zero_count, void* ws, size_t wsb, hipStream_t stream) {
+  g_err.clear();
+  if (n_out < 1 || k < 1 || group_size < 0 || (group_size > 0 && (group_size % 64 != 0 || k % group_size != 0)))
+    return fail(SSM_ERR_SHAPE, "qat step: n_out, k >= 1; group_size 0 or a multiple of 64 dividing k");
+  if (!w_latent || !w_scale || !dw || !w_packed) return fail(SSM_ERR_NULL, "qat step: w_latent, w_scale, dw, w_packed");
+  const int64_t ns = group_size ? n_out * (k / group_size) : 1;
+  ssm_status st = dev(launch_sgd(w_latent, dw, n_out * k, lr, stream), "qat step weights");
+  if (st != SSM_OK) return st;
+  if (d_scale) {
+    st = dev(launch_sgd(w_scale, d_scale, ns, lr_scale, stream), "qat step scales");
+    if (st != SSM_OK) return st;
+  }
+  // the codes under the updated (learned) scales, with their zero count
+  return ssm_ternary_quantize_weights(w_latent, n_out, k, group_size, w_scale, w_packed, w_scale, zero_count, ws, wsb,
+                                      stream);
 }
 
 ssm_status ssm_dense_fwd(const void* x, int32_t dtype, int64_t m, int64_t k, int64_t ldx, const void* w, int64_t n,

@@ -65,4 +65,21 @@ hipError_t launch_dense(const DenseArgs& a, hipStream_t s) {
   return st == rocblas_status_success ? hipSuccess : hipErrorLaunchFailure;
 }
 
+hipError_t sgemm_rm(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                    const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  rocblas_handle h = nullptr;
+  hipError_t e = handle_for_device(&h);
+  if (e != hipSuccess) return e;
+  const float alpha = 1.0f, beta = 0.0f;
+  // a row-major matrix is its column-major transpose: C^T = op(B)^T op(A)^T, same flags
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (rocblas_set_stream(h, s) != rocblas_status_success) return hipErrorInvalidValue;
+  const rocblas_status st =
+      rocblas_sgemm(h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+                    ta ? rocblas_operation_transpose : rocblas_operation_none, (rocblas_int)N, (rocblas_int)M,
+                    (rocblas_int)K, &alpha, B, (rocblas_int)ldb, A, (rocblas_int)lda, &beta, C, (rocblas_int)ldc);
+  return st == rocblas_status_success ? hipSuccess : hipErrorLaunchFailure;
+}
+
 }  // namespace ssm

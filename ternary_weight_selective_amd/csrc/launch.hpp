@@ -112,6 +112,26 @@ struct DenseArgs {
   void* y; int64_t ldy;
 };
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
+// row-major fp32 C[M, N] = op(A) op(B) (op: transposed when the flag is set), C overwritten
+hipError_t sgemm_rm(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                    const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t s);
+
+// ---- straight-through-estimator backward of BitLinear and the QAT update (ste.hip)
+struct SteArgs {
+  int64_t M, K, N;
+  const void* x; int64_t ldx; int x_bf16;
+  const float* gain; float eps;
+  const uint32_t* W; int64_t w_row_words;
+  const float* scale; int64_t group;
+  const float* w_latent;          // for the scale gradient
+  const float* dy; int64_t ld_dy;  // fp32 [M, N]
+  float* dx; int64_t ld_dx;        // fp32 [M, K]
+  float* dw;                       // fp32 [N, K] or null
+  float* dscale;                   // fp32 [1] or [N, K / group] or null (needs dw and w_latent)
+};
+size_t ste_workspace(const SteArgs& a);
+hipError_t launch_ste_bwd(const SteArgs& a, void* ws, hipStream_t s);
+hipError_t launch_sgd(float* w, const float* dw, int64_t n, float lr, hipStream_t s);
 
 // ---- Mamba-1 mixer front (front.hip): x = BitLinear(u; W_in), p = BitLinear(x; W_x) and the
 // dt input's int8 codes in one kernel (A8, one scale per tensor)

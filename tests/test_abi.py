@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = tws.lib()
-    assert tws.ssm_abi_version() == 3
+    assert tws.ssm_abi_version() == 4
     for s in range(8):
         assert L.ssm_status_string(s)
     assert tws.ssm_packed_row_bytes(8) == 4
@@ -255,6 +255,30 @@ def test_mixer_fp_proj_rejects():
     assert L.ssm_mixer_fwd(ctypes.byref(c), ctypes.byref(w3), FAKE, FAKE + 4096, 2, 64, 1, FAKE, 16,
                            None) == WORKSPACE
     assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 256, 512, 16, dt_rank=16, fp_proj=1))) == 0
+
+
+def test_bitlinear_bwd_and_qat_rejects():
+    L = tws.lib()
+    a = tws.BitlinearBwdArgs()
+    a.x, a.x_dtype, a.m, a.k, a.ldx = FAKE, 0, 4, 64, 64
+    a.w_packed, a.w_scale, a.n_out = FAKE, FAKE, 32
+    a.dy, a.ld_dy, a.dx, a.ld_dx = FAKE, 32, FAKE, 64
+    assert L.ssm_bitlinear_bwd(None, FAKE, 1 << 20, None) == NULL
+    assert L.ssm_bitlinear_bwd_workspace_bytes(ctypes.byref(a)) > 0
+    assert L.ssm_bitlinear_bwd(ctypes.byref(a), FAKE, 16, None) == WORKSPACE
+    for field, val, status in (("x_dtype", 2, DTYPE), ("k", 0, SHAPE), ("ld_dy", 16, SHAPE), ("ld_dx", 8, SHAPE),
+                               ("group_size", 100, SHAPE), ("w_packed", None, NULL), ("dy", None, NULL),
+                               ("w_packed", FAKE + 2, ALIGN)):
+        b = tws.BitlinearBwdArgs.from_buffer_copy(a)
+        setattr(b, field, val)
+        assert L.ssm_bitlinear_bwd(ctypes.byref(b), FAKE, 1 << 30, None) == status, field
+    b = tws.BitlinearBwdArgs.from_buffer_copy(a)
+    b.d_scale = FAKE  # needs dw and w_latent
+    assert L.ssm_bitlinear_bwd(ctypes.byref(b), FAKE, 1 << 30, None) == NULL
+    q = L.ssm_qat_sgd_step
+    assert q(None, FAKE, FAKE, None, 4, 64, 0, 0.1, 0.1, FAKE, None, None, 0, None) == NULL
+    assert q(FAKE, FAKE, FAKE, None, 4, 64, 100, 0.1, 0.1, FAKE, None, None, 0, None) == SHAPE
+    assert q(FAKE, FAKE, FAKE, None, 0, 64, 0, 0.1, 0.1, FAKE, None, None, 0, None) == SHAPE
 
 
 def test_conv_rejects():

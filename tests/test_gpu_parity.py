@@ -589,3 +589,63 @@ def test_mixer_fp_proj_parity(name, over, seed):
     out2 = tws.ssm_mixer_fwd(c, tws.mixer_weights(gw), h, add_residual=True, out=h)
     ref2 = oracle.mixer(oracle_config(cfg), ow, u, residual=True)
     assert rel_err(host(out2), ref2) <= tol
+
+
+# ------------------------------------------------------------------ STE backward, QAT step
+
+BWD_CASES = [  # (m, k, n, group, x dtype, gain)
+    (100, 256, 512, 0, "f32", False),   # TriSSM in_proj shape (rows)
+    (77, 512, 256, 0, "bf16", True),    # TriSSM out_proj shape, bf16 activations, gains
+    (64, 256, 200, 128, "f32", False),  # grouped scales, ragged n
+    (33, 1024, 64, 128, "bf16", True),
+    (1, 100, 30, 0, "f32", False),      # one row, ragged k
+]
+
+
+@pytest.mark.parametrize("m,k,n,group,xd,gain", BWD_CASES)
+def test_bitlinear_bwd_parity(m, k, n, group, xd, gain):
+    """Straight-through-estimator backward (dx through RMSNorm, dW, the scale gradient) against
+    the oracle's fp64 evaluation of the same estimator."""
+    g = wl.rng(m + 5 * k + 3 * n + group)
+    x = wl.normal(g, (m, k))
+    if xd == "bf16":
+        x = bf16_values(x)
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    gn = (1.0 + 0.2 * wl.normal(g, (k,))).astype(np.float32) if gain else None
+    dy = wl.normal(g, (m, n))
+    packed, scale, _ = tws.ssm_ternary_quantize_weights(to_dev(w), group)
+    codes, oscale, _ = oracle.quantize_weights(w, group)
+    xdt = torch.bfloat16 if xd == "bf16" else torch.float32
+    dx, dw, ds = tws.ssm_bitlinear_bwd(to_dev(x, xdt), packed, scale, n, to_dev(dy), group_size=group,
+                                       norm_weight=to_dev(gn) if gain else None, w_latent=to_dev(w))
+    ref = oracle.bitlinear_bwd(x, codes, oscale, dy, group=group, norm_w=gn, w_latent=w)
+    assert rel_err(host(dx), ref["dx"]) <= 1e-5
+    assert rel_err(host(dw), ref["dw"]) <= 1e-5
+    # the scale gradient sums terms of both signs: compare against the sum of their magnitudes
+    v = w.astype(np.float64) / (np.repeat(np.asarray(oscale, np.float64).reshape(n, -1), group, axis=1)
+                                if group else float(np.asarray(oscale).ravel()[0]))
+    fac = np.where(np.abs(v) <= 1.0, codes - v, codes)
+    mag = np.abs(ref["dw"] * fac)
+    mag = np.array([mag.sum()]) if group == 0 else mag.reshape(n, k // group, group).sum(axis=2)
+    assert np.all(np.abs(host(ds).reshape(mag.shape) - ref["ds"].reshape(mag.shape)) <= 1e-5 * mag + 1e-12)
+
+
+@pytest.mark.parametrize("group", [0, 128])
+def test_qat_step_parity(group):
+    """One QAT step: the updated weights and scales bit for bit, the codes under the learned
+    scales and their zero count exactly (inputs: seeded gradients of a realistic scale)."""
+    g = wl.rng(70 + group)
+    n, k = 96, 256
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    dw = wl.normal(g, (n, k), 0.0, 1.0)
+    _, s0, _ = oracle.quantize_weights(w, group)
+    s0 = np.asarray(s0, np.float32)
+    ds = wl.normal(g, s0.shape, 0.0, 0.5)
+    lr, lr_s = 1e-3, 1e-3
+    W, s, codes, zeros = oracle.qat_step(w, s0, dw, ds, lr, lr_s, group)
+    wd, sd = to_dev(w), to_dev(s0.ravel())
+    packed, zc = tws.ssm_qat_sgd_step(wd, sd, to_dev(dw), to_dev(np.asarray(ds).ravel()), lr, lr_s, group)
+    np.testing.assert_array_equal(host(wd), W)
+    np.testing.assert_array_equal(host(sd), np.asarray(s).ravel())
+    np.testing.assert_array_equal(host(packed), oracle.pack(codes))
+    assert int(host(zc)[0]) == zeros
