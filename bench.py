@@ -13,7 +13,8 @@ the roofline of the dominant one.  The CPU oracle is timed on a bounded sample o
 workload on the host cores (a reported baseline, not the target).
 
 Also measured: token-by-token decoding of the same stack (one ssm_mixer_step per layer, the
-recurrent state carried in HBM), at the workload's batch and at batch 1.
+recurrent state carried in HBM), at the workload's batch and at batch 1; and the training side
+of one ternary projection (straight-through-estimator backward, one QAT step).
 """
 from __future__ import annotations
 
@@ -75,6 +76,8 @@ def parse_args():
     ap.add_argument("--stages-only", action="store_true", help="skip the headline loop (profiling runs)")
     ap.add_argument("--no-decode", action="store_true", help="skip the token-by-token decode measurement")
     ap.add_argument("--decode-only", action="store_true", help="only the decode measurement (profiling runs)")
+    ap.add_argument("--no-train", action="store_true", help="skip the BitLinear backward / QAT step measurement")
+    ap.add_argument("--train-only", action="store_true", help="only the BitLinear backward / QAT step (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 3 plain device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -380,6 +383,66 @@ def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
     return out
 
 
+def train_bench(prob: Problem, steps: int, warmup: int) -> dict:
+    """The training side of one ternary projection at the workload's shape (its out_proj: the
+    largest k): straight-through-estimator backward (dx through RMSNorm, dW, the scale
+    gradient) and one QAT step (SGD on latent weights and scales, re-ternarised under the
+    learned scales), each timed with HIP events over `steps` calls."""
+    cfg = prob.cfg
+    if "out" not in cfg.proj_shapes or cfg.is_fp("out") or cfg.act_bits != 8:
+        return {}
+    n, k = cfg.proj_shapes["out"]
+    M = cfg.tokens
+    g = wl.rng(7)
+    dev = prob.dev
+    w = torch.from_numpy(wl.normal(g, (n, k), 0.0, 0.02)).to(dev)
+    packed, scale, _ = tws.ssm_ternary_quantize_weights(w, cfg.group_size)
+    x = torch.from_numpy(wl.normal(g, (M, k))).to(dev).to(prob.act)
+    dy = torch.from_numpy(wl.normal(g, (M, n))).to(dev)
+    L = tws.lib()
+    a = tws.BitlinearBwdArgs()
+    dx = torch.empty((M, k), dtype=torch.float32, device=dev)
+    dw = torch.empty((n, k), dtype=torch.float32, device=dev)
+    ds = torch.empty(scale.numel(), dtype=torch.float32, device=dev)
+    a.x, a.x_dtype, a.m, a.k, a.ldx = x.data_ptr(), tws._DTYPES[prob.act], M, k, k
+    a.norm_eps = cfg.norm_eps
+    a.w_packed, a.w_scale, a.n_out, a.group_size = packed.data_ptr(), scale.data_ptr(), n, cfg.group_size
+    a.w_latent, a.dy, a.ld_dy, a.dx, a.ld_dx = w.data_ptr(), dy.data_ptr(), n, dx.data_ptr(), k
+    a.dw, a.d_scale = dw.data_ptr(), ds.data_ptr()
+    nb = L.ssm_bitlinear_bwd_workspace_bytes(ctypes.byref(a))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    zc = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def bwd():
+        st = L.ssm_bitlinear_bwd(ctypes.byref(a), ws.data_ptr(), nb, sh)
+        if st != 0:
+            raise tws.SsmError(st, L.ssm_last_error().decode())
+
+    def qat():
+        st = L.ssm_qat_sgd_step(w.data_ptr(), scale.data_ptr(), dw.data_ptr(), ds.data_ptr(), n, k, cfg.group_size,
+                                1e-6, 0.0, packed.data_ptr(), zc.data_ptr(), None, 0, sh)
+        if st != 0:
+            raise tws.SsmError(st, L.ssm_last_error().decode())
+
+    out = {"projection": "out_proj", "m": M, "n": n, "k": k}
+    for name, fn in (("bwd", bwd), ("qat_step", qat)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name + "_us"] = e0.elapsed_time(e1) * 1e3 / steps
+    flops = 2 * (2.0 * M * n * k)  # the two dense contractions
+    out["bwd_TFLOP/s"] = flops / (out["bwd_us"] * 1e-6) / 1e12
+    out["zero_ratio"] = float(zc.item()) / (n * k)
+    return out
+
+
 def cpu_baseline(cfg: wl.MixerConfig, seed: int, target_s: float) -> dict:
     import oracle
     from oracle import mixer_stack
@@ -433,6 +496,10 @@ def main():
     prob = Problem(cfg, args.seed, dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+
+    if args.train_only:
+        print(json.dumps({"train_bitlinear": train_bench(prob, args.steps, args.warmup)}))
+        return
 
     if args.decode_only:
         print(json.dumps({"decode": decode_bench(prob, args.steps, args.warmup, (cfg.batch, 1))}))
@@ -618,6 +685,8 @@ def main():
     }
     if not args.no_decode:
         line["decode"] = decode_bench(prob, max(args.steps, 50), args.warmup, (cfg.batch, 1))
+    if not args.no_train:
+        line["train_bitlinear"] = train_bench(prob, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds)
     print(json.dumps(line))

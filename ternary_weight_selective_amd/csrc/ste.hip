@@ -128,14 +128,37 @@ __global__ __launch_bounds__(256) void k_scale_grad(const float* __restrict__ dw
   if (lane == 0) out[seg] = acc;
 }
 
-// Sum of n per-row partials in ascending order (one scale per tensor).
+// Sum of n per-row partials (one scale per tensor), one wave in a fixed order: lane j adds
+// rows j, j + 64, ... in fp64, then the wave's butterfly.
 __global__ void k_sum_rows(const float* __restrict__ part, int64_t n, float* __restrict__ out) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    double s = 0.0;
-    for (int64_t i = 0; i < n; ++i) s += (double)part[i];
-    out[0] = (float)s;
-  }
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+  for (int64_t i = lane; i < n; i += 64) s += (double)part[i];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+  if (lane == 0) out[0] = (float)s;
 }
+
+// dW = sum of the token chunks' partial products, in chunk order.
+__global__ __launch_bounds__(256) void k_sum_chunks(const float* __restrict__ part, int64_t count, int64_t chunks,
+                                                    float* __restrict__ dw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  float s = part[i];
+  for (int64_t c = 1; c < chunks; ++c) s += part[c * count + i];
+  dw[i] = s;
+}
+
+namespace {
+// Token chunks for dW = dy^T x̃: the reduction over tokens is split so that the library sees
+// several (n x k x tokens / chunks) products (a single long reduction with a small output
+// leaves most of the chip idle), their partials kept within 64 MB.
+int64_t dw_chunks(int64_t M, int64_t N, int64_t K) {
+  int64_t c = 16;
+  while (c > 1 && (M % c != 0 || M / c < 512 || c * N * K * 4 > (64ll << 20))) c >>= 1;
+  return c;
+}
+}  // namespace
 
 // W -= lr dW; s -= lr_s ds (fp32 fused multiply-adds).
 __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ w, const float* __restrict__ dw, int64_t n,
@@ -187,6 +210,8 @@ size_t ste_workspace(const SteArgs& a) {
   b += al((size_t)a.N * a.K * 4);             // W̃
   b += al((size_t)a.M * a.K * 4);             // dx̂
   b += al((size_t)a.N * 4);                   // per-row scale partials
+  const int64_t ch = dw_chunks(a.M, a.N, a.K);
+  if (ch > 1) b += al((size_t)ch * a.N * a.K * 4);  // dW partials per token chunk
   return b;
 }
 
@@ -198,7 +223,8 @@ hipError_t launch_ste_bwd(const SteArgs& a, void* ws, hipStream_t s) {
   float* rs = (float*)p; p += al((size_t)a.M * 4);
   float* wt = (float*)p; p += al((size_t)a.N * a.K * 4);
   float* dxh = (float*)p; p += al((size_t)a.M * a.K * 4);
-  float* part = (float*)p;
+  float* part = (float*)p; p += al((size_t)a.N * 4);
+  float* dwp = (float*)p;
   hipError_t e = a.x_bf16 ? launch_act_k<bf16_t>(a, xt, rs, s) : launch_act_k<float>(a, xt, rs, s);
   if (e != hipSuccess) return e;
   const int64_t words = a.N * a.w_row_words;
@@ -211,8 +237,19 @@ hipError_t launch_ste_bwd(const SteArgs& a, void* ws, hipStream_t s) {
   e = a.x_bf16 ? launch_rms_bwd_k<bf16_t>(a, rs, dxh, s) : launch_rms_bwd_k<float>(a, rs, dxh, s);
   if (e != hipSuccess) return e;
   if (a.dw) {  // dW [N, K] = dy^T [N, M] x̃ [M, K]
-    e = sgemm_rm(true, false, a.N, a.K, a.M, a.dy, a.ld_dy, xt, a.K, a.dw, a.K, s);
-    if (e != hipSuccess) return e;
+    const int64_t ch = dw_chunks(a.M, a.N, a.K);
+    if (ch > 1) {
+      const int64_t mc = a.M / ch;
+      e = sgemm_rm_batched(true, false, a.N, a.K, mc, a.dy, a.ld_dy, mc * a.ld_dy, xt, a.K, mc * a.K, dwp, a.K,
+                           a.N * a.K, ch, s);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(k_sum_chunks, dim3((unsigned)cdiv(a.N * a.K, 256)), dim3(256), 0, s, dwp, a.N * a.K, ch,
+                         a.dw);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      e = sgemm_rm(true, false, a.N, a.K, a.M, a.dy, a.ld_dy, xt, a.K, a.dw, a.K, s);
+      if (e != hipSuccess) return e;
+    }
   }
   if (a.dscale) {
     const int64_t segs = a.group ? a.N * (a.K / a.group) : a.N;

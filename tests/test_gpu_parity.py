@@ -599,6 +599,8 @@ BWD_CASES = [  # (m, k, n, group, x dtype, gain)
     (64, 256, 200, 128, "f32", False),  # grouped scales, ragged n
     (33, 1024, 64, 128, "bf16", True),
     (1, 100, 30, 0, "f32", False),      # one row, ragged k
+    (2048, 256, 192, 0, "f32", False),  # dW reduction split over token chunks
+    (4096, 128, 96, 128, "bf16", True),
 ]
 
 
