@@ -73,6 +73,9 @@ BL_CASES = [  # (m, k, n, group, act_bits, x dtype, y dtype)
     (97, 2048, 300, 128, 16, "bf16", "bf16"),  # mamba2_ssd in_proj rows, N ragged
     (64, 4096, 256, 128, 16, "bf16", "bf16"),  # mamba2_ssd out_proj rows
     (50, 256, 64, 0, 16, "f32", "f32"),      # A16 per tensor
+    (130, 512, 200, 0, 16, "bf16", "bf16"),  # A16 per tensor, bf16 out (large-tile kernel), ragged m, n
+    (33, 100, 70, 0, 16, "bf16", "bf16"),    # A16, k padded to 128
+    (300, 2048, 4416, 128, 16, "f32", "bf16"),  # A16 grouped, Mamba-2 in_proj width, fp32 input
     (1, 100, 70, 0, 8, "f32", "f32"),        # one row, ragged k
     (100, 2048, 4416, 0, 8, "bf16", "bf16"),  # mamba2_a8 in_proj (tiled int8 path)
     (77, 4096, 2048, 0, 8, "bf16", "bf16"),   # mamba2_a8 out_proj
