@@ -415,3 +415,64 @@ def qat_step(w_latent, w_scale, dw, ds, lr: float, lr_scale: float, group: int =
     s = s.astype(np.float32)
     codes, zeros = ternarize(W, group, s)
     return W, s, codes, zeros
+
+
+def selective_scan_bwd(x, delta, A, Bm, Cm, D, dy, delta_bias=None, softplus: bool = True, h0=None) -> dict:
+    """Backward of the selective scan (the recurrence of ``selective_scan``), fp64, by reverse
+    accumulation through the stored states.  With dt_t = softplus(delta_t + bias),
+    a_t = exp(dt_t A), h_t = a_t h_{t-1} + dt_t x_t B_t and y_t = C_t . h_t + D x_t, the
+    adjoint of the state is g_t = C_t dy_t + a_{t+1} g_{t+1}; then
+      dC_t = sum over channels of dy_t h_t,   dB_t = sum of g_t dt_t x_t,
+      dx_t = D dy_t + dt_t sum_n g_t B_t,     d dt_t = sum_n g_t (h_{t-1} a_t A + x_t B_t),
+      d delta_t = d dt_t * sigmoid(delta_t + bias) (1 above 20, where softplus is the identity),
+      dA = sum_t g_t h_{t-1} a_t dt_t,  dD = sum_t dy_t x_t,  d bias = sum_t d delta_t,
+      dh0 = a_0 g_0.
+    Shapes as ``selective_scan``; dy like y.  Returns a dict of fp64 arrays."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    delta = np.asarray(delta, np.float32).astype(np.float64)
+    A = np.asarray(A, np.float32).astype(np.float64)
+    Bm = np.asarray(Bm, np.float32).astype(np.float64)
+    Cm = np.asarray(Cm, np.float32).astype(np.float64)
+    dy = np.asarray(dy, np.float64)
+    batch, L, HP = x.shape
+    H = delta.shape[2]
+    P = HP // H
+    N = Bm.shape[2]
+    aps = A.ndim == 2
+    Dv = np.zeros(H) if D is None else np.asarray(D, np.float32).astype(np.float64)
+    bias = np.zeros(H) if delta_bias is None else np.asarray(delta_bias, np.float32).astype(np.float64)
+    Ab = A[:, None, :] if aps else A[:, None, None]                      # [H, 1, N or 1]
+    pre = delta + bias[None, None, :]                                    # [B, L, H]
+    dt = np.where(pre > 20.0, pre, np.log1p(np.exp(np.minimum(pre, 20.0)))) if softplus else pre
+    sig = np.where(pre > 20.0, 1.0, 1.0 / (1.0 + np.exp(-pre))) if softplus else np.ones_like(pre)
+    xs = x.reshape(batch, L, H, P)
+    dys = dy.reshape(batch, L, H, P)
+    hs = np.zeros((L + 1, batch, H, P, N))                              # hs[t + 1] = h_t, hs[0] = h0
+    if h0 is not None:
+        hs[0] = np.asarray(h0, np.float32).astype(np.float64).reshape(batch, H, P, N)
+    for t in range(L):
+        a = np.exp(dt[:, t, :, None, None] * Ab[None])                  # [B, H, 1 or P, N or 1]
+        hs[t + 1] = a * hs[t] + (dt[:, t, :, None, None] * xs[:, t, :, :, None]) * Bm[:, t, None, None, :]
+    dx = np.zeros((batch, L, H, P))
+    ddelta = np.zeros((batch, L, H))
+    dB = np.zeros((batch, L, N))
+    dC = np.zeros((batch, L, N))
+    dA = np.zeros_like(A)
+    dD = np.zeros(H)
+    carry = np.zeros((batch, H, P, N))                                   # a_{t+1} g_{t+1}
+    for t in range(L - 1, -1, -1):
+        a = np.exp(dt[:, t, :, None, None] * Ab[None]) * np.ones((1, 1, P, N))
+        g = carry + Cm[:, t, None, None, :] * dys[:, t, :, :, None]
+        hprev = hs[t]
+        dC[:, t] = np.einsum("bhp,bhpn->bn", dys[:, t], hs[t + 1])
+        dB[:, t] = np.einsum("bhpn,bh,bhp->bn", g, dt[:, t], xs[:, t])
+        dx[:, t] = Dv[None, :, None] * dys[:, t] + dt[:, t, :, None] * np.einsum("bhpn,bn->bhp", g, Bm[:, t])
+        ddt = np.einsum("bhpn,bhpn->bh", g, hprev * a * (Ab[None] * np.ones((1, 1, P, N)))) + \
+            np.einsum("bhpn,bhp,bn->bh", g, xs[:, t], Bm[:, t])
+        ddelta[:, t] = ddt * sig[:, t]
+        gA = g * hprev * a * dt[:, t, :, None, None]
+        dA += gA.sum(axis=(0, 2)) if aps else gA.sum(axis=(0, 2, 3))
+        dD += np.einsum("bhp,bhp->h", dys[:, t], xs[:, t])
+        carry = a * g
+    return dict(dx=dx.reshape(batch, L, HP), ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD,
+                dbias=ddelta.sum(axis=(0, 1)), dh0=carry.reshape(batch, H, P, N))
