@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 typedef enum {
   SSM_OK = 0,
@@ -322,6 +322,43 @@ ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w,
  * Errors: SSM_ERR_DTYPE, SSM_ERR_SHAPE (sizes, strides, width, out == x), SSM_ERR_NULL,
  * SSM_ERR_DEVICE.
  */
+/*
+ * ssm_selective_scan_bwd -- the backward of the Mamba-1 kind selective scan (the mixer is
+ * trained end to end; TriSSM README): the exact reverse-mode derivative of the recurrence of
+ * ssm_selective_scan_fwd (a_per_state = 1, headdim = 1; the dt input given as delta, not as a
+ * dt projection).  With dt = softplus(delta + bias), a_t = exp(dt A), h_t = a_t h_{t-1} +
+ * dt x B, y = C . h + D x and the state adjoint g_t = C_t dy_t + a_{t+1} g_{t+1}:
+ *   dx = D dy + dt sum_n g B;  d delta = sum_n g (h_{t-1} a A + x B) * softplus'(delta + bias);
+ *   dA = sum_{b,t} g h_{t-1} a dt;  dB_t = sum_channels g dt x;  dC_t = sum_channels dy h_t;
+ *   dD = sum dy x;  d bias = sum d delta;  dh0 = a_0 g_0.
+ * Inputs as ssm_selective_scan_fwd (act_dtype x, delta, Bm, Cm; fp32 A [H, N], D, bias, h0)
+ * plus dy fp32 [B, L, ld_dy].  Outputs fp32, dense: dx and ddelta [B, L, H], dA [H, N],
+ * dB and dC [B, L, N]; dD, dbias [H] and dh0 [B, H, N] nullable.  The states of the whole
+ * sequence are re-computed into the workspace (B L H N fp32 plus partial sums):
+ * ssm_selective_scan_bwd_workspace_bytes().  Sums over sequences and channel tiles are taken
+ * in a fixed order (results do not depend on timing).
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIGN,
+ * SSM_ERR_WORKSPACE, SSM_ERR_DEVICE.
+ */
+typedef struct {
+  int64_t batch, seqlen, nheads, d_state;
+  int32_t act_dtype; int32_t delta_softplus;
+  const void* x;      int64_t ld_x;
+  const void* delta;  int64_t ld_delta;
+  const float* delta_bias;
+  const float* A;
+  const void* Bm;     int64_t ld_B;
+  const void* Cm;     int64_t ld_C;
+  const float* D;
+  const float* h0;
+  const float* dy;    int64_t ld_dy;
+  float *dx, *ddelta, *dA, *dB, *dC, *dD, *dbias, *dh0;
+} ssm_scan_bwd_args;
+
+size_t ssm_selective_scan_bwd_workspace_bytes(const ssm_scan_bwd_args* a);
+ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_args* a, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /*
  * ssm_bitlinear_bwd -- the backward pass of the A8 BitLinear with straight-through
  * estimators (TriSSM README: BitLinear layers trained with straight-through estimators; the

@@ -43,6 +43,14 @@ class ScanArgs(ctypes.Structure):
                 ("gate", _vp), ("ld_gate", _i64)]
 
 
+class ScanBwdArgs(ctypes.Structure):
+    _fields_ = [("batch", _i64), ("seqlen", _i64), ("nheads", _i64), ("d_state", _i64), ("act_dtype", _i32),
+                ("delta_softplus", _i32), ("x", _vp), ("ld_x", _i64), ("delta", _vp), ("ld_delta", _i64),
+                ("delta_bias", _vp), ("A", _vp), ("Bm", _vp), ("ld_B", _i64), ("Cm", _vp), ("ld_C", _i64),
+                ("D", _vp), ("h0", _vp), ("dy", _vp), ("ld_dy", _i64), ("dx", _vp), ("ddelta", _vp), ("dA", _vp),
+                ("dB", _vp), ("dC", _vp), ("dD", _vp), ("dbias", _vp), ("dh0", _vp)]
+
+
 class BitlinearBwdArgs(ctypes.Structure):
     _fields_ = [("x", _vp), ("x_dtype", _i32), ("pad0", _i32), ("m", _i64), ("k", _i64), ("ldx", _i64),
                 ("norm_weight", _vp), ("norm_eps", ctypes.c_float), ("pad1", _i32), ("w_packed", _vp),
@@ -74,7 +82,7 @@ EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
            "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front", "ssm_mixer_step",
            "ssm_conv1d_silu_fwd", "ssm_dense_fwd", "ssm_bitlinear_bwd_workspace_bytes", "ssm_bitlinear_bwd",
-           "ssm_qat_sgd_step"]
+           "ssm_qat_sgd_step", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd"]
 
 
 def lib():
@@ -120,6 +128,10 @@ def lib():
         L.ssm_qat_sgd_step.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float, _vp, _vp,
                                        _vp, _sz, _vp]
         L.ssm_qat_sgd_step.restype = ctypes.c_int
+        L.ssm_selective_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ScanBwdArgs)]
+        L.ssm_selective_scan_bwd_workspace_bytes.restype = _sz
+        L.ssm_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _vp, _sz, _vp]
+        L.ssm_selective_scan_bwd.restype = ctypes.c_int
         L.ssm_mixer_step.restype = ctypes.c_int
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
@@ -342,6 +354,38 @@ def ssm_mixer_step(cfg: MixerConfig, weights, u: torch.Tensor, state: torch.Tens
     _check(L.ssm_mixer_step(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, _p(state), _p(conv_state),
                             int(add_residual), _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
     return out
+
+
+def ssm_selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, Bm: torch.Tensor, Cm: torch.Tensor,
+                           dy: torch.Tensor, D: torch.Tensor | None = None, delta_bias: torch.Tensor | None = None,
+                           softplus: bool = True, h0: torch.Tensor | None = None, stream=None) -> dict:
+    """Backward of the Mamba-1 kind scan: x, delta [B, L, H], Bm/Cm [B, L, N] (views with a
+    contiguous last dim), A [H, N], dy fp32 [B, L, H].  Returns fp32 gradients dx, ddelta,
+    dA, dB, dC, dD, dbias, dh0."""
+    batch, L, H = x.shape
+    N = Bm.shape[2]
+    dev = x.device
+    f = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty((batch, L, H), **f), ddelta=torch.empty((batch, L, H), **f), dA=torch.empty((H, N), **f),
+             dB=torch.empty((batch, L, N), **f), dC=torch.empty((batch, L, N), **f), dD=torch.empty(H, **f),
+             dbias=torch.empty(H, **f), dh0=torch.empty((batch, H, N), **f))
+    a = ScanBwdArgs()
+    a.batch, a.seqlen, a.nheads, a.d_state = batch, L, H, N
+    a.act_dtype, a.delta_softplus = _DTYPES[x.dtype], int(softplus)
+    a.x, a.ld_x = _p(x), _rows(x, "x")[1]
+    a.delta, a.ld_delta = _p(delta), _rows(delta, "delta")[1]
+    a.delta_bias, a.A = _p(delta_bias), _p(A)
+    a.Bm, a.ld_B = _p(Bm), _rows(Bm, "Bm")[1]
+    a.Cm, a.ld_C = _p(Cm), _rows(Cm, "Cm")[1]
+    a.D, a.h0 = _p(D), _p(h0)
+    a.dy, a.ld_dy = _p(dy), _rows(dy, "dy")[1]
+    for k, v in g.items():
+        setattr(a, k, _p(v))
+    L_ = lib()
+    nb = L_.ssm_selective_scan_bwd_workspace_bytes(ctypes.byref(a))
+    ws = _workspace(nb, dev)
+    _check(L_.ssm_selective_scan_bwd(ctypes.byref(a), _p(ws), nb, _stream(stream)))
+    return g
 
 
 def ssm_bitlinear_bwd(x: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, n_out: int,

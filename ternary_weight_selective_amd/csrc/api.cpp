@@ -5,6 +5,7 @@
 #include <string>
 
 #include "launch.hpp"
+#include "scan_bwd.hpp"
 #include "ssm_ternary.h"
 
 using namespace ssm;
@@ -294,6 +295,32 @@ ssm_status ste_check(const ssm_bitlinear_bwd_args* a, SteArgs* o) {
   return SSM_OK;
 }
 
+ssm_status scan_bwd_check(const ssm_scan_bwd_args* a, ScanBwdArgs* o) {
+  if (!a) return fail(SSM_ERR_NULL, "scan bwd: args is NULL");
+  if (!act_dtype_ok(a->act_dtype)) return fail(SSM_ERR_DTYPE, "scan bwd: act_dtype %d", a->act_dtype);
+  if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1) return fail(SSM_ERR_SHAPE, "scan bwd: batch, seqlen >= 0, nheads >= 1");
+  const int64_t n = a->d_state;
+  if (n != 4 && n != 8 && n != 16 && n != 32 && n != 64) return fail(SSM_ERR_UNSUPPORTED, "scan bwd: d_state %lld", (long long)n);
+  if (a->batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "scan bwd: batch above 65535");
+  if (a->ld_x < a->nheads || a->ld_delta < a->nheads || a->ld_B < n || a->ld_C < n || a->ld_dy < a->nheads)
+    return fail(SSM_ERR_SHAPE, "scan bwd: a row stride is smaller than its row");
+  if (a->batch * a->seqlen > 0 && (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->dy || !a->dx ||
+                                   !a->ddelta || !a->dA || !a->dB || !a->dC))
+    return fail(SSM_ERR_NULL, "scan bwd: x, delta, A, Bm, Cm, dy, dx, ddelta, dA, dB and dC are required");
+  if (!aligned(a->A, 4)) return fail(SSM_ERR_ALIGN, "scan bwd: A must be 4-byte aligned");
+  ScanBwdArgs& s = *o;
+  s = ScanBwdArgs{};
+  s.batch = a->batch; s.L = a->seqlen; s.H = a->nheads; s.N = n;
+  s.act_bf16 = a->act_dtype == SSM_BF16; s.softplus = a->delta_softplus;
+  s.x = a->x; s.ld_x = a->ld_x; s.delta = a->delta; s.ld_delta = a->ld_delta;
+  s.delta_bias = a->delta_bias; s.A = a->A;
+  s.Bm = a->Bm; s.ld_B = a->ld_B; s.Cm = a->Cm; s.ld_C = a->ld_C;
+  s.D = a->D; s.h0 = a->h0; s.dy = a->dy; s.ld_dy = a->ld_dy;
+  s.dx = a->dx; s.ddelta = a->ddelta; s.dA = a->dA; s.dB = a->dB; s.dC = a->dC;
+  s.dD = a->dD; s.dbias = a->dbias; s.dh0 = a->dh0;
+  return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -450,6 +477,26 @@ ssm_status ssm_conv1d_silu_fwd(const void* x, int32_t dtype, int64_t batch, int6
   a.state_out = width > 1 ? state_out : nullptr;
   a.out = out; a.ldo = ldo;
   return dev(launch_conv_silu(a, stream), "conv");
+}
+
+size_t ssm_selective_scan_bwd_workspace_bytes(const ssm_scan_bwd_args* a) {
+  std::string keep = g_err;
+  ScanBwdArgs s;
+  const ssm_status st = scan_bwd_check(a, &s);
+  g_err = keep;
+  return st == SSM_OK ? scan_bwd_workspace(s) : 0;
+}
+
+ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_args* a, void* ws, size_t wsb, hipStream_t stream) {
+  g_err.clear();
+  ScanBwdArgs s;
+  ssm_status st = scan_bwd_check(a, &s);
+  if (st != SSM_OK) return st;
+  if (s.batch * s.L == 0) return SSM_OK;
+  const size_t need = scan_bwd_workspace(s);
+  if (!ws || wsb < need) return fail(SSM_ERR_WORKSPACE, "scan bwd: workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(SSM_ERR_ALIGN, "scan bwd: workspace must be 256-byte aligned");
+  return dev(launch_scan_bwd(s, ws, stream), "scan bwd");
 }
 
 size_t ssm_bitlinear_bwd_workspace_bytes(const ssm_bitlinear_bwd_args* a) {

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = tws.lib()
-    assert tws.ssm_abi_version() == 4
+    assert tws.ssm_abi_version() == 5
     for s in range(8):
         assert L.ssm_status_string(s)
     assert tws.ssm_packed_row_bytes(8) == 4
@@ -279,6 +279,25 @@ def test_bitlinear_bwd_and_qat_rejects():
     assert q(None, FAKE, FAKE, None, 4, 64, 0, 0.1, 0.1, FAKE, None, None, 0, None) == NULL
     assert q(FAKE, FAKE, FAKE, None, 4, 64, 100, 0.1, 0.1, FAKE, None, None, 0, None) == SHAPE
     assert q(FAKE, FAKE, FAKE, None, 0, 64, 0, 0.1, 0.1, FAKE, None, None, 0, None) == SHAPE
+
+
+def test_scan_bwd_rejects():
+    L = tws.lib()
+    a = tws.ScanBwdArgs()
+    a.batch, a.seqlen, a.nheads, a.d_state, a.act_dtype, a.delta_softplus = 2, 8, 64, 16, 0, 1
+    for f in ("x", "delta", "A", "Bm", "Cm", "dy", "dx", "ddelta", "dA", "dB", "dC"):
+        setattr(a, f, FAKE)
+    a.ld_x = a.ld_delta = a.ld_dy = 64
+    a.ld_B = a.ld_C = 16
+    assert L.ssm_selective_scan_bwd(None, FAKE, 1 << 30, None) == NULL
+    assert L.ssm_selective_scan_bwd_workspace_bytes(ctypes.byref(a)) >= 2 * 8 * 64 * 16 * 4
+    assert L.ssm_selective_scan_bwd(ctypes.byref(a), FAKE, 16, None) == WORKSPACE
+    assert L.ssm_selective_scan_bwd(ctypes.byref(a), FAKE + 8, 1 << 30, None) == ALIGN
+    for field, val, status in (("d_state", 12, UNSUPPORTED), ("act_dtype", 2, DTYPE), ("ld_B", 8, SHAPE),
+                               ("ld_dy", 32, SHAPE), ("nheads", 0, SHAPE), ("dB", None, NULL), ("A", FAKE + 2, ALIGN)):
+        b = tws.ScanBwdArgs.from_buffer_copy(a)
+        setattr(b, field, val)
+        assert L.ssm_selective_scan_bwd(ctypes.byref(b), FAKE, 1 << 30, None) == status, field
 
 
 def test_conv_rejects():

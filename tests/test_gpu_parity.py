@@ -654,3 +654,34 @@ def test_qat_step_parity(group):
     np.testing.assert_array_equal(host(sd), np.asarray(s).ravel())
     np.testing.assert_array_equal(host(packed), oracle.pack(codes))
     assert int(host(zc)[0]) == zeros
+
+
+
+SCAN_BWD_CASES = [  # (batch, L, H, N, dtype, h0)
+    (2, 37, 70, 16, "f32", False),     # ragged channel tile, ragged time
+    (3, 130, 128, 8, "bf16", True),
+    (1, 300, 512, 16, "f32", True),
+    (8, 256, 512, 16, "f32", False),   # TriSSM width and length
+    (2, 20, 64, 64, "f32", True),
+]
+
+
+@pytest.mark.parametrize("batch,L,H,N,dt,with_h0", SCAN_BWD_CASES)
+def test_scan_bwd_parity(batch, L, H, N, dt, with_h0):
+    """Backward of the Mamba-1 kind scan against the oracle's reverse accumulation: every
+    gradient to 2e-4 norm-wise (fp32 accumulation over the sequence on the GPU, fp64 in the
+    oracle; the forward's hardware exp2 and softplus)."""
+    p = wl.scan_problem(batch, L, H, 1, N, True, seed=batch * 100 + L + N)
+    g = wl.rng(batch + L + H)
+    dy = wl.normal(g, (batch, L, H))
+    h0 = wl.normal(g, (batch, H, 1, N), 0.0, 0.5) if with_h0 else None
+    if dt == "bf16":
+        p = _bf16_problem(p)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    got = tws.ssm_selective_scan_bwd(to_dev(p["x"], tdt), to_dev(p["delta"], tdt), to_dev(p["A"]),
+                                     to_dev(p["Bm"], tdt), to_dev(p["Cm"], tdt), to_dev(dy), D=to_dev(p["D"]),
+                                     delta_bias=to_dev(p["dt_bias"]), h0=to_dev(h0) if with_h0 else None)
+    ref = oracle.selective_scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["D"], dy,
+                                    delta_bias=p["dt_bias"], h0=h0)
+    for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dbias", "dh0"):
+        assert rel_err(host(got[k]).reshape(ref[k].shape), ref[k]) <= 2e-4, k
