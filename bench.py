@@ -440,6 +440,35 @@ def train_bench(prob: Problem, steps: int, warmup: int) -> dict:
     flops = 2 * (2.0 * M * n * k)  # the two dense contractions
     out["bwd_TFLOP/s"] = flops / (out["bwd_us"] * 1e-6) / 1e12
     out["zero_ratio"] = float(zc.item()) / (n * k)
+    if cfg.kind == wl.MAMBA1:  # the scan's backward at the workload's shape
+        H, N = cfg.d_inner, cfg.d_state
+        p = wl.scan_problem(cfg.batch, cfg.seqlen, H, 1, N, True, seed=5)
+        t = {k: torch.from_numpy(v).to(dev) for k, v in p.items()}
+        for k in ("x", "delta", "Bm", "Cm"):
+            t[k] = t[k].to(prob.act)
+        dys = torch.from_numpy(wl.normal(g, (cfg.batch, cfg.seqlen, H))).to(dev)
+
+        def sbwd():
+            tws.ssm_selective_scan_bwd(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], dys, D=t["D"],
+                                       delta_bias=t["dt_bias"], stream=torch.cuda.current_stream())
+
+        for _ in range(max(1, warmup // 2)):
+            sbwd()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(2, steps // 4)
+        e0.record()
+        for _ in range(reps):
+            sbwd()
+        e1.record()
+        torch.cuda.synchronize()
+        out["scan_bwd_us"] = e0.elapsed_time(e1) * 1e3 / reps
+        # algorithmic bytes: read x, delta, B, C, dy; write dx, ddelta, dB, dC (fp32 grads), plus the
+        # stored states written once and read once
+        es = 2 if prob.act == torch.bfloat16 else 4
+        Mt = cfg.tokens
+        byts = Mt * (2 * H + 2 * N) * es + Mt * H * 4 + Mt * (2 * H + 2 * N) * 4 + 2 * Mt * H * N * 4
+        out["scan_bwd_GBps"] = byts / (out["scan_bwd_us"] * 1e-6) / 1e9
     return out
 
 
