@@ -25,20 +25,14 @@ __device__ __forceinline__ float softplus_b(float v) {
   return v > 20.0f ? v : r;
 }
 
-// dt of (token, channel) and the derivative of the softplus, sigmoid(pre) (1 where the
-// forward is the identity)
-template <typename T>
-__device__ __forceinline__ float dt_of(const ScanBwdArgs& a, int64_t tok, int64_t d, float bias, float* sig) {
-  const float pre = ld_act((const T*)a.delta + tok * a.ld_delta + d) + bias;
-  if (!a.softplus) { *sig = 1.0f; return pre; }
-  *sig = pre > 20.0f ? 1.0f : 1.0f / (1.0f + __builtin_amdgcn_exp2f(-pre * kLog2eB));
-  return softplus_b(pre);
-}
+// steps per register tile of the two passes (the loads of the next tile are in flight while the
+// current one is computed)
+template <int SPL> constexpr int bwd_tile() { return SPL >= 16 ? 1 : (SPL >= 8 ? 2 : (SPL >= 4 ? 4 : 8)); }
 
 // pass 1: the forward recurrence, storing h_t for every step: hs[b][t][d][n]
 template <int NS, typename T>
 __global__ __launch_bounds__(256) void k_scan_save(ScanBwdArgs a, float* __restrict__ hs) {
-  constexpr int SPL = NS / 4;
+  constexpr int SPL = NS / 4, TT = bwd_tile<SPL>();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t b = blockIdx.x, d = (int64_t)blockIdx.y * kCPBb + lane, H = a.H, L = a.L;
   if (d >= H) return;  // no barriers in this kernel
@@ -50,28 +44,55 @@ __global__ __launch_bounds__(256) void k_scan_save(ScanBwdArgs a, float* __restr
     Al[i] = a.A[d * NS + n] * kLog2eB;
     h[i] = a.h0 ? a.h0[(b * H + d) * NS + n] : 0.0f;
   }
-  for (int64_t t = 0; t < L; ++t) {
-    const int64_t tok = b * L + t;
-    float sig;
-    const float dt = dt_of<T>(a, tok, d, bias, &sig);
-    const float dx = dt * ld_act((const T*)a.x + tok * a.ld_x + d);
-    float* hr = hs + (tok * H + d) * NS + w * SPL;
+  float rd[TT], rx[TT], rb[TT][SPL];
+  auto load = [&](int64_t t0) {
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      const float ab = __builtin_amdgcn_exp2f(dt * Al[i]);
-      h[i] = __builtin_fmaf(ab, h[i], dx * ld_act((const T*)a.Bm + tok * a.ld_B + w * SPL + i));
-      hr[i] = h[i];
+    for (int u = 0; u < TT; ++u) {
+      const int64_t t = t0 + u;
+      const bool ok = t < L;
+      const int64_t tok = b * L + (ok ? t : 0);
+      rd[u] = ok ? ld_act((const T*)a.delta + tok * a.ld_delta + d) : 0.0f;
+      rx[u] = ok ? ld_act((const T*)a.x + tok * a.ld_x + d) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) rb[u][i] = ok ? ld_act((const T*)a.Bm + tok * a.ld_B + w * SPL + i) : 0.0f;
+    }
+  };
+  load(0);
+  for (int64_t t0 = 0; t0 < L; t0 += TT) {
+    float cd[TT], cx[TT], cb[TT][SPL];
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+      cd[u] = rd[u];
+      cx[u] = rx[u];
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) cb[u][i] = rb[u][i];
+    }
+    if (t0 + TT < L) load(t0 + TT);
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+      const int64_t t = t0 + u;
+      if (t >= L) break;
+      const float pre = cd[u] + bias;
+      const float dt = a.softplus ? softplus_b(pre) : pre;
+      const float dx = dt * cx[u];
+      float* hr = hs + ((b * L + t) * H + d) * NS + w * SPL;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const float ab = __builtin_amdgcn_exp2f(dt * Al[i]);
+        h[i] = __builtin_fmaf(ab, h[i], dx * cb[u][i]);
+        hr[i] = h[i];
+      }
     }
   }
 }
 
-// pass 2: reverse time
+// pass 2: reverse time, TT steps per register tile (TT <= 2: the reverse step holds more)
 template <int NS, typename T>
 __global__ __launch_bounds__(256) void k_scan_rev(ScanBwdArgs a, const float* __restrict__ hs,
                                                   float* __restrict__ pB, float* __restrict__ pC,
                                                   float* __restrict__ pA, float* __restrict__ pD,
                                                   float* __restrict__ pbias) {
-  constexpr int SPL = NS / 4;
+  constexpr int SPL = NS / 4, TT = bwd_tile<SPL>() > 2 ? 2 : bwd_tile<SPL>();
   __shared__ float s_red[2][2][4][kCPBb];  // [step parity][d dt, sum g B][wave][channel]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t b = blockIdx.x, tile = blockIdx.y, d = tile * kCPBb + lane, H = a.H, L = a.L;
@@ -89,50 +110,91 @@ __global__ __launch_bounds__(256) void k_scan_rev(ScanBwdArgs a, const float* __
     dA[i] = 0.0f;
   }
   float dD = 0.0f, dbias = 0.0f;
-  for (int64_t t = L - 1; t >= 0; --t) {
-    const int64_t tok = b * L + t;
-    float sig;
-    const float dt = dt_of<T>(a, tok, dc, bias, &sig);
-    const float xv = dv ? ld_act((const T*)a.x + tok * a.ld_x + dc) : 0.0f;
-    const float dyv = dv ? a.dy[tok * a.ld_dy + dc] : 0.0f;
-    const float* hr = hs + (tok * H + dc) * NS + w * SPL;
-    const float* hq = hs + ((t > 0 ? tok - 1 : tok) * H + dc) * NS + w * SPL;  // h_{t-1} (t > 0)
-    float pddt = 0.0f, pgb = 0.0f;
+  // per step: pre-activation dt, x, dy, B, C and h_{t-1}; h_t is the previous step's h_{t-1}
+  float rd[TT], rx[TT], ry[TT], rB[TT][SPL], rC[TT][SPL], rh[TT][SPL];
+  auto load = [&](int64_t t1) {  // steps t1, t1 - 1, ..., t1 - TT + 1
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      const int n = w * SPL + i;
-      const float Bn = ld_act((const T*)a.Bm + tok * a.ld_B + n);
-      const float Cn = ld_act((const T*)a.Cm + tok * a.ld_C + n);
-      const float ht = hr[i];
-      const float hprev = t > 0 ? hq[i] : (a.h0 ? a.h0[(b * H + dc) * NS + n] : 0.0f);
-      const float ab = __builtin_amdgcn_exp2f(dt * Al[i]);
-      const float gi = dv ? __builtin_fmaf(Cn, dyv, g[i]) : 0.0f;
-      const float gha = gi * hprev * ab;
-      pddt = __builtin_fmaf(gha, Av[i], __builtin_fmaf(gi * xv, Bn, pddt));
-      pgb = __builtin_fmaf(gi, Bn, pgb);
-      dA[i] = __builtin_fmaf(gha, dt, dA[i]);
-      const float cb = wave_sum_butterfly(gi * dt * xv);       // dB over the block's channels
-      const float cc = wave_sum_butterfly(dv ? dyv * ht : 0.0f);  // dC
-      if (lane == 0) {
-        pB[(tok * ntile + tile) * NS + n] = cb;
-        pC[(tok * ntile + tile) * NS + n] = cc;
+    for (int u = 0; u < TT; ++u) {
+      const int64_t t = t1 - u;
+      const bool ok = t >= 0;
+      const int64_t tok = b * L + (ok ? t : 0);
+      rd[u] = ok ? ld_act((const T*)a.delta + tok * a.ld_delta + dc) : 0.0f;
+      rx[u] = (ok && dv) ? ld_act((const T*)a.x + tok * a.ld_x + dc) : 0.0f;
+      ry[u] = (ok && dv) ? a.dy[tok * a.ld_dy + dc] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int n = w * SPL + i;
+        rB[u][i] = ok ? ld_act((const T*)a.Bm + tok * a.ld_B + n) : 0.0f;
+        rC[u][i] = ok ? ld_act((const T*)a.Cm + tok * a.ld_C + n) : 0.0f;
+        rh[u][i] = t > 0 ? hs[((tok - 1) * H + dc) * NS + n]
+                         : ((ok && a.h0) ? a.h0[(b * H + dc) * NS + n] : 0.0f);
       }
-      g[i] = ab * gi;
     }
-    const int par = (int)(t & 1);
-    s_red[par][0][w][lane] = pddt;
-    s_red[par][1][w][lane] = pgb;
-    __syncthreads();  // one barrier per step: the other parity's buffer is free (see the loop)
-    if (w == 0 && dv) {
-      const float ddt = ((s_red[par][0][0][lane] + s_red[par][0][1][lane]) + s_red[par][0][2][lane]) +
-                        s_red[par][0][3][lane];
-      const float sgb = ((s_red[par][1][0][lane] + s_red[par][1][1][lane]) + s_red[par][1][2][lane]) +
-                        s_red[par][1][3][lane];
-      const float ddl = ddt * sig;
-      a.ddelta[tok * H + dc] = ddl;
-      a.dx[tok * H + dc] = __builtin_fmaf(Dd, dyv, dt * sgb);
-      dbias += ddl;
-      dD = __builtin_fmaf(dyv, xv, dD);
+  };
+  float ht[SPL];  // h_t of the current step
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) ht[i] = hs[((b * L + L - 1) * H + dc) * NS + w * SPL + i];
+  load(L - 1);
+  for (int64_t t1 = L - 1; t1 >= 0; t1 -= TT) {
+    float cd[TT], cx[TT], cy[TT], cB[TT][SPL], cC[TT][SPL], ch[TT][SPL];
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+      cd[u] = rd[u]; cx[u] = rx[u]; cy[u] = ry[u];
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) { cB[u][i] = rB[u][i]; cC[u][i] = rC[u][i]; ch[u][i] = rh[u][i]; }
+    }
+    if (t1 - TT >= 0) load(t1 - TT);
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+      const int64_t t = t1 - u;
+      if (t < 0) break;
+      const int64_t tok = b * L + t;
+      const float pre = cd[u] + bias;
+      float dt, sig;
+      if (a.softplus) {
+        sig = pre > 20.0f ? 1.0f : 1.0f / (1.0f + __builtin_amdgcn_exp2f(-pre * kLog2eB));
+        dt = softplus_b(pre);
+      } else {
+        sig = 1.0f;
+        dt = pre;
+      }
+      const float xv = cx[u], dyv = cy[u];
+      float pddt = 0.0f, pgb = 0.0f;
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int n = w * SPL + i;
+        const float Bn = cB[u][i], Cn = cC[u][i];
+        const float hprev = ch[u][i];
+        const float ab = __builtin_amdgcn_exp2f(dt * Al[i]);
+        const float gi = dv ? __builtin_fmaf(Cn, dyv, g[i]) : 0.0f;
+        const float gha = gi * hprev * ab;
+        pddt = __builtin_fmaf(gha, Av[i], __builtin_fmaf(gi * xv, Bn, pddt));
+        pgb = __builtin_fmaf(gi, Bn, pgb);
+        dA[i] = __builtin_fmaf(gha, dt, dA[i]);
+        const float cb = wave_sum_butterfly(gi * dt * xv);            // dB over the block's channels
+        const float cc = wave_sum_butterfly(dv ? dyv * ht[i] : 0.0f);  // dC
+        if (lane == 0) {
+          pB[(tok * ntile + tile) * NS + n] = cb;
+          pC[(tok * ntile + tile) * NS + n] = cc;
+        }
+        g[i] = ab * gi;
+        ht[i] = hprev;
+      }
+      const int par = (int)(t & 1);
+      s_red[par][0][w][lane] = pddt;
+      s_red[par][1][w][lane] = pgb;
+      __syncthreads();  // one barrier per step: the other parity's buffer is free
+      if (w == 0 && dv) {
+        const float ddt = ((s_red[par][0][0][lane] + s_red[par][0][1][lane]) + s_red[par][0][2][lane]) +
+                          s_red[par][0][3][lane];
+        const float sgb = ((s_red[par][1][0][lane] + s_red[par][1][1][lane]) + s_red[par][1][2][lane]) +
+                          s_red[par][1][3][lane];
+        const float ddl = ddt * sig;
+        a.ddelta[tok * H + dc] = ddl;
+        a.dx[tok * H + dc] = __builtin_fmaf(Dd, dyv, dt * sgb);
+        dbias += ddl;
+        dD = __builtin_fmaf(dyv, xv, dD);
+      }
     }
   }
   if (dv) {
