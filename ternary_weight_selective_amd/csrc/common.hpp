@@ -26,6 +26,9 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 template <typename T> __device__ __forceinline__ float ld_act(const T* p);
 template <> __device__ __forceinline__ float ld_act<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld_act<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+// an activation value already in a register (a prefetched raw element) as fp32
+__device__ __forceinline__ float act_f32(float v) { return v; }
+__device__ __forceinline__ float act_f32(bf16_t v) { return bf16_to_f32(v); }
 
 template <typename T> __device__ __forceinline__ void st_act(T* p, float v);
 template <> __device__ __forceinline__ void st_act<float>(float* p, float v) { *p = v; }

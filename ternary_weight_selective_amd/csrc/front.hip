@@ -139,10 +139,13 @@ __global__ __launch_bounds__(512) void k_m1_front(FrontArgs f) {
     }
     norm_quant_rows<4, KPL1>(v, gn1, Dm, f.eps, &s_q1[it & 1][wave * 4 * QS1], QS1, &s_deq1[it & 1][wave * 4], lane);
   };
-  // dt input codes of row block it (from dr in LDS), G-lane groups, one token per group
+  // dt input codes of row block it (from dr in LDS), G-lane groups, one token per group; the
+  // lane's gain is loaded once, here
+  const int Gl = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
+  const int gl = lane & (Gl - 1);
+  const float gdt = f.g_dt ? f.g_dt[gl < R ? gl : 0] : 1.0f;
   auto dt_codes = [&](int it) {
-    const int Gl = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
-    const int tpw = 64 / Gl, gl = lane & (Gl - 1);
+    const int tpw = 64 / Gl;
     for (int t0 = 0; t0 < BR; t0 += 4 * tpw) {
       const int t = t0 + wave * tpw + lane / Gl;
       const int64_t tok = row0(it) + t;
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(512) void k_m1_front(FrontArgs f) {
       const float ms = __fdiv_rn(s, (float)R);
       const float r = __fdiv_rn(1.0f, sqrt_rn(ms + f.eps));
       float xh = v * r;
-      if (f.g_dt) xh = gl < R ? xh * f.g_dt[gl] : 0.0f;
+      if (f.g_dt) xh = gl < R ? xh * gdt : 0.0f;
       float m = fabsf(xh);
       for (int dd = Gl / 2; dd >= 1; dd >>= 1) m = fmaxf(m, __shfl_xor(m, dd, 64));
       const float sigma = __fdiv_rn(127.0f, fmaxf(m, 1e-5f));
@@ -172,14 +175,24 @@ __global__ __launch_bounds__(512) void k_m1_front(FrontArgs f) {
   const bool one_round = ct1 - ct0 <= TPR;
   uint32_t wv[TPR][KPL1];
   const int wrw1 = Dm / 16, wrw2 = Di / 16;
+  // every load is issued (rows past the weight clamped to row 0) before any is selected, so the
+  // loads of a round are in flight together rather than one round trip each
   auto load_round = [&](int c) {
+    uint32_t raw[TPR][KPL1];
 #pragma unroll
     for (int j = 0; j < TPR; ++j) {
       const int n = (c + j) * 16 + lm;
       const bool ok = (c + j < ct1) && n < Di;
-      const uint32_t* wr = f.w_in + (int64_t)n * wrw1 + kq * KPL1;
+      const uint32_t* wr = f.w_in + (int64_t)(ok ? n : 0) * wrw1 + kq * KPL1;
 #pragma unroll
-      for (int ks = 0; ks < KPL1; ++ks) wv[j][ks] = ok ? wr[ks] : 0u;
+      for (int ks = 0; ks < KPL1; ++ks) raw[j][ks] = wr[ks];
+    }
+#pragma unroll
+    for (int j = 0; j < TPR; ++j) {
+      const int n = (c + j) * 16 + lm;
+      const bool ok = (c + j < ct1) && n < Di;
+#pragma unroll
+      for (int ks = 0; ks < KPL1; ++ks) wv[j][ks] = ok ? raw[j][ks] : 0u;
     }
   };
   const int nct2 = (int)cdiv(PW, 16);
@@ -188,8 +201,11 @@ __global__ __launch_bounds__(512) void k_m1_front(FrontArgs f) {
     const int n = cw_ * 16 + lm;
     const bool ok = wave >= 4 && cw_ < nct2 && n < PW;
     const uint32_t* wr = f.w_x + (int64_t)(ok ? n : 0) * wrw2 + kq * KPL2;
+    uint32_t raw[KPL2];
 #pragma unroll
-    for (int ks = 0; ks < KPL2; ++ks) wx[ks] = ok ? wr[ks] : 0u;
+    for (int ks = 0; ks < KPL2; ++ks) raw[ks] = wr[ks];
+#pragma unroll
+    for (int ks = 0; ks < KPL2; ++ks) wx[ks] = ok ? raw[ks] : 0u;
   }
   if (wave >= 4 && ct0 < ct1) load_round(ct0);
   const double sw1 = (double)f.s_in[0], sw2 = (double)f.s_x[0];

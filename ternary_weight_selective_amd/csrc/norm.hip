@@ -19,12 +19,20 @@ __global__ __launch_bounds__(256) void k_norm(const Tin* __restrict__ x, int64_t
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;  // uniform per wave
   const Tin* xr = x + row * ldx;
+  // raw elements first (all loads in flight together), then fp32, the gains alongside
+  Tin raw[KPL];
+  float gn[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int k = lane + 64 * i;
+    raw[i] = (k < K) ? xr[k] : Tin(0);
+    gn[i] = gain ? gain[k < K ? k : 0] : 1.0f;
+  }
   float v[KPL];
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
-    const int k = lane + 64 * i;
-    v[i] = (k < K) ? ld_act(xr + k) : 0.0f;
+    v[i] = act_f32(raw[i]);
     s = __builtin_fmaf(v[i], v[i], s);
   }
   s = wave_sum_butterfly(s);
@@ -35,7 +43,7 @@ __global__ __launch_bounds__(256) void k_norm(const Tin* __restrict__ x, int64_t
   for (int i = 0; i < KPL; ++i) {
     const int k = lane + 64 * i;
     float t = v[i] * r;
-    if (gain) t = (k < K) ? t * gain[k] : 0.0f;
+    if (gain) t = (k < K) ? t * gn[i] : 0.0f;
     v[i] = t;
     m = fmaxf(m, fabsf(t));
   }
@@ -96,9 +104,20 @@ __global__ __launch_bounds__(256) void k_norm_vec(const Tin* __restrict__ x, int
   const bool rv = row < M;  // all waves take part in the barriers
   char* sr = s_row[wv];
   const int nin = K * (int)sizeof(Tin) / 16;
-  if (rv) {
+  if (rv) {  // every 16-byte chunk of the row in flight at once, then into LDS
+    constexpr int CPL = (IN_B / 16 + 63) / 64;
     const v4i* xr = (const v4i*)(x + row * ldx);
-    for (int c = lane; c < nin; c += 64) *(v4i*)(sr + 16 * c) = xr[c];
+    v4i ch[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      ch[j] = c < nin ? xr[c] : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      if (c < nin) *(v4i*)(sr + 16 * c) = ch[j];
+    }
   }
   lds_sync();
   const Tin* se = (const Tin*)sr;

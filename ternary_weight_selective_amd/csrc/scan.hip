@@ -69,6 +69,7 @@ __global__ __launch_bounds__(256) void k_dt_codes(const void* __restrict__ dr, i
   const int gl = lane & (G - 1);
   const int64_t tok = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
   const bool ok = tok < M;
+  const float gv = g ? g[gl < R ? gl : 0] : 1.0f;  // in flight with the row's load
   float v = 0.0f;
   if (ok && gl < R)
     v = bf16 ? bf16_to_f32(((const bf16_t*)dr)[tok * ld + gl]) : ((const float*)dr)[tok * ld + gl];
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(256) void k_dt_codes(const void* __restrict__ dr, i
   const float ms = __fdiv_rn(s, (float)R);
   const float r = __fdiv_rn(1.0f, sqrt_rn(ms + eps));
   float xh = v * r;
-  if (g) xh = gl < R ? xh * g[gl] : 0.0f;
+  if (g) xh = gl < R ? xh * gv : 0.0f;
   float m = fabsf(xh);
   for (int dd = G / 2; dd >= 1; dd >>= 1) m = fmaxf(m, __shfl_xor(m, dd, 64));
   const float sigma = __fdiv_rn(127.0f, fmaxf(m, 1e-5f));
@@ -137,9 +138,12 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   const int64_t d0 = (int64_t)blockIdx.y * CPB;
   const int64_t d = d0 + lane;
   const bool dv = d < Di;
-  // staging role: thread -> (channel lane, steps w, w + 4, ...)
-  const float bias_s = (dv && a.delta_bias) ? a.delta_bias[d] : 0.0f;
-  const float D_s = (dv && a.D) ? a.D[d] : 0.0f;
+  // staging role: thread -> (channel lane, steps w, w + 4, ...).  Lanes past the last channel
+  // take the per-channel parameters of the last channel (their results are never stored), so
+  // the loads below have no lane-dependent branches and are all in flight together.
+  const int64_t dcl = dv ? d : Di - 1;
+  const float bias_s = a.delta_bias ? a.delta_bias[dcl] : 0.0f;
+  const float D_s = a.D ? a.D[dcl] : 0.0f;
   constexpr int cw = 16 * RW;  // code bytes per token
 
   const T* X = (const T*)a.x;
@@ -150,30 +154,35 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   if (FUSED) {
     s_dt = (double)a.s_dt[0];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t wv = 0;
-      if (dv && q < RW) wv = a.w_dt[d * a.w_dt_row_words + q];
-      wdt[q] = unpack16_i8(wv);
-    }
+    for (int q = 0; q < 4; ++q) wdt[q] = unpack16_i8(q < RW ? a.w_dt[dcl * a.w_dt_row_words + q] : 0u);
   }
 
+  // the initial state: h0 for the first chunk, the carry of the previous chunk otherwise
+  const float* hsrc = nullptr;
+  int64_t hoff = 0;
+  if (!LOCAL) {
+    if (chunk == 0) {
+      hsrc = a.h0;
+      hoff = (b * Di + dcl) * NS;
+    } else {
+      hsrc = ch.st;
+      hoff = ((b * ch.nchunks + chunk - 1) * Di + dcl) * NS;
+    }
+  }
   float Al[SPL], h[SPL];
 #pragma unroll
   for (int i = 0; i < SPL; ++i) {
     const int n = w * SPL + i;
-    Al[i] = dv ? a.A[d * NS + n] * LOG2E : 0.0f;
-    float h_init = 0.0f;
-    if (!LOCAL && dv) {
-      if (chunk == 0) h_init = a.h0 ? a.h0[(b * Di + d) * NS + n] : 0.0f;
-      else h_init = ch.st[((b * ch.nchunks + chunk - 1) * Di + d) * NS + n];
-    }
-    h[i] = h_init;
+    Al[i] = a.A[dcl * NS + n] * LOG2E;
+    h[i] = hsrc ? hsrc[hoff + n] : 0.0f;
   }
   float sum_dt = 0.0f;
 
   // prefetch registers for the next tile: x (and delta) of the thread's items, B, C, the
   // items' dt codes (a whole wave reads the same token row) and dequantisation factors
-  float rx[XPT], rd[FUSED ? 1 : XPT], rb[BPT], rc[BPT], rz[GATE ? XPT : 1];
+  // (raw activation elements: a conditional load that is converted at once makes the compiler
+  // wait for it inside the condition, one round trip per load)
+  T rx[XPT], rd[FUSED ? 1 : XPT], rb[BPT], rc[BPT], rz[GATE ? XPT : 1];
   v4i rq[FUSED ? XPT : 1][RWQ];
   double rf[FUSED ? XPT : 1];
   auto load_tile = [&](int64_t t0) {
@@ -183,9 +192,9 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
       const bool okt = t0 + t < te;
       const bool ok = okt && dv;
       const int64_t tok = b * L + t0 + t;
-      rx[i] = ok ? ld_act(X + tok * a.ld_x + d) : 0.0f;
-      if (GATE) rz[GATE ? i : 0] = ok ? ld_act((const T*)a.gate + tok * a.ld_gate + d) : 0.0f;
-      if (!FUSED) rd[FUSED ? 0 : i] = ok ? ld_act(DL + tok * a.ld_delta + d) : 0.0f;
+      rx[i] = ok ? X[tok * a.ld_x + d] : T(0);
+      if (GATE) rz[GATE ? i : 0] = ok ? ((const T*)a.gate)[tok * a.ld_gate + d] : T(0);
+      if (!FUSED) rd[FUSED ? 0 : i] = ok ? DL[tok * a.ld_delta + d] : T(0);
       if (FUSED) {
 #pragma unroll
         for (int q = 0; q < RWQ; ++q)
@@ -198,8 +207,8 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
       const int e = tid + 256 * i, t = e / NS, n = e % NS;
       const bool ok = (e < TT * NS) && (t0 + t < te);
       const int64_t tok = b * L + t0 + t;
-      rb[i] = ok ? ld_act((const T*)a.Bm + tok * a.ld_B + n) : 0.0f;
-      rc[i] = (ok && !LOCAL) ? ld_act((const T*)a.Cm + tok * a.ld_C + n) : 0.0f;
+      rb[i] = ok ? ((const T*)a.Bm)[tok * a.ld_B + n] : T(0);
+      rc[i] = (ok && !LOCAL) ? ((const T*)a.Cm)[tok * a.ld_C + n] : T(0);
     }
   };
 
@@ -229,9 +238,9 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int t = w + 4 * i;
-      const float xv = rx[i];
+      const float xv = act_f32(rx[i]);
       xcur[i] = xv;
-      if (GATE) zcur[GATE ? i : 0] = rz[GATE ? i : 0];
+      if (GATE) zcur[GATE ? i : 0] = act_f32(rz[GATE ? i : 0]);
       float dtv;
       if (FUSED) {
         int acc = 0;
@@ -241,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
           for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(rq[FUSED ? i : 0][q][j], wdt[q][j], acc, false);
         dtv = (float)((s_dt * (double)acc) * rf[FUSED ? i : 0]);
       } else {
-        dtv = rd[FUSED ? 0 : i];
+        dtv = act_f32(rd[FUSED ? 0 : i]);
       }
       dtv += bias_s;
       if (a.softplus) dtv = softplus_f(dtv);
@@ -251,8 +260,8 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
     for (int i = 0; i < BPT; ++i) {
       const int e = tid + 256 * i;
       if (e < TT * NS) {
-        s_B[buf][e / NS][e % NS] = rb[i];
-        if (!LOCAL) s_C[LOCAL ? 0 : buf][LOCAL ? 0 : e / NS][e % NS] = rc[i];
+        s_B[buf][e / NS][e % NS] = act_f32(rb[i]);
+        if (!LOCAL) s_C[LOCAL ? 0 : buf][LOCAL ? 0 : e / NS][e % NS] = act_f32(rc[i]);
       }
     }
     // 2. next tile in flight
