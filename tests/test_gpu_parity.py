@@ -79,6 +79,7 @@ BL_CASES = [  # (m, k, n, group, act_bits, x dtype, y dtype)
     (1, 100, 70, 0, 8, "f32", "f32"),        # one row, ragged k
     (100, 2048, 4416, 0, 8, "bf16", "bf16"),  # mamba2_a8 in_proj (tiled int8 path)
     (77, 4096, 2048, 0, 8, "bf16", "bf16"),   # mamba2_a8 out_proj
+    (50, 1156, 130, 0, 8, "f32", "f32"),      # large-tile int8 path, odd k-step count, k % 16 != 0
 ]
 
 
@@ -111,7 +112,8 @@ def test_bitlinear_parity(m, k, n, group, bits, xd, yd):
     assert rel_err(host(y), ref) <= TOL[yd]
 
 
-@pytest.mark.parametrize("m,k,n", [(256, 256, 512), (77, 1024, 64), (64, 2048, 4416)])
+@pytest.mark.parametrize("m,k,n", [(256, 256, 512), (77, 1024, 64), (64, 2048, 4416),
+                                   (70, 1088, 200), (40, 64, 96), (300, 1216, 260)])  # odd k-step counts
 def test_bitlinear_int32_from_oracle_codes(m, k, n):
     """Stage-wise S3: the GPU contraction fed the oracle's exact int8 codes and absmax."""
     g = wl.rng(k + n)
