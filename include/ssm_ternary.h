@@ -333,10 +333,11 @@ ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w,
  *   dD = sum dy x;  d bias = sum d delta;  dh0 = a_0 g_0.
  * Inputs as ssm_selective_scan_fwd (act_dtype x, delta, Bm, Cm; fp32 A [H, N], D, bias, h0)
  * plus dy fp32 [B, L, ld_dy].  Outputs fp32, dense: dx and ddelta [B, L, H], dA [H, N],
- * dB and dC [B, L, N]; dD, dbias [H] and dh0 [B, H, N] nullable.  The states of the whole
- * sequence are re-computed into the workspace (B L H N fp32 plus partial sums):
- * ssm_selective_scan_bwd_workspace_bytes().  Sums over sequences and channel tiles are taken
- * in a fixed order (results do not depend on timing).
+ * dB and dC [B, L, N]; dD, dbias [H] and dh0 [B, H, N] nullable.  Time is processed in chunks
+ * of 256 / d_state steps; the workspace holds the states and adjoint carries at the chunk
+ * boundaries (2 B nchunks H N fp32) and partial sums: ssm_selective_scan_bwd_workspace_bytes().
+ * Sums over sequences, chunks and channel tiles are taken in a fixed order (results do not
+ * depend on timing).  seqlen is limited to 65535 chunks.
  * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIGN,
  * SSM_ERR_WORKSPACE, SSM_ERR_DEVICE.
  */

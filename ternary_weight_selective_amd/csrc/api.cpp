@@ -302,6 +302,9 @@ ssm_status scan_bwd_check(const ssm_scan_bwd_args* a, ScanBwdArgs* o) {
   const int64_t n = a->d_state;
   if (n != 4 && n != 8 && n != 16 && n != 32 && n != 64) return fail(SSM_ERR_UNSUPPORTED, "scan bwd: d_state %lld", (long long)n);
   if (a->batch > 65535) return fail(SSM_ERR_UNSUPPORTED, "scan bwd: batch above 65535");
+  if ((a->seqlen + 256 / n - 1) / (256 / n) > 65535)  // time chunks of 256 / d_state steps
+    return fail(SSM_ERR_UNSUPPORTED, "scan bwd: seqlen above %lld for d_state %lld", (long long)(65535 * (256 / n)),
+                (long long)n);
   if (a->ld_x < a->nheads || a->ld_delta < a->nheads || a->ld_B < n || a->ld_C < n || a->ld_dy < a->nheads)
     return fail(SSM_ERR_SHAPE, "scan bwd: a row stride is smaller than its row");
   if (a->batch * a->seqlen > 0 && (!a->x || !a->delta || !a->A || !a->Bm || !a->Cm || !a->dy || !a->dx ||

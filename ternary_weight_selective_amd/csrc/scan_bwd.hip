@@ -2,10 +2,23 @@
 // trained end to end): the exact reverse-mode derivative of the recurrence the forward kernel
 // evaluates.  With dt_t = softplus(delta_t + bias), a_t = exp(dt_t A), h_t = a_t h_{t-1} +
 // dt_t x_t B_t, y_t = C_t . h_t + D x_t, the state adjoint is g_t = C_t dy_t + a_{t+1} g_{t+1}.
-// Pass 1 re-runs the forward and stores every state; pass 2 walks time backwards; pass 3 sums,
-// in a fixed order, the partial gradients of parameters that several blocks share (A, D and the
-// delta bias over sequences; B and C over channel tiles).  Thread layout as in the forward: a
-// block owns 64 channels of one sequence (lane = channel), wave w the states w NS/4 ...
+//
+// Time is cut into chunks of LC steps and every chunk of every (sequence, channel tile) is a
+// block of its own, so the work is spread over B x tiles x chunks blocks.  Both recurrences are
+// linear in their carried value, so each chunk's contribution can be formed from a zero carry
+// and the chunks joined afterwards (the forward scan's chunking, applied to both directions):
+//   1. local: per chunk, the state reached from a zero state (S), the sum of dt (the chunk's
+//      decay is exp(A sum dt)) and the adjoint carry leaving the chunk at its start from a zero
+//      carry at its end (GL);
+//   2. combine: per (sequence, channel, state), in chunk order, S becomes the state at the end
+//      of each chunk (starting from h0), then in reverse order GL becomes the carry entering
+//      each chunk at its end; what leaves chunk 0 is dh0;
+//   3. chunk: per chunk, the states are re-run from the state entering it (kept in registers,
+//      one per step and state) and time walked backwards with the true carry, giving dx, d
+//      delta and the partial sums of dA, dD, d bias (per chunk) and of dB, dC (per channel tile);
+//   4. sums of those partials in a fixed order (results do not depend on timing).
+// Thread layout as in the forward: a block owns 64 channels (lane = channel), wave w the states
+// w NS/4 .. w NS/4 + NS/4 - 1.  A chunk's inputs are staged once into LDS.
 #include "scan_bwd.hpp"
 
 namespace ssm {
@@ -25,190 +38,266 @@ __device__ __forceinline__ float softplus_b(float v) {
   return v > 20.0f ? v : r;
 }
 
-// steps per register tile of the two passes (the loads of the next tile are in flight while the
-// current one is computed)
-template <int SPL> constexpr int bwd_tile() { return SPL >= 16 ? 1 : (SPL >= 8 ? 2 : (SPL >= 4 ? 4 : 8)); }
+// steps per chunk: the chunk's states (LC x NS/4 per lane) stay in registers in pass 3
+template <int NS> constexpr int bwd_chunk() {
+  return NS >= 64 ? 4 : (NS >= 32 ? 8 : (NS >= 16 ? 16 : (NS >= 8 ? 32 : 64)));
+}
 
-// pass 1: the forward recurrence, storing h_t for every step: hs[b][t][d][n]
-template <int NS, typename T>
-__global__ __launch_bounds__(256) void k_scan_save(ScanBwdArgs a, float* __restrict__ hs) {
-  constexpr int SPL = NS / 4, TT = bwd_tile<SPL>();
+// A chunk's inputs in LDS: per (step, channel) dt (0 past the end), softplus'(pre), x and dy
+// (0 for channels past the last), per (step, state) B and C.
+template <int NS, int LC> struct ChunkLds {
+  float dt[LC][kCPBb], sig[LC][kCPBb], x[LC][kCPBb], dy[LC][kCPBb];
+  float B[LC][NS], C[LC][NS];
+};
+
+template <int NS, int LC, typename T>
+__device__ __forceinline__ void stage_chunk(const ScanBwdArgs& a, ChunkLds<NS, LC>& s, int64_t b, int64_t dc, bool dv,
+                                            int64_t t0, int64_t t1, float bias) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t b = blockIdx.x, d = (int64_t)blockIdx.y * kCPBb + lane, H = a.H, L = a.L;
-  if (d >= H) return;  // no barriers in this kernel
-  const float bias = a.delta_bias ? a.delta_bias[d] : 0.0f;
-  float h[SPL], Al[SPL];
+  const int64_t L = a.L;
 #pragma unroll
-  for (int i = 0; i < SPL; ++i) {
-    const int n = w * SPL + i;
-    Al[i] = a.A[d * NS + n] * kLog2eB;
-    h[i] = a.h0 ? a.h0[(b * H + d) * NS + n] : 0.0f;
+  for (int j = 0; j < (LC + 3) / 4; ++j) {
+    const int u = w + 4 * j;
+    if (u >= LC) break;
+    const int64_t t = t0 + u;
+    const bool ok = t < t1;
+    const int64_t tok = b * L + (ok ? t : t0);  // past the end: a valid row, zeroed below
+    const float pre = ld_act((const T*)a.delta + tok * a.ld_delta + dc) + bias;
+    float dt, sg;
+    if (a.softplus) {
+      sg = pre > 20.0f ? 1.0f : 1.0f / (1.0f + __builtin_amdgcn_exp2f(-pre * kLog2eB));
+      dt = softplus_b(pre);
+    } else {
+      sg = 1.0f;
+      dt = pre;
+    }
+    const float xv = ld_act((const T*)a.x + tok * a.ld_x + dc);
+    const float dyv = a.dy[tok * a.ld_dy + dc];
+    s.dt[u][lane] = ok ? dt : 0.0f;
+    s.sig[u][lane] = sg;
+    s.x[u][lane] = (ok && dv) ? xv : 0.0f;
+    s.dy[u][lane] = (ok && dv) ? dyv : 0.0f;
   }
-  float rd[TT], rx[TT], rb[TT][SPL];
-  auto load = [&](int64_t t0) {
-#pragma unroll
-    for (int u = 0; u < TT; ++u) {
-      const int64_t t = t0 + u;
-      const bool ok = t < L;
-      const int64_t tok = b * L + (ok ? t : 0);
-      rd[u] = ok ? ld_act((const T*)a.delta + tok * a.ld_delta + d) : 0.0f;
-      rx[u] = ok ? ld_act((const T*)a.x + tok * a.ld_x + d) : 0.0f;
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) rb[u][i] = ok ? ld_act((const T*)a.Bm + tok * a.ld_B + w * SPL + i) : 0.0f;
-    }
-  };
-  load(0);
-  for (int64_t t0 = 0; t0 < L; t0 += TT) {
-    float cd[TT], cx[TT], cb[TT][SPL];
-#pragma unroll
-    for (int u = 0; u < TT; ++u) {
-      cd[u] = rd[u];
-      cx[u] = rx[u];
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) cb[u][i] = rb[u][i];
-    }
-    if (t0 + TT < L) load(t0 + TT);
-#pragma unroll
-    for (int u = 0; u < TT; ++u) {
-      const int64_t t = t0 + u;
-      if (t >= L) break;
-      const float pre = cd[u] + bias;
-      const float dt = a.softplus ? softplus_b(pre) : pre;
-      const float dx = dt * cx[u];
-      float* hr = hs + ((b * L + t) * H + d) * NS + w * SPL;
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) {
-        const float ab = __builtin_amdgcn_exp2f(dt * Al[i]);
-        h[i] = __builtin_fmaf(ab, h[i], dx * cb[u][i]);
-        hr[i] = h[i];
-      }
-    }
+  for (int e = threadIdx.x; e < LC * NS; e += 256) {
+    const int u = e / NS, n = e % NS;
+    const int64_t t = t0 + u;
+    const int64_t tok = b * L + (t < t1 ? t : t0);
+    s.B[u][n] = ld_act((const T*)a.Bm + tok * a.ld_B + n);
+    s.C[u][n] = ld_act((const T*)a.Cm + tok * a.ld_C + n);
   }
 }
 
-// pass 2: reverse time, TT steps per register tile (TT <= 2: the reverse step holds more)
+struct ChunkBufs {
+  float *S, *SD, *GL;      // [B][NC][H][NS], [B][NC][H], [B][NC][H][NS]
+  float *pB, *pC;          // [B L][tiles][NS]
+  float *pA, *pD, *pbias;  // [B][NC][H][NS], [B][NC][H], [B][NC][H]
+  int64_t nc;
+};
+
+// pass 1: per chunk, the state from a zero state, sum dt, and the adjoint carry from a zero carry
 template <int NS, typename T>
-__global__ __launch_bounds__(256) void k_scan_rev(ScanBwdArgs a, const float* __restrict__ hs,
-                                                  float* __restrict__ pB, float* __restrict__ pC,
-                                                  float* __restrict__ pA, float* __restrict__ pD,
-                                                  float* __restrict__ pbias) {
-  constexpr int SPL = NS / 4, TT = bwd_tile<SPL>() > 2 ? 2 : bwd_tile<SPL>();
-  __shared__ float s_red[2][2][4][kCPBb];  // [step parity][d dt, sum g B][wave][channel]
+__global__ __launch_bounds__(256) void k_bwd_local(ScanBwdArgs a, ChunkBufs cb) {
+  constexpr int SPL = NS / 4, LC = bwd_chunk<NS>();
+  __shared__ ChunkLds<NS, LC> s;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t b = blockIdx.x, tile = blockIdx.y, d = tile * kCPBb + lane, H = a.H, L = a.L;
-  const int64_t ntile = gridDim.y;
+  const int64_t b = blockIdx.x, c = blockIdx.z, H = a.H, L = a.L;
+  const int64_t d = (int64_t)blockIdx.y * kCPBb + lane;
   const bool dv = d < H;
-  const int64_t dc = dv ? d : H - 1;  // lanes past the last channel run on zeros
+  const int64_t dc = dv ? d : H - 1;
+  const int64_t t0 = c * LC, t1 = (t0 + LC < L) ? t0 + LC : L;
   const float bias = a.delta_bias ? a.delta_bias[dc] : 0.0f;
-  const float Dd = a.D ? a.D[dc] : 0.0f;
-  float Av[SPL], Al[SPL], g[SPL], dA[SPL];
+  float Al[SPL];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) Al[i] = a.A[dc * NS + w * SPL + i] * kLog2eB;
+  stage_chunk<NS, LC, T>(a, s, b, dc, dv, t0, t1, bias);
+  __syncthreads();
+  float h[SPL], g[SPL], sdt = 0.0f;
 #pragma unroll
   for (int i = 0; i < SPL; ++i) {
-    Av[i] = a.A[dc * NS + w * SPL + i];
+    h[i] = 0.0f;
+    g[i] = 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < LC; ++u) {  // steps past the end have dt = 0: a = 1, nothing added
+    const float dt = s.dt[u][lane], dx = dt * s.x[u][lane];
+    sdt += dt;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      h[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * Al[i]), h[i], dx * s.B[u][w * SPL + i]);
+  }
+#pragma unroll
+  for (int u = LC - 1; u >= 0; --u) {  // past the end: dy = 0 and a = 1, the carry passes through
+    const float dt = s.dt[u][lane], dyv = s.dy[u][lane];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i)
+      g[i] = __builtin_amdgcn_exp2f(dt * Al[i]) * __builtin_fmaf(s.C[u][w * SPL + i], dyv, g[i]);
+  }
+  if (dv) {
+    const int64_t si = ((b * cb.nc + c) * H + d) * NS + w * SPL;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      cb.S[si + i] = h[i];
+      cb.GL[si + i] = g[i];
+    }
+    if (w == 0) cb.SD[(b * cb.nc + c) * H + d] = sdt;
+  }
+}
+
+// pass 2: per (sequence, channel, state), the chunks joined in order: S[c] becomes the state at
+// the end of chunk c, GL[c] the adjoint carry entering chunk c at its end; dh0 what leaves chunk 0
+__global__ __launch_bounds__(256) void k_bwd_combine(const float* __restrict__ A, const float* __restrict__ h0,
+                                                     ChunkBufs cb, int64_t B, int64_t H, int NS,
+                                                     float* __restrict__ dh0) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * H * NS) return;
+  const int64_t b = i / (H * NS), dn = i % (H * NS), d = dn / NS;
+  const float a2 = A[dn] * kLog2eB;
+  const int64_t sb = b * cb.nc * H * NS + dn, db = b * cb.nc * H + d;  // chunk 0 of this element
+  constexpr int G = 8;  // chunks whose loads are in flight together
+  float h = h0 ? h0[i] : 0.0f;
+  for (int64_t c0 = 0; c0 < cb.nc; c0 += G) {
+    float sv[G], P[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int64_t c = c0 + u < cb.nc ? c0 + u : cb.nc - 1;
+      sv[u] = cb.S[sb + c * H * NS];
+      P[u] = cb.SD[db + c * H];
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (c0 + u >= cb.nc) break;
+      h = __builtin_fmaf(__builtin_amdgcn_exp2f(a2 * P[u]), h, sv[u]);
+      cb.S[sb + (c0 + u) * H * NS] = h;
+    }
+  }
+  float gam = 0.0f;
+  for (int64_t c1 = cb.nc - 1; c1 >= 0; c1 -= G) {  // chunks c1, c1 - 1, ..., c1 - G + 1
+    float gv[G], P[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int64_t c = c1 - u >= 0 ? c1 - u : 0;
+      gv[u] = cb.GL[sb + c * H * NS];
+      P[u] = cb.SD[db + c * H];
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (c1 - u < 0) break;
+      cb.GL[sb + (c1 - u) * H * NS] = gam;
+      gam = __builtin_fmaf(__builtin_amdgcn_exp2f(a2 * P[u]), gam, gv[u]);
+    }
+  }
+  if (dh0) dh0[i] = gam;
+}
+
+// pass 3: per chunk, states re-run from the state entering it, then time walked backwards
+template <int NS, typename T>
+__global__ __launch_bounds__(256) void k_bwd_chunk(ScanBwdArgs a, ChunkBufs cb) {
+  constexpr int SPL = NS / 4, LC = bwd_chunk<NS>();
+  __shared__ ChunkLds<NS, LC> s;
+  __shared__ float s_red[2][2][4][kCPBb];  // [step parity][d dt, sum g B][wave][channel]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t b = blockIdx.x, tile = blockIdx.y, c = blockIdx.z, H = a.H, L = a.L;
+  const int64_t ntile = gridDim.y;
+  const int64_t d = tile * kCPBb + lane;
+  const bool dv = d < H;
+  const int64_t dc = dv ? d : H - 1;  // lanes past the last channel run on zeros
+  const int64_t t0 = c * LC, t1 = (t0 + LC < L) ? t0 + LC : L;
+  const float bias = a.delta_bias ? a.delta_bias[dc] : 0.0f;
+  const float Dd = a.D ? a.D[dc] : 0.0f;
+  float Av[SPL], Al[SPL], h[SPL], g[SPL], dA[SPL];
+  const int64_t si = ((b * cb.nc + c) * H + dc) * NS + w * SPL;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int n = w * SPL + i;
+    Av[i] = a.A[dc * NS + n];
     Al[i] = Av[i] * kLog2eB;
-    g[i] = 0.0f;  // a_{t+1} g_{t+1}
+    h[i] = c > 0 ? cb.S[si - H * NS + i] : (a.h0 ? a.h0[(b * H + dc) * NS + n] : 0.0f);
+    g[i] = dv ? cb.GL[si + i] : 0.0f;  // a_{t+1} g_{t+1} entering the chunk's last step
     dA[i] = 0.0f;
   }
+  stage_chunk<NS, LC, T>(a, s, b, dc, dv, t0, t1, bias);
+  __syncthreads();
+  // the chunk's states: hp[u] = h_{t0 + u - 1}
+  float hp[LC][SPL];
+#pragma unroll
+  for (int u = 0; u < LC; ++u) {
+    const float dt = s.dt[u][lane], dx = dt * s.x[u][lane];
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      hp[u][i] = h[i];
+      h[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * Al[i]), h[i], dx * s.B[u][w * SPL + i]);
+    }
+  }
   float dD = 0.0f, dbias = 0.0f;
-  // per step: pre-activation dt, x, dy, B, C and h_{t-1}; h_t is the previous step's h_{t-1}
-  float rd[TT], rx[TT], ry[TT], rB[TT][SPL], rC[TT][SPL], rh[TT][SPL];
-  auto load = [&](int64_t t1) {  // steps t1, t1 - 1, ..., t1 - TT + 1
+  // h holds h_t of the step being processed (steps past the end left it unchanged)
 #pragma unroll
-    for (int u = 0; u < TT; ++u) {
-      const int64_t t = t1 - u;
-      const bool ok = t >= 0;
-      const int64_t tok = b * L + (ok ? t : 0);
-      rd[u] = ok ? ld_act((const T*)a.delta + tok * a.ld_delta + dc) : 0.0f;
-      rx[u] = (ok && dv) ? ld_act((const T*)a.x + tok * a.ld_x + dc) : 0.0f;
-      ry[u] = (ok && dv) ? a.dy[tok * a.ld_dy + dc] : 0.0f;
+  for (int u = LC - 1; u >= 0; --u) {
+    const int64_t t = t0 + u;
+    if (t >= t1) continue;  // the same for the whole block
+    const int64_t tok = b * L + t;
+    const float dt = s.dt[u][lane], sig = s.sig[u][lane];
+    const float xv = s.x[u][lane], dyv = s.dy[u][lane];
+    float pddt = 0.0f, pgb = 0.0f;
 #pragma unroll
-      for (int i = 0; i < SPL; ++i) {
-        const int n = w * SPL + i;
-        rB[u][i] = ok ? ld_act((const T*)a.Bm + tok * a.ld_B + n) : 0.0f;
-        rC[u][i] = ok ? ld_act((const T*)a.Cm + tok * a.ld_C + n) : 0.0f;
-        rh[u][i] = t > 0 ? hs[((tok - 1) * H + dc) * NS + n]
-                         : ((ok && a.h0) ? a.h0[(b * H + dc) * NS + n] : 0.0f);
+    for (int i = 0; i < SPL; ++i) {
+      const int n = w * SPL + i;
+      const float Bn = s.B[u][n], Cn = s.C[u][n];
+      const float hprev = hp[u][i];
+      const float ab = __builtin_amdgcn_exp2f(dt * Al[i]);
+      const float gi = dv ? __builtin_fmaf(Cn, dyv, g[i]) : 0.0f;
+      const float gha = gi * hprev * ab;
+      pddt = __builtin_fmaf(gha, Av[i], __builtin_fmaf(gi * xv, Bn, pddt));
+      pgb = __builtin_fmaf(gi, Bn, pgb);
+      dA[i] = __builtin_fmaf(gha, dt, dA[i]);
+      const float sb = wave_sum_butterfly(gi * dt * xv);  // dB over the block's channels
+      const float sc = wave_sum_butterfly(dyv * h[i]);    // dC (dy is 0 past the last channel)
+      if (lane == 0) {
+        cb.pB[(tok * ntile + tile) * NS + n] = sb;
+        cb.pC[(tok * ntile + tile) * NS + n] = sc;
       }
+      g[i] = ab * gi;
+      h[i] = hprev;
     }
-  };
-  float ht[SPL];  // h_t of the current step
-#pragma unroll
-  for (int i = 0; i < SPL; ++i) ht[i] = hs[((b * L + L - 1) * H + dc) * NS + w * SPL + i];
-  load(L - 1);
-  for (int64_t t1 = L - 1; t1 >= 0; t1 -= TT) {
-    float cd[TT], cx[TT], cy[TT], cB[TT][SPL], cC[TT][SPL], ch[TT][SPL];
-#pragma unroll
-    for (int u = 0; u < TT; ++u) {
-      cd[u] = rd[u]; cx[u] = rx[u]; cy[u] = ry[u];
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) { cB[u][i] = rB[u][i]; cC[u][i] = rC[u][i]; ch[u][i] = rh[u][i]; }
-    }
-    if (t1 - TT >= 0) load(t1 - TT);
-#pragma unroll
-    for (int u = 0; u < TT; ++u) {
-      const int64_t t = t1 - u;
-      if (t < 0) break;
-      const int64_t tok = b * L + t;
-      const float pre = cd[u] + bias;
-      float dt, sig;
-      if (a.softplus) {
-        sig = pre > 20.0f ? 1.0f : 1.0f / (1.0f + __builtin_amdgcn_exp2f(-pre * kLog2eB));
-        dt = softplus_b(pre);
-      } else {
-        sig = 1.0f;
-        dt = pre;
-      }
-      const float xv = cx[u], dyv = cy[u];
-      float pddt = 0.0f, pgb = 0.0f;
-#pragma unroll
-      for (int i = 0; i < SPL; ++i) {
-        const int n = w * SPL + i;
-        const float Bn = cB[u][i], Cn = cC[u][i];
-        const float hprev = ch[u][i];
-        const float ab = __builtin_amdgcn_exp2f(dt * Al[i]);
-        const float gi = dv ? __builtin_fmaf(Cn, dyv, g[i]) : 0.0f;
-        const float gha = gi * hprev * ab;
-        pddt = __builtin_fmaf(gha, Av[i], __builtin_fmaf(gi * xv, Bn, pddt));
-        pgb = __builtin_fmaf(gi, Bn, pgb);
-        dA[i] = __builtin_fmaf(gha, dt, dA[i]);
-        const float cb = wave_sum_butterfly(gi * dt * xv);            // dB over the block's channels
-        const float cc = wave_sum_butterfly(dv ? dyv * ht[i] : 0.0f);  // dC
-        if (lane == 0) {
-          pB[(tok * ntile + tile) * NS + n] = cb;
-          pC[(tok * ntile + tile) * NS + n] = cc;
-        }
-        g[i] = ab * gi;
-        ht[i] = hprev;
-      }
-      const int par = (int)(t & 1);
-      s_red[par][0][w][lane] = pddt;
-      s_red[par][1][w][lane] = pgb;
-      __syncthreads();  // one barrier per step: the other parity's buffer is free
-      if (w == 0 && dv) {
-        const float ddt = ((s_red[par][0][0][lane] + s_red[par][0][1][lane]) + s_red[par][0][2][lane]) +
-                          s_red[par][0][3][lane];
-        const float sgb = ((s_red[par][1][0][lane] + s_red[par][1][1][lane]) + s_red[par][1][2][lane]) +
-                          s_red[par][1][3][lane];
-        const float ddl = ddt * sig;
-        a.ddelta[tok * H + dc] = ddl;
-        a.dx[tok * H + dc] = __builtin_fmaf(Dd, dyv, dt * sgb);
-        dbias += ddl;
-        dD = __builtin_fmaf(dyv, xv, dD);
-      }
+    const int par = (int)(t & 1);
+    s_red[par][0][w][lane] = pddt;
+    s_red[par][1][w][lane] = pgb;
+    __syncthreads();  // one barrier per step: the other parity's buffer is free
+    if (w == 0 && dv) {
+      const float ddt = ((s_red[par][0][0][lane] + s_red[par][0][1][lane]) + s_red[par][0][2][lane]) +
+                        s_red[par][0][3][lane];
+      const float sgb = ((s_red[par][1][0][lane] + s_red[par][1][1][lane]) + s_red[par][1][2][lane]) +
+                        s_red[par][1][3][lane];
+      const float ddl = ddt * sig;
+      a.ddelta[tok * H + dc] = ddl;
+      a.dx[tok * H + dc] = __builtin_fmaf(Dd, dyv, dt * sgb);
+      dbias += ddl;
+      dD = __builtin_fmaf(dyv, xv, dD);
     }
   }
   if (dv) {
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) {
-      const int n = w * SPL + i;
-      pA[(b * H + dc) * NS + n] = dA[i];
-      if (a.dh0) a.dh0[(b * H + dc) * NS + n] = g[i];
-    }
+    for (int i = 0; i < SPL; ++i) cb.pA[si + i] = dA[i];
     if (w == 0) {
-      pD[b * H + dc] = dD;
-      pbias[b * H + dc] = dbias;
+      cb.pD[(b * cb.nc + c) * H + dc] = dD;
+      cb.pbias[(b * cb.nc + c) * H + dc] = dbias;
     }
   }
+}
+
+// sum of in[(base + m) * inner + i] over m in [m0, m1), m ascending, eight loads in flight
+__device__ __forceinline__ float sum_rows(const float* __restrict__ in, int64_t base, int64_t m0, int64_t m1,
+                                          int64_t inner, int64_t i) {
+  float s = 0.0f;
+  int64_t m = m0;
+  for (; m + 8 <= m1; m += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = in[(base + m + u) * inner + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; m < m1; ++m) s += in[(base + m) * inner + i];
+  return s;
 }
 
 // out[o, i] = sum over m of in[o, m, i], m ascending
@@ -217,28 +306,48 @@ __global__ __launch_bounds__(256) void k_sum_mid(const float* __restrict__ in, i
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= outer * inner) return;
   const int64_t o = e / inner, i = e % inner;
-  float s = 0.0f;
-  for (int64_t m = 0; m < mid; ++m) s += in[(o * mid + m) * inner + i];
-  out[e] = s;
+  out[e] = sum_rows(in, o * mid, 0, mid, inner, i);
+}
+
+// first level of a long sum: part[g, i] = sum over m in segment g (seg rows) of in[m, i]
+__global__ __launch_bounds__(256) void k_sum_seg(const float* __restrict__ in, int64_t mid, int64_t inner, int64_t seg,
+                                                 float* __restrict__ part) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x, g = blockIdx.y;
+  if (i >= inner) return;
+  const int64_t m0 = g * seg, m1 = (m0 + seg < mid) ? m0 + seg : mid;
+  part[g * inner + i] = sum_rows(in, 0, m0, m1, inner, i);
 }
 
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
+int chunk_len(int64_t N) {
+  switch (N) {
+    case 4: return bwd_chunk<4>();
+    case 8: return bwd_chunk<8>();
+    case 16: return bwd_chunk<16>();
+    case 32: return bwd_chunk<32>();
+    default: return bwd_chunk<64>();
+  }
+}
+
 struct BwdPlan {
-  size_t off_hs, off_pB, off_pC, off_pA, off_pD, off_pbias, total;
-  int64_t ntile;
+  size_t off_S, off_SD, off_GL, off_pB, off_pC, off_pA, off_pD, off_pbias, total;
+  int64_t ntile, nc;
 };
 BwdPlan plan_bwd(const ScanBwdArgs& a) {
   BwdPlan p{};
   p.ntile = cdiv(a.H, kCPBb);
-  const int64_t M = a.batch * a.L;
+  p.nc = cdiv(a.L, chunk_len(a.N));
+  const int64_t M = a.batch * a.L, BC = a.batch * p.nc;
   size_t off = 0;
-  p.off_hs = off; off += al256((size_t)M * a.H * a.N * 4);
+  p.off_S = off; off += al256((size_t)BC * a.H * a.N * 4);
+  p.off_SD = off; off += al256((size_t)BC * a.H * 4);
+  p.off_GL = off; off += al256((size_t)BC * a.H * a.N * 4);
   p.off_pB = off; off += al256((size_t)M * p.ntile * a.N * 4);
   p.off_pC = off; off += al256((size_t)M * p.ntile * a.N * 4);
-  p.off_pA = off; off += al256((size_t)a.batch * a.H * a.N * 4);
-  p.off_pD = off; off += al256((size_t)a.batch * a.H * 4);
-  p.off_pbias = off; off += al256((size_t)a.batch * a.H * 4);
+  p.off_pA = off; off += al256((size_t)BC * a.H * a.N * 4);
+  p.off_pD = off; off += al256((size_t)BC * a.H * 4);
+  p.off_pbias = off; off += al256((size_t)BC * a.H * 4);
   p.total = off;
   return p;
 }
@@ -247,26 +356,42 @@ template <int NS, typename T>
 hipError_t launch_bwd_t(const ScanBwdArgs& a, void* ws, hipStream_t s) {
   const BwdPlan p = plan_bwd(a);
   char* base = (char*)ws;
-  float* hs = (float*)(base + p.off_hs);
-  float* pB = (float*)(base + p.off_pB);
-  float* pC = (float*)(base + p.off_pC);
-  float* pA = (float*)(base + p.off_pA);
-  float* pD = (float*)(base + p.off_pD);
-  float* pb = (float*)(base + p.off_pbias);
-  const dim3 grid((unsigned)a.batch, (unsigned)p.ntile), block(256);
-  hipLaunchKernelGGL((k_scan_save<NS, T>), grid, block, 0, s, a, hs);
-  hipLaunchKernelGGL((k_scan_rev<NS, T>), grid, block, 0, s, a, hs, pB, pC, pA, pD, pb);
+  ChunkBufs cb{};
+  cb.S = (float*)(base + p.off_S);
+  cb.SD = (float*)(base + p.off_SD);
+  cb.GL = (float*)(base + p.off_GL);
+  cb.pB = (float*)(base + p.off_pB);
+  cb.pC = (float*)(base + p.off_pC);
+  cb.pA = (float*)(base + p.off_pA);
+  cb.pD = (float*)(base + p.off_pD);
+  cb.pbias = (float*)(base + p.off_pbias);
+  cb.nc = p.nc;
+  const dim3 grid((unsigned)a.batch, (unsigned)p.ntile, (unsigned)p.nc), block(256);
+  hipLaunchKernelGGL((k_bwd_local<NS, T>), grid, block, 0, s, a, cb);
+  const int64_t ne = a.batch * a.H * NS;
+  hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)cdiv(ne, 256)), dim3(256), 0, s, a.A, a.h0, cb, a.batch, a.H, NS,
+                     a.dh0);
+  hipLaunchKernelGGL((k_bwd_chunk<NS, T>), grid, block, 0, s, a, cb);
   const int64_t M = a.batch * a.L;
+  // fixed-order sums; a long one (over sequences x chunks) in segments of 32 first, the
+  // segment sums going to the chunk states' region, which is free once pass 3 has run
   auto sum = [&](const float* in, int64_t outer, int64_t mid, int64_t inner, float* out) {
     if (!out) return;
+    if (outer == 1 && mid > 64) {
+      const int64_t seg = 32, ns = cdiv(mid, seg);
+      hipLaunchKernelGGL(k_sum_seg, dim3((unsigned)cdiv(inner, 256), (unsigned)ns), dim3(256), 0, s, in, mid, inner,
+                         seg, cb.S);
+      in = cb.S;
+      mid = ns;
+    }
     hipLaunchKernelGGL(k_sum_mid, dim3((unsigned)cdiv(outer * inner, 256)), dim3(256), 0, s, in, outer, mid, inner,
                        out);
   };
-  sum(pB, M, p.ntile, NS, a.dB);
-  sum(pC, M, p.ntile, NS, a.dC);
-  sum(pA, 1, a.batch, a.H * NS, a.dA);
-  sum(pD, 1, a.batch, a.H, a.dD);
-  sum(pb, 1, a.batch, a.H, a.dbias);
+  sum(cb.pB, M, p.ntile, NS, a.dB);
+  sum(cb.pC, M, p.ntile, NS, a.dC);
+  sum(cb.pA, 1, a.batch * p.nc, a.H * NS, a.dA);
+  sum(cb.pD, 1, a.batch * p.nc, a.H, a.dD);
+  sum(cb.pbias, 1, a.batch * p.nc, a.H, a.dbias);
   return hipGetLastError();
 }
 

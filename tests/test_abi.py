@@ -290,11 +290,13 @@ def test_scan_bwd_rejects():
     a.ld_x = a.ld_delta = a.ld_dy = 64
     a.ld_B = a.ld_C = 16
     assert L.ssm_selective_scan_bwd(None, FAKE, 1 << 30, None) == NULL
-    assert L.ssm_selective_scan_bwd_workspace_bytes(ctypes.byref(a)) >= 2 * 8 * 64 * 16 * 4
+    # states and adjoint carries at the chunk boundaries (one chunk of 16 steps here), partial sums
+    assert L.ssm_selective_scan_bwd_workspace_bytes(ctypes.byref(a)) >= 2 * (2 * 1 * 64 * 16 * 4) + 2 * 16 * 16 * 4
     assert L.ssm_selective_scan_bwd(ctypes.byref(a), FAKE, 16, None) == WORKSPACE
     assert L.ssm_selective_scan_bwd(ctypes.byref(a), FAKE + 8, 1 << 30, None) == ALIGN
     for field, val, status in (("d_state", 12, UNSUPPORTED), ("act_dtype", 2, DTYPE), ("ld_B", 8, SHAPE),
-                               ("ld_dy", 32, SHAPE), ("nheads", 0, SHAPE), ("dB", None, NULL), ("A", FAKE + 2, ALIGN)):
+                               ("ld_dy", 32, SHAPE), ("nheads", 0, SHAPE), ("dB", None, NULL), ("A", FAKE + 2, ALIGN),
+                               ("seqlen", 65535 * 16 + 1, UNSUPPORTED)):  # more than 65535 time chunks
         b = tws.ScanBwdArgs.from_buffer_copy(a)
         setattr(b, field, val)
         assert L.ssm_selective_scan_bwd(ctypes.byref(b), FAKE, 1 << 30, None) == status, field

@@ -665,6 +665,8 @@ SCAN_BWD_CASES = [  # (batch, L, H, N, dtype, h0)
     (1, 300, 512, 16, "f32", True),
     (8, 256, 512, 16, "f32", False),   # TriSSM width and length
     (2, 20, 64, 64, "f32", True),
+    (2, 100, 64, 4, "f32", True),      # 64-step time chunks, ragged last chunk
+    (1, 45, 96, 32, "bf16", False),    # 8-step time chunks
 ]
 
 
