@@ -38,6 +38,45 @@ __device__ __forceinline__ float softplus_b(float v) {
   return v > 20.0f ? v : r;
 }
 
+// lane value exchanged with lane ^ MASK
+template <int MASK> __device__ __forceinline__ float xchg(float v) {
+  const int i = __float_as_int(v);
+  if constexpr (MASK == 32) return __int_as_float(__shfl_xor(i, 32, 64));
+  else if constexpr (MASK == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false));
+  else if constexpr (MASK == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false));
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x1F | (MASK << 10)));  // bit-mask mode: lane ^ MASK
+}
+
+// one round of a transposed wave sum over the values a[0 .. W): lanes whose bit MASK is clear
+// keep the first half, the others the second, each adding its partner's copy of what it keeps
+template <int MASK, int W, int V>
+__device__ __forceinline__ void xsum_round(float (&a)[V], int lane) {
+  if constexpr (W > 1) {
+    const bool hi = (lane & MASK) != 0;
+#pragma unroll
+    for (int j = 0; j < W / 2; ++j) {
+      const float keep = hi ? a[W / 2 + j] : a[j];
+      const float send = hi ? a[j] : a[W / 2 + j];
+      a[j] = keep + xchg<MASK>(send);
+    }
+  } else {
+    a[0] = a[0] + xchg<MASK>(a[0]);
+  }
+}
+
+// V sums over the 64 lanes at once (V a power of two up to 32): afterwards lane l holds the
+// sum of value l >> (6 - log2 V).  Each value is added up in a fixed tree, the same on every run.
+template <int V> __device__ __forceinline__ float wave_sum_transposed(float (&a)[V], int lane) {
+  xsum_round<32, V, V>(a, lane);
+  xsum_round<16, (V >= 2 ? V / 2 : 1), V>(a, lane);
+  xsum_round<8, (V >= 4 ? V / 4 : 1), V>(a, lane);
+  xsum_round<4, (V >= 8 ? V / 8 : 1), V>(a, lane);
+  xsum_round<2, (V >= 16 ? V / 16 : 1), V>(a, lane);
+  xsum_round<1, (V >= 32 ? V / 32 : 1), V>(a, lane);
+  return a[0];
+}
+template <int V> constexpr int log2c() { return V <= 1 ? 0 : 1 + log2c<V / 2>(); }
+
 // steps per chunk: the chunk's states (LC x NS/4 per lane) stay in registers in pass 3
 template <int NS> constexpr int bwd_chunk() {
   return NS >= 64 ? 4 : (NS >= 32 ? 8 : (NS >= 16 ? 16 : (NS >= 8 ? 32 : 64)));
@@ -117,20 +156,22 @@ __global__ __launch_bounds__(256) void k_bwd_local(ScanBwdArgs a, ChunkBufs cb) 
     h[i] = 0.0f;
     g[i] = 0.0f;
   }
+  float ra[LC][SPL];  // a_t of the chunk's steps, for the reverse loop
 #pragma unroll
   for (int u = 0; u < LC; ++u) {  // steps past the end have dt = 0: a = 1, nothing added
     const float dt = s.dt[u][lane], dx = dt * s.x[u][lane];
     sdt += dt;
 #pragma unroll
-    for (int i = 0; i < SPL; ++i)
-      h[i] = __builtin_fmaf(__builtin_amdgcn_exp2f(dt * Al[i]), h[i], dx * s.B[u][w * SPL + i]);
+    for (int i = 0; i < SPL; ++i) {
+      ra[u][i] = __builtin_amdgcn_exp2f(dt * Al[i]);
+      h[i] = __builtin_fmaf(ra[u][i], h[i], dx * s.B[u][w * SPL + i]);
+    }
   }
 #pragma unroll
   for (int u = LC - 1; u >= 0; --u) {  // past the end: dy = 0 and a = 1, the carry passes through
-    const float dt = s.dt[u][lane], dyv = s.dy[u][lane];
+    const float dyv = s.dy[u][lane];
 #pragma unroll
-    for (int i = 0; i < SPL; ++i)
-      g[i] = __builtin_amdgcn_exp2f(dt * Al[i]) * __builtin_fmaf(s.C[u][w * SPL + i], dyv, g[i]);
+    for (int i = 0; i < SPL; ++i) g[i] = ra[u][i] * __builtin_fmaf(s.C[u][w * SPL + i], dyv, g[i]);
   }
   if (dv) {
     const int64_t si = ((b * cb.nc + c) * H + d) * NS + w * SPL;
@@ -217,7 +258,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(ScanBwdArgs a, ChunkBufs cb) 
   }
   stage_chunk<NS, LC, T>(a, s, b, dc, dv, t0, t1, bias);
   __syncthreads();
-  // the chunk's states: hp[u] = h_{t0 + u - 1}
+  // the chunk's states: hp[u] = h_{t0 + u - 1} (a_t is recomputed in the reverse loop: kept
+  // here it costs more in occupancy than the exponentials it saves)
   float hp[LC][SPL];
 #pragma unroll
   for (int u = 0; u < LC; ++u) {
@@ -238,6 +280,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(ScanBwdArgs a, ChunkBufs cb) 
     const float dt = s.dt[u][lane], sig = s.sig[u][lane];
     const float xv = s.x[u][lane], dyv = s.dy[u][lane];
     float pddt = 0.0f, pgb = 0.0f;
+    float red[2 * SPL];  // this lane's dB (first SPL) and dC terms of the wave's states
 #pragma unroll
     for (int i = 0; i < SPL; ++i) {
       const int n = w * SPL + i;
@@ -249,14 +292,19 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(ScanBwdArgs a, ChunkBufs cb) 
       pddt = __builtin_fmaf(gha, Av[i], __builtin_fmaf(gi * xv, Bn, pddt));
       pgb = __builtin_fmaf(gi, Bn, pgb);
       dA[i] = __builtin_fmaf(gha, dt, dA[i]);
-      const float sb = wave_sum_butterfly(gi * dt * xv);  // dB over the block's channels
-      const float sc = wave_sum_butterfly(dyv * h[i]);    // dC (dy is 0 past the last channel)
-      if (lane == 0) {
-        cb.pB[(tok * ntile + tile) * NS + n] = sb;
-        cb.pC[(tok * ntile + tile) * NS + n] = sc;
-      }
+      red[i] = gi * dt * xv;
+      red[SPL + i] = dyv * h[i];  // dy is 0 past the last channel
       g[i] = ab * gi;
       h[i] = hprev;
+    }
+    {  // dB and dC over the block's channels: one lane per value stores it
+      constexpr int K = log2c<2 * SPL>();
+      const float r = wave_sum_transposed<2 * SPL>(red, lane);
+      const int j = lane >> (6 - K);
+      if ((lane & ((64 >> K) - 1)) == 0) {
+        float* dst = j < SPL ? cb.pB : cb.pC;
+        dst[(tok * ntile + tile) * NS + w * SPL + (j < SPL ? j : j - SPL)] = r;
+      }
     }
     const int par = (int)(t & 1);
     s_red[par][0][w][lane] = pddt;
