@@ -463,11 +463,10 @@ def train_bench(prob: Problem, steps: int, warmup: int) -> dict:
         e1.record()
         torch.cuda.synchronize()
         out["scan_bwd_us"] = e0.elapsed_time(e1) * 1e3 / reps
-        # algorithmic bytes: read x, delta, B, C, dy; write dx, ddelta, dB, dC (fp32 grads), plus the
-        # stored states written once and read once
+        # algorithmic bytes: read x, delta, B, C, dy; write dx, ddelta, dB, dC (fp32 grads)
         es = 2 if prob.act == torch.bfloat16 else 4
         Mt = cfg.tokens
-        byts = Mt * (2 * H + 2 * N) * es + Mt * H * 4 + Mt * (2 * H + 2 * N) * 4 + 2 * Mt * H * N * 4
+        byts = Mt * (2 * H + 2 * N) * es + Mt * H * 4 + Mt * (2 * H + 2 * N) * 4
         out["scan_bwd_GBps"] = byts / (out["scan_bwd_us"] * 1e-6) / 1e9
     return out
 
