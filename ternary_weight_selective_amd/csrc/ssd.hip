@@ -109,12 +109,13 @@ __global__ __launch_bounds__(256) void k_scan_ssd_rec(ScanArgs a) {
 // Chunked evaluation on the matrix cores (the state-space duality of "Transformers are
 // SSMs"): bf16 activations, headdim 64, d_state 64 or 128, chunks of Q = 64 steps.
 // A block owns one (sequence, head) and walks its chunks in order, the P x N state in MFMA
-// accumulators.  With cs_t the inclusive cumulative sum of dt_s A inside a chunk and h_in the
+// accumulators (8 waves: two per SIMD, so that one wave's dependent MFMAs, exponentials and
+// LDS round trips overlap the other's).  With cs_t the inclusive cumulative sum of dt_s A inside a chunk and h_in the
 // state entering it, for t in the chunk
 //   y_t = sum_{s <= t} (C_t . B_s) exp(cs_t - cs_s) dt_s x_s  +  exp(cs_t) C_t h_in^T  +  D x_t
 //   h_out = exp(cs_end) h_in + sum_s exp(cs_end - cs_s) dt_s x_s B_s^T
 // which is the recurrence h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t, y_t = C_t h_t + D x_t
-// regrouped.  Per chunk (4 waves, wave w owning chunk rows 16 w .. 16 w + 15):
+// regrouped.  Per chunk (wave w owning chunk rows 16 (w mod 4) .. + 15 and half the columns):
 //   G = C B^T (bf16 x bf16, exact products, fp32 sums), then the masked, decayed M (fp32);
 //   Y = M X and Z = C h_in^T; y = Y + exp(cs_t) Z + D x;
 //   h = exp(cs_end) h + (w X)^T B, w_s = exp(cs_end - cs_s) dt_s.
@@ -139,12 +140,16 @@ __device__ __forceinline__ float softplus_hw(float v) {
 
 constexpr int kSsdQ = 64, kSsdP = 64;
 
+// 8 waves, two per SIMD: wave w works on row tile rt = w mod 4 (chunk rows, or state rows p)
+// and half hf = w / 4 of the tiles along the other dimension; every output tile is computed
+// by one wave with the same MFMA sequence as with one wave per row tile.
 template <int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_ssd_chunk(ScanArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ssd_chunk(ScanArgs a) {
   constexpr int Q = kSsdQ, P = kSsdP;
   constexpr int XS = Q + 8;          // row stride (elements) of the [.][Q] arrays
   constexpr int NSP = NS + 8;        // row stride of the [.][NS] arrays
   constexpr int NTN = NS / 16;       // 16-wide n tiles
+  constexpr int NTH = NTN / 2;       // n tiles of a wave's state share
   constexpr int KN = NS / 32;        // k steps over n
   __shared__ __align__(16) uint16_t sX[Q * XS];        // x  [t][p]
   __shared__ __align__(16) uint16_t sG[Q * XS];        // gate [t][p] (gated block)
@@ -159,6 +164,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w & 3, hf = w >> 2;
   const int kq = lane >> 4, l16 = lane & 15;
   const int64_t L = a.L, H = a.H;
   const int64_t hd = blockIdx.x % H, b = blockIdx.x / H;
@@ -171,21 +177,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const bf16_t* DT = (const bf16_t*)a.delta;
   bf16_t* Y = (bf16_t*)a.y;
 
-  // state: lane holds h[p = 16 w + 4 kq + r][n = 16 jn + l16]
-  v4f h[NTN];
+  // state: lane holds h[p = 16 rt + 4 kq + r][n = 16 (NTH hf + jn) + l16]
+  v4f h[NTH];
 #pragma unroll
-  for (int jn = 0; jn < NTN; ++jn)
+  for (int jn = 0; jn < NTH; ++jn)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int pp = 16 * w + 4 * kq + r, n = 16 * jn + l16;
+      const int pp = 16 * rt + 4 * kq + r, n = 16 * (NTH * hf + jn) + l16;
       h[jn][r] = a.h0 ? a.h0[((b * H + hd) * P + pp) * NS + n] : 0.0f;
     }
   auto write_h = [&]() {
 #pragma unroll
-    for (int jn = 0; jn < NTN; ++jn)
+    for (int jn = 0; jn < NTH; ++jn)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * w + 4 * kq + r, n = 16 * jn + l16;
+        const int pp = 16 * rt + 4 * kq + r, n = 16 * (NTH * hf + jn) + l16;
         const uint16_t hi = bf_bits(h[jn][r]);
         sH[0][pp * NSP + n] = hi;
         sH[1][pp * NSP + n] = bf_bits(h[jn][r] - bf_val(hi));
@@ -194,8 +200,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   write_h();
 
   // chunk loads, 16-byte chunks with the step index fastest across the lanes (lane = step t,
-  // chunk column q = wave + 4 i), so that the transposed LDS copies are written along rows
-  constexpr int XC = Q * P / 8 / 256, BC = Q * NS / 8 / 256;
+  // chunk column q = wave + 8 i), so that the transposed LDS copies are written along rows
+  constexpr int XC = Q * P / 8 / 512, BC = Q * NS / 8 / 512;
   v4i px[XC], pg[XC], pb[BC], pc[BC];
   float pdt = 0.0f;
   const bf16_t* G = (const bf16_t*)a.gate;
@@ -204,13 +210,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t tok = b * L + c0 + lane;
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
-      const int q = w + 4 * i;
+      const int q = w + 8 * i;
       px[i] = ok ? *(const v4i*)(X + tok * a.ld_x + hd * P + q * 8) : v4i{0, 0, 0, 0};
       if (G) pg[i] = ok ? *(const v4i*)(G + tok * a.ld_gate + hd * P + q * 8) : v4i{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
-      const int q = w + 4 * i;
+      const int q = w + 8 * i;
       pb[i] = ok ? *(const v4i*)(Bm + tok * a.ld_B + q * 8) : v4i{0, 0, 0, 0};
       pc[i] = ok ? *(const v4i*)(Cm + tok * a.ld_C + q * 8) : v4i{0, 0, 0, 0};
     }
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int t = lane;
 #pragma unroll
     for (int i = 0; i < XC; ++i) {
-      const int q = w + 4 * i;
+      const int q = w + 8 * i;
       *(v4i*)(&sX[t * XS + q * 8]) = px[i];
       if (G) *(v4i*)(&sG[t * XS + q * 8]) = pg[i];
       const uint16_t* v = (const uint16_t*)&px[i];
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #pragma unroll
     for (int i = 0; i < BC; ++i) {
-      const int q = w + 4 * i;
+      const int q = w + 8 * i;
       *(v4i*)(&sB[t * NSP + q * 8]) = pb[i];
       *(v4i*)(&sC[t * NSP + q * 8]) = pc[i];
       const uint16_t* v = (const uint16_t*)&pb[i];
@@ -265,88 +271,95 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (ch + 1 < nch) load(c0 + Q);
     const float cs_end = s_cs[Q - 1];
 
-    // G = C B^T for rows 16 w .., s tiles j <= w (the rest is masked); then M into LDS
+    // G = C B^T for rows 16 rt .., s tiles j = 2 hf, 2 hf + 1 when j <= rt (the rest is
+    // masked); then those columns of M into LDS
     {
-      v4f g[4];
+      v4f g[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) g[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int jj = 0; jj < 2; ++jj) g[jj] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) {
-        const v8bf af = __builtin_bit_cast(v8bf, *(const v4i*)(&sC[(16 * w + l16) * NSP + kk * 32 + kq * 8]));
+        const v8bf af = __builtin_bit_cast(v8bf, *(const v4i*)(&sC[(16 * rt + l16) * NSP + kk * 32 + kq * 8]));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j > w) continue;
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * hf + jj;
+          if (j > rt) continue;
           const v8bf bfr = __builtin_bit_cast(v8bf, *(const v4i*)(&sB[(16 * j + l16) * NSP + kk * 32 + kq * 8]));
-          g[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, g[j], 0, 0, 0);
+          g[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, g[jj], 0, 0, 0);
         }
       }
-      // M[t][s] = G exp(cs_t - cs_s) dt_s for s <= t; lane holds t = 16 w + 4 kq + r, s = 16 j + l16
+      // M[t][s] = G exp(cs_t - cs_s) dt_s for s <= t; lane holds t = 16 rt + 4 kq + r, s = 16 j + l16
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int tl = 4 * kq + r, t = 16 * w + tl, sidx = 16 * j + l16;
+          const int j = 2 * hf + jj;
+          const int tl = 4 * kq + r, t = 16 * rt + tl, sidx = 16 * j + l16;
           float m = 0.0f;
-          if (j <= w && sidx <= t) m = g[j][r] * (exp_hw(s_cs[t] - s_cs[sidx]) * s_dt[sidx]);
+          if (j <= rt && sidx <= t) m = g[jj][r] * (exp_hw(s_cs[t] - s_cs[sidx]) * s_dt[sidx]);
           const uint16_t hi = bf_bits(m);
-          sM[w][0][tl * XS + sidx] = hi;
-          sM[w][1][tl * XS + sidx] = bf_bits(m - bf_val(hi));
+          sM[rt][0][tl * XS + sidx] = hi;
+          sM[rt][1][tl * XS + sidx] = bf_bits(m - bf_val(hi));
         }
     }
     __syncthreads();
 
-    // Y = M X (s < 16 w + 16) and Z = C h_in^T; lane holds t = 16 w + 4 kq + r, p = 16 jp + l16
-    v4f yacc[4], zacc[4];
+    // Y = M X (s < 16 rt + 16) and Z = C h_in^T for p tiles jp = 2 hf, 2 hf + 1; lane holds
+    // t = 16 rt + 4 kq + r, p = 16 jp + l16
+    v4f yacc[2], zacc[2];
 #pragma unroll
-    for (int jp = 0; jp < 4; ++jp) { yacc[jp] = v4f{0.f, 0.f, 0.f, 0.f}; zacc[jp] = v4f{0.f, 0.f, 0.f, 0.f}; }
+    for (int jj = 0; jj < 2; ++jj) { yacc[jj] = v4f{0.f, 0.f, 0.f, 0.f}; zacc[jj] = v4f{0.f, 0.f, 0.f, 0.f}; }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      if (kk * 32 > 16 * w + 15) continue;
-      const v8bf mh = __builtin_bit_cast(v8bf, *(const v4i*)(&sM[w][0][l16 * XS + kk * 32 + kq * 8]));
-      const v8bf ml = __builtin_bit_cast(v8bf, *(const v4i*)(&sM[w][1][l16 * XS + kk * 32 + kq * 8]));
+      if (kk * 32 > 16 * rt + 15) continue;
+      const v8bf mh = __builtin_bit_cast(v8bf, *(const v4i*)(&sM[rt][0][l16 * XS + kk * 32 + kq * 8]));
+      const v8bf ml = __builtin_bit_cast(v8bf, *(const v4i*)(&sM[rt][1][l16 * XS + kk * 32 + kq * 8]));
 #pragma unroll
-      for (int jp = 0; jp < 4; ++jp) {
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jp = 2 * hf + jj;
         const v8bf xf = __builtin_bit_cast(v8bf, *(const v4i*)(&sXT[(16 * jp + l16) * XS + kk * 32 + kq * 8]));
-        yacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh, xf, yacc[jp], 0, 0, 0);
-        yacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml, xf, yacc[jp], 0, 0, 0);
+        yacc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh, xf, yacc[jj], 0, 0, 0);
+        yacc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml, xf, yacc[jj], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int kk = 0; kk < KN; ++kk) {
-      const v8bf cf = __builtin_bit_cast(v8bf, *(const v4i*)(&sC[(16 * w + l16) * NSP + kk * 32 + kq * 8]));
+      const v8bf cf = __builtin_bit_cast(v8bf, *(const v4i*)(&sC[(16 * rt + l16) * NSP + kk * 32 + kq * 8]));
 #pragma unroll
-      for (int jp = 0; jp < 4; ++jp) {
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jp = 2 * hf + jj;
         const int off = (16 * jp + l16) * NSP + kk * 32 + kq * 8;
         const v8bf hh = __builtin_bit_cast(v8bf, *(const v4i*)(&sH[0][off]));
         const v8bf hl = __builtin_bit_cast(v8bf, *(const v4i*)(&sH[1][off]));
-        zacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, hh, zacc[jp], 0, 0, 0);
-        zacc[jp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, hl, zacc[jp], 0, 0, 0);
+        zacc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, hh, zacc[jj], 0, 0, 0);
+        zacc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, hl, zacc[jj], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = 16 * w + 4 * kq + r;
+      const int t = 16 * rt + 4 * kq + r;
       if (c0 + t >= L) continue;
       const float et = s_et[t];
       bf16_t* yr = Y + (b * L + c0 + t) * a.ld_y + hd * P;
 #pragma unroll
-      for (int jp = 0; jp < 4; ++jp) {
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jp = 2 * hf + jj;
         const int pp = 16 * jp + l16;
-        float yv = yacc[jp][r] + et * zacc[jp][r] + D_h * bf_val(sX[t * XS + pp]);
+        float yv = yacc[jj][r] + et * zacc[jj][r] + D_h * bf_val(sX[t * XS + pp]);
         if (G) yv = yv * silu_gate(bf_val(sG[t * XS + pp]));
         yr[pp] = f32_to_bf16(yv);
       }
     }
 
-    // state: h = exp(cs_end) h + (w X)^T B; A fragment: p = 16 w + l16, s = 32 kk + 8 kq + u
+    // state: h = exp(cs_end) h + (w X)^T B; A fragment: p = 16 rt + l16, s = 32 kk + 8 kq + u
     const float ed = exp_hw(cs_end);
 #pragma unroll
-    for (int jn = 0; jn < NTN; ++jn)
+    for (int jn = 0; jn < NTH; ++jn)
 #pragma unroll
       for (int r = 0; r < 4; ++r) h[jn][r] *= ed;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const uint16_t* xr = &sXT[(16 * w + l16) * XS + kk * 32 + kq * 8];
+      const uint16_t* xr = &sXT[(16 * rt + l16) * XS + kk * 32 + kq * 8];
       uint16_t ahi[8], alo[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -358,8 +371,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const v8bf ah = __builtin_bit_cast(v8bf, *(const v4i*)ahi);
       const v8bf al = __builtin_bit_cast(v8bf, *(const v4i*)alo);
 #pragma unroll
-      for (int jn = 0; jn < NTN; ++jn) {
-        const v8bf bfr = __builtin_bit_cast(v8bf, *(const v4i*)(&sBT[(16 * jn + l16) * XS + kk * 32 + kq * 8]));
+      for (int jn = 0; jn < NTH; ++jn) {
+        const int n0t = 16 * (NTH * hf + jn);
+        const v8bf bfr = __builtin_bit_cast(v8bf, *(const v4i*)(&sBT[(n0t + l16) * XS + kk * 32 + kq * 8]));
         h[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bfr, h[jn], 0, 0, 0);
         h[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfr, h[jn], 0, 0, 0);
       }
@@ -369,10 +383,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   if (a.h_last) {
 #pragma unroll
-    for (int jn = 0; jn < NTN; ++jn)
+    for (int jn = 0; jn < NTH; ++jn)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * w + 4 * kq + r, n = 16 * jn + l16;
+        const int pp = 16 * rt + 4 * kq + r, n = 16 * (NTH * hf + jn) + l16;
         a.h_last[((b * H + hd) * P + pp) * NS + n] = h[jn][r];
       }
   }
@@ -410,7 +424,7 @@ size_t scan_ssd_workspace(const ScanArgs&) { return 0; }
 hipError_t launch_scan_ssd(const ScanArgs& a, void*, size_t, hipStream_t s) {
   if (a.batch == 0 || a.L == 0) return hipSuccess;
   if (ssd_chunk_ok(a)) {
-    const dim3 grid((unsigned)(a.batch * a.H)), block(256);
+    const dim3 grid((unsigned)(a.batch * a.H)), block(512);
     if (a.N == 128) hipLaunchKernelGGL((k_ssd_chunk<128>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_ssd_chunk<64>), grid, block, 0, s, a);
     return hipGetLastError();
