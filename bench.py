@@ -93,6 +93,7 @@ class Problem:
         self.dev = dev
         lat, u = wl.mixer_problem(cfg, seed=seed)
         self.u_host = u
+        self.lat0 = lat[0]  # the first layer's latent weights (host), for the training-side timings
         self.act = torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32
         self.layers = []  # dicts of device tensors
         for lw in lat:
@@ -468,6 +469,29 @@ def train_bench(prob: Problem, steps: int, warmup: int) -> dict:
         Mt = cfg.tokens
         byts = Mt * (2 * H + 2 * N) * es + Mt * H * 4 + Mt * (2 * H + 2 * N) * 4
         out["scan_bwd_GBps"] = byts / (out["scan_bwd_us"] * 1e-6) / 1e9
+    if cfg.kind == wl.MAMBA1 and not cfg.gated and cfg.fp_proj == 0 and prob.act == torch.float32:
+        # the whole layer's backward (forward again, then the chain) for the stack's first layer
+        lats = {"lat_" + p: torch.from_numpy(prob.lat0["W_" + p]).to(dev) for p in cfg.proj_shapes}
+        dout = torch.from_numpy(wl.normal(g, (cfg.batch, cfg.seqlen, cfg.d_model))).to(dev)
+        mws = torch.empty(tws.ssm_mixer_bwd_workspace_bytes(prob.c, cfg.batch, cfg.seqlen), dtype=torch.uint8,
+                          device=dev)
+
+        def mbwd():
+            return tws.ssm_mixer_bwd(prob.c, prob.mws[0], prob.u, dout, latents=lats, workspace=mws,
+                                     stream=torch.cuda.current_stream())
+
+        for _ in range(max(1, warmup // 2)):
+            mbwd()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(2, steps // 4)
+        e0.record()
+        for _ in range(reps):
+            mbwd()
+        e1.record()
+        torch.cuda.synchronize()
+        out["mixer_bwd_us"] = e0.elapsed_time(e1) * 1e3 / reps
+        out["mixer_bwd_tokens_per_s"] = cfg.tokens / (out["mixer_bwd_us"] * 1e-6)
     return out
 
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 typedef enum {
   SSM_OK = 0,
@@ -283,6 +283,47 @@ size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64
 ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u,
                          void* out, int64_t batch, int64_t seqlen, int32_t add_residual,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ssm_mixer_bwd -- the backward pass of one Mamba-1 kind mixer layer (TriSSM README: the mixer
+ * is trained end to end, its BitLinear layers with straight-through estimators; Ternary Mamba
+ * abstract: quantisation-aware training with learnable scales).  Given dout, the gradient of
+ * the loss with respect to out = mixer(u) (+ u with add_residual), it computes du and the
+ * gradients of the layer's parameters.  The forward is run again with its intermediates kept
+ * in the workspace: x = BL(u; W_in), p = BL(x; W_x) = [dr | B | C], delta = BL(dr; W_dt),
+ * y = scan(x, softplus(delta + dt_bias), A, B, C, D) (the values ssm_mixer_fwd computes); then
+ *   dy    = BL_bwd(W_out; y, dout)                      (+ dW_out, d s_out)
+ *   dx_s, d delta, dA, dB, dC, dD, d dt_bias = ssm_selective_scan_bwd(..., dy)
+ *   d dr  = BL_bwd(W_dt; dr, d delta)                   (+ dW_dt, d s_dt)
+ *   dx_p  = BL_bwd(W_x; x, [d dr | dB | dC])            (+ dW_x, d s_x)
+ *   du    = BL_bwd(W_in; u, dx_s + dx_p) (+ dout)       (+ dW_in, d s_in)
+ * where BL_bwd is ssm_bitlinear_bwd's straight-through backward.
+ * Supported: Mamba-1 kind, not gated, ternary projections (fp_proj 0), act_bits 8,
+ * group_size 0, act_dtype SSM_F32 (else SSM_ERR_UNSUPPORTED).
+ *  u [batch, seqlen, d_model] fp32; dout fp32, same shape; du fp32, same shape (written; may
+ *  not alias u or dout; du and dout 16-byte aligned).  seqlen is limited as in
+ *  ssm_selective_scan_bwd.  batch * seqlen = 0 returns SSM_OK and writes nothing.  grads: NULL or a struct whose pointers are each NULL (not wanted) or
+ *  device fp32 buffers, written: dw_* [n_out, k] (the latent-weight gradients; n_out, k those
+ *  of the projection), ds_* [1] (scale gradients; each needs its dw_* and the latent weights
+ *  lat_* [n_out, k]), dA [d_inner, d_state], dD and d_dt_bias [d_inner].
+ *  workspace: ssm_mixer_bwd_workspace_bytes(c, batch, seqlen) bytes (0 for a configuration or
+ *  size the call rejects), 256-byte aligned; it holds x, p, delta, y and the intermediate
+ *  gradients (7 d_inner + 2 dt_rank + 6 d_state floats per token) plus the largest
+ *  workspace of the steps.  Sums are taken in a fixed order (results do not depend on timing).
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIGN,
+ * SSM_ERR_WORKSPACE, SSM_ERR_DEVICE.
+ */
+typedef struct {
+  const float *lat_in, *lat_x, *lat_dt, *lat_out; /* latent weights (for the scale gradients) */
+  float *dw_in, *dw_x, *dw_dt, *dw_out;
+  float *ds_in, *ds_x, *ds_dt, *ds_out;
+  float *dA, *dD, *d_dt_bias;
+} ssm_mixer_grads;
+
+size_t ssm_mixer_bwd_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64_t seqlen);
+ssm_status ssm_mixer_bwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const ssm_mixer_grads* g,
+                         const float* u, const float* dout, float* du, int64_t batch, int64_t seqlen,
+                         int32_t add_residual, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * ssm_mixer_step -- one decoding step of the mixer layer: ONE new token per sequence, the

@@ -360,7 +360,8 @@ def mixer_stack(cfg, layers: list, u) -> np.ndarray:
 
 # ---------------------------------------------------------------- O10: STE backward, one QAT step
 
-def bitlinear_bwd(x, codes, w_scale, dy, group: int = 0, norm_w=None, eps: float = 1e-5, w_latent=None) -> dict:
+def bitlinear_bwd(x, codes, w_scale, dy, group: int = 0, norm_w=None, eps: float = 1e-5, w_latent=None,
+                  act_bits: int = 8) -> dict:
     """Backward of the A8 BitLinear with straight-through estimators (TriSSM README: BitLinear
     trained with straight-through estimators; the estimator of "Estimating or Propagating
     Gradients Through Stochastic Neurons ...", cited under "Builds on"), fp64.
@@ -375,15 +376,20 @@ def bitlinear_bwd(x, codes, w_scale, dy, group: int = 0, norm_w=None, eps: float
     given the latent weights: with v = W / s, dW̃/ds is q - v where |v| <= 1 and q where the
     clip is active (the step-size rule of learned-step-size quantisation), summed over each
     scale's group:  ds = sum dW (q - v or q).
+    act_bits 16 (W1.58A16, no activation quantiser): x̃ is the fp32 RMSNorm output itself, and
+    dx, dW are then the plain derivatives of that BitLinear.
     Returns dict(dx [m,k], dw [n,k], ds (scalar array or [n, k/group]) or None, x_tilde, r)."""
     x = _f32(x)
     m, k = x.shape
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     n = codes.shape[0]
     dy = np.asarray(dy, dtype=np.float64)
-    _, xq, am, _ = bitlinear(x, codes, w_scale, group, 8, norm_w, eps)
     r = np.array([rms_scale(x[i], eps) for i in range(m)], dtype=np.float32).astype(np.float64)
-    xt = xq.astype(np.float64) * (np.maximum(am, np.float32(1e-5)).astype(np.float64) / 127.0)[:, None]
+    if act_bits == 8:
+        _, xq, am, _ = bitlinear(x, codes, w_scale, group, 8, norm_w, eps)
+        xt = xq.astype(np.float64) * (np.maximum(am, np.float32(1e-5)).astype(np.float64) / 127.0)[:, None]
+    else:
+        xt = np.stack([norm_row(x[i], norm_w, eps) for i in range(m)]).astype(np.float64).reshape(m, k)
     sc = np.asarray(w_scale, dtype=np.float32).astype(np.float64)
     s_full = np.full((n, k), sc.ravel()[0]) if group == 0 else np.repeat(sc.reshape(n, k // group), group, axis=1)
     wt = s_full * codes.astype(np.float64)
@@ -476,3 +482,63 @@ def selective_scan_bwd(x, delta, A, Bm, Cm, D, dy, delta_bias=None, softplus: bo
         carry = a * g
     return dict(dx=dx.reshape(batch, L, HP), ddelta=ddelta, dA=dA, dB=dB, dC=dC, dD=dD,
                 dbias=ddelta.sum(axis=(0, 1)), dh0=carry.reshape(batch, H, P, N))
+
+
+def mixer_bwd(cfg, weights: dict, u, dout, residual: bool = True, latents: dict | None = None) -> dict:
+    """Backward of one Mamba-1 kind mixer layer (not gated, ternary projections, fp32 activations)
+    under the straight-through estimators (TriSSM README: BitLinear layers trained with
+    straight-through estimators, the SSM trained end to end), fp64.
+
+    The forward is evaluated again with the roundings of ``mixer`` (x, p and y stored as fp32; the
+    dt projection output passed to the scan at fp32 width), then the chain runs backwards:
+      dy  = BL_out backward (dout),          scan backward (dy) -> dx_s, d delta, dB, dC, dA, dD, d bias,
+      dp  = [BL_dt backward (d delta) | dB | dC],   dx = dx_s + BL_x backward (dp),
+      du  = BL_in backward (dx) (+ dout when the residual is added).
+    Each BitLinear backward is ``bitlinear_bwd``; its weight gradient is that of the dequantised
+    ternary weights (the latent weights' gradient), and with latents["lat_in" / "lat_x" /
+    "lat_dt" / "lat_out"] its learnable-scale gradient too.  act_bits 16 in cfg evaluates the same
+    chain with no activation quantiser (the surrogate whose derivative the finite-difference
+    pins check).  u, dout [B, L, d_model].  Returns a dict of fp64 arrays: du, dw_in, dw_x, dw_dt,
+    dw_out, dA, dD, d_dt_bias (ds_* for the latents given) and out (the forward's output)."""
+    assert int(cfg["kind"]) == MAMBA1 and int(cfg.get("gated", 0)) == 0 and int(cfg.get("fp_proj", 0)) == 0
+    assert int(cfg["act_dtype"]) == F32 and int(cfg.get("group_size", 0)) == 0
+    ab = int(cfg["act_bits"])
+    eps = cfg.get("norm_eps", 1e-5)
+    u = _f32(u)
+    batch, L, dm = u.shape
+    M = batch * L
+    Di, N, R = cfg["d_inner"], cfg["d_state"], cfg["dt_rank"]
+    w = weights
+    lat = latents or {}
+    u2 = u.reshape(M, dm)
+    dout2 = np.asarray(dout, np.float32).astype(np.float64).reshape(M, dm)
+    x = bitlinear(u2, w["c_in"], w["s_in"], 0, ab, w.get("g_in"), eps)[0].astype(np.float32)
+    p = bitlinear(x, w["c_x"], w["s_x"], 0, ab, w.get("g_x"), eps)[0].astype(np.float32)
+    z = bitlinear(p, w["c_dt"], w["s_dt"], 0, ab, w.get("g_dt"), eps, k=R)[0].astype(np.float32)
+    x3 = x.reshape(batch, L, Di)
+    z3 = z.reshape(batch, L, Di)
+    B3 = np.ascontiguousarray(p[:, R:R + N]).reshape(batch, L, N)
+    C3 = np.ascontiguousarray(p[:, R + N:R + 2 * N]).reshape(batch, L, N)
+    y = selective_scan(x3, z3, w["A"], B3, C3, w.get("D"), w.get("dt_bias"))[0].astype(np.float32).reshape(M, Di)
+    out = bitlinear(y, w["c_out"], w["s_out"], 0, ab, w.get("g_out"), eps)[0]
+    if residual:
+        out = out + u2.astype(np.float64)
+
+    def bl(xin, name, gy):
+        return bitlinear_bwd(xin, w["c_" + name], w["s_" + name], gy, 0, w.get("g_" + name), eps,
+                             lat.get("lat_" + name), act_bits=ab)
+
+    go = bl(y, "out", dout2)
+    sb = selective_scan_bwd(x3, z3, w["A"], B3, C3, w.get("D"), go["dx"].reshape(batch, L, Di),
+                            delta_bias=w.get("dt_bias"))
+    gd = bl(np.ascontiguousarray(p[:, :R]), "dt", sb["ddelta"].reshape(M, Di))
+    dp = np.concatenate([gd["dx"], sb["dB"].reshape(M, N), sb["dC"].reshape(M, N)], axis=1)
+    gx = bl(x, "x", dp)
+    gi = bl(u2, "in", sb["dx"].reshape(M, Di) + gx["dx"])
+    du = gi["dx"] + (dout2 if residual else 0.0)
+    res = dict(du=du.reshape(batch, L, dm), dw_in=gi["dw"], dw_x=gx["dw"], dw_dt=gd["dw"], dw_out=go["dw"],
+               dA=sb["dA"], dD=sb["dD"], d_dt_bias=sb["dbias"], out=out.astype(np.float32).reshape(batch, L, dm))
+    for name, g in (("in", gi), ("x", gx), ("dt", gd), ("out", go)):
+        if g["ds"] is not None:
+            res["ds_" + name] = g["ds"]
+    return res

@@ -70,6 +70,11 @@ class MixerWeights(ctypes.Structure):
                                    "fw_dt", "fw_out")]
 
 
+class MixerGrads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("lat_in", "lat_x", "lat_dt", "lat_out", "dw_in", "dw_x", "dw_dt", "dw_out",
+                                   "ds_in", "ds_x", "ds_dt", "ds_out", "dA", "dD", "d_dt_bias")]
+
+
 class SsmError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(msg)
@@ -82,7 +87,8 @@ EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
            "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front", "ssm_mixer_step",
            "ssm_conv1d_silu_fwd", "ssm_dense_fwd", "ssm_bitlinear_bwd_workspace_bytes", "ssm_bitlinear_bwd",
-           "ssm_qat_sgd_step", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd"]
+           "ssm_qat_sgd_step", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd",
+           "ssm_mixer_bwd_workspace_bytes", "ssm_mixer_bwd"]
 
 
 def lib():
@@ -132,6 +138,11 @@ def lib():
         L.ssm_selective_scan_bwd_workspace_bytes.restype = _sz
         L.ssm_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _vp, _sz, _vp]
         L.ssm_selective_scan_bwd.restype = ctypes.c_int
+        L.ssm_mixer_bwd_workspace_bytes.argtypes = [ctypes.POINTER(MixerConfig), _i64, _i64]
+        L.ssm_mixer_bwd_workspace_bytes.restype = _sz
+        L.ssm_mixer_bwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights),
+                                    ctypes.POINTER(MixerGrads), _vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]
+        L.ssm_mixer_bwd.restype = ctypes.c_int
         L.ssm_mixer_step.restype = ctypes.c_int
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
@@ -386,6 +397,48 @@ def ssm_selective_scan_bwd(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor
     ws = _workspace(nb, dev)
     _check(L_.ssm_selective_scan_bwd(ctypes.byref(a), _p(ws), nb, _stream(stream)))
     return g
+
+
+def ssm_mixer_bwd_workspace_bytes(cfg: MixerConfig, batch: int, seqlen: int) -> int:
+    return int(lib().ssm_mixer_bwd_workspace_bytes(ctypes.byref(cfg), batch, seqlen))
+
+
+def ssm_mixer_bwd(cfg: MixerConfig, weights, u: torch.Tensor, dout: torch.Tensor, add_residual: bool = True,
+                  latents: dict | None = None, workspace: torch.Tensor | None = None, stream=None) -> dict:
+    """Backward of one Mamba-1 kind mixer layer: u, dout fp32 [B, L, d_model] (contiguous).
+    latents (optional): latent weights lat_in / lat_x / lat_dt / lat_out, which add the scale
+    gradients.  Returns fp32 du, dw_in, dw_x, dw_dt, dw_out, dA, dD, d_dt_bias (and ds_* with
+    latents)."""
+    if not u.is_contiguous() or not dout.is_contiguous():
+        raise ValueError("u and dout must be contiguous")
+    if dout.dtype != torch.float32:
+        raise ValueError("dout must be float32")
+    batch, seqlen, dm = u.shape
+    di, n, r = cfg.d_inner, cfg.d_state, cfg.dt_rank
+    pw = r + 2 * n
+    dev = u.device
+    f = dict(dtype=torch.float32, device=dev)
+    out = dict(du=torch.empty((batch, seqlen, dm), **f), dw_in=torch.empty((di, dm), **f),
+               dw_x=torch.empty((pw, di), **f), dw_dt=torch.empty((di, r), **f), dw_out=torch.empty((dm, di), **f),
+               dA=torch.empty((di, n), **f), dD=torch.empty(di, **f), d_dt_bias=torch.empty(di, **f))
+    g = MixerGrads()
+    for k in ("dw_in", "dw_x", "dw_dt", "dw_out", "dA", "dD", "d_dt_bias"):
+        setattr(g, k, _p(out[k]))
+    if latents:
+        for k in ("in", "x", "dt", "out"):
+            lat = latents.get("lat_" + k)
+            if lat is not None:
+                out["ds_" + k] = torch.empty(1, **f)
+                setattr(g, "lat_" + k, _p(lat))
+                setattr(g, "ds_" + k, _p(out["ds_" + k]))
+    mw = weights if isinstance(weights, MixerWeights) else mixer_weights(weights)
+    L = lib()
+    nb = L.ssm_mixer_bwd_workspace_bytes(ctypes.byref(cfg), batch, seqlen)
+    ws = _workspace(nb, dev, workspace)
+    _check(L.ssm_mixer_bwd(ctypes.byref(cfg), ctypes.byref(mw), ctypes.byref(g), _p(u), _p(dout), _p(out["du"]),
+                           batch, seqlen, int(add_residual), _p(ws), nb if ws is None else ws.numel(),
+                           _stream(stream)))
+    return out
 
 
 def ssm_bitlinear_bwd(x: torch.Tensor, w_packed: torch.Tensor, w_scale: torch.Tensor, n_out: int,

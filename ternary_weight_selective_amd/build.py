@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libssm_ternary.so")
 
-SOURCES = ["quant.hip", "norm.hip", "bitlinear.hip", "front.hip", "conv.hip", "scan.hip", "ssd.hip", "ste.hip", "scan_bwd.hip", "dense.cpp",
+SOURCES = ["quant.hip", "norm.hip", "bitlinear.hip", "front.hip", "conv.hip", "scan.hip", "ssd.hip", "ste.hip", "scan_bwd.hip", "mixer_bwd.hip", "dense.cpp",
            "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

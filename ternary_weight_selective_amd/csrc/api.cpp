@@ -1,10 +1,12 @@
 // C ABI entry points: host-side validation, workspace carving and launch sequencing.
 // Nothing here touches device memory except through kernel launches on the caller's stream.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
 
 #include "launch.hpp"
+#include "mixer_bwd.hpp"
 #include "scan_bwd.hpp"
 #include "ssm_ternary.h"
 
@@ -723,3 +725,221 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
 
 }  // namespace
 
+// ------------------------------------------------------------------ mixer backward
+
+namespace {
+// Workspace of the mixer backward: the forward's intermediates (x, p, delta, y), the chain's
+// gradients (dy of the scan output, dx through the scan, d delta, dB, dC, the x_proj output's
+// gradient, dx through x_proj, a dA scratch) and one sub-workspace that the steps take in turn.
+struct MixBwdPlan {
+  int64_t M = 0, PW = 0;
+  size_t off_x = 0, off_p = 0, off_dl = 0, off_y = 0, off_dy = 0, off_dxs = 0, off_ddl = 0, off_dB = 0,
+         off_dC = 0, off_dA = 0, off_dp = 0, off_dxp = 0, off_sub = 0, total = 0;
+};
+
+ssm_status mixer_bwd_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, MixBwdPlan* p) {
+  MixPlan mp;
+  ssm_status st = mix_plan(c, batch, seqlen, &mp);
+  if (st != SSM_OK) return st;
+  if (c->kind != SSM_MIXER_MAMBA1 || c->gated || c->fp_proj || c->act_dtype != SSM_F32)
+    return fail(SSM_ERR_UNSUPPORTED, "mixer bwd: Mamba-1 kind, not gated, ternary projections, fp32 activations");
+  {  // the scan backward's own limits, checked here so that the workspace size is only given for runnable shapes
+    ssm_scan_bwd_args q{};
+    q.batch = batch; q.seqlen = seqlen; q.nheads = c->d_inner; q.d_state = c->d_state; q.act_dtype = SSM_F32;
+    q.ld_x = q.ld_delta = q.ld_dy = c->d_inner; q.ld_B = q.ld_C = c->d_state;
+    const uintptr_t nz = 256;  // stand-ins for the buffers the call itself provides (never dereferenced)
+    q.x = q.delta = q.Bm = q.Cm = (const void*)nz;
+    q.A = q.dy = (const float*)nz;
+    q.dx = q.ddelta = q.dA = q.dB = q.dC = (float*)nz;
+    ScanBwdArgs tmp;
+    st = scan_bwd_check(&q, &tmp);
+    if (st != SSM_OK) return st;
+  }
+  const int64_t M = batch * seqlen, Dm = c->d_model, Di = c->d_inner, N = c->d_state, R = c->dt_rank;
+  p->M = M;
+  p->PW = mp.PW;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  p->off_x = take((size_t)M * Di * 4);
+  p->off_p = take((size_t)M * p->PW * 4);
+  p->off_dl = take((size_t)M * Di * 4);
+  p->off_y = take((size_t)M * Di * 4);
+  p->off_dy = take((size_t)M * Di * 4);
+  p->off_dxs = take((size_t)M * Di * 4);
+  p->off_ddl = take((size_t)M * Di * 4);
+  p->off_dB = take((size_t)M * N * 4);
+  p->off_dC = take((size_t)M * N * 4);
+  p->off_dA = take((size_t)Di * N * 4);
+  p->off_dp = take((size_t)M * p->PW * 4);
+  p->off_dxp = take((size_t)M * Di * 4);
+  p->off_sub = off;
+  // the largest of the steps' own workspaces (sizes depend on shapes only)
+  size_t sub = 0;
+  auto bl_ws = [&](int64_t k, int64_t n) {
+    ssm_bitlinear_args a{};
+    a.x_dtype = SSM_F32; a.act_bits = 8; a.m = M; a.k = k; a.ldx = k; a.n_out = n; a.y_dtype = SSM_F32; a.ldy = n;
+    a.w_packed = (const uint8_t*)(uintptr_t)256; a.w_scale = (const float*)(uintptr_t)256;
+    BLPlan bp;
+    if (bl_plan(&a, &bp) == SSM_OK && bp.total > sub) sub = bp.total;
+  };
+  bl_ws(Dm, Di);
+  bl_ws(Di, p->PW);
+  bl_ws(R, Di);
+  ScanArgs sa{};
+  sa.batch = batch; sa.L = seqlen; sa.H = Di; sa.P = 1; sa.N = N;
+  sub = std::max(sub, scan_m1_workspace(sa));
+  ScanBwdArgs sb{};
+  sb.batch = batch; sb.L = seqlen; sb.H = Di; sb.N = N;
+  sub = std::max(sub, scan_bwd_workspace(sb));
+  auto ste_ws = [&](int64_t k, int64_t n) {
+    SteArgs s2{};
+    s2.M = M; s2.K = k; s2.N = n;
+    sub = std::max(sub, ste_workspace(s2));
+  };
+  ste_ws(Di, Dm);
+  ste_ws(R, Di);
+  ste_ws(Di, p->PW);
+  ste_ws(Dm, Di);
+  p->total = off + align_up(sub);
+  return SSM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t ssm_mixer_bwd_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64_t seqlen) {
+  std::string keep = g_err;
+  MixBwdPlan p;
+  const ssm_status st = mixer_bwd_plan(c, batch, seqlen, &p);
+  g_err = keep;
+  return st == SSM_OK ? p.total : 0;
+}
+
+ssm_status ssm_mixer_bwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const ssm_mixer_grads* g,
+                         const float* u, const float* dout, float* du, int64_t batch, int64_t seqlen,
+                         int32_t add_residual, void* ws, size_t wsb, hipStream_t stream) {
+  g_err.clear();
+  MixBwdPlan p;
+  ssm_status st = mixer_bwd_plan(c, batch, seqlen, &p);
+  if (st != SSM_OK) return st;
+  if (!w || !w->A || !w->w_in || !w->w_x || !w->w_dt || !w->w_out || !w->s_in || !w->s_x || !w->s_dt || !w->s_out)
+    return fail(SSM_ERR_NULL, "mixer bwd: w_in, w_x, w_dt, w_out, their scales and A are required");
+  const ssm_mixer_grads none{};
+  const ssm_mixer_grads& gr = g ? *g : none;
+  if ((gr.ds_in && (!gr.dw_in || !gr.lat_in)) || (gr.ds_x && (!gr.dw_x || !gr.lat_x)) ||
+      (gr.ds_dt && (!gr.dw_dt || !gr.lat_dt)) || (gr.ds_out && (!gr.dw_out || !gr.lat_out)))
+    return fail(SSM_ERR_NULL, "mixer bwd: a scale gradient needs its dw and the latent weights");
+  if (p.M > 0 && (!u || !dout || !du)) return fail(SSM_ERR_NULL, "mixer bwd: u, dout and du are required");
+  if (p.M > 0 && ((const void*)du == (const void*)u || du == dout))
+    return fail(SSM_ERR_SHAPE, "mixer bwd: du may not alias u or dout");
+  if (p.M > 0 && (!aligned(du, 16) || !aligned(dout, 16)))
+    return fail(SSM_ERR_ALIGN, "mixer bwd: du and dout must be 16-byte aligned");
+  if (!ws || wsb < p.total) return fail(SSM_ERR_WORKSPACE, "mixer bwd: workspace needs %zu bytes", p.total);
+  if (!aligned(ws, 256)) return fail(SSM_ERR_ALIGN, "mixer bwd: workspace must be 256-byte aligned");
+  if (p.M == 0) return SSM_OK;
+  char* base = (char*)ws;
+  void* sub = base + p.off_sub;
+  const int64_t M = p.M, Dm = c->d_model, Di = c->d_inner, N = c->d_state, R = c->dt_rank, PW = p.PW;
+  float* x = (float*)(base + p.off_x);
+  float* pp = (float*)(base + p.off_p);
+  float* dl = (float*)(base + p.off_dl);
+  float* y = (float*)(base + p.off_y);
+  float* dy = (float*)(base + p.off_dy);
+  float* dxs = (float*)(base + p.off_dxs);
+  float* ddl = (float*)(base + p.off_ddl);
+  float* dB = (float*)(base + p.off_dB);
+  float* dC = (float*)(base + p.off_dC);
+  float* dp = (float*)(base + p.off_dp);
+  float* dxp = (float*)(base + p.off_dxp);
+
+  // ---- forward again, keeping x, p, delta and y
+  auto bitlinear = [&](const void* xin, int64_t k, int64_t ldx, const uint8_t* wp, const float* sc, const float* gn,
+                       int64_t n, float* out, int64_t ldy) -> ssm_status {
+    ssm_bitlinear_args a{};
+    a.x = xin; a.x_dtype = SSM_F32; a.act_bits = 8;
+    a.m = M; a.k = k; a.ldx = ldx;
+    a.norm_weight = gn; a.norm_eps = c->norm_eps;
+    a.w_packed = wp; a.w_scale = sc; a.n_out = n; a.group_size = 0;
+    a.y = out; a.y_dtype = SSM_F32; a.ldy = ldy;
+    BLPlan bp;
+    ssm_status s2 = bl_plan(&a, &bp);
+    if (s2 != SSM_OK) return s2;
+    return bl_run(&a, bp, sub, stream);
+  };
+  st = bitlinear(u, Dm, Dm, w->w_in, w->s_in, w->g_in, Di, x, Di);
+  if (st != SSM_OK) return st;
+  st = bitlinear(x, Di, Di, w->w_x, w->s_x, w->g_x, PW, pp, PW);
+  if (st != SSM_OK) return st;
+  st = bitlinear(pp, R, PW, w->w_dt, w->s_dt, w->g_dt, Di, dl, Di);
+  if (st != SSM_OK) return st;
+  ssm_scan_args sa{};
+  sa.batch = batch; sa.seqlen = seqlen; sa.nheads = Di; sa.headdim = 1; sa.d_state = N;
+  sa.a_per_state = 1; sa.act_dtype = SSM_F32;
+  sa.x = x; sa.ld_x = Di;
+  sa.delta = dl; sa.ld_delta = Di; sa.delta_bias = w->dt_bias; sa.delta_softplus = 1;
+  sa.A = w->A;
+  sa.Bm = pp + R; sa.ld_B = PW;
+  sa.Cm = pp + R + N; sa.ld_C = PW;
+  sa.D = w->D;
+  sa.y = y; sa.ld_y = Di;
+  st = scan_check(&sa);
+  if (st != SSM_OK) return st;
+  st = dev(launch_scan_m1(to_scan(&sa), sub, stream), "mixer bwd: scan");
+  if (st != SSM_OK) return st;
+
+  // ---- the chain, backwards
+  auto bl_bwd = [&](const float* xin, int64_t k, int64_t ldx, const uint8_t* wp, const float* sc, const float* gn,
+                    const float* lat, int64_t n, const float* gy, int64_t ld_gy, float* gx, int64_t ld_gx,
+                    float* dw, float* ds) -> ssm_status {
+    ssm_bitlinear_bwd_args a{};
+    a.x = xin; a.x_dtype = SSM_F32; a.m = M; a.k = k; a.ldx = ldx;
+    a.norm_weight = gn; a.norm_eps = c->norm_eps;
+    a.w_packed = wp; a.w_scale = sc; a.n_out = n; a.group_size = 0;
+    a.w_latent = lat;
+    a.dy = gy; a.ld_dy = ld_gy;
+    a.dx = gx; a.ld_dx = ld_gx;
+    a.dw = dw; a.d_scale = ds;
+    SteArgs s2;
+    const ssm_status s3 = ste_check(&a, &s2);
+    if (s3 != SSM_OK) return s3;
+    return dev(launch_ste_bwd(s2, sub, stream), "mixer bwd: bitlinear bwd");
+  };
+  st = bl_bwd(y, Di, Di, w->w_out, w->s_out, w->g_out, gr.lat_out, Dm, dout, Dm, dy, Di, gr.dw_out, gr.ds_out);
+  if (st != SSM_OK) return st;
+  ssm_scan_bwd_args qa{};
+  qa.batch = batch; qa.seqlen = seqlen; qa.nheads = Di; qa.d_state = N;
+  qa.act_dtype = SSM_F32; qa.delta_softplus = 1;
+  qa.x = x; qa.ld_x = Di;
+  qa.delta = dl; qa.ld_delta = Di;
+  qa.delta_bias = w->dt_bias; qa.A = w->A;
+  qa.Bm = pp + R; qa.ld_B = PW;
+  qa.Cm = pp + R + N; qa.ld_C = PW;
+  qa.D = w->D; qa.h0 = nullptr;
+  qa.dy = dy; qa.ld_dy = Di;
+  qa.dx = dxs; qa.ddelta = ddl;
+  qa.dA = gr.dA ? gr.dA : (float*)(base + p.off_dA);
+  qa.dB = dB; qa.dC = dC;
+  qa.dD = gr.dD; qa.dbias = gr.d_dt_bias; qa.dh0 = nullptr;
+  ScanBwdArgs sb;
+  st = scan_bwd_check(&qa, &sb);
+  if (st != SSM_OK) return st;
+  st = dev(launch_scan_bwd(sb, sub, stream), "mixer bwd: scan bwd");
+  if (st != SSM_OK) return st;
+  // d dr into the first R columns of the x_proj output's gradient, then dB and dC
+  st = bl_bwd(pp, R, PW, w->w_dt, w->s_dt, w->g_dt, gr.lat_dt, Di, ddl, Di, dp, PW, gr.dw_dt, gr.ds_dt);
+  if (st != SSM_OK) return st;
+  st = dev(launch_copy_cols(dB, M, N, dp + R, PW, stream), "mixer bwd: dB");
+  if (st != SSM_OK) return st;
+  st = dev(launch_copy_cols(dC, M, N, dp + R + N, PW, stream), "mixer bwd: dC");
+  if (st != SSM_OK) return st;
+  st = bl_bwd(x, Di, Di, w->w_x, w->s_x, w->g_x, gr.lat_x, PW, dp, PW, dxp, Di, gr.dw_x, gr.ds_x);
+  if (st != SSM_OK) return st;
+  st = dev(launch_add_f32(dxs, dxp, M * Di, stream), "mixer bwd: dx");
+  if (st != SSM_OK) return st;
+  st = bl_bwd(u, Dm, Dm, w->w_in, w->s_in, w->g_in, gr.lat_in, Di, dxs, Di, du, Dm, gr.dw_in, gr.ds_in);
+  if (st != SSM_OK) return st;
+  if (add_residual) return dev(launch_add_f32(du, dout, M * Dm, stream), "mixer bwd: residual");
+  return SSM_OK;
+}
+
+}  // extern "C"

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import ternary_weight_selective_amd as tws
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = tws.lib()
-    assert tws.ssm_abi_version() == 5
+    assert tws.ssm_abi_version() == 6
     for s in range(8):
         assert L.ssm_status_string(s)
     assert tws.ssm_packed_row_bytes(8) == 4
@@ -300,6 +301,50 @@ def test_scan_bwd_rejects():
         b = tws.ScanBwdArgs.from_buffer_copy(a)
         setattr(b, field, val)
         assert L.ssm_selective_scan_bwd(ctypes.byref(b), FAKE, 1 << 30, None) == status, field
+
+
+def test_mixer_bwd_rejects():
+    L = tws.lib()
+    w = tws.MixerWeights()
+    for name, _ in tws.MixerWeights._fields_:
+        setattr(w, name, FAKE)
+    g = tws.MixerGrads()
+    good = tws.mixer_config(0, 64, 128, 16, dt_rank=8)
+    need = L.ssm_mixer_bwd_workspace_bytes(ctypes.byref(good), 2, 64)
+    assert need >= L.ssm_mixer_workspace_bytes(ctypes.byref(good), 2, 64)
+    bwd = L.ssm_mixer_bwd
+    U, DOUT, DU, WS = FAKE, FAKE + 4096, FAKE + 8192, FAKE + 65536
+    for cfg in (tws.mixer_config(1, 64, 128, 16, nheads=2, headdim=64),
+                tws.mixer_config(0, 64, 128, 16, dt_rank=8, gated=1, d_conv=4),
+                tws.mixer_config(0, 64, 128, 16, dt_rank=8, fp_proj=1),
+                tws.mixer_config(0, 64, 128, 16, dt_rank=8, act_dtype=torch.bfloat16),
+                tws.mixer_config(0, 64, 128, 12, dt_rank=8)):
+        assert L.ssm_mixer_bwd_workspace_bytes(ctypes.byref(cfg), 2, 64) == 0
+        assert bwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(g), U, DOUT, DU, 2, 64, 1, WS, 1 << 30,
+                   None) == UNSUPPORTED
+    # more time chunks than the scan backward takes
+    assert L.ssm_mixer_bwd_workspace_bytes(ctypes.byref(good), 1, 65535 * 16 + 1) == 0
+    assert bwd(ctypes.byref(good), ctypes.byref(w), ctypes.byref(g), U, DOUT, DU, 1, 65535 * 16 + 1, 1, WS, 1 << 40,
+               None) == UNSUPPORTED
+    assert bwd(ctypes.byref(good), ctypes.byref(tws.MixerWeights()), ctypes.byref(g), U, DOUT, DU, 2, 64, 1, WS,
+               1 << 30, None) == NULL
+    g2 = tws.MixerGrads()
+    g2.ds_in, g2.dw_in = FAKE, FAKE  # a scale gradient without the latent weights
+    assert bwd(ctypes.byref(good), ctypes.byref(w), ctypes.byref(g2), U, DOUT, DU, 2, 64, 1, WS, 1 << 30,
+               None) == NULL
+    assert bwd(ctypes.byref(good), ctypes.byref(w), ctypes.byref(g), U, DOUT, None, 2, 64, 1, WS, 1 << 30,
+               None) == NULL
+    assert bwd(ctypes.byref(good), ctypes.byref(w), ctypes.byref(g), U, DOUT, U, 2, 64, 1, WS, 1 << 30,
+               None) == SHAPE
+    assert bwd(ctypes.byref(good), ctypes.byref(w), ctypes.byref(g), U, DOUT, DU + 4, 2, 64, 1, WS, 1 << 30,
+               None) == ALIGN
+    assert bwd(ctypes.byref(good), ctypes.byref(w), ctypes.byref(g), U, DOUT, DU, 2, 64, 1, WS, need - 1,
+               None) == WORKSPACE
+    assert bwd(ctypes.byref(good), ctypes.byref(w), ctypes.byref(g), U, DOUT, DU, 2, 64, 1, WS + 64, 1 << 30,
+               None) == ALIGN
+    # nothing to do for an empty batch, once the workspace is there
+    assert bwd(ctypes.byref(good), ctypes.byref(w), ctypes.byref(g), None, None, None, 0, 64, 1, WS, 1 << 30,
+               None) == OK
 
 
 def test_conv_rejects():

@@ -689,3 +689,67 @@ def test_scan_bwd_parity(batch, L, H, N, dt, with_h0):
                                     delta_bias=p["dt_bias"], h0=h0)
     for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dbias", "dh0"):
         assert rel_err(host(got[k]).reshape(ref[k].shape), ref[k]) <= 2e-4, k
+
+
+# ------------------------------------------------------------------ mixer backward (STE)
+
+MIXER_BWD_CASES = [  # (workload, batch, seqlen, residual, latents, gains)
+    ("bitssm_tiny", 2, 64, True, True, False),
+    ("bitssm_tiny", 1, 37, False, False, True),   # ragged time (one partial scan chunk), RMSNorm gains
+    ("bitssm_tiny", 3, 5, True, True, True),      # shorter than one time chunk
+    ("trissm", 2, 256, True, True, False),         # TriSSM width and length
+    ("trissm", 64, 256, True, True, False),        # the full TriSSM training batch (64 x 256 tokens)
+]
+
+
+def _ds_bound(dw, codes, scale, w_lat):
+    """Sum of the magnitudes of the scale gradient's terms (it sums terms of both signs)."""
+    v = np.asarray(w_lat, np.float64) / float(np.asarray(scale).ravel()[0])
+    fac = np.where(np.abs(v) <= 1.0, codes - v, codes)
+    return float(np.abs(np.asarray(dw, np.float64) * fac).sum())
+
+
+@pytest.mark.parametrize("name,batch,seqlen,residual,latents,gains", MIXER_BWD_CASES)
+def test_mixer_bwd_parity(name, batch, seqlen, residual, latents, gains):
+    """Backward of one Mamba-1 kind mixer layer under the straight-through estimators (forward
+    evaluated again, then out_proj, scan, dt_proj, x_proj and in_proj backwards) against the
+    oracle's fp64 chain: every gradient norm-wise to 5e-4 (fp32 intermediates on the GPU; an
+    activation code that the forward's last-ulp differences move by one step shifts the result by
+    about 1e-5), the scale gradients to 1e-4 of the sum of their terms' magnitudes."""
+    cfg = wl.CONFIGS[name].with_(batch=batch, seqlen=seqlen, layers=1)
+    lat, u = wl.mixer_problem(cfg, seed=batch + seqlen)
+    gw, ow = quantize_layer(cfg, lat[0])
+    if gains:
+        g = wl.rng(seqlen)
+        for pname, (_, k) in cfg.proj_shapes.items():
+            gv = (1.0 + 0.2 * wl.normal(g, (k,))).astype(np.float32)
+            gw["g_" + pname], ow["g_" + pname] = to_dev(gv), gv
+    dout = wl.normal(wl.rng(batch * seqlen), u.shape)
+    lats = {"lat_" + p: lat[0]["W_" + p] for p in cfg.proj_shapes} if latents else None
+    got = tws.ssm_mixer_bwd(gpu_config(cfg), gw, to_dev(u), to_dev(dout), add_residual=residual,
+                            latents={k: to_dev(v) for k, v in lats.items()} if latents else None)
+    ref = oracle.mixer_bwd(oracle_config(cfg), ow, u, dout, residual=residual, latents=lats)
+    errs = {k: rel_err(host(got[k]).reshape(np.shape(ref[k])), ref[k])
+            for k in ("du", "dw_in", "dw_x", "dw_dt", "dw_out", "dA", "dD", "d_dt_bias")}
+    print(name, batch, seqlen, {k: "%.1e" % e for k, e in errs.items()})
+    for k, e in errs.items():
+        assert e <= 5e-4, (k, e)
+    if latents:
+        for p in cfg.proj_shapes:
+            bound = _ds_bound(ref["dw_" + p], ow["c_" + p], ow["s_" + p], lats["lat_" + p])
+            assert abs(float(host(got["ds_" + p])[0]) - float(ref["ds_" + p][0])) <= 1e-4 * bound, p
+
+
+def test_mixer_bwd_empty_and_repeatable():
+    """No tokens: nothing is written and the call succeeds; two calls give identical gradients
+    (fixed summation order)."""
+    cfg = wl.CONFIGS["bitssm_tiny"].with_(batch=2, seqlen=40)
+    lat, u = wl.mixer_problem(cfg, seed=9)
+    gw, _ = quantize_layer(cfg, lat[0])
+    dout = wl.normal(wl.rng(10), u.shape)
+    a = tws.ssm_mixer_bwd(gpu_config(cfg), gw, to_dev(u), to_dev(dout))
+    b = tws.ssm_mixer_bwd(gpu_config(cfg), gw, to_dev(u), to_dev(dout))
+    for k in a:
+        np.testing.assert_array_equal(host(a[k]), host(b[k]), err_msg=k)
+    e = tws.ssm_mixer_bwd(gpu_config(cfg), gw, to_dev(u[:, :0]), to_dev(dout[:, :0]))
+    assert e["du"].shape == (2, 0, cfg.d_model)

@@ -974,3 +974,75 @@ def test_scan_bwd_matches_finite_differences(aps, P):
     for name, gname in names.items():
         fd = _fd_grad(lambda v: loss(name, v), base[name], h=1e-3)
         np.testing.assert_allclose(out[gname], fd, rtol=2e-3, atol=2e-4, err_msg=name)
+
+
+# ------------------------------------------------------------------ mixer backward
+
+def _bwd_layer(cfg, seed, gains=False):
+    lat, u = wl.mixer_problem(cfg, seed=seed)
+    w = _layer_codes(cfg, lat[0])
+    if gains:
+        g = wl.rng(seed + 1)
+        for name, (_, k) in cfg.proj_shapes.items():
+            w["g_" + name] = (1.0 + 0.2 * wl.normal(g, (k,))).astype(np.float32)
+    return lat[0], w, u
+
+
+def test_mixer_bwd_forward_is_the_mixer():
+    """The backward evaluates the forward again: its output equals the oracle mixer's, bit for bit."""
+    cfg = wl.CONFIGS["bitssm_tiny"].with_(seqlen=24)
+    _, w, u = _bwd_layer(cfg, 5, gains=True)
+    dout = wl.normal(wl.rng(6), u.shape)
+    for res in (True, False):
+        got = oracle.mixer_bwd(_cfg_dict(cfg), w, u, dout, residual=res)
+        np.testing.assert_array_equal(got["out"].astype(np.float64), oracle.mixer(_cfg_dict(cfg), w, u, residual=res))
+
+
+def test_mixer_bwd_zero_out_proj():
+    """All-zero out_proj codes: the layer is the identity (with the residual), so du = dout exactly
+    and nothing behind out_proj receives a gradient; out_proj's own weight gradient does not vanish."""
+    cfg = wl.CONFIGS["bitssm_tiny"].with_(seqlen=16)
+    _, w, u = _bwd_layer(cfg, 7)
+    w["c_out"] = np.zeros_like(w["c_out"])
+    dout = wl.normal(wl.rng(8), u.shape)
+    got = oracle.mixer_bwd(_cfg_dict(cfg), w, u, dout)
+    np.testing.assert_array_equal(got["du"], dout.astype(np.float64))
+    for k in ("dw_in", "dw_x", "dw_dt", "dA", "dD", "d_dt_bias"):
+        assert not np.any(got[k]), k
+    assert np.any(got["dw_out"])
+
+
+def test_mixer_bwd_a16_matches_finite_differences():
+    """With the activation quantiser removed (W1.58A16 projections) the estimators pass nothing
+    through a rounding, so the chain's result is the plain derivative of <dout, mixer(u)>: du, dA,
+    dD and the dt bias element by element, and each projection's weight gradient along its own
+    ternary codes (the derivative in that projection's scale), by central differences of the
+    oracle mixer (fp32 activations; steps large against their rounding)."""
+    cfg = wl.MixerConfig("fd", wl.MAMBA1, 8, 16, 4, batch=2, seqlen=5, dt_rank=4, act_bits=16)
+    _, w, u = _bwd_layer(cfg, 11, gains=True)
+    cd = _cfg_dict(cfg)
+    dout = wl.normal(wl.rng(12), u.shape).astype(np.float64)
+    got = oracle.mixer_bwd(cd, w, u, dout, residual=False)
+
+    def loss(**over):
+        q = dict(w)
+        uu = over.pop("u", u)
+        q.update(over)
+        return float(np.sum(dout * oracle.mixer(cd, q, uu, residual=False)))
+
+    h = 1e-3
+    fd = _fd_grad(lambda v: loss(u=v.astype(np.float32)), u.astype(np.float64), h=h)
+    np.testing.assert_allclose(got["du"], fd, rtol=3e-3, atol=3e-4)
+    for name, gname in (("A", "dA"), ("D", "dD"), ("dt_bias", "d_dt_bias")):
+        fd = _fd_grad(lambda v: loss(**{name: v.astype(np.float32)}), w[name].astype(np.float64), h=h)
+        np.testing.assert_allclose(got[gname], fd, rtol=3e-3, atol=3e-4, err_msg=name)
+    # the scales: Richardson-extrapolated differences with steps of 8 % and 4 % of the scale (the
+    # forward's fp32 activations leave ~1e-6 noise in the loss, which smaller steps would amplify);
+    # the dt projection's derivative is ~1e-4 here, so its bound is looser
+    for name, tol in (("in", 3e-3), ("x", 3e-3), ("dt", 5e-2), ("out", 3e-3)):
+        s = np.asarray(w["s_" + name], np.float64)
+        d1, d2 = (_fd_grad(lambda v: loss(**{"s_" + name: v.astype(np.float32)}), s, h=f * float(s[0]))[0]
+                  for f in (8e-2, 4e-2))
+        fd = (4 * d2 - d1) / 3
+        along = float(np.sum(got["dw_" + name] * w["c_" + name]))
+        assert abs(along - fd) <= tol * abs(fd), (name, along, fd)
