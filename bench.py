@@ -78,6 +78,7 @@ def parse_args():
     ap.add_argument("--decode-only", action="store_true", help="only the decode measurement (profiling runs)")
     ap.add_argument("--no-train", action="store_true", help="skip the BitLinear backward / QAT step measurement")
     ap.add_argument("--train-only", action="store_true", help="only the BitLinear backward / QAT step (profiling runs)")
+    ap.add_argument("--mixer-bwd-only", action="store_true", help="only the mixer layer backward (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run 3 plain device copies of 1 GiB (reference for HBM byte counters)")
     return ap.parse_args()
@@ -384,11 +385,23 @@ def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
     return out
 
 
-def train_bench(prob: Problem, steps: int, warmup: int) -> dict:
+def train_bench(prob: Problem, steps: int, warmup: int, parts=("projection", "scan", "mixer")) -> dict:
     """The training side of one ternary projection at the workload's shape (its out_proj: the
     largest k): straight-through-estimator backward (dx through RMSNorm, dW, the scale
     gradient) and one QAT step (SGD on latent weights and scales, re-ternarised under the
-    learned scales), each timed with HIP events over `steps` calls."""
+    learned scales), each timed with HIP events over `steps` calls; then the scan's backward and
+    the whole mixer layer's backward (parts selects which)."""
+    out = {}
+    if "projection" in parts:
+        out.update(_train_projection(prob, steps, warmup))
+    if "scan" in parts:
+        out.update(_train_scan(prob, steps, warmup))
+    if "mixer" in parts:
+        out.update(_train_mixer(prob, steps, warmup))
+    return out
+
+
+def _train_projection(prob: Problem, steps: int, warmup: int) -> dict:
     cfg = prob.cfg
     if "out" not in cfg.proj_shapes or cfg.is_fp("out") or cfg.act_bits != 8:
         return {}
@@ -441,6 +454,12 @@ def train_bench(prob: Problem, steps: int, warmup: int) -> dict:
     flops = 2 * (2.0 * M * n * k)  # the two dense contractions
     out["bwd_TFLOP/s"] = flops / (out["bwd_us"] * 1e-6) / 1e12
     out["zero_ratio"] = float(zc.item()) / (n * k)
+    return out
+
+
+def _train_scan(prob: Problem, steps: int, warmup: int) -> dict:
+    cfg, dev, out = prob.cfg, prob.dev, {}
+    g = wl.rng(8)
     if cfg.kind == wl.MAMBA1:  # the scan's backward at the workload's shape
         H, N = cfg.d_inner, cfg.d_state
         p = wl.scan_problem(cfg.batch, cfg.seqlen, H, 1, N, True, seed=5)
@@ -469,6 +488,12 @@ def train_bench(prob: Problem, steps: int, warmup: int) -> dict:
         Mt = cfg.tokens
         byts = Mt * (2 * H + 2 * N) * es + Mt * H * 4 + Mt * (2 * H + 2 * N) * 4
         out["scan_bwd_GBps"] = byts / (out["scan_bwd_us"] * 1e-6) / 1e9
+    return out
+
+
+def _train_mixer(prob: Problem, steps: int, warmup: int) -> dict:
+    cfg, dev, out = prob.cfg, prob.dev, {}
+    g = wl.rng(9)
     if cfg.kind == wl.MAMBA1 and not cfg.gated and cfg.fp_proj == 0 and prob.act == torch.float32:
         # the whole layer's backward (forward again, then the chain) for the stack's first layer
         lats = {"lat_" + p: torch.from_numpy(prob.lat0["W_" + p]).to(dev) for p in cfg.proj_shapes}
@@ -548,6 +573,10 @@ def main():
     prob = Problem(cfg, args.seed, dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+
+    if args.mixer_bwd_only:
+        print(json.dumps({"train": train_bench(prob, args.steps, args.warmup, parts=("mixer",))}))
+        return
 
     if args.train_only:
         print(json.dumps({"train_bitlinear": train_bench(prob, args.steps, args.warmup)}))
