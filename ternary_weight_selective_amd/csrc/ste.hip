@@ -3,9 +3,13 @@
 // straight-through estimators; Ternary Mamba abstract: grouped QAT with learnable quantisation
 // scales and the zero ratio they can collapse).  The estimator passes gradients through both
 // roundings: dx̂ = dy W̃ with W̃ = s q (the ternary codes times their scale), dW = dy^T x̃ with
-// x̃ the forward's int8 codes dequantised, then the RMSNorm backward.  The two contractions are
-// plain dense fp32 GEMMs (rocBLAS, dense.cpp); the kernels here rebuild the forward's codes,
-// the dequantised operands, the RMSNorm backward and the scale gradient.
+// x̃ the forward's int8 codes dequantised, then the RMSNorm backward.  With one scale per tensor
+// dx comes from k_ste_dx (the codes on the matrix cores, the RMSNorm backward in its epilogue);
+// with grouped scales dx̂ is a dense fp32 GEMM (rocBLAS, dense.cpp) followed by k_rms_bwd.  dW is
+// a dense fp32 GEMM.  The other kernels here rebuild the forward's codes, the dequantised
+// operands and the scale gradient.
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace ssm {
@@ -71,6 +75,180 @@ __global__ __launch_bounds__(256) void k_ste_weights(const uint32_t* __restrict_
     if (k < K) {
       const float sc = group ? scale[n * ng + k / group] : scale[0];
       wt[n * K + k] = sc * (float)cb[i];
+    }
+  }
+}
+
+// The ternary codes transposed and widened for k_ste_dx: qt[k][n] = q[n][k] as bf16 (exactly
+// -1, 0 or +1), zero for n >= N or k >= K (the padding of the matrix-core tiles); row stride np.
+// Thread per element of qt.  A packed word holds weights 16w .. 16w + 15; weight i of a word
+// sits in bits 2 (i / 4) + 8 (i % 4) (01 = +1, 11 = -1, 00 = 0).
+__global__ __launch_bounds__(256) void k_ste_codes_t(const uint32_t* __restrict__ W, int64_t N, int64_t K,
+                                                     int64_t row_words, int64_t np, int64_t kp,
+                                                     bf16_t* __restrict__ qt) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= kp * np) return;
+  const int64_t k = e / np, n = e % np;
+  bf16_t v = 0;
+  if (n < N && k < K) {
+    const int i = (int)(k % 16);
+    const uint32_t f = (W[n * row_words + k / 16] >> (2 * (i >> 2) + 8 * (i & 3))) & 3u;
+    v = f == 1u ? (bf16_t)0x3F80u : (f == 3u ? (bf16_t)0xBF80u : (bf16_t)0u);
+  }
+  qt[e] = v;
+}
+
+// dx for one scale per tensor, on the matrix cores: dx̂ = s (dy q) with bf16 MFMA 16x16x32, then
+// the RMSNorm backward in the epilogue, so dx̂ never reaches memory:
+//   dx = r g dx̂ - x (r^3 / K) sum_j g_j dx̂_j x_j.
+// The codes are exact in bf16.  dy enters as three bf16 terms, each the truncation of what the
+// previous ones leave (hi = trunc(dy), mid = trunc(dy - hi), lo = trunc(dy - hi - mid); every
+// difference is exact), which add up to dy within 2^-24 of its magnitude; their products are
+// accumulated in fp32, smallest first.
+// A block of 4 waves owns RW row tiles of 16 token rows; the 4 / RW waves of a row tile split the
+// ceil(K / 16) column tiles (16 columns each), TW per wave, so that narrow outputs spread over
+// rows rather than leave waves idle.  MFMA operands: A = dy (lane: row lane & 15, inner
+// elements 8 (lane >> 4) .. + 7 of the step), B = qt (lane: column lane & 15, the same inner
+// elements), C: lane holds rows 4 (lane >> 4) + 0..3 of column lane & 15.  Each row's dot
+// product is summed over the wave's tiles in order, over the 16 lanes of its column group
+// (xor 1, 2, 4, 8), then over the row tile's waves in order through LDS.
+template <int RW, int TW, typename Tin>
+__global__ __launch_bounds__(256) void k_ste_dx(const Tin* __restrict__ x, int64_t ldx, const float* __restrict__ dy,
+                                                int64_t ld_dy, int vec, const bf16_t* __restrict__ qt, int64_t np,
+                                                int64_t M, int K, int N, const float* __restrict__ gain,
+                                                const float* __restrict__ scale, const float* __restrict__ rs,
+                                                float* __restrict__ dx, int64_t ld_dx) {
+  constexpr int CWV = 4 / RW;  // waves per row tile
+  __shared__ float s_dot[4][16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w / CWV, cw = w % CWV;
+  const int64_t mb = (int64_t)blockIdx.x * 16 * RW;  // the block's first row (< M)
+  const int64_t m0 = mb + 16 * rt;                    // this wave's row tile (may start past M)
+  const int kt = (K + 15) / 16;
+  const int t0 = cw * TW;
+  const int ng = lane >> 4, nc = lane & 15;
+  int64_t arow = m0 + nc;
+  const bool arv = arow < M;
+  arow = arv ? arow : M - 1;
+  const float* dyr = dy + arow * ld_dy + 8 * ng;
+  v4f acc[TW];
+#pragma unroll
+  for (int j = 0; j < TW; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // the operands of step n0: dy values (raw) and the codes of the wave's tiles; the next step's
+  // are requested before this step's products
+  float a[8];
+  v4i bq[TW];
+  auto load_step = [&](int n0) {
+    if (vec && n0 + 32 <= N) {
+      const v4f u0 = *(const v4f*)(dyr + n0), u1 = *(const v4f*)(dyr + n0 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = u0[i];
+        a[4 + i] = u1[i];
+      }
+    } else {  // the ragged last step: clamped addresses; values past N are zeroed when used
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = n0 + 8 * ng + i;
+        a[i] = dyr[(n < N ? n : N - 1) - 8 * ng];
+      }
+    }
+    // tiles past the last read the last tile's codes (in bounds); their columns are never stored
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int tj = t0 + j < kt ? t0 + j : kt - 1;
+      bq[j] = *(const v4i*)(qt + ((tj * 16 + nc) * (int)np + n0 + 8 * ng));
+    }
+  };
+  load_step(0);
+#pragma unroll 1
+  for (int n0 = 0; n0 < N; n0 += 32) {
+    float ac[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ac[i] = (arv && n0 + 8 * ng + i < N) ? a[i] : 0.0f;
+    v8bf bc[TW];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) bc[j] = __builtin_bit_cast(v8bf, bq[j]);
+    if (n0 + 32 < N) load_step(n0 + 32);
+    v4i hi, mid, lo;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float v = ac[2 * p + e];
+        hb[e] = __float_as_uint(v) & 0xFFFF0000u;
+        const float r1 = v - __uint_as_float(hb[e]);
+        mb[e] = __float_as_uint(r1) & 0xFFFF0000u;
+        const float r2 = r1 - __uint_as_float(mb[e]);
+        lb[e] = __float_as_uint(r2) & 0xFFFF0000u;
+      }
+      hi[p] = (int)((hb[0] >> 16) | hb[1]);
+      mid[p] = (int)((mb[0] >> 16) | mb[1]);
+      lo[p] = (int)((lb[0] >> 16) | lb[1]);
+    }
+    const v8bf ah = __builtin_bit_cast(v8bf, hi), am = __builtin_bit_cast(v8bf, mid),
+               al = __builtin_bit_cast(v8bf, lo);
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bc[j], acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bc[j], acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bc[j], acc[j], 0, 0, 0);
+    }
+  }
+
+  // epilogue: g dx̂ and x of the lane's 4 rows and its column in each tile (32-bit offsets from
+  // the block's first row, which is uniform; rows past M read row M - 1 and are not stored)
+  const float sc = scale[0];
+  const Tin* xb = x + mb * ldx;
+  const int rows = (int)(M - m0 < 16 ? M - m0 : 16);  // valid rows of the tile (<= 0: none)
+  const int last = (int)(M - 1 - mb);                  // the last valid row, from the block's first
+  float xv[TW][4];
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int k = (t0 + j) * 16 + nc;
+    const bool kv = k < K;  // also false for tiles past the last
+    const int kcl = kv ? k : K - 1;
+    const float gv = gain ? gain[kcl] : 1.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lr = 4 * ng + q;
+      const int rb = 16 * rt + lr;
+      const float xr = ld_act(xb + ((rb < last ? rb : last) * (int)ldx + kcl));
+      const bool ok = kv && lr < rows;
+      xv[j][q] = ok ? xr : 0.0f;
+      const float gd = ok ? gv * (sc * acc[j][q]) : 0.0f;
+      acc[j][q] = gd;
+      part[q] = __builtin_fmaf(gd, xv[j][q], part[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) part[q] = part[q] + __shfl_xor(part[q], d, 64);
+  }
+  if (nc == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_dot[w][4 * ng + q] = part[q];
+  }
+  __syncthreads();
+  float* db = dx + mb * ld_dx;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int lr = 4 * ng + q;
+    const int rb = 16 * rt + lr;
+    float dot = s_dot[rt * CWV][lr];
+#pragma unroll
+    for (int c = 1; c < CWV; ++c) dot = dot + s_dot[rt * CWV + c][lr];
+    const float r = rs[mb + (rb < last ? rb : last)];
+    const float c = r * r * r / (float)K * dot;
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int k = (t0 + j) * 16 + nc;
+      if (k < K && lr < rows) db[rb * (int)ld_dx + k] = r * acc[j][q] - xv[j][q] * c;
     }
   }
 }
@@ -185,6 +363,32 @@ hipError_t launch_act_k(const SteArgs& a, float* xt, float* rs, hipStream_t s) {
   return hipGetLastError();
 }
 
+// k_ste_dx serves one scale per tensor and K <= 1024 (the accumulators of 16 tiles per wave).
+bool ste_dx_fused(const SteArgs& a) { return a.group == 0 && a.K <= 1024; }
+
+// (row tiles per block, column tiles per wave) by the number of column tiles: at least 8 tiles
+// per wave where K allows, so that each step's dy conversion feeds 24 products
+template <int RW, int TW, typename Tin>
+hipError_t launch_dx_rt(const SteArgs& a, const bf16_t* qt, int64_t np, const float* rs, int vec, hipStream_t s) {
+  hipLaunchKernelGGL((k_ste_dx<RW, TW, Tin>), dim3((unsigned)cdiv(a.M, 16 * RW)), dim3(256), 0, s, (const Tin*)a.x,
+                     a.ldx, a.dy, a.ld_dy, vec, qt, np, a.M, (int)a.K, (int)a.N, a.gain, a.scale, rs, a.dx, a.ld_dx);
+  return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t launch_dx_k(const SteArgs& a, const bf16_t* qt, int64_t np, const float* rs, hipStream_t s) {
+  const int vec = (a.ld_dy % 4 == 0) && ((uintptr_t)a.dy % 16 == 0);
+  const int64_t kt = cdiv(a.K, 16);
+  if (kt <= 1) return launch_dx_rt<4, 1, Tin>(a, qt, np, rs, vec, s);
+  if (kt <= 2) return launch_dx_rt<4, 2, Tin>(a, qt, np, rs, vec, s);
+  if (kt <= 4) return launch_dx_rt<4, 4, Tin>(a, qt, np, rs, vec, s);
+  if (kt <= 8) return launch_dx_rt<2, 4, Tin>(a, qt, np, rs, vec, s);
+  if (kt <= 16) return launch_dx_rt<2, 8, Tin>(a, qt, np, rs, vec, s);
+  if (kt <= 32) return launch_dx_rt<1, 8, Tin>(a, qt, np, rs, vec, s);
+  if (kt <= 64) return launch_dx_rt<1, 16, Tin>(a, qt, np, rs, vec, s);
+  return hipErrorInvalidValue;
+}
+
 template <typename Tin>
 hipError_t launch_rms_bwd_k(const SteArgs& a, const float* rs, const float* dxh, hipStream_t s) {
   const dim3 grid((unsigned)cdiv(a.M, 4)), block(256);
@@ -207,7 +411,8 @@ size_t ste_workspace(const SteArgs& a) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t b = al((size_t)a.M * a.K * 4);       // x̃
   b += al((size_t)a.M * 4);                   // r
-  b += al((size_t)a.N * a.K * 4);             // W̃
+  // W̃ (fp32 [N, K]), or for k_ste_dx the transposed bf16 codes (padded [K16, N32])
+  b += al(std::max((size_t)a.N * a.K * 4, (size_t)round_up(a.K, 16) * round_up(a.N, 32) * 2));
   b += al((size_t)a.M * a.K * 4);             // dx̂
   b += al((size_t)a.N * 4);                   // per-row scale partials
   const int64_t ch = dw_chunks(a.M, a.N, a.K);
@@ -221,21 +426,32 @@ hipError_t launch_ste_bwd(const SteArgs& a, void* ws, hipStream_t s) {
   char* p = (char*)ws;
   float* xt = (float*)p; p += al((size_t)a.M * a.K * 4);
   float* rs = (float*)p; p += al((size_t)a.M * 4);
-  float* wt = (float*)p; p += al((size_t)a.N * a.K * 4);
+  float* wt = (float*)p;
+  p += al(std::max((size_t)a.N * a.K * 4, (size_t)round_up(a.K, 16) * round_up(a.N, 32) * 2));
   float* dxh = (float*)p; p += al((size_t)a.M * a.K * 4);
   float* part = (float*)p; p += al((size_t)a.N * 4);
   float* dwp = (float*)p;
   hipError_t e = a.x_bf16 ? launch_act_k<bf16_t>(a, xt, rs, s) : launch_act_k<float>(a, xt, rs, s);
   if (e != hipSuccess) return e;
-  const int64_t words = a.N * a.w_row_words;
-  hipLaunchKernelGGL(k_ste_weights, dim3((unsigned)cdiv(words, 256)), dim3(256), 0, s, a.W, a.N, a.K, a.w_row_words,
-                     a.scale, a.group, wt);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // dx̂ [M, K] = dy [M, N] W̃ [N, K]
-  e = sgemm_rm(false, false, a.M, a.K, a.N, a.dy, a.ld_dy, wt, a.K, dxh, a.K, s);
-  if (e != hipSuccess) return e;
-  e = a.x_bf16 ? launch_rms_bwd_k<bf16_t>(a, rs, dxh, s) : launch_rms_bwd_k<float>(a, rs, dxh, s);
-  if (e != hipSuccess) return e;
+  if (ste_dx_fused(a)) {
+    const int64_t np = round_up(a.N, 32), kp = round_up(a.K, 16);
+    bf16_t* qt = (bf16_t*)wt;
+    hipLaunchKernelGGL(k_ste_codes_t, dim3((unsigned)cdiv(kp * np, 256)), dim3(256), 0, s, a.W, a.N, a.K,
+                       a.w_row_words, np, kp, qt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = a.x_bf16 ? launch_dx_k<bf16_t>(a, qt, np, rs, s) : launch_dx_k<float>(a, qt, np, rs, s);
+    if (e != hipSuccess) return e;
+  } else {
+    const int64_t words = a.N * a.w_row_words;
+    hipLaunchKernelGGL(k_ste_weights, dim3((unsigned)cdiv(words, 256)), dim3(256), 0, s, a.W, a.N, a.K,
+                       a.w_row_words, a.scale, a.group, wt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // dx̂ [M, K] = dy [M, N] W̃ [N, K]
+    e = sgemm_rm(false, false, a.M, a.K, a.N, a.dy, a.ld_dy, wt, a.K, dxh, a.K, s);
+    if (e != hipSuccess) return e;
+    e = a.x_bf16 ? launch_rms_bwd_k<bf16_t>(a, rs, dxh, s) : launch_rms_bwd_k<float>(a, rs, dxh, s);
+    if (e != hipSuccess) return e;
+  }
   if (a.dw) {  // dW [N, K] = dy^T [N, M] x̃ [M, K]
     const int64_t ch = dw_chunks(a.M, a.N, a.K);
     if (ch > 1) {

@@ -606,6 +606,10 @@ BWD_CASES = [  # (m, k, n, group, x dtype, gain)
     (1, 100, 30, 0, "f32", False),      # one row, ragged k
     (2048, 256, 192, 0, "f32", False),  # dW reduction split over token chunks
     (4096, 128, 96, 128, "bf16", True),
+    (50, 48, 40, 0, "f32", True),       # narrow output: four row tiles per block, rows past M
+    (300, 20, 100, 0, "f32", True),     # two column tiles, ragged k and n
+    (37, 1024, 70, 0, "bf16", False),   # 64 column tiles, 16 per wave
+    (129, 16, 512, 0, "f32", False),    # the dt projection's shape (one column tile)
 ]
 
 
