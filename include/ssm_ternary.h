@@ -301,14 +301,14 @@ ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
  * Supported: Mamba-1 kind, not gated, ternary projections (fp_proj 0), act_bits 8,
  * group_size 0, act_dtype SSM_F32 (else SSM_ERR_UNSUPPORTED).
  *  u [batch, seqlen, d_model] fp32; dout fp32, same shape; du fp32, same shape (written; may
- *  not alias u or dout; du and dout 16-byte aligned).  seqlen is limited as in
+ *  not alias u or dout).  seqlen is limited as in
  *  ssm_selective_scan_bwd.  batch * seqlen = 0 returns SSM_OK and writes nothing.  grads: NULL or a struct whose pointers are each NULL (not wanted) or
  *  device fp32 buffers, written: dw_* [n_out, k] (the latent-weight gradients; n_out, k those
  *  of the projection), ds_* [1] (scale gradients; each needs its dw_* and the latent weights
  *  lat_* [n_out, k]), dA [d_inner, d_state], dD and d_dt_bias [d_inner].
  *  workspace: ssm_mixer_bwd_workspace_bytes(c, batch, seqlen) bytes (0 for a configuration or
  *  size the call rejects), 256-byte aligned; it holds x, p, delta, y and the intermediate
- *  gradients (7 d_inner + 2 dt_rank + 6 d_state floats per token) plus the largest
+ *  gradients (6 d_inner + 2 dt_rank + 6 d_state floats per token) plus the largest
  *  workspace of the steps.  Sums are taken in a fixed order (results do not depend on timing).
  * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_UNSUPPORTED, SSM_ERR_ALIGN,
  * SSM_ERR_WORKSPACE, SSM_ERR_DEVICE.

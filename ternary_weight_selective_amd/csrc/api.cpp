@@ -734,7 +734,7 @@ namespace {
 struct MixBwdPlan {
   int64_t M = 0, PW = 0;
   size_t off_x = 0, off_p = 0, off_dl = 0, off_y = 0, off_dy = 0, off_dxs = 0, off_ddl = 0, off_dB = 0,
-         off_dC = 0, off_dA = 0, off_dp = 0, off_dxp = 0, off_sub = 0, total = 0;
+         off_dC = 0, off_dA = 0, off_dp = 0, off_sub = 0, total = 0;
 };
 
 ssm_status mixer_bwd_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, MixBwdPlan* p) {
@@ -771,7 +771,6 @@ ssm_status mixer_bwd_plan(const ssm_mixer_config* c, int64_t batch, int64_t seql
   p->off_dC = take((size_t)M * N * 4);
   p->off_dA = take((size_t)Di * N * 4);
   p->off_dp = take((size_t)M * p->PW * 4);
-  p->off_dxp = take((size_t)M * Di * 4);
   p->off_sub = off;
   // the largest of the steps' own workspaces (sizes depend on shapes only)
   size_t sub = 0;
@@ -832,8 +831,6 @@ ssm_status ssm_mixer_bwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
   if (p.M > 0 && (!u || !dout || !du)) return fail(SSM_ERR_NULL, "mixer bwd: u, dout and du are required");
   if (p.M > 0 && ((const void*)du == (const void*)u || du == dout))
     return fail(SSM_ERR_SHAPE, "mixer bwd: du may not alias u or dout");
-  if (p.M > 0 && (!aligned(du, 16) || !aligned(dout, 16)))
-    return fail(SSM_ERR_ALIGN, "mixer bwd: du and dout must be 16-byte aligned");
   if (!ws || wsb < p.total) return fail(SSM_ERR_WORKSPACE, "mixer bwd: workspace needs %zu bytes", p.total);
   if (!aligned(ws, 256)) return fail(SSM_ERR_ALIGN, "mixer bwd: workspace must be 256-byte aligned");
   if (p.M == 0) return SSM_OK;
@@ -850,7 +847,6 @@ ssm_status ssm_mixer_bwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
   float* dB = (float*)(base + p.off_dB);
   float* dC = (float*)(base + p.off_dC);
   float* dp = (float*)(base + p.off_dp);
-  float* dxp = (float*)(base + p.off_dxp);
 
   // ---- forward again, keeping x, p, delta and y
   auto bitlinear = [&](const void* xin, int64_t k, int64_t ldx, const uint8_t* wp, const float* sc, const float* gn,
@@ -890,7 +886,7 @@ ssm_status ssm_mixer_bwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
   // ---- the chain, backwards
   auto bl_bwd = [&](const float* xin, int64_t k, int64_t ldx, const uint8_t* wp, const float* sc, const float* gn,
                     const float* lat, int64_t n, const float* gy, int64_t ld_gy, float* gx, int64_t ld_gx,
-                    float* dw, float* ds) -> ssm_status {
+                    float* dw, float* ds, const float* add, int64_t ld_add) -> ssm_status {
     ssm_bitlinear_bwd_args a{};
     a.x = xin; a.x_dtype = SSM_F32; a.m = M; a.k = k; a.ldx = ldx;
     a.norm_weight = gn; a.norm_eps = c->norm_eps;
@@ -902,9 +898,10 @@ ssm_status ssm_mixer_bwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
     SteArgs s2;
     const ssm_status s3 = ste_check(&a, &s2);
     if (s3 != SSM_OK) return s3;
-    return dev(launch_ste_bwd(s2, sub, stream), "mixer bwd: bitlinear bwd");
+    return dev(launch_ste_bwd_add(s2, add, ld_add, sub, stream), "mixer bwd: bitlinear bwd");
   };
-  st = bl_bwd(y, Di, Di, w->w_out, w->s_out, w->g_out, gr.lat_out, Dm, dout, Dm, dy, Di, gr.dw_out, gr.ds_out);
+  st = bl_bwd(y, Di, Di, w->w_out, w->s_out, w->g_out, gr.lat_out, Dm, dout, Dm, dy, Di, gr.dw_out, gr.ds_out,
+              nullptr, 0);
   if (st != SSM_OK) return st;
   ssm_scan_bwd_args qa{};
   qa.batch = batch; qa.seqlen = seqlen; qa.nheads = Di; qa.d_state = N;
@@ -926,20 +923,17 @@ ssm_status ssm_mixer_bwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, 
   st = dev(launch_scan_bwd(sb, sub, stream), "mixer bwd: scan bwd");
   if (st != SSM_OK) return st;
   // d dr into the first R columns of the x_proj output's gradient, then dB and dC
-  st = bl_bwd(pp, R, PW, w->w_dt, w->s_dt, w->g_dt, gr.lat_dt, Di, ddl, Di, dp, PW, gr.dw_dt, gr.ds_dt);
+  st = bl_bwd(pp, R, PW, w->w_dt, w->s_dt, w->g_dt, gr.lat_dt, Di, ddl, Di, dp, PW, gr.dw_dt, gr.ds_dt, nullptr, 0);
   if (st != SSM_OK) return st;
   st = dev(launch_copy_cols(dB, M, N, dp + R, PW, stream), "mixer bwd: dB");
   if (st != SSM_OK) return st;
   st = dev(launch_copy_cols(dC, M, N, dp + R + N, PW, stream), "mixer bwd: dC");
   if (st != SSM_OK) return st;
-  st = bl_bwd(x, Di, Di, w->w_x, w->s_x, w->g_x, gr.lat_x, PW, dp, PW, dxp, Di, gr.dw_x, gr.ds_x);
+  // dx = dx_s + x_proj's dx, accumulated in place; du = in_proj's dx (+ dout)
+  st = bl_bwd(x, Di, Di, w->w_x, w->s_x, w->g_x, gr.lat_x, PW, dp, PW, dxs, Di, gr.dw_x, gr.ds_x, dxs, Di);
   if (st != SSM_OK) return st;
-  st = dev(launch_add_f32(dxs, dxp, M * Di, stream), "mixer bwd: dx");
-  if (st != SSM_OK) return st;
-  st = bl_bwd(u, Dm, Dm, w->w_in, w->s_in, w->g_in, gr.lat_in, Di, dxs, Di, du, Dm, gr.dw_in, gr.ds_in);
-  if (st != SSM_OK) return st;
-  if (add_residual) return dev(launch_add_f32(du, dout, M * Dm, stream), "mixer bwd: residual");
-  return SSM_OK;
+  return bl_bwd(u, Dm, Dm, w->w_in, w->s_in, w->g_in, gr.lat_in, Di, dxs, Di, du, Dm, gr.dw_in, gr.ds_in,
+                add_residual ? dout : nullptr, Dm);
 }
 
 }  // extern "C"

@@ -11,6 +11,7 @@
 #include <algorithm>
 
 #include "launch.hpp"
+#include "mixer_bwd.hpp"
 
 namespace ssm {
 
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void k_ste_dx(const Tin* __restrict__ x, int64
                                                 int64_t ld_dy, int vec, const bf16_t* __restrict__ qt, int64_t np,
                                                 int64_t M, int K, int N, const float* __restrict__ gain,
                                                 const float* __restrict__ scale, const float* __restrict__ rs,
-                                                float* __restrict__ dx, int64_t ld_dx) {
+                                                const float* add, int64_t ld_add, float* dx, int64_t ld_dx) {
   constexpr int CWV = 4 / RW;  // waves per row tile
   __shared__ float s_dot[4][16];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(256) void k_ste_dx(const Tin* __restrict__ x, int64
   for (int j = 0; j < TW; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   // the operands of step n0: dy values (raw) and the codes of the wave's tiles; the next step's
-  // are requested before this step's products
+  // are requested before this step's products.  (Requesting dy two steps ahead costs a wave per
+  // SIMD of occupancy and measured no faster.)
   float a[8];
   v4i bq[TW];
   auto load_step = [&](int n0) {
@@ -199,12 +201,20 @@ __global__ __launch_bounds__(256) void k_ste_dx(const Tin* __restrict__ x, int64
     }
   }
 
-  // epilogue: g dx̂ and x of the lane's 4 rows and its column in each tile (32-bit offsets from
-  // the block's first row, which is uniform; rows past M read row M - 1 and are not stored)
-  const float sc = scale[0];
+  // epilogue: g dx̂ and x at the lane's positions (rows 4 (lane >> 4) + 0..3 of the row tile,
+  // column lane & 15 of each tile); 32-bit offsets from the block's first row (uniform); rows past
+  // M read row M - 1 and columns past K column K - 1 (neither is stored).  (Requesting x before
+  // the contraction costs a wave per SIMD of occupancy and measured slower.)
   const Tin* xb = x + mb * ldx;
   const int rows = (int)(M - m0 < 16 ? M - m0 : 16);  // valid rows of the tile (<= 0: none)
   const int last = (int)(M - 1 - mb);                  // the last valid row, from the block's first
+  const float sc = scale[0];
+  float rq[4];  // the rows' RMSNorm scales, requested together with x
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rb = 16 * rt + 4 * ng + q;
+    rq[q] = rs[mb + (rb < last ? rb : last)];
+  }
   float xv[TW][4];
   float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -234,6 +244,27 @@ __global__ __launch_bounds__(256) void k_ste_dx(const Tin* __restrict__ x, int64
 #pragma unroll
     for (int q = 0; q < 4; ++q) s_dot[w][4 * ng + q] = part[q];
   }
+  // the accumulated input, from clamped positions with no lane-dependent condition (so that the
+  // loads are in flight together, across the barrier)
+  float av[TW][4];
+  if (add) {
+    const float* ab = add + mb * ld_add;
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int k = (t0 + j) * 16 + nc;
+      const int kcl = k < K ? k : K - 1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rb = 16 * rt + 4 * ng + q;
+        av[j][q] = ab[(rb < last ? rb : last) * (int)ld_add + kcl];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) av[j][q] = 0.0f;
+  }
   __syncthreads();
   float* db = dx + mb * ld_dx;
 #pragma unroll
@@ -243,12 +274,12 @@ __global__ __launch_bounds__(256) void k_ste_dx(const Tin* __restrict__ x, int64
     float dot = s_dot[rt * CWV][lr];
 #pragma unroll
     for (int c = 1; c < CWV; ++c) dot = dot + s_dot[rt * CWV + c][lr];
-    const float r = rs[mb + (rb < last ? rb : last)];
+    const float r = rq[q];
     const float c = r * r * r / (float)K * dot;
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
       const int k = (t0 + j) * 16 + nc;
-      if (k < K && lr < rows) db[rb * (int)ld_dx + k] = r * acc[j][q] - xv[j][q] * c;
+      if (k < K && lr < rows) db[rb * (int)ld_dx + k] = av[j][q] + (r * acc[j][q] - xv[j][q] * c);
     }
   }
 }
@@ -257,8 +288,8 @@ __global__ __launch_bounds__(256) void k_ste_dx(const Tin* __restrict__ x, int64
 template <int KPL, typename Tin>
 __global__ __launch_bounds__(256) void k_rms_bwd(const Tin* __restrict__ x, int64_t M, int K, int64_t ldx,
                                                  const float* __restrict__ gain, const float* __restrict__ rs,
-                                                 const float* __restrict__ dxh, float* __restrict__ dx,
-                                                 int64_t ld_dx) {
+                                                 const float* __restrict__ dxh, const float* add, int64_t ld_add,
+                                                 float* dx, int64_t ld_dx) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
@@ -278,7 +309,10 @@ __global__ __launch_bounds__(256) void k_rms_bwd(const Tin* __restrict__ x, int6
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int k = lane + 64 * i;
-    if (k < K) dx[row * ld_dx + k] = r * gd[i] - xv[i] * c;
+    if (k < K) {
+      const float v = r * gd[i] - xv[i] * c;
+      dx[row * ld_dx + k] = add ? add[row * ld_add + k] + v : v;
+    }
   }
 }
 
@@ -369,31 +403,35 @@ bool ste_dx_fused(const SteArgs& a) { return a.group == 0 && a.K <= 1024; }
 // (row tiles per block, column tiles per wave) by the number of column tiles: at least 8 tiles
 // per wave where K allows, so that each step's dy conversion feeds 24 products
 template <int RW, int TW, typename Tin>
-hipError_t launch_dx_rt(const SteArgs& a, const bf16_t* qt, int64_t np, const float* rs, int vec, hipStream_t s) {
+hipError_t launch_dx_rt(const SteArgs& a, const bf16_t* qt, int64_t np, const float* rs, int vec, const float* add,
+                        int64_t ld_add, hipStream_t s) {
   hipLaunchKernelGGL((k_ste_dx<RW, TW, Tin>), dim3((unsigned)cdiv(a.M, 16 * RW)), dim3(256), 0, s, (const Tin*)a.x,
-                     a.ldx, a.dy, a.ld_dy, vec, qt, np, a.M, (int)a.K, (int)a.N, a.gain, a.scale, rs, a.dx, a.ld_dx);
+                     a.ldx, a.dy, a.ld_dy, vec, qt, np, a.M, (int)a.K, (int)a.N, a.gain, a.scale, rs, add, ld_add,
+                     a.dx, a.ld_dx);
   return hipGetLastError();
 }
 
 template <typename Tin>
-hipError_t launch_dx_k(const SteArgs& a, const bf16_t* qt, int64_t np, const float* rs, hipStream_t s) {
+hipError_t launch_dx_k(const SteArgs& a, const bf16_t* qt, int64_t np, const float* rs, const float* add,
+                       int64_t ld_add, hipStream_t s) {
   const int vec = (a.ld_dy % 4 == 0) && ((uintptr_t)a.dy % 16 == 0);
   const int64_t kt = cdiv(a.K, 16);
-  if (kt <= 1) return launch_dx_rt<4, 1, Tin>(a, qt, np, rs, vec, s);
-  if (kt <= 2) return launch_dx_rt<4, 2, Tin>(a, qt, np, rs, vec, s);
-  if (kt <= 4) return launch_dx_rt<4, 4, Tin>(a, qt, np, rs, vec, s);
-  if (kt <= 8) return launch_dx_rt<2, 4, Tin>(a, qt, np, rs, vec, s);
-  if (kt <= 16) return launch_dx_rt<2, 8, Tin>(a, qt, np, rs, vec, s);
-  if (kt <= 32) return launch_dx_rt<1, 8, Tin>(a, qt, np, rs, vec, s);
-  if (kt <= 64) return launch_dx_rt<1, 16, Tin>(a, qt, np, rs, vec, s);
+  if (kt <= 1) return launch_dx_rt<4, 1, Tin>(a, qt, np, rs, vec, add, ld_add, s);
+  if (kt <= 2) return launch_dx_rt<4, 2, Tin>(a, qt, np, rs, vec, add, ld_add, s);
+  if (kt <= 4) return launch_dx_rt<4, 4, Tin>(a, qt, np, rs, vec, add, ld_add, s);
+  if (kt <= 8) return launch_dx_rt<2, 4, Tin>(a, qt, np, rs, vec, add, ld_add, s);
+  if (kt <= 16) return launch_dx_rt<2, 8, Tin>(a, qt, np, rs, vec, add, ld_add, s);
+  if (kt <= 32) return launch_dx_rt<1, 8, Tin>(a, qt, np, rs, vec, add, ld_add, s);
+  if (kt <= 64) return launch_dx_rt<1, 16, Tin>(a, qt, np, rs, vec, add, ld_add, s);
   return hipErrorInvalidValue;
 }
 
 template <typename Tin>
-hipError_t launch_rms_bwd_k(const SteArgs& a, const float* rs, const float* dxh, hipStream_t s) {
+hipError_t launch_rms_bwd_k(const SteArgs& a, const float* rs, const float* dxh, const float* add, int64_t ld_add,
+                            hipStream_t s) {
   const dim3 grid((unsigned)cdiv(a.M, 4)), block(256);
   const Tin* x = (const Tin*)a.x;
-#define SSM_RB(KK) hipLaunchKernelGGL((k_rms_bwd<KK, Tin>), grid, block, 0, s, x, a.M, (int)a.K, a.ldx, a.gain, rs, dxh, a.dx, a.ld_dx)
+#define SSM_RB(KK) hipLaunchKernelGGL((k_rms_bwd<KK, Tin>), grid, block, 0, s, x, a.M, (int)a.K, a.ldx, a.gain, rs, dxh, add, ld_add, a.dx, a.ld_dx)
   if (a.K <= 64) SSM_RB(1);
   else if (a.K <= 128) SSM_RB(2);
   else if (a.K <= 256) SSM_RB(4);
@@ -420,7 +458,9 @@ size_t ste_workspace(const SteArgs& a) {
   return b;
 }
 
-hipError_t launch_ste_bwd(const SteArgs& a, void* ws, hipStream_t s) {
+hipError_t launch_ste_bwd(const SteArgs& a, void* ws, hipStream_t s) { return launch_ste_bwd_add(a, nullptr, 0, ws, s); }
+
+hipError_t launch_ste_bwd_add(const SteArgs& a, const float* add, int64_t ld_add, void* ws, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   char* p = (char*)ws;
@@ -439,7 +479,7 @@ hipError_t launch_ste_bwd(const SteArgs& a, void* ws, hipStream_t s) {
     hipLaunchKernelGGL(k_ste_codes_t, dim3((unsigned)cdiv(kp * np, 256)), dim3(256), 0, s, a.W, a.N, a.K,
                        a.w_row_words, np, kp, qt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = a.x_bf16 ? launch_dx_k<bf16_t>(a, qt, np, rs, s) : launch_dx_k<float>(a, qt, np, rs, s);
+    e = a.x_bf16 ? launch_dx_k<bf16_t>(a, qt, np, rs, add, ld_add, s) : launch_dx_k<float>(a, qt, np, rs, add, ld_add, s);
     if (e != hipSuccess) return e;
   } else {
     const int64_t words = a.N * a.w_row_words;
@@ -449,7 +489,8 @@ hipError_t launch_ste_bwd(const SteArgs& a, void* ws, hipStream_t s) {
     // dx̂ [M, K] = dy [M, N] W̃ [N, K]
     e = sgemm_rm(false, false, a.M, a.K, a.N, a.dy, a.ld_dy, wt, a.K, dxh, a.K, s);
     if (e != hipSuccess) return e;
-    e = a.x_bf16 ? launch_rms_bwd_k<bf16_t>(a, rs, dxh, s) : launch_rms_bwd_k<float>(a, rs, dxh, s);
+    e = a.x_bf16 ? launch_rms_bwd_k<bf16_t>(a, rs, dxh, add, ld_add, s)
+                 : launch_rms_bwd_k<float>(a, rs, dxh, add, ld_add, s);
     if (e != hipSuccess) return e;
   }
   if (a.dw) {  // dW [N, K] = dy^T [N, M] x̃ [M, K]
