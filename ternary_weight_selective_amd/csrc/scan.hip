@@ -37,14 +37,16 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int RMAX = 64;
 
-// softplus(v) = log(1 + e^v), the identity above 20.  With z = e^v and u = 1 + z,
-// log1p(z) = log(u) * z / (u - 1) compensates the rounding of u; below z = 1e-4 the
-// series z - z^2 / 2 is used.  Branch-free, on the hardware exp2 / log2 / reciprocal.
+// softplus(v) = log(1 + e^v), the identity above 20.  With z = e^v and u = fl(1 + z), the
+// rounding of u is c = (u - 1) - z (exact while u < 2, and below an ulp of the result above),
+// and log1p(z) = log(u) - c / u + O(c^2); taking c for c / u changes the result by at most
+// |c| z / (1 + z) <= 2^-24 min(z, 1), below its own rounding.  Below z = 1e-4 the series
+// z - z^2 / 2 is used.  Branch-free, on the hardware exp2 and log2 (no reciprocal).
 __device__ __forceinline__ float softplus_f(float v) {
   const float z = __builtin_amdgcn_exp2f(v * LOG2E);
   const float u = 1.0f + z;
-  const float um1 = u - 1.0f;
-  const float big = (0.69314718055994531f * __builtin_amdgcn_logf(u)) * (z * __builtin_amdgcn_rcpf(um1));
+  const float c = (u - 1.0f) - z;
+  const float big = 0.69314718055994531f * __builtin_amdgcn_logf(u) - c;
   const float small = z * __builtin_fmaf(-0.5f, z, 1.0f);
   const float r = z < 1e-4f ? small : big;
   return v > 20.0f ? v : r;
