@@ -80,16 +80,19 @@ __global__ __launch_bounds__(256) void k_ste_weights(const uint32_t* __restrict_
   }
 }
 
-// The ternary codes transposed and widened for k_ste_dx: qt[k][n] = q[n][k] as bf16 (exactly
-// -1, 0 or +1), zero for n >= N or k >= K (the padding of the matrix-core tiles); row stride np.
-// Thread per element of qt.  A packed word holds weights 16w .. 16w + 15; weight i of a word
-// sits in bits 2 (i / 4) + 8 (i % 4) (01 = +1, 11 = -1, 00 = 0).
+// The ternary codes widened to bf16 (exactly -1, 0 or +1) in the order k_ste_dx reads them as
+// its B operand: for inner step s (32 values of n), column tile t (16 values of k) and lane l,
+// 8 consecutive elements hold q[n][k] for n = 32 s + 8 (l >> 4) + 0..7, k = 16 t + (l & 15), so
+// each fragment load of a wave is 1 KB contiguous.  Zero for n >= N or k >= K (the padding of
+// the tiles).  Thread per element.  A packed word holds weights 16w .. 16w + 15; weight i of a
+// word sits in bits 2 (i / 4) + 8 (i % 4) (01 = +1, 11 = -1, 00 = 0).
 __global__ __launch_bounds__(256) void k_ste_codes_t(const uint32_t* __restrict__ W, int64_t N, int64_t K,
                                                      int64_t row_words, int64_t np, int64_t kp,
                                                      bf16_t* __restrict__ qt) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= kp * np) return;
-  const int64_t k = e / np, n = e % np;
+  const int64_t kt = kp / 16, l = (e >> 3) & 63, rest = e >> 9;
+  const int64_t n = 32 * (rest / kt) + 8 * (l >> 4) + (e & 7), k = 16 * (rest % kt) + (l & 15);
   bf16_t v = 0;
   if (n < N && k < K) {
     const int i = (int)(k % 16);
@@ -110,7 +113,8 @@ __global__ __launch_bounds__(256) void k_ste_codes_t(const uint32_t* __restrict_
 // ceil(K / 16) column tiles (16 columns each), TW per wave, so that narrow outputs spread over
 // rows rather than leave waves idle.  MFMA operands: A = dy (lane: row lane & 15, inner
 // elements 8 (lane >> 4) .. + 7 of the step), B = qt (lane: column lane & 15, the same inner
-// elements), C: lane holds rows 4 (lane >> 4) + 0..3 of column lane & 15.  Each row's dot
+// elements; one contiguous 1 KB load per tile in k_ste_codes_t's order), C: lane holds rows
+// 4 (lane >> 4) + 0..3 of column lane & 15.  Each row's dot
 // product is summed over the wave's tiles in order, over the 16 lanes of its column group
 // (xor 1, 2, 4, 8), then over the row tile's waves in order through LDS.
 template <int RW, int TW, typename Tin>
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256) void k_ste_dx(const Tin* __restrict__ x, int64
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
       const int tj = t0 + j < kt ? t0 + j : kt - 1;
-      bq[j] = *(const v4i*)(qt + ((tj * 16 + nc) * (int)np + n0 + 8 * ng));
+      bq[j] = *(const v4i*)(qt + ((((n0 >> 5) * kt + tj) * 64 + lane) * 8));
     }
   };
   load_step(0);
