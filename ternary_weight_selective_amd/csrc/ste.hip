@@ -5,9 +5,10 @@
 // roundings: dx̂ = dy W̃ with W̃ = s q (the ternary codes times their scale), dW = dy^T x̃ with
 // x̃ the forward's int8 codes dequantised, then the RMSNorm backward.  With one scale per tensor
 // dx comes from k_ste_dx (the codes on the matrix cores, the RMSNorm backward in its epilogue);
-// with grouped scales dx̂ is a dense fp32 GEMM (rocBLAS, dense.cpp) followed by k_rms_bwd.  dW is
-// a dense fp32 GEMM.  The other kernels here rebuild the forward's codes, the dequantised
-// operands and the scale gradient.
+// with grouped scales dx̂ is a dense fp32 GEMM (rocBLAS, dense.cpp) followed by k_rms_bwd.  dW
+// comes from k_ste_dw (the activation codes on the matrix cores, split over token chunks).  The
+// other kernels here rebuild the forward's codes and the transposed weight codes, and take the
+// scale gradient.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -16,22 +17,26 @@
 namespace ssm {
 
 // One wave per token row: the forward's RMSNorm and absmax int8 codes in the forward's own
-// arithmetic order (so the codes are the forward's), then x̃ = q max(m, 1e-5) / 127 (fp64,
-// rounded once) and the row's RMSNorm scale r.
+// arithmetic order (so the codes are the forward's), kept as the codes q [M, K] and the row's
+// step max(m, 1e-5) / 127 (x̃ = q step), and the row's RMSNorm scale r.  Columns past K load
+// column K - 1 and are zeroed (no lane-dependent condition around the loads).
 template <int KPL, typename Tin>
 __global__ __launch_bounds__(256) void k_ste_act(const Tin* __restrict__ x, int64_t M, int K, int64_t ldx,
-                                                 const float* __restrict__ gain, float eps, float* __restrict__ xt,
-                                                 float* __restrict__ rs) {
+                                                 const float* __restrict__ gain, float eps, int8_t* __restrict__ xq,
+                                                 float* __restrict__ st, float* __restrict__ rs) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;  // uniform per wave
   const Tin* xr = x + row * ldx;
-  float v[KPL];
+  float v[KPL], gv[KPL];
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int k = lane + 64 * i;
-    v[i] = (k < K) ? ld_act(xr + k) : 0.0f;
+    const int kc = k < K ? k : K - 1;
+    const float xv = ld_act(xr + kc);
+    gv[i] = gain ? gain[kc] : 1.0f;
+    v[i] = k < K ? xv : 0.0f;
     s = __builtin_fmaf(v[i], v[i], s);
   }
   s = wave_sum_butterfly(s);
@@ -42,22 +47,140 @@ __global__ __launch_bounds__(256) void k_ste_act(const Tin* __restrict__ x, int6
   for (int i = 0; i < KPL; ++i) {
     const int k = lane + 64 * i;
     float t = v[i] * r;
-    if (gain) t = (k < K) ? t * gain[k] : 0.0f;
+    if (gain) t = (k < K) ? t * gv[i] : 0.0f;
     v[i] = t;
     m = fmaxf(m, fabsf(t));
   }
   m = wave_absmax(m);
   const float mf = fmaxf(m, 1e-5f);
   const float sigma = __fdiv_rn(127.0f, mf);
-  const double step = (double)mf / 127.0;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int k = lane + 64 * i;
     float q = rintf(v[i] * sigma);
     q = fminf(fmaxf(q, -128.0f), 127.0f);
-    if (k < K) xt[row * K + k] = (float)((double)q * step);
+    if (k < K) xq[row * K + k] = (int8_t)(int)q;
   }
-  if (lane == 0) rs[row] = r;
+  if (lane == 0) {
+    rs[row] = r;
+    st[row] = (float)((double)mf / 127.0);
+  }
+}
+
+// dW = dy^T x̃ over one token chunk per blockIdx.z, on the bf16 matrix cores.  x̃ = q st (int8
+// codes, exact in bf16, times the row's step), so dW[n][k] = sum_m (dy[m][n] st_m) q[m][k]; the
+// first factor is rounded once to fp32 and enters as three truncated bf16 terms (as in k_ste_dx),
+// so the products carry fp32 accuracy.  A block owns 64 x 64 outputs, its 4 waves 16 rows (n)
+// x 64 columns (k) each (4 tiles).  Per step of 32 tokens the block stages both operands in LDS
+// transposed ([n][m] and [k][m]), so that each MFMA fragment (8 consecutive tokens) is one 16-byte
+// read; a step's tokens are loaded into registers two steps ahead, and the LDS is
+// double-buffered (one barrier per step).  Tokens past the chunk and rows / columns
+// past N / K enter as zeros.  The chunk's partial dW goes to part[chunk][n][k] (fp32); the
+// chunks are added in order afterwards.
+constexpr int kDwB = 64;   // outputs per block in n and in k
+constexpr int kDwLS = 40;  // LDS row stride (bf16) of the transposed tiles: 32 tokens + padding
+__global__ __launch_bounds__(256) void k_ste_dw(const float* __restrict__ dy, int64_t ld_dy,
+                                                const int8_t* __restrict__ xq, const float* __restrict__ st, int64_t M,
+                                                int N, int K, int64_t chunk, float* __restrict__ part) {
+  __shared__ __align__(16) bf16_t s_a[2][3][kDwB * kDwLS];
+  __shared__ __align__(16) bf16_t s_b[2][kDwB * kDwLS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ng = lane >> 4, nc = lane & 15;
+  const int n0 = blockIdx.x * kDwB, k0 = blockIdx.y * kDwB;
+  const int64_t mb = (int64_t)blockIdx.z * chunk;
+  const int64_t me = mb + chunk < M ? mb + chunk : M;
+  // staging role: column c of the block (an n for dy, a k for the codes), tokens 8 mg .. 8 mg + 7
+  const int c = tid & 63, mg = tid >> 6;
+  const bool nv = n0 + c < N, kv = k0 + c < K;
+  const int ncl = nv ? n0 + c : N - 1, kcl = kv ? k0 + c : K - 1;
+  // two register sets of staged tokens: a step's tokens are requested two steps before they are
+  // written to LDS, so that a whole step's products and barrier cover their latency
+  struct Regs {
+    float a[8], s[8];
+    int8_t q[8];
+  } r0, r1;
+  auto load = [&](int64_t m0, Regs& r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = m0 + 8 * mg + i;
+      const int64_t mc = m < me ? m : me - 1;
+      r.a[i] = dy[mc * ld_dy + ncl];
+      r.s[i] = st[mc];
+      r.q[i] = xq[mc * K + kcl];
+    }
+  };
+  auto stage = [&](int64_t m0, const Regs& r, int buf) {
+    v4i hi, mid, lo, qb;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t hb[2], mbb[2], lb[2], qq[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * p + e;
+        const bool mv = m0 + 8 * mg + i < me;
+        const float v = (mv && nv) ? r.a[i] * r.s[i] : 0.0f;
+        hb[e] = __float_as_uint(v) & 0xFFFF0000u;
+        const float r1 = v - __uint_as_float(hb[e]);
+        mbb[e] = __float_as_uint(r1) & 0xFFFF0000u;
+        const float r2 = r1 - __uint_as_float(mbb[e]);
+        lb[e] = __float_as_uint(r2) & 0xFFFF0000u;
+        qq[e] = __float_as_uint((mv && kv) ? (float)r.q[i] : 0.0f) & 0xFFFF0000u;  // exact in bf16
+      }
+      hi[p] = (int)((hb[0] >> 16) | hb[1]);
+      mid[p] = (int)((mbb[0] >> 16) | mbb[1]);
+      lo[p] = (int)((lb[0] >> 16) | lb[1]);
+      qb[p] = (int)((qq[0] >> 16) | qq[1]);
+    }
+    const int off = c * kDwLS + 8 * mg;
+    *(v4i*)(&s_a[buf][0][off]) = lo;
+    *(v4i*)(&s_a[buf][1][off]) = mid;
+    *(v4i*)(&s_a[buf][2][off]) = hi;
+    *(v4i*)(&s_b[buf][off]) = qb;
+  };
+  v4f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  auto products = [&](int buf) {
+    const int aoff = (16 * w + nc) * kDwLS + 8 * ng;
+    const v8bf al = __builtin_bit_cast(v8bf, *(const v4i*)(&s_a[buf][0][aoff]));
+    const v8bf am = __builtin_bit_cast(v8bf, *(const v4i*)(&s_a[buf][1][aoff]));
+    const v8bf ah = __builtin_bit_cast(v8bf, *(const v4i*)(&s_a[buf][2][aoff]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v8bf b = __builtin_bit_cast(v8bf, *(const v4i*)(&s_b[buf][(16 * j + nc) * kDwLS + 8 * ng]));
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[j], 0, 0, 0);
+    }
+  };
+  if (mb < me) {
+    load(mb, r0);
+    if (mb + 32 < me) load(mb + 32, r1);
+    stage(mb, r0, 0);
+  }
+  // step m0 reads buffer 0, step m0 + 32 buffer 1; a buffer is rewritten after the next barrier
+  for (int64_t m0 = mb; m0 < me; m0 += 64) {
+    __syncthreads();
+    if (m0 + 64 < me) load(m0 + 64, r0);
+    products(0);
+    if (m0 + 32 >= me) break;
+    stage(m0 + 32, r1, 1);
+    __syncthreads();
+    if (m0 + 96 < me) load(m0 + 96, r1);
+    products(1);
+    if (m0 + 64 < me) stage(m0 + 64, r0, 0);
+  }
+  float* pc = part + (int64_t)blockIdx.z * N * K;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k = k0 + 16 * j + nc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 16 * w + 4 * ng + i;
+      if (n < N && k < K) pc[(int64_t)n * K + k] = acc[j][i];
+    }
+  }
 }
 
 // W̃[n, k] = s(n, k / group) q[n, k] (one scale when group == 0); thread per packed word.
@@ -355,24 +478,34 @@ __global__ void k_sum_rows(const float* __restrict__ part, int64_t n, float* __r
   if (lane == 0) out[0] = (float)s;
 }
 
-// dW = sum of the token chunks' partial products, in chunk order.
+// dW = sum of the token chunks' partial products, in chunk order; the loads of eight chunks are
+// issued together (clamped to the last chunk, whose extra values are not added).
 __global__ __launch_bounds__(256) void k_sum_chunks(const float* __restrict__ part, int64_t count, int64_t chunks,
                                                     float* __restrict__ dw) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
-  float s = part[i];
-  for (int64_t c = 1; c < chunks; ++c) s += part[c * count + i];
+  float s = 0.0f;
+  for (int64_t c0 = 0; c0 < chunks; c0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = part[(c0 + j < chunks ? c0 + j : chunks - 1) * count + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < chunks) s = (c0 + j == 0) ? v[0] : s + v[j];
+  }
   dw[i] = s;
 }
 
 namespace {
-// Token chunks for dW = dy^T x̃: the reduction over tokens is split so that the library sees
-// several (n x k x tokens / chunks) products (a single long reduction with a small output
-// leaves most of the chip idle), their partials kept within 64 MB.
-int64_t dw_chunks(int64_t M, int64_t N, int64_t K) {
-  int64_t c = 16;
-  while (c > 1 && (M % c != 0 || M / c < 512 || c * N * K * 4 > (64ll << 20))) c >>= 1;
-  return c;
+// Token chunks of k_ste_dw: enough blocks for the chip (about 512 with the 64 x 64 output tiles;
+// more chunks cost more in partial sums than they gain), chunks of at least 128 tokens (a
+// multiple of 32), partials within 64 MB.
+int64_t dw_chunk_len(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = cdiv(N, kDwB) * cdiv(K, kDwB);
+  int64_t c = std::min<int64_t>(64, std::max<int64_t>(1, cdiv(512, tiles)));
+  c = std::min(c, std::max<int64_t>(1, M / 128));
+  while (c > 1 && c * N * K * 4 > (64ll << 20)) --c;
+  return round_up(cdiv(M, c), 32);
 }
 }  // namespace
 
@@ -385,10 +518,10 @@ __global__ __launch_bounds__(256) void k_sgd(float* __restrict__ w, const float*
 
 namespace {
 template <typename Tin>
-hipError_t launch_act_k(const SteArgs& a, float* xt, float* rs, hipStream_t s) {
+hipError_t launch_act_k(const SteArgs& a, int8_t* xq, float* st, float* rs, hipStream_t s) {
   const dim3 grid((unsigned)cdiv(a.M, 4)), block(256);
   const Tin* x = (const Tin*)a.x;
-#define SSM_ACT(KK) hipLaunchKernelGGL((k_ste_act<KK, Tin>), grid, block, 0, s, x, a.M, (int)a.K, a.ldx, a.gain, a.eps, xt, rs)
+#define SSM_ACT(KK) hipLaunchKernelGGL((k_ste_act<KK, Tin>), grid, block, 0, s, x, a.M, (int)a.K, a.ldx, a.gain, a.eps, xq, st, rs)
   if (a.K <= 64) SSM_ACT(1);
   else if (a.K <= 128) SSM_ACT(2);
   else if (a.K <= 256) SSM_ACT(4);
@@ -451,13 +584,14 @@ hipError_t launch_rms_bwd_k(const SteArgs& a, const float* rs, const float* dxh,
 
 size_t ste_workspace(const SteArgs& a) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  size_t b = al((size_t)a.M * a.K * 4);       // x̃
+  size_t b = al((size_t)a.M * a.K);           // the activation codes q (x̃ = q st)
+  b += al((size_t)a.M * 4);                   // st
   b += al((size_t)a.M * 4);                   // r
   // W̃ (fp32 [N, K]), or for k_ste_dx the transposed bf16 codes (padded [K16, N32])
   b += al(std::max((size_t)a.N * a.K * 4, (size_t)round_up(a.K, 16) * round_up(a.N, 32) * 2));
   b += al((size_t)a.M * a.K * 4);             // dx̂
   b += al((size_t)a.N * 4);                   // per-row scale partials
-  const int64_t ch = dw_chunks(a.M, a.N, a.K);
+  const int64_t ch = a.M > 0 ? cdiv(a.M, dw_chunk_len(a.M, a.N, a.K)) : 1;
   if (ch > 1) b += al((size_t)ch * a.N * a.K * 4);  // dW partials per token chunk
   return b;
 }
@@ -468,14 +602,15 @@ hipError_t launch_ste_bwd_add(const SteArgs& a, const float* add, int64_t ld_add
   if (a.M == 0) return hipSuccess;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   char* p = (char*)ws;
-  float* xt = (float*)p; p += al((size_t)a.M * a.K * 4);
+  int8_t* xq = (int8_t*)p; p += al((size_t)a.M * a.K);
+  float* st = (float*)p; p += al((size_t)a.M * 4);
   float* rs = (float*)p; p += al((size_t)a.M * 4);
   float* wt = (float*)p;
   p += al(std::max((size_t)a.N * a.K * 4, (size_t)round_up(a.K, 16) * round_up(a.N, 32) * 2));
   float* dxh = (float*)p; p += al((size_t)a.M * a.K * 4);
   float* part = (float*)p; p += al((size_t)a.N * 4);
   float* dwp = (float*)p;
-  hipError_t e = a.x_bf16 ? launch_act_k<bf16_t>(a, xt, rs, s) : launch_act_k<float>(a, xt, rs, s);
+  hipError_t e = a.x_bf16 ? launch_act_k<bf16_t>(a, xq, st, rs, s) : launch_act_k<float>(a, xq, st, rs, s);
   if (e != hipSuccess) return e;
   if (ste_dx_fused(a)) {
     const int64_t np = round_up(a.N, 32), kp = round_up(a.K, 16);
@@ -497,19 +632,16 @@ hipError_t launch_ste_bwd_add(const SteArgs& a, const float* add, int64_t ld_add
                  : launch_rms_bwd_k<float>(a, rs, dxh, add, ld_add, s);
     if (e != hipSuccess) return e;
   }
-  if (a.dw) {  // dW [N, K] = dy^T [N, M] x̃ [M, K]
-    const int64_t ch = dw_chunks(a.M, a.N, a.K);
+  if (a.dw) {  // dW [N, K] = dy^T [N, M] x̃ [M, K], per token chunk, then the chunks in order
+    const int64_t cl = dw_chunk_len(a.M, a.N, a.K), ch = cdiv(a.M, cl);
+    const dim3 grid((unsigned)cdiv(a.N, kDwB), (unsigned)cdiv(a.K, kDwB), (unsigned)ch);
+    hipLaunchKernelGGL(k_ste_dw, grid, dim3(256), 0, s, a.dy, a.ld_dy, xq, st, a.M, (int)a.N, (int)a.K, cl,
+                       ch > 1 ? dwp : a.dw);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ch > 1) {
-      const int64_t mc = a.M / ch;
-      e = sgemm_rm_batched(true, false, a.N, a.K, mc, a.dy, a.ld_dy, mc * a.ld_dy, xt, a.K, mc * a.K, dwp, a.K,
-                           a.N * a.K, ch, s);
-      if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_sum_chunks, dim3((unsigned)cdiv(a.N * a.K, 256)), dim3(256), 0, s, dwp, a.N * a.K, ch,
                          a.dw);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-    } else {
-      e = sgemm_rm(true, false, a.N, a.K, a.M, a.dy, a.ld_dy, xt, a.K, a.dw, a.K, s);
-      if (e != hipSuccess) return e;
     }
   }
   if (a.dscale) {
