@@ -82,22 +82,4 @@ hipError_t sgemm_rm(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const flo
   return st == rocblas_status_success ? hipSuccess : hipErrorLaunchFailure;
 }
 
-hipError_t sgemm_rm_batched(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                            int64_t sa, const float* B, int64_t ldb, int64_t sb, float* C, int64_t ldc, int64_t sc,
-                            int64_t batch, hipStream_t s) {
-  if (M == 0 || N == 0 || batch == 0) return hipSuccess;
-  rocblas_handle h = nullptr;
-  hipError_t e = handle_for_device(&h);
-  if (e != hipSuccess) return e;
-  const float alpha = 1.0f, beta = 0.0f;
-  std::lock_guard<std::mutex> lock(g_mu);
-  if (rocblas_set_stream(h, s) != rocblas_status_success) return hipErrorInvalidValue;
-  const rocblas_status st = rocblas_sgemm_strided_batched(
-      h, tb ? rocblas_operation_transpose : rocblas_operation_none,
-      ta ? rocblas_operation_transpose : rocblas_operation_none, (rocblas_int)N, (rocblas_int)M, (rocblas_int)K,
-      &alpha, B, (rocblas_int)ldb, (rocblas_stride)sb, A, (rocblas_int)lda, (rocblas_stride)sa, &beta, C,
-      (rocblas_int)ldc, (rocblas_stride)sc, (rocblas_int)batch);
-  return st == rocblas_status_success ? hipSuccess : hipErrorLaunchFailure;
-}
-
 }  // namespace ssm

@@ -115,10 +115,6 @@ hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
 // row-major fp32 C[M, N] = op(A) op(B) (op: transposed when the flag is set), C overwritten
 hipError_t sgemm_rm(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                     const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t s);
-// the same over `batch` matrices at element strides sa, sb, sc
-hipError_t sgemm_rm_batched(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                            int64_t sa, const float* B, int64_t ldb, int64_t sb, float* C, int64_t ldc, int64_t sc,
-                            int64_t batch, hipStream_t s);
 
 // ---- straight-through-estimator backward of BitLinear and the QAT update (ste.hip)
 struct SteArgs {
