@@ -100,14 +100,19 @@ __global__ __launch_bounds__(256) void k_ste_dw(const float* __restrict__ dy, in
     float a[8], s[8];
     int8_t q[8];
   } r0, r1;
+  // 32-bit offsets from the chunk's first token (uniform bases)
+  const float* dyb = dy + mb * ld_dy;
+  const int8_t* xqb = xq + mb * K;
+  const float* stb = st + mb;
+  const int last = (int)(me - 1 - mb);
   auto load = [&](int64_t m0, Regs& r) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t m = m0 + 8 * mg + i;
-      const int64_t mc = m < me ? m : me - 1;
-      r.a[i] = dy[mc * ld_dy + ncl];
-      r.s[i] = st[mc];
-      r.q[i] = xq[mc * K + kcl];
+      const int m = (int)(m0 - mb) + 8 * mg + i;
+      const int mc = m < last ? m : last;
+      r.a[i] = dyb[mc * (int)ld_dy + ncl];
+      r.s[i] = stb[mc];
+      r.q[i] = xqb[mc * K + kcl];
     }
   };
   auto stage = [&](int64_t m0, const Regs& r, int buf) {
