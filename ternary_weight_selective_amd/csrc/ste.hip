@@ -504,12 +504,15 @@ __global__ __launch_bounds__(256) void k_sum_chunks(const float* __restrict__ pa
 namespace {
 // Token chunks of k_ste_dw: enough blocks for the chip (about 512 with the 64 x 64 output tiles;
 // more chunks cost more in partial sums than they gain), chunks of at least 128 tokens (a
-// multiple of 32), partials within 64 MB.
-int64_t dw_chunk_len(int64_t M, int64_t N, int64_t K) {
+// multiple of 32), partials within 64 MB, and short enough that the kernel's 32-bit offsets
+// within a chunk (tokens x max(ld_dy, K)) cannot overflow.
+int64_t dw_chunk_len(int64_t M, int64_t N, int64_t K, int64_t ld_dy) {
   const int64_t tiles = cdiv(N, kDwB) * cdiv(K, kDwB);
   int64_t c = std::min<int64_t>(64, std::max<int64_t>(1, cdiv(512, tiles)));
   c = std::min(c, std::max<int64_t>(1, M / 128));
   while (c > 1 && c * N * K * 4 > (64ll << 20)) --c;
+  const int64_t row = std::max(ld_dy, K);
+  while (round_up(cdiv(M, c), 32) * row >= (1ll << 31) - row) ++c;
   return round_up(cdiv(M, c), 32);
 }
 }  // namespace
@@ -596,7 +599,7 @@ size_t ste_workspace(const SteArgs& a) {
   b += al(std::max((size_t)a.N * a.K * 4, (size_t)round_up(a.K, 16) * round_up(a.N, 32) * 2));
   b += al((size_t)a.M * a.K * 4);             // dx̂
   b += al((size_t)a.N * 4);                   // per-row scale partials
-  const int64_t ch = a.M > 0 ? cdiv(a.M, dw_chunk_len(a.M, a.N, a.K)) : 1;
+  const int64_t ch = a.M > 0 ? cdiv(a.M, dw_chunk_len(a.M, a.N, a.K, a.ld_dy)) : 1;
   if (ch > 1) b += al((size_t)ch * a.N * a.K * 4);  // dW partials per token chunk
   return b;
 }
@@ -638,7 +641,7 @@ hipError_t launch_ste_bwd_add(const SteArgs& a, const float* add, int64_t ld_add
     if (e != hipSuccess) return e;
   }
   if (a.dw) {  // dW [N, K] = dy^T [N, M] x̃ [M, K], per token chunk, then the chunks in order
-    const int64_t cl = dw_chunk_len(a.M, a.N, a.K), ch = cdiv(a.M, cl);
+    const int64_t cl = dw_chunk_len(a.M, a.N, a.K, a.ld_dy), ch = cdiv(a.M, cl);
     const dim3 grid((unsigned)cdiv(a.N, kDwB), (unsigned)cdiv(a.K, kDwB), (unsigned)ch);
     hipLaunchKernelGGL(k_ste_dw, grid, dim3(256), 0, s, a.dy, a.ld_dy, xq, st, a.M, (int)a.N, (int)a.K, cl,
                        ch > 1 ? dwp : a.dw);
