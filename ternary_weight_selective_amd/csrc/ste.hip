@@ -70,35 +70,41 @@ __global__ __launch_bounds__(256) void k_ste_act(const Tin* __restrict__ x, int6
 // dW = dy^T x̃ over one token chunk per blockIdx.z, on the bf16 matrix cores.  x̃ = q st (int8
 // codes, exact in bf16, times the row's step), so dW[n][k] = sum_m (dy[m][n] st_m) q[m][k]; the
 // first factor is rounded once to fp32 and enters as three truncated bf16 terms (as in k_ste_dx),
-// so the products carry fp32 accuracy.  A block owns 64 x 64 outputs, its 4 waves 16 rows (n)
-// x 64 columns (k) each (4 tiles).  Per step of 32 tokens the block stages both operands in LDS
+// so the products carry fp32 accuracy.  A block owns 64 x 16 KT outputs, its 4 waves 16 rows (n)
+// x 16 KT columns (k) each (KT tiles).  Per step of 32 tokens the block stages both operands in LDS
 // transposed ([n][m] and [k][m]), so that each MFMA fragment (8 consecutive tokens) is one 16-byte
 // read; a step's tokens are loaded into registers two steps ahead, and the LDS is
 // double-buffered (one barrier per step).  Tokens past the chunk and rows / columns
 // past N / K enter as zeros.  The chunk's partial dW goes to part[chunk][n][k] (fp32); the
 // chunks are added in order afterwards.
-constexpr int kDwB = 64;   // outputs per block in n and in k
+constexpr int kDwB = 64;   // outputs per block in n
 constexpr int kDwLS = 40;  // LDS row stride (bf16) of the transposed tiles: 32 tokens + padding
+template <int KT>
 __global__ __launch_bounds__(256) void k_ste_dw(const float* __restrict__ dy, int64_t ld_dy,
                                                 const int8_t* __restrict__ xq, const float* __restrict__ st, int64_t M,
                                                 int N, int K, int64_t chunk, float* __restrict__ part) {
+  constexpr int KW = 16 * KT;   // outputs per block in k
+  constexpr int TPC = 256 / KW; // threads per staged code column
+  constexpr int TQ = 32 / TPC;  // tokens per thread of the code staging (8 or 16)
   __shared__ __align__(16) bf16_t s_a[2][3][kDwB * kDwLS];
-  __shared__ __align__(16) bf16_t s_b[2][kDwB * kDwLS];
+  __shared__ __align__(16) bf16_t s_b[2][KW * kDwLS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ng = lane >> 4, nc = lane & 15;
-  const int n0 = blockIdx.x * kDwB, k0 = blockIdx.y * kDwB;
+  const int n0 = blockIdx.x * kDwB, k0 = blockIdx.y * KW;
   const int64_t mb = (int64_t)blockIdx.z * chunk;
   const int64_t me = mb + chunk < M ? mb + chunk : M;
-  // staging role: column c of the block (an n for dy, a k for the codes), tokens 8 mg .. 8 mg + 7
+  // staging roles: dy column c (an n), tokens 8 mg .. 8 mg + 7; code column cq (a k), tokens
+  // TQ qg .. TQ qg + TQ - 1
   const int c = tid & 63, mg = tid >> 6;
-  const bool nv = n0 + c < N, kv = k0 + c < K;
-  const int ncl = nv ? n0 + c : N - 1, kcl = kv ? k0 + c : K - 1;
+  const int cq = tid % KW, qg = tid / KW;
+  const bool nv = n0 + c < N, kv = k0 + cq < K;
+  const int ncl = nv ? n0 + c : N - 1, kcl = kv ? k0 + cq : K - 1;
   // two register sets of staged tokens: a step's tokens are requested two steps before they are
   // written to LDS, so that a whole step's products and barrier cover their latency
   struct Regs {
     float a[8], s[8];
-    int8_t q[8];
+    int8_t q[TQ];
   } r0, r1;
   // 32-bit offsets from the chunk's first token (uniform bases)
   const float* dyb = dy + mb * ld_dy;
@@ -112,14 +118,18 @@ __global__ __launch_bounds__(256) void k_ste_dw(const float* __restrict__ dy, in
       const int mc = m < last ? m : last;
       r.a[i] = dyb[mc * (int)ld_dy + ncl];
       r.s[i] = stb[mc];
-      r.q[i] = xqb[mc * K + kcl];
+    }
+#pragma unroll
+    for (int i = 0; i < TQ; ++i) {
+      const int m = (int)(m0 - mb) + TQ * qg + i;
+      r.q[i] = xqb[(m < last ? m : last) * K + kcl];
     }
   };
   auto stage = [&](int64_t m0, const Regs& r, int buf) {
-    v4i hi, mid, lo, qb;
+    v4i hi, mid, lo;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      uint32_t hb[2], mbb[2], lb[2], qq[2];
+      uint32_t hb[2], mbb[2], lb[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int i = 2 * p + e;
@@ -130,29 +140,42 @@ __global__ __launch_bounds__(256) void k_ste_dw(const float* __restrict__ dy, in
         mbb[e] = __float_as_uint(r1) & 0xFFFF0000u;
         const float r2 = r1 - __uint_as_float(mbb[e]);
         lb[e] = __float_as_uint(r2) & 0xFFFF0000u;
-        qq[e] = __float_as_uint((mv && kv) ? (float)r.q[i] : 0.0f) & 0xFFFF0000u;  // exact in bf16
       }
       hi[p] = (int)((hb[0] >> 16) | hb[1]);
       mid[p] = (int)((mbb[0] >> 16) | mbb[1]);
       lo[p] = (int)((lb[0] >> 16) | lb[1]);
-      qb[p] = (int)((qq[0] >> 16) | qq[1]);
     }
     const int off = c * kDwLS + 8 * mg;
     *(v4i*)(&s_a[buf][0][off]) = lo;
     *(v4i*)(&s_a[buf][1][off]) = mid;
     *(v4i*)(&s_a[buf][2][off]) = hi;
-    *(v4i*)(&s_b[buf][off]) = qb;
-  };
-  v4f acc[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int g = 0; g < TQ / 8; ++g) {
+      v4i qb;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t qq[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 8 * g + 2 * p + e;
+          const bool mv = m0 + TQ * qg + i < me;
+          qq[e] = __float_as_uint((mv && kv) ? (float)r.q[i] : 0.0f) & 0xFFFF0000u;  // exact in bf16
+        }
+        qb[p] = (int)((qq[0] >> 16) | qq[1]);
+      }
+      *(v4i*)(&s_b[buf][cq * kDwLS + TQ * qg + 8 * g]) = qb;
+    }
+  };
+  v4f acc[KT];
+#pragma unroll
+  for (int j = 0; j < KT; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   auto products = [&](int buf) {
     const int aoff = (16 * w + nc) * kDwLS + 8 * ng;
     const v8bf al = __builtin_bit_cast(v8bf, *(const v4i*)(&s_a[buf][0][aoff]));
     const v8bf am = __builtin_bit_cast(v8bf, *(const v4i*)(&s_a[buf][1][aoff]));
     const v8bf ah = __builtin_bit_cast(v8bf, *(const v4i*)(&s_a[buf][2][aoff]));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < KT; ++j) {
       const v8bf b = __builtin_bit_cast(v8bf, *(const v4i*)(&s_b[buf][(16 * j + nc) * kDwLS + 8 * ng]));
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[j], 0, 0, 0);
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, b, acc[j], 0, 0, 0);
@@ -178,7 +201,7 @@ __global__ __launch_bounds__(256) void k_ste_dw(const float* __restrict__ dy, in
   }
   float* pc = part + (int64_t)blockIdx.z * N * K;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < KT; ++j) {
     const int k = k0 + 16 * j + nc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -502,12 +525,15 @@ __global__ __launch_bounds__(256) void k_sum_chunks(const float* __restrict__ pa
 }
 
 namespace {
-// Token chunks of k_ste_dw: enough blocks for the chip (about 512 with the 64 x 64 output tiles;
+// Token chunks of k_ste_dw: enough blocks for the chip (about 512 output tiles x chunks;
 // more chunks cost more in partial sums than they gain), chunks of at least 128 tokens (a
 // multiple of 32), partials within 64 MB, and short enough that the kernel's 32-bit offsets
 // within a chunk (tokens x max(ld_dy, K)) cannot overflow.
+// column tiles per wave of k_ste_dw: 8 (128 outputs per block in k), 4 for narrow K
+int dw_kt(int64_t K) { return K <= 64 ? 4 : 8; }
+
 int64_t dw_chunk_len(int64_t M, int64_t N, int64_t K, int64_t ld_dy) {
-  const int64_t tiles = cdiv(N, kDwB) * cdiv(K, kDwB);
+  const int64_t tiles = cdiv(N, kDwB) * cdiv(K, 16 * dw_kt(K));
   int64_t c = std::min<int64_t>(64, std::max<int64_t>(1, cdiv(512, tiles)));
   c = std::min(c, std::max<int64_t>(1, M / 128));
   while (c > 1 && c * N * K * 4 > (64ll << 20)) --c;
@@ -642,9 +668,14 @@ hipError_t launch_ste_bwd_add(const SteArgs& a, const float* add, int64_t ld_add
   }
   if (a.dw) {  // dW [N, K] = dy^T [N, M] x̃ [M, K], per token chunk, then the chunks in order
     const int64_t cl = dw_chunk_len(a.M, a.N, a.K, a.ld_dy), ch = cdiv(a.M, cl);
-    const dim3 grid((unsigned)cdiv(a.N, kDwB), (unsigned)cdiv(a.K, kDwB), (unsigned)ch);
-    hipLaunchKernelGGL(k_ste_dw, grid, dim3(256), 0, s, a.dy, a.ld_dy, xq, st, a.M, (int)a.N, (int)a.K, cl,
-                       ch > 1 ? dwp : a.dw);
+    const int kt = dw_kt(a.K);
+    const dim3 grid((unsigned)cdiv(a.N, kDwB), (unsigned)cdiv(a.K, 16 * kt), (unsigned)ch);
+    if (kt == 4)
+      hipLaunchKernelGGL(k_ste_dw<4>, grid, dim3(256), 0, s, a.dy, a.ld_dy, xq, st, a.M, (int)a.N, (int)a.K, cl,
+                         ch > 1 ? dwp : a.dw);
+    else
+      hipLaunchKernelGGL(k_ste_dw<8>, grid, dim3(256), 0, s, a.dy, a.ld_dy, xq, st, a.M, (int)a.N, (int)a.K, cl,
+                         ch > 1 ? dwp : a.dw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ch > 1) {
       hipLaunchKernelGGL(k_sum_chunks, dim3((unsigned)cdiv(a.N * a.K, 256)), dim3(256), 0, s, dwp, a.N * a.K, ch,
