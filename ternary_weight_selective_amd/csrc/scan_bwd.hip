@@ -31,8 +31,8 @@ constexpr int kCPBb = 64;
 __device__ __forceinline__ float softplus_b(float v) {
   const float z = __builtin_amdgcn_exp2f(v * kLog2eB);
   const float u = 1.0f + z;
-  const float um1 = u - 1.0f;
-  const float big = (0.69314718055994531f * __builtin_amdgcn_logf(u)) * (z * __builtin_amdgcn_rcpf(um1));
+  const float c = (u - 1.0f) - z;  // the rounding of u, subtracted from log(u)
+  const float big = 0.69314718055994531f * __builtin_amdgcn_logf(u) - c;
   const float small = z * __builtin_fmaf(-0.5f, z, 1.0f);
   const float r = z < 1e-4f ? small : big;
   return v > 20.0f ? v : r;
