@@ -276,6 +276,11 @@ ssm_status ste_check(const ssm_bitlinear_bwd_args* a, SteArgs* o) {
     return fail(SSM_ERR_SHAPE, "bitlinear bwd: m >= 0, 1 <= k <= %lld, n_out >= 1", (long long)kMaxK);
   if (a->ldx < a->k || a->ld_dy < a->n_out || a->ld_dx < a->k)
     return fail(SSM_ERR_SHAPE, "bitlinear bwd: a row stride is smaller than its row");
+  // the kernels address a tile of up to 32 rows with 32-bit offsets from its first row
+  const int64_t kMaxLd = ((1ll << 31) - 1) / 33;
+  if (a->ldx > kMaxLd || a->ld_dy > kMaxLd || a->ld_dx > kMaxLd)
+    return fail(SSM_ERR_UNSUPPORTED, "bitlinear bwd: row strides above %lld elements are not supported",
+                (long long)kMaxLd);
   if (a->group_size < 0 || (a->group_size > 0 && (a->group_size % 64 != 0 || a->k % a->group_size != 0)))
     return fail(SSM_ERR_SHAPE, "bitlinear bwd: group_size must be 0 or a multiple of 64 dividing k");
   if (!a->w_packed || !a->w_scale) return fail(SSM_ERR_NULL, "bitlinear bwd: w_packed / w_scale is NULL");

@@ -127,11 +127,15 @@ __device__ __forceinline__ uint16_t bf_bits(float f) { return f32_to_bf16(f); }
 __device__ __forceinline__ float bf_val(uint16_t b) { return bf16_to_f32(b); }
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
-// softplus(v) = log(1 + e^v) (the identity above 20) on the hardware exp2 / log2; below
-// e^v = 1e-4 the series e^v (1 - e^v / 2).
+// softplus(v) = log(1 + e^v) (the identity above 20) on the hardware exp2 / log2, with the
+// rounding error c = (u - 1) - z of u = fl(1 + z) subtracted while u < 2 (where it dominates
+// the error of log(u) relative to the small result); below e^v = 1e-4 the series
+// e^v (1 - e^v / 2).
 __device__ __forceinline__ float softplus_hw(float v) {
   const float z = exp_hw(v);
-  const float big = 0.69314718055994531f * __builtin_amdgcn_logf(1.0f + z);
+  const float u = 1.0f + z;
+  const float c = u < 2.0f ? (u - 1.0f) - z : 0.0f;
+  const float big = 0.69314718055994531f * __builtin_amdgcn_logf(u) - c;
   const float small = z * __builtin_fmaf(-0.5f, z, 1.0f);
   const float r = z < 1e-4f ? small : big;
   return v > 20.0f ? v : r;

@@ -538,7 +538,7 @@ int64_t dw_chunk_len(int64_t M, int64_t N, int64_t K, int64_t ld_dy) {
   c = std::min(c, std::max<int64_t>(1, M / 128));
   while (c > 1 && c * N * K * 4 > (64ll << 20)) --c;
   const int64_t row = std::max(ld_dy, K);
-  while (round_up(cdiv(M, c), 32) * row >= (1ll << 31) - row) ++c;
+  while (c < M && round_up(cdiv(M, c), 32) * row >= (1ll << 31) - row) ++c;  // ends: 33 row < 2^31 (checked)
   return round_up(cdiv(M, c), 32);
 }
 }  // namespace

@@ -1,4 +1,7 @@
 """Shared helpers of the GPU parity tests (marshalling seeded inputs to both sides)."""
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -17,6 +20,55 @@ def rel_err(got, ref) -> float:
     ref = np.asarray(ref, dtype=np.float64)
     den = np.linalg.norm(ref)
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def elem_err(got, ref) -> np.ndarray:
+    """Per element |y - y_ref| / (|y_ref| + rms(y_ref)): a localised error (one channel, the
+    last chunk of each sequence) shows at full size here, where the norm-wise ratio dilutes it."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    return np.abs(got - ref) / (np.abs(ref) + (rms if rms > 0 else 1.0))
+
+
+def check(got, ref, tol: float, *, elem: float | None = None, frac: float = 0.0, what: str = "") -> dict:
+    """Float parity of one output tensor.
+      norm-wise relative error <= tol;
+      every element's elem_err <= elem (default: tol itself);
+      at most a fraction `frac` of the elements above tol (default: none).
+    The looser `elem` / `frac` are for outputs behind a chain of int8 quantisers, where a
+    one-ulp float difference upstream may legitimately move a code across a .5 boundary and
+    shift the values it feeds by a quantisation step.  Metrics are appended to the file named
+    by the PARITY_LOG environment variable, when set."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    n = rel_err(got, ref)
+    e = elem_err(got, ref)
+    emax = float(e.max()) if e.size else 0.0
+    above = float(np.mean(e > tol)) if e.size else 0.0
+    elem = tol if elem is None else elem
+    m = {"what": what, "norm": n, "elem_max": emax, "frac_above_tol": above, "tol": tol, "elem": elem,
+         "frac": frac, "size": int(e.size)}
+    path = os.environ.get("PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(m) + "\n")
+    assert n <= tol, m
+    assert emax <= elem, m
+    assert above <= frac, m
+    return m
+
+
+# Outputs behind a chain of int8 quantisers (whole mixer layers with int8 activations): an
+# element may be off by a few quantisation steps of the codes a boundary flip moved (a step of
+# out_proj's codes is s_w max|y| / 127, about 5e-4 of the output's rms at the TriSSM shape),
+# and such elements must stay rare.  fp32 outputs only; bf16 outputs keep the bf16 bound.
+CHAIN = {"elem": 5e-3, "frac": 5e-3}
+
+
+def chain(dtype_name: str) -> dict:
+    return CHAIN if dtype_name == "f32" else {}
 
 
 def to_dev(a, dtype=torch.float32):

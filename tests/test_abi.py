@@ -273,6 +273,11 @@ def test_bitlinear_bwd_and_qat_rejects():
         b = tws.BitlinearBwdArgs.from_buffer_copy(a)
         setattr(b, field, val)
         assert L.ssm_bitlinear_bwd(ctypes.byref(b), FAKE, 1 << 30, None) == status, field
+    for field in ("ldx", "ld_dy", "ld_dx"):  # a 32-row tile must stay within 32-bit offsets
+        b = tws.BitlinearBwdArgs.from_buffer_copy(a)
+        setattr(b, field, ((1 << 31) - 1) // 33 + 1)
+        assert L.ssm_bitlinear_bwd_workspace_bytes(ctypes.byref(b)) == 0, field
+        assert L.ssm_bitlinear_bwd(ctypes.byref(b), FAKE, 1 << 30, None) == UNSUPPORTED, field
     b = tws.BitlinearBwdArgs.from_buffer_copy(a)
     b.d_scale = FAKE  # needs dw and w_latent
     assert L.ssm_bitlinear_bwd(ctypes.byref(b), FAKE, 1 << 30, None) == NULL
@@ -367,3 +372,43 @@ def test_mixer_fuses_front_query():
     assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(1, 256, 256, 64, nheads=4, headdim=64))) == 0
     assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 100, 512, 16, dt_rank=16))) == 0
     assert L.ssm_mixer_fuses_front(None) == 0
+
+
+def test_mixer_fuses_front_whole_range():
+    """The fused front covers d_model in {64, 128, 256, 512} x d_inner in {128, 256, 512, 1024}
+    except 512 x 1024, with x_proj at most 64 wide; nothing else."""
+    L = tws.lib()
+    for dm in (32, 64, 96, 128, 256, 384, 512, 1024):
+        for di in (64, 128, 256, 384, 512, 1024, 2048):
+            c = tws.mixer_config(0, dm, di, 16, dt_rank=16)
+            want = dm in (64, 128, 256, 512) and di in (128, 256, 512, 1024) and not (dm == 512 and di == 1024)
+            assert L.ssm_mixer_fuses_front(ctypes.byref(c)) == int(want), (dm, di)
+    # x_proj width dt_rank + 2 d_state at most 64; dt_rank within [1, 64]
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 256, 512, 16, dt_rank=32))) == 1
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 256, 512, 32, dt_rank=16))) == 0
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 256, 512, 16, dt_rank=33))) == 0
+    # the gated block and full-precision projections never take the fused front
+    assert L.ssm_mixer_fuses_front(ctypes.byref(tws.mixer_config(0, 256, 512, 16, dt_rank=16, gated=1,
+                                                                 d_conv=4))) == 0
+
+
+def test_last_error_is_thread_local():
+    """Each thread sees the detail of its own last failing call, not another thread's."""
+    import threading
+    L = tws.lib()
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, call):
+        assert call() != OK
+        barrier.wait()  # both threads have failed before either reads its text
+        seen[name] = L.ssm_last_error().decode()
+        barrier.wait()
+
+    t1 = threading.Thread(target=worker, args=("scan", lambda: L.ssm_selective_scan_fwd(None, FAKE, 1 << 20, None)))
+    t2 = threading.Thread(target=worker, args=("quant", lambda: L.ssm_ternary_quantize_weights(
+        FAKE, 4, 6, 4, None, FAKE, FAKE, None, FAKE, 1 << 20, None)))
+    t1.start(); t2.start(); t1.join(); t2.join()
+    assert "scan" in seen["scan"] and "quantize" not in seen["scan"], seen
+    assert "quantize" in seen["quant"], seen
+    assert seen["scan"] != seen["quant"]

@@ -11,8 +11,8 @@ import torch
 import oracle
 import ternary_weight_selective_amd as tws
 import workloads as wl
-from gpu_helpers import (DEV, TOL, bf16_values, gpu_config, host, oracle_config, quantize_layer, rel_err,
-                         run_gpu_stack, to_dev, torch_dtype)
+from gpu_helpers import (DEV, TOL, bf16_values, chain, check, gpu_config, host, oracle_config, quantize_layer,
+                         rel_err, run_gpu_stack, to_dev, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,7 +109,7 @@ def test_bitlinear_parity(m, k, n, group, bits, xd, yd):
     else:
         y = tws.ssm_bitlinear_fwd(xt, packed, scale, n, act_bits=bits, group_size=group, bias=to_dev(bias),
                                   y_dtype=ydt)
-    assert rel_err(host(y), ref) <= TOL[yd]
+    check(host(y), ref, TOL[yd], what=f"test_bitlinear_parity {m} {k} {n} {group} {bits}")
 
 
 @pytest.mark.parametrize("m,k,n", [(256, 256, 512), (77, 1024, 64), (64, 2048, 4416),
@@ -125,7 +125,7 @@ def test_bitlinear_int32_from_oracle_codes(m, k, n):
     y, _, _, acc = tws.ssm_bitlinear_fwd(to_dev(oxq, torch.int8), packed, to_dev(oscale), n,
                                          x_absmax=to_dev(oam), debug=True)
     np.testing.assert_array_equal(host(acc), oacc)
-    assert rel_err(host(y), ref) <= 1e-5
+    check(host(y), ref, 1e-5, what="test_bitlinear_int32_from_oracle_codes")
 
 
 def test_bitlinear_edge_rows():
@@ -146,7 +146,7 @@ def test_bitlinear_edge_rows():
     yh = host(y)
     np.testing.assert_array_equal(yh[1], bias)
     assert host(xq)[3, 17] == -127
-    assert rel_err(yh, ref) <= 1e-4
+    check(yh, ref, 1e-4, what="test_bitlinear_edge_rows")
     empty = tws.ssm_bitlinear_fwd(torch.empty((0, k), device=DEV), packed, scale, n)
     assert empty.shape == (0, n)
 
@@ -162,7 +162,7 @@ def test_bitlinear_residual_and_strided_input():
     xt = to_dev(wide)
     y = tws.ssm_bitlinear_fwd(xt[:, :16], packed, scale, 512, k=16, residual=to_dev(res))
     ref, *_ = oracle.bitlinear(wide, codes, oscale, k=16)
-    assert rel_err(host(y), ref + res) <= 1e-6
+    check(host(y), ref + res, 1e-6, what="test_bitlinear_residual_and_strided_input")
 
 
 # ------------------------------------------------------------------ S5-S8: selective scan
@@ -203,10 +203,10 @@ def test_scan_parity(batch, L, H, P, N, aps, dt):
     h0 = wl.normal(wl.rng(4), (batch, H, P, N), 0.0, 0.5)
     ref, href = oracle.selective_scan(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["D"], p["dt_bias"], h0=h0)
     y, hl = _scan_gpu(p, torch.bfloat16 if dt == "bf16" else torch.float32, h0=h0, last=True)
-    assert rel_err(host(y), ref) <= TOL[dt]
+    check(host(y), ref, TOL[dt], what=f"test_scan_parity {batch} {L} {H} {P} {N} {dt}")
     # the SSD chunked path (bf16 activations) carries fp32 operands of its matrix products as
     # two bf16 terms (about 16 significant bits), hence the wider bound on its final state
-    assert rel_err(host(hl), href) <= (1e-4 if dt == "bf16" else 1e-5)
+    check(host(hl), href, (1e-4 if dt == "bf16" else 1e-5), what=f"test_scan_parity h_last {batch} {L} {H} {P} {N} {dt}")
 
 
 def test_scan_long_sequence_sampled():
@@ -222,8 +222,8 @@ def test_scan_long_sequence_sampled():
                dt_bias=p["dt_bias"][ch])
     ref, href = oracle.selective_scan(sub["x"], sub["delta"], sub["A"], sub["Bm"], sub["Cm"], sub["D"],
                                       sub["dt_bias"])
-    assert rel_err(yh[:, :, ch], ref) <= 1e-4
-    assert rel_err(hh[:, ch], href) <= 1e-4
+    check(yh[:, :, ch], ref, 1e-4, what="test_scan_long_sequence_sampled")
+    check(hh[:, ch], href, 1e-4, what="test_scan_long_sequence_sampled")
 
 
 def test_scan_causality_determinism_streaming():
@@ -246,6 +246,49 @@ def test_scan_causality_determinism_streaming():
     np.testing.assert_allclose(np.concatenate([host(ya), host(yb)], 1), y1, rtol=1e-5, atol=1e-5)
 
 
+def _softplus_sweep_problem(H, P, N, aps):
+    """One token per channel (L = 1, zero initial state), x = 1, B = C = the first unit vector,
+    D = 0: then y = softplus(delta + bias) of each channel exactly, in any order of evaluation,
+    so y shows the scan's softplus value by value over the sweep."""
+    v = np.linspace(-30.0, 30.0, H).astype(np.float32)
+    e0 = np.zeros((1, 1, N), np.float32)
+    e0[..., 0] = 1.0
+    A = -np.ones((H, N) if aps else (H,), np.float32)
+    return dict(x=np.ones((1, 1, H * P), np.float32), delta=v.reshape(1, 1, H), Bm=e0, Cm=e0.copy(), A=A,
+                D=np.zeros(H, np.float32), dt_bias=np.zeros(H, np.float32))
+
+
+@pytest.mark.parametrize("H,P,N,aps,dt,rtol", [
+    (3001, 1, 16, True, "f32", 5e-6),     # Mamba-1 kind scan (its softplus also serves the in-scan dt projection)
+    (601, 4, 16, False, "f32", 5e-6),     # SSD kind, recurrent kernel
+    (257, 64, 64, False, "bf16", 8e-3),   # SSD kind, chunked matrix-core kernel (bf16 output)
+])
+def test_scan_softplus_sweep(H, P, N, aps, dt, rtol):
+    """softplus(delta + bias) across [-30, 30], element by element against the oracle's
+    log1p(exp(v)) (the identity above 20): where 1 + e^v rounds at or above 2 the rounding
+    correction must not be applied."""
+    p = _softplus_sweep_problem(H, P, N, aps)
+    if dt == "bf16":
+        p = _bf16_problem(p)
+    ref = np.array([oracle.softplus(float(v)) for v in p["delta"].ravel()])
+    y = host(_scan_gpu(p, torch.bfloat16 if dt == "bf16" else torch.float32)).reshape(H, P)
+    rel = np.abs(y - ref[:, None]) / ref[:, None]
+    assert float(rel.max()) <= rtol, (float(rel.max()), float(p["delta"].ravel()[rel.max(axis=1).argmax()]))
+
+
+def test_scan_bwd_softplus_sweep():
+    """The backward recomputes softplus: with L = 1, zero state, x = 1, B = C = e0, D = 0 and
+    dy = 1, dx = softplus(delta + bias) per channel."""
+    H, N = 3001, 16
+    p = _softplus_sweep_problem(H, 1, N, True)
+    dy = np.ones((1, 1, H), np.float32)
+    got = tws.ssm_selective_scan_bwd(to_dev(p["x"]), to_dev(p["delta"]), to_dev(p["A"]), to_dev(p["Bm"]),
+                                     to_dev(p["Cm"]), to_dev(dy), D=to_dev(p["D"]), delta_bias=to_dev(p["dt_bias"]))
+    ref = np.array([oracle.softplus(float(v)) for v in p["delta"].ravel()])
+    dx = host(got["dx"]).ravel()
+    assert float((np.abs(dx - ref) / ref).max()) <= 5e-6
+
+
 def test_scan_special_cases():
     """B = 0 gives y = D x exactly; empty batch / sequence is a no-op."""
     p = wl.scan_problem(1, 50, 64, 1, 16, True, seed=8)
@@ -266,7 +309,7 @@ def test_mixer_bitssm_tiny(seed):
     gw, ow = quantize_layer(cfg, lat[0])
     out = run_gpu_stack(cfg, [gw], u)
     ref = oracle.mixer(oracle_config(cfg), ow, u)
-    assert rel_err(host(out), ref) <= TOL["f32"]
+    check(host(out), ref, TOL["f32"], what=f"test_mixer_bitssm_tiny {seed}", **chain("f32"))
 
 
 def test_mixer_causality_and_determinism():
@@ -286,10 +329,11 @@ def test_mixer_causality_and_determinism():
 def _stack_sampled(name, seqs, seed=42):
     """Full-size stack on the GPU (the launch configuration the benchmark times).  Each layer is
     checked against the oracle given the same layer input (the GPU's stored input of the
-    sampled sequences; sequences are independent): that is the parity bar per mixer output.
-    The free-running drift (oracle stack from u, no re-synchronisation) is returned too: a
-    one-ulp difference anywhere can flip an int8 code at a .5 boundary, and flips compound
-    through a quantised stack, so the drift is reported, not held to the per-mixer bar."""
+    sampled sequences; sequences are independent): that is the parity bar per mixer output,
+    norm-wise and element by element.  The free-running drift (oracle stack from u, no
+    re-synchronisation) is returned too: a one-ulp difference anywhere can flip an int8 code at
+    a .5 boundary, and flips compound through a quantised stack, so the drift of a many-layer
+    stack is held to a looser bound than one layer's output."""
     cfg = wl.CONFIGS[name]
     lat, u = wl.mixer_problem(cfg, seed=seed)
     if cfg.act_dtype == "bf16":
@@ -299,11 +343,12 @@ def _stack_sampled(name, seqs, seed=42):
     h = to_dev(u, torch_dtype(cfg))
     ws = torch.empty(tws.ssm_mixer_workspace_bytes(c, cfg.batch, cfg.seqlen), dtype=torch.uint8, device=DEV)
     per_layer = []
-    for gw, ow in pairs:
+    for li, (gw, ow) in enumerate(pairs):
         h_in = host(h)[seqs]
         h = tws.ssm_mixer_fwd(c, tws.mixer_weights(gw), h, add_residual=True, out=h, workspace=ws)
         ref = oracle.mixer(oracle_config(cfg), ow, h_in)
-        per_layer.append(rel_err(host(h)[seqs], ref))
+        m = check(host(h)[seqs], ref, TOL[cfg.act_dtype], what=f"{name} layer {li}", **chain(cfg.act_dtype))
+        per_layer.append(m["norm"])
     free = oracle.mixer_stack(oracle_config(cfg), [o for _, o in pairs], u[seqs])
     drift = rel_err(host(h)[seqs], free)
     print(f"{name}: per-layer rel err {['%.2e' % e for e in per_layer]}, free-running drift {drift:.2e}")
@@ -312,24 +357,23 @@ def _stack_sampled(name, seqs, seed=42):
 
 def test_mixer_trissm_stack_sampled():
     per_layer, drift = _stack_sampled("trissm", [0, 37, 63])
-    assert max(per_layer) <= TOL["f32"], per_layer
     assert drift <= 0.05, drift
 
 
 def test_mixer_long_scan_sampled():
+    # one layer: the free-running output is the layer's own, held to the per-layer bar
     per_layer, drift = _stack_sampled("long_scan", [5])
-    assert max(per_layer) <= TOL["f32"], per_layer
+    assert drift <= TOL["f32"], drift
 
 
 def test_mixer_ternaryssm50m_stack_sampled():
     per_layer, drift = _stack_sampled("ternaryssm50m", [0, 15])
-    assert max(per_layer) <= TOL["bf16"], per_layer
     assert drift <= 0.1, drift
 
 
 def test_mixer_mamba2_ssd_sampled():
     per_layer, drift = _stack_sampled("mamba2_ssd", [2])
-    assert max(per_layer) <= TOL["bf16"], per_layer
+    assert drift <= TOL["bf16"], drift
 
 
 def test_mixer_ssd_small_fp32():
@@ -340,7 +384,7 @@ def test_mixer_ssd_small_fp32():
     gw, ow = quantize_layer(cfg, lat[0])
     out = run_gpu_stack(cfg, [gw], u)
     ref = oracle.mixer(oracle_config(cfg), ow, u)
-    assert rel_err(host(out), ref) <= TOL["f32"]
+    check(host(out), ref, TOL["f32"], what="test_mixer_ssd_small_fp32", **chain("f32"))
 
 
 @pytest.mark.parametrize("name,over", [
@@ -415,9 +459,9 @@ def test_mixer_decode_step(name, over, seed):
     out, state = _decode(cfg, gw, u)
     ref = oracle.mixer(oracle_config(cfg), ow, u)
     tol = TOL["bf16"] if cfg.act_dtype == "bf16" else TOL["f32"]
-    assert rel_err(host(out), ref) <= tol
+    check(host(out), ref, tol, what=f"test_mixer_decode_step {name} {seed}", **chain(cfg.act_dtype))
     full = host(run_gpu_stack(cfg, [gw], u))
-    assert rel_err(host(out), full) <= tol
+    check(host(out), full, tol, what=f"test_mixer_decode_step {name} {seed} vs prefill", **chain(cfg.act_dtype))
     assert bool(torch.isfinite(state).all()) and float(state.abs().max()) > 0
 
 
@@ -502,7 +546,7 @@ def test_scan_gate_parity(kind, dt):
                                    to_dev(p["dt_bias"]), True, gate=to_dev(gate, tdt))
     ref, _ = oracle.selective_scan(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["D"], p["dt_bias"])
     sil = np.vectorize(oracle.silu)(gate.astype(np.float64))
-    assert rel_err(host(y), ref * sil) <= (TOL["bf16"] if dt == "bf16" else 1e-5)
+    check(host(y), ref * sil, (TOL["bf16"] if dt == "bf16" else 1e-5), what=f"test_scan_gate_parity {kind} {dt}")
 
 
 GATED_MIXER_CASES = [
@@ -526,17 +570,17 @@ def test_mixer_gated_parity(name, over, seed):
     gw, ow = quantize_layer(cfg, lat[0])
     out = run_gpu_stack(cfg, [gw], u)
     ref = oracle.mixer(oracle_config(cfg), ow, u)
-    assert rel_err(host(out), ref) <= (TOL["bf16"] if cfg.act_dtype == "bf16" else TOL["f32"])
+    check(host(out), ref, TOL[cfg.act_dtype], what=f"test_mixer_gated_parity {name} {seed}", **chain(cfg.act_dtype))
 
 
 def test_mixer_trissm_gated_stack_sampled():
     per_layer, drift = _stack_sampled("trissm_gated", [0, 41])
-    assert max(per_layer) <= TOL["f32"], per_layer
+    assert drift <= 0.05, drift
 
 
 def test_mixer_mamba2_ssd_gated_sampled():
     per_layer, drift = _stack_sampled("mamba2_ssd_gated", [1])
-    assert max(per_layer) <= TOL["bf16"], per_layer
+    assert drift <= TOL["bf16"], drift
 
 
 # ------------------------------------------------------------------ full-precision projections
@@ -564,7 +608,7 @@ def test_dense_parity(m, k, n, dt, res, ldx):
     xd = to_dev(x, tdt)
     y = tws.ssm_dense_fwd(xd[:, :k], to_dev(W, tdt), residual=to_dev(r, tdt) if res else None)
     ref = oracle.dense(x, W, k=k) + (r if res else 0.0)
-    assert rel_err(host(y), ref) <= (4e-3 if dt == "bf16" else 1e-6)
+    check(host(y), ref, (4e-3 if dt == "bf16" else 1e-6), what=f"test_dense_parity {m} {k} {n} {dt}")
 
 
 FP_MIXER_CASES = [
@@ -590,10 +634,10 @@ def test_mixer_fp_proj_parity(name, over, seed):
     h = to_dev(u, torch_dtype(cfg))
     out = tws.ssm_mixer_fwd(c, tws.mixer_weights(gw), h, add_residual=False)
     ref = oracle.mixer(oracle_config(cfg), ow, u, residual=False)
-    assert rel_err(host(out), ref) <= tol
+    check(host(out), ref, tol, what=f"test_mixer_fp_proj_parity {name} {seed}", **chain(cfg.act_dtype))
     out2 = tws.ssm_mixer_fwd(c, tws.mixer_weights(gw), h, add_residual=True, out=h)
     ref2 = oracle.mixer(oracle_config(cfg), ow, u, residual=True)
-    assert rel_err(host(out2), ref2) <= tol
+    check(host(out2), ref2, tol, what=f"test_mixer_fp_proj_parity {name} {seed} residual", **chain(cfg.act_dtype))
 
 
 # ------------------------------------------------------------------ STE backward, QAT step
@@ -630,8 +674,8 @@ def test_bitlinear_bwd_parity(m, k, n, group, xd, gain):
     dx, dw, ds = tws.ssm_bitlinear_bwd(to_dev(x, xdt), packed, scale, n, to_dev(dy), group_size=group,
                                        norm_weight=to_dev(gn) if gain else None, w_latent=to_dev(w))
     ref = oracle.bitlinear_bwd(x, codes, oscale, dy, group=group, norm_w=gn, w_latent=w)
-    assert rel_err(host(dx), ref["dx"]) <= 1e-5
-    assert rel_err(host(dw), ref["dw"]) <= 1e-5
+    check(host(dx), ref["dx"], 1e-5, what=f"test_bitlinear_bwd_parity dx {m} {k} {n} {group}")
+    check(host(dw), ref["dw"], 1e-5, what=f"test_bitlinear_bwd_parity dw {m} {k} {n} {group}")
     # the scale gradient sums terms of both signs: compare against the sum of their magnitudes
     v = w.astype(np.float64) / (np.repeat(np.asarray(oscale, np.float64).reshape(n, -1), group, axis=1)
                                 if group else float(np.asarray(oscale).ravel()[0]))
@@ -692,7 +736,7 @@ def test_scan_bwd_parity(batch, L, H, N, dt, with_h0):
     ref = oracle.selective_scan_bwd(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["D"], dy,
                                     delta_bias=p["dt_bias"], h0=h0)
     for k in ("dx", "ddelta", "dA", "dB", "dC", "dD", "dbias", "dh0"):
-        assert rel_err(host(got[k]).reshape(ref[k].shape), ref[k]) <= 2e-4, k
+        check(host(got[k]).reshape(ref[k].shape), ref[k], 2e-4, what=f"test_scan_bwd_parity {k}")
 
 
 # ------------------------------------------------------------------ mixer backward (STE)
@@ -733,11 +777,9 @@ def test_mixer_bwd_parity(name, batch, seqlen, residual, latents, gains):
     got = tws.ssm_mixer_bwd(gpu_config(cfg), gw, to_dev(u), to_dev(dout), add_residual=residual,
                             latents={k: to_dev(v) for k, v in lats.items()} if latents else None)
     ref = oracle.mixer_bwd(oracle_config(cfg), ow, u, dout, residual=residual, latents=lats)
-    errs = {k: rel_err(host(got[k]).reshape(np.shape(ref[k])), ref[k])
-            for k in ("du", "dw_in", "dw_x", "dw_dt", "dw_out", "dA", "dD", "d_dt_bias")}
-    print(name, batch, seqlen, {k: "%.1e" % e for k, e in errs.items()})
-    for k, e in errs.items():
-        assert e <= 5e-4, (k, e)
+    for k in ("du", "dw_in", "dw_x", "dw_dt", "dw_out", "dA", "dD", "d_dt_bias"):
+        check(host(got[k]).reshape(np.shape(ref[k])), ref[k], 5e-4, what=f"test_mixer_bwd_parity {name} {batch} {k}",
+              elem=5e-3, frac=5e-3)
     if latents:
         for p in cfg.proj_shapes:
             bound = _ds_bound(ref["dw_" + p], ow["c_" + p], ow["s_" + p], lats["lat_" + p])

@@ -527,6 +527,24 @@ def test_mixer_ssd_composition():
     np.testing.assert_array_equal(out, o.astype(np.float32).astype(np.float64).reshape(out.shape))
 
 
+def test_mixer_stack_composition():
+    """A stack of residual mixer layers (the TriSSM README's 12-layer selective SSM) is the
+    layers applied in order, each to the previous layer's stored output: two layers equal two
+    explicit mixer calls, in that order (the reversed order differs); with every out_proj code
+    zero each layer is the identity, so a stack of them returns u exactly."""
+    cfg = wl.CONFIGS["bitssm_tiny"]
+    lat, u = wl.mixer_problem(cfg, seed=45, layers=2)
+    w1, w2 = _layer_codes(cfg, lat[0]), _layer_codes(cfg, lat[1])
+    oc = _cfg_dict(cfg)
+    got = oracle.mixer_stack(oc, [w1, w2], u)
+    h1 = oracle.mixer(oc, w1, u, residual=True).astype(np.float32)
+    np.testing.assert_array_equal(got, oracle.mixer(oc, w2, h1, residual=True))
+    rev = oracle.mixer(oc, w1, oracle.mixer(oc, w2, u, residual=True).astype(np.float32), residual=True)
+    assert not np.array_equal(got, rev)
+    zero = [dict(w, c_out=np.zeros_like(w["c_out"])) for w in (w1, w2, w1)]
+    np.testing.assert_array_equal(oracle.mixer_stack(oc, zero, u), u.astype(np.float64))
+
+
 def test_mixer_causality():
     """TriSSM README tests list causality: perturbing token t of u leaves every output before
     t bitwise unchanged (oracle, Mamba-1 and SSD kinds)."""
@@ -927,6 +945,24 @@ def test_bwd_grouped_scale_gradient_is_per_group():
     b = oracle.bitlinear_bwd(x, cg, sg, dy, group=G, w_latent=w)
     np.testing.assert_allclose(b["dx"], a["dx"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(b["ds"].sum(), a["ds"][0], rtol=1e-10)
+
+
+def test_qat_step_hand_examples():
+    """One QAT step on hand-worked values (tests/golden/qat_step_example.txt): the latent update
+    W - lr dW, the scale update s - lr_s ds, and the codes and zero count under the new scales,
+    per tensor and per group.  A sign or a factor wrong in either update changes the result."""
+    g = _read_golden("qat_step_example.txt")
+    for i, group in ((1, 0), (2, 2)):
+        W, dW = _floats(g[f"W{i}"]), _floats(g[f"dW{i}"])
+        s, ds = _floats(g[f"s{i}"]).ravel(), _floats(g[f"ds{i}"]).ravel()
+        lr, lr_s = (float(v) for v in _floats(g[f"lr{i}"]).ravel())
+        if group:
+            s, ds = s.reshape(W.shape[0], -1), ds.reshape(W.shape[0], -1)
+        Wn, sn, codes, zeros = oracle.qat_step(W, s, dW, ds, lr, lr_s, group)
+        np.testing.assert_array_equal(Wn, _floats(g[f"Wnew{i}"]))
+        np.testing.assert_array_equal(np.asarray(sn).ravel(), _floats(g[f"snew{i}"]).ravel())
+        np.testing.assert_array_equal(codes, _ints(g[f"codes{i}"]))
+        assert zeros == int(g[f"zeros{i}"][0][0])
 
 
 def test_qat_step_zero_lr_and_zero_ratio():

@@ -157,13 +157,15 @@ def mixer_problem(cfg: MixerConfig, seed: int = 42, layers: int | None = None, b
 
 def scan_problem(batch: int, seqlen: int, nheads: int, headdim: int, d_state: int, a_per_state: bool,
                  seed: int = 42):
-    """Scan-only inputs: x, B, C ~ N(0,1); delta pre-activations ~ N(-2,1); A, D, dt_bias as above."""
+    """Scan-only inputs: x, B, C ~ N(0,1); A, D as above; the softplus argument delta + dt_bias
+    ~ N(-2, 1), so that softplus(delta + bias) spans slow and fast decay: delta ~ N(0, 0.75)
+    per token and dt_bias ~ N(-2, 0.25) per channel (the variances add up to 1)."""
     g = rng(seed)
     x = normal(g, (batch, seqlen, nheads * headdim))
-    delta = normal(g, (batch, seqlen, nheads), -2.0, 1.0)
+    delta = normal(g, (batch, seqlen, nheads), 0.0, math.sqrt(0.75))
     Bm = normal(g, (batch, seqlen, d_state))
     Cm = normal(g, (batch, seqlen, d_state))
     A = a_log_uniform(g, (nheads, d_state) if a_per_state else (nheads,))
     D = normal(g, (nheads,), 1.0, 0.1)
-    dt_bias = normal(g, (nheads,), 0.0, 0.5)
+    dt_bias = normal(g, (nheads,), -2.0, 0.5)
     return dict(x=x, delta=delta, Bm=Bm, Cm=Cm, A=A, D=D, dt_bias=dt_bias)
