@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 
 typedef enum {
   SSM_OK = 0,
@@ -283,6 +283,39 @@ size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64
 ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u,
                          void* out, int64_t batch, int64_t seqlen, int32_t add_residual,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ssm_mixer_fwd_stages -- ssm_mixer_fwd with its intermediate stages copied out, for stage-wise
+ * checks of the integer steps inside fused kernels (TriSSM README: the Delta, B, C projections
+ * are BitLinear layers with ternary weights and int8 activations; their int8 codes and int32
+ * sums have one correct value each).  Same launches, same results as ssm_mixer_fwd; after the
+ * scan, the stages the kernels left in the workspace are copied (device to device, on `stream`)
+ * into the caller's buffers, and the in-scan dt projection stores its int32 sums.
+ *  stages: not NULL; each pointer NULL (not wanted) or a device buffer, written:
+ *   x        [M, d_inner] act_dtype: the SSM input (in_proj output; its convolution when gated)
+ *   p        [M, dt_rank + 2 d_state] act_dtype: x_proj output [dr | B | C]
+ *            (SSD kind: the in_proj output v [M, d_inner + 2 d_state + nheads (+ d_inner)])
+ *   dt_codes [M, dt_rank] int8: the int8 absmax codes of dr's RMSNorm (dt_proj's input)
+ *   dt_deq   [M] fp64: max(absmax, 1e-5) / 127 of those rows
+ *   dt_acc   [M, d_inner] int32: the dt projection's accumulators (sum of codes x ternary weights)
+ *   y        [M, d_inner] act_dtype: the scan output (out_proj's input; times SiLU(zg) when gated)
+ *  with M = batch * seqlen.  x and the dt stages exist for the Mamba-1 kind only, the dt stages
+ *  with a ternary dt projection only (else SSM_ERR_UNSUPPORTED).
+ * Errors: as ssm_mixer_fwd; SSM_ERR_NULL when stages is NULL.
+ */
+typedef struct {
+  void* x;
+  void* p;
+  int8_t* dt_codes;
+  double* dt_deq;
+  int32_t* dt_acc;
+  void* y;
+} ssm_mixer_stages;
+
+ssm_status ssm_mixer_fwd_stages(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u,
+                                void* out, int64_t batch, int64_t seqlen, int32_t add_residual,
+                                void* workspace, size_t ws_bytes, const ssm_mixer_stages* stages,
+                                hipStream_t stream);
 
 /*
  * ssm_mixer_bwd -- the backward pass of one Mamba-1 kind mixer layer (TriSSM README: the mixer

@@ -75,6 +75,10 @@ class MixerGrads(ctypes.Structure):
                                    "ds_in", "ds_x", "ds_dt", "ds_out", "dA", "dD", "d_dt_bias")]
 
 
+class MixerStages(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("x", "p", "dt_codes", "dt_deq", "dt_acc", "y")]
+
+
 class SsmError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(msg)
@@ -85,7 +89,7 @@ _lib = None
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed_row_bytes",
            "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
-           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fuses_front", "ssm_mixer_step",
+           "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fwd_stages", "ssm_mixer_fuses_front", "ssm_mixer_step",
            "ssm_conv1d_silu_fwd", "ssm_dense_fwd", "ssm_bitlinear_bwd_workspace_bytes", "ssm_bitlinear_bwd",
            "ssm_qat_sgd_step", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd",
            "ssm_mixer_bwd_workspace_bytes", "ssm_mixer_bwd"]
@@ -147,6 +151,9 @@ def lib():
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
         L.ssm_mixer_fwd.restype = ctypes.c_int
+        L.ssm_mixer_fwd_stages.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64,
+                                           _i64, _i32, _vp, _sz, ctypes.POINTER(MixerStages), _vp]
+        L.ssm_mixer_fwd_stages.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -341,6 +348,36 @@ def ssm_mixer_fwd(cfg: MixerConfig, weights, u: torch.Tensor, add_residual: bool
     _check(L.ssm_mixer_fwd(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, seqlen, int(add_residual),
                            _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
     return out
+
+
+def ssm_mixer_fwd_stages(cfg: MixerConfig, weights, u: torch.Tensor, add_residual: bool = True,
+                         want=("x", "p", "dt_codes", "dt_deq", "dt_acc", "y"), stream=None):
+    """ssm_mixer_fwd with its stages copied out: returns (out, dict of the stages in `want`):
+    x [M, d_inner], p [M, PW] (SSD: v), y [M, d_inner] in the act dtype; dt_codes int8 [M, dt_rank],
+    dt_deq fp64 [M], dt_acc int32 [M, d_inner] (Mamba-1 kind)."""
+    if not u.is_contiguous():
+        raise ValueError("u must be contiguous")
+    batch, seqlen, _ = u.shape
+    M = batch * seqlen
+    mw = weights if isinstance(weights, MixerWeights) else mixer_weights(weights)
+    act = {SSM_F32: torch.float32, SSM_BF16: torch.bfloat16}[cfg.act_dtype]
+    if cfg.kind == SSM_MIXER_MAMBA1:
+        pw = cfg.dt_rank + 2 * cfg.d_state
+    else:
+        pw = cfg.d_inner + 2 * cfg.d_state + cfg.nheads + (cfg.d_inner if cfg.gated else 0)
+    shapes = {"x": ((M, cfg.d_inner), act), "p": ((M, pw), act), "dt_codes": ((M, cfg.dt_rank), torch.int8),
+              "dt_deq": ((M,), torch.float64), "dt_acc": ((M, cfg.d_inner), torch.int32), "y": ((M, cfg.d_inner), act)}
+    got = {k: torch.empty(shapes[k][0], dtype=shapes[k][1], device=u.device) for k in want}
+    st = MixerStages()
+    for k, t in got.items():
+        setattr(st, k, _p(t))
+    out = torch.empty_like(u)
+    L = lib()
+    nb = L.ssm_mixer_workspace_bytes(ctypes.byref(cfg), batch, seqlen)
+    ws = _workspace(nb, u.device)
+    _check(L.ssm_mixer_fwd_stages(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, seqlen,
+                                  int(add_residual), _p(ws), nb, ctypes.byref(st), _stream(stream)))
+    return out, got
 
 
 def ssm_mixer_step(cfg: MixerConfig, weights, u: torch.Tensor, state: torch.Tensor, add_residual: bool = True,

@@ -450,14 +450,22 @@ namespace {
 // (used for one token per sequence only, where no time chunks are formed).
 ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
                      int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb, hipStream_t stream,
-                     float* state, float* conv_state);
+                     float* state, float* conv_state, const ssm_mixer_stages* dbg);
 }  // namespace
 
 ssm_status ssm_mixer_fwd(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
                          int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb,
                          hipStream_t stream) {
   g_err.clear();
-  return mixer_run(c, w, u, out, batch, seqlen, add_residual, ws, wsb, stream, nullptr, nullptr);
+  return mixer_run(c, w, u, out, batch, seqlen, add_residual, ws, wsb, stream, nullptr, nullptr, nullptr);
+}
+
+ssm_status ssm_mixer_fwd_stages(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
+                                int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb,
+                                const ssm_mixer_stages* stages, hipStream_t stream) {
+  g_err.clear();
+  if (!stages) return fail(SSM_ERR_NULL, "mixer stages: stages is NULL");
+  return mixer_run(c, w, u, out, batch, seqlen, add_residual, ws, wsb, stream, nullptr, nullptr, stages);
 }
 
 ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
@@ -467,7 +475,7 @@ ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w,
   if (batch > 0 && !state) return fail(SSM_ERR_NULL, "mixer step: state is NULL");
   if (batch > 0 && c && c->gated && c->d_conv > 1 && !conv_state)
     return fail(SSM_ERR_NULL, "mixer step: conv_state is NULL (gated block)");
-  return mixer_run(c, w, u, out, batch, 1, add_residual, ws, wsb, stream, state, conv_state);
+  return mixer_run(c, w, u, out, batch, 1, add_residual, ws, wsb, stream, state, conv_state, nullptr);
 }
 
 ssm_status ssm_conv1d_silu_fwd(const void* x, int32_t dtype, int64_t batch, int64_t seqlen, int64_t channels,
@@ -568,12 +576,26 @@ ssm_status ssm_dense_fwd(const void* x, int32_t dtype, int64_t m, int64_t k, int
 }  // extern "C"
 
 namespace {
+// Device-to-device copy of `rows` rows of `width` bytes (a stage output, for the checks).
+ssm_status copy_rows(void* dst, const void* src, size_t src_pitch, size_t width, int64_t rows, hipStream_t stream) {
+  if (!dst || rows == 0) return SSM_OK;
+  return dev(hipMemcpy2DAsync(dst, width, src, src_pitch, width, (size_t)rows, hipMemcpyDeviceToDevice, stream),
+             "mixer stage copy");
+}
+
 ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
                      int64_t batch, int64_t seqlen, int32_t add_residual, void* ws, size_t wsb, hipStream_t stream,
-                     float* state, float* conv_state) {
+                     float* state, float* conv_state, const ssm_mixer_stages* dbg) {
   MixPlan p;
   ssm_status st = mix_plan(c, batch, seqlen, &p);
   if (st != SSM_OK) return st;
+  if (dbg) {
+    const bool dt_stage = dbg->dt_codes || dbg->dt_deq || dbg->dt_acc;
+    if (c->kind != SSM_MIXER_MAMBA1 && (dbg->x || dt_stage))
+      return fail(SSM_ERR_UNSUPPORTED, "mixer stages: x and the dt stages exist for the Mamba-1 kind only");
+    if (c->fp_proj == 2 && dt_stage)
+      return fail(SSM_ERR_UNSUPPORTED, "mixer stages: the dt stages need the ternary dt projection (fp_proj < 2)");
+  }
   // full-precision projections: in and out (fp_proj >= 1), x and dt too (fp_proj == 2)
   const bool f_io = c->fp_proj >= 1, f_xdt = c->fp_proj == 2;
   if (!w || !w->A) return fail(SSM_ERR_NULL, "mixer: weights and A are required");
@@ -659,6 +681,7 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     st = scan_check(&sa);
     if (st != SSM_OK) return st;
     ScanArgs sc = to_scan(&sa);
+    if (dbg) sc.dbg_dt_acc = dbg->dt_acc;
     if (p.off_scan + scan_m1_workspace(sc) > wsb)  // the scan's codes region lies inside the workspace
       return fail(SSM_ERR_WORKSPACE, "mixer: scan workspace exceeds %zu bytes", wsb);
     if (front) {  // in_proj, x_proj and the dt input's codes in one kernel, codes into the scan's workspace
@@ -693,6 +716,17 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     }
     st = dev(launch_scan_m1(sc, base + p.off_scan, stream), "mixer scan");
     if (st != SSM_OK) return st;
+    if (dbg) {  // the stages as the kernels left them in the workspace (before out_proj runs)
+      int cw = 0;
+      size_t off_deq = 0;
+      scan_m1_code_layout(sc, &cw, &off_deq);
+      ssm_status e = copy_rows(dbg->x, x, c->d_inner * as, c->d_inner * as, p.M, stream);
+      if (e == SSM_OK) e = copy_rows(dbg->p, pp, p.PW * as, p.PW * as, p.M, stream);
+      if (e == SSM_OK) e = copy_rows(dbg->dt_codes, base + p.off_scan, cw, c->dt_rank, p.M, stream);
+      if (e == SSM_OK) e = copy_rows(dbg->dt_deq, base + p.off_scan + off_deq, 8, 8, p.M, stream);
+      if (e == SSM_OK) e = copy_rows(dbg->y, y, c->d_inner * as, c->d_inner * as, p.M, stream);
+      if (e != SSM_OK) return e;
+    }
     return f_io ? dense(y, c->d_inner, c->d_inner, w->fw_out, c->d_model, out, c->d_model, res)
                 : bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
   }
@@ -724,6 +758,11 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
   if (c->gated) { s.gate = (const char*)v + p.VW0 * as; s.ld_gate = p.VW; }
   st = dev(launch_scan_ssd(s, base + p.off_scan, wsb - p.off_scan, stream), "mixer scan");
   if (st != SSM_OK) return st;
+  if (dbg) {
+    ssm_status e = copy_rows(dbg->p, v, p.VW * as, p.VW * as, p.M, stream);
+    if (e == SSM_OK) e = copy_rows(dbg->y, y, c->d_inner * as, c->d_inner * as, p.M, stream);
+    if (e != SSM_OK) return e;
+  }
   return f_io ? dense(y, c->d_inner, c->d_inner, w->fw_out, c->d_model, out, c->d_model, res)
               : bitlinear(y, c->d_inner, c->d_inner, w->w_out, w->s_out, w->g_out, c->d_model, out, c->d_model, res);
 }

@@ -79,6 +79,7 @@ struct ScanArgs {
   const uint32_t* w_dt; int64_t w_dt_row_words;
   const float* s_dt; const float* g_dt; float eps;
   int dt_codes_ready;  // the dt input's int8 codes and factors are already in the workspace
+  int32_t* dbg_dt_acc;  // nullable [B L, H]: the in-scan dt projection's int32 sums (stage checks)
   const void* gate; int64_t ld_gate;  // nullable: y is multiplied by SiLU(gate) before it is stored
 };
 hipError_t launch_scan_m1(const ScanArgs& a, void* ws, hipStream_t s);

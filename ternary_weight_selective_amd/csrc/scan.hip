@@ -96,6 +96,7 @@ namespace {
 struct DtCodes {
   const int8_t* codes;  // [M, 16 * RW]
   const double* deq;    // [M]
+  int32_t* dbg_acc;     // nullable [M, Di]: the int32 sums, stored for stage-wise checks
 };
 }  // namespace
 
@@ -252,6 +253,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
         for (int q = 0; q < RW; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(rq[FUSED ? i : 0][q][j], wdt[q][j], acc, false);
+        if (!LOCAL && dc.dbg_acc && dv && t0 + t < te) dc.dbg_acc[(b * L + t0 + t) * Di + d] = acc;
         dtv = (float)((s_dt * (double)acc) * rf[FUSED ? i : 0]);
       } else {
         dtv = act_f32(rd[FUSED ? 0 : i]);
@@ -432,6 +434,7 @@ hipError_t launch_m1_t(const ScanArgs& a, void* ws, hipStream_t s) {
     }
     dc.codes = codes;
     dc.deq = deq;
+    dc.dbg_acc = a.dbg_dt_acc;
   }
   // grid (sequence, channel tile, chunk): blocks are dealt to the 8 XCDs round-robin by linear
   // index, so with the sequence fastest the channel tiles of sequence b all run on XCD b mod 8
