@@ -221,11 +221,30 @@ typedef struct {
   int32_t pad1;
   /* optional gate (see above) */
   const void* gate;   int64_t ld_gate;
+  /* optional precomputed dt input codes (with dt_in): when dt_codes is not NULL, the scan reads
+     the int8 codes [B L, 16 ceil(dt_rank / 16)] and fp64 factors dt_deq [B L] that
+     ssm_dt_input_quantize wrote for dt_in, instead of computing them itself */
+  const int8_t* dt_codes;
+  const double* dt_deq;
 } ssm_scan_args;
 
 size_t ssm_selective_scan_workspace_bytes(const ssm_scan_args* a);
 ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* workspace, size_t ws_bytes,
                                   hipStream_t stream);
+
+/*
+ * ssm_dt_input_quantize -- the first step of the scan's dt projection on its own: per token
+ * row m of dt_in (dt_rank values, row stride ld, act dtype `dtype`), RMSNorm with gains g_dt
+ * (NULL = ones) and epsilon eps, then absmax int8 codes (TriSSM README: BitLinear with int8
+ * activations; the same fixed-order arithmetic as ssm_bitlinear_fwd):
+ *   codes [m, 16 ceil(dt_rank / 16)] int8 (zero past dt_rank), deq [m] fp64 = max(absmax, 1e-5) / 127.
+ * Passing them to ssm_selective_scan_fwd (dt_codes, dt_deq) gives exactly the result of the
+ * scan computing them itself.  dt_rank in [1, 64]; m = 0 launches nothing.
+ * Errors: SSM_ERR_NULL, SSM_ERR_SHAPE, SSM_ERR_DTYPE, SSM_ERR_UNSUPPORTED, SSM_ERR_DEVICE.
+ */
+ssm_status ssm_dt_input_quantize(const void* dt_in, int32_t dtype, int64_t m, int64_t dt_rank, int64_t ld,
+                                 const float* g_dt, float eps, int8_t* codes, double* deq,
+                                 hipStream_t stream);
 
 /*
  * ssm_mixer_fwd -- one ternary selective-SSM mixer layer (TriSSM README BitSSM mixer;

@@ -111,6 +111,15 @@ def _p(a, ctype):
     return a.ctypes.data_as(ctype)
 
 
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
 def round_bf16(a) -> np.ndarray:
     """fp32 values rounded to the nearest bf16 (ties to even), returned as fp32."""
     a = _f32(a)

@@ -42,6 +42,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <omp.h>
 
 #define ORC_F32 0
 #define ORC_BF16 1
@@ -658,3 +659,8 @@ int orc_mixer(int kind, int64_t d_model, int64_t d_inner, int64_t d_state, int64
   free(yd);
   return rc;
 }
+
+/* Thread count of the parallel loops above (the timed CPU baseline runs single-threaded and
+ * on every core); the arithmetic and its order per output do not depend on it. */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }

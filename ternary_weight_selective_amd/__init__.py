@@ -40,7 +40,7 @@ class ScanArgs(ctypes.Structure):
                 ("Bm", _vp), ("ld_B", _i64), ("Cm", _vp), ("ld_C", _i64), ("D", _vp), ("h0", _vp),
                 ("h_last", _vp), ("y", _vp), ("ld_y", _i64), ("dt_in", _vp), ("ld_dt_in", _i64), ("dt_rank", _i64),
                 ("w_dt", _vp), ("s_dt", _vp), ("g_dt", _vp), ("dt_eps", ctypes.c_float), ("pad1", _i32),
-                ("gate", _vp), ("ld_gate", _i64)]
+                ("gate", _vp), ("ld_gate", _i64), ("dt_codes", _vp), ("dt_deq", _vp)]
 
 
 class ScanBwdArgs(ctypes.Structure):
@@ -88,7 +88,7 @@ class SsmError(RuntimeError):
 _lib = None
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed_row_bytes",
            "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
-           "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd",
+           "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd", "ssm_dt_input_quantize",
            "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fwd_stages", "ssm_mixer_fuses_front", "ssm_mixer_step",
            "ssm_conv1d_silu_fwd", "ssm_dense_fwd", "ssm_bitlinear_bwd_workspace_bytes", "ssm_bitlinear_bwd",
            "ssm_qat_sgd_step", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd",
@@ -121,6 +121,8 @@ def lib():
         L.ssm_selective_scan_workspace_bytes.restype = _sz
         L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp, _sz, _vp]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
+        L.ssm_dt_input_quantize.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _vp]
+        L.ssm_dt_input_quantize.restype = ctypes.c_int
         L.ssm_mixer_workspace_bytes.argtypes = [ctypes.POINTER(MixerConfig), _i64, _i64]
         L.ssm_mixer_workspace_bytes.restype = _sz
         L.ssm_mixer_fuses_front.argtypes = [ctypes.POINTER(MixerConfig)]
@@ -290,6 +292,8 @@ def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch
         a.dt_in, a.ld_dt_in = _p(dt_proj["dt_in"]), _rows(dt_proj["dt_in"], "dt_in")[1]
         a.dt_rank, a.w_dt, a.s_dt = dt_proj["dt_rank"], _p(dt_proj["w_dt"]), _p(dt_proj["s_dt"])
         a.g_dt, a.dt_eps = _p(dt_proj.get("g_dt")), dt_proj.get("eps", 1e-5)
+        if dt_proj.get("dt_codes") is not None:  # precomputed by ssm_dt_input_quantize
+            a.dt_codes, a.dt_deq = _p(dt_proj["dt_codes"]), _p(dt_proj["dt_deq"])
     a.delta_bias, a.delta_softplus = _p(delta_bias), int(softplus)
     a.A = _p(A)
     a.Bm, a.ld_B = _p(Bm), _rows(Bm, "Bm")[1]
@@ -303,6 +307,18 @@ def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch
     ws = _workspace(nb, x.device)
     _check(L.ssm_selective_scan_fwd(ctypes.byref(a), _p(ws), nb, _stream(stream)))
     return (out, hl) if return_last_state else out
+
+
+def ssm_dt_input_quantize(dt_in: torch.Tensor, dt_rank: int, g_dt: torch.Tensor | None = None, eps: float = 1e-5,
+                          stream=None):
+    """int8 codes [M, 16 ceil(R / 16)] and fp64 factors [M] of the dt input's rows (dt_in [..., >= R],
+    a contiguous last dim), as the scan's dt projection computes them."""
+    m, ld = _rows(dt_in, "dt_in")
+    codes = torch.empty((m, 16 * ((dt_rank + 15) // 16)), dtype=torch.int8, device=dt_in.device)
+    deq = torch.empty(m, dtype=torch.float64, device=dt_in.device)
+    _check(lib().ssm_dt_input_quantize(_p(dt_in), _DTYPES[dt_in.dtype], m, dt_rank, ld, _p(g_dt), eps, _p(codes),
+                                       _p(deq), _stream(stream)))
+    return codes, deq
 
 
 def mixer_config(kind: int, d_model: int, d_inner: int, d_state: int, *, dt_rank: int = 0, nheads: int = 0,

@@ -177,6 +177,9 @@ ssm_status scan_check(const ssm_scan_args* a) {
   if (a->batch * a->seqlen > 0 && (!a->x || (!proj && !a->delta) || !a->A || !a->Bm || !a->Cm || !a->y))
     return fail(SSM_ERR_NULL, "scan: x, delta (or dt_in), A, Bm, Cm and y are required");
   if (a->gate && a->ld_gate < HP) return fail(SSM_ERR_SHAPE, "scan: ld_gate < nheads * headdim");
+  if (a->dt_codes && (!proj || !a->dt_deq))
+    return fail(SSM_ERR_NULL, "scan: dt_codes needs dt_in (for dt_rank) and dt_deq");
+  if (a->dt_codes && !aligned(a->dt_codes, 16)) return fail(SSM_ERR_ALIGN, "scan: dt_codes must be 16-byte aligned");
   return SSM_OK;
 }
 
@@ -201,6 +204,7 @@ ScanArgs to_scan(const ssm_scan_args* a) {
     s.dr = a->dt_in; s.ld_dr = a->ld_dt_in; s.R = (int)a->dt_rank;
     s.w_dt = (const uint32_t*)a->w_dt; s.w_dt_row_words = cdiv(a->dt_rank, 16);
     s.s_dt = a->s_dt; s.g_dt = a->g_dt; s.eps = a->dt_eps;
+    s.ext_codes = a->dt_codes; s.ext_deq = a->dt_deq;
   }
   return s;
 }
@@ -554,6 +558,18 @@ ssm_status ssm_qat_sgd_step(float* w_latent, float* w_scale, const float* dw, co
   // the codes under the updated (learned) scales, with their zero count
   return ssm_ternary_quantize_weights(w_latent, n_out, k, group_size, w_scale, w_packed, w_scale, zero_count, ws, wsb,
                                       stream);
+}
+
+ssm_status ssm_dt_input_quantize(const void* dt_in, int32_t dtype, int64_t m, int64_t dt_rank, int64_t ld,
+                                 const float* g_dt, float eps, int8_t* codes, double* deq, hipStream_t stream) {
+  g_err.clear();
+  if (!act_dtype_ok(dtype)) return fail(SSM_ERR_DTYPE, "dt quantize: dtype %d", dtype);
+  if (m < 0) return fail(SSM_ERR_SHAPE, "dt quantize: m < 0");
+  if (dt_rank < 1 || dt_rank > 64) return fail(SSM_ERR_UNSUPPORTED, "dt quantize: dt_rank must be in [1, 64]");
+  if (ld < dt_rank) return fail(SSM_ERR_SHAPE, "dt quantize: ld < dt_rank");
+  if (m > 0 && (!dt_in || !codes || !deq)) return fail(SSM_ERR_NULL, "dt quantize: dt_in, codes and deq are required");
+  return dev(launch_dt_codes(dt_in, dtype == SSM_BF16, m, ld, (int)dt_rank, g_dt, eps, codes, deq, stream),
+             "dt quantize");
 }
 
 ssm_status ssm_dense_fwd(const void* x, int32_t dtype, int64_t m, int64_t k, int64_t ldx, const void* w, int64_t n,

@@ -80,9 +80,13 @@ struct ScanArgs {
   const float* s_dt; const float* g_dt; float eps;
   int dt_codes_ready;  // the dt input's int8 codes and factors are already in the workspace
   int32_t* dbg_dt_acc;  // nullable [B L, H]: the in-scan dt projection's int32 sums (stage checks)
+  const int8_t* ext_codes; const double* ext_deq;  // nullable: the dt input's codes computed by the caller
   const void* gate; int64_t ld_gate;  // nullable: y is multiplied by SiLU(gate) before it is stored
 };
 hipError_t launch_scan_m1(const ScanArgs& a, void* ws, hipStream_t s);
+// the dt input's int8 codes [M, cw] (cw = 16 ceil(R / 16)) and fp64 factors [M]
+hipError_t launch_dt_codes(const void* dr, int bf16, int64_t M, int64_t ld, int R, const float* g, float eps,
+                           int8_t* codes, double* deq, hipStream_t s);
 size_t scan_m1_workspace(const ScanArgs& a);
 // Where the scan keeps the dt input's codes ([M, *cw] int8 at offset 0) and their fp64
 // dequantisation factors ([M] at *off_deq) in its workspace.

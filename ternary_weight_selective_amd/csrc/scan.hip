@@ -25,8 +25,8 @@
 // row once, with a group of 16..64 lanes in the same fixed order as the standalone
 // BitLinear (for k <= 64 the 64-lane butterfly reduces to the group's butterfly plus exact
 // zero additions); in the scan each channel's int32 dot product with its ternary weight
-// row is v_dot4 instructions, and the dequantisation is the BitLinear epilogue's fp64
-// expression.
+// row is v_dot4 instructions, and the dequantisation s_dt acc max(m, 1e-5) / 127 is fp32
+// (the value never reaches memory: two roundings where a stored BitLinear output has one).
 #include <type_traits>
 
 #include "launch.hpp"
@@ -108,7 +108,7 @@ struct DtCodes {
 // One barrier per tile of TT = 16 steps, with double-buffered LDS: per tile i a thread
 //   1. stages tile i: B, C into LDS, and for its (step, channel) items the step's dt (dot
 //      product of the step's dt codes, held in registers since the previous tile, with the
-//      channel's ternary row; fp64 dequantisation; bias; softplus) and dt x;
+//      channel's ternary row; fp32 dequantisation; bias; softplus) and dt x;
 //   2. requests tile i + 1 (x, B, C, codes) into registers;
 //   3. barrier;
 //   4. adds the four waves' readout partials of tile i - 1, plus D x, and stores y;
@@ -155,9 +155,9 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   const T* DL = (const T*)a.delta;
 
   v4i wdt[4];
-  double s_dt = 0.0;
+  float s_dt = 0.0f;
   if (FUSED) {
-    s_dt = (double)a.s_dt[0];
+    s_dt = a.s_dt[0];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wdt[q] = unpack16_i8(q < RW ? a.w_dt[dcl * a.w_dt_row_words + q] : 0u);
   }
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(rq[FUSED ? i : 0][q][j], wdt[q][j], acc, false);
         if (!LOCAL && dc.dbg_acc && dv && t0 + t < te) dc.dbg_acc[(b * L + t0 + t) * Di + d] = acc;
-        dtv = (float)((s_dt * (double)acc) * rf[FUSED ? i : 0]);
+        dtv = (s_dt * (float)acc) * (float)rf[FUSED ? i : 0];
       } else {
         dtv = act_f32(rd[FUSED ? 0 : i]);
       }
@@ -426,11 +426,11 @@ hipError_t launch_m1_t(const ScanArgs& a, void* ws, hipStream_t s) {
     const int64_t M = a.batch * a.L;
     int8_t* codes = (int8_t*)ws;
     double* deq = (double*)((char*)ws + p.off_deq);
-    if (!a.dt_codes_ready) {
-      const int G = a.R <= 16 ? 16 : (a.R <= 32 ? 32 : 64);
-      const int64_t tok_per_block = 4 * (64 / G);
-      hipLaunchKernelGGL(k_dt_codes, dim3((unsigned)cdiv(M, tok_per_block)), dim3(256), 0, s, a.dr, a.act_bf16, M,
-                         a.ld_dr, a.R, a.g_dt, a.eps, codes, p.cw, deq);
+    if (a.ext_codes) {
+      codes = (int8_t*)a.ext_codes;
+      deq = (double*)a.ext_deq;
+    } else if (!a.dt_codes_ready) {
+      launch_dt_codes(a.dr, a.act_bf16, M, a.ld_dr, a.R, a.g_dt, a.eps, codes, deq, s);
     }
     dc.codes = codes;
     dc.deq = deq;
@@ -478,6 +478,16 @@ hipError_t launch_m1_n(const ScanArgs& a, void* ws, hipStream_t s) {
   }
 }
 }  // namespace
+
+hipError_t launch_dt_codes(const void* dr, int bf16, int64_t M, int64_t ld, int R, const float* g, float eps,
+                           int8_t* codes, double* deq, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int G = R <= 16 ? 16 : (R <= 32 ? 32 : 64);
+  const int64_t tok_per_block = 4 * (64 / G);
+  hipLaunchKernelGGL(k_dt_codes, dim3((unsigned)cdiv(M, tok_per_block)), dim3(256), 0, s, dr, bf16, M, ld, R, g, eps,
+                     codes, 16 * (int)cdiv(R, 16), deq);
+  return hipGetLastError();
+}
 
 void scan_m1_code_layout(const ScanArgs& a, int* cw, size_t* off_deq) {
   const ScanPlan p = plan_scan(a);

@@ -107,32 +107,41 @@ __global__ __launch_bounds__(256) void k_scan_ssd_rec(ScanArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // Chunked evaluation on the matrix cores (the state-space duality of "Transformers are
-// SSMs"): bf16 activations, headdim 64, d_state 64 or 128, chunks of Q = 64 steps.
-// A block owns one (sequence, head) and walks its chunks in order, the P x N state in MFMA
-// accumulators (8 waves: two per SIMD, so that one wave's dependent MFMAs, exponentials and
-// LDS round trips overlap the other's).  With cs_t the inclusive cumulative sum of dt_s A inside a chunk and h_in the
-// state entering it, for t in the chunk
-//   y_t = sum_{s <= t} (C_t . B_s) exp(cs_t - cs_s) dt_s x_s  +  exp(cs_t) C_t h_in^T  +  D x_t
+// SSMs"): bf16 activations, headdim 64, d_state 64 or 128, chunks of Q = 64 steps.  With cs_t
+// the inclusive cumulative sum of dt_s A inside a chunk and h_in the state entering it, for t
+// in the chunk
+//   y_t   = sum_{s <= t} (C_t . B_s) exp(cs_t - cs_s) dt_s x_s + exp(cs_t) C_t h_in^T + D x_t
 //   h_out = exp(cs_end) h_in + sum_s exp(cs_end - cs_s) dt_s x_s B_s^T
 // which is the recurrence h_t = exp(dt_t A) h_{t-1} + dt_t x_t B_t, y_t = C_t h_t + D x_t
-// regrouped.  Per chunk (wave w owning chunk rows 16 (w mod 4) .. + 15 and half the columns):
-//   G = C B^T (bf16 x bf16, exact products, fp32 sums), then the masked, decayed M (fp32);
-//   Y = M X and Z = C h_in^T; y = Y + exp(cs_t) Z + D x;
-//   h = exp(cs_end) h + (w X)^T B, w_s = exp(cs_end - cs_s) dt_s.
-// The fp32 operands (M, h_in, w X) enter the bf16 MFMAs as two bf16 terms (value = hi + lo,
-// about 16 significant bits), the bf16 activations as they are.
-// LDS holds the chunk's x, x^T, B, B^T, C (bf16), the waves' M rows and h_in (hi, lo).
+// regrouped.
+//
+// Work split.  Time is cut into S segments of whole chunks; a block owns 4 heads of one
+// sequence and one segment, and walks the segment's chunks in order (8 waves: wave w takes head
+// w / 2 and the state columns p of half w mod 2).  Segments run in parallel: pass 1 computes the
+// end state of every segment but the last from a zero state (state update only), a combine
+// composes them in order ((P, h_loc) o h = P h + h_loc, P = exp(A sum dt)), and pass 2 runs
+// every segment from its true incoming state, writing y.
+//
+// Per chunk, everything is matrix products on 16 x 16 x 32 bf16 MFMAs in transposed form, so
+// that no product's result goes through LDS to become another's operand:
+//   G^T = B C^T                       (A: B rows, B-operand: C rows; both staged row-major)
+//   M^T = G^T (.) exp(cs_t - cs_s) dt_s on s <= t, plus D on the diagonal (the D x term)
+//   y^T = x^T M^T + exp(cs_t) (h C^T)  (x^T staged transposed; M^T and h straight from the
+//                                       accumulators of G^T and of the state)
+//   h^T = exp(cs_end) h^T + B^T (w x) with w_s = exp(cs_end - cs_s) dt_s
+// An accumulator tile holds, per lane, 4 consecutive rows of one column; two such tiles give
+// the 8 reduction slots a lane feeds to a 16 x 16 x 32 MFMA, in a permuted order of the
+// reduction index that the other operand's lane reads in the same order (a sum over k does not
+// depend on the order).  fp32 operands (M^T, h, w x) enter as two bf16 terms: the truncated
+// value and the truncated remainder, about 16 significant bits; bf16 activations as they are.
 namespace {
-__device__ __forceinline__ uint16_t bf_bits(float f) { return f32_to_bf16(f); }
-__device__ __forceinline__ float bf_val(uint16_t b) { return bf16_to_f32(b); }
 constexpr float kLog2e = 1.4426950408889634f;
-__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 // softplus(v) = log(1 + e^v) (the identity above 20) on the hardware exp2 / log2, with the
 // rounding error c = (u - 1) - z of u = fl(1 + z) subtracted while u < 2 (where it dominates
 // the error of log(u) relative to the small result); below e^v = 1e-4 the series
 // e^v (1 - e^v / 2).
 __device__ __forceinline__ float softplus_hw(float v) {
-  const float z = exp_hw(v);
+  const float z = __builtin_amdgcn_exp2f(v * kLog2e);
   const float u = 1.0f + z;
   const float c = u < 2.0f ? (u - 1.0f) - z : 0.0f;
   const float big = 0.69314718055994531f * __builtin_amdgcn_logf(u) - c;
@@ -140,269 +149,477 @@ __device__ __forceinline__ float softplus_hw(float v) {
   const float r = z < 1e-4f ? small : big;
   return v > 20.0f ? v : r;
 }
-}  // namespace
 
 constexpr int kSsdQ = 64, kSsdP = 64;
+constexpr int kSsdHB = 4;           // heads per block
+constexpr int kSsdXS = kSsdQ + 8;   // row stride (bf16) of [.][Q] arrays in LDS
 
-// 8 waves, two per SIMD: wave w works on row tile rt = w mod 4 (chunk rows, or state rows p)
-// and half hf = w / 4 of the tiles along the other dimension; every output tile is computed
-// by one wave with the same MFMA sequence as with one wave per row tile.
-template <int NS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ssd_chunk(ScanArgs a) {
-  constexpr int Q = kSsdQ, P = kSsdP;
-  constexpr int XS = Q + 8;          // row stride (elements) of the [.][Q] arrays
-  constexpr int NSP = NS + 8;        // row stride of the [.][NS] arrays
-  constexpr int NTN = NS / 16;       // 16-wide n tiles
-  constexpr int NTH = NTN / 2;       // n tiles of a wave's state share
-  constexpr int KN = NS / 32;        // k steps over n
-  __shared__ __align__(16) uint16_t sX[Q * XS];        // x  [t][p]
-  __shared__ __align__(16) uint16_t sG[Q * XS];        // gate [t][p] (gated block)
-  __shared__ __align__(16) uint16_t sXT[P * XS];       // x^T [p][s]
-  __shared__ __align__(16) uint16_t sB[Q * NSP];       // B  [s][n]
-  __shared__ __align__(16) uint16_t sBT[NS * XS];      // B^T [n][s]
-  __shared__ __align__(16) uint16_t sC[Q * NSP];       // C  [t][n]
-  __shared__ __align__(16) uint16_t sM[4][2][16 * XS]; // per wave: M rows (hi, lo) [t][s]
-  __shared__ __align__(16) uint16_t sH[2][P * NSP];    // h_in (hi, lo) [p][n]
-  __shared__ float s_dt[Q], s_cs[Q];
-  __shared__ float s_w[Q], s_et[Q];  // exp(cs_end - cs_s) dt_s and exp(cs_t)
+struct SsdSeg {
+  int S;              // segments per sequence
+  int seg_ch;         // chunks per segment
+  float* hloc;        // [B, S-1, H, P, N]: pass 1 end states, then (combine) incoming states
+  float* sdec;        // [B, S-1, H]: log2 of each segment's decay, sum of dt A log2 e
+};
 
+// v (fp32) as two bf16 terms: hi = v truncated, lo = (v - hi) truncated.
+__device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
+  hi = __float_as_uint(v) & 0xFFFF0000u;
+  lo = __float_as_uint(v - __uint_as_float(hi)) & 0xFFFF0000u;
+}
+// bf16 pair (a in the low half, b in the high half) from two truncated fp32 bit patterns
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | b; }
+
+__device__ __forceinline__ v8bf ld8(const uint16_t* p) { return __builtin_bit_cast(v8bf, *(const v4i*)p); }
+// 4 + 4 bf16 from two 8-byte locations
+__device__ __forceinline__ v8bf ld44(const uint16_t* p0, const uint16_t* p1) {
+  const uint2 a = *(const uint2*)p0, b = *(const uint2*)p1;
+  return __builtin_bit_cast(v8bf, v4i{(int)a.x, (int)a.y, (int)b.x, (int)b.y});
+}
+__device__ __forceinline__ v8bf mk8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(v8bf, v4i{(int)a, (int)b, (int)c, (int)d});
+}
+}  // namespace
+
+template <int NS, bool LOCAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ssd_seg(ScanArgs a, SsdSeg sg) {
+  constexpr int Q = kSsdQ, P = kSsdP, HB = kSsdHB, XS = kSsdXS;
+  constexpr int NSP = NS + 8;   // row stride (bf16) of the row-major [t][n] arrays
+  constexpr int NT = NS / 16;   // n tiles
+  constexpr int NK = NS / 32;   // 32-wide k steps over n
+  __shared__ __align__(16) uint16_t sBr[LOCAL ? 1 : Q * NSP];  // B [s][n]
+  __shared__ __align__(16) uint16_t sC[LOCAL ? 1 : Q * NSP];   // C [t][n]
+  __shared__ __align__(16) uint16_t sBT[NS * XS];              // B^T [n][s]
+  __shared__ __align__(16) uint16_t sXT[HB][P * XS];           // x^T [p][s] per head
+  __shared__ __align__(16) float s_cs[HB][Q], s_dt[HB][Q], s_w[HB][Q], s_et[HB][Q];
+
+  // Element (r, c) of the row-major [64][NS] arrays: its 16-byte chunk c / 8 is stored at
+  // position (c / 8) ^ ((r / 16) mod 4), so that 16 lanes writing rows 4 apart, and 16 lanes
+  // reading 16 consecutive rows, each reach distinct banks.
+  auto rm = [](int r, int c) { return r * NSP + ((((c >> 3) ^ ((r >> 4) & 3))) << 3) + (c & 7); };
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rt = w & 3, hf = w >> 2;
+  const int hl = w >> 1, ph = w & 1;
   const int kq = lane >> 4, l16 = lane & 15;
   const int64_t L = a.L, H = a.H;
-  const int64_t hd = blockIdx.x % H, b = blockIdx.x / H;
-  const float A_h = a.A[hd];
-  const float bias_h = a.delta_bias ? a.delta_bias[hd] : 0.0f;
-  const float D_h = a.D ? a.D[hd] : 0.0f;
+  const int64_t nhb = cdiv(H, HB);
+  // blocks are dealt to the 8 XCDs round-robin by index: block i takes work item
+  // (i mod 8) T / 8 + i / 8, so that each XCD works through a contiguous run of items, heads
+  // fastest, and its L2 serves the B and C rows that all heads of a sequence share
+  const int64_t T = (int64_t)gridDim.x, i = blockIdx.x;
+  const int64_t wi = (T % 8 == 0) ? (i % 8) * (T / 8) + i / 8 : i;
+  const int64_t nbh = a.batch * nhb;
+  const int seg = (int)(wi / nbh);
+  const int64_t b = (wi % nbh) / nhb, hb = wi % nhb;
+  const int64_t head = hb * HB + hl;
+  const bool hv = head < H;
+  const int64_t hc = hv ? head : H - 1;  // parameters of a valid head for waves past the last
+  const float A2 = a.A[hc] * kLog2e;
+  const float bias_h = a.delta_bias ? a.delta_bias[hc] : 0.0f;
+  const float D_h = a.D ? a.D[hc] : 0.0f;
   const bf16_t* X = (const bf16_t*)a.x;
   const bf16_t* Bm = (const bf16_t*)a.Bm;
   const bf16_t* Cm = (const bf16_t*)a.Cm;
   const bf16_t* DT = (const bf16_t*)a.delta;
-  bf16_t* Y = (bf16_t*)a.y;
-
-  // state: lane holds h[p = 16 rt + 4 kq + r][n = 16 (NTH hf + jn) + l16]
-  v4f h[NTH];
-#pragma unroll
-  for (int jn = 0; jn < NTH; ++jn)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int pp = 16 * rt + 4 * kq + r, n = 16 * (NTH * hf + jn) + l16;
-      h[jn][r] = a.h0 ? a.h0[((b * H + hd) * P + pp) * NS + n] : 0.0f;
-    }
-  auto write_h = [&]() {
-#pragma unroll
-    for (int jn = 0; jn < NTH; ++jn)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * rt + 4 * kq + r, n = 16 * (NTH * hf + jn) + l16;
-        const uint16_t hi = bf_bits(h[jn][r]);
-        sH[0][pp * NSP + n] = hi;
-        sH[1][pp * NSP + n] = bf_bits(h[jn][r] - bf_val(hi));
-      }
-  };
-  write_h();
-
-  // chunk loads, 16-byte chunks with the step index fastest across the lanes (lane = step t,
-  // chunk column q = wave + 8 i), so that the transposed LDS copies are written along rows
-  constexpr int XC = Q * P / 8 / 512, BC = Q * NS / 8 / 512;
-  v4i px[XC], pg[XC], pb[BC], pc[BC];
-  float pdt = 0.0f;
   const bf16_t* G = (const bf16_t*)a.gate;
-  auto load = [&](int64_t c0) {
-    const bool ok = c0 + lane < L;
-    const int64_t tok = b * L + c0 + lane;
-#pragma unroll
-    for (int i = 0; i < XC; ++i) {
-      const int q = w + 8 * i;
-      px[i] = ok ? *(const v4i*)(X + tok * a.ld_x + hd * P + q * 8) : v4i{0, 0, 0, 0};
-      if (G) pg[i] = ok ? *(const v4i*)(G + tok * a.ld_gate + hd * P + q * 8) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int i = 0; i < BC; ++i) {
-      const int q = w + 8 * i;
-      pb[i] = ok ? *(const v4i*)(Bm + tok * a.ld_B + q * 8) : v4i{0, 0, 0, 0};
-      pc[i] = ok ? *(const v4i*)(Cm + tok * a.ld_C + q * 8) : v4i{0, 0, 0, 0};
-    }
-    if (w == 0) pdt = ok ? bf16_to_f32(DT[tok * a.ld_delta + hd]) : 0.0f;
-  };
-  auto stage = [&](int64_t c0) {
-    const int t = lane;
-#pragma unroll
-    for (int i = 0; i < XC; ++i) {
-      const int q = w + 8 * i;
-      *(v4i*)(&sX[t * XS + q * 8]) = px[i];
-      if (G) *(v4i*)(&sG[t * XS + q * 8]) = pg[i];
-      const uint16_t* v = (const uint16_t*)&px[i];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) sXT[(q * 8 + u) * XS + t] = v[u];
-    }
-#pragma unroll
-    for (int i = 0; i < BC; ++i) {
-      const int q = w + 8 * i;
-      *(v4i*)(&sB[t * NSP + q * 8]) = pb[i];
-      *(v4i*)(&sC[t * NSP + q * 8]) = pc[i];
-      const uint16_t* v = (const uint16_t*)&pb[i];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) sBT[(q * 8 + u) * XS + t] = v[u];
-    }
-    if (w == 0) {  // dt = softplus(delta + bias) (0 past the end), cs = inclusive cumsum of dt A
-      float dt = 0.0f;
-      if (c0 + lane < L) {
-        dt = pdt + bias_h;
-        if (a.softplus) dt = softplus_hw(dt);
-      }
-      float cs = dt * A_h;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float o = __shfl_up(cs, d, 64);
-        if (lane >= d) cs += o;
-      }
-      const float cend = __shfl(cs, 63, 64);
-      s_dt[lane] = dt;
-      s_cs[lane] = cs;
-      s_w[lane] = exp_hw(cend - cs) * dt;
-      s_et[lane] = exp_hw(cs);
-    }
-  };
-
+  bf16_t* Y = (bf16_t*)a.y;
   const int64_t nch = cdiv(L, Q);
-  load(0);
-  for (int64_t ch = 0; ch < nch; ++ch) {
-    const int64_t c0 = ch * Q;
-    stage(c0);
-    __syncthreads();
-    if (ch + 1 < nch) load(c0 + Q);
-    const float cs_end = s_cs[Q - 1];
+  const int64_t ch0 = (int64_t)seg * sg.seg_ch;
+  const int64_t ch1 = ch0 + sg.seg_ch < nch ? ch0 + sg.seg_ch : nch;
 
-    // G = C B^T for rows 16 rt .., s tiles j = 2 hf, 2 hf + 1 when j <= rt (the rest is
-    // masked); then those columns of M into LDS
-    {
-      v4f g[2];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) g[jj] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KN; ++kk) {
-        const v8bf af = __builtin_bit_cast(v8bf, *(const v4i*)(&sC[(16 * rt + l16) * NSP + kk * 32 + kq * 8]));
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = 2 * hf + jj;
-          if (j > rt) continue;
-          const v8bf bfr = __builtin_bit_cast(v8bf, *(const v4i*)(&sB[(16 * j + l16) * NSP + kk * 32 + kq * 8]));
-          g[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, g[jj], 0, 0, 0);
-        }
-      }
-      // M[t][s] = G exp(cs_t - cs_s) dt_s for s <= t; lane holds t = 16 rt + 4 kq + r, s = 16 j + l16
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 2 * hf + jj;
-          const int tl = 4 * kq + r, t = 16 * rt + tl, sidx = 16 * j + l16;
-          float m = 0.0f;
-          if (j <= rt && sidx <= t) m = g[jj][r] * (exp_hw(s_cs[t] - s_cs[sidx]) * s_dt[sidx]);
-          const uint16_t hi = bf_bits(m);
-          sM[rt][0][tl * XS + sidx] = hi;
-          sM[rt][1][tl * XS + sidx] = bf_bits(m - bf_val(hi));
-        }
-    }
-    __syncthreads();
-
-    // Y = M X (s < 16 rt + 16) and Z = C h_in^T for p tiles jp = 2 hf, 2 hf + 1; lane holds
-    // t = 16 rt + 4 kq + r, p = 16 jp + l16
-    v4f yacc[2], zacc[2];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) { yacc[jj] = v4f{0.f, 0.f, 0.f, 0.f}; zacc[jj] = v4f{0.f, 0.f, 0.f, 0.f}; }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (kk * 32 > 16 * rt + 15) continue;
-      const v8bf mh = __builtin_bit_cast(v8bf, *(const v4i*)(&sM[rt][0][l16 * XS + kk * 32 + kq * 8]));
-      const v8bf ml = __builtin_bit_cast(v8bf, *(const v4i*)(&sM[rt][1][l16 * XS + kk * 32 + kq * 8]));
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int jp = 2 * hf + jj;
-        const v8bf xf = __builtin_bit_cast(v8bf, *(const v4i*)(&sXT[(16 * jp + l16) * XS + kk * 32 + kq * 8]));
-        yacc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh, xf, yacc[jj], 0, 0, 0);
-        yacc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml, xf, yacc[jj], 0, 0, 0);
-      }
+  // state h^T: lane holds h[p = 16 (2 ph + ip) + l16][n = 16 mn + 4 kq + r]
+  v4f hT[NT][2];
+  {
+    const float* src = nullptr;
+    if (!LOCAL) {
+      if (seg == 0) src = a.h0 ? a.h0 + (b * H + hc) * (int64_t)P * NS : nullptr;
+      else src = sg.hloc + ((b * (sg.S - 1) + seg - 1) * H + hc) * (int64_t)P * NS;
     }
 #pragma unroll
-    for (int kk = 0; kk < KN; ++kk) {
-      const v8bf cf = __builtin_bit_cast(v8bf, *(const v4i*)(&sC[(16 * rt + l16) * NSP + kk * 32 + kq * 8]));
+    for (int mn = 0; mn < NT; ++mn)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int jp = 2 * hf + jj;
-        const int off = (16 * jp + l16) * NSP + kk * 32 + kq * 8;
-        const v8bf hh = __builtin_bit_cast(v8bf, *(const v4i*)(&sH[0][off]));
-        const v8bf hl = __builtin_bit_cast(v8bf, *(const v4i*)(&sH[1][off]));
-        zacc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, hh, zacc[jj], 0, 0, 0);
-        zacc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cf, hl, zacc[jj], 0, 0, 0);
+      for (int ip = 0; ip < 2; ++ip) {
+        const int pp = 16 * (2 * ph + ip) + l16;
+        hT[mn][ip] = src ? *(const v4f*)(src + pp * NS + 16 * mn + 4 * kq) : v4f{0.f, 0.f, 0.f, 0.f};
       }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 16 * rt + 4 * kq + r;
-      if (c0 + t >= L) continue;
-      const float et = s_et[t];
-      bf16_t* yr = Y + (b * L + c0 + t) * a.ld_y + hd * P;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int jp = 2 * hf + jj;
-        const int pp = 16 * jp + l16;
-        float yv = yacc[jj][r] + et * zacc[jj][r] + D_h * bf_val(sX[t * XS + pp]);
-        if (G) yv = yv * silu_gate(bf_val(sG[t * XS + pp]));
-        yr[pp] = f32_to_bf16(yv);
-      }
-    }
-
-    // state: h = exp(cs_end) h + (w X)^T B; A fragment: p = 16 rt + l16, s = 32 kk + 8 kq + u
-    const float ed = exp_hw(cs_end);
-#pragma unroll
-    for (int jn = 0; jn < NTH; ++jn)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) h[jn][r] *= ed;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint16_t* xr = &sXT[(16 * rt + l16) * XS + kk * 32 + kq * 8];
-      uint16_t ahi[8], alo[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int sidx = kk * 32 + kq * 8 + u;
-        const float v = bf_val(xr[u]) * s_w[sidx];
-        ahi[u] = bf_bits(v);
-        alo[u] = bf_bits(v - bf_val(ahi[u]));
-      }
-      const v8bf ah = __builtin_bit_cast(v8bf, *(const v4i*)ahi);
-      const v8bf al = __builtin_bit_cast(v8bf, *(const v4i*)alo);
-#pragma unroll
-      for (int jn = 0; jn < NTH; ++jn) {
-        const int n0t = 16 * (NTH * hf + jn);
-        const v8bf bfr = __builtin_bit_cast(v8bf, *(const v4i*)(&sBT[(n0t + l16) * XS + kk * 32 + kq * 8]));
-        h[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bfr, h[jn], 0, 0, 0);
-        h[jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bfr, h[jn], 0, 0, 0);
-      }
-    }
-    __syncthreads();
-    write_h();
   }
-  if (a.h_last) {
+
+  // ---- chunk loads into registers: 4 consecutive steps x 8 consecutive columns per task ----
+  // x of the block's heads (columns hb HB P .. + HB P): tasks (cg = tid % 32, tg = tid / 32)
+  // B (and C): NS / 8 column groups x 16 step groups; B on threads [0, NBT), C on [NBT, 2 NBT)
+  constexpr int NBT = NS / 8 * 16;
+  // a set of prefetch registers: one chunk's x, B (or C) and dt (raw bf16).  Every load is
+  // unconditional, from a clamped address, and kept raw: a load whose value is converted or
+  // selected at once makes the compiler wait for all loads in flight right there; the rows past
+  // the sequence's end are zeroed when the chunk is staged.
+  struct Pre {
+    v4i x[4], b[4];
+    bf16_t dt;   // state pass: raw
+    float dtf;   // output pass: converted at the load (its wait then covers the chunk's loads)
+  };
+  // (the step group is the fastest index across lanes, so that the transposed LDS writes of 16
+  // lanes fill one row and the next 16 lanes the row 8 below: distinct banks)
+  const int xtg = tid & 15, xcg = tid >> 4;
+  const bool xv = (int64_t)hb * HB * P + xcg * 8 < H * P;  // the task's columns exist
+  const bool isb = tid < NBT, isc = !LOCAL && tid >= NBT && tid < 2 * NBT;
+  const int btask = isb ? tid : tid - NBT;
+  const int btg = btask & 15, bcg = btask >> 4;
+  const bf16_t* xsrc = X + hb * HB * P + (xv ? xcg * 8 : 0);
+  const bf16_t* bsrc = (isc ? Cm : Bm) + bcg * 8;
+  const int64_t bld = isc ? a.ld_C : a.ld_B;
+  const bf16_t* dsrc = DT + hc;
+  auto load = [&](Pre& pr, int64_t c0) {
+    if constexpr (LOCAL) {
 #pragma unroll
-    for (int jn = 0; jn < NTH; ++jn)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pp = 16 * rt + 4 * kq + r, n = 16 * (NTH * hf + jn) + l16;
-        a.h_last[((b * H + hd) * P + pp) * NS + n] = h[jn][r];
+      for (int u = 0; u < 4; ++u) {
+        const int64_t t = c0 + 4 * xtg + u;
+        pr.x[u] = *(const v4i*)(xsrc + (b * L + (t < L ? t : L - 1)) * a.ld_x);
       }
+      if (isb) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t t = c0 + 4 * btg + u;
+          pr.b[u] = *(const v4i*)(bsrc + (b * L + (t < L ? t : L - 1)) * bld);
+        }
+      }
+      const int64_t td = c0 + lane;
+      pr.dt = dsrc[(b * L + (td < L ? td : L - 1)) * a.ld_delta];
+    } else {
+      // (fewer registers: the output pass's products leave little room)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t t = c0 + 4 * xtg + u;
+        const bool ok = xv && t < L;
+        pr.x[u] = ok ? *(const v4i*)(X + (b * L + t) * a.ld_x + hb * HB * P + xcg * 8) : v4i{0, 0, 0, 0};
+      }
+      if (isb || isc) {
+        const bf16_t* src = isb ? Bm : Cm;
+        const int64_t ld = isb ? a.ld_B : a.ld_C;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t t = c0 + 4 * btg + u;
+          pr.b[u] = t < L ? *(const v4i*)(src + (b * L + t) * ld + bcg * 8) : v4i{0, 0, 0, 0};
+        }
+      }
+      if (ph == 0) pr.dtf = (hv && c0 + lane < L) ? bf16_to_f32(DT[(b * L + c0 + lane) * a.ld_delta + head]) : 0.0f;
+    }
+  };
+  // transposed 8-byte writes: column u of the 4 step vectors v0..v3 (8 bf16 each)
+  auto tcol = [&](const v4i (&v)[4], int u) -> uint2 {
+    const int d = u >> 1;
+    const uint32_t sel = (u & 1) ? 0x07060302u : 0x05040100u;
+    return uint2{__builtin_amdgcn_perm((uint32_t)v[1][d], (uint32_t)v[0][d], sel),
+                 __builtin_amdgcn_perm((uint32_t)v[3][d], (uint32_t)v[2][d], sel)};
+  };
+  float cs_end = 0.0f;  // this chunk's cs at its last step (log2 domain), per wave
+  auto stage = [&](Pre& pr, int64_t c0) {
+    // rows past the sequence's end (and columns past the last head) staged as zeros (the
+    // output pass loaded zeros there)
+    if constexpr (LOCAL) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (!(xv && c0 + 4 * xtg + u < L)) pr.x[u] = v4i{0, 0, 0, 0};
+        if (c0 + 4 * btg + u >= L) pr.b[u] = v4i{0, 0, 0, 0};
+      }
+    }
+    {
+      const int hh = xcg >> 3, p0 = (xcg & 7) * 8;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) *(uint2*)(&sXT[hh][(p0 + u) * XS + 4 * xtg]) = tcol(pr.x, u);
+    }
+    if (isb) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) *(uint2*)(&sBT[(bcg * 8 + u) * XS + 4 * btg]) = tcol(pr.b, u);
+      if (!LOCAL) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *(v4i*)(&sBr[rm(4 * btg + u, bcg * 8)]) = pr.b[u];
+      }
+    }
+    if (!LOCAL && isc) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *(v4i*)(&sC[rm(4 * btg + u, bcg * 8)]) = pr.b[u];
+    }
+    // dt = softplus(delta + bias) (0 past the end), cs = inclusive cumsum of dt A log2 e
+    // (computed on every lane, then selected: no branch around the use of a loaded value)
+    float dt = 0.0f;
+    if constexpr (LOCAL) {
+      dt = bf16_to_f32(pr.dt) + bias_h;
+      if (a.softplus) dt = softplus_hw(dt);
+      dt = (ph == 0 && hv && c0 + lane < L) ? dt : 0.0f;
+    } else if (ph == 0 && hv && c0 + lane < L) {
+      dt = pr.dtf + bias_h;
+      if (a.softplus) dt = softplus_hw(dt);
+    }
+    float cs = dt * A2;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float o = __shfl_up(cs, d, 64);
+      if (lane >= d) cs += o;
+    }
+    cs_end = __shfl(cs, 63, 64);
+    if (ph == 0) {
+      s_cs[hl][lane] = cs;
+      s_dt[hl][lane] = dt;
+      s_w[hl][lane] = __builtin_amdgcn_exp2f(cs_end - cs) * dt;
+      s_et[hl][lane] = __builtin_amdgcn_exp2f(cs);
+    }
+  };
+
+  // Loads run DEPTH chunks ahead: the state-only pass (few registers) keeps two sets of
+  // prefetch registers, the output pass one.
+  constexpr int DEPTH = LOCAL ? 2 : 1;
+  float sdec = 0.0f;
+  auto body = [&](Pre& pr, int64_t ch) {
+    const int64_t c0 = ch * Q;
+    stage(pr, c0);
+    __syncthreads();
+    // the loads of chunk ch + DEPTH into the set just staged, in flight through this chunk's
+    // work (the output pass issues them after its outputs, whose products need the registers);
+    // unconditional (past the segment's end they repeat its last chunk, from the cache), so that
+    // the wait for each set counts the loads issued after it exactly
+    if (LOCAL) load(pr, (ch + DEPTH < ch1 ? ch + DEPTH : ch1 - 1) * Q);
+    else if (ch + 1 < ch1) load(pr, c0 + Q);
+    // the head's dt comes from its even wave's load: both waves take its staged cs_end
+    cs_end = s_cs[hl][Q - 1];
+    sdec += cs_end;
+    const float* ws_ = s_w[hl];
+
+    if (!LOCAL) {
+      // ---- Z^T = h C^T per (p tile ip, t tile jt), scaled by exp(cs_t): lane holds
+      // Z^T[p = 16 (2 ph + ip) + 4 kq + r][t = 16 jt + l16]
+      v4f zacc[2][4];
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) zacc[ip][jt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m2 = 0; m2 < NT / 2; ++m2) {
+        v8bf ah[2], al[2];
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip) {
+          uint32_t hi[8], lo[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            split2(hT[2 * m2][ip][r], hi[r], lo[r]);
+            split2(hT[2 * m2 + 1][ip][r], hi[4 + r], lo[4 + r]);
+          }
+          ah[ip] = mk8(pack_hi(hi[0], hi[1]), pack_hi(hi[2], hi[3]), pack_hi(hi[4], hi[5]), pack_hi(hi[6], hi[7]));
+          al[ip] = mk8(pack_hi(lo[0], lo[1]), pack_hi(lo[2], lo[3]), pack_hi(lo[4], lo[5]), pack_hi(lo[6], lo[7]));
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          // C rows t = 16 jt + l16 at the slots' n (32 m2 + 4 kq + u, 32 m2 + 16 + 4 kq + u)
+          const int tr = 16 * jt + l16;
+          const v8bf cf = ld44(&sC[rm(tr, 32 * m2 + 4 * kq)], &sC[rm(tr, 32 * m2 + 16 + 4 * kq)]);
+#pragma unroll
+          for (int ip = 0; ip < 2; ++ip) {
+            zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ip], cf, zacc[ip][jt], 0, 0, 0);
+            zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ip], cf, zacc[ip][jt], 0, 0, 0);
+          }
+        }
+      }
+      const float* cs_ = s_cs[hl];
+      const float* dt_ = s_dt[hl];
+      const float* et_ = s_et[hl];
+      const uint16_t* xt = sXT[hl];
+      // x^T rows p = 16 (2 ph + ip) + l16 at the slots' s (32 pr + 4 kq + u, 32 pr + 16 + 4 kq + u)
+      v8bf xa[2][2];
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const uint16_t* xr = &xt[(16 * (2 * ph + ip) + l16) * XS + 32 * pr + 4 * kq];
+          xa[ip][pr] = ld44(xr, xr + 16);
+        }
+      // ---- per t tile jt: G^T tiles (s tile ms <= jt; lane holds G^T[16 ms + 4 kq + r][16 jt + l16]),
+      // M^T = G^T exp(cs_t - cs_s) dt_s on s <= t (+ D on the diagonal), then y^T += x^T M^T
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        v4f g[4];
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) g[ms] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          const v8bf cb = ld8(&sC[rm(16 * jt + l16, 32 * kk + 8 * kq)]);
+#pragma unroll
+          for (int ms = 0; ms <= jt; ++ms)
+            g[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld8(&sBr[rm(16 * ms + l16, 32 * kk + 8 * kq)]), cb,
+                                                            g[ms], 0, 0, 0);
+        }
+        const int t = 16 * jt + l16;
+        const float cst = cs_[t];
+        const float e = et_[t];
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) zacc[ip][jt][r] *= e;
+        uint32_t mh[4][2], mlo[4][2];
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+          if (ms > jt) {  // above the diagonal: zero (the partner of a diagonal tile in its pair)
+            mh[ms][0] = mh[ms][1] = mlo[ms][0] = mlo[ms][1] = 0u;
+            continue;
+          }
+          const v4f css = *(const v4f*)(&cs_[16 * ms + 4 * kq]);
+          const v4f dts = *(const v4f*)(&dt_[16 * ms + 4 * kq]);
+          uint32_t hi[4], lo[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int sidx = 16 * ms + 4 * kq + r;
+            float m = 0.0f;
+            if (sidx <= t) m = g[ms][r] * (__builtin_amdgcn_exp2f(cst - css[r]) * dts[r]);
+            if (sidx == t) m += D_h;
+            split2(m, hi[r], lo[r]);
+          }
+          mh[ms][0] = pack_hi(hi[0], hi[1]);
+          mh[ms][1] = pack_hi(hi[2], hi[3]);
+          mlo[ms][0] = pack_hi(lo[0], lo[1]);
+          mlo[ms][1] = pack_hi(lo[2], lo[3]);
+        }
+#pragma unroll
+        for (int pr = 0; 2 * pr <= jt; ++pr) {
+          const v8bf bh = mk8(mh[2 * pr][0], mh[2 * pr][1], mh[2 * pr + 1][0], mh[2 * pr + 1][1]);
+          const v8bf bl = mk8(mlo[2 * pr][0], mlo[2 * pr][1], mlo[2 * pr + 1][0], mlo[2 * pr + 1][1]);
+#pragma unroll
+          for (int ip = 0; ip < 2; ++ip) {
+            zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[ip][pr], bh, zacc[ip][jt], 0, 0, 0);
+            zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[ip][pr], bl, zacc[ip][jt], 0, 0, 0);
+          }
+        }
+        // ---- y: lane holds y[t][p = 16 (2 ph + ip) + 4 kq + r]
+        const int64_t tg = c0 + t;
+        if (hv && tg < L) {
+#pragma unroll
+          for (int ip = 0; ip < 2; ++ip) {
+            const int64_t col = head * P + 16 * (2 * ph + ip) + 4 * kq;
+            float v[4] = {zacc[ip][jt][0], zacc[ip][jt][1], zacc[ip][jt][2], zacc[ip][jt][3]};
+            if (G) {
+              const uint2 gg = *(const uint2*)(G + (b * L + tg) * a.ld_gate + col);
+              v[0] *= silu_gate(bf16_to_f32((bf16_t)(gg.x & 0xFFFFu)));
+              v[1] *= silu_gate(bf16_to_f32((bf16_t)(gg.x >> 16)));
+              v[2] *= silu_gate(bf16_to_f32((bf16_t)(gg.y & 0xFFFFu)));
+              v[3] *= silu_gate(bf16_to_f32((bf16_t)(gg.y >> 16)));
+            }
+            const uint2 o{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                          (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
+            *(uint2*)(Y + (b * L + tg) * a.ld_y + col) = o;
+          }
+        }
+      }
+    }
+
+    // ---- state: h^T = exp(cs_end) h^T + B^T (w x)
+    const float ed = __builtin_amdgcn_exp2f(cs_end);
+#pragma unroll
+    for (int mn = 0; mn < NT; ++mn)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hT[mn][ip][r] *= ed;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const v4f w0 = *(const v4f*)(&ws_[32 * kk + 8 * kq]);
+      const v4f w1 = *(const v4f*)(&ws_[32 * kk + 8 * kq + 4]);
+      const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      v8bf xh[2], xl[2];
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) {
+        const v4i raw = *(const v4i*)(&sXT[hl][(16 * (2 * ph + ip) + l16) * XS + 32 * kk + 8 * kq]);
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t word = (uint32_t)raw[u >> 1];
+          const float xvv = __uint_as_float((u & 1) ? (word & 0xFFFF0000u) : (word << 16));
+          split2(xvv * wv[u], hi[u], lo[u]);
+        }
+        xh[ip] = mk8(pack_hi(hi[0], hi[1]), pack_hi(hi[2], hi[3]), pack_hi(hi[4], hi[5]), pack_hi(hi[6], hi[7]));
+        xl[ip] = mk8(pack_hi(lo[0], lo[1]), pack_hi(lo[2], lo[3]), pack_hi(lo[4], lo[5]), pack_hi(lo[6], lo[7]));
+      }
+#pragma unroll
+      for (int mn = 0; mn < NT; ++mn) {
+        const v8bf bt = ld8(&sBT[(16 * mn + l16) * XS + 32 * kk + 8 * kq]);
+#pragma unroll
+        for (int ip = 0; ip < 2; ++ip) {
+          hT[mn][ip] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt, xh[ip], hT[mn][ip], 0, 0, 0);
+          hT[mn][ip] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt, xl[ip], hT[mn][ip], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  };
+  Pre p0, p1;
+  load(p0, ch0 * Q);
+  if (DEPTH == 1) {
+    for (int64_t ch = ch0; ch < ch1; ++ch) body(p0, ch);
+  } else {
+    load(p1, (ch0 + 1 < ch1 ? ch0 + 1 : ch0) * Q);
+    int64_t ch = ch0;
+    for (; ch + 1 < ch1; ch += 2) {  // the two sets by parity, each named statically
+      body(p0, ch);
+      body(p1, ch + 1);
+    }
+    if (ch < ch1) body(p0, ch);
+  }
+
+  // ---- the segment's end state: pass 1 keeps it (and the segment's decay) for the combine;
+  // the last segment of pass 2 returns it
+  float* dst = nullptr;
+  if (LOCAL) dst = sg.hloc + ((b * (sg.S - 1) + seg) * H + hc) * (int64_t)P * NS;
+  else if (a.h_last && seg == sg.S - 1) dst = a.h_last + (b * H + hc) * (int64_t)P * NS;
+  if (dst && hv) {
+#pragma unroll
+    for (int mn = 0; mn < NT; ++mn)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip) *(v4f*)(dst + (16 * (2 * ph + ip) + l16) * NS + 16 * mn + 4 * kq) = hT[mn][ip];
+  }
+  if (LOCAL && hv && ph == 0 && lane == 0) sg.sdec[(b * (sg.S - 1) + seg) * H + head] = sdec;
+}
+
+// Combine over segments, per (sequence, head, state element): afterwards hloc[b, s] holds the
+// state entering segment s + 1.
+__global__ __launch_bounds__(256) void k_ssd_combine(const float* __restrict__ h0, float* __restrict__ hloc,
+                                                     const float* __restrict__ sdec, int64_t B, int64_t H,
+                                                     int64_t PN, int S) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * H * PN) return;
+  const int64_t b = i / (H * PN), hp = i % (H * PN), hd = hp / PN, e = hp % PN;
+  float h = h0 ? h0[i] : 0.0f;
+  for (int s = 0; s + 1 < S; ++s) {
+    const int64_t j = ((b * (S - 1) + s) * H + hd) * PN + e;
+    h = __builtin_fmaf(__builtin_amdgcn_exp2f(sdec[(b * (S - 1) + s) * H + hd]), h, hloc[j]);
+    hloc[j] = h;
   }
 }
 
-// The chunked kernel takes bf16 activations with headdim 64, d_state 64 or 128, and row
-// strides and bases that allow 16-byte loads of x, B and C.
+// The chunked kernels take bf16 activations with headdim 64, d_state 64 or 128, and row
+// strides and bases that allow 16-byte loads of x, B and C (8-byte loads of the gate).
 static bool ssd_chunk_ok(const ScanArgs& a) {
   auto al = [](const void* p) { return ((uintptr_t)p % 16) == 0; };
   return a.act_bf16 && a.P == kSsdP && (a.N == 64 || a.N == 128) && a.ld_x % 8 == 0 && a.ld_B % 8 == 0 &&
-         a.ld_C % 8 == 0 && al(a.x) && al(a.Bm) && al(a.Cm) && (!a.gate || (a.ld_gate % 8 == 0 && al(a.gate)));
+         a.ld_C % 8 == 0 && al(a.x) && al(a.Bm) && al(a.Cm) && (!a.gate || (a.ld_gate % 4 == 0 && ((uintptr_t)a.gate % 8) == 0));
 }
+
+namespace {
+// Segment count: a function of the shape only.  Blocks of (sequence, 4 heads) below 256 (one
+// per MI355X compute unit) are multiplied by time segments of whole chunks.
+struct SsdPlan {
+  int S = 1, seg_ch = 1;
+  size_t ws = 0;
+};
+SsdPlan plan_ssd(const ScanArgs& a) {
+  SsdPlan p;
+  const int64_t nch = cdiv(a.L, kSsdQ);
+  const int64_t blocks = a.batch * cdiv(a.H, kSsdHB);
+  int64_t S = 1;
+  if (blocks < 256) S = cdiv(256, blocks);
+  if (S > nch) S = nch;
+  if (S < 1) S = 1;
+  p.seg_ch = (int)cdiv(nch, S);
+  p.S = (int)cdiv(nch, p.seg_ch);
+  if (p.S > 1)
+    p.ws = (size_t)a.batch * (p.S - 1) * a.H * ((size_t)a.P * a.N + 1) * sizeof(float);
+  return p;
+}
+}  // namespace
 
 template <int NS, typename T>
 static void launch_ssd_t(const ScanArgs& a, hipStream_t s) {
@@ -423,14 +640,37 @@ static hipError_t launch_ssd_n(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t scan_ssd_workspace(const ScanArgs&) { return 0; }
+// The segment carries of the chunked kernels (any dtype or alignment: a workspace query knows
+// the shape only).
+size_t scan_ssd_workspace(const ScanArgs& a) {
+  if (a.batch == 0 || a.L == 0 || a.P != kSsdP || (a.N != 64 && a.N != 128)) return 0;
+  return plan_ssd(a).ws;
+}
 
-hipError_t launch_scan_ssd(const ScanArgs& a, void*, size_t, hipStream_t s) {
+hipError_t launch_scan_ssd(const ScanArgs& a, void* ws, size_t wsb, hipStream_t s) {
   if (a.batch == 0 || a.L == 0) return hipSuccess;
   if (ssd_chunk_ok(a)) {
-    const dim3 grid((unsigned)(a.batch * a.H)), block(512);
-    if (a.N == 128) hipLaunchKernelGGL((k_ssd_chunk<128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ssd_chunk<64>), grid, block, 0, s, a);
+    const SsdPlan p = plan_ssd(a);
+    if (p.ws > wsb || (p.ws && !ws)) return hipErrorInvalidValue;
+    SsdSeg sg{};
+    sg.S = p.S;
+    sg.seg_ch = p.seg_ch;
+    if (p.S > 1) {
+      sg.hloc = (float*)ws;
+      sg.sdec = sg.hloc + (size_t)a.batch * (p.S - 1) * a.H * a.P * a.N;
+    }
+    const unsigned nb = (unsigned)(a.batch * cdiv(a.H, kSsdHB));
+    if (p.S > 1) {
+      const dim3 g1(nb * (unsigned)(p.S - 1));
+      if (a.N == 128) hipLaunchKernelGGL((k_ssd_seg<128, true>), g1, dim3(512), 0, s, a, sg);
+      else hipLaunchKernelGGL((k_ssd_seg<64, true>), g1, dim3(512), 0, s, a, sg);
+      const int64_t n = a.batch * a.H * a.P * a.N;
+      hipLaunchKernelGGL(k_ssd_combine, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, a.h0, sg.hloc, sg.sdec,
+                         a.batch, a.H, a.P * a.N, p.S);
+    }
+    const dim3 g2(nb * (unsigned)p.S);
+    if (a.N == 128) hipLaunchKernelGGL((k_ssd_seg<128, false>), g2, dim3(512), 0, s, a, sg);
+    else hipLaunchKernelGGL((k_ssd_seg<64, false>), g2, dim3(512), 0, s, a, sg);
     return hipGetLastError();
   }
   return a.act_bf16 ? launch_ssd_n<bf16_t>(a, s) : launch_ssd_n<float>(a, s);

@@ -60,15 +60,23 @@ def check(got, ref, tol: float, *, elem: float | None = None, frac: float = 0.0,
     return m
 
 
-# Outputs behind a chain of int8 quantisers (whole mixer layers with int8 activations): an
-# element may be off by a few quantisation steps of the codes a boundary flip moved (a step of
-# out_proj's codes is s_w max|y| / 127, about 5e-4 of the output's rms at the TriSSM shape),
-# and such elements must stay rare.  fp32 outputs only; bf16 outputs keep the bf16 bound.
-CHAIN = {"elem": 5e-3, "frac": 5e-3}
+# Outputs behind a chain of rounded stages, compared end to end (whole mixer layers):
+#  fp32: int8 quantisers in the chain; an element may be off by a few quantisation steps of
+#   the codes a boundary flip moved (a step of out_proj's codes is s_w max|y| / 127, about 5e-4
+#   of the output's rms at the TriSSM shape), and such elements must stay rare;
+#  bf16: every stored activation is rounded to bf16 and the A16 projections take x_hat as bf16,
+#   so dt, B, C and x differ by bf16 steps before the scan, and the decays exp(A sum dt) scale a
+#   dt difference by |A sum dt|: single elements of a layer's output move by a few 1e-2 while
+#   each stage fed the previous stage's values stays within 2e-2 (tested stage by stage).
+CHAIN = {"f32": {"elem": 5e-3, "frac": 5e-3}, "bf16_a16": {"elem": 6e-2, "frac": 1e-3}}
 
 
-def chain(dtype_name: str) -> dict:
-    return CHAIN if dtype_name == "f32" else {}
+def chain(dtype_name: str, a16: bool = False) -> dict:
+    """Bounds for a whole layer's output; bf16 outputs of int8-activation layers keep the bf16
+    bound itself (their projections' stored outputs are exact up to the final rounding)."""
+    if dtype_name == "f32":
+        return CHAIN["f32"]
+    return CHAIN["bf16_a16"] if a16 else {}
 
 
 def to_dev(a, dtype=torch.float32):
