@@ -233,6 +233,21 @@ ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* workspace, size_
                                   hipStream_t stream);
 
 /*
+ * ssm_selective_scan_fwd_noalloc -- ssm_selective_scan_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation): the same kernels and results, with the scratch memory (the dt input's codes,
+ * the carries between time chunks or segments) in an array the library holds on each GPU,
+ * SSM_NOALLOC_SCRATCH_BYTES long, instead of a caller workspace.  The call allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (concurrent
+ * streams, threads) race and must be serialised by the caller.  The array holds the last
+ * call's contents; each call writes what it reads.
+ * Errors: as ssm_selective_scan_fwd; SSM_ERR_UNSUPPORTED when the shape needs more scratch
+ * than SSM_NOALLOC_SCRATCH_BYTES (ssm_selective_scan_workspace_bytes gives the need).
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ssm_status ssm_selective_scan_fwd_noalloc(const ssm_scan_args* a, hipStream_t stream);
+
+/*
  * ssm_dt_input_quantize -- the first step of the scan's dt projection on its own: per token
  * row m of dt_in (dt_rank values, row stride ld, act dtype `dtype`), RMSNorm with gains g_dt
  * (NULL = ones) and epsilon eps, then absmax int8 codes (TriSSM README: BitLinear with int8

@@ -88,7 +88,8 @@ class SsmError(RuntimeError):
 _lib = None
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed_row_bytes",
            "ssm_ternary_quantize_workspace_bytes", "ssm_ternary_quantize_weights", "ssm_bitlinear_workspace_bytes",
-           "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd", "ssm_dt_input_quantize",
+           "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_noalloc",
+           "ssm_dt_input_quantize",
            "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fwd_stages", "ssm_mixer_fuses_front", "ssm_mixer_step",
            "ssm_conv1d_silu_fwd", "ssm_dense_fwd", "ssm_bitlinear_bwd_workspace_bytes", "ssm_bitlinear_bwd",
            "ssm_qat_sgd_step", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd",
@@ -121,6 +122,8 @@ def lib():
         L.ssm_selective_scan_workspace_bytes.restype = _sz
         L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _vp, _sz, _vp]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
+        L.ssm_selective_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanArgs), _vp]
+        L.ssm_selective_scan_fwd_noalloc.restype = ctypes.c_int
         L.ssm_dt_input_quantize.argtypes = [_vp, _i32, _i64, _i64, _i64, _vp, ctypes.c_float, _vp, _vp, _vp]
         L.ssm_dt_input_quantize.restype = ctypes.c_int
         L.ssm_mixer_workspace_bytes.argtypes = [ctypes.POINTER(MixerConfig), _i64, _i64]
@@ -268,8 +271,8 @@ def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch
                            Cm: torch.Tensor, D: torch.Tensor | None = None, delta_bias: torch.Tensor | None = None,
                            softplus: bool = True, h0: torch.Tensor | None = None, return_last_state: bool = False,
                            out: torch.Tensor | None = None, dt_proj: dict | None = None,
-                           gate: torch.Tensor | None = None, stream=None):
-    """Selective scan.  x [B, L, H*P], delta [B, L, H], Bm/Cm [B, L, N]; A [H, N] (Mamba-1 kind,
+                           gate: torch.Tensor | None = None, noalloc: bool = False, stream=None):
+    """Selective scan (noalloc: through ssm_selective_scan_fwd_noalloc, the library's own scratch).  x [B, L, H*P], delta [B, L, H], Bm/Cm [B, L, N]; A [H, N] (Mamba-1 kind,
     P = 1) or [H] (SSD kind).  Views with a contiguous last dim and even row strides are fine.
     dt_proj (Mamba-1 kind): dict(dt_in [B, L, >= R] view, w_dt packed [H, row bytes], s_dt [1],
     dt_rank R, optional g_dt, eps): dt is the A8 BitLinear of dt_in computed inside the scan
@@ -303,6 +306,9 @@ def ssm_selective_scan_fwd(x: torch.Tensor, delta: torch.Tensor | None, A: torch
     if gate is not None:
         a.gate, a.ld_gate = _p(gate), _rows(gate, "gate")[1]
     L = lib()
+    if noalloc:
+        _check(L.ssm_selective_scan_fwd_noalloc(ctypes.byref(a), _stream(stream)))
+        return (out, hl) if return_last_state else out
     nb = L.ssm_selective_scan_workspace_bytes(ctypes.byref(a))
     ws = _workspace(nb, x.device)
     _check(L.ssm_selective_scan_fwd(ctypes.byref(a), _p(ws), nb, _stream(stream)))

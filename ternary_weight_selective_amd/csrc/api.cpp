@@ -423,6 +423,25 @@ ssm_status ssm_selective_scan_fwd(const ssm_scan_args* a, void* ws, size_t wsb, 
   return dev(launch_scan_ssd(s, ws, wsb, stream), "scan");
 }
 
+ssm_status ssm_selective_scan_fwd_noalloc(const ssm_scan_args* a, hipStream_t stream) {
+  g_err.clear();
+  ssm_status st = scan_check(a);
+  if (st != SSM_OK) return st;
+  const ScanArgs s = to_scan(a);
+  const size_t need = a->a_per_state ? scan_m1_workspace(s) : scan_ssd_workspace(s);
+  static_assert(kStaticScratchBytes == SSM_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+  if (need > kStaticScratchBytes)
+    return fail(SSM_ERR_UNSUPPORTED, "scan noalloc: needs %zu bytes of scratch, more than the %zu the library holds",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need) {
+    st = dev(static_scratch(&ws), "scan noalloc scratch");
+    if (st != SSM_OK) return st;
+  }
+  if (a->a_per_state) return dev(launch_scan_m1(s, ws, stream), "scan noalloc");
+  return dev(launch_scan_ssd(s, ws, kStaticScratchBytes, stream), "scan noalloc");
+}
+
 size_t ssm_mixer_workspace_bytes(const ssm_mixer_config* c, int64_t batch, int64_t seqlen) {
   std::string keep = g_err;
   MixPlan p;

@@ -92,6 +92,12 @@ size_t scan_m1_workspace(const ScanArgs& a);
 // dequantisation factors ([M] at *off_deq) in its workspace.
 void scan_m1_code_layout(const ScanArgs& a, int* cw, size_t* off_deq);
 
+// The library's static scratch array on the current device (scan.hip): kStaticScratchBytes,
+// 256-byte aligned, shared by every call on that device.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(void** ptr);
+
 // ---- causal depthwise convolution + SiLU (conv.hip)
 struct ConvArgs {
   int64_t batch, L, C;

@@ -27,6 +27,7 @@
 // zero additions); in the scan each channel's int32 dot product with its ternary weight
 // row is v_dot4 instructions, and the dequantisation s_dt acc max(m, 1e-5) / 127 is fp32
 // (the value never reaches memory: two roundings where a stored BitLinear output has one).
+#include <mutex>
 #include <type_traits>
 
 #include "launch.hpp"
@@ -503,6 +504,31 @@ size_t scan_m1_workspace(const ScanArgs& a) {
 hipError_t launch_scan_m1(const ScanArgs& a, void* ws, hipStream_t s) {
   if (a.batch == 0 || a.L == 0) return hipSuccess;
   return a.act_bf16 ? launch_m1_n<bf16_t>(a, ws, s) : launch_m1_n<float>(a, ws, s);
+}
+
+// ---- the library's own scratch memory, for callers that cannot allocate (static_scratch)
+// One array per GPU, held until the process ends.  Its name is a host-side stand-in in host
+// code: the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int d = 0;
+  hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) return e;
+  if (d < 0 || d >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[d]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[d] = p;
+  }
+  *ptr = g_scratch_ptr[d];
+  return hipSuccess;
 }
 
 }  // namespace ssm
