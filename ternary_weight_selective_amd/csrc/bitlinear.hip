@@ -134,14 +134,28 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 // Tile order: blocks are dealt to the 8 XCDs round-robin, so block b works on tile
 // (b mod 8) * ceil(T / 8) + b / 8: each XCD takes a contiguous run of tiles (outputs
 // fastest) and its L2 serves the activation rows of few token tiles.
+constexpr int kBigStages = 4;  // LDS stages of k_gemm_i8_big (ST - 1 k steps in flight)
+
+// Wait until at most N vector-memory operations of this wave are outstanding (vmcnt only).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <typename Tout, int BN, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_i8_big(GemmArgs a) {
-  constexpr int BMT = 256, BKT = 64, AS = BKT + 16;
+  constexpr int BMT = 256, BKT = 64, ST = kBigStages;
   constexpr int WN = BN / 2, NT = WN / 16, MT = 8;
-  constexpr int CPT = BMT * 4 / 256;   // activation chunks (16 bytes) per thread and k step
-  constexpr int WPT = BN * 4 / 256;    // packed weight words per thread and k step
-  __shared__ __align__(16) int8_t s_a[2][BMT * AS];
-  __shared__ __align__(16) int8_t s_w[2][BN * AS];
+  constexpr int ABYTES = BMT * BKT, WWORDS = BN * 4;
+  constexpr int AL = BMT / 16 / 4;      // 16-row activation loads per wave and stage
+  constexpr int WL = WWORDS / 64 / 4;   // 64-word weight loads per wave and stage
+  constexpr int L = AL + WL;            // loads per wave and stage
+  // one LDS array for both operands (with two the compiler makes every LDS read wait for
+  // all loads in flight)
+  __shared__ __align__(16) int8_t smem[ST * (ABYTES + WWORDS * 4)];
+  int8_t* const s_a = smem;
+  uint32_t* const s_w = (uint32_t*)(smem + ST * ABYTES);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -151,103 +165,161 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t li = blockIdx.x / 8, t = (blockIdx.x % 8) * chunk + li;
   if (li >= chunk || t >= T) return;
   const int64_t m0 = (t / nb) * BMT, n0 = (t % nb) * BN;
-  const int8_t* A = (const int8_t*)a.A;
-  v4i pa[CPT];
-  uint32_t pw[WPT];
-  auto load = [&](int64_t k0) {
+  const int nk = (int)(a.Kp / BKT);
+  // activation scales of the lane's rows, loaded now for the epilogue
+  float amx[MT];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int e = tid + 256 * c, r = e >> 2, q = e & 3;
-      const int64_t gm = m0 + r;
-      pa[c] = gm < a.M ? *(const v4i*)(A + gm * a.lda + k0 + q * 16) : v4i{0, 0, 0, 0};
-    }
+  for (int i = 0; i < MT; ++i) {
+    const int64_t m = m0 + wm * 128 + i * 16 + l16;
+    amx[i] = a.absmax[m < a.M ? m : a.M - 1];
+  }
+  // Operands go from global memory straight into LDS (each lane's 16 or 4 bytes land at
+  // lane * size past the wave's LDS base), ST - 1 steps ahead of the MFMAs.  Rows past the
+  // end are clamped to the last row (their results are never stored) and weight words past a
+  // row's end to its last word (they meet the zero padding of the activations), so every wave
+  // issues the same L loads per step and the wait for the oldest step is a constant count.
+  // Activation rows are stored as four 16-byte chunks in the order q ^ ((row / 2) mod 4).
+  const int8_t* ag[AL];
 #pragma unroll
-    for (int c = 0; c < WPT; ++c) {
-      const int e = tid + 256 * c, r = e >> 2, q = e & 3;
-      const int64_t gn = n0 + r, kw = k0 / 16 + q;
-      pw[c] = (gn < a.N && kw < a.w_row_words) ? a.W[gn * a.w_row_words + kw] : 0u;
-    }
-  };
-  auto store = [&](int buf) {
+  for (int c = 0; c < AL; ++c) {
+    const int r = wave * (BMT / 4) + c * 16 + (lane >> 2);
+    const int64_t gm = m0 + r < a.M ? m0 + r : a.M - 1;
+    ag[c] = (const int8_t*)a.A + gm * a.lda + (((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+  }
+  const uint32_t* wg[WL];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int e = tid + 256 * c, r = e >> 2, q = e & 3;
-      *(v4i*)(&s_a[buf][r * AS + q * 16]) = pa[c];
-    }
+  for (int c = 0; c < WL; ++c) {
+    const int e = (wave * WL + c) * 64 + lane;
+    const int64_t gn = n0 + (e >> 2) < a.N ? n0 + (e >> 2) : a.N - 1;
+    wg[c] = a.W + gn * a.w_row_words;
+  }
+  const int wq = lane & 3;
+  const int64_t wlast = a.w_row_words - 1;
+  auto issue = [&](int ks, int8_t* __restrict__ da, uint32_t* __restrict__ dw) {
+    const int k = ks < nk ? ks : nk - 1;
 #pragma unroll
-    for (int c = 0; c < WPT; ++c) {
-      const int e = tid + 256 * c, r = e >> 2, q = e & 3;
-      *(v4i*)(&s_w[buf][r * AS + q * 16]) = unpack16_i8(pw[c]);
-    }
+    for (int c = 0; c < AL; ++c)
+      __builtin_amdgcn_global_load_lds((const void*)(ag[c] + (int64_t)k * BKT),
+                                       (__attribute__((address_space(3))) void*)(da + (wave * (BMT / 4) + c * 16) * BKT),
+                                       16, 0, 0);
+    const int64_t kw = (int64_t)k * 4 + wq;
+#pragma unroll
+    for (int c = 0; c < WL; ++c)
+      __builtin_amdgcn_global_load_lds((const void*)(wg[c] + (kw < wlast ? kw : wlast)),
+                                       (__attribute__((address_space(3))) void*)(dw + (wave * WL + c) * 64),
+                                       4, 0, 0);
   };
   v4i acc[MT][NT];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-  const int nk = (int)(a.Kp / BKT);
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) load((int64_t)(ks + 1) * BKT);
-    // all operand fragments of the step first (one LDS wait), then its MFMAs
+  const int aoff = (wm * 128 + l16) * BKT + ((kq ^ ((l16 >> 1) & 3)) << 4);
+  const int woff = (wn * WN + l16) * 4 + kq;
+  // The prologue fills stages 0 .. ST - 2 and waits for them; from then on iteration ks issues
+  // the loads of k step ks + ST - 1 and contracts step ks.  The loads and the LDS reads of one
+  // iteration go through separate restrict-qualified slot pointers (they never touch the same
+  // slot), which lets the reads start without waiting for the loads in flight.
+#pragma unroll
+  for (int st = 0; st < ST - 1; ++st) issue(st, s_a + st * ABYTES, s_w + st * WWORDS);
+  vm_wait<0>();
+  auto iter = [&](int ks, const int8_t* __restrict__ ra, const uint32_t* __restrict__ rw,
+                  int8_t* __restrict__ da, uint32_t* __restrict__ dw) {
+    issue(ks + ST - 1, da, dw);
+    uint32_t wpk[NT];
     v4i wf[NT], bfr[MT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) wf[j] = *(const v4i*)(&s_w[buf][(wn * WN + j * 16 + l16) * AS + kq * 16]);
+    for (int j = 0; j < NT; ++j) wpk[j] = rw[woff + j * 64];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) bfr[i] = *(const v4i*)(&s_a[buf][(wm * 128 + i * 16 + l16) * AS + kq * 16]);
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs (the scheduler sinks them)
+    for (int i = 0; i < MT; ++i) bfr[i] = *(const v4i*)(ra + aoff + i * 16 * BKT);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int j = 0; j < NT; ++j) wf[j] = unpack16_i8(wpk[j]);
+    if constexpr (BN == 256) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[j], bfr[i], acc[i][j], 0, 0, 0);
-    if (ks + 1 < nk) store(buf ^ 1);
-    __syncthreads();
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[j], bfr[i], acc[i][j], 0, 0, 0);
+  };
+  // this wave's loads of step ks are done once at most (ST - 2) * L of its loads are in flight;
+  // the barrier makes every wave's loads of step ks visible and retires step ks - 1's reads of
+  // the slot about to be refilled.  (The two loop forms differ only in how the register
+  // allocator treats them: each keeps its accumulators in place, without copies.)
+  auto step = [&](int ks) {
+    vm_wait<(ST - 2) * L>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int rs = ks % ST, ws = (ks + ST - 1) % ST;
+    iter(ks, s_a + rs * ABYTES, s_w + rs * WWORDS, s_a + ws * ABYTES, s_w + ws * WWORDS);
+  };
+  if constexpr (BN == 256) {
+    for (int ks = 0; ks < nk; ++ks) step(ks);
+  } else {
+    int ks = 0;
+    do step(ks); while (++ks < nk);
   }
 
   // epilogue: lane holds token l16 of each token tile and outputs 4 kq .. 4 kq + 3 of each
-  // output tile
+  // output tile.  Every global load of a row (its activation scale, bias, residual) is issued
+  // before the row's first use, so the row waits for memory once.
   const double sw = (double)a.w_scale[0];
   const int vb = (int)sizeof(typename Vec4<Tout>::type);
   const bool vec_ok = (a.ldy % 4 == 0) && (((uintptr_t)a.y) % vb == 0) &&
-                      (!a.bias || ((uintptr_t)a.bias) % 16 == 0);
+                      (!a.bias || ((uintptr_t)a.bias) % 16 == 0) &&
+                      (!a.residual || (a.ld_res % 4 == 0 && ((uintptr_t)a.residual) % vb == 0));
+  double deq[MT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int64_t m = m0 + wm * 128 + i * 16 + l16;
-    if (m >= a.M) continue;
-    const double deq = (double)fmaxf(a.absmax[m], 1e-5f) / 127.0;
+  for (int i = 0; i < MT; ++i) deq[i] = (double)fmaxf(amx[i], 1e-5f) / 127.0;
+  if (vec_ok && n0 + BN <= a.N) {
+    float4 bb[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int64_t n = n0 + wn * WN + j * 16 + kq * 4;
-      if (n >= a.N) continue;
-      double y[4];
+    for (int j = 0; j < NT; ++j)
+      bb[j] = a.bias ? *(const float4*)(a.bias + n0 + wn * WN + j * 16 + kq * 4) : float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) y[q] = (sw * (double)acc[i][j][q]) * deq;
-      if (vec_ok && n + 3 < a.N) {
-        if (a.bias) {
-          const float4 bb = *(const float4*)(a.bias + n);
-          y[0] += bb.x; y[1] += bb.y; y[2] += bb.z; y[3] += bb.w;
-        }
+    for (int i = 0; i < MT; ++i) {
+      const int64_t m = m0 + wm * 128 + i * 16 + l16;
+      if (m >= a.M) continue;
+      typename Vec4<Tout>::type res[NT];
+      if (a.residual) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          res[j] = *(const typename Vec4<Tout>::type*)((const Tout*)a.residual + m * a.ld_res + n0 + wn * WN + j * 16 + kq * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int64_t n = n0 + wn * WN + j * 16 + kq * 4;
+        double y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[q] = (sw * (double)acc[i][j][q]) * deq[i];
+        if (a.bias) { y[0] += bb[j].x; y[1] += bb[j].y; y[2] += bb[j].z; y[3] += bb[j].w; }
         if (a.residual) {
-          const Tout* rp = (const Tout*)a.residual + m * a.ld_res + n;
+          const Tout* rv = (const Tout*)&res[j];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) y[q] += (double)ld_act(rp + q);
+          for (int q = 0; q < 4; ++q) y[q] += (double)ld_act(rv + q);
         }
         Tout o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) st_act(&o[q], (float)y[q]);
         *(typename Vec4<Tout>::type*)((Tout*)a.y + m * a.ldy + n) = *(const typename Vec4<Tout>::type*)o;
-      } else {
+        if (DBG)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (n + q < a.N) store_out<Tout>(a, m, n + q, y[q]);
+          for (int q = 0; q < 4; ++q) a.dbg_acc[m * a.N + n + q] = acc[i][j][q];
       }
-      if (DBG)
+    }
+    return;
+  }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (n + q < a.N) a.dbg_acc[m * a.N + n + q] = acc[i][j][q];
+  for (int i = 0; i < MT; ++i) {
+    const int64_t m = m0 + wm * 128 + i * 16 + l16;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t n = n0 + wn * WN + j * 16 + kq * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (n + q >= a.N) continue;
+        store_out<Tout>(a, m, n + q, (sw * (double)acc[i][j][q]) * deq[i]);
+        if (DBG) a.dbg_acc[m * a.N + n + q] = acc[i][j][q];
+      }
     }
   }
 }
@@ -849,6 +921,7 @@ static void launch_big(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_i8(const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (a.Kp < 64 || a.Kp % 64 != 0) return hipErrorInvalidValue;
   if (a.group == 0) {
     const bool d = a.dbg_acc != nullptr;
     if (a.y_bf16) { if (d) launch_big<bf16_t, true>(a, s); else launch_big<bf16_t, false>(a, s); }
