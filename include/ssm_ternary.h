@@ -481,7 +481,10 @@ ssm_status ssm_selective_scan_bwd(const ssm_scan_bwd_args* a, void* workspace, s
  *   d_scale = sum over each scale's weights of dW (q - W/s) where |W/s| <= 1, dW q elsewhere
  *   (learnable scales, Ternary Mamba abstract; the learned-step-size rule).
  * All fp32 except x (act dtype).  The forward's codes are rebuilt from x exactly as the
- * forward computes them.  The two contractions are dense fp32 GEMMs on rocBLAS.
+ * forward computes them.  Both contractions run on the library's own matrix-core kernels:
+ * with one scale per tensor dx̂ multiplies dy by the bf16 codes (the RMSNorm backward fused
+ * into its epilogue) when k <= 1024, otherwise (and with grouped scales) dy W̃ is a dense fp32
+ * product; dW multiplies dy by the activation codes over token chunks.
  *  x [m, ldx] (first k columns), norm_weight [k] or NULL, w_packed / w_scale / group_size as
  *  ssm_ternary_quantize_weights wrote them, w_latent [n_out, k] (for d_scale), dy [m, ld_dy],
  *  dx [m, ld_dx] (written), dw [n_out, k] or NULL, d_scale [1] or [n_out, k/group] or NULL.
@@ -523,12 +526,12 @@ ssm_status ssm_qat_sgd_step(float* w_latent, float* w_scale, const float* dw, co
 /*
  * ssm_dense_fwd -- a full-precision linear layer, y = x W^T (+ residual): the in and out
  * projections of the TriSSM model, and every projection of its fp_ssm baseline (TriSSM
- * README).  No RMSNorm, no quantisation, no bias.  A plain dense GEMM, delegated to rocBLAS
- * (fp32; or bf16 operands with fp32 accumulation and a bf16 result).
+ * README).  No RMSNorm, no quantisation, no bias.  A plain dense GEMM on the library's own
+ * matrix-core kernel: fp32 operands on fp32 MFMA, or bf16 operands on bf16 MFMA, fp32
+ * accumulation, the residual added in fp32, one rounding to dtype.
  *  x: [m, ldx] of dtype (first k columns);  w: [n, k] of dtype, row-major;
  *  residual: [m, ld_res] of dtype or NULL (may equal y);  y: [m, ldy] of dtype, not x.
- * The first call on a device creates that device's rocBLAS handle (rocBLAS then sets up its
- * own workspace); nothing else is allocated.  Asynchronous on stream.
+ * Allocates nothing and keeps no state; asynchronous on stream.
  * Errors: SSM_ERR_DTYPE, SSM_ERR_SHAPE (sizes, strides, sizes of 2^31 or more, y == x),
  * SSM_ERR_NULL, SSM_ERR_DEVICE.
  */

@@ -113,7 +113,7 @@ struct ConvArgs {
 constexpr int kConvMaxK = 8;
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t s);
 
-// ---- full-precision linear layer (dense.cpp, rocBLAS): y[M, N] = x[M, K] W[N, K]^T (+ residual)
+// ---- full-precision linear layer (dense.hip): y[M, N] = x[M, K] W[N, K]^T (+ residual)
 struct DenseArgs {
   int64_t M, N, K;
   int bf16;                      // activations and weights bf16 (else fp32)
@@ -123,9 +123,9 @@ struct DenseArgs {
   void* y; int64_t ldy;
 };
 hipError_t launch_dense(const DenseArgs& a, hipStream_t s);
-// row-major fp32 C[M, N] = op(A) op(B) (op: transposed when the flag is set), C overwritten
-hipError_t sgemm_rm(bool ta, bool tb, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                    const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t s);
+// row-major fp32 C[M, N] = A[M, K] B[K, N], C overwritten
+hipError_t sgemm_nn(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                    float* C, int64_t ldc, hipStream_t s);
 
 // ---- straight-through-estimator backward of BitLinear and the QAT update (ste.hip)
 struct SteArgs {

@@ -5,7 +5,7 @@
 // roundings: dx̂ = dy W̃ with W̃ = s q (the ternary codes times their scale), dW = dy^T x̃ with
 // x̃ the forward's int8 codes dequantised, then the RMSNorm backward.  With one scale per tensor
 // dx comes from k_ste_dx (the codes on the matrix cores, the RMSNorm backward in its epilogue);
-// with grouped scales dx̂ is a dense fp32 GEMM (rocBLAS, dense.cpp) followed by k_rms_bwd.  dW
+// with grouped scales (or k > 1024) dx̂ is a dense fp32 GEMM (sgemm_nn) followed by k_rms_bwd.  dW
 // comes from k_ste_dw (the activation codes on the matrix cores, split over token chunks).  The
 // other kernels here rebuild the forward's codes and the transposed weight codes, and take the
 // scale gradient.
@@ -660,7 +660,7 @@ hipError_t launch_ste_bwd_add(const SteArgs& a, const float* add, int64_t ld_add
                        a.w_row_words, a.scale, a.group, wt);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // dx̂ [M, K] = dy [M, N] W̃ [N, K]
-    e = sgemm_rm(false, false, a.M, a.K, a.N, a.dy, a.ld_dy, wt, a.K, dxh, a.K, s);
+    e = sgemm_nn(a.M, a.K, a.N, a.dy, a.ld_dy, wt, a.K, dxh, a.K, s);
     if (e != hipSuccess) return e;
     e = a.x_bf16 ? launch_rms_bwd_k<bf16_t>(a, rs, dxh, add, ld_add, s)
                  : launch_rms_bwd_k<float>(a, rs, dxh, add, ld_add, s);
