@@ -965,16 +965,29 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
 }  // namespace ssm
 
 namespace ssm {
-// Persistent grid: one block of 8 waves per compute unit is enough to keep both roles busy.
+// Persistent grid: as many blocks of 8 waves as fit on every compute unit at once (two where
+// registers and LDS allow, which doubles the loads in flight), never more than row blocks.
 // Results do not depend on it (every row is computed the same way by whichever block owns it).
-constexpr int64_t kRowsGrid = 256;
+template <typename K>
+static int64_t rows_grid(K kernel) {
+  int dev = 0, ncu = 256, occ = 1;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1) ncu = 256;
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 512, 0) != hipSuccess || occ < 1) occ = 1;
+  return (int64_t)ncu * (occ < 2 ? occ : 2);
+}
 
 template <typename Tin, typename Tout, int KPL>
 static void launch_rows_t(const GemmArgs& g, const RowArgs& r, hipStream_t s) {
   const int64_t nrb = cdiv(g.M, kRowsBR);
-  const dim3 grid((unsigned)(nrb < kRowsGrid ? nrb : kRowsGrid)), block(512);
   const bool dbg = g.dbg_acc || r.dbg_xq || r.dbg_absmax;
-#define SSM_ROWS(RES, DBG) hipLaunchKernelGGL((k_bl_rows<Tin, Tout, KPL, RES, DBG>), grid, block, 0, s, g, r)
+#define SSM_ROWS(RES, DBG)                                                                  \
+  do {                                                                                      \
+    static const int64_t cap = rows_grid(k_bl_rows<Tin, Tout, KPL, RES, DBG>);              \
+    const dim3 grid((unsigned)(nrb < cap ? nrb : cap)), block(512);                         \
+    hipLaunchKernelGGL((k_bl_rows<Tin, Tout, KPL, RES, DBG>), grid, block, 0, s, g, r);     \
+  } while (0)
   if (g.residual) { if (dbg) SSM_ROWS(true, true); else SSM_ROWS(true, false); }
   else { if (dbg) SSM_ROWS(false, true); else SSM_ROWS(false, false); }
 #undef SSM_ROWS
