@@ -693,6 +693,24 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     void* x = c->gated ? base + p.off_xc : xz;         // the SSM input
     void* pp = base + p.off_p;
     void* y = base + p.off_y;
+    // one decoding step on kernels of its own (spread over the chip rather than one row block)
+    if (state && seqlen == 1 && !dbg && !c->gated && !c->fp_proj && c->act_bits == 8 && c->group_size == 0 &&
+        batch <= 1024 && aligned(w->w_in, 16) && aligned(w->w_x, 16) && aligned(w->w_out, 16) &&
+        aligned(w->A, 16) && aligned(state, 16) &&
+        decode_supported((int)c->d_model, (int)c->d_inner, (int)c->d_state, (int)c->dt_rank, (int)p.PW)) {
+      DecodeArgs da{};
+      da.B = batch; da.Dm = (int)c->d_model; da.Di = (int)c->d_inner; da.NS = (int)c->d_state;
+      da.R = (int)c->dt_rank; da.PW = (int)p.PW; da.act_bf16 = c->act_dtype == SSM_BF16;
+      da.u = u; da.out = out; da.add_residual = add_residual ? 1 : 0;
+      da.w_in = (const uint32_t*)w->w_in; da.s_in = w->s_in; da.g_in = w->g_in;
+      da.w_x = (const uint32_t*)w->w_x; da.s_x = w->s_x; da.g_x = w->g_x;
+      da.w_dt = (const uint32_t*)w->w_dt; da.w_dt_row_words = cdiv(c->dt_rank, 16); da.s_dt = w->s_dt;
+      da.g_dt = w->g_dt;
+      da.dt_bias = w->dt_bias; da.A = w->A; da.D = w->D;
+      da.w_out = (const uint32_t*)w->w_out; da.s_out = w->s_out; da.g_out = w->g_out;
+      da.eps = c->norm_eps; da.state = state; da.x = base + p.off_x;
+      return dev(launch_decode_m1(da, stream), "mixer decode step");
+    }
     const bool front = !c->gated && !c->fp_proj &&
                        front_supported((int)c->d_model, (int)c->d_inner, (int)p.PW, (int)c->dt_rank);
     ssm_scan_args sa{};

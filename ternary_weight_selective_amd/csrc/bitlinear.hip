@@ -470,9 +470,6 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
 // unchanged.
 namespace {
 
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
 
 // Block barrier that orders LDS accesses only (outstanding global loads and stores of the
 // waves are not waited for).

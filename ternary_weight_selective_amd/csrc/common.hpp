@@ -86,6 +86,85 @@ __device__ __forceinline__ float wave_absmax(float m) {
   return __uint_as_float(u);
 }
 
+// Correctly rounded fp32 square root.  The device's fp32 sqrt instruction sequence is not
+// correctly rounded (it is off by one ulp on some inputs); a correctly rounded fp64 square
+// root rounded once to fp32 is, because 53 >= 2 * 24 + 2 bits make the double rounding
+// innocuous for square roots.
+__device__ __forceinline__ float sqrt_rn(float x) { return (float)__dsqrt_rn((double)x); }
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// softplus(v) = log(1 + e^v), the identity above 20.  With z = e^v and u = fl(1 + z), the
+// rounding error of u is c = (u - 1) - z (both subtractions exact), and
+// log(1 + z) = log(u) - c / u + O(c^2).  While u < 2, |c| <= 2^-24 and taking c for c / u
+// changes the result by at most |c| z / (1 + z), below its own rounding.  From u = 2 on, c
+// can reach half an ulp of u, far more than c / u <= 2^-24, which is below the rounding of a
+// result >= log 2: the correction is dropped there.  Below z = 1e-4 the series z - z^2 / 2.
+// Branch-free, on the hardware exp2 and log2 (no reciprocal).
+__device__ __forceinline__ float softplus_f(float v) {
+  const float z = __builtin_amdgcn_exp2f(v * LOG2E);
+  const float u = 1.0f + z;
+  const float c = u < 2.0f ? (u - 1.0f) - z : 0.0f;
+  const float big = 0.69314718055994531f * __builtin_amdgcn_logf(u) - c;
+  const float small = z * __builtin_fmaf(-0.5f, z, 1.0f);
+  const float r = z < 1e-4f ? small : big;
+  return v > 20.0f ? v : r;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// RMSNorm + absmax int8 codes of RPW rows of K values held in the canonical lane layout (lane
+// j holds columns j + 64 i, zero past K): the lane partials, the wave butterfly, the scalar
+// tail once for the RPW rows (lane j takes row j mod RPW), codes into sq (row stride qs) and
+// max(absmax, 1e-5) / 127 into sdeq.  gn: the gain per lane column (1 when absent).
+template <int RPW, int KPL>
+__device__ __forceinline__ void norm_quant_rows(float (&v)[RPW][KPL], const float (&gn)[KPL], int K, float eps,
+                                                int8_t* sq, int qs, double* sdeq, int lane) {
+  float ss[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) s = __builtin_fmaf(v[rr][i], v[rr][i], s);
+    ss[rr] = wave_sum_butterfly(s);
+  }
+  float sel = ss[0];
+#pragma unroll
+  for (int rr = 1; rr < RPW; ++rr) sel = (lane % RPW) == rr ? ss[rr] : sel;
+  const float rs_l = __fdiv_rn(1.0f, sqrt_rn(__fdiv_rn(sel, (float)K) + eps));
+  float mx[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const float rs = readlane_f(rs_l, rr);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const float t = (v[rr][i] * rs) * gn[i];
+      v[rr][i] = t;
+      m = fmaxf(m, fabsf(t));
+    }
+    mx[rr] = wave_absmax(m);
+  }
+  float msel = mx[0];
+#pragma unroll
+  for (int rr = 1; rr < RPW; ++rr) msel = (lane % RPW) == rr ? mx[rr] : msel;
+  const float mf = fmaxf(msel, 1e-5f);
+  const float sigma_l = __fdiv_rn(127.0f, mf);
+  if (lane < RPW) sdeq[lane] = (double)mf / 127.0;
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const float sigma = readlane_f(sigma_l, rr);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      float q = rintf(v[rr][i] * sigma);
+      q = fminf(fmaxf(q, -128.0f), 127.0f);
+      sq[rr * qs + lane + 64 * i] = (int8_t)(int)q;
+    }
+  }
+}
+
 // 16 ternary codes of one packed word -> 16 int8 in weight order.  Dword j of the
 // result holds weights 4j..4j+3; their 2-bit codes sit at bits 2j of bytes 0..3, so a
 // shift and mask leave one code per byte and a byte permute maps code 0/1/3 to
@@ -126,11 +205,6 @@ __device__ __forceinline__ uint32_t tern2_to_bf16x2(uint32_t b) {
   return vlo | (vhi << 16);
 }
 
-// Correctly rounded fp32 square root.  The device's fp32 sqrt instruction sequence is not
-// correctly rounded (it is off by one ulp on some inputs); a correctly rounded fp64 square
-// root rounded once to fp32 is, because 53 >= 2 * 24 + 2 bits make the double rounding
-// innocuous for square roots.
-__device__ __forceinline__ float sqrt_rn(float x) { return (float)__dsqrt_rn((double)x); }
 
 __host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }

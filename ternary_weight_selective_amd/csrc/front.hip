@@ -23,9 +23,6 @@ namespace {
 constexpr int FBR = 16;     // token rows per row block
 constexpr int FRMAX = 64;   // widest dr
 
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
 
 // Block barrier ordering LDS only (outstanding global loads and stores are not waited for).
 __device__ __forceinline__ void bar_lds() {
@@ -38,55 +35,6 @@ template <typename T> struct V4;
 template <> struct V4<float> { typedef float4 type; };
 template <> struct V4<bf16_t> { typedef uint2 type; };
 
-// RMSNorm + absmax int8 codes of RPW rows of K values held in the canonical lane layout (lane
-// j holds columns j + 64 i, zero past K): the lane partials, the wave butterfly, the scalar
-// tail once for the RPW rows (lane j takes row j mod RPW), codes into sq (row stride qs) and
-// max(absmax, 1e-5) / 127 into sdeq.  gn: the gain per lane column (1 when absent).
-template <int RPW, int KPL>
-__device__ __forceinline__ void norm_quant_rows(float (&v)[RPW][KPL], const float (&gn)[KPL], int K, float eps,
-                                                int8_t* sq, int qs, double* sdeq, int lane) {
-  float ss[RPW];
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) s = __builtin_fmaf(v[rr][i], v[rr][i], s);
-    ss[rr] = wave_sum_butterfly(s);
-  }
-  float sel = ss[0];
-#pragma unroll
-  for (int rr = 1; rr < RPW; ++rr) sel = (lane % RPW) == rr ? ss[rr] : sel;
-  const float rs_l = __fdiv_rn(1.0f, sqrt_rn(__fdiv_rn(sel, (float)K) + eps));
-  float mx[RPW];
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    const float rs = readlane_f(rs_l, rr);
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const float t = (v[rr][i] * rs) * gn[i];
-      v[rr][i] = t;
-      m = fmaxf(m, fabsf(t));
-    }
-    mx[rr] = wave_absmax(m);
-  }
-  float msel = mx[0];
-#pragma unroll
-  for (int rr = 1; rr < RPW; ++rr) msel = (lane % RPW) == rr ? mx[rr] : msel;
-  const float mf = fmaxf(msel, 1e-5f);
-  const float sigma_l = __fdiv_rn(127.0f, mf);
-  if (lane < RPW) sdeq[lane] = (double)mf / 127.0;
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    const float sigma = readlane_f(sigma_l, rr);
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      float q = rintf(v[rr][i] * sigma);
-      q = fminf(fmaxf(q, -128.0f), 127.0f);
-      sq[rr * qs + lane + 64 * i] = (int8_t)(int)q;
-    }
-  }
-}
 }  // namespace
 
 template <typename T, int KPL1, int KPL2>

@@ -35,25 +35,7 @@
 namespace ssm {
 
 namespace {
-constexpr float LOG2E = 1.4426950408889634f;
 constexpr int RMAX = 64;
-
-// softplus(v) = log(1 + e^v), the identity above 20.  With z = e^v and u = fl(1 + z), the
-// rounding error of u is c = (u - 1) - z (both subtractions exact), and
-// log(1 + z) = log(u) - c / u + O(c^2).  While u < 2, |c| <= 2^-24 and taking c for c / u
-// changes the result by at most |c| z / (1 + z), below its own rounding.  From u = 2 on, c
-// can reach half an ulp of u, far more than c / u <= 2^-24, which is below the rounding of a
-// result >= log 2: the correction is dropped there.  Below z = 1e-4 the series z - z^2 / 2.
-// Branch-free, on the hardware exp2 and log2 (no reciprocal).
-__device__ __forceinline__ float softplus_f(float v) {
-  const float z = __builtin_amdgcn_exp2f(v * LOG2E);
-  const float u = 1.0f + z;
-  const float c = u < 2.0f ? (u - 1.0f) - z : 0.0f;
-  const float big = 0.69314718055994531f * __builtin_amdgcn_logf(u) - c;
-  const float small = z * __builtin_fmaf(-0.5f, z, 1.0f);
-  const float r = z < 1e-4f ? small : big;
-  return v > 20.0f ? v : r;
-}
 
 struct ChunkArgs {
   int64_t chunk_len;  // time steps per chunk (a multiple of the tile length)

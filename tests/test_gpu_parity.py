@@ -587,6 +587,30 @@ def test_mixer_decode_step(name, over, seed):
     assert bool(torch.isfinite(state).all()) and float(state.abs().max()) > 0
 
 
+DECODE_EXACT_CASES = [  # configurations the decode step runs on its own kernels
+    ("trissm", dict(batch=4, seqlen=12, layers=1), 21),
+    ("trissm", dict(batch=17, seqlen=5, layers=1), 22),     # two 16-row groups, the second ragged
+    ("ternaryssm50m", dict(batch=3, seqlen=6, layers=1), 23),  # bf16, d_inner 1024, dt_rank 32
+    ("bitssm_tiny", {}, 24),
+]
+
+
+@pytest.mark.parametrize("name,over,seed", DECODE_EXACT_CASES)
+def test_mixer_decode_step_equals_prefill(name, over, seed):
+    """The decode step's kernels evaluate every quantity as the whole-sequence path does (same
+    norms, codes, int32 sums, fp64 epilogues, dt dequantisation and state recurrence), so the
+    token-by-token outputs equal the prefill's bit for bit."""
+    cfg = wl.CONFIGS[name].with_(**over)
+    lat, u = wl.mixer_problem(cfg, seed=seed, layers=1)
+    if cfg.act_dtype == "bf16":
+        u = bf16_values(u)
+    gw, _ = quantize_layer(cfg, lat[0])
+    out, state = _decode(cfg, gw, u)
+    full = host(run_gpu_stack(cfg, [gw], u))
+    np.testing.assert_array_equal(host(out), full)
+    assert bool(torch.isfinite(state).all())
+
+
 # ------------------------------------------------------------------ gated block
 
 def _ulp_diff(got, ref, bf16: bool):
