@@ -59,7 +59,7 @@ KERNEL_SOURCES = {  # source files whose text defines each timed kernel (for sta
     "ssd": ["ssd.hip", "common.hpp", "launch.hpp"],
     "bitlinear": ["norm.hip", "bitlinear.hip", "common.hpp", "launch.hpp"],
     "conv": ["conv.hip", "common.hpp", "launch.hpp"],
-    "dense": ["dense.cpp", "launch.hpp"],
+    "dense": ["dense.hip", "launch.hpp"],
 }
 
 
