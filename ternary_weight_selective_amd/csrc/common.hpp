@@ -35,6 +35,14 @@ template <typename T> __device__ __forceinline__ void st_act(T* p, float v);
 template <> __device__ __forceinline__ void st_act<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st_act<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// Block barrier ordering LDS only: global loads still in flight are not waited for (for
+// phases that exchange data through LDS alone).
+__device__ __forceinline__ void bar_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // SiLU of the gate branch, fp32: z / (1 + 2^(-z log2 e)) with the hardware exp2 (an infinite
 // exponential for very negative z gives -0).
 __device__ __forceinline__ float silu_gate(float z) {

@@ -20,13 +20,6 @@
 namespace ssm {
 
 namespace {
-// Block barrier ordering LDS only: global loads still in flight are not waited for (the
-// phases exchange data through LDS alone).
-__device__ __forceinline__ void bar_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // One 64-lane wave: RMSNorm + absmax codes of the single row held in LDS (K = 64 KPL
 // values), the canonical lane layout, codes into sq and the factor into *sdeq.

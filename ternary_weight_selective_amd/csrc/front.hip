@@ -24,13 +24,6 @@ constexpr int FBR = 16;     // token rows per row block
 constexpr int FRMAX = 64;   // widest dr
 
 
-// Block barrier ordering LDS only (outstanding global loads and stores are not waited for).
-__device__ __forceinline__ void bar_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 template <typename T> struct V4;
 template <> struct V4<float> { typedef float4 type; };
 template <> struct V4<bf16_t> { typedef uint2 type; };

@@ -161,19 +161,61 @@ struct SsdSeg {
   float* sdec;        // [B, S-1, H]: log2 of each segment's decay, sum of dt A log2 e
 };
 
-// v (fp32) as two bf16 terms: hi = v truncated, lo = (v - hi) truncated.
-__device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
-  hi = __float_as_uint(v) & 0xFFFF0000u;
-  lo = __float_as_uint(v - __uint_as_float(hi)) & 0xFFFF0000u;
+// bf16 pair (a in the low half, b in the high half): the upper 16 bits of each fp32 pattern
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+// fp32 values a, b as two bf16 terms each, packed in pairs: hi = the values truncated to bf16,
+// lo = the remainders v - hi truncated to bf16.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  hi = pack_hi(ua, ub);
+  lo = pack_hi(__float_as_uint(a - __uint_as_float(ua & 0xFFFF0000u)),
+               __float_as_uint(b - __uint_as_float(ub & 0xFFFF0000u)));
 }
-// bf16 pair (a in the low half, b in the high half) from two truncated fp32 bit patterns
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | b; }
+// two fp32 values rounded to bf16 (nearest, ties to even), a in the low half
+__device__ __forceinline__ uint32_t cvt_pair(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+// inclusive prefix sum over the 64 lanes of a wave on DPP moves: shifts by 1, 2, 4, 8 inside
+// each row of 16 lanes, then the row totals carried forward (lane 15 into rows 1 and 3, lane
+// 31 into rows 2 and 3)
+__device__ __forceinline__ float dpp_add(float x, float y) { return x + y; }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_mv(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x = dpp_add(x, dpp_mv<0x111, 0xF>(x));  // row_shr:1
+  x = dpp_add(x, dpp_mv<0x112, 0xF>(x));  // row_shr:2
+  x = dpp_add(x, dpp_mv<0x114, 0xF>(x));  // row_shr:4
+  x = dpp_add(x, dpp_mv<0x118, 0xF>(x));  // row_shr:8
+  x = dpp_add(x, dpp_mv<0x142, 0xA>(x));  // row_bcast:15
+  x = dpp_add(x, dpp_mv<0x143, 0xC>(x));  // row_bcast:31
+  return x;
+}
 
 __device__ __forceinline__ v8bf ld8(const uint16_t* p) { return __builtin_bit_cast(v8bf, *(const v4i*)p); }
 // 4 + 4 bf16 from two 8-byte locations
 __device__ __forceinline__ v8bf ld44(const uint16_t* p0, const uint16_t* p1) {
   const uint2 a = *(const uint2*)p0, b = *(const uint2*)p1;
   return __builtin_bit_cast(v8bf, v4i{(int)a.x, (int)a.y, (int)b.x, (int)b.y});
+}
+// A buffer resource over [base, base + bytes): loads past the end read zeros, stores past it
+// are dropped; offsets are 32-bit byte offsets per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutside = 0x80000000u;  // an offset past any resource here
+__device__ __forceinline__ v4i buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st8(uint2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2_t, v), r, off, 0, 0);
 }
 __device__ __forceinline__ v8bf mk8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(v8bf, v4i{(int)a, (int)b, (int)c, (int)d});
@@ -183,23 +225,33 @@ __device__ __forceinline__ v8bf mk8(uint32_t a, uint32_t b, uint32_t c, uint32_t
 template <int NS, bool LOCAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ssd_seg(ScanArgs a, SsdSeg sg) {
   constexpr int Q = kSsdQ, P = kSsdP, HB = kSsdHB, XS = kSsdXS;
-  constexpr int NSP = NS + 8;   // row stride (bf16) of the row-major [t][n] arrays
   constexpr int NT = NS / 16;   // n tiles
   constexpr int NK = NS / 32;   // 32-wide k steps over n
-  __shared__ __align__(16) uint16_t sBr[LOCAL ? 1 : Q * NSP];  // B [s][n]
-  __shared__ __align__(16) uint16_t sC[LOCAL ? 1 : Q * NSP];   // C [t][n]
+  __shared__ __align__(16) uint16_t sBr[LOCAL ? 1 : Q * NS];  // B [s][n]
+  __shared__ __align__(16) uint16_t sC[LOCAL ? 1 : Q * NS];   // C [t][n]
   __shared__ __align__(16) uint16_t sBT[NS * XS];              // B^T [n][s]
   __shared__ __align__(16) uint16_t sXT[HB][P * XS];           // x^T [p][s] per head
   __shared__ __align__(16) float s_cs[HB][Q], s_dt[HB][Q], s_w[HB][Q], s_et[HB][Q];
+  __shared__ __align__(16) float s_b[LOCAL ? 1 : HB][Q];
+  // G^T = B C^T of the chunk (shared by the heads): its 10 tiles on and below the diagonal in
+  // the accumulator layout, tile (t tile jt, s tile ms <= jt) at index jt (jt + 1) / 2 + ms
+  __shared__ __align__(16) float sG[LOCAL ? 1 : 10 * 256];
 
-  // Element (r, c) of the row-major [64][NS] arrays: its 16-byte chunk c / 8 is stored at
-  // position (c / 8) ^ ((r / 16) mod 4), so that 16 lanes writing rows 4 apart, and 16 lanes
-  // reading 16 consecutive rows, each reach distinct banks.
-  auto rm = [](int r, int c) { return r * NSP + ((((c >> 3) ^ ((r >> 4) & 3))) << 3) + (c & 7); };
+  // Element (r, c) of the [64][NS] arrays B and C (bf16 index): panels of 32 columns, each 64
+  // rows of 64 bytes, a row's 16-byte chunk q at position q ^ ((r / 2) mod 4).  A fragment read
+  // (16 consecutive rows, one chunk per group of 16 lanes) then reaches every bank once per
+  // 8 lanes, and its address is a per-lane base plus a constant.
+  auto pm = [](int r, int c) { return (c >> 5) * (Q * 32) + r * 32 + ((((c >> 3) & 3) ^ ((r >> 1) & 3)) << 3) + (c & 7); };
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = w >> 1, ph = w & 1;
   const int kq = lane >> 4, l16 = lane & 15;
+  // per-lane bases of the fragment reads of B and C: pm(16 i + l16, 32 k + 8 kq) = fb + 2048 k +
+  // 512 i; pm(16 i + l16, 32 k + 4 kq) = zb0 + ..., and 16 columns further zb1 + ...
+  const int sw = (l16 >> 1) & 3;
+  const int fb = l16 * 32 + ((kq ^ sw) << 3);
+  const int zb0 = l16 * 32 + (((kq >> 1) ^ sw) << 3) + 4 * (kq & 1);
+  const int zb1 = l16 * 32 + ((((kq >> 1) + 2) ^ sw) << 3) + 4 * (kq & 1);
   const int64_t L = a.L, H = a.H;
   const int64_t nhb = cdiv(H, HB);
   // blocks are dealt to the 8 XCDs round-robin by index: block i takes work item
@@ -248,61 +300,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // B (and C): NS / 8 column groups x 16 step groups; B on threads [0, NBT), C on [NBT, 2 NBT)
   constexpr int NBT = NS / 8 * 16;
   // a set of prefetch registers: one chunk's x, B (or C) and dt (raw bf16).  Every load is
-  // unconditional, from a clamped address, and kept raw: a load whose value is converted or
-  // selected at once makes the compiler wait for all loads in flight right there; the rows past
-  // the sequence's end are zeroed when the chunk is staged.
+  // unconditional and kept raw (a load whose value is converted or selected at once makes the
+  // compiler wait for all loads in flight right there); rows past the sequence's end, and
+  // columns past the last head, read as zeros.
   struct Pre {
     v4i x[4], b[4];
-    bf16_t dt;   // state pass: raw
-    float dtf;   // output pass: converted at the load (its wait then covers the chunk's loads)
+    bf16_t dt;   // raw; converted when the chunk is staged
   };
   // (the step group is the fastest index across lanes, so that the transposed LDS writes of 16
   // lanes fill one row and the next 16 lanes the row 8 below: distinct banks)
   const int xtg = tid & 15, xcg = tid >> 4;
   const bool xv = (int64_t)hb * HB * P + xcg * 8 < H * P;  // the task's columns exist
-  const bool isb = tid < NBT, isc = !LOCAL && tid >= NBT && tid < 2 * NBT;
+  // (NBT is a multiple of 64: which of B and C a thread moves is a per-wave choice, and so are
+  // the row base and stride below)
+  const bool isb = w * 64 < NBT, isc = !LOCAL && !isb && w * 64 < 2 * NBT;
+  static_assert(NBT % 64 == 0, "B and C tasks by whole waves");
   const int btask = isb ? tid : tid - NBT;
   const int btg = btask & 15, bcg = btask >> 4;
-  const bf16_t* xsrc = X + hb * HB * P + (xv ? xcg * 8 : 0);
-  const bf16_t* bsrc = (isc ? Cm : Bm) + bcg * 8;
+  const bf16_t* bbase = isc ? Cm : Bm;
   const int64_t bld = isc ? a.ld_C : a.ld_B;
-  const bf16_t* dsrc = DT + hc;
-  auto load = [&](Pre& pr, int64_t c0) {
-    if constexpr (LOCAL) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t t = c0 + 4 * xtg + u;
-        pr.x[u] = *(const v4i*)(xsrc + (b * L + (t < L ? t : L - 1)) * a.ld_x);
-      }
-      if (isb) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t t = c0 + 4 * btg + u;
-          pr.b[u] = *(const v4i*)(bsrc + (b * L + (t < L ? t : L - 1)) * bld);
-        }
-      }
-      const int64_t td = c0 + lane;
-      pr.dt = dsrc[(b * L + (td < L ? td : L - 1)) * a.ld_delta];
-    } else {
-      // (fewer registers: the output pass's products leave little room)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t t = c0 + 4 * xtg + u;
-        const bool ok = xv && t < L;
-        pr.x[u] = ok ? *(const v4i*)(X + (b * L + t) * a.ld_x + hb * HB * P + xcg * 8) : v4i{0, 0, 0, 0};
-      }
-      if (isb || isc) {
-        const bf16_t* src = isb ? Bm : Cm;
-        const int64_t ld = isb ? a.ld_B : a.ld_C;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t t = c0 + 4 * btg + u;
-          pr.b[u] = t < L ? *(const v4i*)(src + (b * L + t) * ld + bcg * 8) : v4i{0, 0, 0, 0};
-        }
-      }
-      if (ph == 0) pr.dtf = (hv && c0 + lane < L) ? bf16_to_f32(DT[(b * L + c0 + lane) * a.ld_delta + head]) : 0.0f;
+  // Addresses: the chunk's rows as a buffer resource shared by the wave (rows past the
+  // sequence's end read as zeros), plus a 32-bit byte offset per lane (row strides below 2^24
+  // elements, checked at launch).
+  const uint32_t xcol = xcg * 8, bcol = bcg * 8;
+  auto rows_in = [&](int64_t c0) -> uint32_t { return (uint32_t)(L - c0 < Q ? L - c0 : Q); };
+  // part u of a chunk's loads (the parts are issued spread over a chunk's work)
+  auto load_part = [&](Pre& pr, int64_t c0, int u) {
+    const uint32_t rv = rows_in(c0);
+    const auto rx = buf_rsrc(X + (b * L + c0) * a.ld_x + hb * HB * P, rv * (uint32_t)a.ld_x * 2u);
+    pr.x[u] = buf_ld16(rx, xv ? ((uint32_t)(4 * xtg + u) * (uint32_t)a.ld_x + xcol) * 2u : kOutside);
+    if (isb || isc) {
+      const auto rb = buf_rsrc(bbase + (b * L + c0) * bld, rv * (uint32_t)bld * 2u);
+      pr.b[u] = buf_ld16(rb, ((uint32_t)(4 * btg + u) * (uint32_t)bld + bcol) * 2u);
+    }
+    if (u == 0) {
+      const auto rd = buf_rsrc(DT + (b * L + c0) * a.ld_delta + hc, rv * (uint32_t)a.ld_delta * 2u);
+      pr.dt = (bf16_t)__builtin_amdgcn_raw_buffer_load_b16(rd, (uint32_t)lane * (uint32_t)a.ld_delta * 2u, 0, 0);
     }
   };
+  auto load = [&](Pre& pr, int64_t c0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_part(pr, c0, u);
+  };
+
   // transposed 8-byte writes: column u of the 4 step vectors v0..v3 (8 bf16 each)
   auto tcol = [&](const v4i (&v)[4], int u) -> uint2 {
     const int d = u >> 1;
@@ -312,15 +352,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   float cs_end = 0.0f;  // this chunk's cs at its last step (log2 domain), per wave
   auto stage = [&](Pre& pr, int64_t c0) {
-    // rows past the sequence's end (and columns past the last head) staged as zeros (the
-    // output pass loaded zeros there)
-    if constexpr (LOCAL) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (!(xv && c0 + 4 * xtg + u < L)) pr.x[u] = v4i{0, 0, 0, 0};
-        if (c0 + 4 * btg + u >= L) pr.b[u] = v4i{0, 0, 0, 0};
-      }
-    }
     {
       const int hh = xcg >> 3, p0 = (xcg & 7) * 8;
 #pragma unroll
@@ -331,36 +362,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int u = 0; u < 8; ++u) *(uint2*)(&sBT[(bcg * 8 + u) * XS + 4 * btg]) = tcol(pr.b, u);
       if (!LOCAL) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) *(v4i*)(&sBr[rm(4 * btg + u, bcg * 8)]) = pr.b[u];
+        for (int u = 0; u < 4; ++u) *(v4i*)(&sBr[pm(4 * btg + u, bcg * 8)]) = pr.b[u];
       }
     }
     if (!LOCAL && isc) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) *(v4i*)(&sC[rm(4 * btg + u, bcg * 8)]) = pr.b[u];
+      for (int u = 0; u < 4; ++u) *(v4i*)(&sC[pm(4 * btg + u, bcg * 8)]) = pr.b[u];
     }
     // dt = softplus(delta + bias) (0 past the end), cs = inclusive cumsum of dt A log2 e
     // (computed on every lane, then selected: no branch around the use of a loaded value)
-    float dt = 0.0f;
-    if constexpr (LOCAL) {
-      dt = bf16_to_f32(pr.dt) + bias_h;
-      if (a.softplus) dt = softplus_hw(dt);
-      dt = (ph == 0 && hv && c0 + lane < L) ? dt : 0.0f;
-    } else if (ph == 0 && hv && c0 + lane < L) {
-      dt = pr.dtf + bias_h;
-      if (a.softplus) dt = softplus_hw(dt);
-    }
-    float cs = dt * A2;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float o = __shfl_up(cs, d, 64);
-      if (lane >= d) cs += o;
-    }
-    cs_end = __shfl(cs, 63, 64);
+    float dt = bf16_to_f32(pr.dt) + bias_h;
+    if (a.softplus) dt = softplus_hw(dt);
+    dt = (ph == 0 && hv && c0 + lane < L) ? dt : 0.0f;
+    const float cs = wave_prefix_sum(dt * A2);
+    cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), 63));
     if (ph == 0) {
       s_cs[hl][lane] = cs;
       s_dt[hl][lane] = dt;
       s_w[hl][lane] = __builtin_amdgcn_exp2f(cs_end - cs) * dt;
       s_et[hl][lane] = __builtin_amdgcn_exp2f(cs);
+      // decay from step s to the last step of its 16-step tile, times dt_s (at most dt_s: cs
+      // does not increase with dt >= 0 and A <= 0, and in general the two factors of a decay
+      // split at a tile's end have the sign of the whole)
+      if (!LOCAL) s_b[hl][lane] = __builtin_amdgcn_exp2f(__shfl(cs, lane | 15, 64) - cs) * dt;
     }
   };
 
@@ -372,18 +396,33 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t c0 = ch * Q;
     stage(pr, c0);
     __syncthreads();
-    // the loads of chunk ch + DEPTH into the set just staged, in flight through this chunk's
-    // work (the output pass issues them after its outputs, whose products need the registers);
-    // unconditional (past the segment's end they repeat its last chunk, from the cache), so that
-    // the wait for each set counts the loads issued after it exactly
-    if (LOCAL) load(pr, (ch + DEPTH < ch1 ? ch + DEPTH : ch1 - 1) * Q);
-    else if (ch + 1 < ch1) load(pr, c0 + Q);
+    // the loads of chunk ch + DEPTH go into the set just staged, in four parts spread over this
+    // chunk's products (issued at once, 64 KB per block would hold every wave at the address
+    // unit); in the state pass unconditional (past the segment's end they repeat its last chunk,
+    // from the cache), so that the wait for each set counts the loads issued after it exactly
+    const int64_t cn = (ch + DEPTH < ch1 ? ch + DEPTH : ch1 - 1) * Q;
+    const bool more = !LOCAL && ch + 1 < ch1;
     // the head's dt comes from its even wave's load: both waves take its staged cs_end
     cs_end = s_cs[hl][Q - 1];
     sdec += cs_end;
     const float* ws_ = s_w[hl];
 
     if (!LOCAL) {
+      // ---- the G^T tiles: wave w computes tile w (waves 0 and 1 also tiles 8 and 9)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int tix = w + 8 * k;
+        if (tix < 10) {
+          const int jt = tix >= 6 ? 3 : tix >= 3 ? 2 : tix >= 1 ? 1 : 0;
+          const int ms = tix - jt * (jt + 1) / 2;
+          v4f gt = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk)
+            gt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld8(&sBr[fb + 2048 * kk + 512 * ms]),
+                                                         ld8(&sC[fb + 2048 * kk + 512 * jt]), gt, 0, 0, 0);
+          *(v4f*)(&sG[tix * 256 + lane * 4]) = gt;
+        }
+      }
       // ---- Z^T = h C^T per (p tile ip, t tile jt), scaled by exp(cs_t): lane holds
       // Z^T[p = 16 (2 ph + ip) + 4 kq + r][t = 16 jt + l16]
       v4f zacc[2][4];
@@ -393,33 +432,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int jt = 0; jt < 4; ++jt) zacc[ip][jt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m2 = 0; m2 < NT / 2; ++m2) {
-        v8bf ah[2], al[2];
+        __builtin_amdgcn_sched_barrier(0);
+        v8bf ah[2];
 #pragma unroll
-        for (int ip = 0; ip < 2; ++ip) {
-          uint32_t hi[8], lo[8];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            split2(hT[2 * m2][ip][r], hi[r], lo[r]);
-            split2(hT[2 * m2 + 1][ip][r], hi[4 + r], lo[4 + r]);
-          }
-          ah[ip] = mk8(pack_hi(hi[0], hi[1]), pack_hi(hi[2], hi[3]), pack_hi(hi[4], hi[5]), pack_hi(hi[6], hi[7]));
-          al[ip] = mk8(pack_hi(lo[0], lo[1]), pack_hi(lo[2], lo[3]), pack_hi(lo[4], lo[5]), pack_hi(lo[6], lo[7]));
-        }
+        for (int ip = 0; ip < 2; ++ip)
+          ah[ip] = mk8(cvt_pair(hT[2 * m2][ip][0], hT[2 * m2][ip][1]), cvt_pair(hT[2 * m2][ip][2], hT[2 * m2][ip][3]),
+                       cvt_pair(hT[2 * m2 + 1][ip][0], hT[2 * m2 + 1][ip][1]),
+                       cvt_pair(hT[2 * m2 + 1][ip][2], hT[2 * m2 + 1][ip][3]));
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
           // C rows t = 16 jt + l16 at the slots' n (32 m2 + 4 kq + u, 32 m2 + 16 + 4 kq + u)
-          const int tr = 16 * jt + l16;
-          const v8bf cf = ld44(&sC[rm(tr, 32 * m2 + 4 * kq)], &sC[rm(tr, 32 * m2 + 16 + 4 * kq)]);
+          const v8bf cf = ld44(&sC[zb0 + 2048 * m2 + 512 * jt], &sC[zb1 + 2048 * m2 + 512 * jt]);
 #pragma unroll
           for (int ip = 0; ip < 2; ++ip) {
             zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ip], cf, zacc[ip][jt], 0, 0, 0);
-            zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[ip], cf, zacc[ip][jt], 0, 0, 0);
           }
         }
       }
+      bar_lds();  // the G^T tiles written
       const float* cs_ = s_cs[hl];
       const float* dt_ = s_dt[hl];
       const float* et_ = s_et[hl];
+      const float* bs_ = s_b[LOCAL ? 0 : hl];
       const uint16_t* xt = sXT[hl];
       // x^T rows p = 16 (2 ph + ip) + l16 at the slots' s (32 pr + 4 kq + u, 32 pr + 16 + 4 kq + u)
       v8bf xa[2][2];
@@ -434,17 +468,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // M^T = G^T exp(cs_t - cs_s) dt_s on s <= t (+ D on the diagonal), then y^T += x^T M^T
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
+        // (each t tile's reads, products and stores kept together: hoisted LDS reads of later
+        // tiles would need more registers than a wave has)
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) load_part(pr, cn, jt);
         v4f g[4];
 #pragma unroll
-        for (int ms = 0; ms < 4; ++ms) g[ms] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          const v8bf cb = ld8(&sC[rm(16 * jt + l16, 32 * kk + 8 * kq)]);
-#pragma unroll
-          for (int ms = 0; ms <= jt; ++ms)
-            g[ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld8(&sBr[rm(16 * ms + l16, 32 * kk + 8 * kq)]), cb,
-                                                            g[ms], 0, 0, 0);
-        }
+        for (int ms = 0; ms <= jt; ++ms) g[ms] = *(const v4f*)(&sG[(jt * (jt + 1) / 2 + ms) * 256 + lane * 4]);
         const int t = 16 * jt + l16;
         const float cst = cs_[t];
         const float e = et_[t];
@@ -452,62 +482,69 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int ip = 0; ip < 2; ++ip)
 #pragma unroll
           for (int r = 0; r < 4; ++r) zacc[ip][jt][r] *= e;
-        uint32_t mh[4][2], mlo[4][2];
+        uint32_t mh[4][2];
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
           if (ms > jt) {  // above the diagonal: zero (the partner of a diagonal tile in its pair)
-            mh[ms][0] = mh[ms][1] = mlo[ms][0] = mlo[ms][1] = 0u;
+            mh[ms][0] = mh[ms][1] = 0u;
             continue;
           }
-          const v4f css = *(const v4f*)(&cs_[16 * ms + 4 * kq]);
-          const v4f dts = *(const v4f*)(&dt_[16 * ms + 4 * kq]);
-          uint32_t hi[4], lo[4];
+          float m[4];
+          if (ms < jt) {
+            // below the diagonal (every s < t): exp2(cs_t - cs_s) dt_s as exp2(cs_t - cs_e) times
+            // exp2(cs_e - cs_s) dt_s, e the last step of s's tile (the second factor staged)
+            const float at = __builtin_amdgcn_exp2f(cst - cs_[16 * ms + 15]);
+            const v4f bs = *(const v4f*)(&bs_[16 * ms + 4 * kq]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int sidx = 16 * ms + 4 * kq + r;
-            float m = 0.0f;
-            if (sidx <= t) m = g[ms][r] * (__builtin_amdgcn_exp2f(cst - css[r]) * dts[r]);
-            if (sidx == t) m += D_h;
-            split2(m, hi[r], lo[r]);
+            for (int r = 0; r < 4; ++r) m[r] = g[ms][r] * bs[r] * at;
+          } else {
+            const v4f css = *(const v4f*)(&cs_[16 * ms + 4 * kq]);
+            const v4f dts = *(const v4f*)(&dt_[16 * ms + 4 * kq]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int sidx = 16 * ms + 4 * kq + r;
+              m[r] = 0.0f;
+              if (sidx <= t) m[r] = g[ms][r] * (__builtin_amdgcn_exp2f(cst - css[r]) * dts[r]);
+              if (sidx == t) m[r] += D_h;
+            }
           }
-          mh[ms][0] = pack_hi(hi[0], hi[1]);
-          mh[ms][1] = pack_hi(hi[2], hi[3]);
-          mlo[ms][0] = pack_hi(lo[0], lo[1]);
-          mlo[ms][1] = pack_hi(lo[2], lo[3]);
+          mh[ms][0] = cvt_pair(m[0], m[1]);
+          mh[ms][1] = cvt_pair(m[2], m[3]);
         }
 #pragma unroll
         for (int pr = 0; 2 * pr <= jt; ++pr) {
           const v8bf bh = mk8(mh[2 * pr][0], mh[2 * pr][1], mh[2 * pr + 1][0], mh[2 * pr + 1][1]);
-          const v8bf bl = mk8(mlo[2 * pr][0], mlo[2 * pr][1], mlo[2 * pr + 1][0], mlo[2 * pr + 1][1]);
 #pragma unroll
           for (int ip = 0; ip < 2; ++ip) {
             zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[ip][pr], bh, zacc[ip][jt], 0, 0, 0);
-            zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[ip][pr], bl, zacc[ip][jt], 0, 0, 0);
           }
         }
-        // ---- y: lane holds y[t][p = 16 (2 ph + ip) + 4 kq + r]
-        const int64_t tg = c0 + t;
-        if (hv && tg < L) {
+        // ---- y: lane holds y[t][p = 16 (2 ph + ip) + 4 kq + r] (rows past the sequence's end
+        // fall outside the chunk's resource: their stores are dropped)
+        if (hv) {
+          const uint32_t rv = rows_in(c0);
+          const auto ry = buf_rsrc(Y + (b * L + c0) * a.ld_y + head * P, rv * (uint32_t)a.ld_y * 2u);
 #pragma unroll
           for (int ip = 0; ip < 2; ++ip) {
-            const int64_t col = head * P + 16 * (2 * ph + ip) + 4 * kq;
+            const uint32_t colw = 16 * (2 * ph + ip) + 4 * kq;
             float v[4] = {zacc[ip][jt][0], zacc[ip][jt][1], zacc[ip][jt][2], zacc[ip][jt][3]};
             if (G) {
-              const uint2 gg = *(const uint2*)(G + (b * L + tg) * a.ld_gate + col);
+              const auto rg = buf_rsrc(G + (b * L + c0) * a.ld_gate + head * P, rv * (uint32_t)a.ld_gate * 2u);
+              const uint2 gg = buf_ld8(rg, ((uint32_t)t * (uint32_t)a.ld_gate + colw) * 2u);
               v[0] *= silu_gate(bf16_to_f32((bf16_t)(gg.x & 0xFFFFu)));
               v[1] *= silu_gate(bf16_to_f32((bf16_t)(gg.x >> 16)));
               v[2] *= silu_gate(bf16_to_f32((bf16_t)(gg.y & 0xFFFFu)));
               v[3] *= silu_gate(bf16_to_f32((bf16_t)(gg.y >> 16)));
             }
-            const uint2 o{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                          (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
-            *(uint2*)(Y + (b * L + tg) * a.ld_y + col) = o;
+            const uint2 o{cvt_pair(v[0], v[1]), cvt_pair(v[2], v[3])};
+            buf_st8(o, ry, ((uint32_t)t * (uint32_t)a.ld_y + colw) * 2u);
           }
         }
       }
     }
 
     // ---- state: h^T = exp(cs_end) h^T + B^T (w x)
+    __builtin_amdgcn_sched_barrier(0);
     const float ed = __builtin_amdgcn_exp2f(cs_end);
 #pragma unroll
     for (int mn = 0; mn < NT; ++mn)
@@ -517,6 +554,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int r = 0; r < 4; ++r) hT[mn][ip][r] *= ed;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      if (LOCAL) load_part(pr, cn, 2 * kk);
       const v4f w0 = *(const v4f*)(&ws_[32 * kk + 8 * kq]);
       const v4f w1 = *(const v4f*)(&ws_[32 * kk + 8 * kq + 4]);
       const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
@@ -524,18 +562,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int ip = 0; ip < 2; ++ip) {
         const v4i raw = *(const v4i*)(&sXT[hl][(16 * (2 * ph + ip) + l16) * XS + 32 * kk + 8 * kq]);
-        uint32_t hi[8], lo[8];
+        uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t word = (uint32_t)raw[u >> 1];
-          const float xvv = __uint_as_float((u & 1) ? (word & 0xFFFF0000u) : (word << 16));
-          split2(xvv * wv[u], hi[u], lo[u]);
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t word = (uint32_t)raw[d];
+          split_pair(__uint_as_float(word << 16) * wv[2 * d], __uint_as_float(word & 0xFFFF0000u) * wv[2 * d + 1],
+                     hi[d], lo[d]);
         }
-        xh[ip] = mk8(pack_hi(hi[0], hi[1]), pack_hi(hi[2], hi[3]), pack_hi(hi[4], hi[5]), pack_hi(hi[6], hi[7]));
-        xl[ip] = mk8(pack_hi(lo[0], lo[1]), pack_hi(lo[2], lo[3]), pack_hi(lo[4], lo[5]), pack_hi(lo[6], lo[7]));
+        xh[ip] = mk8(hi[0], hi[1], hi[2], hi[3]);
+        xl[ip] = mk8(lo[0], lo[1], lo[2], lo[3]);
       }
 #pragma unroll
       for (int mn = 0; mn < NT; ++mn) {
+        if (LOCAL && mn == NT / 2) load_part(pr, cn, 2 * kk + 1);
         const v8bf bt = ld8(&sBT[(16 * mn + l16) * XS + 32 * kk + 8 * kq]);
 #pragma unroll
         for (int ip = 0; ip < 2; ++ip) {
@@ -576,25 +615,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // Combine over segments, per (sequence, head, state element): afterwards hloc[b, s] holds the
 // state entering segment s + 1.
+template <int V>
 __global__ __launch_bounds__(256) void k_ssd_combine(const float* __restrict__ h0, float* __restrict__ hloc,
                                                      const float* __restrict__ sdec, int64_t B, int64_t H,
                                                      int64_t PN, int S) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  typedef float fv __attribute__((ext_vector_type(V)));
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;  // V consecutive state elements
   if (i >= B * H * PN) return;
   const int64_t b = i / (H * PN), hp = i % (H * PN), hd = hp / PN, e = hp % PN;
-  float h = h0 ? h0[i] : 0.0f;
-  for (int s = 0; s + 1 < S; ++s) {
-    const int64_t j = ((b * (S - 1) + s) * H + hd) * PN + e;
-    h = __builtin_fmaf(__builtin_amdgcn_exp2f(sdec[(b * (S - 1) + s) * H + hd]), h, hloc[j]);
-    hloc[j] = h;
+  fv h = h0 ? *(const fv*)(h0 + i) : fv{};
+  // four segments' loads first, then their chain of updates
+  for (int s0 = 0; s0 + 1 < S; s0 += 4) {
+    const int n = (S - 1 - s0) < 4 ? (S - 1 - s0) : 4;
+    fv v[4];
+    float d[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t bs = b * (S - 1) + s0 + (k < n ? k : 0);
+      v[k] = *(const fv*)(hloc + (bs * H + hd) * PN + e);
+      d[k] = __builtin_amdgcn_exp2f(sdec[bs * H + hd]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < n) {
+#pragma unroll
+        for (int c = 0; c < V; ++c) h[c] = __builtin_fmaf(d[k], h[c], v[k][c]);
+        *(fv*)(hloc + ((b * (S - 1) + s0 + k) * H + hd) * PN + e) = h;
+      }
+    }
   }
 }
 
-// The chunked kernels take bf16 activations with headdim 64, d_state 64 or 128, and row
-// strides and bases that allow 16-byte loads of x, B and C (8-byte loads of the gate).
+// The chunked kernels take bf16 activations with headdim 64, d_state 64 or 128, dt through
+// softplus (dt >= 0: the decay exponent cs is monotone along a chunk, which the split of the
+// decays at tile ends relies on), and row strides and bases that allow 16-byte loads of x, B
+// and C (8-byte loads of the gate), below 2^24 elements.
 static bool ssd_chunk_ok(const ScanArgs& a) {
   auto al = [](const void* p) { return ((uintptr_t)p % 16) == 0; };
-  return a.act_bf16 && a.P == kSsdP && (a.N == 64 || a.N == 128) && a.ld_x % 8 == 0 && a.ld_B % 8 == 0 &&
+  const int64_t lim = int64_t(1) << 24;
+  if (a.ld_x >= lim || a.ld_B >= lim || a.ld_C >= lim || a.ld_delta >= lim || a.ld_y >= lim || a.ld_gate >= lim)
+    return false;
+  return a.act_bf16 && a.softplus && a.P == kSsdP && (a.N == 64 || a.N == 128) && a.ld_x % 8 == 0 && a.ld_B % 8 == 0 &&
          a.ld_C % 8 == 0 && al(a.x) && al(a.Bm) && al(a.Cm) && (!a.gate || (a.ld_gate % 4 == 0 && ((uintptr_t)a.gate % 8) == 0));
 }
 
@@ -665,8 +726,12 @@ hipError_t launch_scan_ssd(const ScanArgs& a, void* ws, size_t wsb, hipStream_t 
       if (a.N == 128) hipLaunchKernelGGL((k_ssd_seg<128, true>), g1, dim3(512), 0, s, a, sg);
       else hipLaunchKernelGGL((k_ssd_seg<64, true>), g1, dim3(512), 0, s, a, sg);
       const int64_t n = a.batch * a.H * a.P * a.N;
-      hipLaunchKernelGGL(k_ssd_combine, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, a.h0, sg.hloc, sg.sdec,
-                         a.batch, a.H, a.P * a.N, p.S);
+      if (!a.h0 || (uintptr_t)a.h0 % 16 == 0)
+        hipLaunchKernelGGL(k_ssd_combine<4>, dim3((unsigned)cdiv(n, 1024)), dim3(256), 0, s, a.h0, sg.hloc, sg.sdec,
+                           a.batch, a.H, a.P * a.N, p.S);
+      else
+        hipLaunchKernelGGL(k_ssd_combine<1>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, a.h0, sg.hloc, sg.sdec,
+                           a.batch, a.H, a.P * a.N, p.S);
     }
     const dim3 g2(nb * (unsigned)p.S);
     if (a.N == 128) hipLaunchKernelGGL((k_ssd_seg<128, false>), g2, dim3(512), 0, s, a, sg);

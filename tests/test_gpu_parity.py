@@ -209,6 +209,24 @@ def test_scan_parity(batch, L, H, P, N, aps, dt):
     check(host(hl), href, (1e-4 if dt == "bf16" else 1e-5), what=f"test_scan_parity h_last {batch} {L} {H} {P} {N} {dt}")
 
 
+def test_scan_ssd_dt_without_softplus():
+    """SSD kind, bf16, a chunk-eligible shape, dt taken as given (no softplus, some dt < 0): the
+    library routes it to the recurrent kernel (the chunked one splits decays in a way that needs
+    dt >= 0) and matches the oracle."""
+    p = _bf16_problem(wl.scan_problem(2, 130, 4, 64, 64, False, seed=21))
+    p["dt_bias"] = np.full_like(p["dt_bias"], 0.05)  # dt = delta + 0.05 ~ N(0.05, 0.75): mixed signs
+    p["A"] = p["A"] * 0.05  # keep exp(dt A) moderate for either sign of dt
+    h0 = wl.normal(wl.rng(5), (2, 4, 64, 64), 0.0, 0.5)
+    ref, href = oracle.selective_scan(p["x"], p["delta"], p["A"], p["Bm"], p["Cm"], p["D"], p["dt_bias"], h0=h0,
+                                      softplus=False)
+    y, hl = tws.ssm_selective_scan_fwd(to_dev(p["x"], torch.bfloat16), to_dev(p["delta"], torch.bfloat16),
+                                       to_dev(p["A"]), to_dev(p["Bm"], torch.bfloat16),
+                                       to_dev(p["Cm"], torch.bfloat16), to_dev(p["D"]), to_dev(p["dt_bias"]),
+                                       False, to_dev(h0), return_last_state=True)
+    check(host(y), ref, TOL["bf16"], what="test_scan_ssd_dt_without_softplus y")
+    check(host(hl), href, 1e-4, what="test_scan_ssd_dt_without_softplus h_last")
+
+
 def test_scan_long_sequence_sampled():
     """long_scan workload (batch 8, L 8192, 512 channels, d_state 16), full size on the GPU;
     the oracle checks 24 channels of every sequence (channels are independent)."""
