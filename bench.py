@@ -600,10 +600,11 @@ def fp_inout_bench(args, sh, dev) -> dict:
 # ------------------------------------------------------------------ decode and training side
 
 def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
-    """Token-by-token decoding through the whole stack (ssm_mixer_step per layer, one token per
-    sequence, the recurrent state of every layer carried in HBM), one token step captured as a
-    HIP graph and replayed.  Algorithmic bytes per token step: the packed ternary weights and
-    scales of every layer, the fp32 state read and written, and the token's input and output."""
+    """Token-by-token decoding through the whole stack (ssm_mixer_stack_step: one token per
+    sequence through every layer, the recurrent state of every layer carried in HBM; beside it
+    the same step as ssm_mixer_step per layer), one token step captured as a HIP graph and
+    replayed.  Algorithmic bytes per token step: the packed ternary weights and scales of every
+    layer, the fp32 state read and written, and the token's input and output."""
     cfg = prob.cfg
     L = tws.lib()
     cb = ctypes.byref(prob.c)
@@ -613,6 +614,10 @@ def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
     for B in batches:
         nb = tws.ssm_mixer_workspace_bytes(prob.c, B, 1)
         ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=prob.dev)
+        nbs = tws.ssm_mixer_stack_workspace_bytes(prob.c, B)
+        wss = torch.empty(max(nbs, 256), dtype=torch.uint8, device=prob.dev)
+        nl = len(prob.mws)
+        wp = (ctypes.POINTER(tws.MixerWeights) * nl)(*[ctypes.pointer(m) for m in prob.mws])
         shape = (B, cfg.d_inner, cfg.d_state) if cfg.kind == wl.MAMBA1 else (B, cfg.nheads, cfg.headdim, cfg.d_state)
         states = [torch.zeros(shape, dtype=torch.float32, device=prob.dev) for _ in prob.mws]
         cshape = (B, cfg.d_conv - 1, cfg.conv_channels)
@@ -621,7 +626,10 @@ def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
         u = prob.u[:B, 0].contiguous()
         bufs = [torch.empty_like(u), torch.empty_like(u)]
 
-        def token_step(sh):
+        sp = (ctypes.c_void_p * nl)(*[t.data_ptr() for t in states])
+        cp = None if cstates[0] is None else (ctypes.c_void_p * nl)(*[t.data_ptr() for t in cstates])
+
+        def layer_steps(sh):
             h = u
             for i, mw in enumerate(prob.mws):
                 o = bufs[i % 2]
@@ -630,31 +638,40 @@ def decode_bench(prob: Problem, steps: int, warmup: int, batches) -> dict:
                                         1, ws.data_ptr(), nb, sh))
                 h = o
 
-        g = torch.cuda.CUDAGraph()
-        s2 = torch.cuda.Stream()
-        s2.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s2):
-            token_step(s2.cuda_stream)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=s2):
+        def stack_step(sh):
+            status(L.ssm_mixer_stack_step(cb, wp, nl, u.data_ptr(), bufs[0].data_ptr(), B, sp, cp, 1, wss.data_ptr(),
+                                          nbs, sh))
+
+        def timed(token_step):
+            g = torch.cuda.CUDAGraph()
+            s2 = torch.cuda.Stream()
+            s2.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s2):
                 token_step(s2.cuda_stream)
-        torch.cuda.synchronize()
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=s2):
+                    token_step(s2.cuda_stream)
+            torch.cuda.synchronize()
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            del g
+            return e0.elapsed_time(e1) * 1e3 / steps
+
+        us = timed(stack_step)
+        us_layers = timed(layer_steps)
         sbytes = 2 * sum(t.numel() * 4 for t in states + [c for c in cstates if c is not None])
         byts = wbytes + sbytes + 2 * B * cfg.d_model * es
-        out[f"batch_{B}"] = {"us_per_token_step": us, "tokens_per_s": B / (us * 1e-6), "layers": len(prob.mws),
+        out[f"batch_{B}"] = {"us_per_token_step": us, "tokens_per_s": B / (us * 1e-6), "layers": nl,
                              "bytes_per_step": byts, "GBps": byts / (us * 1e-6) / 1e9,
+                             "us_per_token_step_layer_by_layer": us_layers,
                              "finite": bool(all(torch.isfinite(t).all() for t in states))}
-        del g
     return out
 
 

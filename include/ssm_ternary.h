@@ -414,6 +414,31 @@ ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * ssm_mixer_stack_step -- one decoding step through a stack of nlayers mixer layers of one
+ * configuration c (the output of layer l is the input of layer l + 1): ONE new token per
+ * sequence (the TernarySSM and TriSSM pages' recurrent inference, a whole model's layers per
+ * token).  The result, and every state afterwards, is bit-identical to calling ssm_mixer_step
+ * for layer 0, 1, ..., nlayers - 1 in turn.  Mamba-1 kind layers with ternary projections,
+ * per-tensor scales, int8 activations and no gate run in one kernel launch per 24 layers, a
+ * block per sequence keeping the activations between layers on chip and fetching each
+ * layer's first weights while the previous layer runs; any other layer runs as ssm_mixer_step.
+ *  w:           host array of nlayers pointers, layer l's weights (as ssm_mixer_step);
+ *  states:      host array of nlayers device pointers, layer l's state (as ssm_mixer_step);
+ *  conv_states: host array of nlayers pointers (gated block with d_conv > 1), or NULL;
+ *  u, out:      [batch, d_model] in act_dtype (out may equal u when add_residual != 0);
+ *  workspace:   ssm_mixer_stack_workspace_bytes(c, batch) bytes of device memory, 256-byte
+ *               aligned (the layers' workspace and the activations between layers).
+ * All device memory caller-owned; asynchronous on stream; nothing allocated.
+ * Errors: SSM_ERR_SHAPE (nlayers < 1, the configuration's), SSM_ERR_NULL, SSM_ERR_WORKSPACE,
+ * SSM_ERR_ALIGN, and those of ssm_mixer_step for any layer.
+ */
+size_t ssm_mixer_stack_workspace_bytes(const ssm_mixer_config* c, int64_t batch);
+ssm_status ssm_mixer_stack_step(const ssm_mixer_config* c, const ssm_mixer_weights* const* w, int32_t nlayers,
+                                const void* u, void* out, int64_t batch, float* const* states,
+                                float* const* conv_states, int32_t add_residual, void* workspace,
+                                size_t ws_bytes, hipStream_t stream);
+
+/*
  * ssm_conv1d_silu_fwd -- the gated block's short causal depthwise convolution with SiLU
  * (Mamba, cited under "Builds on" of "Baseline Shape Decides the Verdict ..."):
  *   a[b, t, c] = bias[c] + sum_{j < width} w[c, j] * x[b, t - width + 1 + j, c]

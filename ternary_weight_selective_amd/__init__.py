@@ -91,6 +91,7 @@ EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_last_error", "ssm_packed
            "ssm_bitlinear_fwd", "ssm_selective_scan_workspace_bytes", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_noalloc",
            "ssm_dt_input_quantize",
            "ssm_mixer_workspace_bytes", "ssm_mixer_fwd", "ssm_mixer_fwd_stages", "ssm_mixer_fuses_front", "ssm_mixer_step",
+           "ssm_mixer_stack_workspace_bytes", "ssm_mixer_stack_step",
            "ssm_conv1d_silu_fwd", "ssm_dense_fwd", "ssm_bitlinear_bwd_workspace_bytes", "ssm_bitlinear_bwd",
            "ssm_qat_sgd_step", "ssm_selective_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd",
            "ssm_mixer_bwd_workspace_bytes", "ssm_mixer_bwd"]
@@ -153,6 +154,12 @@ def lib():
                                     ctypes.POINTER(MixerGrads), _vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]
         L.ssm_mixer_bwd.restype = ctypes.c_int
         L.ssm_mixer_step.restype = ctypes.c_int
+        L.ssm_mixer_stack_workspace_bytes.argtypes = [ctypes.POINTER(MixerConfig), _i64]
+        L.ssm_mixer_stack_workspace_bytes.restype = _sz
+        L.ssm_mixer_stack_step.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(ctypes.POINTER(MixerWeights)),
+                                           _i32, _vp, _vp, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i32, _vp,
+                                           _sz, _vp]
+        L.ssm_mixer_stack_step.restype = ctypes.c_int
         L.ssm_mixer_fwd.argtypes = [ctypes.POINTER(MixerConfig), ctypes.POINTER(MixerWeights), _vp, _vp, _i64, _i64,
                                     _i32, _vp, _sz, _vp]
         L.ssm_mixer_fwd.restype = ctypes.c_int
@@ -423,6 +430,36 @@ def ssm_mixer_step(cfg: MixerConfig, weights, u: torch.Tensor, state: torch.Tens
     ws = _workspace(nb, u.device, workspace)
     _check(L.ssm_mixer_step(ctypes.byref(cfg), ctypes.byref(mw), _p(u), _p(out), batch, _p(state), _p(conv_state),
                             int(add_residual), _p(ws), nb if ws is None else ws.numel(), _stream(stream)))
+    return out
+
+
+def ssm_mixer_stack_workspace_bytes(cfg: MixerConfig, batch: int) -> int:
+    return int(lib().ssm_mixer_stack_workspace_bytes(ctypes.byref(cfg), batch))
+
+
+def ssm_mixer_stack_step(cfg: MixerConfig, weights: list, u: torch.Tensor, states: list, add_residual: bool = True,
+                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         conv_states: list | None = None, stream=None):
+    """One decoding step through a stack of layers (weights[l], states[l]; the output of layer l
+    feeds layer l + 1) on u [B, d_model]; every state (fp32, contiguous) is read and overwritten
+    in place.  Equal to ssm_mixer_step applied layer by layer."""
+    n = len(weights)
+    if len(states) != n or (conv_states is not None and len(conv_states) != n):
+        raise ValueError("one state (and conv_state) per layer")
+    if not u.is_contiguous() or any(not t.is_contiguous() or t.dtype != torch.float32 for t in states):
+        raise ValueError("u and the states must be contiguous, the states float32")
+    mws = [w if isinstance(w, MixerWeights) else mixer_weights(w) for w in weights]
+    wp = (ctypes.POINTER(MixerWeights) * n)(*[ctypes.pointer(m) for m in mws])
+    sp = (_vp * n)(*[t.data_ptr() for t in states])
+    cp = None if conv_states is None else (_vp * n)(*[_p(t) for t in conv_states])
+    batch = u.shape[0]
+    if out is None:
+        out = torch.empty_like(u)
+    L = lib()
+    nb = L.ssm_mixer_stack_workspace_bytes(ctypes.byref(cfg), batch)
+    ws = _workspace(nb, u.device, workspace)
+    _check(L.ssm_mixer_stack_step(ctypes.byref(cfg), wp, n, _p(u), _p(out), batch, sp, cp, int(add_residual), _p(ws),
+                                  nb if ws is None else ws.numel(), _stream(stream)))
     return out
 
 

@@ -469,6 +469,38 @@ int32_t ssm_mixer_fuses_front(const ssm_mixer_config* c) {
 }
 
 namespace {
+// The decode kernel's conditions for one layer: Mamba-1 kind, ternary projections with
+// per-tensor scales and int8 activations, no gate, sizes it is built for, 16-byte aligned
+// packed weights, gains, A and state.
+bool dec_layer_ok(const ssm_mixer_config* c, const ssm_mixer_weights* w, const float* state, int64_t batch,
+                  int64_t pw) {
+  return c->kind == SSM_MIXER_MAMBA1 && w && state && !c->gated && !c->fp_proj && c->act_bits == 8 &&
+         c->group_size == 0 && batch <= 1024 && w->w_in && w->w_x && w->w_dt && w->w_out && w->s_in && w->s_x &&
+         w->s_dt && w->s_out && w->A && aligned(w->w_in, 16) && aligned(w->w_x, 16) && aligned(w->w_out, 16) &&
+         aligned(w->A, 16) && aligned(state, 16) && aligned(w->g_in, 16) && aligned(w->g_x, 16) &&
+         aligned(w->g_out, 16) && aligned(w->g_dt, 16) &&
+         decode_supported((int)c->d_model, (int)c->d_inner, (int)c->d_state, (int)c->dt_rank, (int)pw);
+}
+DecodeArgs dec_args(const ssm_mixer_config* c, int64_t batch, int64_t pw, const void* u, void* out,
+                    int32_t add_residual) {
+  DecodeArgs da{};
+  da.B = batch; da.Dm = (int)c->d_model; da.Di = (int)c->d_inner; da.NS = (int)c->d_state;
+  da.R = (int)c->dt_rank; da.PW = (int)pw; da.act_bf16 = c->act_dtype == SSM_BF16;
+  da.u = u; da.out = out; da.add_residual = add_residual ? 1 : 0;
+  da.w_dt_row_words = cdiv(c->dt_rank, 16);
+  da.eps = c->norm_eps;
+  return da;
+}
+void dec_layer(DecodeLayer& L, const ssm_mixer_weights* w, float* state) {
+  L.w_in = (const uint32_t*)w->w_in; L.s_in = w->s_in; L.g_in = w->g_in;
+  L.w_x = (const uint32_t*)w->w_x; L.s_x = w->s_x; L.g_x = w->g_x;
+  L.w_dt = (const uint32_t*)w->w_dt; L.s_dt = w->s_dt; L.g_dt = w->g_dt;
+  L.dt_bias = w->dt_bias; L.A = w->A; L.D = w->D;
+  L.w_out = (const uint32_t*)w->w_out; L.s_out = w->s_out; L.g_out = w->g_out;
+  L.state = state;
+  L.gains = (w->g_in ? 1 : 0) | (w->g_x ? 2 : 0) | (w->g_out ? 4 : 0) | (w->g_dt ? 8 : 0);
+}
+
 // One mixer layer; state (nullable): the scan's initial state, overwritten with its final state
 // (used for one token per sequence only, where no time chunks are formed).
 ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, const void* u, void* out,
@@ -499,6 +531,61 @@ ssm_status ssm_mixer_step(const ssm_mixer_config* c, const ssm_mixer_weights* w,
   if (batch > 0 && c && c->gated && c->d_conv > 1 && !conv_state)
     return fail(SSM_ERR_NULL, "mixer step: conv_state is NULL (gated block)");
   return mixer_run(c, w, u, out, batch, 1, add_residual, ws, wsb, stream, state, conv_state, nullptr);
+}
+
+size_t ssm_mixer_stack_workspace_bytes(const ssm_mixer_config* c, int64_t batch) {
+  std::string keep = g_err;
+  MixPlan p;
+  const ssm_status st = mix_plan(c, batch, 1, &p);
+  g_err = keep;
+  if (st != SSM_OK) return 0;
+  // the layer's workspace, then two [batch, d_model] activation buffers
+  return align_up(ssm_mixer_workspace_bytes(c, batch, 1)) + 2 * align_up((size_t)batch * c->d_model * act_size(c->act_dtype));
+}
+
+ssm_status ssm_mixer_stack_step(const ssm_mixer_config* c, const ssm_mixer_weights* const* w, int32_t nlayers,
+                                const void* u, void* out, int64_t batch, float* const* states,
+                                float* const* conv_states, int32_t add_residual, void* ws, size_t wsb,
+                                hipStream_t stream) {
+  g_err.clear();
+  MixPlan p;
+  ssm_status st = mix_plan(c, batch, 1, &p);
+  if (st != SSM_OK) return st;
+  if (nlayers < 1) return fail(SSM_ERR_SHAPE, "mixer stack step: nlayers %d < 1", (int)nlayers);
+  if (!w || !states) return fail(SSM_ERR_NULL, "mixer stack step: w and states are required");
+  if (batch > 0 && (!u || !out)) return fail(SSM_ERR_NULL, "mixer stack step: u / out is NULL");
+  if (out == u && !add_residual) return fail(SSM_ERR_SHAPE, "mixer stack step: out may alias u only with add_residual");
+  const size_t need = ssm_mixer_stack_workspace_bytes(c, batch);
+  if (!ws || wsb < need) return fail(SSM_ERR_WORKSPACE, "mixer stack step: workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(SSM_ERR_ALIGN, "mixer stack step: workspace must be 256-byte aligned");
+  if (batch == 0) return SSM_OK;
+  const size_t lwb = align_up(ssm_mixer_workspace_bytes(c, batch, 1));
+  const size_t ab = align_up((size_t)batch * c->d_model * act_size(c->act_dtype));
+  void* buf[2] = {(char*)ws + lwb, (char*)ws + lwb + ab};
+  bool fused = true;
+  for (int l = 0; l < nlayers && fused; ++l) fused = dec_layer_ok(c, w[l], states[l], batch, p.PW);
+  if (fused) {  // the layers in launches of up to kDecMaxLayers, activations kept in LDS inside one
+    for (int l0 = 0, g = 0; l0 < nlayers; l0 += kDecMaxLayers, ++g) {
+      const int nl = nlayers - l0 < kDecMaxLayers ? nlayers - l0 : kDecMaxLayers;
+      const void* in = l0 == 0 ? u : buf[(g - 1) % 2];
+      void* o = l0 + nl == nlayers ? out : buf[g % 2];
+      DecodeArgs da = dec_args(c, batch, p.PW, in, o, add_residual);
+      da.nl = nl;
+      for (int j = 0; j < nl; ++j) dec_layer(da.layer[j], w[l0 + j], states[l0 + j]);
+      st = dev(launch_decode_m1(da, stream), "mixer stack step");
+      if (st != SSM_OK) return st;
+    }
+    return SSM_OK;
+  }
+  // any other layer: ssm_mixer_step per layer, the activations between layers in the workspace
+  for (int l = 0; l < nlayers; ++l) {
+    const void* in = l == 0 ? u : buf[(l - 1) % 2];
+    void* o = l + 1 == nlayers ? out : buf[l % 2];
+    st = ssm_mixer_step(c, w[l], in, o, batch, states[l], conv_states ? conv_states[l] : nullptr, add_residual, ws,
+                        lwb, stream);
+    if (st != SSM_OK) return st;
+  }
+  return SSM_OK;
 }
 
 ssm_status ssm_conv1d_silu_fwd(const void* x, int32_t dtype, int64_t batch, int64_t seqlen, int64_t channels,
@@ -693,22 +780,11 @@ ssm_status mixer_run(const ssm_mixer_config* c, const ssm_mixer_weights* w, cons
     void* x = c->gated ? base + p.off_xc : xz;         // the SSM input
     void* pp = base + p.off_p;
     void* y = base + p.off_y;
-    // one decoding step on kernels of its own (spread over the chip rather than one row block)
-    if (state && seqlen == 1 && !dbg && !c->gated && !c->fp_proj && c->act_bits == 8 && c->group_size == 0 &&
-        batch <= 1024 && aligned(w->w_in, 16) && aligned(w->w_x, 16) && aligned(w->w_out, 16) &&
-        aligned(w->A, 16) && aligned(state, 16) &&
-        decode_supported((int)c->d_model, (int)c->d_inner, (int)c->d_state, (int)c->dt_rank, (int)p.PW)) {
-      DecodeArgs da{};
-      da.B = batch; da.Dm = (int)c->d_model; da.Di = (int)c->d_inner; da.NS = (int)c->d_state;
-      da.R = (int)c->dt_rank; da.PW = (int)p.PW; da.act_bf16 = c->act_dtype == SSM_BF16;
-      da.u = u; da.out = out; da.add_residual = add_residual ? 1 : 0;
-      da.w_in = (const uint32_t*)w->w_in; da.s_in = w->s_in; da.g_in = w->g_in;
-      da.w_x = (const uint32_t*)w->w_x; da.s_x = w->s_x; da.g_x = w->g_x;
-      da.w_dt = (const uint32_t*)w->w_dt; da.w_dt_row_words = cdiv(c->dt_rank, 16); da.s_dt = w->s_dt;
-      da.g_dt = w->g_dt;
-      da.dt_bias = w->dt_bias; da.A = w->A; da.D = w->D;
-      da.w_out = (const uint32_t*)w->w_out; da.s_out = w->s_out; da.g_out = w->g_out;
-      da.eps = c->norm_eps; da.state = state; da.x = base + p.off_x;
+    // one decoding step on a kernel of its own (a block per sequence runs the whole layer)
+    if (seqlen == 1 && !dbg && dec_layer_ok(c, w, state, batch, p.PW)) {
+      DecodeArgs da = dec_args(c, batch, p.PW, u, out, add_residual);
+      da.nl = 1;
+      dec_layer(da.layer[0], w, state);
       return dev(launch_decode_m1(da, stream), "mixer decode step");
     }
     const bool front = !c->gated && !c->fp_proj &&

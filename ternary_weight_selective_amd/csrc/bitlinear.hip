@@ -136,13 +136,6 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 // fastest) and its L2 serves the activation rows of few token tiles.
 constexpr int kBigStages = 4;  // LDS stages of k_gemm_i8_big (ST - 1 k steps in flight)
 
-// Wait until at most N vector-memory operations of this wave are outstanding (vmcnt only).
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 template <typename Tout, int BN, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_i8_big(GemmArgs a) {
   constexpr int BMT = 256, BKT = 64, ST = kBigStages;

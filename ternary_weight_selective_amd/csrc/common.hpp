@@ -35,6 +35,13 @@ template <typename T> __device__ __forceinline__ void st_act(T* p, float v);
 template <> __device__ __forceinline__ void st_act<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st_act<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding (vmcnt only).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Block barrier ordering LDS only: global loads still in flight are not waited for (for
 // phases that exchange data through LDS alone).
 __device__ __forceinline__ void bar_lds() {

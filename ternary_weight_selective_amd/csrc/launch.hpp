@@ -158,20 +158,27 @@ struct FrontArgs {
   int8_t* codes; int cw; double* deq;
 };
 bool front_supported(int Dm, int Di, int PW, int R);
-// ---- one decoding step of the Mamba-1 kind mixer, ternary projections (decode.hip)
+// ---- decoding steps of the Mamba-1 kind mixer, ternary projections (decode.hip): one token
+// per sequence through nl consecutive layers (the output of layer l is the input of l + 1)
+struct DecodeLayer {
+  const uint32_t* w_in; const float* s_in; const float* g_in;    // packed [Di, Dm / 16 words]
+  const uint32_t* w_x; const float* s_x; const float* g_x;       // packed [PW, Di / 16 words]
+  const uint32_t* w_dt; const float* s_dt; const float* g_dt;    // packed [Di, w_dt_row_words]
+  const float* dt_bias; const float* A; const float* D;          // [Di], [Di, NS], [Di]
+  const uint32_t* w_out; const float* s_out; const float* g_out;  // packed [Dm, Di / 16 words]
+  float* state;                                                  // [B, Di, NS], read and written
+  int gains;  // bit 0 .. 3: g_in, g_x, g_out, g_dt given
+};
+constexpr int kDecMaxLayers = 24;  // layers per launch (the kernel argument holds their pointers)
 struct DecodeArgs {
   int64_t B;                     // sequences (one token each)
   int Dm, Di, NS, R, PW;         // d_model, d_inner, d_state, dt_rank, x_proj width (R + 2 NS)
   int act_bf16;
   const void* u; void* out; int add_residual;  // [B, Dm] of the activation type
-  const uint32_t* w_in; const float* s_in; const float* g_in;    // packed [Di, Dm / 16 words]
-  const uint32_t* w_x; const float* s_x; const float* g_x;       // packed [PW, Di / 16 words]
-  const uint32_t* w_dt; int64_t w_dt_row_words; const float* s_dt; const float* g_dt;  // [Di, ...]
-  const float* dt_bias; const float* A; const float* D;          // [Di], [Di, NS], [Di]
-  const uint32_t* w_out; const float* s_out; const float* g_out;  // packed [Dm, Di / 16 words]
+  int64_t w_dt_row_words;
   float eps;
-  float* state;                  // [B, Di, NS], read and written
-  void* x;                       // [B, Di] workspace of the activation type
+  int nl;                        // layers, 1 .. kDecMaxLayers
+  DecodeLayer layer[kDecMaxLayers];
 };
 bool decode_supported(int Dm, int Di, int NS, int R, int PW);
 hipError_t launch_decode_m1(const DecodeArgs& a, hipStream_t s);

@@ -204,6 +204,30 @@ def test_mixer_step_rejects():
                 None) == NULL  # the convolution's state is required
 
 
+def test_mixer_stack_step_rejects():
+    L = tws.lib()
+    w = tws.MixerWeights()
+    for name, _ in tws.MixerWeights._fields_:
+        setattr(w, name, FAKE)
+    good = tws.mixer_config(0, 64, 128, 16, dt_rank=8)
+    nb = L.ssm_mixer_stack_workspace_bytes(ctypes.byref(good), 2)
+    assert nb >= L.ssm_mixer_workspace_bytes(ctypes.byref(good), 2, 1) + 2 * 2 * 64 * 4
+    ws = (ctypes.POINTER(tws.MixerWeights) * 2)(ctypes.pointer(w), ctypes.pointer(w))
+    st = (ctypes.c_void_p * 2)(FAKE + 8192, FAKE + 16384)
+    step = L.ssm_mixer_stack_step
+    assert step(ctypes.byref(good), ws, 0, FAKE, FAKE + 4096, 2, st, None, 1, FAKE, nb, None) == SHAPE
+    assert step(ctypes.byref(good), None, 2, FAKE, FAKE + 4096, 2, st, None, 1, FAKE, nb, None) == NULL
+    assert step(ctypes.byref(good), ws, 2, FAKE, FAKE + 4096, 2, None, None, 1, FAKE, nb, None) == NULL
+    assert step(ctypes.byref(good), ws, 2, FAKE, FAKE + 4096, 2, st, None, 1, FAKE, nb - 1, None) == WORKSPACE
+    assert step(ctypes.byref(good), ws, 2, FAKE, FAKE + 4096, 2, st, None, 1, FAKE + 8, nb, None) == ALIGN
+    assert step(ctypes.byref(good), ws, 2, FAKE, FAKE, 2, st, None, 0, FAKE, nb, None) == SHAPE
+    bad = tws.mixer_config(0, 64, 128, 16, dt_rank=0)
+    assert step(ctypes.byref(bad), ws, 2, FAKE, FAKE + 4096, 2, st, None, 1, FAKE, nb, None) == UNSUPPORTED
+    assert L.ssm_mixer_stack_workspace_bytes(ctypes.byref(bad), 2) == 0
+    # nothing to do for an empty batch
+    assert step(ctypes.byref(good), ws, 2, None, None, 0, st, None, 1, FAKE, nb, None) == 0
+
+
 def test_mixer_gated_needs_conv_weights_and_room():
     L = tws.lib()
     w = tws.MixerWeights()

@@ -629,6 +629,50 @@ def test_mixer_decode_step_equals_prefill(name, over, seed):
     assert bool(torch.isfinite(state).all())
 
 
+STACK_CASES = [  # (config, overrides, layers, seed)
+    ("trissm", dict(batch=3, seqlen=4), 5, 31),           # one fused launch
+    ("trissm", dict(batch=1, seqlen=3), 26, 32),          # two fused launches (24 + 2 layers)
+    ("trissm", dict(batch=64, seqlen=2), 12, 36),         # the decode measurement's stack
+    ("ternaryssm50m", dict(batch=2, seqlen=3), 3, 33),    # bf16, d_model 512, d_inner 1024, dt_rank 32
+    ("bitssm_tiny", dict(seqlen=3), 2, 37),
+    ("trissm_gated", dict(batch=2, seqlen=3), 3, 34),     # layer by layer (gated block)
+    ("mamba2_ssd", dict(d_model=256, d_inner=256, d_state=64, nheads=4, headdim=64, batch=2, seqlen=3), 2, 35),
+]
+
+
+@pytest.mark.parametrize("name,over,layers,seed", STACK_CASES)
+def test_mixer_stack_step_equals_layer_steps(name, over, layers, seed):
+    """ssm_mixer_stack_step equals ssm_mixer_step applied layer after layer, bit for bit, in the
+    outputs of every token and in every layer's state afterwards."""
+    cfg = wl.CONFIGS[name].with_(layers=layers, **over)
+    lat, u = wl.mixer_problem(cfg, seed=seed, layers=layers)
+    if cfg.act_dtype == "bf16":
+        u = bf16_values(u)
+    gws = [quantize_layer(cfg, lat[i])[0] for i in range(layers)]
+    c = gpu_config(cfg)
+    ud = to_dev(u, torch_dtype(cfg))
+    B, L, _ = ud.shape
+    shape = (B, cfg.d_inner, cfg.d_state) if cfg.kind == wl.MAMBA1 else (B, cfg.nheads, cfg.headdim, cfg.d_state)
+    st1 = [torch.zeros(shape, dtype=torch.float32, device=DEV) for _ in range(layers)]
+    st2 = [torch.zeros(shape, dtype=torch.float32, device=DEV) for _ in range(layers)]
+    conv = cfg.gated and cfg.d_conv > 1
+    cshape = (B, cfg.d_conv - 1, cfg.conv_channels)
+    cs1 = [torch.zeros(cshape, dtype=torch.float32, device=DEV) if conv else None for _ in range(layers)]
+    cs2 = [torch.zeros(cshape, dtype=torch.float32, device=DEV) for _ in range(layers)] if conv else None
+    mws = [tws.mixer_weights(g) for g in gws]
+    ws1 = torch.empty(tws.ssm_mixer_workspace_bytes(c, B, 1), dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty(tws.ssm_mixer_stack_workspace_bytes(c, B), dtype=torch.uint8, device=DEV)
+    for t in range(L):
+        tok = ud[:, t].contiguous()
+        h = tok
+        for i in range(layers):
+            h = tws.ssm_mixer_step(c, mws[i], h, st1[i], add_residual=True, workspace=ws1, conv_state=cs1[i])
+        o = tws.ssm_mixer_stack_step(c, mws, tok, st2, add_residual=True, workspace=ws2, conv_states=cs2)
+        np.testing.assert_array_equal(host(o), host(h), err_msg=f"token {t}")
+    for i in range(layers):
+        np.testing.assert_array_equal(host(st2[i]), host(st1[i]), err_msg=f"state of layer {i}")
+
+
 # ------------------------------------------------------------------ gated block
 
 def _ulp_diff(got, ref, bf16: bool):
