@@ -39,6 +39,9 @@ __global__ __launch_bounds__(512) void k_m1_front(FrontArgs f) {
   __shared__ __align__(16) int8_t s_q1[2][BR * QS1];
   __shared__ double s_deq1[2][BR];
   __shared__ __align__(16) float s_x[BR * DIM];
+  // element (r, c) of x in s_x: the 16-byte granule c / 4 of row r at position (c / 4) ^ (r mod 8),
+  // so that the in_proj epilogue's 16-byte writes (16 rows at one column) spread over the banks
+  auto xs = [](int r, int c) { return r * DIM + ((((c >> 2) ^ (r & 7))) << 2) + (c & 3); };
   __shared__ __align__(16) int8_t s_q2[BR * QS2];
   __shared__ double s_deq2[BR];
   __shared__ float s_dr[BR * FRMAX];
@@ -197,8 +200,7 @@ __global__ __launch_bounds__(512) void k_m1_front(FrontArgs f) {
           T o[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) st_act(&o[q], (float)((sw1 * (double)acc[j][q]) * deq));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) s_x[lm * DIM + n + q] = ld_act(&o[q]);
+          *(float4*)(&s_x[xs(lm, n)]) = make_float4(ld_act(&o[0]), ld_act(&o[1]), ld_act(&o[2]), ld_act(&o[3]));
           if (m < M) {
             if (vx && n + 3 < Di) {
               *(typename V4<T>::type*)(X + m * Di + n) = *(const typename V4<T>::type*)o;
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(512) void k_m1_front(FrontArgs f) {
         const int r = wave * 2 + rr;
         const bool rv = m0 + r < M;
 #pragma unroll
-        for (int i = 0; i < KPL2; ++i) v[rr][i] = rv ? s_x[r * DIM + lane + 64 * i] : 0.0f;
+        for (int i = 0; i < KPL2; ++i) v[rr][i] = rv ? s_x[xs(r, lane + 64 * i)] : 0.0f;
       }
       norm_quant_rows<2, KPL2>(v, gn2, Di, f.eps, &s_q2[wave * 2 * QS2], QS2, &s_deq2[wave * 2], lane);
     }
