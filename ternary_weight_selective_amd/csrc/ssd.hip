@@ -123,8 +123,10 @@ __global__ __launch_bounds__(256) void k_scan_ssd_rec(ScanArgs a) {
 // every segment from its true incoming state, writing y.
 //
 // Per chunk, everything is matrix products on 16 x 16 x 32 bf16 MFMAs in transposed form, so
-// that no product's result goes through LDS to become another's operand:
-//   G^T = B C^T                       (A: B rows, B-operand: C rows; both staged row-major)
+// that no per-head product's result goes through LDS to become another's operand:
+//   G^T = B C^T                       (A: B rows, B-operand: C rows; both staged row-major;
+//                                       the same for every head: computed once per block and
+//                                       shared through LDS)
 //   M^T = G^T (.) exp(cs_t - cs_s) dt_s on s <= t, plus D on the diagonal (the D x term)
 //   y^T = x^T M^T + exp(cs_t) (h C^T)  (x^T staged transposed; M^T and h straight from the
 //                                       accumulators of G^T and of the state)
@@ -132,8 +134,11 @@ __global__ __launch_bounds__(256) void k_scan_ssd_rec(ScanArgs a) {
 // An accumulator tile holds, per lane, 4 consecutive rows of one column; two such tiles give
 // the 8 reduction slots a lane feeds to a 16 x 16 x 32 MFMA, in a permuted order of the
 // reduction index that the other operand's lane reads in the same order (a sum over k does not
-// depend on the order).  fp32 operands (M^T, h, w x) enter as two bf16 terms: the truncated
-// value and the truncated remainder, about 16 significant bits; bf16 activations as they are.
+// depend on the order).  Precision: bf16 activations enter as they are; the fp32 operands of
+// the readout (M^T and h, whose products only feed the bf16 output y) are rounded to bf16,
+// nearest even; the state update's fp32 operand w x enters as two bf16 terms, the truncated
+// value and the truncated remainder (about 16 significant bits), so that the carried fp32 state
+// keeps that accuracy.
 namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 // softplus(v) = log(1 + e^v) (the identity above 20) on the hardware exp2 / log2, with the
@@ -381,9 +386,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       s_dt[hl][lane] = dt;
       s_w[hl][lane] = __builtin_amdgcn_exp2f(cs_end - cs) * dt;
       s_et[hl][lane] = __builtin_amdgcn_exp2f(cs);
-      // decay from step s to the last step of its 16-step tile, times dt_s (at most dt_s: cs
-      // does not increase with dt >= 0 and A <= 0, and in general the two factors of a decay
-      // split at a tile's end have the sign of the whole)
+      // the decay from step s to the last step e of its 16-step tile, times dt_s: the factor of
+      // exp2(cs_t - cs_s) = exp2(cs_t - cs_e) exp2(cs_e - cs_s) that depends on s alone (cs is
+      // monotone, dt >= 0, so neither factor leaves the range of the whole)
       if (!LOCAL) s_b[hl][lane] = __builtin_amdgcn_exp2f(__shfl(cs, lane | 15, 64) - cs) * dt;
     }
   };
