@@ -180,6 +180,16 @@ ssm_status scan_check(const ssm_scan_args* a) {
   if (a->dt_codes && (!proj || !a->dt_deq))
     return fail(SSM_ERR_NULL, "scan: dt_codes needs dt_in (for dt_rank) and dt_deq");
   if (a->dt_codes && !aligned(a->dt_codes, 16)) return fail(SSM_ERR_ALIGN, "scan: dt_codes must be 16-byte aligned");
+  if (a->a_per_state == 1) {  // the Mamba-1 kind kernel addresses one sequence of a tensor with 32-bit byte offsets
+    int64_t ld = a->ld_x > a->ld_y ? a->ld_x : a->ld_y;
+    if (a->ld_B > ld) ld = a->ld_B;
+    if (a->ld_C > ld) ld = a->ld_C;
+    if (!proj && a->ld_delta > ld) ld = a->ld_delta;
+    if (a->gate && a->ld_gate > ld) ld = a->ld_gate;
+    if (ld < 64) ld = 64;  // the dt codes: <= 64 bytes per token
+    if (a->seqlen * ld * (int64_t)act_size(a->act_dtype) >= (int64_t(1) << 31))
+      return fail(SSM_ERR_UNSUPPORTED, "scan: one sequence spans 2 GiB or more of a tensor");
+  }
   return SSM_OK;
 }
 
@@ -254,6 +264,9 @@ ssm_status mix_plan(const ssm_mixer_config* c, int64_t batch, int64_t seqlen, Mi
     if (c->fp_proj == 2) { p->off_dl = off; off = align_up(off + (size_t)p->M * c->d_inner * as); }  // stored dt
     p->off_y = off; off = align_up(off + (size_t)p->M * c->d_inner * as);
     p->off_scan = off;
+    const int64_t wmax = p->XW > p->PW ? p->XW : p->PW;  // widest row the scan reads (32-bit offsets per sequence)
+    if (seqlen * (wmax > 64 ? wmax : 64) * (int64_t)as >= (int64_t(1) << 31))
+      return fail(SSM_ERR_UNSUPPORTED, "mixer: one sequence spans 2 GiB or more of an activation tensor");
   } else if (c->kind == SSM_MIXER_SSD) {
     if (c->nheads < 1 || c->headdim < 1 || c->nheads * c->headdim != c->d_inner)
       return fail(SSM_ERR_SHAPE, "mixer: nheads * headdim must equal d_inner");

@@ -35,6 +35,29 @@ template <typename T> __device__ __forceinline__ void st_act(T* p, float v);
 template <> __device__ __forceinline__ void st_act<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st_act<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// A buffer resource over [base, base + bytes): loads past the end read zeros, stores past it
+// are dropped; offsets are 32-bit byte offsets (a per-lane part and a wave-uniform part).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutside = 0x80000000u;  // an offset past any resource here (all < 2^31 bytes)
+// One activation element (fp32 or bf16 bits) at byte offset voff + soff.
+template <typename T> __device__ __forceinline__ T buf_ld_act(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <> __device__ __forceinline__ float buf_ld_act<float>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+template <> __device__ __forceinline__ bf16_t buf_ld_act<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (bf16_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+// Store v as an activation (fp32, or bf16 rounded to nearest even).
+template <typename T> __device__ __forceinline__ void buf_st_act(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <> __device__ __forceinline__ void buf_st_act<float>(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ void buf_st_act<bf16_t>(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, voff, soff, 0);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding (vmcnt only).
 template <int N>
 __device__ __forceinline__ void vm_wait() {

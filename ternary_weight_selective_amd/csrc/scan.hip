@@ -98,6 +98,11 @@ struct DtCodes {
 //   5. runs the recurrence over tile i, writing its partials.
 // A buffer of tile i is rewritten at tile i + 2, after the barrier of tile i + 1 that every
 // wave reaches only once it has finished with tile i.
+// Memory is reached through buffer resources over the block's sequence: a wave-uniform row
+// offset plus a per-lane column offset, no per-item address arithmetic or branches; rows past
+// the sequence end read zeros and their stores are dropped.  A tile that ends past the
+// sequence runs its missing steps with dt = 0 (the state is left unchanged).  Lanes past the
+// last channel take the last channel's parameters and store nothing.
 // MODE 1 (LOCAL): pass 1 (zero start, no readout; writes the chunk's end state and sum(dt)).
 // MODE 2 (GATE): the readout is multiplied by SiLU of the gate input before it is stored.
 template <int NS, typename T, int RW, int MODE>
@@ -111,6 +116,7 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   constexpr int XPT = TT * CPB / 256;                    // (step, channel) items per thread
   constexpr int BPT = (TT * NS + 255) / 256;             // B (and C) elements per thread per tile
   constexpr int RWQ = FUSED ? RW : 1;
+  constexpr uint32_t S = sizeof(T);
   __shared__ float2 s_dd[2][TT][CPB];  // (dt, dt * x)
   __shared__ __align__(16) float s_B[2][TT][NS];
   __shared__ __align__(16) float s_C[LOCAL ? 1 : 2][LOCAL ? 1 : TT][NS];
@@ -121,21 +127,48 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   const int64_t Di = a.H, L = a.L;
   const int64_t b = blockIdx.x;   // sequence fastest: the channel tiles of a sequence share an XCD
   const int chunk = blockIdx.z;
-  const int64_t tb = (int64_t)chunk * ch.chunk_len;
-  const int64_t te = (tb + ch.chunk_len < L) ? tb + ch.chunk_len : L;
+  // step indices within the sequence are 32-bit (a sequence spans less than 2^31 bytes)
+  const int tb = __builtin_amdgcn_readfirstlane((int)(chunk * ch.chunk_len));
+  const int te = __builtin_amdgcn_readfirstlane((int)((chunk * ch.chunk_len + ch.chunk_len < L) ? chunk * ch.chunk_len + ch.chunk_len : L));
   const int64_t d0 = (int64_t)blockIdx.y * CPB;
   const int64_t d = d0 + lane;
   const bool dv = d < Di;
-  // staging role: thread -> (channel lane, steps w, w + 4, ...).  Lanes past the last channel
-  // take the per-channel parameters of the last channel (their results are never stored), so
-  // the loads below have no lane-dependent branches and are all in flight together.
+  // per-channel parameters: lanes past the last channel take the last channel's (their results
+  // are never stored), so these loads have no lane-dependent branches
   const int64_t dcl = dv ? d : Di - 1;
   const float bias_s = a.delta_bias ? a.delta_bias[dcl] : 0.0f;
   const float D_s = a.D ? a.D[dcl] : 0.0f;
   constexpr int cw = 16 * RW;  // code bytes per token
 
-  const T* X = (const T*)a.x;
-  const T* DL = (const T*)a.delta;
+  // buffer resources over sequence b (rows 0 .. L - 1; activation tensors from channel d0)
+  const int64_t row0 = b * L;
+  const int64_t nch = Di - d0;
+  auto act_rsrc = [&](const void* p, int64_t ld) {
+    return buf_rsrc((const T*)p + row0 * ld + d0, (uint32_t)(((L - 1) * ld + nch) * S));
+  };
+  const auto rX = act_rsrc(a.x, a.ld_x);
+  const auto rDL = act_rsrc(FUSED ? a.x : a.delta, FUSED ? a.ld_x : a.ld_delta);
+  const auto rZ = act_rsrc(GATE ? a.gate : a.x, GATE ? a.ld_gate : a.ld_x);
+  const auto rY = act_rsrc(a.y, a.ld_y);
+  const auto rB = buf_rsrc((const T*)a.Bm + row0 * a.ld_B, (uint32_t)(((L - 1) * a.ld_B + NS) * S));
+  const auto rC = buf_rsrc((const T*)a.Cm + row0 * a.ld_C, (uint32_t)(((L - 1) * a.ld_C + NS) * S));
+  const auto rQ = buf_rsrc(FUSED ? dc.codes + row0 * cw : nullptr, FUSED ? (uint32_t)(L * cw) : 0u);
+  const auto rF = buf_rsrc(FUSED ? dc.deq + row0 : nullptr, FUSED ? (uint32_t)(L * 8) : 0u);
+  const auto rG = buf_rsrc(dc.dbg_acc ? dc.dbg_acc + row0 * Di + d0 : nullptr,
+                           dc.dbg_acc ? (uint32_t)(((L - 1) * Di + nch) * 4) : 0u);
+  const uint32_t vlane = (uint32_t)lane * S;
+  // row strides in bytes (wave-uniform)
+  const uint32_t sx = (uint32_t)a.ld_x * S, sdl = (uint32_t)(FUSED ? a.ld_x : a.ld_delta) * S;
+  const uint32_t sz = (uint32_t)(GATE ? a.ld_gate : a.ld_x) * S, sy = (uint32_t)a.ld_y * S;
+  const uint32_t sb = (uint32_t)a.ld_B * S, sc = (uint32_t)a.ld_C * S;
+  // B and C: thread -> elements (t, n) = divmod(tid + 256 i, NS) of a tile
+  uint32_t vb[BPT], vc[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const int e = tid + 256 * i, t = e / NS, n = e % NS;
+    vb[i] = e < TT * NS ? (uint32_t)t * sb + (uint32_t)n * S : kOutside;
+    vc[i] = e < TT * NS ? (uint32_t)t * sc + (uint32_t)n * S : kOutside;
+  }
 
   v4i wdt[4];
   float s_dt = 0.0f;
@@ -168,59 +201,48 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
 
   // prefetch registers for the next tile: x (and delta) of the thread's items, B, C, the
   // items' dt codes (a whole wave reads the same token row) and dequantisation factors
-  // (raw activation elements: a conditional load that is converted at once makes the compiler
-  // wait for it inside the condition, one round trip per load)
   T rx[XPT], rd[FUSED ? 1 : XPT], rb[BPT], rc[BPT], rz[GATE ? XPT : 1];
   v4i rq[FUSED ? XPT : 1][RWQ];
   double rf[FUSED ? XPT : 1];
-  auto load_tile = [&](int64_t t0) {
+  auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
-      const int t = w + 4 * i;
-      const bool okt = t0 + t < te;
-      const bool ok = okt && dv;
-      const int64_t tok = b * L + t0 + t;
-      rx[i] = ok ? X[tok * a.ld_x + d] : T(0);
-      if (GATE) rz[GATE ? i : 0] = ok ? ((const T*)a.gate)[tok * a.ld_gate + d] : T(0);
-      if (!FUSED) rd[FUSED ? 0 : i] = ok ? DL[tok * a.ld_delta + d] : T(0);
+      const uint32_t row = (uint32_t)(t0 + w + 4 * i);
+      rx[i] = buf_ld_act<T>(rX, vlane, row * sx);
+      if (GATE) rz[GATE ? i : 0] = buf_ld_act<T>(rZ, vlane, row * sz);
+      if (!FUSED) rd[FUSED ? 0 : i] = buf_ld_act<T>(rDL, vlane, row * sdl);
       if (FUSED) {
 #pragma unroll
         for (int q = 0; q < RWQ; ++q)
-          rq[FUSED ? i : 0][q] = okt ? ((const v4i*)(dc.codes + tok * cw))[q] : v4i{0, 0, 0, 0};
-        rf[FUSED ? i : 0] = okt ? dc.deq[tok] : 0.0;
+          rq[FUSED ? i : 0][q] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rQ, 16u * q, row * cw, 0));
+        rf[FUSED ? i : 0] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(rF, 0u, row * 8u, 0));
       }
     }
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
-      const int e = tid + 256 * i, t = e / NS, n = e % NS;
-      const bool ok = (e < TT * NS) && (t0 + t < te);
-      const int64_t tok = b * L + t0 + t;
-      rb[i] = ok ? ((const T*)a.Bm)[tok * a.ld_B + n] : T(0);
-      rc[i] = (ok && !LOCAL) ? ((const T*)a.Cm)[tok * a.ld_C + n] : T(0);
+      rb[i] = buf_ld_act<T>(rB, vb[i], (uint32_t)t0 * sb);
+      if (!LOCAL) rc[i] = buf_ld_act<T>(rC, vc[i], (uint32_t)t0 * sc);
     }
   };
 
   float xprev[XPT];  // x of the previous tile's items, for D x
   float zprev[GATE ? XPT : 1];  // and their gate inputs
-  int64_t tprev = -1;  // first step of the tile whose readout is pending
-  auto store_y = [&](int buf, int64_t t0p) {
-    T* Y = (T*)a.y;
+  int tprev = -1;  // first step of the tile whose readout is pending
+  auto store_y = [&](int buf, int t0p) {
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int t = w + 4 * i;
-      if ((t0p + t < te) && dv) {
-        const float y = ((s_yp[LOCAL ? 0 : buf][0][t][lane] + s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 1][t][lane]) +
-                         s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 2][t][lane]) + s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 3][t][lane];
-        float yo = y + D_s * xprev[i];
-        if (GATE) yo = yo * silu_gate(zprev[GATE ? i : 0]);
-        st_act(Y + (b * L + t0p + t) * a.ld_y + d, yo);
-      }
+      const float y = ((s_yp[LOCAL ? 0 : buf][0][t][lane] + s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 1][t][lane]) +
+                       s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 2][t][lane]) + s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : 3][t][lane];
+      float yo = y + D_s * xprev[i];
+      if (GATE) yo = yo * silu_gate(zprev[GATE ? i : 0]);
+      if (dv) buf_st_act<T>(yo, rY, vlane, (uint32_t)(t0p + t) * sy);
     }
   };
 
   load_tile(tb);
   int buf = 0;
-  for (int64_t t0 = tb; t0 < te; t0 += TT, buf ^= 1) {
+  for (int t0 = tb; t0 < te; t0 += TT, buf ^= 1) {
     // 1. stage this tile: B, C; per item dt, softplus, dt * x
     float xcur[XPT], zcur[GATE ? XPT : 1];
 #pragma unroll
@@ -236,13 +258,15 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
         for (int q = 0; q < RW; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(rq[FUSED ? i : 0][q][j], wdt[q][j], acc, false);
-        if (!LOCAL && dc.dbg_acc && dv && t0 + t < te) dc.dbg_acc[(b * L + t0 + t) * Di + d] = acc;
+        if (!LOCAL && dc.dbg_acc && dv)
+          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc, rG, (uint32_t)lane * 4u, (uint32_t)(t0 + t) * (uint32_t)Di * 4u, 0);
         dtv = (s_dt * (float)acc) * (float)rf[FUSED ? i : 0];
       } else {
         dtv = act_f32(rd[FUSED ? 0 : i]);
       }
       dtv += bias_s;
       if (a.softplus) dtv = softplus_f(dtv);
+      if (t0 + t >= te) dtv = 0.0f;  // past the sequence end: the state stays as it is
       s_dd[buf][t][lane] = make_float2(dtv, dtv * xv);
     }
 #pragma unroll
@@ -268,54 +292,37 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
     // 5. recurrence.  B and C of a step are the same for the whole wave (broadcast LDS reads);
     //    groups of GQ steps, software-pipelined: the LDS reads of group g + 1 are issued before
     //    the arithmetic of group g
-    const int tmax = (int)((te - t0) < TT ? (te - t0) : TT);
-    if (tmax == TT) {
-      constexpr int GQ = 4, NG = TT / GQ;
-      float bq[2][GQ][SPL], cq[2][GQ][SPL];
-      float2 dd[2][GQ];
-      auto ld = [&](int tt, int sl) {
+    constexpr int GQ = 4, NG = TT / GQ;
+    float bq[2][GQ][SPL], cq[2][GQ][SPL];
+    float2 dd[2][GQ];
+    auto ld = [&](int tt, int sl) {
 #pragma unroll
-        for (int u = 0; u < GQ; ++u) {
-          const int t = tt + u;
+      for (int u = 0; u < GQ; ++u) {
+        const int t = tt + u;
 #pragma unroll
-          for (int i = 0; i < SPL; ++i) {
-            bq[sl][u][i] = s_B[buf][t][w * SPL + i];
-            if (!LOCAL) cq[sl][u][i] = s_C[LOCAL ? 0 : buf][LOCAL ? 0 : t][w * SPL + i];
-          }
-          dd[sl][u] = s_dd[buf][t][lane];
+        for (int i = 0; i < SPL; ++i) {
+          bq[sl][u][i] = s_B[buf][t][w * SPL + i];
+          if (!LOCAL) cq[sl][u][i] = s_C[LOCAL ? 0 : buf][LOCAL ? 0 : t][w * SPL + i];
         }
-      };
-      ld(0, 0);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int sl = g & 1;
-        if (g + 1 < NG) ld((g + 1) * GQ, sl ^ 1);
-#pragma unroll
-        for (int u = 0; u < GQ; ++u) {
-          float yp = 0.0f;
-#pragma unroll
-          for (int i = 0; i < SPL; ++i) {
-            const float ab = __builtin_amdgcn_exp2f(dd[sl][u].x * Al[i]);
-            h[i] = __builtin_fmaf(ab, h[i], dd[sl][u].y * bq[sl][u][i]);
-            if (!LOCAL) yp = i == 0 ? cq[sl][u][0] * h[0] : __builtin_fmaf(cq[sl][u][i], h[i], yp);
-          }
-          if (LOCAL) sum_dt += dd[sl][u].x;
-          else s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : w][LOCAL ? 0 : g * GQ + u][lane] = yp;
-        }
+        dd[sl][u] = s_dd[buf][t][lane];
       }
-    } else {
-      for (int t = 0; t < tmax; ++t) {
-        const float2 ddt = s_dd[buf][t][lane];
+    };
+    ld(0, 0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int sl = g & 1;
+      if (g + 1 < NG) ld((g + 1) * GQ, sl ^ 1);
+#pragma unroll
+      for (int u = 0; u < GQ; ++u) {
         float yp = 0.0f;
 #pragma unroll
         for (int i = 0; i < SPL; ++i) {
-          const float ab = __builtin_amdgcn_exp2f(ddt.x * Al[i]);
-          h[i] = __builtin_fmaf(ab, h[i], ddt.y * s_B[buf][t][w * SPL + i]);
-          if (!LOCAL) yp = i == 0 ? s_C[LOCAL ? 0 : buf][LOCAL ? 0 : t][w * SPL] * h[0]
-                                  : __builtin_fmaf(s_C[LOCAL ? 0 : buf][LOCAL ? 0 : t][w * SPL + i], h[i], yp);
+          const float ab = __builtin_amdgcn_exp2f(dd[sl][u].x * Al[i]);
+          h[i] = __builtin_fmaf(ab, h[i], dd[sl][u].y * bq[sl][u][i]);
+          if (!LOCAL) yp = i == 0 ? cq[sl][u][0] * h[0] : __builtin_fmaf(cq[sl][u][i], h[i], yp);
         }
-        if (LOCAL) sum_dt += ddt.x;
-        else s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : w][LOCAL ? 0 : t][lane] = yp;
+        if (LOCAL) sum_dt += dd[sl][u].x;
+        else s_yp[LOCAL ? 0 : buf][LOCAL ? 0 : w][LOCAL ? 0 : g * GQ + u][lane] = yp;
       }
     }
   }

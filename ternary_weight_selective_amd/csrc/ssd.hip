@@ -206,12 +206,6 @@ __device__ __forceinline__ v8bf ld44(const uint16_t* p0, const uint16_t* p1) {
   const uint2 a = *(const uint2*)p0, b = *(const uint2*)p1;
   return __builtin_bit_cast(v8bf, v4i{(int)a.x, (int)a.y, (int)b.x, (int)b.y});
 }
-// A buffer resource over [base, base + bytes): loads past the end read zeros, stores past it
-// are dropped; offsets are 32-bit byte offsets per lane.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-constexpr uint32_t kOutside = 0x80000000u;  // an offset past any resource here
 __device__ __forceinline__ v4i buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
