@@ -13,8 +13,9 @@
 // Every value is computed as the whole-sequence path computes it: the same fixed-order norms
 // and absmax quantisation, the same int32 sums, the same fp64 epilogues rounded once to the
 // activation type, the same in-scan dt dequantisation in fp32, softplus, exp2 recurrence and
-// readout order (four groups of NS / 4 states, each accumulated by fused multiply-adds, the
-// groups added in order, then D x).
+// readout order (d_state 16: eight state pairs, each an fma chain, summed in the scan's
+// in-wave tree; otherwise four groups of NS / 4 states, each accumulated by fused
+// multiply-adds, the groups added in order; then D x).
 #include "launch.hpp"
 
 namespace ssm {
@@ -353,17 +354,32 @@ __global__ __launch_bounds__(512) void k_dec_stack(DecodeArgs a) {
         const float xv = s_v[c];
         const float ddy = dtv * xv;
         float y = 0.0f;
+        if constexpr (NS == 16) {  // eight state pairs, summed in the scan's in-wave tree
+          float pp[8];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float yp = 0.0f;
+          for (int g = 0; g < 8; ++g) {
 #pragma unroll
-          for (int i = 0; i < SPL; ++i) {
-            const int n = g * SPL + i;
-            const float ab = __builtin_amdgcn_exp2f(dtv * (Al[j][n] * LOG2E));
-            h[j][n] = __builtin_fmaf(ab, h[j][n], ddy * Bv[n]);
-            yp = i == 0 ? Cv[n] * h[j][n] : __builtin_fmaf(Cv[n], h[j][n], yp);
+            for (int i = 0; i < 2; ++i) {
+              const int n = 2 * g + i;
+              const float ab = __builtin_amdgcn_exp2f(dtv * (Al[j][n] * LOG2E));
+              h[j][n] = __builtin_fmaf(ab, h[j][n], ddy * Bv[n]);
+            }
+            pp[g] = __builtin_fmaf(Cv[2 * g + 1], h[j][2 * g + 1], Cv[2 * g] * h[j][2 * g]);
           }
-          y = g == 0 ? yp : y + yp;
+          y = ((pp[0] + pp[4]) + (pp[2] + pp[6])) + ((pp[1] + pp[5]) + (pp[3] + pp[7]));
+        } else {  // four groups of NS / 4 states, added in order
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float yp = 0.0f;
+#pragma unroll
+            for (int i = 0; i < SPL; ++i) {
+              const int n = g * SPL + i;
+              const float ab = __builtin_amdgcn_exp2f(dtv * (Al[j][n] * LOG2E));
+              h[j][n] = __builtin_fmaf(ab, h[j][n], ddy * Bv[n]);
+              yp = i == 0 ? Cv[n] * h[j][n] : __builtin_fmaf(Cv[n], h[j][n], yp);
+            }
+            y = g == 0 ? yp : y + yp;
+          }
         }
         const float yo = y + Dc[j] * xv;
         T r;

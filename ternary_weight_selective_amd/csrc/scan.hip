@@ -342,6 +342,250 @@ __global__ __launch_bounds__(256, 2) void k_scan_m1(ScanArgs a, ChunkArgs ch, Dt
   }
 }
 
+// d_state 16: the states of a channel are split over lanes instead of waves.  Lane l of a wave
+// holds channel c = l mod 8 of the wave's 8 channels and the state pair (2g, 2g + 1), g = l / 8;
+// a block is 4 waves (32 channels).  A layer at the TriSSM shape is then 4096 waves, four per
+// SIMD (measured: the VALU issues the recurrence ~1.25x faster than with two), and the readout
+// sum over the 8 pairs stays inside the wave: the 8 steps of a tile are reduced and scattered
+// at once (lanes 32 apart, then 16 with the permlane swaps, then 8 with a row rotation), after
+// which lane (g, c) holds the whole readout of step bitrev3(g) of channel c.  Each pairwise sum
+// adds the same two operands on both lanes, so y = ((p0 + p4) + (p2 + p6)) + ((p1 + p5) +
+// (p3 + p7)) for the pair partials p (each an fma chain over its two states), then + D x.
+// The same lane stages that (step, channel) item: its dt (dot product of the step's dt codes
+// with the channel's ternary row, fp32 dequantisation, bias, softplus) and dt x into a
+// per-wave LDS area, and keeps x for D x; each wave stages the tile's B and C for itself, so
+// the waves never wait for one another (no block barrier).  Tiles of TT = 8 steps,
+// double-buffered LDS: per tile stage, request the tile after next into registers,
+// recurrence, readout.
+// MODE 1 (LOCAL): pass 1 of the chunked scan; MODE 2 (GATE): readout times SiLU(gate).
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// value of lane l ^ 8 (rotation of each 16-lane row by 8)
+__device__ __forceinline__ float xor8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+template <typename T, int RW, int MODE>
+__global__ __launch_bounds__(256, RW >= 3 ? 2 : 4) void k_scan_m1_g8(ScanArgs a, ChunkArgs ch, DtCodes dc) {
+  constexpr bool LOCAL = MODE == 1;
+  constexpr bool GATE = MODE == 2;
+  constexpr bool FUSED = RW > 0;
+  constexpr int NS = 16, SPL = 2, CPW = 8, NW = 4, CPB = CPW * NW, TT = 8;
+  constexpr int RWQ = FUSED ? RW : 1;
+  constexpr uint32_t S = sizeof(T);
+  constexpr int cw = 16 * RW;
+  // rows padded to TT + 2 steps: the 8 distinct 16-byte reads of a wave fall in distinct banks
+  __shared__ __align__(16) float s_B[2][NW][NS / SPL][TT + 2][SPL];  // [buf][wave][pair][step][state of the pair]
+  __shared__ __align__(16) float s_C[LOCAL ? 1 : 2][NW][NS / SPL][TT + 2][SPL];
+  __shared__ __align__(16) float2 s_dd[2][NW][CPW][TT + 2];      // [buf][wave][channel][step]: (dt, dt x)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 3, c = lane & 7;
+  const int si = ((g & 1) << 2) | (g & 2) | (g >> 2);  // the step this lane stages and reads out
+  const int64_t Di = a.H, L = a.L;
+  const int64_t b = blockIdx.x;
+  const int chunk = blockIdx.z;
+  const int tb = __builtin_amdgcn_readfirstlane((int)(chunk * ch.chunk_len));
+  const int te = __builtin_amdgcn_readfirstlane((int)((chunk * ch.chunk_len + ch.chunk_len < L) ? chunk * ch.chunk_len + ch.chunk_len : L));
+  const int64_t d0 = (int64_t)blockIdx.y * CPB + w * CPW;  // the wave's first channel
+  const int64_t d = d0 + c;
+  const bool dv = d < Di;
+  const int64_t dcl = dv ? d : Di - 1;
+  const float bias_s = a.delta_bias ? a.delta_bias[dcl] : 0.0f;
+  const float D_s = a.D ? a.D[dcl] : 0.0f;
+
+  // buffer resources over sequence b (activation tensors from channel d0)
+  const int64_t row0 = b * L;
+  const int64_t nch = Di - d0;
+  auto act_rsrc = [&](const void* p, int64_t ld) {
+    const int64_t n = (L - 1) * ld + nch;
+    return buf_rsrc((const T*)p + row0 * ld + d0, n > 0 ? (uint32_t)(n * S) : 0u);
+  };
+  const auto rX = act_rsrc(a.x, a.ld_x);
+  const auto rDL = act_rsrc(FUSED ? a.x : a.delta, FUSED ? a.ld_x : a.ld_delta);
+  const auto rZ = act_rsrc(GATE ? a.gate : a.x, GATE ? a.ld_gate : a.ld_x);
+  const auto rY = act_rsrc(a.y, a.ld_y);
+  // B and C of a tile, staged by each wave for itself (no barrier between waves): lane ->
+  // step bt = l / 8, state pair bp = l mod 8, elements (bt, 2 bp) and (bt, 2 bp + 1)
+  const int bt = lane >> 3, bp = lane & 7;
+  const auto rB = buf_rsrc((const T*)a.Bm + row0 * a.ld_B, (uint32_t)(((L - 1) * a.ld_B + NS) * S));
+  const auto rC = buf_rsrc((const T*)a.Cm + row0 * a.ld_C, (uint32_t)(((L - 1) * a.ld_C + NS) * S));
+  const uint32_t vb = ((uint32_t)bt * (uint32_t)a.ld_B + 2u * bp) * S, sb = (uint32_t)a.ld_B * S;
+  const uint32_t vc = ((uint32_t)bt * (uint32_t)a.ld_C + 2u * bp) * S, sc = (uint32_t)a.ld_C * S;
+  const auto rQ = buf_rsrc(FUSED ? dc.codes + row0 * cw : nullptr, FUSED ? (uint32_t)(L * cw) : 0u);
+  const auto rF = buf_rsrc(FUSED ? dc.deq + row0 : nullptr, FUSED ? (uint32_t)(L * 8) : 0u);
+  const auto rG = buf_rsrc(dc.dbg_acc ? dc.dbg_acc + row0 * Di + d0 : nullptr,
+                           (dc.dbg_acc && nch > 0) ? (uint32_t)(((L - 1) * Di + nch) * 4) : 0u);
+  const uint32_t sx = (uint32_t)a.ld_x * S, sdl = (uint32_t)(FUSED ? a.ld_x : a.ld_delta) * S;
+  const uint32_t sz = (uint32_t)(GATE ? a.ld_gate : a.ld_x) * S, sy = (uint32_t)a.ld_y * S;
+  // per-lane offsets of the lane's item (step si, channel c)
+  const uint32_t vx = (uint32_t)si * sx + (uint32_t)c * S, vdl = (uint32_t)si * sdl + (uint32_t)c * S;
+  const uint32_t vz = (uint32_t)si * sz + (uint32_t)c * S;
+  // stores: lanes past the last channel write outside their resource (dropped), so every store
+  // is issued unconditionally and the waits for loads stay exact counts
+  const uint32_t vy = dv ? (uint32_t)si * sy + (uint32_t)c * S : kOutside;
+  const uint32_t vg = dv ? ((uint32_t)si * (uint32_t)Di + (uint32_t)c) * 4u : kOutside;
+
+  v4i wdt[4];
+  float s_dt = 0.0f;
+  if (FUSED) {
+    s_dt = a.s_dt[0];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wdt[q] = unpack16_i8(q < RW ? a.w_dt[dcl * a.w_dt_row_words + q] : 0u);
+  }
+  const float* hsrc = nullptr;
+  int64_t hoff = 0;
+  if (!LOCAL) {
+    if (chunk == 0) {
+      hsrc = a.h0;
+      hoff = (b * Di + dcl) * NS;
+    } else {
+      hsrc = ch.st;
+      hoff = ((b * ch.nchunks + chunk - 1) * Di + dcl) * NS;
+    }
+  }
+  float Al[SPL], h[SPL];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    Al[i] = a.A[dcl * NS + SPL * g + i] * LOG2E;
+    h[i] = hsrc ? hsrc[hoff + SPL * g + i] : 0.0f;
+  }
+  float sum_dt = 0.0f;
+
+  // Register sets for two tiles: the loads of tile i + 2 are issued as tile i is staged, so a
+  // tile's data has two tiles of work to arrive.  Every load is unconditional (rows past the
+  // sequence read zeros), so the waits are exact counts, and tiles run in pairs: a tile wholly
+  // past the sequence end (odd tile count) runs with dt = 0 and stores nothing.
+  struct Regs {
+    T rx, rd, rz, rb0, rb1, rc0, rc1;
+    v4i rq[RWQ];
+    double rf;
+  };
+  Regs R0, R1;
+  auto load_tile = [&](Regs& r, int t0) {
+    const uint32_t tr = (uint32_t)t0;
+    r.rx = buf_ld_act<T>(rX, vx, tr * sx);
+    if (GATE) r.rz = buf_ld_act<T>(rZ, vz, tr * sz);
+    if (!FUSED) r.rd = buf_ld_act<T>(rDL, vdl, tr * sdl);
+    if (FUSED) {
+#pragma unroll
+      for (int q = 0; q < RWQ; ++q)
+        r.rq[q] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rQ, (uint32_t)si * cw + 16u * q, tr * cw, 0));
+      r.rf = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(rF, (uint32_t)si * 8u, tr * 8u, 0));
+    }
+    r.rb0 = buf_ld_act<T>(rB, vb, tr * sb);
+    r.rb1 = buf_ld_act<T>(rB, vb + S, tr * sb);
+    if (!LOCAL) {
+      r.rc0 = buf_ld_act<T>(rC, vc, tr * sc);
+      r.rc1 = buf_ld_act<T>(rC, vc + S, tr * sc);
+    }
+  };
+
+  auto run_tile = [&](Regs& r, int t0, int buf) {
+    // 1. stage: this lane's item, and the block's B and C.  x and the gate input are kept for
+    //    the readout in registers of their own (a copy), so that the loads of the tile after
+    //    next can refill r in place (otherwise the compiler rotates the register sets across
+    //    iterations and waits for those loads at the end of each pair)
+    float xv, zv = 0.0f;
+    asm("v_mov_b32 %0, %1" : "=v"(xv) : "v"(act_f32(r.rx)));
+    if (GATE) asm("v_mov_b32 %0, %1" : "=v"(zv) : "v"(act_f32(r.rz)));
+    float dtv;
+    if (FUSED) {
+      int acc = 0;
+#pragma unroll
+      for (int q = 0; q < RW; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_sdot4(r.rq[q][j], wdt[q][j], acc, false);
+      if (!LOCAL)  // dropped unless the sums are asked for (rG is then empty) and the lane holds a channel
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc, rG, vg, (uint32_t)t0 * (uint32_t)Di * 4u, 0);
+      dtv = (s_dt * (float)acc) * (float)r.rf;
+    } else {
+      dtv = act_f32(r.rd);
+    }
+    dtv += bias_s;
+    if (a.softplus) dtv = softplus_f(dtv);
+    if (t0 + si >= te) dtv = 0.0f;  // past the sequence end: the state stays as it is
+    s_dd[buf][w][c][si] = make_float2(dtv, dtv * xv);
+    *(float2*)&s_B[buf][w][bp][bt][0] = make_float2(act_f32(r.rb0), act_f32(r.rb1));
+    if (!LOCAL) *(float2*)&s_C[LOCAL ? 0 : buf][w][bp][bt][0] = make_float2(act_f32(r.rc0), act_f32(r.rc1));
+    // 2. the tile after next in flight
+    load_tile(r, t0 + 2 * TT);
+    // 3. this wave's LDS writes before its reads (LDS executes a wave's operations in order;
+    //    the fences keep the compiler from reordering them)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 4. recurrence over the tile, two steps per LDS read
+    float yp[TT];
+#pragma unroll
+    for (int t = 0; t < TT; t += 2) {
+      const float4 dd = *(const float4*)&s_dd[buf][w][c][t];
+      const float4 bb = *(const float4*)&s_B[buf][w][g][t][0];
+      float4 cc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (!LOCAL) cc = *(const float4*)&s_C[LOCAL ? 0 : buf][w][LOCAL ? 0 : g][t][0];
+      {
+        const float ab0 = __builtin_amdgcn_exp2f(dd.x * Al[0]);
+        const float ab1 = __builtin_amdgcn_exp2f(dd.x * Al[1]);
+        h[0] = __builtin_fmaf(ab0, h[0], dd.y * bb.x);
+        h[1] = __builtin_fmaf(ab1, h[1], dd.y * bb.y);
+        yp[t] = __builtin_fmaf(cc.y, h[1], cc.x * h[0]);
+      }
+      {
+        const float ab0 = __builtin_amdgcn_exp2f(dd.z * Al[0]);
+        const float ab1 = __builtin_amdgcn_exp2f(dd.z * Al[1]);
+        h[0] = __builtin_fmaf(ab0, h[0], dd.w * bb.z);
+        h[1] = __builtin_fmaf(ab1, h[1], dd.w * bb.w);
+        yp[t + 1] = __builtin_fmaf(cc.w, h[1], cc.z * h[0]);
+      }
+      if (LOCAL) sum_dt += dd.x + dd.z;
+    }
+    if (!LOCAL) {
+      // 5. readout: reduce the 8 pair partials of each step and scatter the steps over the lanes
+#pragma unroll
+      for (int j = 0; j < 4; ++j) swap32(yp[2 * j], yp[2 * j + 1]);
+      float r1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r1[j] = yp[2 * j] + yp[2 * j + 1];
+      swap16(r1[0], r1[1]);
+      swap16(r1[2], r1[3]);
+      const float r20 = r1[0] + r1[1], r21 = r1[2] + r1[3];
+      const bool hi8 = (lane & 8) != 0;
+      const float keep = hi8 ? r21 : r20, give = hi8 ? r20 : r21;
+      const float y = keep + xor8(give);
+      float yo = y + D_s * xv;
+      if (GATE) yo = yo * silu_gate(zv);
+      buf_st_act<T>(yo, rY, vy, (uint32_t)t0 * sy);  // lanes past the last channel: outside rY
+    }
+  };
+
+  load_tile(R0, tb);
+  __builtin_amdgcn_sched_barrier(0);  // tile 0's loads stay ahead of tile 1's (exact wait counts)
+  load_tile(R1, tb + TT);
+  for (int t0 = tb; t0 < te; t0 += 2 * TT) {
+    run_tile(R0, t0, 0);
+    run_tile(R1, t0 + TT, 1);
+  }
+  if (LOCAL) {
+    if (dv) {
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) ch.st[((b * ch.nchunks + chunk) * Di + d) * NS + SPL * g + i] = h[i];
+      if (g == 0) ch.sdt[(b * ch.nchunks + chunk) * Di + d] = sum_dt;
+    }
+  } else if (a.h_last && dv && chunk == ch.nchunks - 1) {
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) a.h_last[(b * Di + d) * NS + SPL * g + i] = h[i];
+  }
+}
+
 // Pass 2: for every (sequence, channel, state), compose the chunks in order.  Afterwards
 // st[b, c] holds the state entering chunk c + 1.
 __global__ __launch_bounds__(256) void k_scan_m1_combine(const float* __restrict__ A, const float* __restrict__ h0,
@@ -371,20 +615,26 @@ struct ScanPlan {
   size_t off_deq = 0, off_st = 0, ws = 0;
 };
 
+// d_state 16 runs k_scan_m1_g8: 32 channels and pairs of 8-step tiles per block, four blocks
+// per compute unit.
+constexpr int kCPB16 = 32, kTT16 = 16;  // chunks hold whole pairs of 8-step tiles
+
 // Chunk count: a pure function of the shape (so results do not depend on the device).
-// Blocks of batch x channel tiles below 512 (two per MI355X compute unit) are multiplied
-// by time chunks of at least 128 steps.
+// Blocks of batch x channel tiles below a full chip (512 blocks of k_scan_m1, two per MI355X
+// compute unit; 1024 of k_scan_m1_g8) are multiplied by time chunks of at least 128 steps.
 ScanPlan plan_scan(const ScanArgs& a) {
   ScanPlan p;
-  const int64_t blocks = cdiv(a.H, kCPB) * a.batch;
+  const bool g8 = a.N == 16;
+  const int64_t full = g8 ? 1024 : 512;
+  const int64_t blocks = cdiv(a.H, g8 ? kCPB16 : kCPB) * a.batch;
   int64_t T = 1;
-  if (blocks < 512) {
-    T = cdiv(512, blocks);
+  if (blocks < full) {
+    T = cdiv(full, blocks);
     const int64_t tmax = a.L / 128;
     if (T > tmax) T = tmax;
     if (T < 1) T = 1;
   }
-  p.chunk_len = round_up(cdiv(a.L, T), kTT);
+  p.chunk_len = round_up(cdiv(a.L, T), g8 ? kTT16 : kTT);
   p.T = (int)cdiv(a.L, p.chunk_len);
   const int64_t M = a.batch * a.L;
   size_t off = 0;
@@ -429,11 +679,15 @@ hipError_t launch_m1_t(const ScanArgs& a, void* ws, hipStream_t s) {
   // grid (sequence, channel tile, chunk): blocks are dealt to the 8 XCDs round-robin by linear
   // index, so with the sequence fastest the channel tiles of sequence b all run on XCD b mod 8
   // and share its L2 for B, C and the dt codes
-  const unsigned gx = (unsigned)a.batch, gy = (unsigned)cdiv(a.H, kCPB);
+  const unsigned gx = (unsigned)a.batch, gy = (unsigned)cdiv(a.H, NS == 16 ? kCPB16 : kCPB);
   const int rw = fused ? p.cw / 16 : 0;
   auto run = [&](auto rwc, bool local, unsigned gz) {
     constexpr int RWc = decltype(rwc)::value;
-    if (local) hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, 1>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+    if (NS == 16) {
+      if (local) hipLaunchKernelGGL((k_scan_m1_g8<T, RWc, 1>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+      else if (a.gate) hipLaunchKernelGGL((k_scan_m1_g8<T, RWc, 2>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+      else hipLaunchKernelGGL((k_scan_m1_g8<T, RWc, 0>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
+    } else if (local) hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, 1>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
     else if (a.gate) hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, 2>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
     else hipLaunchKernelGGL((k_scan_m1<NS, T, RWc, 0>), dim3(gx, gy, gz), dim3(256), 0, s, a, ch, dc);
   };
