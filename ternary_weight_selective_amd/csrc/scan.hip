@@ -570,7 +570,17 @@ __global__ __launch_bounds__(256, RW >= 3 ? 2 : 4) void k_scan_m1_g8(ScanArgs a,
   load_tile(R0, tb);
   __builtin_amdgcn_sched_barrier(0);  // tile 0's loads stay ahead of tile 1's (exact wait counts)
   load_tile(R1, tb + TT);
+  // Wave priority by progress: the arbiter favours the oldest wave, so the four waves of a SIMD
+  // would otherwise finish one after another, the last ones alone on the SIMD; a wave drops its
+  // priority a step per quarter of its tiles done, so the waves advance together (measured: the
+  // layer's span 46 -> 43 us at the TriSSM shape).
+  const int npairs = (te - tb + 2 * TT - 1) / (2 * TT);
   for (int t0 = tb; t0 < te; t0 += 2 * TT) {
+    const int q = (4 * ((t0 - tb) / (2 * TT))) / npairs;  // quarters done (uniform)
+    if (q == 0) __builtin_amdgcn_s_setprio(3);
+    else if (q == 1) __builtin_amdgcn_s_setprio(2);
+    else if (q == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     run_tile(R0, t0, 0);
     run_tile(R1, t0 + TT, 1);
   }
