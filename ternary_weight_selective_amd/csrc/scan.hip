@@ -524,14 +524,23 @@ __global__ __launch_bounds__(256, RW >= 3 ? 2 : 4) void k_scan_m1_g8(ScanArgs a,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // 4. recurrence over the tile, two steps per LDS read
+    // 4. recurrence over the tile, two steps per LDS read; the reads of the next two steps are
+    //    issued before the arithmetic of the current two (kept in place by scheduling fences),
+    //    so a wave's LDS traffic is spread over its recurrence
     float yp[TT];
+    float4 dd = *(const float4*)&s_dd[buf][w][c][0];
+    float4 bb = *(const float4*)&s_B[buf][w][g][0][0];
+    float4 cc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (!LOCAL) cc = *(const float4*)&s_C[LOCAL ? 0 : buf][w][LOCAL ? 0 : g][0][0];
 #pragma unroll
     for (int t = 0; t < TT; t += 2) {
-      const float4 dd = *(const float4*)&s_dd[buf][w][c][t];
-      const float4 bb = *(const float4*)&s_B[buf][w][g][t][0];
-      float4 cc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (!LOCAL) cc = *(const float4*)&s_C[LOCAL ? 0 : buf][w][LOCAL ? 0 : g][t][0];
+      float4 ddn = dd, bbn = bb, ccn = cc;
+      if (t + 2 < TT) {
+        ddn = *(const float4*)&s_dd[buf][w][c][t + 2];
+        bbn = *(const float4*)&s_B[buf][w][g][t + 2][0];
+        if (!LOCAL) ccn = *(const float4*)&s_C[LOCAL ? 0 : buf][w][LOCAL ? 0 : g][t + 2][0];
+      }
+      __builtin_amdgcn_sched_barrier(0);
       {
         const float ab0 = __builtin_amdgcn_exp2f(dd.x * Al[0]);
         const float ab1 = __builtin_amdgcn_exp2f(dd.x * Al[1]);
@@ -547,6 +556,10 @@ __global__ __launch_bounds__(256, RW >= 3 ? 2 : 4) void k_scan_m1_g8(ScanArgs a,
         yp[t + 1] = __builtin_fmaf(cc.w, h[1], cc.z * h[0]);
       }
       if (LOCAL) sum_dt += dd.x + dd.z;
+      __builtin_amdgcn_sched_barrier(0);
+      dd = ddn;
+      bb = bbn;
+      cc = ccn;
     }
     if (!LOCAL) {
       // 5. readout: reduce the 8 pair partials of each step and scatter the steps over the lanes
