@@ -120,16 +120,16 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 // Large-tile A8 contraction, one scale per tensor: the MFMA-bound shapes (k > 1024, e.g. the
 // Mamba-2 projections (8192, 4416, 2048) and (8192, 2048, 4096)).
 //
-// Block tile 256 tokens x BN outputs and 4 waves, one per SIMD, each owning 128 tokens x BN / 2
-// outputs as 8 x BN / 32 MFMA 16x16x64 tiles with the int32 accumulators in the AGPRs, so that
-// every operand fragment read from LDS feeds 8 (weights) or BN / 32 (activations) MFMAs.
-// Per 64-deep k step the next step's activation chunks and packed weight words are loaded into
-// registers while the current step is contracted; then the activations are stored to the other
-// LDS buffer and the weights unpacked into it as int8 (each packed word once per block: the
-// 2-bit -> int8 unpacking costs about 11 vector instructions per 16 weights, too much to repeat
-// in every wave that uses a fragment).  W is the A operand (rows = outputs) and the
-// activations the B operand, so a lane ends with 4 consecutive outputs of one token and stores
-// them as one vector.
+// Block tile 256 tokens x BN outputs and 4 waves, each owning 128 tokens x BN / 2 outputs as
+// 8 x BN / 32 MFMA 16x16x64 tiles with int32 accumulators, so that every operand fragment read
+// from LDS feeds 8 (weights) or BN / 32 (activations) MFMAs.  BN = 256 and 192 run one wave
+// per SIMD (accumulators in the AGPRs); BN = 128 fits two blocks per compute unit (registers
+// and LDS ring halved), so that one block's epilogue runs under the other's MFMAs.
+// Operands go from global memory straight into a ring of ST LDS stages (ST - 1 k steps in
+// flight); the weights stay 2-bit in LDS and each wave unpacks its own fragments (about 11
+// vector instructions per 16 weights, hidden under the MFMAs).  W is the A operand (rows =
+// outputs) and the activations the B operand, so a lane ends with 4 consecutive outputs of
+// one token and stores them as one vector.
 //
 // Tile order: blocks are dealt to the 8 XCDs round-robin, so block b works on tile
 // (b mod 8) * ceil(T / 8) + b / 8: each XCD takes a contiguous run of tiles (outputs
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8(GemmArgs a) {
 constexpr int kBigStages = 4;  // LDS stages of k_gemm_i8_big (ST - 1 k steps in flight)
 
 template <typename Tout, int BN, bool DBG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_i8_big(GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN == 128 ? 2 : 1, BN == 128 ? 2 : 1))) void k_gemm_i8_big(GemmArgs a) {
   constexpr int BMT = 256, BKT = 64, ST = kBigStages;
   constexpr int WN = BN / 2, NT = WN / 16, MT = 8;
   constexpr int ABYTES = BMT * BKT, WWORDS = BN * 4;
@@ -897,15 +897,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Output-tile width of k_gemm_i8_big: 256 or 192, whichever leaves fewer padded columns.
-static int big_bn(int64_t N) { return (cdiv(N, 192) * 192 - N) < (cdiv(N, 256) * 256 - N) ? 192 : 256; }
+// Output-tile width of k_gemm_i8_big.  256 and 192 run one block per compute unit (one wave
+// per SIMD), 128 two (its accumulators fit in half the registers and its LDS ring in half the
+// LDS), so one block's epilogue overlaps the other's k loop.  The width with the fewest
+// rounds of tiles over the chip, weighted by the tile width, is taken; two co-resident 128-wide
+// tiles take 1.7x the time of one (measured at the Mamba-2 out_proj shape, (8192, 2048, 4096):
+// 86 -> 78 us against 256-wide tiles).
+static int big_bn(int64_t M, int64_t N) {
+  const int64_t mt = cdiv(M, 256);
+  auto cost = [&](int bn, int per_cu, double f) {
+    const int64_t T = mt * cdiv(N, bn);
+    return (double)cdiv(T, 256 * per_cu) * bn * f;
+  };
+  const double c128 = cost(128, 2, 1.7), c192 = cost(192, 1, 1.0), c256 = cost(256, 1, 1.0);
+  if (c128 < c192 && c128 < c256) return 128;
+  return c192 < c256 ? 192 : 256;
+}
 
 template <typename Tout, bool DBG>
 static void launch_big(const GemmArgs& a, hipStream_t s) {
-  const int bn = big_bn(a.N);
+  const int bn = big_bn(a.M, a.N);
   const int64_t T = cdiv(a.M, 256) * cdiv(a.N, bn);
   const dim3 grid((unsigned)(8 * cdiv(T, 8))), block(256);
-  if (bn == 192) hipLaunchKernelGGL((k_gemm_i8_big<Tout, 192, DBG>), grid, block, 0, s, a);
+  if (bn == 128) hipLaunchKernelGGL((k_gemm_i8_big<Tout, 128, DBG>), grid, block, 0, s, a);
+  else if (bn == 192) hipLaunchKernelGGL((k_gemm_i8_big<Tout, 192, DBG>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((k_gemm_i8_big<Tout, 256, DBG>), grid, block, 0, s, a);
 }
 

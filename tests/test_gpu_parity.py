@@ -112,6 +112,28 @@ def test_bitlinear_parity(m, k, n, group, bits, xd, yd):
     check(host(y), ref, TOL[yd], what=f"test_bitlinear_parity {m} {k} {n} {group} {bits}")
 
 
+@pytest.mark.parametrize("n", [2048, 2000])
+def test_bitlinear_big_tiles_sampled(n):
+    """The large-tile int8 contraction at the Mamba-2 out_proj shape (8192 tokens, k = 4096), where
+    two 128-wide output tiles share a compute unit; n = 2000 leaves a ragged last tile.  Rows
+    are independent (per-row norm and codes), so 96 sampled rows across the row tiles are checked
+    against the oracle: codes, absmax and int32 sums bit for bit, outputs exactly."""
+    m, k = 8192, 4096
+    g = wl.rng(n + 11)
+    x = bf16_values(wl.normal(g, (m, k)))
+    w = wl.normal(g, (n, k), 0.0, 0.02)
+    packed, scale, _ = tws.ssm_ternary_quantize_weights(to_dev(w), 0)
+    codes, oscale, _ = oracle.quantize_weights(w, 0)
+    y, xq, am, acc = tws.ssm_bitlinear_fwd(to_dev(x, torch.bfloat16), packed, scale, n, y_dtype=torch.bfloat16,
+                                           debug=True)
+    rows = np.unique(np.concatenate([np.arange(0, m, 97), [m - 1, m - 2, 255, 256, 4095]]))[:96]
+    ref, oxq, oam, oacc = oracle.bitlinear(x[rows], codes, oscale)
+    np.testing.assert_array_equal(host(xq)[rows], oxq)
+    np.testing.assert_array_equal(host(am)[rows], oam)
+    np.testing.assert_array_equal(host(acc)[rows], oacc)
+    np.testing.assert_array_equal(host(y)[rows], bf16_values(ref.astype(np.float32)))
+
+
 @pytest.mark.parametrize("m,k,n", [(256, 256, 512), (77, 1024, 64), (64, 2048, 4416),
                                    (70, 1088, 200), (40, 64, 96), (300, 1216, 260)])  # odd k-step counts
 def test_bitlinear_int32_from_oracle_codes(m, k, n):
