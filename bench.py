@@ -500,7 +500,8 @@ def scan_roofline(cfg: wl.MixerConfig, stages: dict, workload: str) -> dict:
     roof = {"bound": "hbm", "achieved": cost["bytes"] / avg_s / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = read_traffic(kind, "scan", workload)
-    roof["kernel"] = "k_scan_m1" if cfg.kind == wl.MAMBA1 else "k_ssd_seg (+ k_ssd_combine)"
+    roof["kernel"] = (("k_scan_m1_g8" if cfg.d_state == 16 else "k_scan_m1") if cfg.kind == wl.MAMBA1
+                      else "k_ssd_seg (+ k_ssd_combine)")
     roof["bytes_per_launch"] = cost["bytes"]
     roof["bytes_per_token"] = cost["bytes"] / cfg.tokens
     roof["avg_launch_us"] = st["avg_us"]
