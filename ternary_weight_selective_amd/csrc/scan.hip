@@ -643,15 +643,19 @@ struct ScanPlan {
 constexpr int kCPB16 = 32, kTT16 = 16;  // chunks hold whole pairs of 8-step tiles
 
 // Chunk count: a pure function of the shape (so results do not depend on the device).
-// Blocks of batch x channel tiles below a full chip (512 blocks of k_scan_m1, two per MI355X
-// compute unit; 1024 of k_scan_m1_g8) are multiplied by time chunks of at least 128 steps.
+// Fewer than 512 blocks of batch x channel tiles (two waves per SIMD) are multiplied by time
+// chunks of at least 128 steps, up to a full chip: 512 blocks of k_scan_m1 (two per MI355X
+// compute unit), 1024 of k_scan_m1_g8 (four).  From 512 blocks on k_scan_m1_g8 runs unchunked:
+// going from two to four waves per SIMD does not pay for pass 1 (measured at the TernarySSM
+// shape, 16 x 1024 tokens x 1024 channels: 149 us chunked in two, 107 us unchunked; the
+// long-sequence shape, 8 x 8192 x 512, takes 273 us in 8 chunks, 330 us in 4).
 ScanPlan plan_scan(const ScanArgs& a) {
   ScanPlan p;
   const bool g8 = a.N == 16;
   const int64_t full = g8 ? 1024 : 512;
   const int64_t blocks = cdiv(a.H, g8 ? kCPB16 : kCPB) * a.batch;
   int64_t T = 1;
-  if (blocks < full) {
+  if (blocks < 512) {
     T = cdiv(full, blocks);
     const int64_t tmax = a.L / 128;
     if (T > tmax) T = tmax;
