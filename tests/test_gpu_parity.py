@@ -311,6 +311,40 @@ def test_scan_precomputed_dt_codes_identical():
     np.testing.assert_array_equal(y1, y2)
 
 
+@pytest.mark.parametrize("B,L,Di,R,dt,gated", [
+    (2, 70, 96, 40, "f32", False),   # dt_rank 40: three 16-byte code words per token
+    (1, 300, 96, 64, "f32", True),   # dt_rank 64 (four words), cut in two time chunks, gated
+    (2, 50, 72, 48, "bf16", True),   # bf16, three words, gated, a partly filled last wave
+])
+def test_scan_dt_projection_wide_rank(B, L, Di, R, dt, gated):
+    """d_state 16 scan with the dt projection evaluated inside it, at wide dt ranks, against the
+    oracle: the dt pre-activation is the oracle's BitLinear of the dt input (int8 codes and
+    int32 sums identical; the in-scan dequantisation is fp32, reading 38), then the oracle's
+    scan, then the SiLU gate."""
+    N = 16
+    g = wl.rng(B * 1000 + L + R)
+    p = wl.scan_problem(B, L, Di, 1, N, True, seed=L + R)
+    dr = wl.normal(g, (B, L, R))
+    w = wl.normal(g, (Di, R), 0.0, 0.02)
+    z = wl.normal(g, (B, L, Di))
+    x, Bm, Cm = p["x"], p["Bm"], p["Cm"]
+    tdt = torch.float32
+    if dt == "bf16":
+        x, Bm, Cm, dr, z = (bf16_values(v) for v in (x, Bm, Cm, dr, z))
+        tdt = torch.bfloat16
+    packed, scale, _ = tws.ssm_ternary_quantize_weights(to_dev(w))
+    codes, oscale, _ = oracle.quantize_weights(w, 0)
+    pre, *_ = oracle.bitlinear(dr.reshape(B * L, R), codes, oscale)
+    y = tws.ssm_selective_scan_fwd(to_dev(x, tdt), None, to_dev(p["A"]), to_dev(Bm, tdt), to_dev(Cm, tdt),
+                                   to_dev(p["D"]), to_dev(p["dt_bias"]), True,
+                                   dt_proj=dict(dt_in=to_dev(dr, tdt), w_dt=packed, s_dt=scale, dt_rank=R),
+                                   gate=to_dev(z, tdt) if gated else None)
+    ref, _ = oracle.selective_scan(x, pre.reshape(B, L, Di), p["A"], Bm, Cm, p["D"], p["dt_bias"], True)
+    if gated:
+        ref = ref * np.vectorize(oracle.silu)(z.astype(np.float64))
+    check(host(y), ref, TOL[dt], what=f"test_scan_dt_projection_wide_rank {B} {L} {Di} {R} {dt} {gated}")
+
+
 def _softplus_sweep_problem(H, P, N, aps):
     """One token per channel (L = 1, zero initial state), x = 1, B = C = the first unit vector,
     D = 0: then y = softplus(delta + bias) of each channel exactly, in any order of evaluation,
