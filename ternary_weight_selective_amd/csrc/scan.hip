@@ -3,16 +3,17 @@
 // evaluated with a parallel associative scan).  A is per (channel, state); one channel per
 // head.
 //
-// Work split.  A block owns 64 channels (the lanes) of one sequence and one time chunk; its
-// 4 waves split the NS states into 4 groups, so that B and C of a step are the same for a
-// whole wave: they are read from LDS at wave-uniform addresses (a broadcast), for a group of
-// steps at a time with one wait.  Each lane runs the recurrence of NS / 4 states over time in
+// Two kernels.  d_state 16 (k_scan_m1_g8): a channel's states are split over lanes, 8
+// channels x 8 state pairs per wave, independent waves; the readout sum over the pairs is
+// reduced inside the wave (kernel comment below).  Other d_state (k_scan_m1): a block owns 64
+// channels (the lanes) of one sequence and one time chunk; its 4 waves split the NS states
+// into 4 groups, so that B and C of a step are the same for a whole wave: they are read from
+// LDS at wave-uniform addresses (a broadcast); the waves' readout partials meet in LDS and are
+// added in wave order.  In both, each lane runs the recurrence of its states over time in
 // registers: per state and step one exp2 (A is pre-scaled by log2 e), two multiplies and two
-// fused multiply-adds; the kernel is bound by VALU issue.  The waves' readout partials meet
-// in LDS and are added in wave order.
-//
-// Time is staged through LDS in tiles of 32 steps: the next tile's x, B, C (and dt input
-// codes) are loaded into registers, coalesced, while the current tile runs.
+// fused multiply-adds.  Time is staged through LDS in tiles (16 and 8 steps): the next tiles'
+// x, B, C (and dt input codes) are loaded into registers through buffer resources over the
+// block's sequence while the current tile runs.
 //
 // Chunks (the carried inter-chunk state).  When batch x channel tiles give too few blocks
 // to fill the chip, the sequence is cut into T chunks: pass 1 runs every chunk but the last
