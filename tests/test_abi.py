@@ -123,6 +123,9 @@ def _scan(**kw):
     (dict(x=None), NULL),
     (dict(A=None), NULL),
     (dict(Cm=None), NULL),
+    # one sequence spanning 2 GiB of a tensor (the Mamba-1 kind kernels use 32-bit offsets)
+    (dict(seqlen=1 << 22, ld_x=128), UNSUPPORTED),
+    (dict(seqlen=1 << 17, ld_B=4096, ld_C=4096), UNSUPPORTED),
 ])
 def test_scan_rejects(kw, status):
     L = tws.lib()
