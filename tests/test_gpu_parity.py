@@ -112,13 +112,14 @@ def test_bitlinear_parity(m, k, n, group, bits, xd, yd):
     check(host(y), ref, TOL[yd], what=f"test_bitlinear_parity {m} {k} {n} {group} {bits}")
 
 
-@pytest.mark.parametrize("n", [2048, 2000])
-def test_bitlinear_big_tiles_sampled(n):
+@pytest.mark.parametrize("m,k,n", [(8192, 4096, 2048), (8192, 4096, 2000), (16384, 512, 1024)])
+def test_bitlinear_big_tiles_sampled(m, k, n):
     """The large-tile int8 contraction at the Mamba-2 out_proj shape (8192 tokens, k = 4096), where
-    two 128-wide output tiles share a compute unit; n = 2000 leaves a ragged last tile.  Rows
-    are independent (per-row norm and codes), so 96 sampled rows across the row tiles are checked
-    against the oracle: codes, absmax and int32 sums bit for bit, outputs exactly."""
-    m, k = 8192, 4096
+    two 128-wide output tiles share a compute unit (n = 2000 leaves a ragged last tile), and at the
+    TernarySSM in_proj shape (16384 tokens, k = 512, n = 1024), which takes the norm kernel + the
+    large-tile contraction instead of the row-block kernel.  Rows are independent (per-row norm
+    and codes), so 96 sampled rows across the row tiles are checked against the oracle: codes,
+    absmax and int32 sums bit for bit, outputs exactly."""
     g = wl.rng(n + 11)
     x = bf16_values(wl.normal(g, (m, k)))
     w = wl.normal(g, (n, k), 0.0, 0.02)
@@ -126,7 +127,7 @@ def test_bitlinear_big_tiles_sampled(n):
     codes, oscale, _ = oracle.quantize_weights(w, 0)
     y, xq, am, acc = tws.ssm_bitlinear_fwd(to_dev(x, torch.bfloat16), packed, scale, n, y_dtype=torch.bfloat16,
                                            debug=True)
-    rows = np.unique(np.concatenate([np.arange(0, m, 97), [m - 1, m - 2, 255, 256, 4095]]))[:96]
+    rows = np.unique(np.concatenate([np.arange(0, m, m // 89), [m - 1, m - 2, 255, 256, 4095]]))
     ref, oxq, oam, oacc = oracle.bitlinear(x[rows], codes, oscale)
     np.testing.assert_array_equal(host(xq)[rows], oxq)
     np.testing.assert_array_equal(host(am)[rows], oam)
