@@ -51,10 +51,9 @@ struct BLPlan {
 // wave's run of 16-column tiles fits one round (k <= 64 KPL with KPL a power of two, up to
 // min(32 / KPL, 8) tiles per wave, four consumer waves); wider projections reload their weights
 // for every 16-row block.  From kRowsBigM rows on, when the large-tile contraction has at least
-// one 256 x 192 tile per compute unit, the norm kernel + that contraction is faster (TernarySSM
-// shape, 16384 tokens, bf16: in_proj 512 -> 1024 52.6 -> 34.5 us; its out_proj 1024 -> 512,
-// 192 tiles, stays on the row-block kernel: 50.9 us against 79.3).  Both paths give the same
-// bits (same codes, int32 sums and fp64 epilogue).
+// one 256 x 128 tile per compute unit, the norm kernel + that contraction is faster (TernarySSM
+// shape, 16384 tokens, bf16: in_proj 512 -> 1024 52.6 -> 34 us, out_proj 1024 -> 512 50.5 ->
+// 45 us).  Both paths give the same bits (same codes, int32 sums and fp64 epilogue).
 constexpr int64_t kRowsBigM = 2048;
 bool rows_one_round(int64_t k, int64_t n) {
   int64_t kpl = 1;
@@ -93,7 +92,7 @@ ssm_status bl_plan(const ssm_bitlinear_args* a, BLPlan* p) {
     return SSM_OK;
   }
   if (a->act_bits == 8 && a->group_size == 0 && a->k <= kRowsMaxK && (!a->residual || a->n_out <= kRowsResN) &&
-      (a->m < kRowsBigM || rows_one_round(a->k, a->n_out) || cdiv(a->m, 256) * cdiv(a->n_out, 192) < 256)) {
+      (a->m < kRowsBigM || rows_one_round(a->k, a->n_out) || cdiv(a->m, 256) * cdiv(a->n_out, 128) < 256)) {
     p->rows = true;
     p->total = 0;
     return SSM_OK;

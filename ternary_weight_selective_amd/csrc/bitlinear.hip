@@ -902,9 +902,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // LDS), so one block's epilogue overlaps the other's k loop.  The width with the fewest
 // rounds of tiles over the chip, weighted by the tile width, is taken; two co-resident 128-wide
 // tiles take 1.7x the time of one (measured at the Mamba-2 out_proj shape, (8192, 2048, 4096):
-// 86 -> 78 us against 256-wide tiles).
+// 86 -> 78 us against 256-wide tiles).  When the 128-wide tiles fit one round (two per compute
+// unit) they are taken outright: at k <= 1024 a 192-wide tile per compute unit runs latency-bound
+// (TernarySSM out_proj (16384, 512, 1024): 44.7 us with 128-wide tiles, 78.8 with 192).
 static int big_bn(int64_t M, int64_t N) {
   const int64_t mt = cdiv(M, 256);
+  if (mt * cdiv(N, 128) <= 512) return 128;
   auto cost = [&](int bn, int per_cu, double f) {
     const int64_t T = mt * cdiv(N, bn);
     return (double)cdiv(T, 256 * per_cu) * bn * f;
