@@ -245,12 +245,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = w >> 1, ph = w & 1;
   const int kq = lane >> 4, l16 = lane & 15;
-  // per-lane bases of the fragment reads of B and C: pm(16 i + l16, 32 k + 8 kq) = fb + 2048 k +
-  // 512 i; pm(16 i + l16, 32 k + 4 kq) = zb0 + ..., and 16 columns further zb1 + ...
+  // per-lane base of the fragment reads of B and C: pm(16 i + l16, 32 k + 8 kq) = fb + 2048 k +
+  // 512 i
   const int sw = (l16 >> 1) & 3;
   const int fb = l16 * 32 + ((kq ^ sw) << 3);
-  const int zb0 = l16 * 32 + (((kq >> 1) ^ sw) << 3) + 4 * (kq & 1);
-  const int zb1 = l16 * 32 + ((((kq >> 1) + 2) ^ sw) << 3) + 4 * (kq & 1);
   const int64_t L = a.L, H = a.H;
   const int64_t nhb = cdiv(H, HB);
   // blocks are dealt to the 8 XCDs round-robin by index: block i takes work item
@@ -277,7 +275,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t ch0 = (int64_t)seg * sg.seg_ch;
   const int64_t ch1 = ch0 + sg.seg_ch < nch ? ch0 + sg.seg_ch : nch;
 
-  // state h^T: lane holds h[p = 16 (2 ph + ip) + l16][n = 16 mn + 4 kq + r]
+  // state h^T: lane holds h[p = 16 (2 ph + ip) + l16][n = nst(mn) + 8 kq + r], where the state
+  // tiles are taken in pairs: nst(mn) = 32 (mn / 2) + 4 (mn mod 2).  A pair of tiles then holds
+  // eight consecutive n per lane, the k order of one 16-byte fragment read of C's rows in the
+  // product h C^T below (the A rows of the state update are read in the same order).
+  auto nst = [](int mn) { return 32 * (mn >> 1) + 4 * (mn & 1); };
   v4f hT[NT][2];
   {
     const float* src = nullptr;
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int ip = 0; ip < 2; ++ip) {
         const int pp = 16 * (2 * ph + ip) + l16;
-        hT[mn][ip] = src ? *(const v4f*)(src + pp * NS + 16 * mn + 4 * kq) : v4f{0.f, 0.f, 0.f, 0.f};
+        hT[mn][ip] = src ? *(const v4f*)(src + pp * NS + nst(mn) + 8 * kq) : v4f{0.f, 0.f, 0.f, 0.f};
       }
   }
 
@@ -440,8 +442,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                        cvt_pair(hT[2 * m2 + 1][ip][2], hT[2 * m2 + 1][ip][3]));
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          // C rows t = 16 jt + l16 at the slots' n (32 m2 + 4 kq + u, 32 m2 + 16 + 4 kq + u)
-          const v8bf cf = ld44(&sC[zb0 + 2048 * m2 + 512 * jt], &sC[zb1 + 2048 * m2 + 512 * jt]);
+          // C rows t = 16 jt + l16 at the slots' n (32 m2 + 8 kq + u)
+          const v8bf cf = ld8(&sC[fb + 2048 * m2 + 512 * jt]);
 #pragma unroll
           for (int ip = 0; ip < 2; ++ip) {
             zacc[ip][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[ip], cf, zacc[ip][jt], 0, 0, 0);
@@ -574,7 +576,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int mn = 0; mn < NT; ++mn) {
         if (LOCAL && mn == NT / 2) load_part(pr, cn, 2 * kk + 1);
-        const v8bf bt = ld8(&sBT[(16 * mn + l16) * XS + 32 * kk + 8 * kq]);
+        // B^T row n = nst(mn) + 8 (l16 / 4) + l16 mod 4 (output row 4 kq + r is then n = nst(mn) + 8 kq + r)
+        const v8bf bt = ld8(&sBT[(nst(mn) + 8 * (l16 >> 2) + (l16 & 3)) * XS + 32 * kk + 8 * kq]);
 #pragma unroll
         for (int ip = 0; ip < 2; ++ip) {
           hT[mn][ip] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt, xh[ip], hT[mn][ip], 0, 0, 0);
@@ -607,7 +610,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int mn = 0; mn < NT; ++mn)
 #pragma unroll
-      for (int ip = 0; ip < 2; ++ip) *(v4f*)(dst + (16 * (2 * ph + ip) + l16) * NS + 16 * mn + 4 * kq) = hT[mn][ip];
+      for (int ip = 0; ip < 2; ++ip) *(v4f*)(dst + (16 * (2 * ph + ip) + l16) * NS + nst(mn) + 8 * kq) = hT[mn][ip];
   }
   if (LOCAL && hv && ph == 0 && lane == 0) sg.sdec[(b * (sg.S - 1) + seg) * H + head] = sdec;
 }
