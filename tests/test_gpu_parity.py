@@ -112,12 +112,13 @@ def test_bitlinear_parity(m, k, n, group, bits, xd, yd):
     check(host(y), ref, TOL[yd], what=f"test_bitlinear_parity {m} {k} {n} {group} {bits}")
 
 
-@pytest.mark.parametrize("m,k,n", [(8192, 4096, 2048), (8192, 4096, 2000), (16384, 512, 1024)])
+@pytest.mark.parametrize("m,k,n", [(8192, 4096, 2048), (8192, 4096, 2000), (16384, 512, 1024), (8195, 1024, 1024)])
 def test_bitlinear_big_tiles_sampled(m, k, n):
     """The large-tile int8 contraction at the Mamba-2 out_proj shape (8192 tokens, k = 4096), where
     two 128-wide output tiles share a compute unit (n = 2000 leaves a ragged last tile), and at the
     TernarySSM in_proj shape (16384 tokens, k = 512, n = 1024), which takes the norm kernel + the
-    large-tile contraction instead of the row-block kernel.  Rows are independent (per-row norm
+    large-tile contraction instead of the row-block kernel; 8195 rows of k = 1024 leave a ragged
+    last row tile.  Rows are independent (per-row norm
     and codes), so 96 sampled rows across the row tiles are checked against the oracle: codes,
     absmax and int32 sums bit for bit, outputs exactly."""
     g = wl.rng(n + 11)
