@@ -104,6 +104,14 @@ __global__ __launch_bounds__(256) void k_norm_vec(const Tin* __restrict__ x, int
   const bool rv = row < M;  // all waves take part in the barriers
   char* sr = s_row[wv];
   const int nin = K * (int)sizeof(Tin) / 16;
+  // the gains first, unconditionally from clamped columns: a load under a lane-dependent
+  // condition would be waited for inside it, one memory round trip per load
+  float gn[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int k = lane + 64 * i;
+    gn[i] = gain ? gain[k < K ? k : K - 1] : 1.0f;
+  }
   if (rv) {  // every 16-byte chunk of the row in flight at once, then into LDS
     constexpr int CPL = (IN_B / 16 + 63) / 64;
     const v4i* xr = (const v4i*)(x + row * ldx);
@@ -124,9 +132,10 @@ __global__ __launch_bounds__(256) void k_norm_vec(const Tin* __restrict__ x, int
   float v[KPL];
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) {
+  for (int i = 0; i < KPL; ++i) {  // (every column of the buffer is read; those past K are masked)
     const int k = lane + 64 * i;
-    v[i] = (rv && k < K) ? ld_act(se + k) : 0.0f;
+    const float e = ld_act(se + k);
+    v[i] = (rv && k < K) ? e : 0.0f;
     s = __builtin_fmaf(v[i], v[i], s);
   }
   s = wave_sum_butterfly(s);
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(256) void k_norm_vec(const Tin* __restrict__ x, int
   for (int i = 0; i < KPL; ++i) {
     const int k = lane + 64 * i;
     float t = v[i] * r;
-    if (gain) t = (k < K) ? t * gain[k] : 0.0f;
+    if (gain) t = (k < K) ? t * gn[i] : 0.0f;
     v[i] = t;
     m = fmaxf(m, fabsf(t));
   }
